@@ -1,0 +1,203 @@
+"""CPU oracle for the KV-cache codec and compressed-cache decode attention.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+benchmark's CPU-baseline leg may import this package; the library and its
+Python binding never do.  It shares no code with the GPU path: the arithmetic
+lives in ``tq_oracle.c`` (plain loops, fp64), this module only marshals numpy
+arrays.
+
+Every function is pinned by ``tests/test_oracle_pins.py`` against facts that do
+not come from the oracle itself (closed forms, textbook values, the pages'
+worked byte count and fidelity figures, brute force on tiny inputs).
+"""
+import ctypes
+import functools
+import math
+import os
+
+import numpy as np
+
+_DIR = os.path.dirname(os.path.abspath(__file__))
+_lib = None
+
+
+def _L():
+    global _lib
+    if _lib is None:
+        path = os.path.join(_DIR, "liboracle.so")
+        if not os.path.exists(path):
+            raise RuntimeError("oracle/liboracle.so is not built; run __graft_entry__.build()")
+        lib = ctypes.CDLL(path)
+        vp, i32, i64, dbl = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_double
+        lib.orc_half_to_double.argtypes = [ctypes.c_uint16]
+        lib.orc_half_to_double.restype = dbl
+        lib.orc_hadamard.argtypes = [i32, vp]
+        lib.orc_rotation.argtypes = [i32, vp, vp]
+        lib.orc_lloyd_max.argtypes = [i32, vp, vp, vp]
+        lib.orc_lloyd_max.restype = i32
+        lib.orc_norm16.argtypes = [vp, i32, vp]
+        lib.orc_norm16.restype = ctypes.c_uint16
+        lib.orc_encode.argtypes = [vp, i64, i32, i32, vp, vp, vp, vp, vp, vp]
+        lib.orc_pack_rows.argtypes = [vp, i64, i32, i32, vp]
+        lib.orc_unpack_rows.argtypes = [vp, i64, i32, i32, vp]
+        lib.orc_pack_vtile.argtypes = [vp, i32, i32, vp]
+        lib.orc_unpack_vtile.argtypes = [vp, i32, i32, vp]
+        lib.orc_dequant.argtypes = [vp, vp, i64, i32, vp, vp, vp]
+        lib.orc_attention.argtypes = [vp, i32, vp, vp, i64, i32, vp]
+        _lib = lib
+    return _lib
+
+
+def _p(a):
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def half_to_double(h):
+    return _L().orc_half_to_double(int(h))
+
+
+def hadamard(d):
+    """Sylvester Hadamard matrix H_d (float64, entries +-1)."""
+    H = np.zeros((d, d), dtype=np.float64)
+    _L().orc_hadamard(d, _p(H))
+    return H
+
+
+def rotation(d, sign_bits):
+    """R = H D / sqrt(d) for the layer's sign bits (d/8 bytes, LSB-first)."""
+    sb = _c(sign_bits, np.uint8)
+    assert sb.size == d // 8
+    R = np.zeros((d, d), dtype=np.float64)
+    _L().orc_rotation(d, _p(sb), _p(R))
+    return R
+
+
+@functools.lru_cache(maxsize=None)
+def lloyd_max_unit(bits):
+    """Lloyd-Max levels, thresholds and distortion for N(0,1), 2^bits levels."""
+    L = 1 << bits
+    c = np.zeros(L)
+    t = np.zeros(max(L - 1, 1))
+    mse = np.zeros(1)
+    it = _L().orc_lloyd_max(bits, _p(c), _p(t), _p(mse))
+    c.setflags(write=False)
+    t.setflags(write=False)
+    return c, t[: L - 1], float(mse[0]), it
+
+
+def codebook(d, bits):
+    """Levels and thresholds for N(0, 1/d): the unit codebook over sqrt(d)."""
+    c, t, _, _ = lloyd_max_unit(bits)
+    return c / math.sqrt(d), t / math.sqrt(d)
+
+
+def norm16(x):
+    """fp16 bits of the correctly rounded norm of one fp16 vector (uint16 bits)."""
+    xb = _c(x, np.uint16)
+    ex = np.zeros(1)
+    h = _L().orc_norm16(_p(xb), xb.size, _p(ex))
+    return h, float(ex[0])
+
+
+def encode(x, bits, sign_bits, want_band=True):
+    """Encode fp16 vectors x[n][d] (uint16 bits).
+
+    Returns (codes uint8 [n][d] unpacked, norms uint16 [n], band float64 [n][d])."""
+    xb = _c(x, np.uint16)
+    n, d = xb.shape
+    R = rotation(d, sign_bits)
+    c, t = codebook(d, bits)
+    codes = np.zeros((n, d), dtype=np.uint8)
+    norms = np.zeros(n, dtype=np.uint16)
+    band = np.zeros((n, d)) if want_band else None
+    _L().orc_encode(_p(xb), n, d, bits, _p(R), _p(_c(c, np.float64)), _p(_c(t, np.float64)),
+                    _p(codes), _p(norms), _p(band) if want_band else None)
+    return codes, norms, band
+
+
+def pack_rows(codes, bits):
+    cb = _c(codes, np.uint8)
+    n, d = cb.shape
+    out = np.zeros((n, d * bits // 8), dtype=np.uint8)
+    _L().orc_pack_rows(_p(cb), n, d, bits, _p(out))
+    return out
+
+
+def unpack_rows(packed, d, bits):
+    pb = _c(packed, np.uint8)
+    n = pb.shape[0]
+    out = np.zeros((n, d), dtype=np.uint8)
+    _L().orc_unpack_rows(_p(pb), n, d, bits, _p(out))
+    return out
+
+
+def pack_vtiles(codes, bits):
+    """codes [T][d] (T a multiple of 32) -> value tiles [T/32][32*d*bits/8]."""
+    cb = _c(codes, np.uint8)
+    T, d = cb.shape
+    assert T % 32 == 0
+    out = np.zeros((T // 32, 32 * d * bits // 8), dtype=np.uint8)
+    for k in range(T // 32):
+        tile = np.ascontiguousarray(cb[32 * k: 32 * k + 32])
+        row = np.zeros(32 * d * bits // 8, dtype=np.uint8)
+        _L().orc_pack_vtile(_p(tile), d, bits, _p(row))
+        out[k] = row
+    return out
+
+
+def unpack_vtiles(tiles, d, bits):
+    tb = _c(tiles, np.uint8)
+    nt = tb.shape[0]
+    out = np.zeros((nt * 32, d), dtype=np.uint8)
+    for k in range(nt):
+        row = np.ascontiguousarray(tb[k])
+        cod = np.zeros((32, d), dtype=np.uint8)
+        _L().orc_unpack_vtile(_p(row), d, bits, _p(cod))
+        out[32 * k: 32 * k + 32] = cod
+    return out
+
+
+def dequant(codes, norms, bits, sign_bits):
+    """x_hat[n][d] = n16 * R^T c[codes] in the original domain (float64)."""
+    cb = _c(codes, np.uint8)
+    n, d = cb.shape
+    R = rotation(d, sign_bits)
+    c, _ = codebook(d, bits)
+    out = np.zeros((n, d))
+    _L().orc_dequant(_p(cb), _p(_c(norms, np.uint16)), n, d, _p(R), _p(_c(c, np.float64)),
+                     _p(out))
+    return out
+
+
+def attention(q, K, V):
+    """softmax(q K^T / sqrt d) V for q[G][d], K[T][d], V[T][d] (float64)."""
+    qb = _c(q, np.float64)
+    G, d = qb.shape
+    Kb = _c(K, np.float64)
+    Vb = _c(V, np.float64)
+    T = Kb.shape[0]
+    out = np.zeros((G, d))
+    _L().orc_attention(_p(qb), G, _p(Kb), _p(Vb), T, d, _p(out))
+    return out
+
+
+def halves_to_double(x):
+    """fp16 bit patterns -> float64 values (exact)."""
+    return np.asarray(x, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+def decode_stream(k16, v16, q16, bits_k, bits_v, sign_bits):
+    """The whole path for one (layer, seq, kv head) stream, in the original
+    domain: encode K and V, dequantize, attend with the G queries q16[G][d].
+
+    Returns dict(out[G][d], k_codes, k_norms, k_band, v_codes, v_norms, v_band)."""
+    kc, kn, kb = encode(k16, bits_k, sign_bits)
+    vc, vn, vb = encode(v16, bits_v, sign_bits)
+    K = dequant(kc, kn, bits_k, sign_bits)
+    V = dequant(vc, vn, bits_v, sign_bits)
+    out = attention(halves_to_double(q16), K, V)
+    return dict(out=out, k_codes=kc, k_norms=kn, k_band=kb, v_codes=vc, v_norms=vn, v_band=vb)

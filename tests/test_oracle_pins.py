@@ -1,0 +1,464 @@
+"""Pins of the CPU oracle against facts it does not produce itself.
+
+Each test names what it pins and where the fact comes from: the pages (their
+worked byte count, config table and fidelity figures), closed forms, textbook
+values, algebraic identities, and brute force on tiny inputs.
+"""
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+from scipy import integrate, stats
+
+import oracle
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _figures():
+    out = {}
+    with open(os.path.join(GOLDEN, "page_figures.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                k, v = line.split()
+                out[k] = float(v)
+    return out
+
+
+def _rand_signs(rng, d):
+    return rng.integers(0, 256, size=d // 8, dtype=np.uint8)
+
+
+# ------------------------------------------------------------------ Hadamard
+
+
+@pytest.mark.parametrize("d", [1, 2, 4, 8, 16, 64, 128, 256])
+def test_hadamard_closed_form_and_orthogonality(d):
+    """Sylvester matrix: H[i][j] = (-1)^popcount(i & j), H = H^T, H H = d I."""
+    H = oracle.hadamard(d)
+    ref = np.array([[(-1) ** bin(i & j).count("1") for j in range(d)] for i in range(d)])
+    assert np.array_equal(H, ref)
+    assert np.array_equal(H, H.T)
+    assert np.array_equal(H @ H, d * np.eye(d))
+
+
+def test_fwht_brute_force_small():
+    """A textbook in-place butterfly FWHT on the basis vectors reproduces H (d <= 16)."""
+    for d in (2, 4, 8, 16):
+        H = oracle.hadamard(d)
+        for k in range(d):
+            v = np.zeros(d)
+            v[k] = 1.0
+            h = 1
+            while h < d:
+                for i in range(0, d, 2 * h):
+                    for j in range(i, i + h):
+                        a, b = v[j], v[j + h]
+                        v[j], v[j + h] = a + b, a - b
+                h *= 2
+            assert np.array_equal(v, H[:, k])
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_rotation_orthogonal_and_inner_products(d):
+    """R = H D / sqrt(d) is orthogonal; it keeps norms and q.k = (Rq).(Rk)."""
+    rng = np.random.default_rng(d)
+    sb = _rand_signs(rng, d)
+    R = oracle.rotation(d, sb)
+    assert np.abs(R.T @ R - np.eye(d)).max() < 1e-14
+    s = np.array([-1.0 if (sb[j // 8] >> (j % 8)) & 1 else 1.0 for j in range(d)])
+    H = np.array([[(-1) ** bin(i & j).count("1") for j in range(d)] for i in range(d)])
+    assert np.abs(R - H * s[None, :] / math.sqrt(d)).max() < 1e-15
+    x, q, k = rng.standard_normal((3, d))
+    assert abs(np.linalg.norm(R @ x) - np.linalg.norm(x)) < 1e-12
+    assert abs((R @ q) @ (R @ k) - q @ k) < 1e-12
+
+
+# ----------------------------------------------------------------- codebooks
+
+
+def _golden_levels():
+    rows = {}
+    with open(os.path.join(GOLDEN, "lloyd_max_gaussian.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if line and not line.startswith("#"):
+                v = line.split()
+                dec = len(v[1].split(".")[1])
+                rows[int(v[0])] = (float(v[1]), [float(x) for x in v[2:]], 0.6 * 10.0 ** -dec)
+    return rows
+
+
+def test_lloyd_max_one_bit_closed_form():
+    """b = 1: levels +-sqrt(2/pi), distortion 1 - 2/pi (exact)."""
+    c, t, mse, _ = oracle.lloyd_max_unit(1)
+    assert abs(c[1] - math.sqrt(2 / math.pi)) < 1e-12 and c[0] == -c[1]
+    assert t[0] == 0.0
+    assert abs(mse - (1 - 2 / math.pi)) < 1e-12
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_lloyd_max_textbook_levels(bits):
+    """Levels and distortion agree with the textbook Gaussian table."""
+    mse_ref, lv, mse_tol = _golden_levels()[bits]
+    c, _, mse, _ = oracle.lloyd_max_unit(bits)
+    L = 1 << bits
+    assert np.abs(c[L // 2:] - np.array(lv)).max() < 2e-4
+    assert abs(mse - mse_ref) < mse_tol  # the table's last printed digit
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_lloyd_max_optimality_conditions(bits):
+    """Centroid condition by an independent adaptive quadrature (scipy), the
+    midpoint condition, antisymmetry, and cell probabilities summing to 1."""
+    c, t, mse, _ = oracle.lloyd_max_unit(bits)
+    L = 1 << bits
+    edges = [-np.inf] + list(t) + [np.inf]
+    tot = 0.0
+    dist = 0.0
+    for k in range(L):
+        a, b = edges[k], edges[k + 1]
+        mass = stats.norm.cdf(b) - stats.norm.cdf(a)
+        mom = stats.norm.pdf(a) - stats.norm.pdf(b)  # integral of z phi(z)
+        assert abs(mom / mass - c[k]) < 1e-11
+        tot += mass
+        dist += integrate.quad(lambda z: (z - c[k]) ** 2 * stats.norm.pdf(z), a, b,
+                               epsabs=1e-14, epsrel=1e-12)[0]
+    assert abs(tot - 1.0) < 1e-14
+    assert abs(dist - mse) < 1e-10
+    assert np.allclose(t, 0.5 * (c[1:] + c[:-1]), rtol=0, atol=0)
+    assert np.array_equal(c, -c[::-1])
+    assert np.all(np.diff(c) > 0)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_distortion_within_stated_bound(bits):
+    """Unit-variance distortion below the bound (sqrt(3) pi / 2) 4^-b that the
+    tqai page's test suite states ("Test Suite", first item)."""
+    _, _, mse, _ = oracle.lloyd_max_unit(bits)
+    bound = math.sqrt(3) * math.pi / 2 * 4.0 ** (-bits)
+    assert mse < bound
+    # and the bound is not slack by an order of magnitude (it would be for a
+    # wrong density or a dropped term)
+    assert mse > 0.5 * bound
+
+
+def test_codebook_scaling_with_dimension():
+    """N(0, 1/d) codebook = unit codebook / sqrt(d)."""
+    c1, t1, _, _ = oracle.lloyd_max_unit(4)
+    c, t = oracle.codebook(128, 4)
+    assert np.allclose(c * math.sqrt(128), c1, atol=1e-15)
+    assert np.allclose(t * math.sqrt(128), t1, atol=1e-15)
+
+
+# ---------------------------------------------------------------------- norm
+
+_POS = np.arange(0, 0x7C00, dtype=np.uint16)
+_QUANTA = [int(Fraction(float(v)) * (1 << 24)) for v in _POS.view(np.float16)]
+
+
+def _norm16_exact(x16):
+    """Independent exact RNE: binary search of 4 S among the squared sums of
+    neighbouring fp16 values (all in units of 2^-24), Python integers."""
+    S = 0
+    for v in np.asarray(x16, np.uint16).view(np.float16):
+        m = int(Fraction(float(v)) * (1 << 24))
+        S += m * m
+    S4 = 4 * S
+    lo, hi = 0, len(_QUANTA) - 1
+    # largest p with (A_{p-1} + A_p)^2 <= 4S (p = 0 if none)
+    while lo < hi:
+        mid = (lo + hi + 1) // 2
+        if (_QUANTA[mid - 1] + _QUANTA[mid]) ** 2 <= S4:
+            lo = mid
+        else:
+            hi = mid - 1
+    p = lo
+    if p > 0 and (_QUANTA[p - 1] + _QUANTA[p]) ** 2 == S4 and p % 2 == 1:
+        p -= 1  # exact midpoint: the even pattern wins
+    if p == len(_QUANTA) - 1 and (2 * _QUANTA[p] + 2 ** 24 * 32) ** 2 <= S4:
+        return 0x7C00
+    return p
+
+
+def test_norm_exact_random():
+    """fp16 norm equals an independent exact computation on random vectors of
+    the workload's distribution, including near-tie cases."""
+    rng = np.random.default_rng(7)
+    for trial in range(3000):
+        d = [64, 128, 256][trial % 3]
+        x = (rng.standard_normal(d) * math.exp(rng.standard_normal())).astype(np.float16)
+        if trial % 5 == 0:
+            x[rng.integers(0, d, 4)] *= 10
+        xb = x.view(np.uint16)
+        h, _ = oracle.norm16(xb)
+        assert h == _norm16_exact(xb)
+
+
+def test_norm_ties_and_special_cases():
+    """Exact midpoints round to even; zero, single element, subnormals."""
+    tie = np.array([1233, 1644], np.float16).view(np.uint16)  # 3-4-5: norm 2055
+    assert oracle.norm16(tie)[0] == np.float16(2056).view(np.uint16)
+    tie2 = np.array([1239, 1652], np.float16).view(np.uint16)  # norm 2065 -> 2064
+    assert oracle.norm16(tie2)[0] == np.float16(2064).view(np.uint16)
+    above = np.array([1233, 1644, 2 ** -24], np.float16).view(np.uint16)
+    assert oracle.norm16(above)[0] == np.float16(2056).view(np.uint16)
+    below = np.array([1239, 1652, 0.0], np.float16).view(np.uint16)
+    assert oracle.norm16(below)[0] == np.float16(2064).view(np.uint16)
+    assert oracle.norm16(np.zeros(128, np.uint16))[0] == 0
+    for v in [1.5, -3.25, 6.1e-5, 2 ** -24, 65504.0]:
+        x = np.zeros(64, np.float16)
+        x[17] = v
+        assert oracle.norm16(x.view(np.uint16))[0] == np.float16(abs(v)).view(np.uint16)
+    big = np.full(4, 65504, np.float16).view(np.uint16)  # norm 131008 -> inf
+    assert oracle.norm16(big)[0] == 0x7C00
+    for trial in range(200):
+        rng = np.random.default_rng(trial)
+        x = (rng.standard_normal(128) * 1e-6).astype(np.float16).view(np.uint16)
+        assert oracle.norm16(x)[0] == _norm16_exact(x)
+
+
+# ------------------------------------------------------------------ quantize
+
+
+def test_quantize_argmin_equals_threshold_count():
+    """Scalar argmin (the oracle's rule) equals the count of thresholds below y
+    outside the 1e-6 band; the band is the distance to the nearest threshold."""
+    d, bits = 128, 4
+    rng = np.random.default_rng(3)
+    sb = _rand_signs(rng, d)
+    x = rng.standard_normal((400, d)).astype(np.float16).view(np.uint16)
+    codes, norms, band = oracle.encode(x, bits, sb)
+    R = oracle.rotation(d, sb)
+    c, t = oracle.codebook(d, bits)
+    xf = x.view(np.float16).astype(np.float64)
+    y = (xf @ R.T) / np.linalg.norm(xf, axis=1, keepdims=True)
+    cnt = np.searchsorted(t, y, side="left")
+    far = band > 1e-6
+    assert np.array_equal(codes[far], cnt[far])
+    assert np.allclose(band, np.abs(y[..., None] - t).min(-1), atol=1e-13)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_code_histogram_matches_gaussian_cells(bits):
+    """After rotation each coordinate is ~N(0, 1/d): code frequencies match the
+    Gaussian cell probabilities (chi-square, isotropic inputs)."""
+    d = 128
+    x = synth.iso_host(4242, bits, 1500, d)
+    sb = synth.sign_bits(4242, 0, d)
+    codes, _, _ = oracle.encode(x, bits, sb, want_band=False)
+    _, t, _, _ = oracle.lloyd_max_unit(bits)
+    edges = np.r_[-np.inf, t, np.inf]
+    p = np.diff(stats.norm.cdf(edges))
+    obs = np.bincount(codes.ravel(), minlength=1 << bits)
+    chi2 = ((obs - p * obs.sum()) ** 2 / (p * obs.sum())).sum()
+    assert stats.chi2.sf(chi2, (1 << bits) - 1) > 1e-4
+
+
+def test_zero_vector_and_symmetry():
+    """Zero vector: norm 0 and every code 2^(b-1) - 1 (y = 0 sits on the middle
+    threshold; the tie goes to the smaller index).  Exact power-of-two scaling
+    keeps the codes; negation mirrors them (antisymmetric codebook)."""
+    d = 128
+    rng = np.random.default_rng(11)
+    sb = _rand_signs(rng, d)
+    for bits in (2, 3, 4):
+        codes, norms, _ = oracle.encode(np.zeros((2, d), np.uint16), bits, sb)
+        assert np.all(codes == (1 << (bits - 1)) - 1) and np.all(norms == 0)
+        x = rng.standard_normal((50, d)).astype(np.float16)
+        c1, n1, b1 = oracle.encode(x.view(np.uint16), bits, sb)
+        c2, n2, _ = oracle.encode((x * np.float16(4)).view(np.uint16), bits, sb)
+        c3, n3, _ = oracle.encode((-x).view(np.uint16), bits, sb)
+        assert np.array_equal(c1, c2)
+        assert np.array_equal(n2.view(np.float16), n1.view(np.float16) * np.float16(4))
+        far = b1 > 1e-9
+        assert np.array_equal(c3[far], ((1 << bits) - 1 - c1)[far])
+        assert np.array_equal(n3, n1)
+
+
+# ------------------------------------------------------------------- packing
+
+
+def test_bytes_per_token_worked_example():
+    """The tqai page's worked example: FP16 K+V at head dim 128 is 512 B per
+    token per KV head; K4/V2 with fp16 norms is 100 B.  Also the config
+    table's average bits and memory saved."""
+    f = _figures()
+    d = 128
+    rng = np.random.default_rng(0)
+    k = oracle.pack_rows(rng.integers(0, 16, (1, d)), 4)
+    v = oracle.pack_rows(rng.integers(0, 4, (1, d)), 2)
+    per_token = k.nbytes + v.nbytes + 2 + 2
+    assert 2 * d * 2 == f["bytes_per_token_fp16"]
+    assert per_token == f["bytes_per_token_k4v2"]
+    for kb, vb, name in ((4, 2, "k4v2"), (3, 2, "k3v2"), (4, 3, "k4v3")):
+        assert (kb + vb) / 2 == f["avg_bits_" + name]
+        codes_only = d * (kb + vb) / 8
+        with_norms = codes_only + 4
+        saved = 100 * (1 - with_norms / 512)
+        saved_codes_only = 100 * (1 - codes_only / 512)
+        # the table rounds; K4/V3's 78% matches the codes-only saving
+        assert abs(saved - f["saved_pct_" + name]) < 1.0 or \
+            abs(saved_codes_only - f["saved_pct_" + name]) < 1.0
+
+
+def test_pack_rows_bit_positions():
+    """LSB-first: code i occupies bits [b i, b i + b) of the row."""
+    c = np.zeros((1, 64), np.uint8)
+    c[0, 1] = 1
+    assert oracle.pack_rows(c, 4)[0, 0] == 0x10
+    c = np.zeros((1, 64), np.uint8)
+    c[0, 2] = 7  # bits 6, 7, 8
+    p = oracle.pack_rows(c, 3)[0]
+    assert p[0] == 0xC0 and p[1] == 0x01 and p[2:].sum() == 0
+    c = np.zeros((1, 64), np.uint8)
+    c[0, 3] = 2  # 2-bit code at bits 6..7 -> 0b10 << 6
+    assert oracle.pack_rows(c, 2)[0, 0] == 0x80
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_pack_round_trips(bits, d):
+    rng = np.random.default_rng(bits * d)
+    for n in (1, 7, 33):
+        c = rng.integers(0, 1 << bits, (n, d), dtype=np.uint8)
+        assert np.array_equal(oracle.unpack_rows(oracle.pack_rows(c, bits), d, bits), c)
+    c = rng.integers(0, 1 << bits, (64, d), dtype=np.uint8)
+    tiles = oracle.pack_vtiles(c, bits)
+    assert tiles.shape == (2, 32 * d * bits // 8)
+    assert np.array_equal(oracle.unpack_vtiles(tiles, d, bits), c)
+
+
+def test_vtile_bit_positions():
+    """Value tile: segment 16q + r holds coordinate r*(d/16)+m of token tok(q,u)
+    at bit (8m + u) * b; check one hand-placed code."""
+    d, bits = 128, 2
+    c = np.zeros((32, d), np.uint8)
+    # token 21 = 16 + 4*1 + 1 -> q = 1, u = 5; coordinate 3*8 + 2 -> r = 3, m = 2
+    c[21, 26] = 3
+    t = oracle.pack_vtiles(c, bits)[0]
+    seg = d * bits // 16
+    bit = (8 * 2 + 5) * bits
+    nz = np.flatnonzero(t)
+    assert list(nz) == [(16 * 1 + 3) * seg + bit // 8]
+    assert t[nz[0]] == 3 << (bit % 8)
+
+
+# ------------------------------------------------------------------ fidelity
+
+
+def test_fidelity_matches_tqai_benchmark():
+    """Synthetic accuracy figures of the tqai page ("The CLI"): 4-bit keys and
+    2-bit values on isotropic Gaussian vectors, head dim 128.  NMSE within
+    1.5%, cosine within 5e-4, SNR within 0.1 dB; SNR = -10 log10 NMSE and
+    cos ~ sqrt(1 - NMSE) hold internally."""
+    f = _figures()
+    d = 128
+    x = synth.iso_host(2024, 0, 6000, d)
+    sb = synth.sign_bits(2024, 0, d)
+    xf = x.view(np.float16).astype(np.float64)
+    for bits, key in ((4, "keys4"), (2, "values2")):
+        codes, norms, _ = oracle.encode(x, bits, sb, want_band=False)
+        xh = oracle.dequant(codes, norms, bits, sb)
+        nmse = ((xh - xf) ** 2).sum() / (xf ** 2).sum()
+        snr = -10 * math.log10(nmse)
+        cos = np.mean((xh * xf).sum(1) / np.linalg.norm(xh, axis=1) / np.linalg.norm(xf, axis=1))
+        assert abs(nmse / f[key + "_nmse"] - 1) < 0.015, nmse
+        assert abs(snr - f[key + "_snr_db"]) < 0.1
+        assert abs(cos - f[key + "_cos"]) < 5e-4, cos
+        assert abs(cos - math.sqrt(1 - nmse)) < 2e-3
+
+
+# ----------------------------------------------------------------- attention
+
+
+def test_attention_hand_example():
+    """d = 4, T = 2: weights are a logistic function of the score gap."""
+    q = np.array([[2.0, 0.0, 0.0, 0.0]])
+    K = np.array([[1.0, 0, 0, 0], [0, 1.0, 0, 0]])
+    V = np.array([[1.0, 2, 3, 4], [-1.0, 0, 1, 0]])
+    # scores 2/2 = 1 and 0: p0 = e/(e+1)
+    p0 = math.e / (math.e + 1)
+    out = oracle.attention(q, K, V)
+    assert np.allclose(out[0], p0 * V[0] + (1 - p0) * V[1], atol=1e-15)
+
+
+def test_attention_special_cases():
+    rng = np.random.default_rng(5)
+    d, T = 64, 37
+    K = rng.standard_normal((T, d))
+    V = rng.standard_normal((T, d))
+    q = rng.standard_normal((3, d))
+    # one token: the output is that value
+    assert np.allclose(oracle.attention(q, K[:1], V[:1]), np.repeat(V[:1], 3, 0), atol=1e-15)
+    # zero query or identical keys: uniform weights, output = mean value
+    assert np.allclose(oracle.attention(np.zeros((1, d)), K, V)[0], V.mean(0), atol=1e-14)
+    assert np.allclose(oracle.attention(q, np.repeat(K[:1], T, 0), V), np.repeat(V.mean(0)[None], 3, 0),
+                       atol=1e-14)
+    # token order does not matter
+    perm = rng.permutation(T)
+    assert np.allclose(oracle.attention(q, K, V), oracle.attention(q, K[perm], V[perm]), atol=1e-14)
+    # no tokens: zeros
+    assert np.array_equal(oracle.attention(q, K[:0], V[:0]), np.zeros((3, d)))
+
+
+def test_rotated_domain_evaluation_matches_plain():
+    """Attention evaluated in the rotated domain (scores (Rq).c, values summed
+    as levels, one R^T at the end) equals the oracle's plain evaluation over
+    the dequantized cache."""
+    d, T = 128, 300
+    rng = np.random.default_rng(9)
+    sb = _rand_signs(rng, d)
+    k = (rng.standard_normal((T, d)) * 3).astype(np.float16).view(np.uint16)
+    v = rng.standard_normal((T, d)).astype(np.float16).view(np.uint16)
+    q = rng.standard_normal((4, d))
+    kc, kn, _ = oracle.encode(k, 4, sb, want_band=False)
+    vc, vn, _ = oracle.encode(v, 2, sb, want_band=False)
+    plain = oracle.attention(q, oracle.dequant(kc, kn, 4, sb), oracle.dequant(vc, vn, 2, sb))
+    R = oracle.rotation(d, sb)
+    ck, _ = oracle.codebook(d, 4)
+    cv, _ = oracle.codebook(d, 2)
+    knf = kn.view(np.float16).astype(np.float64)
+    vnf = vn.view(np.float16).astype(np.float64)
+    s = ((q @ R.T) @ ck[kc].T) * knf[None] / math.sqrt(d)
+    p = np.exp(s - s.max(1, keepdims=True))
+    acc = (p * vnf[None]) @ cv[vc]
+    rot = (acc @ R) / p.sum(1, keepdims=True)
+    assert np.abs(rot - plain).max() < 1e-12
+
+
+# ------------------------------------------------------------------ generator
+
+
+def test_generator_determinism_and_shape():
+    a = synth.kv_host(1001, 0, 3, 1, 2, 128, 100, 5)
+    b = synth.kv_host(1001, 0, 3, 1, 2, 128, 100, 5)
+    c = synth.kv_host(1001, 0, 3, 1, 2, 128, 98, 7)
+    assert np.array_equal(a, b) and np.array_equal(a, c[2:])
+    assert not np.array_equal(a, synth.kv_host(1001, 1, 3, 1, 2, 128, 100, 5))
+
+
+def test_generator_distribution():
+    """N(0,1) moments, 4 distinct outlier channels x10, lognormal(0, 0.5)
+    per-token scale, balanced sign bits."""
+    z = synth.normals_host(99, 0, 400000)
+    assert abs(z.mean()) < 0.01 and abs(z.std() - 1) < 0.01
+    assert abs((z ** 4).mean() - 3) < 0.05
+    d = 128
+    o = synth.outliers(1002, 0, 5, 3, d)
+    assert len(set(o.tolist())) == 4 and o.min() >= 0 and o.max() < d
+    x = synth.kv_host(1002, 0, 5, 0, 3, d, 0, 4000).view(np.float16).astype(np.float64)
+    rms = np.sqrt((x ** 2).mean(0))
+    mask = np.zeros(d, bool)
+    mask[o] = True
+    ratio = rms[mask].mean() / rms[~mask].mean()
+    assert 8.5 < ratio < 11.5
+    # token scale: log of the per-token rms of the normal channels ~ N(0, 0.5^2)
+    ls = np.log(np.sqrt((x[:, ~mask] ** 2).mean(1)))
+    assert abs(ls.std() - 0.5) < 0.03
+    bits = np.unpackbits(synth.sign_bits(1002, 0, 4096)[None], axis=1)
+    assert abs(bits.mean() - 0.5) < 0.03
