@@ -1,0 +1,186 @@
+/*
+ * tq.h -- TurboQuant-style KV-cache compression and compressed-cache decode
+ * attention for AMD Instinct MI355X (gfx950).  C ABI: plain pointers and sizes.
+ *
+ * The method (sources are the pages this library is built from):
+ *   - Each per-head key or value vector x (fp16, head dim d) is split into its
+ *     norm, stored in FP16, and the unit vector x / ||x||
+ *     ("We Built a Python Library That Cuts LLM Memory Usage by 80%", section
+ *     "The Paper").
+ *   - The unit vector is rotated by the randomized Hadamard transform
+ *     y = (1/sqrt d) H D x (AdapTQ page, "How it works (HAR + VQ)", step 1),
+ *     computed as a fast Walsh-Hadamard transform.  D is a per-layer diagonal
+ *     of signs, shared by keys, values and queries of that layer.
+ *   - Each rotated coordinate, distributed about N(0, 1/d), is quantized
+ *     independently with the Lloyd-Max codebook for that Gaussian at 2, 3 or 4
+ *     bits ("We Built ...", "The Paper"; AdapTQ page, step 2), and the codes
+ *     are bit-packed ("We Built ...", "What's Next": bit-packing).
+ *   - Decode attention rotates the query once and scores it against the codes
+ *     through codebook lookups without dequantizing back to the original
+ *     domain (AdapTQ page, step 3); values are accumulated in the rotated
+ *     domain and rotated back once, the transform being reversible
+ *     ("TurboQuant: 4-bit KV Cache Quantization ... FWHT Preprocessing",
+ *     section "FWHT Preprocessing Layer").
+ *
+ * Conventions for every call:
+ *   - Device pointers are allocated and owned by the caller; the library never
+ *     allocates or frees them.  Host pointers are marked "host".
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Calls that launch kernels are asynchronous on that stream.
+ *   - Every argument the host can check is checked before any launch; on an
+ *     error nothing is written and nothing is launched.  Launch failures
+ *     return TQ_ERR_DEVICE.
+ *   - Supported: head_dim in {64, 128, 256}; bits in {2, 3, 4}.
+ *   - fp16 values travel as their 16-bit patterns (uint16_t).
+ *
+ * Packed formats:
+ *   Row layout (tq_encode output, the key cache):
+ *     one vector = d*bits/8 bytes, a little-endian bit string; coordinate i's
+ *     code occupies bits [bits*i, bits*i + bits); bit j is bit (j % 8) of byte
+ *     j / 8.  Code k means the k-th smallest codebook level.
+ *   Value-tile layout (the value cache):
+ *     the codes of 32 consecutive tokens form a tile of 32*d*bits/8 bytes, cut
+ *     into 64 segments of d*bits/16 bytes.  Segment l = 16*q + r (q in 0..3,
+ *     r in 0..15) is a little-endian bit string holding, for m in 0..d/16-1 and
+ *     u in 0..7, at bit offset (8*m + u)*bits, the code of coordinate
+ *     r*(d/16) + m of tile token tok(q,u) = 4q + u (u < 4) or 16 + 4q + u - 4
+ *     (u >= 4).  The order matches the matrix-core operand layout of the
+ *     decode kernel, so one 16-byte load per lane feeds its value products.
+ *   Norms: fp16 (RNE of the exact Euclidean norm), one per vector.
+ *   Sign bits: d bits per layer, LSB-first in d/8 bytes; bit i set means
+ *     D_ii = -1.
+ */
+#ifndef TQ_H
+#define TQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TQ_OK = 0,
+  TQ_ERR_ARG = 1,         /* null pointer, bad size, misaligned buffer */
+  TQ_ERR_UNSUPPORTED = 2, /* head_dim / bits / group size outside the supported set */
+  TQ_ERR_CAPACITY = 3,    /* an append would write past the cache capacity */
+  TQ_ERR_WORKSPACE = 4,   /* decode workspace smaller than required */
+  TQ_ERR_DEVICE = 5       /* a HIP call or kernel launch failed */
+} tq_status;
+
+/* Human-readable name of a status code (static string). */
+const char* tq_status_str(tq_status s);
+
+/* ------------------------------------------------------------- codebooks -- */
+
+/* Lloyd-Max codebook for N(0, 1/d) ("We Built ...", "The Paper"; AdapTQ page,
+ * step 2: Max-Lloyd codebooks).  Host only, no device work.
+ * centroids (host, 2^bits floats): the levels in increasing order;
+ * bounds (host, 2^bits - 1 floats): the decision thresholds (midpoints).
+ * Returns TQ_ERR_UNSUPPORTED for d or bits outside the supported set. */
+tq_status tq_codebook_compute(int head_dim, int bits, float* centroids, float* bounds);
+
+typedef struct tq_codebook_s* tq_codebook;
+
+/* Build the codebook for (head_dim, bits) and upload its device tables (the
+ * encoder's bucket table and the decoder's lookup table) to the current HIP
+ * device.  Synchronous.  *out receives an immutable handle, usable from any
+ * thread and stream on that device; release it with tq_codebook_free. */
+tq_status tq_codebook_init(int head_dim, int bits, tq_codebook* out);
+
+/* Host copy of the levels / thresholds the device tables were built from
+ * (same as tq_codebook_compute), and the handle's parameters. */
+tq_status tq_codebook_read(tq_codebook cb, float* centroids, float* bounds);
+int tq_codebook_head_dim(tq_codebook cb);
+int tq_codebook_bits(tq_codebook cb);
+
+/* Frees the handle and its device tables (synchronises the device). */
+void tq_codebook_free(tq_codebook cb);
+
+/* ---------------------------------------------------------------- encode -- */
+
+/* Encode n vectors ("We Built ...", "The Paper": norm split, rotation,
+ * per-coordinate codebook quantization; AdapTQ page, steps 1-2).
+ * x:         device, fp16 [n][x_stride] (the first d values of each row are
+ *            the vector), 16-byte aligned, x_stride % 8 == 0, x_stride >= d.
+ * sign_bits: device, d/8 bytes (this layer's D).
+ * codes:     device, [n][d*bits/8] row layout, 8-byte aligned.
+ * norms:     device, fp16 [n], 2-byte aligned.
+ * The codebook fixes d and bits.  n == 0 is a no-op. */
+tq_status tq_encode(tq_codebook cb, const uint16_t* x, int64_t n, int64_t x_stride,
+                    const uint8_t* sign_bits, uint8_t* codes, uint16_t* norms,
+                    void* stream);
+
+/* ------------------------------------------------------------- the cache -- */
+
+/* One compressed KV cache layer; layer i of a multi-layer call lives at the
+ * base pointers plus i * layer_stride (bytes) of each array.
+ *   k_codes: [batch][kv_heads][capacity][d*bits_k/8]     row layout
+ *   v_codes: [batch][kv_heads][capacity/32][32*d*bits_v/8] value-tile layout
+ *   k_norms, v_norms: fp16 [batch][kv_heads][capacity]
+ * capacity % 32 == 0.  Code arrays 16-byte aligned, norm arrays 8-byte
+ * aligned, layer strides multiples of 16.  Rows at or past a sequence's
+ * length are never read by decode. */
+typedef struct {
+  uint8_t* k_codes;
+  uint8_t* v_codes;
+  uint16_t* k_norms;
+  uint16_t* v_norms;
+  int batch, kv_heads, head_dim, bits_k, bits_v, capacity;
+  int64_t layer_stride_k_codes, layer_stride_v_codes;
+  int64_t layer_stride_k_norms, layer_stride_v_norms;
+} tq_kv_cache;
+
+/* Bytes of each array for one layer (host helper, no device work). */
+tq_status tq_cache_layer_bytes(const tq_kv_cache* c, int64_t* k_codes, int64_t* v_codes,
+                               int64_t* k_norms, int64_t* v_norms);
+
+/* Append t_new tokens per sequence to n_layers layers ("We Built ...",
+ * "Under the Hood": the cache compresses on each update).
+ * k_new, v_new: device fp16 [n_layers][batch][kv_heads][t_new][d], 16-byte
+ *               aligned, contiguous.
+ * sign_bits:    device [n_layers][d/8].
+ * pos:          device int32 [batch]: the first row written for sequence b;
+ *               rows pos[b] .. pos[b] + t_new - 1 of every layer and head are
+ *               written, nothing else changes (partially covered value tiles
+ *               keep their other tokens' bits).
+ * host_max_pos: max_b pos[b] if the caller knows it (then host_max_pos + t_new
+ *               <= capacity is checked, else TQ_ERR_CAPACITY), or -1 (then rows
+ *               at or past capacity are skipped on the device).
+ * cbk, cbv:     codebooks with (head_dim, bits_k) and (head_dim, bits_v).
+ * Writing a token with tq_append equals encoding it alone with tq_encode, bit
+ * for bit (value codes rearranged into the tile layout). */
+tq_status tq_append(const tq_kv_cache* c, tq_codebook cbk, tq_codebook cbv,
+                    const uint8_t* sign_bits, const uint16_t* k_new, const uint16_t* v_new,
+                    int t_new, const int32_t* pos, int32_t host_max_pos, int n_layers,
+                    void* stream);
+
+/* ---------------------------------------------------------------- decode -- */
+
+/* Workspace (device bytes, 256-byte aligned) tq_decode_attn needs for these
+ * shapes; 0 means none.  Host helper. */
+size_t tq_decode_workspace_bytes(const tq_kv_cache* c, int q_heads, int max_len,
+                                 int n_layers);
+
+/* One decode step of attention over the compressed cache for n_layers layers
+ * ("We Built ...", "Test Suite": softmax(Q K^T / sqrt d) V; AdapTQ page,
+ * step 3: rotated query scored against the packed codes through lookup
+ * tables).  Query head h reads KV head h / (q_heads / kv_heads).
+ * q:        device fp16 [n_layers][batch][q_heads][d], 16-byte aligned.
+ * seq_lens: device int32 [batch]: tokens 0 .. len-1 are attended; values are
+ *           clamped to [0, max_len]; len 0 gives a zero output.
+ * max_len:  host upper bound on seq_lens, <= capacity (sizes the grid).
+ * out:      device fp32 [n_layers][batch][q_heads][d], in the original domain.
+ * ws:       device workspace of at least tq_decode_workspace_bytes(...) bytes.
+ * Supported group sizes q_heads / kv_heads: 1 .. 8. */
+tq_status tq_decode_attn(const tq_kv_cache* c, tq_codebook cbk, tq_codebook cbv,
+                         const uint8_t* sign_bits, const uint16_t* q, int q_heads,
+                         const int32_t* seq_lens, int max_len, int n_layers, float* out,
+                         void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TQ_H */

@@ -1,0 +1,337 @@
+/*
+ * Host side of the C ABI: status strings, codebook construction and upload,
+ * argument validation, dispatch to the gfx950 launchers.
+ */
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "tq.h"
+#include "tq_internal.h"
+
+extern "C" const char* tq_status_str(tq_status s) {
+  switch (s) {
+    case TQ_OK: return "TQ_OK";
+    case TQ_ERR_ARG: return "TQ_ERR_ARG";
+    case TQ_ERR_UNSUPPORTED: return "TQ_ERR_UNSUPPORTED";
+    case TQ_ERR_CAPACITY: return "TQ_ERR_CAPACITY";
+    case TQ_ERR_WORKSPACE: return "TQ_ERR_WORKSPACE";
+    case TQ_ERR_DEVICE: return "TQ_ERR_DEVICE";
+  }
+  return "TQ_ERR_UNKNOWN";
+}
+
+static bool supported_dim(int d) { return d == 64 || d == 128 || d == 256; }
+static bool supported_bits(int b) { return b >= 2 && b <= 4; }
+
+/* ------------------------------------------------------------ Lloyd-Max -- */
+
+/* P(Z > x) for Z ~ N(0,1), accurate in the tails. */
+static double upper_tail(double x) { return 0.5 * erfc(x * 0.70710678118654752440); }
+static double gauss_pdf(double x) { return 0.39894228040143267794 * exp(-0.5 * x * x); }
+
+/* Probability of the cell (a, b), written so that no tail is computed as a
+ * difference of numbers near 1. */
+static double cell_mass(double a, double b) {
+  if (a >= 0.0) return upper_tail(a) - upper_tail(b);
+  if (b <= 0.0) return upper_tail(-b) - upper_tail(-a);
+  return 1.0 - upper_tail(-a) - upper_tail(b);
+}
+
+/* Lloyd-Max quantizer of N(0,1) by the fixed-point iteration of the two
+ * optimality conditions, with the conditional means in closed form:
+ * E[Z | a < Z < b] = (pdf(a) - pdf(b)) / P(a < Z < b).  Levels start uniform
+ * on [-3, 3]; the set is made exactly antisymmetric at the end; levels and
+ * thresholds are then scaled by 1/sqrt(d) for the N(0, 1/d) coordinates. */
+int tq_lloyd_max_host(int d, int bits, double* c, double* t) {
+  const int L = 1 << bits;
+  for (int k = 0; k < L; ++k) c[k] = -3.0 + 6.0 * (k + 0.5) / L;
+  int it = 0;
+  for (; it < 1000000; ++it) {
+    for (int k = 0; k + 1 < L; ++k) t[k] = 0.5 * (c[k] + c[k + 1]);
+    double move = 0.0;
+    for (int k = 0; k < L; ++k) {
+      double a = k == 0 ? -INFINITY : t[k - 1];
+      double b = k == L - 1 ? INFINITY : t[k];
+      double pa = k == 0 ? 0.0 : gauss_pdf(a), pb = k == L - 1 ? 0.0 : gauss_pdf(b);
+      double nc = (pa - pb) / cell_mass(a, b);
+      move = fmax(move, fabs(nc - c[k]));
+      c[k] = nc;
+    }
+    if (move < 1e-15) break;
+  }
+  for (int k = 0; k < L / 2; ++k) {
+    double m = 0.5 * (c[L - 1 - k] - c[k]);
+    c[k] = -m;
+    c[L - 1 - k] = m;
+  }
+  double s = 1.0 / sqrt((double)d);
+  for (int k = 0; k < L; ++k) c[k] *= s;
+  for (int k = 0; k + 1 < L; ++k) t[k] = 0.5 * (c[k] + c[k + 1]);
+  return it;
+}
+
+extern "C" tq_status tq_codebook_compute(int head_dim, int bits, float* centroids,
+                                         float* bounds) {
+  if (!supported_dim(head_dim) || !supported_bits(bits)) return TQ_ERR_UNSUPPORTED;
+  if (!centroids || !bounds) return TQ_ERR_ARG;
+  double c[16], t[15];
+  tq_lloyd_max_host(head_dim, bits, c, t);
+  for (int k = 0; k < (1 << bits); ++k) centroids[k] = (float)c[k];
+  for (int k = 0; k + 1 < (1 << bits); ++k) bounds[k] = (float)t[k];
+  return TQ_OK;
+}
+
+/* ------------------------------------------------------ decoder LUT scale -- */
+
+/* fp16 bits nearest (ties to even) to a positive double in fp16's normal range. */
+static uint16_t half_rne_normal(double v) {
+  uint64_t u;
+  memcpy(&u, &v, 8);
+  int e = (int)((u >> 52) & 0x7FF) - 1023;
+  uint64_t sig = (u & 0x000FFFFFFFFFFFFFull) | (1ull << 52);
+  uint64_t q = sig >> 42, rem = sig & ((1ull << 42) - 1), half = 1ull << 41;
+  if (rem > half || (rem == half && (q & 1))) ++q;
+  if (q == 2048) { q = 1024; ++e; }
+  return (uint16_t)(((e + 15) << 10) | (uint16_t)(q - 1024));
+}
+
+static double half_value(uint16_t h) {
+  int e = (h >> 10) & 31, f = h & 1023;
+  double v = e ? ldexp(1024.0 + f, e - 25) : ldexp((double)f, -24);
+  return (h & 0x8000) ? -v : v;
+}
+
+/* The decoder stores levels as fp16(c_k * sigma); queries are scaled by
+ * 1/sigma and outputs by 1/sigma, so sigma cancels.  Pick sigma in [1, 2) that
+ * minimises the worst relative fp16 rounding error over the levels. */
+static float lut_scale(const double* c, int L) {
+  double best = 1e300, best_s = 1.0;
+  const int steps = 1 << 20;
+  for (int i = 0; i < steps; ++i) {
+    double s = 1.0 + (double)i / steps, worst = 0.0;
+    for (int k = L / 2; k < L; ++k) {
+      double v = c[k] * s;
+      double r = fabs(half_value(half_rne_normal(v)) / v - 1.0);
+      if (r > worst) worst = r;
+      if (worst >= best) break;
+    }
+    if (worst < best) { best = worst; best_s = s; }
+  }
+  return (float)best_s;
+}
+
+/* --------------------------------------------------------------- handles -- */
+
+static tq_status build_codebook(int d, int bits, tq_codebook_s* cb) {
+  const int L = 1 << bits;
+  cb->d = d;
+  cb->bits = bits;
+  tq_lloyd_max_host(d, bits, cb->centroids64, cb->bounds64);
+  for (int k = 0; k < L; ++k) cb->centroids[k] = (float)cb->centroids64[k];
+  for (int k = 0; k + 1 < L; ++k) cb->bounds[k] = (float)cb->bounds64[k];
+  /* bucket width <= 0.8 of the closest threshold gap */
+  double gap = 1e300;
+  for (int k = 0; k + 2 < L; ++k) gap = fmin(gap, cb->bounds64[k + 1] - cb->bounds64[k]);
+  int nbh = 1;
+  while (nbh * gap < 1.25) nbh *= 2;
+  cb->nb_half = nbh;
+  cb->enc_entries = 2 * nbh + 2;
+  cb->sigma = lut_scale(cb->centroids64, L);
+  return TQ_OK;
+}
+
+extern "C" tq_status tq_codebook_init(int head_dim, int bits, tq_codebook* out) {
+  if (!out) return TQ_ERR_ARG;
+  *out = nullptr;
+  if (!supported_dim(head_dim) || !supported_bits(bits)) return TQ_ERR_UNSUPPORTED;
+  tq_codebook_s* cb = (tq_codebook_s*)calloc(1, sizeof(tq_codebook_s));
+  if (!cb) return TQ_ERR_ARG;
+  build_codebook(head_dim, bits, cb);
+  const int L = 1 << bits;
+
+  /* encoder bucket table */
+  const int ne = cb->enc_entries;
+  tq_enc_entry* et = (tq_enc_entry*)calloc((size_t)ne, sizeof(tq_enc_entry));
+  float thr_u[15];
+  for (int k = 0; k + 1 < L; ++k) thr_u[k] = (float)((cb->bounds64[k] + 1.0) * cb->nb_half + 1.0);
+  for (int j = 0; j < ne; ++j) {
+    uint32_t base = 0;
+    float thr = (float)(j + 1);
+    int inside = 0;
+    for (int k = 0; k + 1 < L; ++k) {
+      if (thr_u[k] < (float)j) ++base;
+      else if (thr_u[k] < (float)(j + 1)) { thr = thr_u[k]; ++inside; }
+    }
+    if (inside > 1) { free(et); free(cb); return TQ_ERR_UNSUPPORTED; }
+    et[j].thr = thr;
+    et[j].base = base;
+  }
+  /* decoder lookup table: fp16(level * sigma) */
+  uint16_t h[16];
+  for (int k = 0; k < L; ++k) {
+    double v = cb->centroids64[k] * cb->sigma;
+    uint16_t m = half_rne_normal(fabs(v));
+    h[k] = (uint16_t)(v < 0 ? (m | 0x8000) : m);
+  }
+  size_t lut_words = bits == 2 ? 512 : (bits == 3 ? 64 : 256);
+  uint32_t* lut = (uint32_t*)calloc(lut_words, 4);
+  if (bits == 4) {
+    for (int b = 0; b < 256; ++b) lut[b] = h[b & 15] | ((uint32_t)h[b >> 4] << 16);
+  } else if (bits == 3) {
+    for (int v = 0; v < 64; ++v) lut[v] = h[v & 7] | ((uint32_t)h[v >> 3] << 16);
+  } else {
+    for (int b = 0; b < 256; ++b) {
+      lut[2 * b] = h[b & 3] | ((uint32_t)h[(b >> 2) & 3] << 16);
+      lut[2 * b + 1] = h[(b >> 4) & 3] | ((uint32_t)h[b >> 6] << 16);
+    }
+  }
+  size_t enc_bytes = ((size_t)ne * sizeof(tq_enc_entry) + 255) & ~(size_t)255;
+  size_t total = enc_bytes + lut_words * 4;
+  tq_status st = TQ_OK;
+  if (hipGetDevice(&cb->device) != hipSuccess || hipMalloc(&cb->dev_mem, total) != hipSuccess) {
+    st = TQ_ERR_DEVICE;
+  } else if (hipMemcpy(cb->dev_mem, et, (size_t)ne * sizeof(tq_enc_entry),
+                       hipMemcpyHostToDevice) != hipSuccess ||
+             hipMemcpy((char*)cb->dev_mem + enc_bytes, lut, lut_words * 4,
+                       hipMemcpyHostToDevice) != hipSuccess) {
+    (void)hipFree(cb->dev_mem);
+    st = TQ_ERR_DEVICE;
+  }
+  free(et);
+  free(lut);
+  if (st != TQ_OK) { free(cb); return st; }
+  cb->enc_table = (const tq_enc_entry*)cb->dev_mem;
+  cb->dec_lut = (const uint32_t*)((char*)cb->dev_mem + enc_bytes);
+  *out = cb;
+  return TQ_OK;
+}
+
+extern "C" tq_status tq_codebook_read(tq_codebook cb, float* centroids, float* bounds) {
+  if (!cb || !centroids || !bounds) return TQ_ERR_ARG;
+  for (int k = 0; k < (1 << cb->bits); ++k) centroids[k] = cb->centroids[k];
+  for (int k = 0; k + 1 < (1 << cb->bits); ++k) bounds[k] = cb->bounds[k];
+  return TQ_OK;
+}
+
+extern "C" int tq_codebook_head_dim(tq_codebook cb) { return cb ? cb->d : 0; }
+extern "C" int tq_codebook_bits(tq_codebook cb) { return cb ? cb->bits : 0; }
+
+extern "C" void tq_codebook_free(tq_codebook cb) {
+  if (!cb) return;
+  if (cb->dev_mem) {
+    int cur = -1;
+    (void)hipGetDevice(&cur);
+    if (cur != cb->device) (void)hipSetDevice(cb->device);
+    (void)hipDeviceSynchronize();
+    (void)hipFree(cb->dev_mem);
+    if (cur >= 0 && cur != cb->device) (void)hipSetDevice(cur);
+  }
+  free(cb);
+}
+
+/* ------------------------------------------------------------ validation -- */
+
+static bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+extern "C" tq_status tq_encode(tq_codebook cb, const uint16_t* x, int64_t n, int64_t x_stride,
+                               const uint8_t* sign_bits, uint8_t* codes, uint16_t* norms,
+                               void* stream) {
+  if (!cb || n < 0) return TQ_ERR_ARG;
+  if (n == 0) return TQ_OK;
+  if (!x || !sign_bits || !codes || !norms) return TQ_ERR_ARG;
+  if (x_stride < cb->d || x_stride % 8 != 0) return TQ_ERR_ARG;
+  if (!aligned(x, 16) || !aligned(codes, 8) || !aligned(norms, 2)) return TQ_ERR_ARG;
+  return tq_launch_encode_rows(cb, x, n, x_stride, sign_bits, codes, norms,
+                               (hipStream_t)stream);
+}
+
+static tq_status check_cache(const tq_kv_cache* c) {
+  if (!c) return TQ_ERR_ARG;
+  if (!supported_dim(c->head_dim) || !supported_bits(c->bits_k) || !supported_bits(c->bits_v))
+    return TQ_ERR_UNSUPPORTED;
+  if (c->batch <= 0 || c->kv_heads <= 0 || c->capacity <= 0 || c->capacity % 32 != 0)
+    return TQ_ERR_ARG;
+  if (!c->k_codes || !c->v_codes || !c->k_norms || !c->v_norms) return TQ_ERR_ARG;
+  if (!aligned(c->k_codes, 16) || !aligned(c->v_codes, 16) || !aligned(c->k_norms, 8) ||
+      !aligned(c->v_norms, 8))
+    return TQ_ERR_ARG;
+  if (c->layer_stride_k_codes % 16 || c->layer_stride_v_codes % 16 ||
+      c->layer_stride_k_norms % 16 || c->layer_stride_v_norms % 16)
+    return TQ_ERR_ARG;
+  return TQ_OK;
+}
+
+extern "C" tq_status tq_cache_layer_bytes(const tq_kv_cache* c, int64_t* k_codes,
+                                          int64_t* v_codes, int64_t* k_norms,
+                                          int64_t* v_norms) {
+  if (!c) return TQ_ERR_ARG;
+  if (!supported_dim(c->head_dim) || !supported_bits(c->bits_k) || !supported_bits(c->bits_v))
+    return TQ_ERR_UNSUPPORTED;
+  if (c->batch <= 0 || c->kv_heads <= 0 || c->capacity <= 0 || c->capacity % 32 != 0)
+    return TQ_ERR_ARG;
+  int64_t rows = (int64_t)c->batch * c->kv_heads * c->capacity;
+  if (k_codes) *k_codes = rows * c->head_dim * c->bits_k / 8;
+  if (v_codes) *v_codes = rows * c->head_dim * c->bits_v / 8;
+  if (k_norms) *k_norms = rows * 2;
+  if (v_norms) *v_norms = rows * 2;
+  return TQ_OK;
+}
+
+static bool codebook_matches(const tq_codebook_s* cb, int d, int bits) {
+  return cb && cb->d == d && cb->bits == bits;
+}
+
+extern "C" tq_status tq_append(const tq_kv_cache* c, tq_codebook cbk, tq_codebook cbv,
+                               const uint8_t* sign_bits, const uint16_t* k_new,
+                               const uint16_t* v_new, int t_new, const int32_t* pos,
+                               int32_t host_max_pos, int n_layers, void* stream) {
+  tq_status st = check_cache(c);
+  if (st != TQ_OK) return st;
+  if (!codebook_matches(cbk, c->head_dim, c->bits_k) ||
+      !codebook_matches(cbv, c->head_dim, c->bits_v))
+    return TQ_ERR_ARG;
+  if (t_new < 0 || n_layers < 1) return TQ_ERR_ARG;
+  if (t_new == 0) return TQ_OK;
+  if (!sign_bits || !k_new || !v_new || !pos) return TQ_ERR_ARG;
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(pos, 4)) return TQ_ERR_ARG;
+  if (host_max_pos < -1) return TQ_ERR_ARG;
+  if (host_max_pos >= 0 && (int64_t)host_max_pos + t_new > c->capacity) return TQ_ERR_CAPACITY;
+  return tq_launch_append(c, cbk, cbv, sign_bits, k_new, v_new, t_new, pos, n_layers,
+                          (hipStream_t)stream);
+}
+
+static tq_status check_decode(const tq_kv_cache* c, int q_heads, int max_len, int n_layers) {
+  tq_status st = check_cache(c);
+  if (st != TQ_OK) return st;
+  if (q_heads <= 0 || n_layers < 1 || max_len < 0 || max_len > c->capacity) return TQ_ERR_ARG;
+  if (q_heads % c->kv_heads != 0) return TQ_ERR_ARG;
+  if (q_heads / c->kv_heads > 8) return TQ_ERR_UNSUPPORTED;
+  return TQ_OK;
+}
+
+extern "C" size_t tq_decode_workspace_bytes(const tq_kv_cache* c, int q_heads, int max_len,
+                                            int n_layers) {
+  if (check_decode(c, q_heads, max_len, n_layers) != TQ_OK) return 0;
+  return tq_plan_decode(c, q_heads, max_len, n_layers).ws_bytes;
+}
+
+extern "C" tq_status tq_decode_attn(const tq_kv_cache* c, tq_codebook cbk, tq_codebook cbv,
+                                    const uint8_t* sign_bits, const uint16_t* q, int q_heads,
+                                    const int32_t* seq_lens, int max_len, int n_layers,
+                                    float* out, void* ws, size_t ws_bytes, void* stream) {
+  tq_status st = check_decode(c, q_heads, max_len, n_layers);
+  if (st != TQ_OK) return st;
+  if (!codebook_matches(cbk, c->head_dim, c->bits_k) ||
+      !codebook_matches(cbv, c->head_dim, c->bits_v))
+    return TQ_ERR_ARG;
+  if (!sign_bits || !q || !seq_lens || !out) return TQ_ERR_ARG;
+  if (!aligned(q, 16) || !aligned(out, 16) || !aligned(seq_lens, 4)) return TQ_ERR_ARG;
+  tq_decode_plan plan = tq_plan_decode(c, q_heads, max_len, n_layers);
+  if (plan.ws_bytes > 0 && (!ws || ws_bytes < plan.ws_bytes || !aligned(ws, 256)))
+    return TQ_ERR_WORKSPACE;
+  return tq_launch_decode(c, cbk, cbv, sign_bits, q, q_heads, seq_lens, max_len, n_layers, out,
+                          ws, plan, (hipStream_t)stream);
+}

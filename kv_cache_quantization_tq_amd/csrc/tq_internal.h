@@ -1,0 +1,65 @@
+/*
+ * Internal declarations shared by the host entry points (tq_host.cpp) and the
+ * gfx950 kernels (tq_encode.hip, tq_decode.hip).
+ */
+#ifndef TQ_INTERNAL_H
+#define TQ_INTERNAL_H
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tq.h"
+
+/* Encoder bucket table: the rotated, normalised coordinate y in [-1, 1] maps
+ * to u = (y + 1) * nb_half + 1, bucket floor(u) in 1 .. 2*nb_half + 1 (entry 0
+ * is never selected, so u stays positive).  A bucket holds
+ * at most one threshold: code = base + (u > thr).  Buckets without a threshold
+ * store thr = bucket + 1, never exceeded inside the bucket. */
+struct tq_enc_entry {
+  float thr;
+  uint32_t base;
+};
+
+struct tq_codebook_s {
+  int d, bits;
+  int nb_half;           /* buckets per unit of y */
+  int enc_entries;       /* 2 * nb_half + 2 */
+  float sigma;           /* decoder lookup-table scale (levels stored as fp16(c * sigma)) */
+  double centroids64[16];
+  double bounds64[15];
+  float centroids[16];
+  float bounds[15];
+  int device;
+  void* dev_mem;         /* one device allocation: encoder table, then decoder table */
+  const tq_enc_entry* enc_table;
+  const uint32_t* dec_lut; /* bits 2: 256 x 2 words; bits 3: 64 words; bits 4: 256 words */
+};
+
+/* Host-side Lloyd-Max (levels / thresholds in fp64, N(0, 1/d)). */
+int tq_lloyd_max_host(int d, int bits, double* c, double* t);
+
+/* Launchers (argument checks are done by the callers). */
+tq_status tq_launch_encode_rows(const tq_codebook_s* cb, const uint16_t* x, int64_t n,
+                                int64_t x_stride, const uint8_t* sign_bits, uint8_t* codes,
+                                uint16_t* norms, hipStream_t stream);
+
+tq_status tq_launch_append(const tq_kv_cache* c, const tq_codebook_s* cbk,
+                           const tq_codebook_s* cbv, const uint8_t* sign_bits,
+                           const uint16_t* k_new, const uint16_t* v_new, int t_new,
+                           const int32_t* pos, int n_layers, hipStream_t stream);
+
+/* Split count and workspace layout of one decode call. */
+struct tq_decode_plan {
+  int splits;          /* token splits per (layer, seq, kv head) */
+  int tiles_per_split; /* 32-token tiles per split */
+  size_t ws_bytes;     /* partial (m, l, acc[d]) records; 0 when splits == 1 */
+};
+tq_decode_plan tq_plan_decode(const tq_kv_cache* c, int q_heads, int max_len, int n_layers);
+
+tq_status tq_launch_decode(const tq_kv_cache* c, const tq_codebook_s* cbk,
+                           const tq_codebook_s* cbv, const uint8_t* sign_bits,
+                           const uint16_t* q, int q_heads, const int32_t* seq_lens,
+                           int max_len, int n_layers, float* out, void* ws,
+                           const tq_decode_plan& plan, hipStream_t stream);
+
+#endif

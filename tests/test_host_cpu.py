@@ -1,0 +1,108 @@
+"""Host-side checks that need no GPU: the C ABI loads and exports every
+declared symbol, argument validation happens before any device work, the
+library's codebook agrees with the oracle's, and the decode planning."""
+import ctypes
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+import kv_cache_quantization_tq_amd as tq
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "tq.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(tq_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_declarations_are_exported():
+    names = _declared()
+    assert set(names) == set(tq.EXPORTS)
+    L = tq.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings():
+    L = tq.lib()
+    for code, name in tq.STATUS.items():
+        assert L.tq_status_str(code).decode() == name
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_library_codebook_matches_oracle(d, bits):
+    """Independent Lloyd-Max implementations (erfc closed forms vs Simpson
+    quadrature) agree to fp32 rounding."""
+    c, t = tq.codebook_compute(d, bits)
+    oc, ot = oracle.codebook(d, bits)
+    assert np.abs(np.array(c) - oc).max() <= 1e-7 * np.abs(oc).max()
+    assert np.abs(np.array(t) - ot).max() <= 1e-7 * np.abs(oc).max()
+
+
+def test_codebook_compute_rejects_unsupported():
+    L = tq.lib()
+    buf = (ctypes.c_float * 16)()
+    assert L.tq_codebook_compute(96, 4, buf, buf) == 2
+    assert L.tq_codebook_compute(128, 5, buf, buf) == 2
+    assert L.tq_codebook_compute(128, 4, None, buf) == 1
+
+
+def _fake_cache(**kw):
+    s = tq.KVCacheStruct()
+    s.k_codes = s.v_codes = s.k_norms = s.v_norms = 1 << 20
+    s.batch, s.kv_heads, s.head_dim, s.bits_k, s.bits_v, s.capacity = 1, 8, 128, 4, 2, 1024
+    for k, v in kw.items():
+        setattr(s, k, v)
+    return s
+
+
+def test_validation_before_device_work():
+    """Bad caches and sizes are rejected on the host (no GPU is touched)."""
+    L = tq.lib()
+    vp = ctypes.c_void_p
+    bad = [dict(capacity=1000), dict(head_dim=96), dict(bits_k=5), dict(batch=0),
+           dict(k_codes=(1 << 20) + 4), dict(layer_stride_k_codes=8)]
+    for kw in bad:
+        s = _fake_cache(**kw)
+        rc = L.tq_append(ctypes.byref(s), None, None, vp(1), vp(16), vp(16), 1, vp(4), 0, 1, None)
+        assert rc in (1, 2), kw
+        rc = L.tq_decode_attn(ctypes.byref(s), None, None, vp(1), vp(16), 8, vp(4), 16, 1, vp(16),
+                              None, 0, None)
+        assert rc in (1, 2), kw
+    s = _fake_cache()
+    # group size 16 is unsupported; q_heads not a multiple of kv_heads is an error
+    assert L.tq_decode_attn(ctypes.byref(s), None, None, vp(1), vp(16), 128, vp(4), 16, 1, vp(16),
+                            None, 0, None) == 2
+    assert L.tq_decode_attn(ctypes.byref(s), None, None, vp(1), vp(16), 12, vp(4), 16, 1, vp(16),
+                            None, 0, None) == 1
+    # max_len beyond capacity
+    assert L.tq_decode_attn(ctypes.byref(s), None, None, vp(1), vp(16), 32, vp(4), 2048, 1,
+                            vp(16), None, 0, None) == 1
+    # null codebook handles
+    assert L.tq_encode(None, vp(16), 4, 128, vp(1), vp(16), vp(16), None) == 1
+    assert L.tq_append(ctypes.byref(s), None, None, vp(1), vp(16), vp(16), 1, vp(4), 0, 1,
+                       None) == 1
+
+
+def test_workspace_planning():
+    L = tq.lib()
+    s = _fake_cache(capacity=32768)
+    # one layer, 8 KV heads, 32K tokens: several splits -> records of (d + 2) floats
+    nb = L.tq_decode_workspace_bytes(ctypes.byref(s), 32, 32768, 1)
+    assert nb > 0 and nb % (32 * 130 * 4) == 0
+    # many units -> one split, no workspace
+    s.batch = 64
+    assert L.tq_decode_workspace_bytes(ctypes.byref(s), 32, 8192, 32) == 0
+    # layer bytes: the page's 100 B per token per KV head at d = 128, K4/V2
+    s = _fake_cache(batch=1, kv_heads=1, capacity=32)
+    k, v, kn, vn = (ctypes.c_int64() for _ in range(4))
+    assert L.tq_cache_layer_bytes(ctypes.byref(s), ctypes.byref(k), ctypes.byref(v),
+                                  ctypes.byref(kn), ctypes.byref(vn)) == 0
+    assert (k.value + v.value + kn.value + vn.value) // 32 == 100
