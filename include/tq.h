@@ -159,7 +159,9 @@ tq_status tq_append(const tq_kv_cache* c, tq_codebook cbk, tq_codebook cbv,
 /* ---------------------------------------------------------------- decode -- */
 
 /* Workspace (device bytes, 256-byte aligned) tq_decode_attn needs for these
- * shapes; 0 means none.  Host helper. */
+ * shapes; 0 means none.  Host helper.  The workspace must be zero-filled
+ * before its first use; every call leaves it ready for the next (its arrival
+ * counters return to zero).  Calls that share a workspace must not overlap. */
 size_t tq_decode_workspace_bytes(const tq_kv_cache* c, int q_heads, int max_len,
                                  int n_layers);
 

@@ -215,9 +215,9 @@ def decode(cache, cbk, cbv, sign_bits, q, seq_lens, max_len, out, ws=None, layer
 
 
 def workspace(cache, q_heads, max_len, n_layers=None, layer0=0, device="cuda"):
-    """A torch workspace tensor sized for tq_decode_attn (None if none is needed)."""
+    """A zero-filled torch workspace for tq_decode_attn (None if none is needed)."""
     import torch
     nb = decode_workspace_bytes(cache, q_heads, max_len, n_layers, layer0)
     if nb == 0:
         return None
-    return torch.empty(nb, dtype=torch.uint8, device=device)
+    return torch.zeros(nb, dtype=torch.uint8, device=device)

@@ -20,6 +20,9 @@
  *           fp16 remainder q'' - fp16(q''); a row_ror:8 DPP add joins them.
  *   values: Acc^T[16 coords x 16 cols] += Vdeq[16 x 32 tokens] * P'[32 x 16],
  *           P' = fp16(p * m_j), one MFMA per 16 coordinates.
+ * Splits of one (layer, seq, kv head) write (m, l, acc) records; the last
+ * split to arrive (an atomic counter per unit, reset by that split) merges
+ * them and writes the output, so a call is a single kernel.
  * The levels are stored as fp16(c * sigma) with sigma chosen per codebook to
  * minimise their fp16 rounding; sigma is divided out of the query and output.
  *
@@ -40,47 +43,53 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = 4;        /* waves per workgroup */
-constexpr int kRep = 8;          /* lookup-table copies in LDS (lane % kRep) */
-constexpr float kLog2e = 1.4426950408889634f;
-
+constexpr int kWaves = 8;        /* waves per workgroup */
+/* Decoder lookup tables in LDS.  Every lookup maps the codes of two
+ * coordinates to their two fp16 levels (one 32-bit word):
+ *   bits 4: a byte (256 entries), bits 3: 6 bits (64), bits 2: a nibble (16).
+ * Entry e owns a 256-byte row holding 64 copies of its word; lane l reads copy
+ * l, at byte (e << 8) | (l << 2), so the 64 lanes of a lookup hit 64 different
+ * banks whatever the codes.  The address is one byte permute for bits 4 and 2
+ * (the index byte goes to bits 8..15, the lane offset to bits 0..7). */
 template <int B>
 struct Lut {
-  /* bits 2: byte -> 4 halves (2 words); 3: 6 bits -> 2 halves; 4: byte -> 2 halves */
-  static constexpr int ENTRIES = B == 3 ? 64 : 256;
-  static constexpr int WORDS = B == 2 ? 2 : 1;
-  static constexpr int BYTES = ENTRIES * WORDS * 4 * kRep;
+  static constexpr int ENTRIES = B == 4 ? 256 : (B == 3 ? 64 : 16);
+  static constexpr int BYTES = ENTRIES * 256;
 };
 
-/* Copy a lookup table into LDS with kRep interleaved copies:
- * entry e copy r at word (e * kRep + r) * WORDS. */
+/* Fill a table: the source is one word per entry. */
 template <int B>
 __device__ inline void load_lut(uint32_t* dst, const uint32_t* src) {
-  constexpr int W = Lut<B>::WORDS;
-  for (int i = threadIdx.x; i < Lut<B>::ENTRIES * kRep; i += blockDim.x) {
-    const int e = i / kRep;
-#pragma unroll
-    for (int w = 0; w < W; ++w) dst[i * W + w] = src[e * W + w];
-  }
+  for (int i = threadIdx.x; i < Lut<B>::ENTRIES * 64; i += blockDim.x) dst[i] = src[i >> 6];
 }
 
-/* Dequantize an 8*B-bit field (8 codes) into 8 fp16 (4 words). */
+/* LDS word at byte address a of table t (a = (entry << 8) | lane offset). */
+__device__ inline uint32_t lut_at(const uint32_t* t, uint32_t a) {
+  return *(const uint32_t*)((const char*)t + a);
+}
+
+/* v_perm_b32 selector putting byte k of the first operand at bits 8..15 and
+ * byte 0 of the second at bits 0..7, zeros above. */
+__device__ inline constexpr uint32_t sel_byte(int k) { return 0x0C0C0000u | ((4u + k) << 8); }
+
+/* Dequantize an 8*B-bit field (8 codes) into 8 fp16 (4 words).  lo: the
+ * lane's offset word (lane * 4). */
 template <int B>
-__device__ inline u32x4 deq8(const uint32_t* lut, uint32_t f) {
+__device__ inline u32x4 deq8(const uint32_t* lut, uint32_t f, uint32_t lo) {
   u32x4 o;
   if constexpr (B == 4) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) o[k] = lut[((f >> (8 * k)) & 0xFFu) * kRep];
+    for (int k = 0; k < 4; ++k) o[k] = lut_at(lut, __builtin_amdgcn_perm(f, lo, sel_byte(k)));
   } else if constexpr (B == 3) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) o[k] = lut[((f >> (6 * k)) & 0x3Fu) * kRep];
+    for (int k = 0; k < 4; ++k) o[k] = lut_at(lut, (((f >> (6 * k)) & 0x3Fu) << 8) | lo);
   } else {
-    const uint2 a = *(const uint2*)(lut + ((f & 0xFFu) * kRep) * 2);
-    const uint2 b = *(const uint2*)(lut + (((f >> 8) & 0xFFu) * kRep) * 2);
-    o[0] = a.x;
-    o[1] = a.y;
-    o[2] = b.x;
-    o[3] = b.y;
+    /* nibbles 0, 2 in bytes 0, 1 of g; nibbles 1, 3 in bytes 0, 1 of h */
+    const uint32_t g = f & 0x0F0Fu, h = (f >> 4) & 0x0F0Fu;
+    o[0] = lut_at(lut, __builtin_amdgcn_perm(g, lo, sel_byte(0)));
+    o[1] = lut_at(lut, __builtin_amdgcn_perm(h, lo, sel_byte(0)));
+    o[2] = lut_at(lut, __builtin_amdgcn_perm(g, lo, sel_byte(1)));
+    o[3] = lut_at(lut, __builtin_amdgcn_perm(h, lo, sel_byte(1)));
   }
   return o;
 }
@@ -122,8 +131,23 @@ __device__ inline void load_words(const uint8_t* p, uint32_t (&w)[(N + 3) / 4]) 
   }
 }
 
+/* v + v of the lane 8 places along in the same row (a single v_add_f32_dpp) */
 __device__ inline float ror8_add(float v) {
-  return v + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xF, 0xF, false));
+  return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, true));
+}
+
+/* max / sum over the four 16-lane rows (lanes n, n+16, n+32, n+48) */
+__device__ inline float rows_max(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ inline float rows_sum(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 __device__ inline float h2f(uint32_t h) { return (float)__builtin_bit_cast(_Float16, (uint16_t)h); }
@@ -160,8 +184,18 @@ struct DecArgs {
   float qscale;    /* log2(e) / (d * sigma_K) */
   float oscale;    /* 1 / (sqrt(d) * sigma_V) */
   float* out;
-  float* ws;
+  void* ws;        /* [units] int32 arrival counters (zero between calls), then records */
+  int64_t ctr_bytes;
 };
+
+/* LDS of one decode block. */
+template <int D, int BK, int BV>
+constexpr size_t decode_lds_bytes() {
+  return (size_t)((Lut<BK>::BYTES + Lut<BV>::BYTES) > kWaves * (8 * D + 16) * 4
+                      ? (Lut<BK>::BYTES + Lut<BV>::BYTES)
+                      : kWaves * (8 * D + 16) * 4) +
+         8 * D * 4;
+}
 
 /* In-LDS Walsh-Hadamard transform of G rows of D floats (block-wide). */
 template <int D>
@@ -179,18 +213,126 @@ __device__ inline void lds_fwht(float* buf, int G) {
   }
 }
 
+/* One 32-token tile's loads for one lane. */
+template <class DG>
+struct TileRegs {
+  uint32_t kw0[DG::KW], kw1[DG::KW], vw[DG::VW];
+  uint2 kn0, kn1, vn0, vn1;
+};
+
+template <class DG>
+__device__ inline void load_tile(TileRegs<DG>& r, const uint8_t* kbase, const uint8_t* vbase,
+                                 const uint16_t* knb, const uint16_t* vnb, int tile, int n) {
+  const int tok0 = tile * 32;
+  load_words<DG::KB, DG::KA>(kbase + (int64_t)(tok0 + n) * DG::RB, r.kw0);
+  load_words<DG::KB, DG::KA>(kbase + (int64_t)(tok0 + 16 + n) * DG::RB, r.kw1);
+  load_words<DG::SEG, DG::VA>(vbase + (int64_t)tile * DG::TILE, r.vw);
+  r.kn0 = *(const uint2*)(knb + tok0);
+  r.kn1 = *(const uint2*)(knb + tok0 + 16);
+  r.vn0 = *(const uint2*)(vnb + tok0);
+  r.vn1 = *(const uint2*)(vnb + tok0 + 16);
+}
+
+/* fp32 x times an fp16 value given by its bits (one mixed-precision FMA). */
+__device__ inline float mul_h(float x, uint32_t h) {
+  return __builtin_fmaf(x, (float)__builtin_bit_cast(_Float16, (uint16_t)h), 0.0f);
+}
+
+/* Score, softmax-update and accumulate one tile.  PARTIAL: some of its tokens
+ * lie at or past len and are masked out. */
+template <class DG, int BK, int BV, bool PARTIAL>
+__device__ inline void tile_step(const TileRegs<DG>& r, const half8 (&bq)[DG::KS],
+                                 const uint32_t* lk, const uint32_t* lv, uint32_t lo,
+                                 floatx4 (&acc)[DG::VM], float& m_run, float& l_run, int tok0,
+                                 int len, int q4) {
+  floatx4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < DG::KS; ++s) {
+    const u32x4 a0 = deq8<BK>(lk, field<BK>(r.kw0, s), lo);
+    s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, a0), bq[s], s0, 0, 0, 0);
+    const u32x4 a1 = deq8<BK>(lk, field<BK>(r.kw1, s), lo);
+    s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, a1), bq[s], s1, 0, 0, 0);
+  }
+  /* tokens tok0 + 4 q4 + u (u < 4) and tok0 + 16 + 4 q4 + u - 4 */
+  const uint32_t knw[4] = {r.kn0.x, r.kn0.y, r.kn1.x, r.kn1.y};
+  const uint32_t vnw[4] = {r.vn0.x, r.vn0.y, r.vn1.x, r.vn1.y};
+  float sc[8];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    sc[i] = ror8_add(s0[i]);
+    sc[4 + i] = ror8_add(s1[i]);
+  }
+  float mt = -1e30f;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const float v = mul_h(sc[u], (knw[u / 2] >> (16 * (u & 1))) & 0xFFFFu);
+    if (PARTIAL) {
+      const int tok = tok0 + (u < 4 ? 4 * q4 + u : 16 + 4 * q4 + (u - 4));
+      sc[u] = tok < len ? v : -INFINITY;
+    } else {
+      sc[u] = v;
+    }
+    mt = fmaxf(mt, sc[u]);
+  }
+  mt = rows_max(mt);
+  const float m_new = fmaxf(m_run, mt);
+  if (__any(m_new > m_run)) { /* rescale the running sums, lazily */
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+    l_run *= alpha;
+#pragma unroll
+    for (int m = 0; m < DG::VM; ++m) acc[m] *= alpha;
+    m_run = m_new;
+  }
+  half8 pb;
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const float p = __builtin_amdgcn_exp2f(sc[u] - m_run);
+    l_run += p;
+    const uint32_t vh = (vnw[u / 2] >> (16 * (u & 1))) & 0xFFFFu;
+    _Float16 pv = (_Float16)mul_h(p, vh);
+    if (PARTIAL) {
+      const int tok = tok0 + (u < 4 ? 4 * q4 + u : 16 + 4 * q4 + (u - 4));
+      pv = tok < len ? pv : (_Float16)0.0f;
+    }
+    pb[u] = pv;
+  }
+  if constexpr (BV == 2) {
+    /* a value word holds two 8-code fields: split its nibbles once */
+#pragma unroll
+    for (int j = 0; j < DG::VW; ++j) {
+      const uint32_t g = r.vw[j] & 0x0F0F0F0Fu, h = (r.vw[j] >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        u32x4 av;
+        av[0] = lut_at(lv, __builtin_amdgcn_perm(g, lo, sel_byte(2 * half)));
+        av[1] = lut_at(lv, __builtin_amdgcn_perm(h, lo, sel_byte(2 * half)));
+        av[2] = lut_at(lv, __builtin_amdgcn_perm(g, lo, sel_byte(2 * half + 1)));
+        av[3] = lut_at(lv, __builtin_amdgcn_perm(h, lo, sel_byte(2 * half + 1)));
+        const int m = 2 * j + half;
+        acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, av), pb, acc[m], 0, 0, 0);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int m = 0; m < DG::VM; ++m) {
+      const u32x4 av = deq8<BV>(lv, field<BV>(r.vw, m), lo);
+      acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, av), pb, acc[m], 0, 0, 0);
+    }
+  }
+}
+
 template <int D, int BK, int BV>
 __global__ void __launch_bounds__(64 * kWaves)
 decode_kernel(DecArgs a) {
   using DG = DecGeo<D, BK, BV>;
-  extern __shared__ __align__(16) char smem[];
-  uint32_t* lut_k = (uint32_t*)smem;
-  uint32_t* lut_v = (uint32_t*)(smem + Lut<BK>::BYTES);
-  const int lut_bytes = Lut<BK>::BYTES + Lut<BV>::BYTES;
-  const int merge_bytes = kWaves * (8 * D + 16) * 4;
-  float* qbuf = (float*)(smem + (lut_bytes > merge_bytes ? lut_bytes : merge_bytes));
+  /* static LDS (addresses known at compile time, so table bases fold into
+   * the ds_read offset field): [V table | K table] during the token loop,
+   * reused as the wave-merge buffer afterwards; then the rotated queries */
+  __shared__ __align__(16) char smem[decode_lds_bytes<D, BK, BV>()];
+  uint32_t* lut_v = (uint32_t*)smem;
+  uint32_t* lut_k = (uint32_t*)(smem + Lut<BV>::BYTES);
+  float* qbuf = (float*)(smem + decode_lds_bytes<D, BK, BV>() - 8 * D * 4);
   float* mbuf = (float*)smem; /* aliases the tables after the token loop */
-
   const int G = a.group;
   const int split = blockIdx.x % a.splits;
   int64_t unit = blockIdx.x / a.splits;
@@ -242,78 +384,36 @@ decode_kernel(DecArgs a) {
                          lane * DG::SEG;
   const uint16_t* knb = (const uint16_t*)(a.k_norms + layer * a.ls_kn) + sh * a.capacity + 4 * q4;
   const uint16_t* vnb = (const uint16_t*)(a.v_norms + layer * a.ls_vn) + sh * a.capacity + 4 * q4;
-  const uint32_t* lk = lut_k + (lane % kRep) * Lut<BK>::WORDS;
-  const uint32_t* lv = lut_v + (lane % kRep) * Lut<BV>::WORDS;
+  const uint32_t lo = (uint32_t)lane << 2;
 
   floatx4 acc[DG::VM];
 #pragma unroll
   for (int m = 0; m < DG::VM; ++m) acc[m] = floatx4{0.f, 0.f, 0.f, 0.f};
   float m_run = -1e30f, l_run = 0.0f;
 
-  for (int tile = t_begin + wave; tile < t_end; tile += kWaves) {
-    const int tok0 = tile * 32;
-    uint32_t kw0[DG::KW], kw1[DG::KW], vw[DG::VW];
-    load_words<DG::KB, DG::KA>(kbase + (int64_t)(tok0 + n) * DG::RB, kw0);
-    load_words<DG::KB, DG::KA>(kbase + (int64_t)(tok0 + 16 + n) * DG::RB, kw1);
-    load_words<DG::SEG, DG::VA>(vbase + (int64_t)tile * DG::TILE, vw);
-    const uint2 kn0 = *(const uint2*)(knb + tok0);
-    const uint2 kn1 = *(const uint2*)(knb + tok0 + 16);
-    const uint2 vn0 = *(const uint2*)(vnb + tok0);
-    const uint2 vn1 = *(const uint2*)(vnb + tok0 + 16);
-
-    floatx4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < DG::KS; ++s) {
-      const u32x4 a0 = deq8<BK>(lk, field<BK>(kw0, s));
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, a0), bq[s], s0, 0, 0, 0);
-      const u32x4 a1 = deq8<BK>(lk, field<BK>(kw1, s));
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, a1), bq[s], s1, 0, 0, 0);
-    }
-    /* scores of tokens tok0 + 4 q4 + i (block 0) and tok0 + 16 + 4 q4 + i */
-    float sc[8];
-    const uint32_t knw[4] = {kn0.x, kn0.y, kn1.x, kn1.y};
-    const uint32_t vnw[4] = {vn0.x, vn0.y, vn1.x, vn1.y};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      sc[i] = ror8_add(s0[i]);
-      sc[4 + i] = ror8_add(s1[i]);
-    }
-    float mt = -1e30f;
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int tok = tok0 + (u < 4 ? 4 * q4 + u : 16 + 4 * q4 + (u - 4));
-      const uint32_t kh = (knw[u / 2] >> (16 * (u & 1))) & 0xFFFFu;
-      const float v = sc[u] * h2f(kh);
-      sc[u] = tok < len ? v : -INFINITY;
-      mt = fmaxf(mt, sc[u]);
-    }
-    mt = fmaxf(mt, __shfl_xor(mt, 16));
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float m_new = fmaxf(m_run, mt);
-    if (__any(m_new > m_run)) { /* rescale the running sums, lazily */
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run *= alpha;
-#pragma unroll
-      for (int m = 0; m < DG::VM; ++m) acc[m] *= alpha;
-      m_run = m_new;
-    }
-    half8 pb;
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const float p = __builtin_amdgcn_exp2f(sc[u] - m_run);
-      l_run += p;
-      const uint32_t vh = (vnw[u / 2] >> (16 * (u & 1))) & 0xFFFFu;
-      const int tok = tok0 + (u < 4 ? 4 * q4 + u : 16 + 4 * q4 + (u - 4));
-      pb[u] = tok < len ? (_Float16)(p * h2f(vh)) : (_Float16)0.0f;
-    }
-#pragma unroll
-    for (int m = 0; m < DG::VM; ++m) {
-      const u32x4 av = deq8<BV>(lv, field<BV>(vw, m));
-      acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, av), pb, acc[m], 0, 0, 0);
-    }
+  /* software pipeline: the next tile's loads are in flight while this one is
+   * scored and accumulated */
+  /* full tiles, software-pipelined: the next tile's loads are in flight
+   * while this one is scored and accumulated */
+  const int full_end = (len / 32) < t_end ? (len / 32) : t_end;
+  TileRegs<DG> ra, rb; /* ping-pong: no register copies between tiles */
+  int tile = t_begin + wave;
+  if (tile < full_end) load_tile<DG>(ra, kbase, vbase, knb, vnb, tile, n);
+  while (tile < full_end) {
+    if (tile + kWaves < full_end) load_tile<DG>(rb, kbase, vbase, knb, vnb, tile + kWaves, n);
+    tile_step<DG, BK, BV, false>(ra, bq, lut_k, lut_v, lo, acc, m_run, l_run, tile * 32, len, q4);
+    tile += kWaves;
+    if (tile >= full_end) break;
+    if (tile + kWaves < full_end) load_tile<DG>(ra, kbase, vbase, knb, vnb, tile + kWaves, n);
+    tile_step<DG, BK, BV, false>(rb, bq, lut_k, lut_v, lo, acc, m_run, l_run, tile * 32, len, q4);
+    tile += kWaves;
   }
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
+  /* the ragged last tile, if this wave owns it */
+  if (tile < t_end) {
+    load_tile<DG>(ra, kbase, vbase, knb, vnb, tile, n);
+    tile_step<DG, BK, BV, true>(ra, bq, lut_k, lut_v, lo, acc, m_run, l_run, tile * 32, len, q4);
+  }
+  l_run = rows_sum(l_run);
 
   /* merge the waves: mbuf[w] = {m[8], l[8], acc[8][D]} */
   __syncthreads(); /* tables are dead from here on */
@@ -366,84 +466,126 @@ decode_kernel(DecArgs a) {
       a.out[head0 * D + t] = v;
     }
   } else {
-    /* partial record per (head, split): {m, l, acc[D]} */
+    /* partial record per (head, split): {m, l, acc[D]}, after the counters */
+    const int64_t uid = blockIdx.x / a.splits;
+    float* recs = (float*)((char*)a.ws + a.ctr_bytes);
     for (int t = threadIdx.x; t < G * (D + 2); t += blockDim.x) {
       const int g = t / (D + 2), k = t % (D + 2);
-      float* rec = a.ws + ((head0 + g) * a.splits + split) * (D + 2);
+      float* rec = recs + ((head0 + g) * a.splits + split) * (D + 2);
       rec[k] = k == 0 ? mg[g] : (k == 1 ? lg[g] : res[g * D + (k - 2)]);
     }
-  }
-}
-
-/* Merge the split records of one head and rotate back: one block per head. */
-template <int D>
-__global__ void __launch_bounds__(256)
-combine_kernel(const float* __restrict__ ws, int splits, const uint8_t* __restrict__ sign_bits,
-               int heads_per_layer, float oscale, float* __restrict__ out) {
-  __shared__ float buf[D];
-  __shared__ float ML[2];
-  const int64_t head = blockIdx.x;
-  const int layer = (int)(head / heads_per_layer);
-  const float* rec = ws + head * splits * (D + 2);
-  if (threadIdx.x == 0) {
-    float M = -1e30f;
-    for (int s = 0; s < splits; ++s) M = fmaxf(M, rec[s * (D + 2)]);
-    float L = 0.0f;
-    for (int s = 0; s < splits; ++s)
-      L += __builtin_amdgcn_exp2f(rec[s * (D + 2)] - M) * rec[s * (D + 2) + 1];
-    ML[0] = M;
-    ML[1] = L;
-  }
-  __syncthreads();
-  for (int i = threadIdx.x; i < D; i += blockDim.x) {
-    float acc = 0.0f;
-    for (int s = 0; s < splits; ++s)
-      acc += __builtin_amdgcn_exp2f(rec[s * (D + 2)] - ML[0]) * rec[s * (D + 2) + 2 + i];
-    buf[i] = acc;
-  }
-  __syncthreads();
-  lds_fwht<D>(buf, 1);
-  const uint8_t* sb = sign_bits + (int64_t)layer * (D / 8);
-  for (int i = threadIdx.x; i < D; i += blockDim.x) {
-    float v = ML[1] > 0.0f ? buf[i] * oscale / ML[1] : 0.0f;
-    if ((sb[i >> 3] >> (i & 7)) & 1) v = -v;
-    out[head * D + i] = v;
+    /* the last split of the unit to finish merges all of them */
+    __threadfence();
+    __syncthreads();
+    __shared__ int last;
+    if (threadIdx.x == 0) {
+      int* ctr = (int*)a.ws + uid;
+      const int ticket = atomicAdd(ctr, 1);
+      last = ticket == a.splits - 1;
+      if (last) *ctr = 0; /* every split has arrived: ready for the next call */
+    }
+    __syncthreads();
+    if (!last) return;
+    __threadfence();
+    if (threadIdx.x < G) {
+      const int g = threadIdx.x;
+      const float* r = recs + (head0 + g) * a.splits * (D + 2);
+      float M = -1e30f;
+      for (int sp = 0; sp < a.splits; ++sp) M = fmaxf(M, r[sp * (D + 2)]);
+      float L = 0.0f;
+      for (int sp = 0; sp < a.splits; ++sp)
+        L += __builtin_amdgcn_exp2f(r[sp * (D + 2)] - M) * r[sp * (D + 2) + 1];
+      mg[g] = M;
+      lg[g] = L;
+    }
+    __syncthreads();
+    for (int t = threadIdx.x; t < G * D; t += blockDim.x) {
+      const int g = t / D, i = t % D;
+      const float* r = recs + (head0 + g) * a.splits * (D + 2);
+      float s = 0.0f;
+      for (int sp = 0; sp < a.splits; ++sp)
+        s += __builtin_amdgcn_exp2f(r[sp * (D + 2)] - mg[g]) * r[sp * (D + 2) + 2 + i];
+      res[t] = s;
+    }
+    __syncthreads();
+    lds_fwht<D>(res, G);
+    for (int t = threadIdx.x; t < G * D; t += blockDim.x) {
+      const int g = t / D, i = t % D;
+      const float L = lg[g];
+      float v = L > 0.0f ? res[t] * a.oscale / L : 0.0f;
+      if ((sb[i >> 3] >> (i & 7)) & 1) v = -v;
+      a.out[head0 * D + t] = v;
+    }
   }
 }
 
 template <int D, int BK, int BV>
 tq_status launch_decode_t(const DecArgs& a, hipStream_t s) {
-  const int lut_bytes = Lut<BK>::BYTES + Lut<BV>::BYTES;
-  const int merge_bytes = kWaves * (8 * D + 16) * 4;
-  const size_t lds = (size_t)(lut_bytes > merge_bytes ? lut_bytes : merge_bytes) + 8 * D * 4;
   const int64_t blocks = (int64_t)a.n_layers * a.batch * a.kv_heads * a.splits;
-  hipLaunchKernelGGL((decode_kernel<D, BK, BV>), dim3((unsigned)blocks), dim3(64 * kWaves), lds, s,
+  hipLaunchKernelGGL((decode_kernel<D, BK, BV>), dim3((unsigned)blocks), dim3(64 * kWaves), 0, s,
                      a);
-  if (hipGetLastError() != hipSuccess) return TQ_ERR_DEVICE;
-  if (a.splits > 1) {
-    const int64_t heads = (int64_t)a.n_layers * a.batch * a.q_heads;
-    hipLaunchKernelGGL((combine_kernel<D>), dim3((unsigned)heads), dim3(256), 0, s, a.ws,
-                       a.splits, a.sign_bits, a.batch * a.q_heads, a.oscale, a.out);
-    if (hipGetLastError() != hipSuccess) return TQ_ERR_DEVICE;
-  }
-  return TQ_OK;
+  return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_DEVICE;
 }
 
 }  // namespace
 
+/* Blocks of this instantiation the device runs at once (occupancy x CUs);
+ * looked up once per process, with a fallback when no device answers. */
+template <int D, int BK, int BV>
+int concurrent_blocks_t() {
+  static int cached = 0;
+  if (cached == 0) {
+    int dev = 0, cus = 0, per = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, decode_kernel<D, BK, BV>, 64 * kWaves,
+                                                     0) != hipSuccess ||
+        cus <= 0 || per <= 0) {
+      (void)hipGetLastError();
+      return 256 * 2;
+    }
+    cached = cus * per;
+  }
+  return cached;
+}
+
+static int concurrent_blocks(int d, int bk, int bv) {
+#define TQ_OCC(DD, KK, VV) \
+  if (d == DD && bk == KK && bv == VV) return concurrent_blocks_t<DD, KK, VV>();
+#define TQ_OCC_D(DD) \
+  TQ_OCC(DD, 2, 2) TQ_OCC(DD, 2, 3) TQ_OCC(DD, 2, 4) TQ_OCC(DD, 3, 2) TQ_OCC(DD, 3, 3) \
+  TQ_OCC(DD, 3, 4) TQ_OCC(DD, 4, 2) TQ_OCC(DD, 4, 3) TQ_OCC(DD, 4, 4)
+  TQ_OCC_D(64) TQ_OCC_D(128) TQ_OCC_D(256)
+#undef TQ_OCC_D
+#undef TQ_OCC
+  return 512;
+}
+
+/* Split count: the smallest that keeps the last round of blocks at least 90%
+ * full (blocks / (rounds * concurrent)), else the best one found, with every
+ * wave keeping at least two tiles. */
 tq_decode_plan tq_plan_decode(const tq_kv_cache* c, int q_heads, int max_len, int n_layers) {
   tq_decode_plan p;
   const int64_t units = (int64_t)n_layers * c->batch * c->kv_heads;
   const int tiles = (max_len + 31) / 32;
-  const int64_t target_blocks = 1024;
-  int splits = (int)((target_blocks + units - 1) / units);
-  const int max_splits = tiles / (4 * kWaves);
-  if (splits > max_splits) splits = max_splits;
-  if (splits < 1) splits = 1;
+  const int64_t conc = concurrent_blocks(c->head_dim, c->bits_k, c->bits_v);
+  int max_splits = tiles / (2 * kWaves);
+  if (max_splits > 64) max_splits = 64;
+  if (max_splits < 1) max_splits = 1;
+  int splits = 1;
+  double best = -1.0;
+  for (int sp = 1; sp <= max_splits; ++sp) {
+    const int64_t blocks = units * sp;
+    const int64_t rounds = (blocks + conc - 1) / conc;
+    const double eff = (double)blocks / (double)(rounds * conc);
+    if (eff > best + 1e-9) { best = eff; splits = sp; }
+    if (eff >= 0.9) break;
+  }
   p.splits = splits;
   p.tiles_per_split = tiles > 0 ? (tiles + splits - 1) / splits : 0;
-  p.ws_bytes = splits > 1 ? (size_t)n_layers * c->batch * q_heads * splits *
-                                (c->head_dim + 2) * sizeof(float)
+  p.ctr_bytes = ((size_t)units * sizeof(int) + 255) & ~(size_t)255;
+  p.ws_bytes = splits > 1 ? p.ctr_bytes + (size_t)n_layers * c->batch * q_heads * splits *
+                                              (c->head_dim + 2) * sizeof(float)
                           : 0;
   return p;
 }
@@ -480,7 +622,8 @@ tq_status tq_launch_decode(const tq_kv_cache* c, const tq_codebook_s* cbk,
   a.qscale = (float)(1.4426950408889634 / (d * cbk->sigma));
   a.oscale = (float)(1.0 / (sqrt(d) * cbv->sigma));
   a.out = out;
-  a.ws = (float*)ws;
+  a.ws = ws;
+  a.ctr_bytes = (int64_t)plan.ctr_bytes;
 #define TQ_DEC(DD, KK, VV) \
   if (c->head_dim == DD && c->bits_k == KK && c->bits_v == VV) return launch_decode_t<DD, KK, VV>(a, s);
 #define TQ_DEC_D(DD) \

@@ -176,18 +176,13 @@ extern "C" tq_status tq_codebook_init(int head_dim, int bits, tq_codebook* out) 
     uint16_t m = half_rne_normal(fabs(v));
     h[k] = (uint16_t)(v < 0 ? (m | 0x8000) : m);
   }
-  size_t lut_words = bits == 2 ? 512 : (bits == 3 ? 64 : 256);
+  /* one word per entry: the fp16 levels of two codes (first code in the low
+   * half); the entry index is a byte (bits 4), 6 bits (bits 3) or a nibble
+   * (bits 2) holding the two codes */
+  size_t lut_words = bits == 2 ? 16 : (bits == 3 ? 64 : 256);
   uint32_t* lut = (uint32_t*)calloc(lut_words, 4);
-  if (bits == 4) {
-    for (int b = 0; b < 256; ++b) lut[b] = h[b & 15] | ((uint32_t)h[b >> 4] << 16);
-  } else if (bits == 3) {
-    for (int v = 0; v < 64; ++v) lut[v] = h[v & 7] | ((uint32_t)h[v >> 3] << 16);
-  } else {
-    for (int b = 0; b < 256; ++b) {
-      lut[2 * b] = h[b & 3] | ((uint32_t)h[(b >> 2) & 3] << 16);
-      lut[2 * b + 1] = h[(b >> 4) & 3] | ((uint32_t)h[b >> 6] << 16);
-    }
-  }
+  for (size_t e = 0; e < lut_words; ++e)
+    lut[e] = h[e & (L - 1)] | ((uint32_t)h[e >> bits] << 16);
   size_t enc_bytes = ((size_t)ne * sizeof(tq_enc_entry) + 255) & ~(size_t)255;
   size_t total = enc_bytes + lut_words * 4;
   tq_status st = TQ_OK;

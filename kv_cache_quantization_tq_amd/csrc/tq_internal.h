@@ -32,7 +32,7 @@ struct tq_codebook_s {
   int device;
   void* dev_mem;         /* one device allocation: encoder table, then decoder table */
   const tq_enc_entry* enc_table;
-  const uint32_t* dec_lut; /* bits 2: 256 x 2 words; bits 3: 64 words; bits 4: 256 words */
+  const uint32_t* dec_lut; /* one word (two fp16 levels) per pair of codes: 2^(2*bits) words */
 };
 
 /* Host-side Lloyd-Max (levels / thresholds in fp64, N(0, 1/d)). */
@@ -52,7 +52,8 @@ tq_status tq_launch_append(const tq_kv_cache* c, const tq_codebook_s* cbk,
 struct tq_decode_plan {
   int splits;          /* token splits per (layer, seq, kv head) */
   int tiles_per_split; /* 32-token tiles per split */
-  size_t ws_bytes;     /* partial (m, l, acc[d]) records; 0 when splits == 1 */
+  size_t ctr_bytes;    /* per-unit arrival counters, 256-byte padded */
+  size_t ws_bytes;     /* counters + (m, l, acc[d]) records; 0 when splits == 1 */
 };
 tq_decode_plan tq_plan_decode(const tq_kv_cache* c, int q_heads, int max_len, int n_layers);
 

@@ -96,7 +96,7 @@ def test_workspace_planning():
     s = _fake_cache(capacity=32768)
     # one layer, 8 KV heads, 32K tokens: several splits -> records of (d + 2) floats
     nb = L.tq_decode_workspace_bytes(ctypes.byref(s), 32, 32768, 1)
-    assert nb > 0 and nb % (32 * 130 * 4) == 0
+    assert nb > 0 and (nb - 256) % (32 * 130 * 4) == 0
     # many units -> one split, no workspace
     s.batch = 64
     assert L.tq_decode_workspace_bytes(ctypes.byref(s), 32, 8192, 32) == 0
