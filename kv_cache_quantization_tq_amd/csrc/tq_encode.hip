@@ -8,14 +8,15 @@
  *   y_i = h_i / (sqrt(d) n)            rotated unit vector, ~N(0, 1/d)
  *   code_i = #{k : t_k < y_i}          Lloyd-Max thresholds t_k
  *
- * Work layout: 64 coordinates per lane, d/64 lanes per vector, 64/(d/64)
+ * Work layout: 32 coordinates per lane, d/32 lanes per vector, 2048/d
  * vectors per wave pass.  A pass reads its vectors with fully coalesced
- * 128-bit loads into a padded LDS stage, then each lane reads back its own
- * 128 bytes.  The sign flip D is an XOR on the fp16 sign bits during staging.
- * The FWHT runs its first six stages inside the lane's registers and the rest
- * across the lanes of a vector with DPP quad permutes.
+ * 128-bit loads, XORs the sign flip D into the fp16 sign bits and writes them
+ * to a padded LDS stage, from which each lane reads back its own 64 bytes; the
+ * next pass's loads are issued before this pass is computed.  The FWHT runs
+ * five stages inside the lane's registers and the rest across the lanes of a
+ * vector (DPP quad permutes, ds_swizzle for the eighth-lane stage).
  *
- * Norm: sum of exact fp32 squares (8 chains of 8, then a tree), ~13 roundings,
+ * Norm: sum of exact fp32 squares (4 chains of 8, then a tree), <= 13 roundings,
  * so |S32 - S| <= 13 * 2^-24 S.  The fp16 candidate is accepted when S32 is
  * far enough from both rounding midpoints; otherwise the vector's fp16 inputs
  * are re-summed in fp64 and, if still ambiguous, exactly in 128-bit integers.
@@ -31,8 +32,11 @@
 
 namespace {
 
-constexpr int kStagePitch = 144; /* LDS bytes per lane's 128-byte chunk, padded */
-constexpr int kEncRep = 4;       /* copies of the bucket table (lane % kEncRep) */
+#ifndef TQ_ENC_WPE
+#define TQ_ENC_WPE 3 /* registers for at least this many waves per SIMD */
+#endif
+constexpr int kPitch = 80;   /* LDS bytes per lane's 64-byte chunk, padded */
+constexpr int kEncRep = 16;  /* copies of the bucket table (lane % 16): conflict-free 64-bit reads */
 
 __device__ inline void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -40,13 +44,17 @@ __device__ inline void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-/* DPP quad permutes: xor 1 = [1,0,3,2], xor 2 = [2,3,0,1]. */
-template <int CTRL>
-__device__ inline float dpp_f(float v) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+/* Butterfly partners: DPP quad permutes for lane xor 1 and xor 2, ds_swizzle
+ * (bit mode) for lane xor 4. */
+__device__ inline float xor1(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, true));
 }
-constexpr int kQuadXor1 = 0xB1;
-constexpr int kQuadXor2 = 0x4E;
+__device__ inline float xor2(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, true));
+}
+__device__ inline float xor4(float v) {
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), (4 << 10) | 0x1F));
+}
 
 __device__ inline float half_lo(uint32_t w) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xFFFFu));
@@ -60,9 +68,9 @@ __device__ inline float half_bits_to_float(uint32_t h) {
 
 template <int D>
 struct Geo {
-  static constexpr int LPV = D / 64;       /* lanes per vector */
-  static constexpr int VPW = 64 / LPV;     /* vectors per wave pass */
-  static constexpr int CPR = D / 8;        /* 16-byte chunks per vector */
+  static constexpr int LPV = D / 32;   /* lanes per vector */
+  static constexpr int VPW = 64 / LPV; /* vectors per wave pass */
+  static constexpr int CPR = D / 8;    /* 16-byte chunks per vector */
 };
 
 /* Per-lane XOR masks for the sign flip: every staging load of this lane
@@ -70,31 +78,43 @@ struct Geo {
 template <int D>
 __device__ inline void sign_masks(const uint8_t* sign_bits, int lane, uint32_t (&m)[4]) {
   const int ch = lane % Geo<D>::CPR;
-  uint32_t b = sign_bits[ch];
+  const uint32_t b = sign_bits[ch];
 #pragma unroll
   for (int j = 0; j < 4; ++j)
     m[j] = (((b >> (2 * j)) & 1u) << 15) | (((b >> (2 * j + 1)) & 1u) << 31);
 }
 
-/* Coalesced load of vectors v in [vlo, vhi) of a pass (vector v at
- * base + v * stride elements) into the wave's LDS stage, sign-flipped.
- * Vectors outside the range are staged as zeros. */
+/* Global loads of one pass: vectors v in [vlo, vhi) at base + v * stride
+ * elements; chunk c = 64 k + lane.  Vectors outside the range read as zero. */
 template <int D>
-__device__ inline void stage_pass(const uint16_t* base, int64_t stride, int vlo, int vhi,
-                                  const uint32_t (&sm)[4], char* stage, int lane) {
+__device__ inline void pass_load(const uint16_t* base, int64_t stride, int vlo, int vhi,
+                                 uint4 (&g)[4], int lane) {
   using G = Geo<D>;
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
+  for (int k = 0; k < 4; ++k) {
     const int c = 64 * k + lane;
     const int v = c / G::CPR, ch = c % G::CPR;
-    uint4 val = make_uint4(0u, 0u, 0u, 0u);
-    if (v >= vlo && v < vhi) val = *(const uint4*)(base + (int64_t)v * stride + ch * 8);
+    g[k] = make_uint4(0u, 0u, 0u, 0u);
+    if (v >= vlo && v < vhi) g[k] = *(const uint4*)(base + (int64_t)v * stride + ch * 8);
+  }
+}
+
+/* Sign-flip the loaded chunks and put them in the wave's stage: lane
+ * owner = v * LPV + ch / 4 receives chunk ch at (ch % 4) * 16. */
+template <int D>
+__device__ inline void pass_stage(const uint4 (&g)[4], const uint32_t (&sm)[4], char* stage,
+                                  int lane) {
+  using G = Geo<D>;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int c = 64 * k + lane;
+    const int v = c / G::CPR, ch = c % G::CPR;
+    uint4 val = g[k];
     val.x ^= sm[0];
     val.y ^= sm[1];
     val.z ^= sm[2];
     val.w ^= sm[3];
-    const int owner = v * G::LPV + ch / 8;
-    *(uint4*)(stage + owner * kStagePitch + (ch % 8) * 16) = val;
+    *(uint4*)(stage + (v * G::LPV + ch / 4) * kPitch + (ch % 4) * 16) = val;
   }
 }
 
@@ -179,65 +199,87 @@ __device__ inline uint32_t norm16_exact(unsigned __int128 S, uint32_t p) {
   return p;
 }
 
-/* Slow norm of vector v of the pass from the LDS stage (every lane of the
- * vector reads all of it).  Signs were flipped during staging; squares do not
- * care. */
+/* Exact fp16 norm of vector v of the pass from the LDS stage, by 128-bit
+ * integer sums; reached only when even the fp64 sum sits within 1e-13 of a
+ * rounding midpoint (exact ties).  Kept out of line: it needs registers the
+ * hot path should not reserve.  Signs were flipped during staging; squares
+ * do not care. */
 template <int D>
-__device__ __attribute__((noinline)) uint32_t norm16_slow(const char* stage, int v) {
+__device__ __attribute__((noinline)) uint32_t norm16_exact_stage(const char* stage, int v,
+                                                                 uint32_t guess) {
   using G = Geo<D>;
-  double S = 0.0;
-  for (int p = 0; p < G::LPV; ++p)
-    for (int j = 0; j < 32; ++j) {
-      uint32_t w = *(const uint32_t*)(stage + (v * G::LPV + p) * kStagePitch + 4 * j);
-      double a = (double)half_lo(w), b = (double)half_hi(w);
-      S += a * a;
-      S += b * b;
-    }
-  uint32_t n16;
-  if (norm16_check_f64(S, &n16)) return n16;
   unsigned __int128 E = 0;
   for (int p = 0; p < G::LPV; ++p)
-    for (int j = 0; j < 32; ++j) {
-      uint32_t w = *(const uint32_t*)(stage + (v * G::LPV + p) * kStagePitch + 4 * j);
-      unsigned __int128 a = half_units(w & 0x7FFFu), b = half_units((w >> 16) & 0x7FFFu);
+    for (int j = 0; j < 16; ++j) {
+      const uint32_t w = *(const uint32_t*)(stage + (v * G::LPV + p) * kPitch + 4 * j);
+      const unsigned __int128 a = half_units(w & 0x7FFFu), b = half_units((w >> 16) & 0x7FFFu);
       E += a * a + b * b;
     }
-  return norm16_exact(E, n16);
+  return norm16_exact(E, guess);
 }
 
-/* Encode the lane's 64 coordinates of one vector of a pass whose data sits
- * in the LDS stage.  Returns the packed codes (64*BITS/32 words) and the
- * vector's fp16 norm (the same on all lanes of the vector). */
+/* fp64 re-sum of vector v from the stage (rare), then the exact fallback. */
+template <int D>
+__device__ inline uint32_t norm16_slow(const char* stage, int v) {
+  using G = Geo<D>;
+  double S = 0.0;
+#pragma unroll 1
+  for (int k = 0; k < 16 * G::LPV; ++k) {
+    const uint32_t w = *(const uint32_t*)(stage + (v * G::LPV + k / 16) * kPitch + 4 * (k % 16));
+    const double a = (double)half_lo(w), b = (double)half_hi(w);
+    S = __builtin_fma(a, a, S);
+    S = __builtin_fma(b, b, S);
+  }
+  uint32_t n16;
+  if (norm16_check_f64(S, &n16)) return n16;
+  return norm16_exact_stage<D>(stage, v, n16);
+}
+
+/* a + b and a - b of the two fp16 halves of w, in fp32 (one mixed-precision
+ * FMA each: a * 1 + (+-b)). */
+__device__ inline void half_pair_sum_diff(uint32_t w, float* sum, float* diff) {
+  float s, d;
+  asm("v_fma_mix_f32 %0, %1, 1.0, %1 op_sel:[0,0,1] op_sel_hi:[1,0,1]" : "=v"(s) : "v"(w));
+  asm("v_fma_mix_f32 %0, %1, 1.0, -%1 op_sel:[0,0,1] op_sel_hi:[1,0,1]" : "=v"(d) : "v"(w));
+  *sum = s;
+  *diff = d;
+}
+
+/* Encode the lane's 32 coordinates of its vector (data in the LDS stage).
+ * Returns the packed codes (BITS words) and the vector's fp16 norm, the same
+ * on all lanes of the vector.
+ *
+ * Cross-lane butterflies: each lane computes own + c * partner with
+ * c = -1 on the lane whose index bit is set, one DPP-fused FMA per value; the
+ * upper lane then holds the negated a - b, so lane values carry the sign
+ * (-1)^popcount(lane bits), folded into the quantizer scale. */
 template <int D, int BITS>
 __device__ inline void encode_lane(const char* stage, const tq_enc_entry* table, float nbh,
-                                   int lane, uint32_t (&packed)[2 * BITS], uint32_t* n16_out) {
+                                   int lane, uint32_t (&packed)[BITS], uint32_t* n16_out,
+                                   bool* sure_out) {
   using G = Geo<D>;
-  uint32_t w[32];
+  uint32_t w[16];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    uint4 t = *(const uint4*)(stage + lane * kStagePitch + 16 * j);
+  for (int j = 0; j < 4; ++j) {
+    const uint4 t = *(const uint4*)(stage + lane * kPitch + 16 * j);
     w[4 * j] = t.x;
     w[4 * j + 1] = t.y;
     w[4 * j + 2] = t.z;
     w[4 * j + 3] = t.w;
   }
-  float v[64];
-  float sq[8];
+  float v[32];
+  float sq[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-  for (int k = 0; k < 8; ++k) sq[k] = 0.0f;
-  /* first butterfly stage straight from fp16; squares from the same values */
-#pragma unroll
-  for (int j = 0; j < 32; ++j) {
+  for (int j = 0; j < 16; ++j) {
+    half_pair_sum_diff(w[j], &v[2 * j], &v[2 * j + 1]);
     const float a = half_lo(w[j]), b = half_hi(w[j]);
-    v[2 * j] = a + b;
-    v[2 * j + 1] = a - b;
-    sq[j & 7] = __builtin_fmaf(a, a, sq[j & 7]);
-    sq[j & 7] = __builtin_fmaf(b, b, sq[j & 7]);
+    sq[j & 3] = __builtin_fmaf(a, a, sq[j & 3]);
+    sq[j & 3] = __builtin_fmaf(b, b, sq[j & 3]);
   }
 #pragma unroll
-  for (int h = 2; h < 64; h <<= 1) {
+  for (int h = 2; h < 32; h <<= 1) {
 #pragma unroll
-    for (int i = 0; i < 64; ++i) {
+    for (int i = 0; i < 32; ++i) {
       if (!(i & h)) {
         const float a = v[i], b = v[i + h];
         v[i] = a + b;
@@ -245,39 +287,60 @@ __device__ inline void encode_lane(const char* stage, const tq_enc_entry* table,
       }
     }
   }
-  float S = ((sq[0] + sq[1]) + (sq[2] + sq[3])) + ((sq[4] + sq[5]) + (sq[6] + sq[7]));
+  float S = (sq[0] + sq[1]) + (sq[2] + sq[3]);
+  float sigma = 1.0f;
   if constexpr (G::LPV >= 2) {
-    const float sg = (lane & 1) ? -1.0f : 1.0f;
+    const float c = (lane & 1) ? -1.0f : 1.0f;
 #pragma unroll
-    for (int i = 0; i < 64; ++i) v[i] = __builtin_fmaf(sg, v[i], dpp_f<kQuadXor1>(v[i]));
-    S += dpp_f<kQuadXor1>(S);
+    for (int i = 0; i < 32; ++i) v[i] = __builtin_fmaf(xor1(v[i]), c, v[i]);
+    S += xor1(S);
+    sigma *= c;
   }
   if constexpr (G::LPV >= 4) {
-    const float sg = (lane & 2) ? -1.0f : 1.0f;
+    const float c = (lane & 2) ? -1.0f : 1.0f;
 #pragma unroll
-    for (int i = 0; i < 64; ++i) v[i] = __builtin_fmaf(sg, v[i], dpp_f<kQuadXor2>(v[i]));
-    S += dpp_f<kQuadXor2>(S);
+    for (int i = 0; i < 32; ++i) v[i] = __builtin_fmaf(xor2(v[i]), c, v[i]);
+    S += xor2(S);
+    sigma *= c;
+  }
+  if constexpr (G::LPV >= 8) {
+    const float c = (lane & 4) ? -1.0f : 1.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) v[i] = __builtin_fmaf(xor4(v[i]), c, v[i]);
+    S += xor4(S);
+    sigma *= c;
   }
   uint32_t n16;
-  if (!norm16_check_f32(S, &n16)) n16 = norm16_slow<D>(stage, lane / G::LPV);
-  *n16_out = n16;
+  const bool sure = norm16_check_f32(S, &n16);
 
-  /* u = (y + 1) * nbh with y = h / (sqrt(d) * ||x||) */
-  const float scale = S > 0.0f ? nbh * __builtin_amdgcn_rsqf(S * (float)D) : 0.0f;
-  const float off = nbh + 1.0f; /* bucket 0 stays unused, so u > 0 */
-  const tq_enc_entry* tab = table + (lane % kEncRep);
+  /* u = (y + 1) * nbh + 1 with y = h / (sqrt(d) * ||x||); bucket floor(u) */
+  const float scale = S > 0.0f ? sigma * nbh * __builtin_amdgcn_rsqf(S * (float)D) : 0.0f;
+  const float off = nbh + 1.0f;
+  const char* tab = (const char*)table + (lane & (kEncRep - 1)) * sizeof(tq_enc_entry);
 #pragma unroll
-  for (int k = 0; k < 2 * BITS; ++k) packed[k] = 0u;
+  for (int k = 0; k < BITS; ++k) packed[k] = 0u;
 #pragma unroll
-  for (int i = 0; i < 64; ++i) {
+  for (int i = 0; i < 32; ++i) {
+    /* bound how far the scheduler hoists table reads (registers) */
+    if (i % 8 == 0) __builtin_amdgcn_sched_barrier(0);
     const float u = __builtin_fmaf(v[i], scale, off);
     const uint32_t b = (uint32_t)u;
-    const tq_enc_entry e = tab[b * kEncRep];
+    const tq_enc_entry e = *(const tq_enc_entry*)(tab + b * (kEncRep * sizeof(tq_enc_entry)));
     const uint32_t code = e.base + (u > e.thr ? 1u : 0u);
     const int bit = BITS * i;
     packed[bit / 32] |= code << (bit % 32);
     if ((bit % 32) + BITS > 32) packed[bit / 32 + 1] |= code >> (32 - bit % 32);
   }
+  *n16_out = n16;
+  *sure_out = sure;
+}
+
+/* The vector's fp16 norm once its codes are stored (the codes do not depend
+ * on it): the rare undecided candidates are settled here, where the
+ * coordinates are no longer live. */
+template <int D>
+__device__ inline uint32_t settle_norm(const char* stage, int lane, uint32_t n16, bool sure) {
+  return sure ? n16 : norm16_slow<D>(stage, lane / Geo<D>::LPV);
 }
 
 /* Copy the bucket table into LDS, kEncRep interleaved copies. */
@@ -285,26 +348,32 @@ __device__ inline void load_table(tq_enc_entry* dst, const tq_enc_entry* src, in
   for (int i = threadIdx.x; i < entries * kEncRep; i += blockDim.x) dst[i] = src[i / kEncRep];
 }
 
-/* Store a lane's packed codes at byte address dst (8-byte aligned). */
+/* Store a lane's 4*BITS bytes of codes at dst (4-byte aligned; 8 for BITS 2,
+ * 16 for BITS 4). */
 template <int BITS>
-__device__ inline void store_packed(uint8_t* dst, const uint32_t (&p)[2 * BITS]) {
+__device__ inline void store_packed(uint8_t* dst, const uint32_t (&p)[BITS]) {
   if constexpr (BITS == 4) {
     *(uint4*)dst = make_uint4(p[0], p[1], p[2], p[3]);
-    *(uint4*)(dst + 16) = make_uint4(p[4], p[5], p[6], p[7]);
   } else if constexpr (BITS == 2) {
-    *(uint4*)dst = make_uint4(p[0], p[1], p[2], p[3]);
-  } else {
     *(uint2*)dst = make_uint2(p[0], p[1]);
-    *(uint2*)(dst + 8) = make_uint2(p[2], p[3]);
-    *(uint2*)(dst + 16) = make_uint2(p[4], p[5]);
+  } else {
+    uint32_t* d = (uint32_t*)dst;
+    d[0] = p[0];
+    d[1] = p[1];
+    d[2] = p[2];
   }
+}
+
+__host__ __device__ inline int table_bytes(int entries) {
+  return (entries * kEncRep * (int)sizeof(tq_enc_entry) + 15) & ~15;
 }
 
 constexpr int kRowsWaves = 4;
 
-/* tq_encode: n vectors, row layout.  Waves take passes grid-stride. */
+/* tq_encode: n vectors, row layout.  Each wave takes passes grid-stride and
+ * loads the next pass while it encodes the current one. */
 template <int D, int BITS>
-__global__ void __launch_bounds__(64 * kRowsWaves)
+__global__ void __launch_bounds__(64 * kRowsWaves) __attribute__((amdgpu_waves_per_eu(TQ_ENC_WPE)))
 encode_rows_kernel(const uint16_t* __restrict__ x, int64_t n, int64_t stride,
                    const uint8_t* __restrict__ sign_bits, const tq_enc_entry* __restrict__ table,
                    int entries, float nbh, uint8_t* __restrict__ codes,
@@ -312,29 +381,37 @@ encode_rows_kernel(const uint16_t* __restrict__ x, int64_t n, int64_t stride,
   using G = Geo<D>;
   extern __shared__ __align__(16) char smem[];
   tq_enc_entry* tab = (tq_enc_entry*)smem;
-  char* stage = smem + ((entries * kEncRep * (int)sizeof(tq_enc_entry) + 15) & ~15) +
-                (threadIdx.x / 64) * 64 * kStagePitch;
+  const int lane = threadIdx.x % 64;
+  char* stage = smem + table_bytes(entries) + (threadIdx.x / 64) * 64 * kPitch;
   load_table(tab, table, entries);
   __syncthreads();
-  const int lane = threadIdx.x % 64;
   uint32_t sm[4];
   sign_masks<D>(sign_bits, lane, sm);
   const int64_t passes = (n + G::VPW - 1) / G::VPW;
-  const int64_t wave0 = (int64_t)blockIdx.x * kRowsWaves + threadIdx.x / 64;
   const int64_t wstride = (int64_t)gridDim.x * kRowsWaves;
-  const int rowbytes = D * BITS / 8;
-  for (int64_t ps = wave0; ps < passes; ps += wstride) {
+  int64_t ps = (int64_t)blockIdx.x * kRowsWaves + threadIdx.x / 64;
+  uint4 g[4];
+  if (ps < passes) {
+    const int64_t r0 = ps * G::VPW;
+    pass_load<D>(x + r0 * stride, stride, 0, (int)(n - r0 < G::VPW ? n - r0 : G::VPW), g, lane);
+  }
+  for (; ps < passes; ps += wstride) {
     const int64_t row0 = ps * G::VPW;
     const int nv = (int)(n - row0 < G::VPW ? n - row0 : G::VPW);
-    stage_pass<D>(x + row0 * stride, stride, 0, nv, sm, stage, lane);
+    pass_stage<D>(g, sm, stage, lane);
     wave_lds_sync();
-    uint32_t packed[2 * BITS], n16;
-    encode_lane<D, BITS>(stage, tab, nbh, lane, packed, &n16);
-    const int v = lane / G::LPV, part = lane % G::LPV;
-    if (v < nv) {
-      store_packed<BITS>(codes + (row0 + v) * rowbytes + part * (8 * BITS), packed);
-      if (part == 0) norms[row0 + v] = (uint16_t)n16;
+    const int64_t nx = ps + wstride;
+    if (nx < passes) {
+      const int64_t r1 = nx * G::VPW;
+      pass_load<D>(x + r1 * stride, stride, 0, (int)(n - r1 < G::VPW ? n - r1 : G::VPW), g, lane);
     }
+    uint32_t packed[BITS], n16;
+    bool sure;
+    encode_lane<D, BITS>(stage, tab, nbh, lane, packed, &n16, &sure);
+    const int v = lane / G::LPV, part = lane % G::LPV;
+    if (v < nv) store_packed<BITS>(codes + (row0 + v) * (D * BITS / 8) + part * (4 * BITS), packed);
+    n16 = settle_norm<D>(stage, lane, n16, sure);
+    if (v < nv && part == 0) norms[row0 + v] = (uint16_t)n16;
     wave_lds_sync(); /* the next pass overwrites the stage */
   }
 }
@@ -360,141 +437,191 @@ struct AppendArgs {
   float nbh_k, nbh_v;
 };
 
+/* A 32-token tile takes WPT waves (VPW vectors each); a block of 4 waves
+ * works on TPB tiles side by side. */
 template <int D>
 struct AppendGeo {
-  static constexpr int WPK = D >= 256 ? 2 : 1;  /* waves per kind for a 32-token tile */
-  static constexpr int WAVES = 2 * WPK;
+  static constexpr int WPT = 32 / Geo<D>::VPW < 1 ? 1 : 32 / Geo<D>::VPW;
+  static constexpr int TPB = 4 / WPT;
 };
+constexpr int kAppendWaves = 4;
 
-/* One task = one 32-token tile of one (layer, seq, kv head) stream: keys go
- * to rows, values are assembled into the tile layout in LDS and merged with
- * the tile's existing bits when the append covers it only partly. */
+/* Rows of tile `tile` receiving tokens of this append, [jlo, jhi). */
+__device__ inline bool tile_range(const AppendArgs& a, int p0, int tile, int* jlo, int* jhi) {
+  int lo = p0 - 32 * tile, hi = p0 + a.t_new - 32 * tile;
+  if (lo < 0) lo = 0;
+  if (hi > 32) hi = 32;
+  if (32 * tile + hi > a.capacity) hi = a.capacity - 32 * tile;
+  *jlo = lo;
+  *jhi = hi;
+  return hi > lo;
+}
+
+/* Task t of a role: (layer, seq, head, slot) with slot the tile offset from
+ * the first tile touched by the append. */
+__device__ inline void task_coords(const AppendArgs& a, int64_t task, int* layer, int* b, int* h,
+                                   int* slot) {
+  *slot = (int)(task % a.slots);
+  int64_t r = task / a.slots;
+  *h = (int)(r % a.heads);
+  r /= a.heads;
+  *b = (int)(r % a.batch);
+  *layer = (int)(r / a.batch);
+}
+
+/* blockIdx.y = 0: keys (rows); 1: values (tiles).  Every wave loops over its
+ * tasks grid-stride, loading the next task's vectors while encoding. */
 template <int D, int BK, int BV>
-__global__ void __launch_bounds__(64 * AppendGeo<D>::WAVES)
+__global__ void __launch_bounds__(64 * kAppendWaves) __attribute__((amdgpu_waves_per_eu(TQ_ENC_WPE)))
 append_kernel(AppendArgs a) {
   using G = Geo<D>;
   using AG = AppendGeo<D>;
   extern __shared__ __align__(16) char smem[];
-  const int tk_bytes = (a.ent_k * kEncRep * (int)sizeof(tq_enc_entry) + 15) & ~15;
-  const int tv_bytes = (a.ent_v * kEncRep * (int)sizeof(tq_enc_entry) + 15) & ~15;
-  tq_enc_entry* tab_k = (tq_enc_entry*)smem;
-  tq_enc_entry* tab_v = (tq_enc_entry*)(smem + tk_bytes);
-  uint8_t* vbuf = (uint8_t*)(smem + tk_bytes + tv_bytes);  /* [32][D] value codes */
+  const bool is_v = blockIdx.y == 1;
+  const int ent = is_v ? a.ent_v : a.ent_k;
+  const int tb = table_bytes(a.ent_k > a.ent_v ? a.ent_k : a.ent_v);
+  tq_enc_entry* tab = (tq_enc_entry*)smem;
   const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
-  char* stage = smem + tk_bytes + tv_bytes + 32 * D + wave * 64 * kStagePitch;
-  load_table(tab_k, a.tab_k, a.ent_k);
-  load_table(tab_v, a.tab_v, a.ent_v);
+  const int slot_in_block = wave / AG::WPT, sub = wave % AG::WPT;
+  char* stage = smem + tb + wave * 64 * kPitch;
+  uint8_t* vbuf = (uint8_t*)(smem + tb + kAppendWaves * 64 * kPitch) + slot_in_block * 32 * D;
+  load_table(tab, is_v ? a.tab_v : a.tab_k, ent);
   __syncthreads();
-
-  const int kind = wave / AG::WPK, sub = wave % AG::WPK;
+  const float nbh = is_v ? a.nbh_v : a.nbh_k;
+  const uint16_t* src_all = is_v ? a.v_new : a.k_new;
   const int64_t tasks = (int64_t)a.n_layers * a.batch * a.heads * a.slots;
-  const int64_t seg_bytes = D * BV / 16;
-  for (int64_t task = blockIdx.x; task < tasks; task += gridDim.x) {
-    const int slot = (int)(task % a.slots);
-    int64_t r = task / a.slots;
-    const int h = (int)(r % a.heads);
-    r /= a.heads;
-    const int b = (int)(r % a.batch);
-    const int layer = (int)(r / a.batch);
-    const int p0 = a.pos[b];
-    if (p0 < 0) continue; /* uniform over the block */
-    const int tile = p0 / 32 + slot;
-    /* rows 32*tile + j, j in [jlo, jhi), receive tokens 32*tile + j - p0 */
-    int jlo = p0 - 32 * tile, jhi = p0 + a.t_new - 32 * tile;
-    if (jlo < 0) jlo = 0;
-    if (jhi > 32) jhi = 32;
-    if (32 * tile + jhi > a.capacity) jhi = a.capacity - 32 * tile;
-    if (jhi <= jlo) continue; /* uniform over the block */
+  const int64_t step = (int64_t)gridDim.x * AG::TPB;
+  const int j0 = sub * G::VPW; /* this wave's first tile row */
 
-    const uint8_t* sb = a.sign_bits + (int64_t)layer * (D / 8);
-    uint32_t sm[4];
-    sign_masks<D>(sb, lane, sm);
-    const int64_t stream = ((int64_t)layer * a.batch + b) * a.heads + h;
-    const uint16_t* src = (kind == 0 ? a.k_new : a.v_new) + stream * a.t_new * D;
-    /* this wave's vectors: tile rows j = sub * VPW + v */
-    const int j0 = sub * G::VPW;
-    const int64_t tok0 = 32 * (int64_t)tile + j0 - p0; /* source token of v = 0 */
-    const int vlo = jlo - j0, vhi = jhi - j0;
-    const bool active = (vhi > 0) && (vlo < G::VPW) && (j0 < 32);
-    if (active) {
-      stage_pass<D>(src + tok0 * D, D, vlo, vhi, sm, stage, lane);
+  /* per-task geometry of this wave, and its prefetch */
+  auto setup = [&](int64_t task, int* layer, int* b, int* h, int* tile, int* jlo, int* jhi,
+                   const uint16_t** src) -> bool {
+    int slot;
+    task_coords(a, task, layer, b, h, &slot);
+    const int p0 = a.pos[*b];
+    if (p0 < 0) return false;
+    *tile = p0 / 32 + slot;
+    if (!tile_range(a, p0, *tile, jlo, jhi)) return false;
+    const int64_t stream = ((int64_t)*layer * a.batch + *b) * a.heads + *h;
+    *src = src_all + (stream * a.t_new + 32 * (int64_t)*tile + j0 - p0) * D;
+    return true;
+  };
+
+  int64_t task = (int64_t)blockIdx.x * AG::TPB + slot_in_block;
+  uint4 g[4];
+  {
+    int layer, b, h, tile, jlo, jhi;
+    const uint16_t* src;
+    if (task < tasks && setup(task, &layer, &b, &h, &tile, &jlo, &jhi, &src))
+      pass_load<D>(src, D, jlo - j0, jhi - j0, g, lane);
+  }
+  /* every wave runs the same number of iterations (barriers inside) */
+  const int64_t iters = (tasks + step - 1) / step;
+  for (int64_t it = 0; it < iters; ++it, task += step) {
+    int layer = 0, b = 0, h = 0, tile = 0, jlo = 0, jhi = 0;
+    const uint16_t* src = nullptr;
+    const bool live = task < tasks && setup(task, &layer, &b, &h, &tile, &jlo, &jhi, &src);
+    uint32_t n16 = 0;
+    uint32_t pk[BK > BV ? BK : BV];
+    if (live) {
+      uint32_t sm[4];
+      sign_masks<D>(a.sign_bits + (int64_t)layer * (D / 8), lane, sm);
+      pass_stage<D>(g, sm, stage, lane);
       wave_lds_sync();
-      uint32_t n16;
-      const int v = lane / G::LPV, part = lane % G::LPV;
-      const int jrow = j0 + v;
-      const bool mine = v >= vlo && v < vhi && jrow < 32;
-      const int64_t row = ((int64_t)b * a.heads + h) * a.capacity + 32 * (int64_t)tile + jrow;
-      if (kind == 0) {
-        uint32_t pk[2 * BK];
-        encode_lane<D, BK>(stage, tab_k, a.nbh_k, lane, pk, &n16);
-        if (mine) {
-          store_packed<BK>(a.k_codes + layer * a.ls_kc + row * (D * BK / 8) + part * (8 * BK), pk);
-          if (part == 0)
-            *(uint16_t*)((uint8_t*)a.k_norms + layer * a.ls_kn + row * 2) = (uint16_t)n16;
+    }
+    {
+      int l2, b2, h2, t2, lo2, hi2;
+      const uint16_t* s2;
+      const int64_t nt = task + step;
+      if (nt < tasks && setup(nt, &l2, &b2, &h2, &t2, &lo2, &hi2, &s2))
+        pass_load<D>(s2, D, lo2 - j0, hi2 - j0, g, lane);
+    }
+    const int v = lane / G::LPV, part = lane % G::LPV;
+    const int jrow = j0 + v;
+    const bool mine = live && jrow >= jlo && jrow < jhi;
+    const int64_t row = ((int64_t)b * a.heads + h) * a.capacity + 32 * (int64_t)tile + jrow;
+    if (live && !is_v) {
+      uint32_t p4[BK];
+      bool sure;
+      encode_lane<D, BK>(stage, tab, nbh, lane, p4, &n16, &sure);
+      if (mine)
+        store_packed<BK>(a.k_codes + layer * a.ls_kc + row * (D * BK / 8) + part * (4 * BK), p4);
+      n16 = settle_norm<D>(stage, lane, n16, sure);
+      if (mine && part == 0)
+        *(uint16_t*)((uint8_t*)a.k_norms + layer * a.ls_kn + row * 2) = (uint16_t)n16;
+    } else if (live) {
+      uint32_t pv[BV];
+      bool sure;
+      encode_lane<D, BV>(stage, tab, nbh, lane, pv, &n16, &sure);
+      /* unpacked codes of this lane's 32 coordinates -> vbuf[jrow][part*32 ..] */
+      if (jrow < 32) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          uint32_t word = 0;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int i = 4 * k + e, bit = BV * i;
+            uint32_t c = pv[bit / 32] >> (bit % 32);
+            if ((bit % 32) + BV > 32) c |= pv[bit / 32 + 1] << (32 - bit % 32);
+            word |= (c & ((1u << BV) - 1u)) << (8 * e);
+          }
+          *(uint32_t*)(vbuf + jrow * D + part * 32 + 4 * k) = word;
         }
-      } else {
-        uint32_t pv[2 * BV];
-        encode_lane<D, BV>(stage, tab_v, a.nbh_v, lane, pv, &n16);
-        if (mine && part == 0)
-          *(uint16_t*)((uint8_t*)a.v_norms + layer * a.ls_vn + row * 2) = (uint16_t)n16;
-        /* unpacked codes of this lane's 64 coordinates -> vbuf[jrow][part*64 ..] */
-        if (jrow < 32) {
+      }
+      n16 = settle_norm<D>(stage, lane, n16, sure);
+      if (mine && part == 0)
+        *(uint16_t*)((uint8_t*)a.v_norms + layer * a.ls_vn + row * 2) = (uint16_t)n16;
+    }
+    (void)pk;
+    if (is_v) {
+      __syncthreads();
+      /* the first wave of each tile builds the 64 segments of its tile */
+      if (live && sub == 0) {
+        const int q = lane / 16, rr = lane % 16;
+        constexpr int M = D / 16;
+        constexpr int SW = D * BV / 64; /* segment words */
+        uint32_t seg[SW], mask[SW];
 #pragma unroll
-          for (int k = 0; k < 16; ++k) {
-            uint32_t word = 0;
+        for (int k = 0; k < SW; ++k) {
+          seg[k] = 0u;
+          mask[k] = 0u;
+        }
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int i = 4 * k + e, bit = BV * i;
-              uint32_t c = pv[bit / 32] >> (bit % 32);
-              if ((bit % 32) + BV > 32) c |= pv[bit / 32 + 1] << (32 - bit % 32);
-              word |= (c & ((1u << BV) - 1u)) << (8 * e);
+        for (int u = 0; u < 8; ++u) {
+          const int tj = tile_token(q, u);
+          const bool valid = tj >= jlo && tj < jhi;
+          uint8_t cb[M];
+#pragma unroll
+          for (int m = 0; m < M; ++m) cb[m] = vbuf[tj * D + rr * M + m];
+#pragma unroll
+          for (int m = 0; m < M; ++m) {
+            const int bit = (8 * m + u) * BV;
+            const uint32_t c = valid ? cb[m] : 0u;
+            const uint32_t f = valid ? ((1u << BV) - 1u) : 0u;
+            seg[bit / 32] |= c << (bit % 32);
+            mask[bit / 32] |= f << (bit % 32);
+            if ((bit % 32) + BV > 32) {
+              seg[bit / 32 + 1] |= c >> (32 - bit % 32);
+              mask[bit / 32 + 1] |= f >> (32 - bit % 32);
             }
-            *(uint32_t*)(vbuf + jrow * D + part * 64 + 4 * k) = word;
           }
         }
-      }
-    }
-    __syncthreads();
-    /* value tile assembly: lane l of the first value wave builds segment l */
-    if (kind == 1 && sub == 0) {
-      const int q = lane / 16, rr = lane % 16;
-      constexpr int M = D / 16;
-      constexpr int SW = D * BV / 64; /* segment words */
-      uint32_t seg[SW], mask[SW];
+        const int64_t tile_base = (((int64_t)b * a.heads + h) * (a.capacity / 32) + tile) *
+                                  (32 * D * BV / 8);
+        uint32_t* dst = (uint32_t*)(a.v_codes + layer * a.ls_vc + tile_base +
+                                    (int64_t)lane * (D * BV / 16));
+        const bool full = (jlo == 0 && jhi == 32);
 #pragma unroll
-      for (int k = 0; k < SW; ++k) { seg[k] = 0u; mask[k] = 0u; }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int tj = tile_token(q, u);
-        const bool valid = tj >= jlo && tj < jhi;
-        uint8_t cb[M];
-#pragma unroll
-        for (int m = 0; m < M; ++m) cb[m] = vbuf[tj * D + rr * M + m];
-#pragma unroll
-        for (int m = 0; m < M; ++m) {
-          const int bit = (8 * m + u) * BV;
-          const uint32_t c = valid ? cb[m] : 0u;
-          const uint32_t f = valid ? ((1u << BV) - 1u) : 0u;
-          seg[bit / 32] |= c << (bit % 32);
-          mask[bit / 32] |= f << (bit % 32);
-          if ((bit % 32) + BV > 32) {
-            seg[bit / 32 + 1] |= c >> (32 - bit % 32);
-            mask[bit / 32 + 1] |= f >> (32 - bit % 32);
-          }
+        for (int k = 0; k < SW; ++k) {
+          uint32_t val = seg[k];
+          if (!full) val = (dst[k] & ~mask[k]) | (seg[k] & mask[k]);
+          dst[k] = val;
         }
       }
-      const int64_t tile_base = (((int64_t)b * a.heads + h) * (a.capacity / 32) + tile) *
-                                (32 * D * BV / 8);
-      uint32_t* dst = (uint32_t*)(a.v_codes + layer * a.ls_vc + tile_base + lane * seg_bytes);
-      const bool full = (jlo == 0 && jhi == 32);
-#pragma unroll
-      for (int k = 0; k < SW; ++k) {
-        uint32_t val = seg[k];
-        if (!full) val = (dst[k] & ~mask[k]) | (seg[k] & mask[k]);
-        dst[k] = val;
-      }
+      __syncthreads(); /* vbuf is reused by the next task */
+    } else {
+      wave_lds_sync(); /* the stage is reused by the next task */
     }
-    __syncthreads(); /* vbuf and stages are reused by the next task */
   }
 }
 
@@ -504,9 +631,8 @@ tq_status launch_rows_t(const tq_codebook_s* cb, const uint16_t* x, int64_t n, i
   using G = Geo<D>;
   const int64_t passes = (n + G::VPW - 1) / G::VPW;
   int64_t blocks = (passes + kRowsWaves - 1) / kRowsWaves;
-  if (blocks > 2048) blocks = 2048;
-  const size_t lds = ((cb->enc_entries * kEncRep * sizeof(tq_enc_entry) + 15) & ~(size_t)15) +
-                     (size_t)kRowsWaves * 64 * kStagePitch;
+  if (blocks > 4096) blocks = 4096;
+  const size_t lds = table_bytes(cb->enc_entries) + (size_t)kRowsWaves * 64 * kPitch;
   hipLaunchKernelGGL((encode_rows_kernel<D, BITS>), dim3((unsigned)blocks), dim3(64 * kRowsWaves),
                      lds, s, x, n, stride, sb, cb->enc_table, cb->enc_entries,
                      (float)cb->nb_half, codes, norms);
@@ -517,11 +643,11 @@ template <int D, int BK, int BV>
 tq_status launch_append_t(const AppendArgs& a, hipStream_t s) {
   using AG = AppendGeo<D>;
   const int64_t tasks = (int64_t)a.n_layers * a.batch * a.heads * a.slots;
-  int64_t blocks = tasks < 4096 ? tasks : 4096;
-  const size_t lds = ((a.ent_k * kEncRep * sizeof(tq_enc_entry) + 15) & ~(size_t)15) +
-                     ((a.ent_v * kEncRep * sizeof(tq_enc_entry) + 15) & ~(size_t)15) +
-                     32 * D + (size_t)AG::WAVES * 64 * kStagePitch;
-  hipLaunchKernelGGL((append_kernel<D, BK, BV>), dim3((unsigned)blocks), dim3(64 * AG::WAVES),
+  int64_t blocks = (tasks + AG::TPB - 1) / AG::TPB;
+  if (blocks > 2048) blocks = 2048;
+  const size_t lds = table_bytes(a.ent_k > a.ent_v ? a.ent_k : a.ent_v) +
+                     (size_t)kAppendWaves * 64 * kPitch + (size_t)AG::TPB * 32 * D;
+  hipLaunchKernelGGL((append_kernel<D, BK, BV>), dim3((unsigned)blocks, 2), dim3(64 * kAppendWaves),
                      lds, s, a);
   return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_DEVICE;
 }
