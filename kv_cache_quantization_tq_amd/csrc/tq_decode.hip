@@ -40,6 +40,7 @@
 namespace {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
@@ -57,10 +58,29 @@ struct Lut {
   static constexpr int BYTES = ENTRIES * 256;
 };
 
+/* Key tables at 3 and 4 bits also carry each level's remainder: an entry is
+ * {fp16 pair, bf16 remainder pair} (8 bytes), its 256-byte row holds 32
+ * copies and lane l reads copy l % 32 (a 64-bit read serves at most 32 lanes
+ * per LDS cycle, so those still hit distinct banks).  Scores reach tens of
+ * nats at long context, where the 1e-4 relative fp16 rounding of a 4-bit
+ * level would move the softmax visibly; hi + lo is exact to ~2e-7. */
+template <int B>
+struct KSplit {
+  static constexpr bool ON = B >= 3;
+};
+
 /* Fill a table: the source is one word per entry. */
 template <int B>
 __device__ inline void load_lut(uint32_t* dst, const uint32_t* src) {
   for (int i = threadIdx.x; i < Lut<B>::ENTRIES * 64; i += blockDim.x) dst[i] = src[i >> 6];
+}
+
+/* Fill a split key table from the fp16 words and the remainder words. */
+template <int B>
+__device__ inline void load_lut_split(uint32_t* dst, const uint32_t* hi, const uint32_t* lo) {
+  uint2* d2 = (uint2*)dst;
+  for (int i = threadIdx.x; i < Lut<B>::ENTRIES * 32; i += blockDim.x)
+    d2[i] = make_uint2(hi[i >> 5], lo[i >> 5]);
 }
 
 /* LDS word at byte address a of table t (a = (entry << 8) | lane offset). */
@@ -92,6 +112,21 @@ __device__ inline u32x4 deq8(const uint32_t* lut, uint32_t f, uint32_t lo) {
     o[3] = lut_at(lut, __builtin_amdgcn_perm(h, lo, sel_byte(1)));
   }
   return o;
+}
+
+/* The split form of deq8 for key tables: 8 fp16 levels (hi) and their bf16
+ * remainders (lo).  lo8: the lane's copy offset ((lane & 31) * 8). */
+template <int B>
+__device__ inline void deq8_split(const uint32_t* lut, uint32_t f, uint32_t lo8, u32x4& hi,
+                                  u32x4& lo) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const uint32_t a = B == 4 ? __builtin_amdgcn_perm(f, lo8, sel_byte(k))
+                              : ((((f >> (6 * k)) & 0x3Fu) << 8) | lo8);
+    const uint2 w = *(const uint2*)((const char*)lut + a);
+    hi[k] = w.x;
+    lo[k] = w.y;
+  }
 }
 
 /* Bits [8*B*s, 8*B*(s+1)) of a little-endian bit string held in words. */
@@ -180,6 +215,7 @@ struct DecArgs {
   const uint16_t* q;
   const int32_t* seq_lens;
   const uint32_t* lut_k;
+  const uint32_t* lut_k_lo;
   const uint32_t* lut_v;
   float qscale;    /* log2(e) / (d * sigma_K) */
   float oscale;    /* 1 / (sqrt(d) * sigma_V) */
@@ -242,16 +278,27 @@ __device__ inline float mul_h(float x, uint32_t h) {
  * lie at or past len and are masked out. */
 template <class DG, int BK, int BV, bool PARTIAL>
 __device__ inline void tile_step(const TileRegs<DG>& r, const half8 (&bq)[DG::KS],
+                                 const bf16x8 (&bql)[KSplit<BK>::ON ? DG::KS : 1],
                                  const uint32_t* lk, const uint32_t* lv, uint32_t lo,
-                                 floatx4 (&acc)[DG::VM], float& m_run, float& l_run, int tok0,
-                                 int len, int q4) {
+                                 uint32_t lo8, float lo_col, floatx4 (&acc)[DG::VM],
+                                 float& m_run, float& l_run, int tok0, int len, int q4) {
   floatx4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int s = 0; s < DG::KS; ++s) {
-    const u32x4 a0 = deq8<BK>(lk, field<BK>(r.kw0, s), lo);
-    s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, a0), bq[s], s0, 0, 0, 0);
-    const u32x4 a1 = deq8<BK>(lk, field<BK>(r.kw1, s), lo);
-    s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, a1), bq[s], s1, 0, 0, 0);
+    if constexpr (KSplit<BK>::ON) {
+      u32x4 h0, l0, h1, l1;
+      deq8_split<BK>(lk, field<BK>(r.kw0, s), lo8, h0, l0);
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, h0), bq[s], s0, 0, 0, 0);
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, l0), bql[s], s0, 0, 0, 0);
+      deq8_split<BK>(lk, field<BK>(r.kw1, s), lo8, h1, l1);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, h1), bq[s], s1, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, l1), bql[s], s1, 0, 0, 0);
+    } else {
+      const u32x4 a0 = deq8<BK>(lk, field<BK>(r.kw0, s), lo);
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, a0), bq[s], s0, 0, 0, 0);
+      const u32x4 a1 = deq8<BK>(lk, field<BK>(r.kw1, s), lo);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, a1), bq[s], s1, 0, 0, 0);
+    }
   }
   /* tokens tok0 + 4 q4 + u (u < 4) and tok0 + 16 + 4 q4 + u - 4 */
   const uint32_t knw[4] = {r.kn0.x, r.kn0.y, r.kn1.x, r.kn1.y};
@@ -289,7 +336,9 @@ __device__ inline void tile_step(const TileRegs<DG>& r, const half8 (&bq)[DG::KS
     const float p = __builtin_amdgcn_exp2f(sc[u] - m_run);
     l_run += p;
     const uint32_t vh = (vnw[u / 2] >> (16 * (u & 1))) & 0xFFFFu;
-    _Float16 pv = (_Float16)mul_h(p, vh);
+    /* columns 0..7 take fp16(p m), columns 8..15 the fp16 remainder */
+    const float pm = mul_h(p, vh);
+    _Float16 pv = (_Float16)__builtin_fmaf(-lo_col, (float)(_Float16)pm, pm);
     if (PARTIAL) {
       const int tok = tok0 + (u < 4 ? 4 * q4 + u : 16 + 4 * q4 + (u - 4));
       pv = tok < len ? pv : (_Float16)0.0f;
@@ -343,7 +392,10 @@ decode_kernel(DecArgs a) {
   const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
   const int q4 = lane / 16, n = lane % 16;
 
-  load_lut<BK>(lut_k, a.lut_k);
+  if constexpr (KSplit<BK>::ON)
+    load_lut_split<BK>(lut_k, a.lut_k, a.lut_k_lo);
+  else
+    load_lut<BK>(lut_k, a.lut_k);
   load_lut<BV>(lut_v, a.lut_v);
   /* rotated queries: qbuf[g][i] = (D q_g)_i, then FWHT, then scale */
   const uint8_t* sb = a.sign_bits + (int64_t)layer * (D / 8);
@@ -356,8 +408,11 @@ decode_kernel(DecArgs a) {
   __syncthreads();
   lds_fwht<D>(qbuf, G);
 
-  /* B operands of the score products (hi part in columns 0..7, lo in 8..15) */
+  /* B operands of the score products (hi part in columns 0..7, lo in 8..15),
+   * and for split key tables the bf16 query that multiplies the level
+   * remainders (columns 0..7; the rest zero) */
   half8 bq[DG::KS];
+  bf16x8 bql[KSplit<BK>::ON ? DG::KS : 1];
   {
     const int g = n & 7;
 #pragma unroll
@@ -367,6 +422,7 @@ decode_kernel(DecArgs a) {
         float v = g < G ? qbuf[g * D + q4 * DG::KQ + 8 * s + r] * a.qscale : 0.0f;
         _Float16 hi = (_Float16)v;
         bq[s][r] = n < 8 ? hi : (_Float16)(v - (float)hi);
+        if constexpr (KSplit<BK>::ON) bql[s][r] = n < 8 ? (__bf16)v : (__bf16)0.0f;
       }
     }
   }
@@ -385,6 +441,8 @@ decode_kernel(DecArgs a) {
   const uint16_t* knb = (const uint16_t*)(a.k_norms + layer * a.ls_kn) + sh * a.capacity + 4 * q4;
   const uint16_t* vnb = (const uint16_t*)(a.v_norms + layer * a.ls_vn) + sh * a.capacity + 4 * q4;
   const uint32_t lo = (uint32_t)lane << 2;
+  const uint32_t lo8 = (uint32_t)(lane & 31) << 3;
+  const float lo_col = n < 8 ? 0.0f : 1.0f; /* this lane's column holds remainders */
 
   floatx4 acc[DG::VM];
 #pragma unroll
@@ -401,19 +459,24 @@ decode_kernel(DecArgs a) {
   if (tile < full_end) load_tile<DG>(ra, kbase, vbase, knb, vnb, tile, n);
   while (tile < full_end) {
     if (tile + kWaves < full_end) load_tile<DG>(rb, kbase, vbase, knb, vnb, tile + kWaves, n);
-    tile_step<DG, BK, BV, false>(ra, bq, lut_k, lut_v, lo, acc, m_run, l_run, tile * 32, len, q4);
+    tile_step<DG, BK, BV, false>(ra, bq, bql, lut_k, lut_v, lo, lo8, lo_col, acc, m_run, l_run, tile * 32, len, q4);
     tile += kWaves;
     if (tile >= full_end) break;
     if (tile + kWaves < full_end) load_tile<DG>(ra, kbase, vbase, knb, vnb, tile + kWaves, n);
-    tile_step<DG, BK, BV, false>(rb, bq, lut_k, lut_v, lo, acc, m_run, l_run, tile * 32, len, q4);
+    tile_step<DG, BK, BV, false>(rb, bq, bql, lut_k, lut_v, lo, lo8, lo_col, acc, m_run, l_run, tile * 32, len, q4);
     tile += kWaves;
   }
   /* the ragged last tile, if this wave owns it */
   if (tile < t_end) {
     load_tile<DG>(ra, kbase, vbase, knb, vnb, tile, n);
-    tile_step<DG, BK, BV, true>(ra, bq, lut_k, lut_v, lo, acc, m_run, l_run, tile * 32, len, q4);
+    tile_step<DG, BK, BV, true>(ra, bq, bql, lut_k, lut_v, lo, lo8, lo_col, acc, m_run, l_run, tile * 32, len, q4);
   }
   l_run = rows_sum(l_run);
+  /* value sums: column g (< 8) += column g + 8 (the fp16 remainders of p m) */
+#pragma unroll
+  for (int m = 0; m < DG::VM; ++m)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[m][i] = ror8_add(acc[m][i]);
 
   /* merge the waves: mbuf[w] = {m[8], l[8], acc[8][D]} */
   __syncthreads(); /* tables are dead from here on */
@@ -617,6 +680,7 @@ tq_status tq_launch_decode(const tq_kv_cache* c, const tq_codebook_s* cbk,
   a.q = q;
   a.seq_lens = seq_lens;
   a.lut_k = cbk->dec_lut;
+  a.lut_k_lo = cbk->dec_lut_lo;
   a.lut_v = cbv->dec_lut;
   const double d = c->head_dim;
   a.qscale = (float)(1.4426950408889634 / (d * cbk->sigma));

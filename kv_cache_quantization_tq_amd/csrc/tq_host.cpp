@@ -98,6 +98,14 @@ static uint16_t half_rne_normal(double v) {
   return (uint16_t)(((e + 15) << 10) | (uint16_t)(q - 1024));
 }
 
+/* bf16 bits of f, round to nearest even (f finite). */
+static uint16_t bf16_rne(float f) {
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
 static double half_value(uint16_t h) {
   int e = (h >> 10) & 31, f = h & 1023;
   double v = e ? ldexp(1024.0 + f, e - 25) : ldexp((double)f, -24);
@@ -178,19 +186,28 @@ extern "C" tq_status tq_codebook_init(int head_dim, int bits, tq_codebook* out) 
   }
   /* one word per entry: the fp16 levels of two codes (first code in the low
    * half); the entry index is a byte (bits 4), 6 bits (bits 3) or a nibble
-   * (bits 2) holding the two codes */
+   * (bits 2) holding the two codes.  A second table of the same shape holds
+   * the bf16 of each level's fp16 rounding remainder, so hi + lo carries the
+   * level to about 2^-20 relative where key scores need it. */
+  uint16_t r16[16];
+  for (int k = 0; k < L; ++k) {
+    double v = cb->centroids64[k] * cb->sigma;
+    r16[k] = bf16_rne((float)(v - half_value(h[k])));
+  }
   size_t lut_words = bits == 2 ? 16 : (bits == 3 ? 64 : 256);
-  uint32_t* lut = (uint32_t*)calloc(lut_words, 4);
-  for (size_t e = 0; e < lut_words; ++e)
+  uint32_t* lut = (uint32_t*)calloc(2 * lut_words, 4);
+  for (size_t e = 0; e < lut_words; ++e) {
     lut[e] = h[e & (L - 1)] | ((uint32_t)h[e >> bits] << 16);
+    lut[lut_words + e] = r16[e & (L - 1)] | ((uint32_t)r16[e >> bits] << 16);
+  }
   size_t enc_bytes = ((size_t)ne * sizeof(tq_enc_entry) + 255) & ~(size_t)255;
-  size_t total = enc_bytes + lut_words * 4;
+  size_t total = enc_bytes + 2 * lut_words * 4;
   tq_status st = TQ_OK;
   if (hipGetDevice(&cb->device) != hipSuccess || hipMalloc(&cb->dev_mem, total) != hipSuccess) {
     st = TQ_ERR_DEVICE;
   } else if (hipMemcpy(cb->dev_mem, et, (size_t)ne * sizeof(tq_enc_entry),
                        hipMemcpyHostToDevice) != hipSuccess ||
-             hipMemcpy((char*)cb->dev_mem + enc_bytes, lut, lut_words * 4,
+             hipMemcpy((char*)cb->dev_mem + enc_bytes, lut, 2 * lut_words * 4,
                        hipMemcpyHostToDevice) != hipSuccess) {
     (void)hipFree(cb->dev_mem);
     st = TQ_ERR_DEVICE;
@@ -200,6 +217,7 @@ extern "C" tq_status tq_codebook_init(int head_dim, int bits, tq_codebook* out) 
   if (st != TQ_OK) { free(cb); return st; }
   cb->enc_table = (const tq_enc_entry*)cb->dev_mem;
   cb->dec_lut = (const uint32_t*)((char*)cb->dev_mem + enc_bytes);
+  cb->dec_lut_lo = cb->dec_lut + (bits == 2 ? 16 : (bits == 3 ? 64 : 256));
   *out = cb;
   return TQ_OK;
 }

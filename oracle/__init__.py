@@ -190,14 +190,18 @@ def halves_to_double(x):
     return np.asarray(x, dtype=np.uint16).view(np.float16).astype(np.float64)
 
 
-def decode_stream(k16, v16, q16, bits_k, bits_v, sign_bits):
+def decode_stream(k16, v16, q16, bits_k, bits_v, sign_bits, full=False):
     """The whole path for one (layer, seq, kv head) stream, in the original
     domain: encode K and V, dequantize, attend with the G queries q16[G][d].
 
-    Returns dict(out[G][d], k_codes, k_norms, k_band, v_codes, v_norms, v_band)."""
+    Returns dict(out[G][d], k_codes, k_norms, k_band, v_codes, v_norms, v_band)
+    and, with full=True, the dequantized K[T][d] and V[T][d] too."""
     kc, kn, kb = encode(k16, bits_k, sign_bits)
     vc, vn, vb = encode(v16, bits_v, sign_bits)
     K = dequant(kc, kn, bits_k, sign_bits)
     V = dequant(vc, vn, bits_v, sign_bits)
     out = attention(halves_to_double(q16), K, V)
-    return dict(out=out, k_codes=kc, k_norms=kn, k_band=kb, v_codes=vc, v_norms=vn, v_band=vb)
+    r = dict(out=out, k_codes=kc, k_norms=kn, k_band=kb, v_codes=vc, v_norms=vn, v_band=vb)
+    if full:
+        r["K"], r["V"] = K, V
+    return r

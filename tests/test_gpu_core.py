@@ -9,7 +9,8 @@ import pytest
 import kv_cache_quantization_tq_amd as tq
 import oracle
 import synth
-from helpers import MAX_ABS, REL_L2, attention_errors, compare_codes, require_gpu
+from helpers import (attention_errors, check_attention, compare_codes,
+                     oracle_attention_with_bound, require_gpu)
 
 pytestmark = pytest.mark.gpu
 SEED = 1001
@@ -180,14 +181,17 @@ def _decode_case(torch, d, bk, bv, G, lens, Lyr=2, H=2, seed=SEED):
 
 def _oracle_decode(seed, d, bk, bv, G, lens, sbs, q16, Lyr=2, H=2):
     ref = np.zeros((Lyr, len(lens), G * H, d))
+    bound = np.zeros_like(ref)
     for l in range(Lyr):
         for b, n in enumerate(lens):
             for h in range(H):
                 k = synth.kv_host(seed, 0, l, b, h, d, 0, n)
                 v = synth.kv_host(seed, 1, l, b, h, d, 0, n)
-                r = oracle.decode_stream(k, v, q16[l, b, h * G:(h + 1) * G], bk, bv, sbs[l])
-                ref[l, b, h * G:(h + 1) * G] = r["out"]
-    return ref
+                o, bd, _ = oracle_attention_with_bound(k, v, q16[l, b, h * G:(h + 1) * G], bk, bv,
+                                                       sbs[l])
+                ref[l, b, h * G:(h + 1) * G] = o
+                bound[l, b, h * G:(h + 1) * G] = bd
+    return ref, bound
 
 
 @pytest.mark.parametrize("d,bk,bv,G,lens", [
@@ -203,10 +207,8 @@ def _oracle_decode(seed, d, bk, bv, G, lens, sbs, q16, Lyr=2, H=2):
 def test_decode_parity(d, bk, bv, G, lens):
     torch = require_gpu()
     _, sbs, q16, out, _ = _decode_case(torch, d, bk, bv, G, lens)
-    ref = _oracle_decode(SEED, d, bk, bv, G, lens, sbs, q16)
-    rel, mx = attention_errors(out, ref)
-    print(f"decode d={d} K{bk}/V{bv} G={G} lens={lens}: rel-L2 {rel:.3e} max-abs {mx:.3e}")
-    assert rel <= REL_L2 and mx <= MAX_ABS, (rel, mx)
+    ref, bound = _oracle_decode(SEED, d, bk, bv, G, lens, sbs, q16)
+    check_attention(out, ref, bound, f"decode d={d} K{bk}/V{bv} G={G} lens={lens}")
     for b, n in enumerate(lens):
         if n == 0:
             assert np.all(out[:, b] == 0)
