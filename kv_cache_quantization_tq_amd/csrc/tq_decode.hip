@@ -40,57 +40,63 @@
 namespace {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 8;        /* waves per workgroup */
-/* Decoder lookup tables in LDS.  Every lookup maps the codes of two
- * coordinates to their two fp16 levels (one 32-bit word):
- *   bits 4: a byte (256 entries), bits 3: 6 bits (64), bits 2: a nibble (16).
- * Entry e owns a 256-byte row holding 64 copies of its word; lane l reads copy
- * l, at byte (e << 8) | (l << 2), so the 64 lanes of a lookup hit 64 different
- * banks whatever the codes.  The address is one byte permute for bits 4 and 2
- * (the index byte goes to bits 8..15, the lane offset to bits 0..7). */
+/* Decoder lookup tables in LDS.  Every table row is 256 bytes and holds
+ * copies of one entry, one copy per lane (64 copies of a 4-byte entry, or 32
+ * copies of an 8-byte entry, lane l reading copy l % 32: a 64-bit read serves
+ * at most 32 lanes per LDS cycle), so the lanes of a lookup hit distinct
+ * banks whatever the codes.  The row address is one byte permute: the index
+ * byte goes to bits 8..15, the lane's copy offset to bits 0..7.
+ *   Word tables (4-byte entries): the fp16 levels of two codes, indexed by a
+ *     byte (bits 4), 6 bits (bits 3) or a nibble (bits 2).
+ *   Split key tables (bits 3 and 4, 8-byte entries): {fp16 pair, fp16 pair
+ *     of (level - fp16 level) * 2^11}.  Key scores reach tens of nats at
+ *     long context, where the ~1e-4 relative fp16 rounding of a level would
+ *     move the softmax visibly; the remainder, multiplied by q * 2^-11 in the
+ *     same matrix product, makes the level exact to ~2^-22.
+ *   Quad value tables (bits 2, 8-byte entries): the four fp16 levels of a
+ *     byte of four codes. */
 template <int B>
-struct Lut {
+struct KTab {
+  static constexpr bool SPLIT = B >= 3;
   static constexpr int ENTRIES = B == 4 ? 256 : (B == 3 ? 64 : 16);
   static constexpr int BYTES = ENTRIES * 256;
 };
-
-/* Key tables at 3 and 4 bits also carry each level's remainder: an entry is
- * {fp16 pair, bf16 remainder pair} (8 bytes), its 256-byte row holds 32
- * copies and lane l reads copy l % 32 (a 64-bit read serves at most 32 lanes
- * per LDS cycle, so those still hit distinct banks).  Scores reach tens of
- * nats at long context, where the 1e-4 relative fp16 rounding of a 4-bit
- * level would move the softmax visibly; hi + lo is exact to ~2e-7. */
 template <int B>
-struct KSplit {
-  static constexpr bool ON = B >= 3;
+struct VTab {
+  static constexpr bool QUAD = B == 2;
+  static constexpr int ENTRIES = B == 3 ? 64 : 256;
+  static constexpr int BYTES = ENTRIES * 256;
 };
 
-/* Fill a table: the source is one word per entry. */
-template <int B>
-__device__ inline void load_lut(uint32_t* dst, const uint32_t* src) {
-  for (int i = threadIdx.x; i < Lut<B>::ENTRIES * 64; i += blockDim.x) dst[i] = src[i >> 6];
+/* Fill a word table: 64 copies of src[e] per row. */
+__device__ inline void fill_words(uint32_t* dst, const uint32_t* src, int entries) {
+  for (int i = threadIdx.x; i < entries * 64; i += blockDim.x) dst[i] = src[i >> 6];
 }
 
-/* Fill a split key table from the fp16 words and the remainder words. */
-template <int B>
-__device__ inline void load_lut_split(uint32_t* dst, const uint32_t* hi, const uint32_t* lo) {
+/* Fill an 8-byte-entry table: 32 copies of {a[e], b[e]} per row. */
+__device__ inline void fill_pairs(uint32_t* dst, const uint32_t* a, const uint32_t* b,
+                                  int entries, int stride) {
   uint2* d2 = (uint2*)dst;
-  for (int i = threadIdx.x; i < Lut<B>::ENTRIES * 32; i += blockDim.x)
-    d2[i] = make_uint2(hi[i >> 5], lo[i >> 5]);
+  for (int i = threadIdx.x; i < entries * 32; i += blockDim.x)
+    d2[i] = make_uint2(a[(i >> 5) * stride], b[(i >> 5) * stride]);
 }
 
 /* LDS word at byte address a of table t (a = (entry << 8) | lane offset). */
 __device__ inline uint32_t lut_at(const uint32_t* t, uint32_t a) {
   return *(const uint32_t*)((const char*)t + a);
 }
+__device__ inline uint2 lut_at2(const uint32_t* t, uint32_t a) {
+  return *(const uint2*)((const char*)t + a);
+}
 
 /* v_perm_b32 selector putting byte k of the first operand at bits 8..15 and
- * byte 0 of the second at bits 0..7, zeros above. */
-__device__ inline constexpr uint32_t sel_byte(int k) { return 0x0C0C0000u | ((4u + k) << 8); }
+ * bytes 0 and 2 of the second (the lane offset, and the table base / 64 KB)
+ * at bits 0..7 and 16..23. */
+__device__ inline constexpr uint32_t sel_byte(int k) { return 0x0C020000u | ((4u + k) << 8); }
 
 /* Dequantize an 8*B-bit field (8 codes) into 8 fp16 (4 words).  lo: the
  * lane's offset word (lane * 4). */
@@ -114,19 +120,21 @@ __device__ inline u32x4 deq8(const uint32_t* lut, uint32_t f, uint32_t lo) {
   return o;
 }
 
-/* The split form of deq8 for key tables: 8 fp16 levels (hi) and their bf16
- * remainders (lo).  lo8: the lane's copy offset ((lane & 31) * 8). */
+/* The split key lookup of an 8*B-bit field (8 codes): two matrix operands,
+ * each {fp16 pair, remainder pair, fp16 pair, remainder pair} of 4 codes.
+ * lo8: the lane's copy offset ((lane & 31) * 8). */
 template <int B>
-__device__ inline void deq8_split(const uint32_t* lut, uint32_t f, uint32_t lo8, u32x4& hi,
-                                  u32x4& lo) {
+__device__ inline void deq8_split(const uint32_t* lut, uint32_t f, uint32_t lo8, u32x4& a0,
+                                  u32x4& a1) {
+  uint2 w[4];
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const uint32_t a = B == 4 ? __builtin_amdgcn_perm(f, lo8, sel_byte(k))
                               : ((((f >> (6 * k)) & 0x3Fu) << 8) | lo8);
-    const uint2 w = *(const uint2*)((const char*)lut + a);
-    hi[k] = w.x;
-    lo[k] = w.y;
+    w[k] = lut_at2(lut, a);
   }
+  a0 = u32x4{w[0].x, w[0].y, w[1].x, w[1].y};
+  a1 = u32x4{w[2].x, w[2].y, w[3].x, w[3].y};
 }
 
 /* Bits [8*B*s, 8*B*(s+1)) of a little-endian bit string held in words. */
@@ -217,6 +225,7 @@ struct DecArgs {
   const uint32_t* lut_k;
   const uint32_t* lut_k_lo;
   const uint32_t* lut_v;
+  const uint32_t* lut_v_quad;
   float qscale;    /* log2(e) / (d * sigma_K) */
   float oscale;    /* 1 / (sqrt(d) * sigma_V) */
   float* out;
@@ -227,8 +236,8 @@ struct DecArgs {
 /* LDS of one decode block. */
 template <int D, int BK, int BV>
 constexpr size_t decode_lds_bytes() {
-  return (size_t)((Lut<BK>::BYTES + Lut<BV>::BYTES) > kWaves * (8 * D + 16) * 4
-                      ? (Lut<BK>::BYTES + Lut<BV>::BYTES)
+  return (size_t)((KTab<BK>::BYTES + VTab<BV>::BYTES) > kWaves * (8 * D + 16) * 4
+                      ? (KTab<BK>::BYTES + VTab<BV>::BYTES)
                       : kWaves * (8 * D + 16) * 4) +
          8 * D * 4;
 }
@@ -277,26 +286,26 @@ __device__ inline float mul_h(float x, uint32_t h) {
 /* Score, softmax-update and accumulate one tile.  PARTIAL: some of its tokens
  * lie at or past len and are masked out. */
 template <class DG, int BK, int BV, bool PARTIAL>
-__device__ inline void tile_step(const TileRegs<DG>& r, const half8 (&bq)[DG::KS],
-                                 const bf16x8 (&bql)[KSplit<BK>::ON ? DG::KS : 1],
+__device__ inline void tile_step(const TileRegs<DG>& r,
+                                 const half8 (&bq)[KTab<BK>::SPLIT ? 2 * DG::KS : DG::KS],
                                  const uint32_t* lk, const uint32_t* lv, uint32_t lo,
-                                 uint32_t lo8, float lo_col, floatx4 (&acc)[DG::VM],
+                                 uint32_t lo8, uint32_t lok, float lo_col, floatx4 (&acc)[DG::VM],
                                  float& m_run, float& l_run, int tok0, int len, int q4) {
   floatx4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int s = 0; s < DG::KS; ++s) {
-    if constexpr (KSplit<BK>::ON) {
-      u32x4 h0, l0, h1, l1;
-      deq8_split<BK>(lk, field<BK>(r.kw0, s), lo8, h0, l0);
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, h0), bq[s], s0, 0, 0, 0);
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, l0), bql[s], s0, 0, 0, 0);
-      deq8_split<BK>(lk, field<BK>(r.kw1, s), lo8, h1, l1);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, h1), bq[s], s1, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, l1), bql[s], s1, 0, 0, 0);
+    if constexpr (KTab<BK>::SPLIT) {
+      u32x4 a0, a1;
+      deq8_split<BK>(lk, field<BK>(r.kw0, s), lok, a0, a1);
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, a0), bq[2 * s], s0, 0, 0, 0);
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, a1), bq[2 * s + 1], s0, 0, 0, 0);
+      deq8_split<BK>(lk, field<BK>(r.kw1, s), lok, a0, a1);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, a0), bq[2 * s], s1, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, a1), bq[2 * s + 1], s1, 0, 0, 0);
     } else {
-      const u32x4 a0 = deq8<BK>(lk, field<BK>(r.kw0, s), lo);
+      const u32x4 a0 = deq8<BK>(lk, field<BK>(r.kw0, s), lok);
       s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, a0), bq[s], s0, 0, 0, 0);
-      const u32x4 a1 = deq8<BK>(lk, field<BK>(r.kw1, s), lo);
+      const u32x4 a1 = deq8<BK>(lk, field<BK>(r.kw1, s), lok);
       s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, a1), bq[s], s1, 0, 0, 0);
     }
   }
@@ -323,7 +332,7 @@ __device__ inline void tile_step(const TileRegs<DG>& r, const half8 (&bq)[DG::KS
   }
   mt = rows_max(mt);
   const float m_new = fmaxf(m_run, mt);
-  if (__any(m_new > m_run)) { /* rescale the running sums, lazily */
+  if (__builtin_expect(__any(m_new > m_run), 0)) { /* rescale the running sums */
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     l_run *= alpha;
 #pragma unroll
@@ -345,21 +354,15 @@ __device__ inline void tile_step(const TileRegs<DG>& r, const half8 (&bq)[DG::KS
     }
     pb[u] = pv;
   }
-  if constexpr (BV == 2) {
-    /* a value word holds two 8-code fields: split its nibbles once */
+  if constexpr (VTab<BV>::QUAD) {
+    /* a value word holds two 16-bit fields; each byte of one is four tokens'
+     * codes, looked up as four fp16 levels at once */
 #pragma unroll
-    for (int j = 0; j < DG::VW; ++j) {
-      const uint32_t g = r.vw[j] & 0x0F0F0F0Fu, h = (r.vw[j] >> 4) & 0x0F0F0F0Fu;
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        u32x4 av;
-        av[0] = lut_at(lv, __builtin_amdgcn_perm(g, lo, sel_byte(2 * half)));
-        av[1] = lut_at(lv, __builtin_amdgcn_perm(h, lo, sel_byte(2 * half)));
-        av[2] = lut_at(lv, __builtin_amdgcn_perm(g, lo, sel_byte(2 * half + 1)));
-        av[3] = lut_at(lv, __builtin_amdgcn_perm(h, lo, sel_byte(2 * half + 1)));
-        const int m = 2 * j + half;
-        acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, av), pb, acc[m], 0, 0, 0);
-      }
+    for (int m = 0; m < DG::VM; ++m) {
+      const uint2 w0 = lut_at2(lv, __builtin_amdgcn_perm(r.vw[m / 2], lo8, sel_byte(2 * (m & 1))));
+      const uint2 w1 = lut_at2(lv, __builtin_amdgcn_perm(r.vw[m / 2], lo8, sel_byte(2 * (m & 1) + 1)));
+      const u32x4 av = {w0.x, w0.y, w1.x, w1.y};
+      acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, av), pb, acc[m], 0, 0, 0);
     }
   } else {
 #pragma unroll
@@ -379,7 +382,12 @@ decode_kernel(DecArgs a) {
    * reused as the wave-merge buffer afterwards; then the rotated queries */
   __shared__ __align__(16) char smem[decode_lds_bytes<D, BK, BV>()];
   uint32_t* lut_v = (uint32_t*)smem;
-  uint32_t* lut_k = (uint32_t*)(smem + Lut<BV>::BYTES);
+  uint32_t* lut_k = (uint32_t*)(smem + VTab<BV>::BYTES);
+  /* Key lookups address the key table from the LDS base: its part below
+   * 64 KB folds into the ds_read offset field, the 64 KB pages ride in the
+   * lane-offset operand of the address permute (no extra add per lookup). */
+  constexpr uint32_t KPAGE = VTab<BV>::BYTES & ~0xFFFFu;
+  const uint32_t* lut_k_rd = (const uint32_t*)(smem + (VTab<BV>::BYTES - KPAGE));
   float* qbuf = (float*)(smem + decode_lds_bytes<D, BK, BV>() - 8 * D * 4);
   float* mbuf = (float*)smem; /* aliases the tables after the token loop */
   const int G = a.group;
@@ -392,11 +400,14 @@ decode_kernel(DecArgs a) {
   const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
   const int q4 = lane / 16, n = lane % 16;
 
-  if constexpr (KSplit<BK>::ON)
-    load_lut_split<BK>(lut_k, a.lut_k, a.lut_k_lo);
+  if constexpr (KTab<BK>::SPLIT)
+    fill_pairs(lut_k, a.lut_k, a.lut_k_lo, KTab<BK>::ENTRIES, 1);
   else
-    load_lut<BK>(lut_k, a.lut_k);
-  load_lut<BV>(lut_v, a.lut_v);
+    fill_words(lut_k, a.lut_k, KTab<BK>::ENTRIES);
+  if constexpr (VTab<BV>::QUAD)
+    fill_pairs(lut_v, a.lut_v_quad, a.lut_v_quad + 1, VTab<BV>::ENTRIES, 2);
+  else
+    fill_words(lut_v, a.lut_v, VTab<BV>::ENTRIES);
   /* rotated queries: qbuf[g][i] = (D q_g)_i, then FWHT, then scale */
   const uint8_t* sb = a.sign_bits + (int64_t)layer * (D / 8);
   const uint16_t* qg = a.q + (((int64_t)layer * a.batch + b) * a.q_heads + (int64_t)kv * G) * D;
@@ -408,21 +419,36 @@ decode_kernel(DecArgs a) {
   __syncthreads();
   lds_fwht<D>(qbuf, G);
 
-  /* B operands of the score products (hi part in columns 0..7, lo in 8..15),
-   * and for split key tables the bf16 query that multiplies the level
-   * remainders (columns 0..7; the rest zero) */
-  half8 bq[DG::KS];
-  bf16x8 bql[KSplit<BK>::ON ? DG::KS : 1];
+  /* B operands of the score products: fp16(q'') in columns 0..7 (one per
+   * head), the fp16 remainder q'' - fp16(q'') in columns 8..15.  With split
+   * key tables an operand covers 4 coordinates c0..c3 of the lane's 8 as
+   * rows [c0 c1 c0' c1' c2 c3 c2' c3'], where the primed rows meet the level
+   * remainders and hold fp16(q'' * 2^-11) in columns 0..7, zero elsewhere. */
+  constexpr int NB = KTab<BK>::SPLIT ? 2 * DG::KS : DG::KS;
+  half8 bq[NB];
   {
     const int g = n & 7;
+    const float* qg = qbuf + g * D + q4 * DG::KQ;
 #pragma unroll
-    for (int s = 0; s < DG::KS; ++s) {
+    for (int t = 0; t < NB; ++t) {
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
-        float v = g < G ? qbuf[g * D + q4 * DG::KQ + 8 * s + r] * a.qscale : 0.0f;
-        _Float16 hi = (_Float16)v;
-        bq[s][r] = n < 8 ? hi : (_Float16)(v - (float)hi);
-        if constexpr (KSplit<BK>::ON) bql[s][r] = n < 8 ? (__bf16)v : (__bf16)0.0f;
+        int j;
+        bool rem = false;
+        if constexpr (KTab<BK>::SPLIT) {
+          j = 4 * t + 2 * (r / 4) + (r & 1);
+          rem = (r & 2) != 0;
+        } else {
+          j = 8 * t + r;
+        }
+        const float v = g < G ? qg[j] * a.qscale : 0.0f;
+        const _Float16 hi = (_Float16)v;
+        _Float16 e;
+        if (rem)
+          e = n < 8 ? (_Float16)(v * 0x1p-11f) : (_Float16)0.0f;
+        else
+          e = n < 8 ? hi : (_Float16)(v - (float)hi);
+        bq[t][r] = e;
       }
     }
   }
@@ -440,8 +466,9 @@ decode_kernel(DecArgs a) {
                          lane * DG::SEG;
   const uint16_t* knb = (const uint16_t*)(a.k_norms + layer * a.ls_kn) + sh * a.capacity + 4 * q4;
   const uint16_t* vnb = (const uint16_t*)(a.v_norms + layer * a.ls_vn) + sh * a.capacity + 4 * q4;
-  const uint32_t lo = (uint32_t)lane << 2;
-  const uint32_t lo8 = (uint32_t)(lane & 31) << 3;
+  const uint32_t lo = (uint32_t)lane << 2;           /* value tables, 4-byte entries */
+  const uint32_t lo8 = (uint32_t)(lane & 31) << 3;   /* value tables, 8-byte entries */
+  const uint32_t lok = (KTab<BK>::SPLIT ? lo8 : lo) | KPAGE; /* key table */
   const float lo_col = n < 8 ? 0.0f : 1.0f; /* this lane's column holds remainders */
 
   floatx4 acc[DG::VM];
@@ -459,17 +486,17 @@ decode_kernel(DecArgs a) {
   if (tile < full_end) load_tile<DG>(ra, kbase, vbase, knb, vnb, tile, n);
   while (tile < full_end) {
     if (tile + kWaves < full_end) load_tile<DG>(rb, kbase, vbase, knb, vnb, tile + kWaves, n);
-    tile_step<DG, BK, BV, false>(ra, bq, bql, lut_k, lut_v, lo, lo8, lo_col, acc, m_run, l_run, tile * 32, len, q4);
+    tile_step<DG, BK, BV, false>(ra, bq, lut_k_rd, lut_v, lo, lo8, lok, lo_col, acc, m_run, l_run, tile * 32, len, q4);
     tile += kWaves;
     if (tile >= full_end) break;
     if (tile + kWaves < full_end) load_tile<DG>(ra, kbase, vbase, knb, vnb, tile + kWaves, n);
-    tile_step<DG, BK, BV, false>(rb, bq, bql, lut_k, lut_v, lo, lo8, lo_col, acc, m_run, l_run, tile * 32, len, q4);
+    tile_step<DG, BK, BV, false>(rb, bq, lut_k_rd, lut_v, lo, lo8, lok, lo_col, acc, m_run, l_run, tile * 32, len, q4);
     tile += kWaves;
   }
   /* the ragged last tile, if this wave owns it */
   if (tile < t_end) {
     load_tile<DG>(ra, kbase, vbase, knb, vnb, tile, n);
-    tile_step<DG, BK, BV, true>(ra, bq, bql, lut_k, lut_v, lo, lo8, lo_col, acc, m_run, l_run, tile * 32, len, q4);
+    tile_step<DG, BK, BV, true>(ra, bq, lut_k_rd, lut_v, lo, lo8, lok, lo_col, acc, m_run, l_run, tile * 32, len, q4);
   }
   l_run = rows_sum(l_run);
   /* value sums: column g (< 8) += column g + 8 (the fp16 remainders of p m) */
@@ -681,6 +708,7 @@ tq_status tq_launch_decode(const tq_kv_cache* c, const tq_codebook_s* cbk,
   a.seq_lens = seq_lens;
   a.lut_k = cbk->dec_lut;
   a.lut_k_lo = cbk->dec_lut_lo;
+  a.lut_v_quad = cbv->dec_quad;
   a.lut_v = cbv->dec_lut;
   const double d = c->head_dim;
   a.qscale = (float)(1.4426950408889634 / (d * cbk->sigma));

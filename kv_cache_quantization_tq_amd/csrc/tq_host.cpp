@@ -98,12 +98,16 @@ static uint16_t half_rne_normal(double v) {
   return (uint16_t)(((e + 15) << 10) | (uint16_t)(q - 1024));
 }
 
-/* bf16 bits of f, round to nearest even (f finite). */
-static uint16_t bf16_rne(float f) {
-  uint32_t u;
-  memcpy(&u, &f, 4);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+/* fp16 bits of v, round to nearest even, subnormals included (|v| < 65504). */
+static uint16_t half_rne(double v) {
+  const double a = fabs(v);
+  uint16_t m;
+  if (a < ldexp(1.0, -14)) {
+    m = (uint16_t)nearbyint(ldexp(a, 24)); /* 1024 lands on the smallest normal */
+  } else {
+    m = half_rne_normal(a);
+  }
+  return (uint16_t)(v < 0 ? (m | 0x8000) : m);
 }
 
 static double half_value(uint16_t h) {
@@ -184,30 +188,40 @@ extern "C" tq_status tq_codebook_init(int head_dim, int bits, tq_codebook* out) 
     uint16_t m = half_rne_normal(fabs(v));
     h[k] = (uint16_t)(v < 0 ? (m | 0x8000) : m);
   }
-  /* one word per entry: the fp16 levels of two codes (first code in the low
-   * half); the entry index is a byte (bits 4), 6 bits (bits 3) or a nibble
-   * (bits 2) holding the two codes.  A second table of the same shape holds
-   * the bf16 of each level's fp16 rounding remainder, so hi + lo carries the
-   * level to about 2^-20 relative where key scores need it. */
+  /* Decoder tables (device copies are spread over LDS rows by the kernel):
+   *  pair[e]:    the fp16 levels of the two codes held by index e (first
+   *              code in the low half); e is a byte (bits 4), 6 bits (bits 3)
+   *              or a nibble (bits 2).
+   *  pair_lo[e]: the same codes' remainders fp16((level - fp16 level) * 2^11),
+   *              so that hi + lo * 2^-11 carries a level to ~2^-22 relative
+   *              (key scores at long context need more than fp16).
+   *  quad[e]:    bits 2 only, e a byte of four codes: their four fp16 levels
+   *              (two words, first code lowest). */
   uint16_t r16[16];
   for (int k = 0; k < L; ++k) {
     double v = cb->centroids64[k] * cb->sigma;
-    r16[k] = bf16_rne((float)(v - half_value(h[k])));
+    r16[k] = half_rne((v - half_value(h[k])) * 2048.0);
   }
-  size_t lut_words = bits == 2 ? 16 : (bits == 3 ? 64 : 256);
-  uint32_t* lut = (uint32_t*)calloc(2 * lut_words, 4);
-  for (size_t e = 0; e < lut_words; ++e) {
+  const size_t pw = bits == 2 ? 16 : (bits == 3 ? 64 : 256);
+  const size_t qw = bits == 2 ? 512 : 0;
+  uint32_t* lut = (uint32_t*)calloc(2 * pw + qw, 4);
+  for (size_t e = 0; e < pw; ++e) {
     lut[e] = h[e & (L - 1)] | ((uint32_t)h[e >> bits] << 16);
-    lut[lut_words + e] = r16[e & (L - 1)] | ((uint32_t)r16[e >> bits] << 16);
+    lut[pw + e] = r16[e & (L - 1)] | ((uint32_t)r16[e >> bits] << 16);
   }
+  for (size_t e = 0; e < qw / 2; ++e) {
+    lut[2 * pw + 2 * e] = h[e & 3] | ((uint32_t)h[(e >> 2) & 3] << 16);
+    lut[2 * pw + 2 * e + 1] = h[(e >> 4) & 3] | ((uint32_t)h[(e >> 6) & 3] << 16);
+  }
+  const size_t lut_words = 2 * pw + qw;
   size_t enc_bytes = ((size_t)ne * sizeof(tq_enc_entry) + 255) & ~(size_t)255;
-  size_t total = enc_bytes + 2 * lut_words * 4;
+  size_t total = enc_bytes + lut_words * 4;
   tq_status st = TQ_OK;
   if (hipGetDevice(&cb->device) != hipSuccess || hipMalloc(&cb->dev_mem, total) != hipSuccess) {
     st = TQ_ERR_DEVICE;
   } else if (hipMemcpy(cb->dev_mem, et, (size_t)ne * sizeof(tq_enc_entry),
                        hipMemcpyHostToDevice) != hipSuccess ||
-             hipMemcpy((char*)cb->dev_mem + enc_bytes, lut, 2 * lut_words * 4,
+             hipMemcpy((char*)cb->dev_mem + enc_bytes, lut, lut_words * 4,
                        hipMemcpyHostToDevice) != hipSuccess) {
     (void)hipFree(cb->dev_mem);
     st = TQ_ERR_DEVICE;
@@ -218,6 +232,7 @@ extern "C" tq_status tq_codebook_init(int head_dim, int bits, tq_codebook* out) 
   cb->enc_table = (const tq_enc_entry*)cb->dev_mem;
   cb->dec_lut = (const uint32_t*)((char*)cb->dev_mem + enc_bytes);
   cb->dec_lut_lo = cb->dec_lut + (bits == 2 ? 16 : (bits == 3 ? 64 : 256));
+  cb->dec_quad = bits == 2 ? cb->dec_lut + 32 : nullptr;
   *out = cb;
   return TQ_OK;
 }

@@ -33,7 +33,8 @@ struct tq_codebook_s {
   void* dev_mem;         /* one device allocation: encoder table, then decoder table */
   const tq_enc_entry* enc_table;
   const uint32_t* dec_lut; /* one word (two fp16 levels) per pair of codes: 2^(2*bits) words */
-  const uint32_t* dec_lut_lo; /* same shape: two bf16 remainders (level - fp16 level) */
+  const uint32_t* dec_lut_lo; /* same shape: two fp16 remainders (level - fp16 level) * 2^11 */
+  const uint32_t* dec_quad;   /* bits 2: four fp16 levels (two words) per byte of codes */
 };
 
 /* Host-side Lloyd-Max (levels / thresholds in fp64, N(0, 1/d)). */
