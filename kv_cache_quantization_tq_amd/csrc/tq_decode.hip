@@ -209,6 +209,7 @@ struct DecGeo {
   static constexpr int VW = SEG / 4;
   static constexpr int VA = (SEG % 16 == 0) ? 16 : (SEG % 8 == 0 ? 8 : 4);
   static constexpr int TILE = 32 * D * BV / 8;  /* value tile bytes */
+  static constexpr int DEPTH = D == 256 ? 2 : 3; /* tiles in flight per wave (registers) */
 };
 
 struct DecArgs {
@@ -476,27 +477,58 @@ decode_kernel(DecArgs a) {
   for (int m = 0; m < DG::VM; ++m) acc[m] = floatx4{0.f, 0.f, 0.f, 0.f};
   float m_run = -1e30f, l_run = 0.0f;
 
-  /* software pipeline: the next tile's loads are in flight while this one is
-   * scored and accumulated */
-  /* full tiles, software-pipelined: the next tile's loads are in flight
-   * while this one is scored and accumulated */
+  /* full tiles, software-pipelined: the loads of the next tiles are in
+   * flight while this one is scored and accumulated (a ring of register
+   * sets, so no copies between tiles).  Prefetches are issued on every path
+   * (past the end they re-read the wave's last tile) so the number of loads
+   * in flight is the same everywhere and each wait covers only the tile
+   * about to be used. */
   const int full_end = (len / 32) < t_end ? (len / 32) : t_end;
-  TileRegs<DG> ra, rb; /* ping-pong: no register copies between tiles */
   int tile = t_begin + wave;
-  if (tile < full_end) load_tile<DG>(ra, kbase, vbase, knb, vnb, tile, n);
-  while (tile < full_end) {
-    if (tile + kWaves < full_end) load_tile<DG>(rb, kbase, vbase, knb, vnb, tile + kWaves, n);
-    tile_step<DG, BK, BV, false>(ra, bq, lut_k_rd, lut_v, lo, lo8, lok, lo_col, acc, m_run, l_run, tile * 32, len, q4);
-    tile += kWaves;
-    if (tile >= full_end) break;
-    if (tile + kWaves < full_end) load_tile<DG>(ra, kbase, vbase, knb, vnb, tile + kWaves, n);
-    tile_step<DG, BK, BV, false>(rb, bq, lut_k_rd, lut_v, lo, lo8, lok, lo_col, acc, m_run, l_run, tile * 32, len, q4);
-    tile += kWaves;
+  constexpr int W = kWaves;
+  if (tile < full_end) {
+    const int last = full_end - 1;
+    auto pf = [&](TileRegs<DG>& r, int t) {
+      load_tile<DG>(r, kbase, vbase, knb, vnb, t < last ? t : last, n);
+    };
+    auto step = [&](const TileRegs<DG>& r) {
+      tile_step<DG, BK, BV, false>(r, bq, lut_k_rd, lut_v, lo, lo8, lok, lo_col, acc, m_run,
+                                   l_run, tile * 32, len, q4);
+    };
+    if constexpr (DG::DEPTH == 3) {
+      TileRegs<DG> ra, rb, rc;
+      pf(ra, tile);
+      pf(rb, tile + W);
+      for (;;) {
+        pf(rc, tile + 2 * W);
+        step(ra);
+        if ((tile += W) >= full_end) break;
+        pf(ra, tile + 2 * W);
+        step(rb);
+        if ((tile += W) >= full_end) break;
+        pf(rb, tile + 2 * W);
+        step(rc);
+        if ((tile += W) >= full_end) break;
+      }
+    } else {
+      TileRegs<DG> ra, rb;
+      pf(ra, tile);
+      for (;;) {
+        pf(rb, tile + W);
+        step(ra);
+        if ((tile += W) >= full_end) break;
+        pf(ra, tile + W);
+        step(rb);
+        if ((tile += W) >= full_end) break;
+      }
+    }
   }
   /* the ragged last tile, if this wave owns it */
   if (tile < t_end) {
-    load_tile<DG>(ra, kbase, vbase, knb, vnb, tile, n);
-    tile_step<DG, BK, BV, true>(ra, bq, lut_k_rd, lut_v, lo, lo8, lok, lo_col, acc, m_run, l_run, tile * 32, len, q4);
+    TileRegs<DG> rp;
+    load_tile<DG>(rp, kbase, vbase, knb, vnb, tile, n);
+    tile_step<DG, BK, BV, true>(rp, bq, lut_k_rd, lut_v, lo, lo8, lok, lo_col, acc, m_run, l_run,
+                                tile * 32, len, q4);
   }
   l_run = rows_sum(l_run);
   /* value sums: column g (< 8) += column g + 8 (the fp16 remainders of p m) */
