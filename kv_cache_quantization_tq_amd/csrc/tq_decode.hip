@@ -43,7 +43,12 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = 8;        /* waves per workgroup */
+/* Waves per workgroup.  One block fills a CU (its lookup tables take most of
+ * the LDS), so this is the CU's occupancy: 12 waves (3 per SIMD) where the
+ * registers allow it (<= 170 VGPRs), else 8. */
+constexpr int waves_for(int d, int bk, int bv) {
+  return (d == 256 || (d == 128 && bk == 4 && bv == 4)) ? 8 : 12;
+}
 /* Decoder lookup tables in LDS.  Every table row is 256 bytes and holds
  * copies of one entry, one copy per lane (64 copies of a 4-byte entry, or 32
  * copies of an 8-byte entry, lane l reading copy l % 32: a 64-bit read serves
@@ -72,17 +77,43 @@ struct VTab {
   static constexpr int BYTES = ENTRIES * 256;
 };
 
-/* Fill a word table: 64 copies of src[e] per row. */
-__device__ inline void fill_words(uint32_t* dst, const uint32_t* src, int entries) {
-  for (int i = threadIdx.x; i < entries * 64; i += blockDim.x) dst[i] = src[i >> 6];
+/* Fill a word table: 64 copies of src[e] per row.  All of a thread's source
+ * words are loaded before any is stored, so the block waits for one round of
+ * (L2-resident) loads rather than one per iteration. */
+template <int ENTRIES, int WAVES>
+__device__ inline void fill_words(uint32_t* dst, const uint32_t* src) {
+  constexpr int N = ENTRIES * 64, T = 64 * WAVES, IT = (N + T - 1) / T;
+  uint32_t v[IT];
+#pragma unroll
+  for (int k = 0; k < IT; ++k) {
+    const int i = threadIdx.x + k * T;
+    v[k] = i < N ? src[i >> 6] : 0u;
+  }
+#pragma unroll
+  for (int k = 0; k < IT; ++k) {
+    const int i = threadIdx.x + k * T;
+    if (i < N) dst[i] = v[k];
+  }
 }
 
-/* Fill an 8-byte-entry table: 32 copies of {a[e], b[e]} per row. */
+/* Fill an 8-byte-entry table: 32 copies of {a[e * stride], b[e * stride]}
+ * per row (loads batched as above). */
+template <int ENTRIES, int WAVES>
 __device__ inline void fill_pairs(uint32_t* dst, const uint32_t* a, const uint32_t* b,
-                                  int entries, int stride) {
+                                  int stride) {
+  constexpr int N = ENTRIES * 32, T = 64 * WAVES, IT = (N + T - 1) / T;
+  uint2 v[IT];
+#pragma unroll
+  for (int k = 0; k < IT; ++k) {
+    const int i = threadIdx.x + k * T;
+    v[k] = i < N ? make_uint2(a[(i >> 5) * stride], b[(i >> 5) * stride]) : make_uint2(0u, 0u);
+  }
   uint2* d2 = (uint2*)dst;
-  for (int i = threadIdx.x; i < entries * 32; i += blockDim.x)
-    d2[i] = make_uint2(a[(i >> 5) * stride], b[(i >> 5) * stride]);
+#pragma unroll
+  for (int k = 0; k < IT; ++k) {
+    const int i = threadIdx.x + k * T;
+    if (i < N) d2[i] = v[k];
+  }
 }
 
 /* LDS word at byte address a of table t (a = (entry << 8) | lane offset). */
@@ -237,9 +268,9 @@ struct DecArgs {
 /* LDS of one decode block. */
 template <int D, int BK, int BV>
 constexpr size_t decode_lds_bytes() {
-  return (size_t)((KTab<BK>::BYTES + VTab<BV>::BYTES) > kWaves * (8 * D + 16) * 4
+  return (size_t)((KTab<BK>::BYTES + VTab<BV>::BYTES) > waves_for(D, BK, BV) * (8 * D + 16) * 4
                       ? (KTab<BK>::BYTES + VTab<BV>::BYTES)
-                      : kWaves * (8 * D + 16) * 4) +
+                      : waves_for(D, BK, BV) * (8 * D + 16) * 4) +
          8 * D * 4;
 }
 
@@ -266,17 +297,33 @@ struct TileRegs {
   uint2 kn0, kn1, vn0, vn1;
 };
 
+/* Addresses of one wave's loads: wave-uniform bases (scalar registers; the
+ * per-tile advance is scalar arithmetic) plus constant per-lane offsets. */
+struct TileAddr {
+  const uint8_t* k;   /* key rows of the stream */
+  const uint8_t* v;   /* value tiles of the stream */
+  const uint8_t* kn;  /* key norms (bytes) */
+  const uint8_t* vn;  /* value norms (bytes) */
+  uint32_t koff, voff, noff;
+};
+
 template <class DG>
-__device__ inline void load_tile(TileRegs<DG>& r, const uint8_t* kbase, const uint8_t* vbase,
-                                 const uint16_t* knb, const uint16_t* vnb, int tile, int n) {
-  const int tok0 = tile * 32;
-  load_words<DG::KB, DG::KA>(kbase + (int64_t)(tok0 + n) * DG::RB, r.kw0);
-  load_words<DG::KB, DG::KA>(kbase + (int64_t)(tok0 + 16 + n) * DG::RB, r.kw1);
-  load_words<DG::SEG, DG::VA>(vbase + (int64_t)tile * DG::TILE, r.vw);
-  r.kn0 = *(const uint2*)(knb + tok0);
-  r.kn1 = *(const uint2*)(knb + tok0 + 16);
-  r.vn0 = *(const uint2*)(vnb + tok0);
-  r.vn1 = *(const uint2*)(vnb + tok0 + 16);
+__device__ inline void load_tile(TileRegs<DG>& r, const TileAddr& ad, int tile) {
+  const uint8_t* kt = ad.k + (int64_t)tile * (32 * DG::RB);
+  load_words<DG::KB, DG::KA>(kt + ad.koff, r.kw0);
+  load_words<DG::KB, DG::KA>(kt + 16 * DG::RB + ad.koff, r.kw1);
+  load_words<DG::SEG, DG::VA>(ad.v + (int64_t)tile * DG::TILE + ad.voff, r.vw);
+  const uint8_t* knt = ad.kn + (int64_t)tile * 64 + ad.noff;
+  const uint8_t* vnt = ad.vn + (int64_t)tile * 64 + ad.noff;
+  r.kn0 = *(const uint2*)knt;
+  r.kn1 = *(const uint2*)(knt + 32);
+  r.vn0 = *(const uint2*)vnt;
+  r.vn1 = *(const uint2*)(vnt + 32);
+}
+
+/* x * h + c, h an fp16 value given by its bits (one mixed-precision FMA). */
+__device__ inline float fma_h(float x, uint32_t h, float c) {
+  return __builtin_fmaf(x, (float)__builtin_bit_cast(_Float16, (uint16_t)h), c);
 }
 
 /* fp32 x times an fp16 value given by its bits (one mixed-precision FMA). */
@@ -291,7 +338,8 @@ __device__ inline void tile_step(const TileRegs<DG>& r,
                                  const half8 (&bq)[KTab<BK>::SPLIT ? 2 * DG::KS : DG::KS],
                                  const uint32_t* lk, const uint32_t* lv, uint32_t lo,
                                  uint32_t lo8, uint32_t lok, float lo_col, floatx4 (&acc)[DG::VM],
-                                 float& m_run, float& l_run, int tok0, int len, int q4) {
+                                 float& m_run, float& l_run, bool& first, int tok0, int len,
+                                 int q4) {
   floatx4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int s = 0; s < DG::KS; ++s) {
@@ -319,31 +367,37 @@ __device__ inline void tile_step(const TileRegs<DG>& r,
     sc[i] = ror8_add(s0[i]);
     sc[4 + i] = ror8_add(s1[i]);
   }
-  float mt = -1e30f;
+  /* scores relative to the running max: w = s - m_run in one fma */
+  float mt = -INFINITY;
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
-    const float v = mul_h(sc[u], (knw[u / 2] >> (16 * (u & 1))) & 0xFFFFu);
+    const float w = fma_h(sc[u], (knw[u / 2] >> (16 * (u & 1))) & 0xFFFFu, -m_run);
     if (PARTIAL) {
       const int tok = tok0 + (u < 4 ? 4 * q4 + u : 16 + 4 * q4 + (u - 4));
-      sc[u] = tok < len ? v : -INFINITY;
+      sc[u] = tok < len ? w : -INFINITY;
     } else {
-      sc[u] = v;
+      sc[u] = w;
     }
     mt = fmaxf(mt, sc[u]);
   }
   mt = rows_max(mt);
-  const float m_new = fmaxf(m_run, mt);
-  if (__builtin_expect(__any(m_new > m_run), 0)) { /* rescale the running sums */
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+  /* a new maximum (or the wave's first tile, which sets it): move the
+   * reference and rescale the running sums; rare after the first tiles */
+  if (__builtin_expect(__any(mt > 0.0f) || first, 0)) {
+    const float dm = first ? mt : fmaxf(mt, 0.0f);
+    const float alpha = first ? 0.0f : __builtin_amdgcn_exp2f(-dm);
     l_run *= alpha;
 #pragma unroll
     for (int m = 0; m < DG::VM; ++m) acc[m] *= alpha;
-    m_run = m_new;
+    m_run += dm;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) sc[u] -= dm;
+    first = false;
   }
   half8 pb;
 #pragma unroll
   for (int u = 0; u < 8; ++u) {
-    const float p = __builtin_amdgcn_exp2f(sc[u] - m_run);
+    const float p = __builtin_amdgcn_exp2f(sc[u]);
     l_run += p;
     const uint32_t vh = (vnw[u / 2] >> (16 * (u & 1))) & 0xFFFFu;
     /* columns 0..7 take fp16(p m), columns 8..15 the fp16 remainder */
@@ -375,9 +429,10 @@ __device__ inline void tile_step(const TileRegs<DG>& r,
 }
 
 template <int D, int BK, int BV>
-__global__ void __launch_bounds__(64 * kWaves)
+__global__ void __launch_bounds__(64 * waves_for(D, BK, BV))
 decode_kernel(DecArgs a) {
   using DG = DecGeo<D, BK, BV>;
+  constexpr int kWaves = waves_for(D, BK, BV);
   /* static LDS (addresses known at compile time, so table bases fold into
    * the ds_read offset field): [V table | K table] during the token loop,
    * reused as the wave-merge buffer afterwards; then the rotated queries */
@@ -398,17 +453,19 @@ decode_kernel(DecArgs a) {
   unit /= a.kv_heads;
   const int b = (int)(unit % a.batch);
   const int layer = (int)(unit / a.batch);
-  const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+  /* the wave index is uniform within a wave: say so, so that tile indices
+   * and load bases live in scalar registers */
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64), lane = threadIdx.x % 64;
   const int q4 = lane / 16, n = lane % 16;
 
   if constexpr (KTab<BK>::SPLIT)
-    fill_pairs(lut_k, a.lut_k, a.lut_k_lo, KTab<BK>::ENTRIES, 1);
+    fill_pairs<KTab<BK>::ENTRIES, kWaves>(lut_k, a.lut_k, a.lut_k_lo, 1);
   else
-    fill_words(lut_k, a.lut_k, KTab<BK>::ENTRIES);
+    fill_words<KTab<BK>::ENTRIES, kWaves>(lut_k, a.lut_k);
   if constexpr (VTab<BV>::QUAD)
-    fill_pairs(lut_v, a.lut_v_quad, a.lut_v_quad + 1, VTab<BV>::ENTRIES, 2);
+    fill_pairs<VTab<BV>::ENTRIES, kWaves>(lut_v, a.lut_v_quad, a.lut_v_quad + 1, 2);
   else
-    fill_words(lut_v, a.lut_v, VTab<BV>::ENTRIES);
+    fill_words<VTab<BV>::ENTRIES, kWaves>(lut_v, a.lut_v);
   /* rotated queries: qbuf[g][i] = (D q_g)_i, then FWHT, then scale */
   const uint8_t* sb = a.sign_bits + (int64_t)layer * (D / 8);
   const uint16_t* qg = a.q + (((int64_t)layer * a.batch + b) * a.q_heads + (int64_t)kv * G) * D;
@@ -462,11 +519,14 @@ decode_kernel(DecArgs a) {
   if (t_end > ntiles) t_end = ntiles;
 
   const int64_t sh = (int64_t)b * a.kv_heads + kv;
-  const uint8_t* kbase = a.k_codes + layer * a.ls_kc + sh * a.capacity * DG::RB + q4 * DG::KB;
-  const uint8_t* vbase = a.v_codes + layer * a.ls_vc + sh * (a.capacity / 32) * DG::TILE +
-                         lane * DG::SEG;
-  const uint16_t* knb = (const uint16_t*)(a.k_norms + layer * a.ls_kn) + sh * a.capacity + 4 * q4;
-  const uint16_t* vnb = (const uint16_t*)(a.v_norms + layer * a.ls_vn) + sh * a.capacity + 4 * q4;
+  TileAddr ad;
+  ad.k = a.k_codes + layer * a.ls_kc + sh * a.capacity * DG::RB;
+  ad.v = a.v_codes + layer * a.ls_vc + sh * (a.capacity / 32) * DG::TILE;
+  ad.kn = a.k_norms + layer * a.ls_kn + sh * a.capacity * 2;
+  ad.vn = a.v_norms + layer * a.ls_vn + sh * a.capacity * 2;
+  ad.koff = (uint32_t)(n * DG::RB + q4 * DG::KB);
+  ad.voff = (uint32_t)(lane * DG::SEG);
+  ad.noff = (uint32_t)(8 * q4);
   const uint32_t lo = (uint32_t)lane << 2;           /* value tables, 4-byte entries */
   const uint32_t lo8 = (uint32_t)(lane & 31) << 3;   /* value tables, 8-byte entries */
   const uint32_t lok = (KTab<BK>::SPLIT ? lo8 : lo) | KPAGE; /* key table */
@@ -475,7 +535,9 @@ decode_kernel(DecArgs a) {
   floatx4 acc[DG::VM];
 #pragma unroll
   for (int m = 0; m < DG::VM; ++m) acc[m] = floatx4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -1e30f, l_run = 0.0f;
+  /* running max (base 2) of this wave's scores, set by its first tile */
+  float m_run = 0.0f, l_run = 0.0f;
+  bool first = true;
 
   /* full tiles, software-pipelined: the loads of the next tiles are in
    * flight while this one is scored and accumulated (a ring of register
@@ -485,15 +547,15 @@ decode_kernel(DecArgs a) {
    * about to be used. */
   const int full_end = (len / 32) < t_end ? (len / 32) : t_end;
   int tile = t_begin + wave;
-  constexpr int W = kWaves;
+  constexpr int W = kWaves;  /* tile stride between a wave's tiles */
   if (tile < full_end) {
     const int last = full_end - 1;
     auto pf = [&](TileRegs<DG>& r, int t) {
-      load_tile<DG>(r, kbase, vbase, knb, vnb, t < last ? t : last, n);
+      load_tile<DG>(r, ad, t < last ? t : last);
     };
     auto step = [&](const TileRegs<DG>& r) {
       tile_step<DG, BK, BV, false>(r, bq, lut_k_rd, lut_v, lo, lo8, lok, lo_col, acc, m_run,
-                                   l_run, tile * 32, len, q4);
+                                   l_run, first, tile * 32, len, q4);
     };
     if constexpr (DG::DEPTH == 3) {
       TileRegs<DG> ra, rb, rc;
@@ -526,10 +588,11 @@ decode_kernel(DecArgs a) {
   /* the ragged last tile, if this wave owns it */
   if (tile < t_end) {
     TileRegs<DG> rp;
-    load_tile<DG>(rp, kbase, vbase, knb, vnb, tile, n);
+    load_tile<DG>(rp, ad, tile);
     tile_step<DG, BK, BV, true>(rp, bq, lut_k_rd, lut_v, lo, lo8, lok, lo_col, acc, m_run, l_run,
-                                tile * 32, len, q4);
+                                first, tile * 32, len, q4);
   }
+  if (first) m_run = -1e30f; /* no tiles: contributes nothing to the merge */
   l_run = rows_sum(l_run);
   /* value sums: column g (< 8) += column g + 8 (the fp16 remainders of p m) */
 #pragma unroll
@@ -644,7 +707,7 @@ decode_kernel(DecArgs a) {
 template <int D, int BK, int BV>
 tq_status launch_decode_t(const DecArgs& a, hipStream_t s) {
   const int64_t blocks = (int64_t)a.n_layers * a.batch * a.kv_heads * a.splits;
-  hipLaunchKernelGGL((decode_kernel<D, BK, BV>), dim3((unsigned)blocks), dim3(64 * kWaves), 0, s,
+  hipLaunchKernelGGL((decode_kernel<D, BK, BV>), dim3((unsigned)blocks), dim3(64 * waves_for(D, BK, BV)), 0, s,
                      a);
   return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_DEVICE;
 }
@@ -660,7 +723,7 @@ int concurrent_blocks_t() {
     int dev = 0, cus = 0, per = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, decode_kernel<D, BK, BV>, 64 * kWaves,
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, decode_kernel<D, BK, BV>, 64 * waves_for(D, BK, BV),
                                                      0) != hipSuccess ||
         cus <= 0 || per <= 0) {
       (void)hipGetLastError();
@@ -691,7 +754,8 @@ tq_decode_plan tq_plan_decode(const tq_kv_cache* c, int q_heads, int max_len, in
   const int64_t units = (int64_t)n_layers * c->batch * c->kv_heads;
   const int tiles = (max_len + 31) / 32;
   const int64_t conc = concurrent_blocks(c->head_dim, c->bits_k, c->bits_v);
-  int max_splits = tiles / (2 * kWaves);
+  const int waves = waves_for(c->head_dim, c->bits_k, c->bits_v);
+  int max_splits = tiles / (2 * waves);
   if (max_splits > 64) max_splits = 64;
   if (max_splits < 1) max_splits = 1;
   int splits = 1;
