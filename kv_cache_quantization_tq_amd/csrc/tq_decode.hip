@@ -225,7 +225,6 @@ __device__ inline float rows_sum(float v) {
 }
 
 __device__ inline float h2f(uint32_t h) { return (float)__builtin_bit_cast(_Float16, (uint16_t)h); }
-__device__ inline uint32_t f2h(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
 
 template <int D, int BK, int BV>
 struct DecGeo {

@@ -4,27 +4,42 @@
  * Per vector ("We Built a Python Library That Cuts LLM Memory Usage by 80%",
  * "The Paper"; AdapTQ page, "How it works (HAR + VQ)", steps 1-2):
  *   n   = ||x|| (fp16, correctly rounded)
- *   h   = H D x (fast Walsh-Hadamard transform, unnormalised)
+ *   h   = H D x (Walsh-Hadamard transform of the sign-flipped vector,
+ *         unnormalised)
  *   y_i = h_i / (sqrt(d) n)            rotated unit vector, ~N(0, 1/d)
  *   code_i = #{k : t_k < y_i}          Lloyd-Max thresholds t_k
  *
- * Work layout: 32 coordinates per lane, d/32 lanes per vector, 2048/d
- * vectors per wave pass.  A pass reads its vectors with fully coalesced
- * 128-bit loads, XORs the sign flip D into the fp16 sign bits and writes them
- * to a padded LDS stage, from which each lane reads back its own 64 bytes; the
- * next pass's loads are issued before this pass is computed.  The FWHT runs
- * five stages inside the lane's registers and the rest across the lanes of a
- * vector (DPP quad permutes, ds_swizzle for the eighth-lane stage).
+ * Work layout.  A wave pass encodes 16 vectors.  Lane (q4, n) = (lane / 16,
+ * lane % 16) holds coordinates 32 j + 8 q4 .. 32 j + 8 q4 + 7 of vector n for
+ * every 32-coordinate block j (one 16-byte load per block), XORs the sign
+ * flip D into their fp16 sign bits and squares them for the norm.
  *
- * Norm: sum of exact fp32 squares (4 chains of 8, then a tree), <= 13 roundings,
- * so |S32 - S| <= 13 * 2^-24 S.  The fp16 candidate is accepted when S32 is
- * far enough from both rounding midpoints; otherwise the vector's fp16 inputs
- * are re-summed in fp64 and, if still ambiguous, exactly in 128-bit integers.
+ * The transform runs on the matrix cores (v_mfma_f32_16x16x32_f16) as the
+ * product H_d X, X the pass's 16 vectors as columns.  A 16 x 32 tile of H_d
+ * (output rows 16 ob .. 16 ob + 15, input columns 32 j .. 32 j + 31) is, with
+ * Sylvester's H[r][c] = (-1)^popcount(r & c),
+ *   (-1)^popcount((ob >> 1) & j) * T_(ob & 1),
+ *   T_h[r][k] = (-1)^(popcount(r & k) + h * (k >> 4)),  r < 16, k < 32,
+ * so two constant +-1 operands (and their negations) serve the whole matrix:
+ * d/16 * d/32 products per pass, accumulated in fp32 from exact fp16 inputs.
+ * Lane (q4, n) then holds transformed coordinates 16 ob + 4 q4 + i (i < 4) of
+ * vector n.
  *
- * Quantizer: u = (y + 1) * nb_half + 1 = fma(h, scale, nb_half + 1) selects one of the
- * codebook's buckets in LDS (at most one threshold per bucket), code = base +
- * (u > thr).  The comparison happens in fp32 on u; it differs from the exact
- * decision only for coordinates within ~1e-7 of a threshold.
+ * Norm: sum of exact fp32 squares (4 chains, then a tree and a 4-lane sum),
+ * at most 2 d/32 + 3 roundings, so |S32 - S| stays below norm_del(d) S.  The
+ * fp16 candidate is accepted when S32 is far enough from both rounding
+ * midpoints; otherwise the inputs are re-summed in fp64 and, if still
+ * ambiguous, exactly in 128-bit integers.
+ *
+ * Quantizer: u = (y + 1) * nb_half + 1 = fma(h, scale, nb_half + 1) selects
+ * one of the codebook's buckets in LDS (at most one threshold per bucket),
+ * code = base + (u > thr).  The comparison happens in fp32 on u; it differs
+ * from the exact decision only for coordinates within ~1e-7 of a threshold.
+ *
+ * Output.  Key rows: the four lanes of a vector exchange their 4-code pieces
+ * with 4 x 4 word transposes (permlane swaps), after which each lane owns d/4
+ * consecutive coordinates and stores them packed.  Value tiles: code bytes go
+ * to an LDS tile buffer from which the tile's 64 segments are built.
  */
 #include <hip/hip_runtime.h>
 
@@ -35,25 +50,49 @@ namespace {
 #ifndef TQ_ENC_WPE
 #define TQ_ENC_WPE 3 /* registers for at least this many waves per SIMD */
 #endif
-constexpr int kPitch = 80;   /* LDS bytes per lane's 64-byte chunk, padded */
-constexpr int kEncRep = 16;  /* copies of the bucket table (lane % 16): conflict-free 64-bit reads */
 
-__device__ inline void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-/* Butterfly partners: DPP quad permutes for lane xor 1 and xor 2, ds_swizzle
- * (bit mode) for lane xor 4. */
-__device__ inline float xor1(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, true));
+constexpr int kVec = 16;     /* vectors per wave pass (the matrix-core N) */
+constexpr int kEncRep = 32;  /* copies of the bucket table (lane % 32): a 64-bit LDS read
+                                serves 32 lanes per cycle, each on its own pair of banks */
+
+template <int D>
+struct EGeo {
+  static constexpr int J = D / 32;  /* 32-coordinate input blocks */
+  static constexpr int OB = D / 16; /* 16-coordinate output blocks */
+  static constexpr int T = OB / 4;  /* output blocks per lane of a row chunk */
+};
+
+/* Relative error bound used by the fp32 norm test: the sum has at most
+ * 2 J + 3 roundings (chains of 2 J fmas, a 2-level tree, a 4-lane sum); one
+ * more for the scaled comparison, and a margin. */
+template <int D>
+constexpr float norm_del() { return (float)(2 * (D / 32) + 6) * 5.9604645e-8f; }
+
+/* Sums over the four lanes n, n + 16, n + 32, n + 48 (one vector's lanes). */
+__device__ inline float col_sum(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
-__device__ inline float xor2(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, true));
-}
-__device__ inline float xor4(float v) {
-  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), (4 << 10) | 0x1F));
+__device__ inline double col_sum_f64(double v) {
+  uint64_t u = __builtin_bit_cast(uint64_t, v);
+  uint32_t lo = (uint32_t)u, hi = (uint32_t)(u >> 32);
+  auto a = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+  auto b = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+  v = __builtin_bit_cast(double, (uint64_t)a[0] | ((uint64_t)b[0] << 32)) +
+      __builtin_bit_cast(double, (uint64_t)a[1] | ((uint64_t)b[1] << 32));
+  u = __builtin_bit_cast(uint64_t, v);
+  lo = (uint32_t)u;
+  hi = (uint32_t)(u >> 32);
+  auto c = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+  auto e = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+  return __builtin_bit_cast(double, (uint64_t)c[0] | ((uint64_t)e[0] << 32)) +
+         __builtin_bit_cast(double, (uint64_t)c[1] | ((uint64_t)e[1] << 32));
 }
 
 __device__ inline float half_lo(uint32_t w) {
@@ -66,67 +105,15 @@ __device__ inline float half_bits_to_float(uint32_t h) {
   return (float)__builtin_bit_cast(_Float16, (uint16_t)h);
 }
 
-template <int D>
-struct Geo {
-  static constexpr int LPV = D / 32;   /* lanes per vector */
-  static constexpr int VPW = 64 / LPV; /* vectors per wave pass */
-  static constexpr int CPR = D / 8;    /* 16-byte chunks per vector */
-};
-
-/* Per-lane XOR masks for the sign flip: every staging load of this lane
- * handles chunk (lane % CPR), coordinates 8*ch .. 8*ch+7. */
-template <int D>
-__device__ inline void sign_masks(const uint8_t* sign_bits, int lane, uint32_t (&m)[4]) {
-  const int ch = lane % Geo<D>::CPR;
-  const uint32_t b = sign_bits[ch];
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-    m[j] = (((b >> (2 * j)) & 1u) << 15) | (((b >> (2 * j + 1)) & 1u) << 31);
-}
-
-/* Global loads of one pass: vectors v in [vlo, vhi) at base + v * stride
- * elements; chunk c = 64 k + lane.  Vectors outside the range read as zero. */
-template <int D>
-__device__ inline void pass_load(const uint16_t* base, int64_t stride, int vlo, int vhi,
-                                 uint4 (&g)[4], int lane) {
-  using G = Geo<D>;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int c = 64 * k + lane;
-    const int v = c / G::CPR, ch = c % G::CPR;
-    g[k] = make_uint4(0u, 0u, 0u, 0u);
-    if (v >= vlo && v < vhi) g[k] = *(const uint4*)(base + (int64_t)v * stride + ch * 8);
-  }
-}
-
-/* Sign-flip the loaded chunks and put them in the wave's stage: lane
- * owner = v * LPV + ch / 4 receives chunk ch at (ch % 4) * 16. */
-template <int D>
-__device__ inline void pass_stage(const uint4 (&g)[4], const uint32_t (&sm)[4], char* stage,
-                                  int lane) {
-  using G = Geo<D>;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int c = 64 * k + lane;
-    const int v = c / G::CPR, ch = c % G::CPR;
-    uint4 val = g[k];
-    val.x ^= sm[0];
-    val.y ^= sm[1];
-    val.z ^= sm[2];
-    val.w ^= sm[3];
-    *(uint4*)(stage + (v * G::LPV + ch / 4) * kPitch + (ch % 4) * 16) = val;
-  }
-}
-
 /* fp16 value of a non-negative pattern; 0x7C00 stands for 65536 here. */
 __device__ inline float half_pos(uint32_t p) {
   return p >= 0x7C00u ? 65536.0f : half_bits_to_float(p);
 }
 
 /* Accept the candidate RNE(sqrt(S)) only if S (with relative error below
- * del) lies strictly inside its rounding interval. */
-__device__ inline bool norm16_check_f32(float S, uint32_t* out) {
-  const float del = 4.0e-6f;
+ * del) lies strictly inside its rounding interval.  Midpoints of fp16
+ * neighbours have at most 12 significant bits, so their squares are exact. */
+__device__ inline bool norm16_check_f32(float S, float del, uint32_t* out) {
   if (S == 0.0f) { *out = 0; return true; }
   uint32_t p = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)__builtin_sqrtf(S));
   if (p > 0x7C00u) p = 0x7C00u;
@@ -199,169 +186,236 @@ __device__ inline uint32_t norm16_exact(unsigned __int128 S, uint32_t p) {
   return p;
 }
 
-/* Exact fp16 norm of vector v of the pass from the LDS stage, by 128-bit
+/* Exact fp16 norm of the D fp16 values at vec (global memory), by 128-bit
  * integer sums; reached only when even the fp64 sum sits within 1e-13 of a
- * rounding midpoint (exact ties).  Kept out of line: it needs registers the
- * hot path should not reserve.  Signs were flipped during staging; squares
- * do not care. */
+ * rounding midpoint (exact ties).  Kept out of line. */
 template <int D>
-__device__ __attribute__((noinline)) uint32_t norm16_exact_stage(const char* stage, int v,
-                                                                 uint32_t guess) {
-  using G = Geo<D>;
+__device__ __attribute__((noinline)) uint32_t norm16_exact_global(const uint16_t* vec,
+                                                                  uint32_t guess) {
   unsigned __int128 E = 0;
-  for (int p = 0; p < G::LPV; ++p)
-    for (int j = 0; j < 16; ++j) {
-      const uint32_t w = *(const uint32_t*)(stage + (v * G::LPV + p) * kPitch + 4 * j);
-      const unsigned __int128 a = half_units(w & 0x7FFFu), b = half_units((w >> 16) & 0x7FFFu);
-      E += a * a + b * b;
-    }
+  for (int i = 0; i < D; ++i) {
+    const unsigned __int128 a = half_units(vec[i] & 0x7FFFu);
+    E += a * a;
+  }
   return norm16_exact(E, guess);
 }
 
-/* fp64 re-sum of vector v from the stage (rare), then the exact fallback. */
-template <int D>
-__device__ inline uint32_t norm16_slow(const char* stage, int v) {
-  using G = Geo<D>;
-  double S = 0.0;
-#pragma unroll 1
-  for (int k = 0; k < 16 * G::LPV; ++k) {
-    const uint32_t w = *(const uint32_t*)(stage + (v * G::LPV + k / 16) * kPitch + 4 * (k % 16));
-    const double a = (double)half_lo(w), b = (double)half_hi(w);
-    S = __builtin_fma(a, a, S);
-    S = __builtin_fma(b, b, S);
-  }
-  uint32_t n16;
-  if (norm16_check_f64(S, &n16)) return n16;
-  return norm16_exact_stage<D>(stage, v, n16);
+/* Word w of a uint4. */
+__device__ inline uint32_t u4w(const uint4& u, int w) {
+  return w == 0 ? u.x : (w == 1 ? u.y : (w == 2 ? u.z : u.w));
 }
 
-/* a + b and a - b of the two fp16 halves of w, in fp32 (one mixed-precision
- * FMA each: a * 1 + (+-b)). */
-__device__ inline void half_pair_sum_diff(uint32_t w, float* sum, float* diff) {
-  float s, d;
-  asm("v_fma_mix_f32 %0, %1, 1.0, %1 op_sel:[0,0,1] op_sel_hi:[1,0,1]" : "=v"(s) : "v"(w));
-  asm("v_fma_mix_f32 %0, %1, 1.0, -%1 op_sel:[0,0,1] op_sel_hi:[1,0,1]" : "=v"(d) : "v"(w));
-  *sum = s;
-  *diff = d;
-}
-
-/* Encode the lane's 32 coordinates of its vector (data in the LDS stage).
- * Returns the packed codes (BITS words) and the vector's fp16 norm, the same
- * on all lanes of the vector.
- *
- * Cross-lane butterflies: each lane computes own + c * partner with
- * c = -1 on the lane whose index bit is set, one DPP-fused FMA per value; the
- * upper lane then holds the negated a - b, so lane values carry the sign
- * (-1)^popcount(lane bits), folded into the quantizer scale. */
-template <int D, int BITS>
-__device__ inline void encode_lane(const char* stage, const tq_enc_entry* table, float nbh,
-                                   int lane, uint32_t (&packed)[BITS], uint32_t* n16_out,
-                                   bool* sure_out) {
-  using G = Geo<D>;
-  uint32_t w[16];
+/* Matrix operands T_0, T_1 of the transform and their negations, as held by
+ * lane (q4, n): row n, columns 8 q4 .. 8 q4 + 7. */
+struct HTiles {
+  half8 p[2], m[2];
+};
+__device__ inline HTiles h_tiles(int n, int q4) {
+  HTiles t;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const uint4 t = *(const uint4*)(stage + lane * kPitch + 16 * j);
-    w[4 * j] = t.x;
-    w[4 * j + 1] = t.y;
-    w[4 * j + 2] = t.z;
-    w[4 * j + 3] = t.w;
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int k = 8 * q4 + r;
+      const int par = (__builtin_popcount(n & k & 15) + h * (k >> 4)) & 1;
+      t.p[h][r] = par ? (_Float16)-1.0f : (_Float16)1.0f;
+      t.m[h][r] = par ? (_Float16)1.0f : (_Float16)-1.0f;
+    }
+  return t;
+}
+
+/* Sign-flip masks of lane (q4, .): block j's coordinates 32 j + 8 q4 .. +7
+ * are byte 4 j + q4 of the layer's sign bits; word w holds two of them. */
+template <int D>
+__device__ inline void sign_masks(const uint8_t* sb, int q4, uint32_t (&m)[EGeo<D>::J][4]) {
+#pragma unroll
+  for (int j = 0; j < EGeo<D>::J; ++j) {
+    const uint32_t b = sb[4 * j + q4];
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      m[j][w] = (((b >> (2 * w)) & 1u) << 15) | (((b >> (2 * w + 1)) & 1u) << 31);
   }
-  float v[32];
+}
+
+/* One pass's input registers: block j's 8 fp16 values of the lane's vector. */
+template <int D>
+struct XRegs {
+  uint4 w[EGeo<D>::J];
+};
+
+template <int D>
+__device__ inline void load_x(XRegs<D>& x, const uint16_t* vec, int q4) {
+#pragma unroll
+  for (int j = 0; j < EGeo<D>::J; ++j) x.w[j] = *(const uint4*)(vec + 32 * j + 8 * q4);
+}
+
+/* Encode the pass held in xr.  Columns without a vector of their own hold a
+ * copy of a real row (loads are clamped), which is encoded and discarded, so
+ * the pass needs no masking; vec: the column's fp16 values in global memory
+ * (read only by the exact-tie fallback).  piece[ob] receives the codes of
+ * coordinates 16 ob + 4 q4 + i, i < 4: BITS bits each (first lowest), or one
+ * byte each when BYTES.  Returns the fp16 norm (the same on the vector's four
+ * lanes). */
+template <int D, int BITS, bool BYTES>
+__device__ inline uint32_t encode_pass(const XRegs<D>& xr,
+                                       const uint32_t (&sm)[EGeo<D>::J][4], const HTiles& ht,
+                                       const char* tab, float nbh, const uint16_t* vec,
+                                       uint32_t (&piece)[EGeo<D>::OB]) {
+  using G = EGeo<D>;
+  uint32_t x[G::J][4];
+#pragma unroll
+  for (int j = 0; j < G::J; ++j)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) x[j][w] = u4w(xr.w[j], w) ^ sm[j][w];
+
+  /* norm: exact fp32 squares, 4 chains */
   float sq[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    half_pair_sum_diff(w[j], &v[2 * j], &v[2 * j + 1]);
-    const float a = half_lo(w[j]), b = half_hi(w[j]);
-    sq[j & 3] = __builtin_fmaf(a, a, sq[j & 3]);
-    sq[j & 3] = __builtin_fmaf(b, b, sq[j & 3]);
-  }
+  for (int j = 0; j < G::J; ++j)
 #pragma unroll
-  for (int h = 2; h < 32; h <<= 1) {
+    for (int w = 0; w < 4; ++w) {
+      const float a = half_lo(x[j][w]), b = half_hi(x[j][w]);
+      sq[w] = __builtin_fmaf(a, a, sq[w]);
+      sq[w] = __builtin_fmaf(b, b, sq[w]);
+    }
+  const float S = col_sum((sq[0] + sq[1]) + (sq[2] + sq[3]));
+  uint32_t n16;
+  const bool sure = norm16_check_f32(S, norm_del<D>(), &n16);
+  if (__builtin_expect(__any(!sure), 0)) {
+    /* rare: fp64 from the registers, then exact integers from memory */
+    double s64 = 0.0;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      if (!(i & h)) {
-        const float a = v[i], b = v[i + h];
-        v[i] = a + b;
-        v[i + h] = a - b;
+    for (int j = 0; j < G::J; ++j)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const double a = (double)half_lo(x[j][w]), b = (double)half_hi(x[j][w]);
+        s64 = __builtin_fma(a, a, s64);
+        s64 = __builtin_fma(b, b, s64);
       }
+    s64 = col_sum_f64(s64);
+    if (!sure) {
+      uint32_t p64;
+      if (norm16_check_f64(s64, &p64))
+        n16 = p64;
+      else
+        n16 = norm16_exact_global<D>(vec, p64);
     }
   }
-  float S = (sq[0] + sq[1]) + (sq[2] + sq[3]);
-  float sigma = 1.0f;
-  if constexpr (G::LPV >= 2) {
-    const float c = (lane & 1) ? -1.0f : 1.0f;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) v[i] = __builtin_fmaf(xor1(v[i]), c, v[i]);
-    S += xor1(S);
-    sigma *= c;
-  }
-  if constexpr (G::LPV >= 4) {
-    const float c = (lane & 2) ? -1.0f : 1.0f;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) v[i] = __builtin_fmaf(xor2(v[i]), c, v[i]);
-    S += xor2(S);
-    sigma *= c;
-  }
-  if constexpr (G::LPV >= 8) {
-    const float c = (lane & 4) ? -1.0f : 1.0f;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) v[i] = __builtin_fmaf(xor4(v[i]), c, v[i]);
-    S += xor4(S);
-    sigma *= c;
-  }
-  uint32_t n16;
-  const bool sure = norm16_check_f32(S, &n16);
 
-  /* u = (y + 1) * nbh + 1 with y = h / (sqrt(d) * ||x||); bucket floor(u) */
-  const float scale = S > 0.0f ? sigma * nbh * __builtin_amdgcn_rsqf(S * (float)D) : 0.0f;
+  /* H_d X on the matrix cores, one 16-coordinate output block at a time */
+  half8 b[G::J];
+#pragma unroll
+  for (int j = 0; j < G::J; ++j)
+    b[j] = __builtin_bit_cast(half8, u32x4{x[j][0], x[j][1], x[j][2], x[j][3]});
+  const float scale = S > 0.0f ? nbh * __builtin_amdgcn_rsqf(S * (float)D) : 0.0f;
   const float off = nbh + 1.0f;
-  const char* tab = (const char*)table + (lane & (kEncRep - 1)) * sizeof(tq_enc_entry);
 #pragma unroll
-  for (int k = 0; k < BITS; ++k) packed[k] = 0u;
+  for (int ob = 0; ob < G::OB; ++ob) {
+    floatx4 y = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    /* bound how far the scheduler hoists table reads (registers) */
-    if (i % 8 == 0) __builtin_amdgcn_sched_barrier(0);
-    const float u = __builtin_fmaf(v[i], scale, off);
-    const uint32_t b = (uint32_t)u;
-    const tq_enc_entry e = *(const tq_enc_entry*)(tab + b * (kEncRep * sizeof(tq_enc_entry)));
-    const uint32_t code = e.base + (u > e.thr ? 1u : 0u);
-    const int bit = BITS * i;
-    packed[bit / 32] |= code << (bit % 32);
-    if ((bit % 32) + BITS > 32) packed[bit / 32 + 1] |= code >> (32 - bit % 32);
+    for (int j = 0; j < G::J; ++j) {
+      const bool neg = __builtin_popcount((ob >> 1) & j) & 1;
+      y = __builtin_amdgcn_mfma_f32_16x16x32_f16(neg ? ht.m[ob & 1] : ht.p[ob & 1], b[j], y, 0,
+                                                 0, 0);
+    }
+    /* quantize: u = (y + 1) * nbh + 1, bucket floor(u) */
+    uint32_t pc = 0u;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float u = __builtin_fmaf(y[i], scale, off);
+      const uint32_t bk = (uint32_t)u;
+      const tq_enc_entry e = *(const tq_enc_entry*)(tab + bk * (kEncRep * sizeof(tq_enc_entry)));
+      const uint32_t code = e.base + (u > e.thr ? 1u : 0u);
+      pc |= code << (BYTES ? 8 * i : BITS * i);
+    }
+    piece[ob] = pc;
   }
-  *n16_out = n16;
-  *sure_out = sure;
+  return n16;
 }
 
-/* The vector's fp16 norm once its codes are stored (the codes do not depend
- * on it): the rare undecided candidates are settled here, where the
- * coordinates are no longer live. */
-template <int D>
-__device__ inline uint32_t settle_norm(const char* stage, int lane, uint32_t n16, bool sure) {
-  return sure ? n16 : norm16_slow<D>(stage, lane / Geo<D>::LPV);
+/* OR the w-bit value v into the bit string out at bit position pos. */
+template <int NW>
+__device__ inline void put_bits(uint32_t (&out)[NW], int pos, uint32_t v, int w) {
+  out[pos / 32] |= v << (pos % 32);
+  if ((pos % 32) + w > 32 && pos / 32 + 1 < NW) out[pos / 32 + 1] |= v >> (32 - pos % 32);
+}
+
+/* 4 x 4 transpose of 32-bit words over a vector's four lanes: before, lane q
+ * holds r[q'] for every q'; after, lane q' holds in r[q] what lane q held in
+ * r[q']. */
+__device__ inline void transpose4(uint32_t (&r)[4]) {
+  auto s0 = __builtin_amdgcn_permlane32_swap(r[0], r[2], false, false);
+  auto s1 = __builtin_amdgcn_permlane32_swap(r[1], r[3], false, false);
+  r[0] = s0[0];
+  r[2] = s0[1];
+  r[1] = s1[0];
+  r[3] = s1[1];
+  auto s2 = __builtin_amdgcn_permlane16_swap(r[0], r[1], false, false);
+  auto s3 = __builtin_amdgcn_permlane16_swap(r[2], r[3], false, false);
+  r[0] = s2[0];
+  r[1] = s2[1];
+  r[2] = s3[0];
+  r[3] = s3[1];
+}
+
+/* Words of a lane's packed row chunk (d/4 coordinates of BITS bits). */
+template <int D, int BITS>
+struct Chunk {
+  static constexpr int BYTES = D * BITS / 32;
+  static constexpr int NW = (BYTES + 3) / 4;
+};
+
+/* Key-row output: afterwards lane (q4, n) holds the packed codes of
+ * coordinates q4 d/4 .. (q4 + 1) d/4 - 1 of vector n (first code lowest).
+ * Lane q sends lane q' its pieces of output blocks q' T .. q' T + T - 1, two
+ * per word. */
+template <int D, int BITS>
+__device__ inline void gather_row_chunk(const uint32_t (&piece)[EGeo<D>::OB],
+                                        uint32_t (&out)[Chunk<D, BITS>::NW]) {
+  constexpr int T = EGeo<D>::T, PB = 4 * BITS;
+  constexpr int NWT = (T + 1) / 2; /* transposed words per lane pair */
+#pragma unroll
+  for (int k = 0; k < Chunk<D, BITS>::NW; ++k) out[k] = 0u;
+#pragma unroll
+  for (int k = 0; k < NWT; ++k) {
+    uint32_t r[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int t0 = 2 * k, t1 = 2 * k + 1;
+      r[q] = piece[q * T + t0] | (t1 < T ? piece[q * T + t1] << 16 : 0u);
+    }
+    transpose4(r);
+    /* r[q]: lane q's pieces of blocks q' T + 2k (low half), + 2k + 1 (high);
+     * coordinate 16 t + 4 q + i of the chunk sits at bit BITS (16 t + 4 q + i) */
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      put_bits(out, 16 * BITS * (2 * k) + PB * q, r[q] & 0xFFFFu, PB);
+      if (2 * k + 1 < T) put_bits(out, 16 * BITS * (2 * k + 1) + PB * q, r[q] >> 16, PB);
+    }
+  }
+}
+
+/* Store a lane's packed row chunk at dst (dst aligned to 8 bytes when the
+ * chunk size is a multiple of 8, else to 2). */
+template <int D, int BITS>
+__device__ inline void store_chunk(uint8_t* dst, const uint32_t (&p)[Chunk<D, BITS>::NW]) {
+  constexpr int NB = Chunk<D, BITS>::BYTES;
+  if constexpr (NB % 8 == 0) {
+#pragma unroll
+    for (int k = 0; k < NB / 8; ++k) *(uint2*)(dst + 8 * k) = make_uint2(p[2 * k], p[2 * k + 1]);
+  } else if constexpr (NB % 4 == 0) {
+#pragma unroll
+    for (int k = 0; k < NB / 4; ++k) *(uint32_t*)(dst + 4 * k) = p[k];
+  } else {
+#pragma unroll
+    for (int k = 0; k < NB / 2; ++k)
+      *(uint16_t*)(dst + 2 * k) = (uint16_t)(p[k / 2] >> (16 * (k & 1)));
+  }
 }
 
 /* Copy the bucket table into LDS, kEncRep interleaved copies. */
 __device__ inline void load_table(tq_enc_entry* dst, const tq_enc_entry* src, int entries) {
   for (int i = threadIdx.x; i < entries * kEncRep; i += blockDim.x) dst[i] = src[i / kEncRep];
-}
-
-/* Store a lane's 4*BITS bytes of codes at dst (4-byte aligned; 8 for BITS 2,
- * 16 for BITS 4). */
-template <int BITS>
-__device__ inline void store_packed(uint8_t* dst, const uint32_t (&p)[BITS]) {
-  if constexpr (BITS == 4) {
-    *(uint4*)dst = make_uint4(p[0], p[1], p[2], p[3]);
-  } else if constexpr (BITS == 2) {
-    *(uint2*)dst = make_uint2(p[0], p[1]);
-  } else {
-    uint32_t* d = (uint32_t*)dst;
-    d[0] = p[0];
-    d[1] = p[1];
-    d[2] = p[2];
-  }
 }
 
 __host__ __device__ inline int table_bytes(int entries) {
@@ -371,48 +425,59 @@ __host__ __device__ inline int table_bytes(int entries) {
 constexpr int kRowsWaves = 4;
 
 /* tq_encode: n vectors, row layout.  Each wave takes passes grid-stride and
- * loads the next pass while it encodes the current one. */
+ * loads the next pass while it encodes the current one (loads are issued
+ * on every path, clamped to real rows, so waits cover only the pass in use). */
 template <int D, int BITS>
-__global__ void __launch_bounds__(64 * kRowsWaves) __attribute__((amdgpu_waves_per_eu(TQ_ENC_WPE)))
+__global__ void __launch_bounds__(64 * kRowsWaves) __attribute__((amdgpu_waves_per_eu(D == 256 ? 2 : TQ_ENC_WPE)))
 encode_rows_kernel(const uint16_t* __restrict__ x, int64_t n, int64_t stride,
                    const uint8_t* __restrict__ sign_bits, const tq_enc_entry* __restrict__ table,
                    int entries, float nbh, uint8_t* __restrict__ codes,
                    uint16_t* __restrict__ norms) {
-  using G = Geo<D>;
+  using G = EGeo<D>;
   extern __shared__ __align__(16) char smem[];
   tq_enc_entry* tab = (tq_enc_entry*)smem;
-  const int lane = threadIdx.x % 64;
-  char* stage = smem + table_bytes(entries) + (threadIdx.x / 64) * 64 * kPitch;
+  const int lane = threadIdx.x % 64, q4 = lane / 16, nl = lane % 16;
   load_table(tab, table, entries);
   __syncthreads();
-  uint32_t sm[4];
-  sign_masks<D>(sign_bits, lane, sm);
-  const int64_t passes = (n + G::VPW - 1) / G::VPW;
+  const char* mytab = (const char*)tab + (lane & (kEncRep - 1)) * sizeof(tq_enc_entry);
+  uint32_t sm[G::J][4];
+  sign_masks<D>(sign_bits, q4, sm);
+  const HTiles ht = h_tiles(nl, q4);
+  const int64_t passes = (n + kVec - 1) / kVec;
   const int64_t wstride = (int64_t)gridDim.x * kRowsWaves;
-  int64_t ps = (int64_t)blockIdx.x * kRowsWaves + threadIdx.x / 64;
-  uint4 g[4];
-  if (ps < passes) {
-    const int64_t r0 = ps * G::VPW;
-    pass_load<D>(x + r0 * stride, stride, 0, (int)(n - r0 < G::VPW ? n - r0 : G::VPW), g, lane);
-  }
-  for (; ps < passes; ps += wstride) {
-    const int64_t row0 = ps * G::VPW;
-    const int nv = (int)(n - row0 < G::VPW ? n - row0 : G::VPW);
-    pass_stage<D>(g, sm, stage, lane);
-    wave_lds_sync();
-    const int64_t nx = ps + wstride;
-    if (nx < passes) {
-      const int64_t r1 = nx * G::VPW;
-      pass_load<D>(x + r1 * stride, stride, 0, (int)(n - r1 < G::VPW ? n - r1 : G::VPW), g, lane);
+  int64_t ps = (int64_t)blockIdx.x * kRowsWaves + __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
+  if (ps >= passes) return;
+  /* this lane's row in pass p, clamped to a real row */
+  auto row_of = [&](int64_t p) -> int64_t {
+    const int64_t r = p * kVec + nl;
+    return r < n ? r : n - 1;
+  };
+  auto body = [&](const XRegs<D>& xr, int64_t p) {
+    const int64_t r = p * kVec + nl;
+    const bool valid = r < n;
+    uint32_t piece[G::OB];
+    const uint32_t n16 = encode_pass<D, BITS, false>(xr, sm, ht, mytab, nbh,
+                                                     x + row_of(p) * stride, piece);
+    uint32_t out[Chunk<D, BITS>::NW];
+    gather_row_chunk<D, BITS>(piece, out);
+    if (valid) {
+      store_chunk<D, BITS>(codes + r * (D * BITS / 8) + q4 * Chunk<D, BITS>::BYTES, out);
+      if (q4 == 0) norms[r] = (uint16_t)n16;
     }
-    uint32_t packed[BITS], n16;
-    bool sure;
-    encode_lane<D, BITS>(stage, tab, nbh, lane, packed, &n16, &sure);
-    const int v = lane / G::LPV, part = lane % G::LPV;
-    if (v < nv) store_packed<BITS>(codes + (row0 + v) * (D * BITS / 8) + part * (4 * BITS), packed);
-    n16 = settle_norm<D>(stage, lane, n16, sure);
-    if (v < nv && part == 0) norms[row0 + v] = (uint16_t)n16;
-    wave_lds_sync(); /* the next pass overwrites the stage */
+  };
+  XRegs<D> xa, xb;
+  load_x<D>(xa, x + row_of(ps) * stride, q4);
+  for (;;) {
+    const int64_t p1 = ps + wstride;
+    load_x<D>(xb, x + row_of(p1 < passes ? p1 : ps) * stride, q4);
+    body(xa, ps);
+    ps = p1;
+    if (ps >= passes) break;
+    const int64_t p2 = ps + wstride;
+    load_x<D>(xa, x + row_of(p2 < passes ? p2 : ps) * stride, q4);
+    body(xb, ps);
+    ps = p2;
+    if (ps >= passes) break;
   }
 }
 
@@ -427,6 +492,7 @@ struct AppendArgs {
   uint16_t* v_norms;
   int64_t ls_kc, ls_vc, ls_kn, ls_vn; /* layer strides, bytes */
   int batch, heads, capacity, t_new, n_layers, slots;
+  int64_t chunk;                      /* tile pairs per block */
   const uint16_t* k_new;
   const uint16_t* v_new;
   const uint8_t* sign_bits;
@@ -437,14 +503,10 @@ struct AppendArgs {
   float nbh_k, nbh_v;
 };
 
-/* A 32-token tile takes WPT waves (VPW vectors each); a block of 4 waves
- * works on TPB tiles side by side. */
-template <int D>
-struct AppendGeo {
-  static constexpr int WPT = 32 / Geo<D>::VPW < 1 ? 1 : 32 / Geo<D>::VPW;
-  static constexpr int TPB = 4 / WPT;
-};
+/* A 32-token tile takes two waves (16 vectors each); a block of 4 waves
+ * works on two tiles side by side. */
 constexpr int kAppendWaves = 4;
+constexpr int kTPB = 2;
 
 /* Rows of tile `tile` receiving tokens of this append, [jlo, jhi). */
 __device__ inline bool tile_range(const AppendArgs& a, int p0, int tile, int* jlo, int* jhi) {
@@ -469,114 +531,111 @@ __device__ inline void task_coords(const AppendArgs& a, int64_t task, int* layer
   *layer = (int)(r / a.batch);
 }
 
-/* blockIdx.y = 0: keys (rows); 1: values (tiles).  Every wave loops over its
- * tasks grid-stride, loading the next task's vectors while encoding. */
+/* Geometry of one wave's part of a task. */
+struct TaskGeo {
+  bool live;
+  int layer, b, h, tile, jlo, jhi;
+  const uint16_t* src; /* fp16 input row of tile row j0 (the wave's first row) */
+};
+
+/* blockIdx.y = 0: keys (rows); 1: values (tiles).  Block k takes the tile
+ * pairs [k chunk, (k + 1) chunk) in order (consecutive tiles of a stream, so
+ * the layer and its sign flip rarely change), loading the next pair's
+ * vectors while encoding the current one. */
 template <int D, int BK, int BV>
-__global__ void __launch_bounds__(64 * kAppendWaves) __attribute__((amdgpu_waves_per_eu(TQ_ENC_WPE)))
+__global__ void __launch_bounds__(64 * kAppendWaves) __attribute__((amdgpu_waves_per_eu(D == 256 ? 2 : TQ_ENC_WPE)))
 append_kernel(AppendArgs a) {
-  using G = Geo<D>;
-  using AG = AppendGeo<D>;
+  using G = EGeo<D>;
   extern __shared__ __align__(16) char smem[];
   const bool is_v = blockIdx.y == 1;
   const int ent = is_v ? a.ent_v : a.ent_k;
   const int tb = table_bytes(a.ent_k > a.ent_v ? a.ent_k : a.ent_v);
   tq_enc_entry* tab = (tq_enc_entry*)smem;
-  const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
-  const int slot_in_block = wave / AG::WPT, sub = wave % AG::WPT;
-  char* stage = smem + tb + wave * 64 * kPitch;
-  uint8_t* vbuf = (uint8_t*)(smem + tb + kAppendWaves * 64 * kPitch) + slot_in_block * 32 * D;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64), lane = threadIdx.x % 64;
+  const int q4 = lane / 16, nl = lane % 16;
+  const int slot_in_block = wave / 2, sub = wave % 2;
+  uint8_t* vbuf = (uint8_t*)(smem + tb) + slot_in_block * 32 * D; /* tile codes [row][coord] */
   load_table(tab, is_v ? a.tab_v : a.tab_k, ent);
   __syncthreads();
+  const char* mytab = (const char*)tab + (lane & (kEncRep - 1)) * sizeof(tq_enc_entry);
   const float nbh = is_v ? a.nbh_v : a.nbh_k;
   const uint16_t* src_all = is_v ? a.v_new : a.k_new;
   const int64_t tasks = (int64_t)a.n_layers * a.batch * a.heads * a.slots;
-  const int64_t step = (int64_t)gridDim.x * AG::TPB;
-  const int j0 = sub * G::VPW; /* this wave's first tile row */
+  const int j0 = sub * kVec; /* this wave's first tile row */
+  const HTiles ht = h_tiles(nl, q4);
 
-  /* per-task geometry of this wave, and its prefetch */
-  auto setup = [&](int64_t task, int* layer, int* b, int* h, int* tile, int* jlo, int* jhi,
-                   const uint16_t** src) -> bool {
+  auto setup = [&](int64_t task) -> TaskGeo {
+    TaskGeo g;
+    g.live = false;
+    g.layer = g.b = g.h = g.tile = g.jlo = g.jhi = 0;
+    g.src = src_all;
+    if (task >= tasks) return g;
     int slot;
-    task_coords(a, task, layer, b, h, &slot);
-    const int p0 = a.pos[*b];
-    if (p0 < 0) return false;
-    *tile = p0 / 32 + slot;
-    if (!tile_range(a, p0, *tile, jlo, jhi)) return false;
-    const int64_t stream = ((int64_t)*layer * a.batch + *b) * a.heads + *h;
-    *src = src_all + (stream * a.t_new + 32 * (int64_t)*tile + j0 - p0) * D;
-    return true;
+    task_coords(a, task, &g.layer, &g.b, &g.h, &slot);
+    const int p0 = a.pos[g.b];
+    if (p0 < 0) return g;
+    g.tile = p0 / 32 + slot;
+    if (!tile_range(a, p0, g.tile, &g.jlo, &g.jhi)) return g;
+    /* this wave's 16 rows must meet the appended ones */
+    if (g.jhi <= j0 || g.jlo >= j0 + kVec) {
+      g.src = src_all;
+    } else {
+      const int64_t stream = ((int64_t)g.layer * a.batch + g.b) * a.heads + g.h;
+      g.src = src_all + (stream * a.t_new + 32 * (int64_t)g.tile + j0 - p0) * D;
+    }
+    g.live = true;
+    return g;
+  };
+  /* the lane's input row of a task, clamped into the task's appended rows
+   * that this wave covers (any real row when it covers none) */
+  auto lane_src = [&](const TaskGeo& g) -> const uint16_t* {
+    const int lo = g.jlo > j0 ? g.jlo : j0, hi = g.jhi < j0 + kVec ? g.jhi : j0 + kVec;
+    if (!g.live || hi <= lo) return src_all;
+    int j = j0 + nl;
+    if (j < lo) j = lo;
+    if (j >= hi) j = hi - 1;
+    return g.src + (int64_t)(j - j0) * D;
   };
 
-  int64_t task = (int64_t)blockIdx.x * AG::TPB + slot_in_block;
-  uint4 g[4];
-  {
-    int layer, b, h, tile, jlo, jhi;
-    const uint16_t* src;
-    if (task < tasks && setup(task, &layer, &b, &h, &tile, &jlo, &jhi, &src))
-      pass_load<D>(src, D, jlo - j0, jhi - j0, g, lane);
-  }
-  /* every wave runs the same number of iterations (barriers inside) */
-  const int64_t iters = (tasks + step - 1) / step;
-  for (int64_t it = 0; it < iters; ++it, task += step) {
-    int layer = 0, b = 0, h = 0, tile = 0, jlo = 0, jhi = 0;
-    const uint16_t* src = nullptr;
-    const bool live = task < tasks && setup(task, &layer, &b, &h, &tile, &jlo, &jhi, &src);
-    uint32_t n16 = 0;
-    uint32_t pk[BK > BV ? BK : BV];
-    if (live) {
-      uint32_t sm[4];
-      sign_masks<D>(a.sign_bits + (int64_t)layer * (D / 8), lane, sm);
-      pass_stage<D>(g, sm, stage, lane);
-      wave_lds_sync();
+  const int64_t pairs = (tasks + kTPB - 1) / kTPB;
+  const int64_t first = (int64_t)blockIdx.x * a.chunk;
+  int64_t last = first + a.chunk;
+  if (last > pairs) last = pairs;
+  if (first >= last) return;
+
+  uint32_t sm[G::J][4];
+  int sm_layer = -1;
+
+  auto body = [&](const XRegs<D>& xr, const TaskGeo& g) {
+    if (g.live && g.layer != sm_layer) {
+      sign_masks<D>(a.sign_bits + (int64_t)g.layer * (D / 8), q4, sm);
+      sm_layer = g.layer;
     }
-    {
-      int l2, b2, h2, t2, lo2, hi2;
-      const uint16_t* s2;
-      const int64_t nt = task + step;
-      if (nt < tasks && setup(nt, &l2, &b2, &h2, &t2, &lo2, &hi2, &s2))
-        pass_load<D>(s2, D, lo2 - j0, hi2 - j0, g, lane);
-    }
-    const int v = lane / G::LPV, part = lane % G::LPV;
-    const int jrow = j0 + v;
-    const bool mine = live && jrow >= jlo && jrow < jhi;
-    const int64_t row = ((int64_t)b * a.heads + h) * a.capacity + 32 * (int64_t)tile + jrow;
-    if (live && !is_v) {
-      uint32_t p4[BK];
-      bool sure;
-      encode_lane<D, BK>(stage, tab, nbh, lane, p4, &n16, &sure);
-      if (mine)
-        store_packed<BK>(a.k_codes + layer * a.ls_kc + row * (D * BK / 8) + part * (4 * BK), p4);
-      n16 = settle_norm<D>(stage, lane, n16, sure);
-      if (mine && part == 0)
-        *(uint16_t*)((uint8_t*)a.k_norms + layer * a.ls_kn + row * 2) = (uint16_t)n16;
-    } else if (live) {
-      uint32_t pv[BV];
-      bool sure;
-      encode_lane<D, BV>(stage, tab, nbh, lane, pv, &n16, &sure);
-      /* unpacked codes of this lane's 32 coordinates -> vbuf[jrow][part*32 ..] */
-      if (jrow < 32) {
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          uint32_t word = 0;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int i = 4 * k + e, bit = BV * i;
-            uint32_t c = pv[bit / 32] >> (bit % 32);
-            if ((bit % 32) + BV > 32) c |= pv[bit / 32 + 1] << (32 - bit % 32);
-            word |= (c & ((1u << BV) - 1u)) << (8 * e);
-          }
-          *(uint32_t*)(vbuf + jrow * D + part * 32 + 4 * k) = word;
-        }
+    const int jrow = j0 + nl;
+    const bool mine = g.live && jrow >= g.jlo && jrow < g.jhi;
+    const int64_t row = ((int64_t)g.b * a.heads + g.h) * a.capacity + 32 * (int64_t)g.tile + jrow;
+    const uint16_t* vec = lane_src(g);
+    uint32_t piece[G::OB];
+    if (!is_v) {
+      const uint32_t n16 = encode_pass<D, BK, false>(xr, sm, ht, mytab, nbh, vec, piece);
+      uint32_t out[Chunk<D, BK>::NW];
+      gather_row_chunk<D, BK>(piece, out);
+      if (mine) {
+        store_chunk<D, BK>(a.k_codes + g.layer * a.ls_kc + row * (D * BK / 8) +
+                               q4 * Chunk<D, BK>::BYTES, out);
+        if (q4 == 0) *(uint16_t*)((uint8_t*)a.k_norms + g.layer * a.ls_kn + row * 2) = (uint16_t)n16;
       }
-      n16 = settle_norm<D>(stage, lane, n16, sure);
-      if (mine && part == 0)
-        *(uint16_t*)((uint8_t*)a.v_norms + layer * a.ls_vn + row * 2) = (uint16_t)n16;
-    }
-    (void)pk;
-    if (is_v) {
+    } else {
+      const uint32_t n16 = encode_pass<D, BV, true>(xr, sm, ht, mytab, nbh, vec, piece);
+      /* code bytes of coordinates 16 ob + 4 q4 .. +3 -> vbuf[jrow] */
+#pragma unroll
+      for (int ob = 0; ob < G::OB; ++ob)
+        *(uint32_t*)(vbuf + jrow * D + 16 * ob + 4 * q4) = piece[ob];
+      if (mine && q4 == 0)
+        *(uint16_t*)((uint8_t*)a.v_norms + g.layer * a.ls_vn + row * 2) = (uint16_t)n16;
       __syncthreads();
       /* the first wave of each tile builds the 64 segments of its tile */
-      if (live && sub == 0) {
+      if (g.live && sub == 0) {
         const int q = lane / 16, rr = lane % 16;
         constexpr int M = D / 16;
         constexpr int SW = D * BV / 64; /* segment words */
@@ -589,7 +648,7 @@ append_kernel(AppendArgs a) {
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
           const int tj = tile_token(q, u);
-          const bool valid = tj >= jlo && tj < jhi;
+          const bool valid = tj >= g.jlo && tj < g.jhi;
           uint8_t cb[M];
 #pragma unroll
           for (int m = 0; m < M; ++m) cb[m] = vbuf[tj * D + rr * M + m];
@@ -606,11 +665,11 @@ append_kernel(AppendArgs a) {
             }
           }
         }
-        const int64_t tile_base = (((int64_t)b * a.heads + h) * (a.capacity / 32) + tile) *
+        const int64_t tile_base = (((int64_t)g.b * a.heads + g.h) * (a.capacity / 32) + g.tile) *
                                   (32 * D * BV / 8);
-        uint32_t* dst = (uint32_t*)(a.v_codes + layer * a.ls_vc + tile_base +
+        uint32_t* dst = (uint32_t*)(a.v_codes + g.layer * a.ls_vc + tile_base +
                                     (int64_t)lane * (D * BV / 16));
-        const bool full = (jlo == 0 && jhi == 32);
+        const bool full = (g.jlo == 0 && g.jhi == 32);
 #pragma unroll
         for (int k = 0; k < SW; ++k) {
           uint32_t val = seg[k];
@@ -619,20 +678,33 @@ append_kernel(AppendArgs a) {
         }
       }
       __syncthreads(); /* vbuf is reused by the next task */
-    } else {
-      wave_lds_sync(); /* the stage is reused by the next task */
     }
+  };
+
+  /* every wave of the block runs the same iterations (barriers inside) */
+  XRegs<D> xa, xb;
+  TaskGeo ga = setup(first * kTPB + slot_in_block);
+  load_x<D>(xa, lane_src(ga), q4);
+  int64_t it = first;
+  for (;;) {
+    const TaskGeo gb = setup((it + 1 < last ? it + 1 : it) * kTPB + slot_in_block);
+    load_x<D>(xb, lane_src(gb), q4);
+    body(xa, ga);
+    if (++it >= last) break;
+    ga = setup((it + 1 < last ? it + 1 : it) * kTPB + slot_in_block);
+    load_x<D>(xa, lane_src(ga), q4);
+    body(xb, gb);
+    if (++it >= last) break;
   }
 }
 
 template <int D, int BITS>
 tq_status launch_rows_t(const tq_codebook_s* cb, const uint16_t* x, int64_t n, int64_t stride,
                         const uint8_t* sb, uint8_t* codes, uint16_t* norms, hipStream_t s) {
-  using G = Geo<D>;
-  const int64_t passes = (n + G::VPW - 1) / G::VPW;
+  const int64_t passes = (n + kVec - 1) / kVec;
   int64_t blocks = (passes + kRowsWaves - 1) / kRowsWaves;
   if (blocks > 4096) blocks = 4096;
-  const size_t lds = table_bytes(cb->enc_entries) + (size_t)kRowsWaves * 64 * kPitch;
+  const size_t lds = table_bytes(cb->enc_entries);
   hipLaunchKernelGGL((encode_rows_kernel<D, BITS>), dim3((unsigned)blocks), dim3(64 * kRowsWaves),
                      lds, s, x, n, stride, sb, cb->enc_table, cb->enc_entries,
                      (float)cb->nb_half, codes, norms);
@@ -640,13 +712,13 @@ tq_status launch_rows_t(const tq_codebook_s* cb, const uint16_t* x, int64_t n, i
 }
 
 template <int D, int BK, int BV>
-tq_status launch_append_t(const AppendArgs& a, hipStream_t s) {
-  using AG = AppendGeo<D>;
+tq_status launch_append_t(AppendArgs a, hipStream_t s) {
   const int64_t tasks = (int64_t)a.n_layers * a.batch * a.heads * a.slots;
-  int64_t blocks = (tasks + AG::TPB - 1) / AG::TPB;
-  if (blocks > 2048) blocks = 2048;
-  const size_t lds = table_bytes(a.ent_k > a.ent_v ? a.ent_k : a.ent_v) +
-                     (size_t)kAppendWaves * 64 * kPitch + (size_t)AG::TPB * 32 * D;
+  const int64_t pairs = (tasks + kTPB - 1) / kTPB;
+  int64_t blocks = pairs < 2048 ? pairs : 2048;
+  a.chunk = (pairs + blocks - 1) / blocks;
+  blocks = (pairs + a.chunk - 1) / a.chunk;
+  const size_t lds = table_bytes(a.ent_k > a.ent_v ? a.ent_k : a.ent_v) + (size_t)kTPB * 32 * D;
   hipLaunchKernelGGL((append_kernel<D, BK, BV>), dim3((unsigned)blocks, 2), dim3(64 * kAppendWaves),
                      lds, s, a);
   return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_DEVICE;
@@ -686,6 +758,7 @@ tq_status tq_launch_append(const tq_kv_cache* c, const tq_codebook_s* cbk,
   a.t_new = t_new;
   a.n_layers = n_layers;
   a.slots = (t_new + 31) / 32 + 1;
+  a.chunk = 1;
   a.k_new = k_new;
   a.v_new = v_new;
   a.sign_bits = sign_bits;
