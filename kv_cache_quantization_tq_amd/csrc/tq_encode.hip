@@ -485,6 +485,86 @@ encode_rows_kernel(const uint16_t* __restrict__ x, int64_t n, int64_t stride,
 
 __device__ inline int tile_token(int q, int u) { return u < 4 ? 4 * q + u : 16 + 4 * q + (u - 4); }
 
+/* Row pitch of the value-tile code buffer. */
+template <int D>
+constexpr int kVPitch = D + 16;
+
+/* The codes of one token's coordinates r M .. r M + M - 1 (M = d/16 bytes). */
+template <int D>
+struct TokCodes {
+  uint32_t w[D / 64];
+};
+template <int D>
+__device__ inline TokCodes<D> read_tok(const uint8_t* p) {
+  TokCodes<D> t;
+  if constexpr (D == 64) {
+    t.w[0] = *(const uint32_t*)p;
+  } else if constexpr (D == 128) {
+    const uint2 v = *(const uint2*)p;
+    t.w[0] = v.x;
+    t.w[1] = v.y;
+  } else {
+    const uint4 v = *(const uint4*)p;
+    t.w[0] = v.x;
+    t.w[1] = v.y;
+    t.w[2] = v.z;
+    t.w[3] = v.w;
+  }
+  return t;
+}
+
+/* Build segment `lane` (q = lane / 16, r = lane % 16) of a value tile from
+ * the code bytes in vbuf (rows = tile tokens, kVPitch bytes apart) and store
+ * it at tile_dst: for m < d/16 and u < 8, the code of coordinate r d/16 + m of
+ * token tile_token(q, u) at bit (8 m + u) BV.  Tokens outside [jlo, jhi) keep
+ * the bits already in memory. */
+template <int D, int BV>
+__device__ inline void build_value_tile(const uint8_t* vbuf, int lane, int jlo, int jhi,
+                                        uint8_t* tile_dst) {
+  constexpr int M = D / 16;
+  constexpr int SW = D * BV / 64; /* segment words */
+  const int q = lane / 16, rr = lane % 16;
+  uint32_t seg[SW];
+#pragma unroll
+  for (int k = 0; k < SW; ++k) seg[k] = 0u;
+  uint32_t valid_u = 0u; /* bit u: token u of the segment is being written */
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int tj = tile_token(q, u);
+    valid_u |= (tj >= jlo && tj < jhi ? 1u : 0u) << u;
+    const TokCodes<D> t = read_tok<D>(vbuf + tj * kVPitch<D> + rr * M);
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const uint32_t c = __builtin_amdgcn_ubfe(t.w[m / 4], 8 * (m % 4), 8);
+      const int bit = (8 * m + u) * BV;
+      seg[bit / 32] |= c << (bit % 32);
+      if ((bit % 32) + BV > 32) seg[bit / 32 + 1] |= c >> (32 - bit % 32);
+    }
+  }
+  uint32_t* dst = (uint32_t*)(tile_dst + (int64_t)lane * (D * BV / 16));
+  if (jlo == 0 && jhi == 32) {
+#pragma unroll
+    for (int k = 0; k < SW; ++k) dst[k] = seg[k];
+  } else {
+    /* keep the other tokens' bits */
+    uint32_t mask[SW];
+#pragma unroll
+    for (int k = 0; k < SW; ++k) mask[k] = 0u;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const uint32_t f = (valid_u >> u) & 1u ? ((1u << BV) - 1u) : 0u;
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        const int bit = (8 * m + u) * BV;
+        mask[bit / 32] |= f << (bit % 32);
+        if ((bit % 32) + BV > 32) mask[bit / 32 + 1] |= f >> (32 - bit % 32);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < SW; ++k) dst[k] = (dst[k] & ~mask[k]) | (seg[k] & mask[k]);
+  }
+}
+
 struct AppendArgs {
   uint8_t* k_codes;
   uint8_t* v_codes;
@@ -519,16 +599,41 @@ __device__ inline bool tile_range(const AppendArgs& a, int p0, int tile, int* jl
   return hi > lo;
 }
 
-/* Task t of a role: (layer, seq, head, slot) with slot the tile offset from
- * the first tile touched by the append. */
-__device__ inline void task_coords(const AppendArgs& a, int64_t task, int* layer, int* b, int* h,
-                                   int* slot) {
-  *slot = (int)(task % a.slots);
+/* Task coordinates (layer, seq, head, slot), slot the tile offset from the
+ * first tile touched by the append; tasks are numbered with slot fastest.
+ * The divisions happen once per block; later tasks advance by carries. */
+struct TaskIter {
+  int64_t task;
+  int layer, b, h, slot;
+};
+
+__device__ inline TaskIter task_at(const AppendArgs& a, int64_t task) {
+  TaskIter t;
+  t.task = task;
+  t.slot = (int)(task % a.slots);
   int64_t r = task / a.slots;
-  *h = (int)(r % a.heads);
+  t.h = (int)(r % a.heads);
   r /= a.heads;
-  *b = (int)(r % a.batch);
-  *layer = (int)(r / a.batch);
+  t.b = (int)(r % a.batch);
+  t.layer = (int)(r / a.batch);
+  return t;
+}
+
+/* The task `step` further on (step <= slots). */
+__device__ inline TaskIter task_advance(const AppendArgs& a, TaskIter t, int step) {
+  t.task += step;
+  t.slot += step;
+  if (t.slot >= a.slots) {
+    t.slot -= a.slots;
+    if (++t.h == a.heads) {
+      t.h = 0;
+      if (++t.b == a.batch) {
+        t.b = 0;
+        ++t.layer;
+      }
+    }
+  }
+  return t;
 }
 
 /* Geometry of one wave's part of a task. */
@@ -554,7 +659,9 @@ append_kernel(AppendArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64), lane = threadIdx.x % 64;
   const int q4 = lane / 16, nl = lane % 16;
   const int slot_in_block = wave / 2, sub = wave % 2;
-  uint8_t* vbuf = (uint8_t*)(smem + tb) + slot_in_block * 32 * D; /* tile codes [row][coord] */
+  /* tile codes [row][coord], rows padded by 16 bytes so that the 64 lanes'
+   * 4-byte writes of one output block fall on distinct banks */
+  uint8_t* vbuf = (uint8_t*)(smem + tb) + slot_in_block * 32 * kVPitch<D>;
   load_table(tab, is_v ? a.tab_v : a.tab_k, ent);
   __syncthreads();
   const char* mytab = (const char*)tab + (lane & (kEncRep - 1)) * sizeof(tq_enc_entry);
@@ -564,14 +671,16 @@ append_kernel(AppendArgs a) {
   const int j0 = sub * kVec; /* this wave's first tile row */
   const HTiles ht = h_tiles(nl, q4);
 
-  auto setup = [&](int64_t task) -> TaskGeo {
+  auto setup = [&](const TaskIter& t) -> TaskGeo {
     TaskGeo g;
     g.live = false;
-    g.layer = g.b = g.h = g.tile = g.jlo = g.jhi = 0;
+    g.layer = t.layer;
+    g.b = t.b;
+    g.h = t.h;
+    g.tile = g.jlo = g.jhi = 0;
     g.src = src_all;
-    if (task >= tasks) return g;
-    int slot;
-    task_coords(a, task, &g.layer, &g.b, &g.h, &slot);
+    if (t.task >= tasks) return g;
+    const int slot = t.slot;
     const int p0 = a.pos[g.b];
     if (p0 < 0) return g;
     g.tile = p0 / 32 + slot;
@@ -630,68 +739,39 @@ append_kernel(AppendArgs a) {
       /* code bytes of coordinates 16 ob + 4 q4 .. +3 -> vbuf[jrow] */
 #pragma unroll
       for (int ob = 0; ob < G::OB; ++ob)
-        *(uint32_t*)(vbuf + jrow * D + 16 * ob + 4 * q4) = piece[ob];
+        *(uint32_t*)(vbuf + jrow * kVPitch<D> + 16 * ob + 4 * q4) = piece[ob];
       if (mine && q4 == 0)
         *(uint16_t*)((uint8_t*)a.v_norms + g.layer * a.ls_vn + row * 2) = (uint16_t)n16;
       __syncthreads();
       /* the first wave of each tile builds the 64 segments of its tile */
-      if (g.live && sub == 0) {
-        const int q = lane / 16, rr = lane % 16;
-        constexpr int M = D / 16;
-        constexpr int SW = D * BV / 64; /* segment words */
-        uint32_t seg[SW], mask[SW];
-#pragma unroll
-        for (int k = 0; k < SW; ++k) {
-          seg[k] = 0u;
-          mask[k] = 0u;
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int tj = tile_token(q, u);
-          const bool valid = tj >= g.jlo && tj < g.jhi;
-          uint8_t cb[M];
-#pragma unroll
-          for (int m = 0; m < M; ++m) cb[m] = vbuf[tj * D + rr * M + m];
-#pragma unroll
-          for (int m = 0; m < M; ++m) {
-            const int bit = (8 * m + u) * BV;
-            const uint32_t c = valid ? cb[m] : 0u;
-            const uint32_t f = valid ? ((1u << BV) - 1u) : 0u;
-            seg[bit / 32] |= c << (bit % 32);
-            mask[bit / 32] |= f << (bit % 32);
-            if ((bit % 32) + BV > 32) {
-              seg[bit / 32 + 1] |= c >> (32 - bit % 32);
-              mask[bit / 32 + 1] |= f >> (32 - bit % 32);
-            }
-          }
-        }
-        const int64_t tile_base = (((int64_t)g.b * a.heads + g.h) * (a.capacity / 32) + g.tile) *
-                                  (32 * D * BV / 8);
-        uint32_t* dst = (uint32_t*)(a.v_codes + g.layer * a.ls_vc + tile_base +
-                                    (int64_t)lane * (D * BV / 16));
-        const bool full = (g.jlo == 0 && g.jhi == 32);
-#pragma unroll
-        for (int k = 0; k < SW; ++k) {
-          uint32_t val = seg[k];
-          if (!full) val = (dst[k] & ~mask[k]) | (seg[k] & mask[k]);
-          dst[k] = val;
-        }
-      }
+      if (g.live && sub == 0)
+        build_value_tile<D, BV>(vbuf, lane, g.jlo, g.jhi,
+                                a.v_codes + g.layer * a.ls_vc +
+                                    (((int64_t)g.b * a.heads + g.h) * (a.capacity / 32) + g.tile) *
+                                        (32 * D * BV / 8));
       __syncthreads(); /* vbuf is reused by the next task */
     }
   };
 
   /* every wave of the block runs the same iterations (barriers inside) */
   XRegs<D> xa, xb;
-  TaskGeo ga = setup(first * kTPB + slot_in_block);
+  TaskIter tnext = task_at(a, first * kTPB + slot_in_block);
+  TaskGeo ga = setup(tnext);
   load_x<D>(xa, lane_src(ga), q4);
+  /* the geometry of the pair after `it` (the same pair again at the end,
+   * so the prefetch loads are issued on every path) */
+  auto next_geo = [&](int64_t it, const TaskGeo& same) -> TaskGeo {
+    if (it + 1 >= last) return same;
+    tnext = task_advance(a, tnext, kTPB);
+    return setup(tnext);
+  };
   int64_t it = first;
   for (;;) {
-    const TaskGeo gb = setup((it + 1 < last ? it + 1 : it) * kTPB + slot_in_block);
+    const TaskGeo gb = next_geo(it, ga);
     load_x<D>(xb, lane_src(gb), q4);
     body(xa, ga);
     if (++it >= last) break;
-    ga = setup((it + 1 < last ? it + 1 : it) * kTPB + slot_in_block);
+    ga = next_geo(it, gb);
     load_x<D>(xa, lane_src(ga), q4);
     body(xb, gb);
     if (++it >= last) break;
@@ -718,7 +798,8 @@ tq_status launch_append_t(AppendArgs a, hipStream_t s) {
   int64_t blocks = pairs < 2048 ? pairs : 2048;
   a.chunk = (pairs + blocks - 1) / blocks;
   blocks = (pairs + a.chunk - 1) / a.chunk;
-  const size_t lds = table_bytes(a.ent_k > a.ent_v ? a.ent_k : a.ent_v) + (size_t)kTPB * 32 * D;
+  const size_t lds = table_bytes(a.ent_k > a.ent_v ? a.ent_k : a.ent_v) +
+                     (size_t)kTPB * 32 * kVPitch<D>;
   hipLaunchKernelGGL((append_kernel<D, BK, BV>), dim3((unsigned)blocks, 2), dim3(64 * kAppendWaves),
                      lds, s, a);
   return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_DEVICE;
