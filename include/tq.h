@@ -104,7 +104,7 @@ void tq_codebook_free(tq_codebook cb);
  * per-coordinate codebook quantization; AdapTQ page, steps 1-2).
  * x:         device, fp16 [n][x_stride] (the first d values of each row are
  *            the vector), 16-byte aligned, x_stride % 8 == 0, x_stride >= d.
- * sign_bits: device, d/8 bytes (this layer's D).
+ * sign_bits: device, d/8 bytes (this layer's D), 4-byte aligned.
  * codes:     device, [n][d*bits/8] row layout, 8-byte aligned.
  * norms:     device, fp16 [n], 2-byte aligned.
  * The codebook fixes d and bits.  n == 0 is a no-op. */
@@ -140,7 +140,7 @@ tq_status tq_cache_layer_bytes(const tq_kv_cache* c, int64_t* k_codes, int64_t* 
  * "Under the Hood": the cache compresses on each update).
  * k_new, v_new: device fp16 [n_layers][batch][kv_heads][t_new][d], 16-byte
  *               aligned, contiguous.
- * sign_bits:    device [n_layers][d/8].
+ * sign_bits:    device [n_layers][d/8], 4-byte aligned.
  * pos:          device int32 [batch]: the first row written for sequence b;
  *               rows pos[b] .. pos[b] + t_new - 1 of every layer and head are
  *               written, nothing else changes (partially covered value tiles

@@ -224,13 +224,22 @@ __device__ inline HTiles h_tiles(int n, int q4) {
   return t;
 }
 
+/* Read-only kernel inputs read through the constant address space, so that
+ * uniform reads become scalar loads (the kernel never writes them). */
+template <class T>
+__device__ inline T ld_const(const T* p) {
+  return *(const __attribute__((address_space(4))) T*)p;
+}
+
 /* Sign-flip masks of lane (q4, .): block j's coordinates 32 j + 8 q4 .. +7
- * are byte 4 j + q4 of the layer's sign bits; word w holds two of them. */
+ * are byte 4 j + q4 of the layer's sign bits (word j, read with a scalar
+ * load; sb is 4-byte aligned); word w of the masks holds two of them. */
 template <int D>
 __device__ inline void sign_masks(const uint8_t* sb, int q4, uint32_t (&m)[EGeo<D>::J][4]) {
 #pragma unroll
   for (int j = 0; j < EGeo<D>::J; ++j) {
-    const uint32_t b = sb[4 * j + q4];
+    const uint32_t sw = ld_const((const uint32_t*)sb + j);
+    const uint32_t b = (sw >> (8 * q4)) & 0xFFu;
 #pragma unroll
     for (int w = 0; w < 4; ++w)
       m[j][w] = (((b >> (2 * w)) & 1u) << 15) | (((b >> (2 * w + 1)) & 1u) << 31);
@@ -681,7 +690,9 @@ append_kernel(AppendArgs a) {
     g.src = src_all;
     if (t.task >= tasks) return g;
     const int slot = t.slot;
-    const int p0 = a.pos[g.b];
+    /* a scalar load: the index is uniform (a vector load here would make the
+     * wave wait for all its outstanding memory operations) */
+    const int p0 = ld_const(a.pos + g.b);
     if (p0 < 0) return g;
     g.tile = p0 / 32 + slot;
     if (!tile_range(a, p0, g.tile, &g.jlo, &g.jhi)) return g;

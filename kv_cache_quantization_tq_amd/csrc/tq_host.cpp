@@ -271,7 +271,8 @@ extern "C" tq_status tq_encode(tq_codebook cb, const uint16_t* x, int64_t n, int
   if (n == 0) return TQ_OK;
   if (!x || !sign_bits || !codes || !norms) return TQ_ERR_ARG;
   if (x_stride < cb->d || x_stride % 8 != 0) return TQ_ERR_ARG;
-  if (!aligned(x, 16) || !aligned(codes, 8) || !aligned(norms, 2)) return TQ_ERR_ARG;
+  if (!aligned(x, 16) || !aligned(codes, 8) || !aligned(norms, 2) || !aligned(sign_bits, 4))
+    return TQ_ERR_ARG;
   return tq_launch_encode_rows(cb, x, n, x_stride, sign_bits, codes, norms,
                                (hipStream_t)stream);
 }
@@ -324,7 +325,8 @@ extern "C" tq_status tq_append(const tq_kv_cache* c, tq_codebook cbk, tq_codeboo
   if (t_new < 0 || n_layers < 1) return TQ_ERR_ARG;
   if (t_new == 0) return TQ_OK;
   if (!sign_bits || !k_new || !v_new || !pos) return TQ_ERR_ARG;
-  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(pos, 4)) return TQ_ERR_ARG;
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(pos, 4) || !aligned(sign_bits, 4))
+    return TQ_ERR_ARG;
   if (host_max_pos < -1) return TQ_ERR_ARG;
   if (host_max_pos >= 0 && (int64_t)host_max_pos + t_new > c->capacity) return TQ_ERR_CAPACITY;
   return tq_launch_append(c, cbk, cbv, sign_bits, k_new, v_new, t_new, pos, n_layers,
