@@ -290,10 +290,24 @@ __device__ inline void lds_fwht(float* buf, int G) {
 }
 
 /* One 32-token tile's loads for one lane. */
-template <class DG>
+/* One 32-token tile's loads for one lane.  The norms are only those of the
+ * tokens whose softmax this lane computes (see tile_step): four consecutive
+ * tokens (CF 2) or two (CF 4). */
+template <int CF>
+struct NormWords;
+template <>
+struct NormWords<2> {
+  typedef uint2 T;
+};
+template <>
+struct NormWords<4> {
+  typedef uint32_t T;
+};
+
+template <class DG, int CF>
 struct TileRegs {
   uint32_t kw0[DG::KW], kw1[DG::KW], vw[DG::VW];
-  uint2 kn0, kn1, vn0, vn1;
+  typename NormWords<CF>::T kn, vn;
 };
 
 /* Addresses of one wave's loads: wave-uniform bases (scalar registers; the
@@ -306,18 +320,42 @@ struct TileAddr {
   uint32_t koff, voff, noff;
 };
 
-template <class DG>
-__device__ inline void load_tile(TileRegs<DG>& r, const TileAddr& ad, int tile) {
+template <class DG, int CF>
+__device__ inline void load_tile(TileRegs<DG, CF>& r, const TileAddr& ad, int tile) {
+  typedef typename NormWords<CF>::T NT;
   const uint8_t* kt = ad.k + (int64_t)tile * (32 * DG::RB);
   load_words<DG::KB, DG::KA>(kt + ad.koff, r.kw0);
   load_words<DG::KB, DG::KA>(kt + 16 * DG::RB + ad.koff, r.kw1);
   load_words<DG::SEG, DG::VA>(ad.v + (int64_t)tile * DG::TILE + ad.voff, r.vw);
-  const uint8_t* knt = ad.kn + (int64_t)tile * 64 + ad.noff;
-  const uint8_t* vnt = ad.vn + (int64_t)tile * 64 + ad.noff;
-  r.kn0 = *(const uint2*)knt;
-  r.kn1 = *(const uint2*)(knt + 32);
-  r.vn0 = *(const uint2*)vnt;
-  r.vn1 = *(const uint2*)(vnt + 32);
+  r.kn = *(const NT*)(ad.kn + (int64_t)tile * 64 + ad.noff);
+  r.vn = *(const NT*)(ad.vn + (int64_t)tile * 64 + ad.noff);
+}
+
+/* Tile token (0..31) of slot u (0..7) of a lane in row q4 of the products. */
+__device__ inline int tok_of(int q4, int u) { return u < 4 ? 4 * q4 + u : 16 + 4 * q4 + (u - 4); }
+
+/* DPP move within 16-lane rows (lanes whose source lies outside the row
+ * read 0). */
+template <int CTRL>
+__device__ inline float dpp_mov(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+template <int CTRL>
+__device__ inline uint32_t dpp_mov_u(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, true);
+}
+constexpr int kShl4 = 0x104, kShl8 = 0x108, kShl12 = 0x10C;
+constexpr int kShr4 = 0x114, kShr8 = 0x118;
+constexpr int kRor4 = 0x124, kRor8 = 0x128;
+
+__device__ inline float max_ror4(float v) {
+  return fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kRor4, 0xF, 0xF, false)));
+}
+__device__ inline float max_ror8(float v) {
+  return fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kRor8, 0xF, 0xF, false)));
+}
+__device__ inline float add_ror4(float v) {
+  return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), kRor4, 0xF, 0xF, false));
 }
 
 /* x * h + c, h an fp16 value given by its bits (one mixed-precision FMA). */
@@ -332,13 +370,13 @@ __device__ inline float mul_h(float x, uint32_t h) {
 
 /* Score, softmax-update and accumulate one tile.  PARTIAL: some of its tokens
  * lie at or past len and are masked out. */
-template <class DG, int BK, int BV, bool PARTIAL>
-__device__ inline void tile_step(const TileRegs<DG>& r,
+template <class DG, int BK, int BV, bool PARTIAL, int CF>
+__device__ inline void tile_step(const TileRegs<DG, CF>& r,
                                  const half8 (&bq)[KTab<BK>::SPLIT ? 2 * DG::KS : DG::KS],
                                  const uint32_t* lk, const uint32_t* lv, uint32_t lo,
-                                 uint32_t lo8, uint32_t lok, float lo_col, floatx4 (&acc)[DG::VM],
+                                 uint32_t lo8, uint32_t lok, floatx4 (&acc)[DG::VM],
                                  float& m_run, float& l_run, bool& first, int tok0, int len,
-                                 int q4) {
+                                 int q4, int n) {
   floatx4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int s = 0; s < DG::KS; ++s) {
@@ -357,29 +395,69 @@ __device__ inline void tile_step(const TileRegs<DG>& r,
       s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, a1), bq[s], s1, 0, 0, 0);
     }
   }
-  /* tokens tok0 + 4 q4 + u (u < 4) and tok0 + 16 + 4 q4 + u - 4 */
-  const uint32_t knw[4] = {r.kn0.x, r.kn0.y, r.kn1.x, r.kn1.y};
-  const uint32_t vnw[4] = {r.vn0.x, r.vn0.y, r.vn1.x, r.vn1.y};
-  float sc[8];
+  /* Softmax on compacted values.  After the products lane (q4, n) holds, for
+   * slots u = 0..7 (tile token tok_of(q4, u)), column n's partial score:
+   * columns 0..7 the fp16(q'') part of head n, 8..15 the remainder part of
+   * head n - 8.  Joined (hi + lo) and spread over the row's lanes so that
+   * each lane owns V = 8 / CF distinct (token, head) scores:
+   *   CF 2: lane n takes slots 4 b + v (b = n >> 3) of head n & 7;
+   *   CF 4 (group <= 4): lane n takes slots 2 a + v (a = n >> 2) of head
+   *   n & 3. */
+  constexpr int V = 8 / CF;
+  float sc[V];
+  int slot0;
+  const bool upper = n >= 8; /* lane-constant selectors */
+  if constexpr (CF == 2) {
+    slot0 = upper ? 4 : 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    sc[i] = ror8_add(s0[i]);
-    sc[4 + i] = ror8_add(s1[i]);
+    for (int v = 0; v < 4; ++v) {
+      /* every lane runs both cross-lane moves (a lane that skipped one would
+       * leave its partner reading a disabled lane), then selects */
+      const float a0 = ror8_add(s0[v]), a1 = ror8_add(s1[v]);
+      sc[v] = upper ? a1 : a0;
+    }
+  } else {
+    slot0 = 2 * (n >> 2);
+    const bool odd = (n & 4) != 0;
+    float j[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      j[i] = ror8_add(s0[i]);
+      j[4 + i] = ror8_add(s1[i]);
+    }
+    /* lanes 8..11 repeat heads 0..3, so slots 4, 5 are local there; groups
+     * 4..7 and 12..15 take slots 2, 3 and 6, 7 from four lanes down */
+#pragma unroll
+    for (int v = 0; v < 2; ++v) {
+      const float x = upper ? j[4 + v] : j[v];
+      const float t = upper ? j[6 + v] : j[2 + v];
+      const float y = dpp_mov<kShr4>(t);
+      sc[v] = odd ? y : x;
+    }
   }
   /* scores relative to the running max: w = s - m_run in one fma */
+  uint32_t knh[V], vnh[V];
+  if constexpr (CF == 2) {
+    knh[0] = r.kn.x & 0xFFFFu; knh[1] = r.kn.x >> 16; knh[2] = r.kn.y & 0xFFFFu; knh[3] = r.kn.y >> 16;
+    vnh[0] = r.vn.x & 0xFFFFu; vnh[1] = r.vn.x >> 16; vnh[2] = r.vn.y & 0xFFFFu; vnh[3] = r.vn.y >> 16;
+  } else {
+    knh[0] = r.kn & 0xFFFFu; knh[1] = r.kn >> 16;
+    vnh[0] = r.vn & 0xFFFFu; vnh[1] = r.vn >> 16;
+  }
   float mt = -INFINITY;
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const float w = fma_h(sc[u], (knw[u / 2] >> (16 * (u & 1))) & 0xFFFFu, -m_run);
+  for (int v = 0; v < V; ++v) {
+    const float w = fma_h(sc[v], knh[v], -m_run);
     if (PARTIAL) {
-      const int tok = tok0 + (u < 4 ? 4 * q4 + u : 16 + 4 * q4 + (u - 4));
-      sc[u] = tok < len ? w : -INFINITY;
+      sc[v] = tok0 + tok_of(q4, slot0 + v) < len ? w : -INFINITY;
     } else {
-      sc[u] = w;
+      sc[v] = w;
     }
-    mt = fmaxf(mt, sc[u]);
+    mt = fmaxf(mt, sc[v]);
   }
-  mt = rows_max(mt);
+  /* max over the lanes that share the head, then over the rows */
+  if constexpr (CF == 4) mt = max_ror4(mt);
+  mt = rows_max(max_ror8(mt));
   /* a new maximum (or the wave's first tile, which sets it): move the
    * reference and rescale the running sums; rare after the first tiles */
   if (__builtin_expect(__any(mt > 0.0f) || first, 0)) {
@@ -390,24 +468,46 @@ __device__ inline void tile_step(const TileRegs<DG>& r,
     for (int m = 0; m < DG::VM; ++m) acc[m] *= alpha;
     m_run += dm;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) sc[u] -= dm;
+    for (int v = 0; v < V; ++v) sc[v] -= dm;
     first = false;
   }
-  half8 pb;
+  /* p, then P' = p m split into fp16(p m) (columns 0..7) and the fp16
+   * remainder (columns 8..15), as fp16 pairs of consecutive slots */
+  uint32_t hp[V / 2], lp[V / 2];
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const float p = __builtin_amdgcn_exp2f(sc[u]);
-    l_run += p;
-    const uint32_t vh = (vnw[u / 2] >> (16 * (u & 1))) & 0xFFFFu;
-    /* columns 0..7 take fp16(p m), columns 8..15 the fp16 remainder */
-    const float pm = mul_h(p, vh);
-    _Float16 pv = (_Float16)__builtin_fmaf(-lo_col, (float)(_Float16)pm, pm);
-    if (PARTIAL) {
-      const int tok = tok0 + (u < 4 ? 4 * q4 + u : 16 + 4 * q4 + (u - 4));
-      pv = tok < len ? pv : (_Float16)0.0f;
-    }
-    pb[u] = pv;
+  for (int v = 0; v < V; v += 2) {
+    const float p0 = __builtin_amdgcn_exp2f(sc[v]), p1 = __builtin_amdgcn_exp2f(sc[v + 1]);
+    l_run += p0 + p1;
+    const float m0 = mul_h(p0, vnh[v]), m1 = mul_h(p1, vnh[v + 1]);
+    const _Float16 h0 = (_Float16)m0, h1 = (_Float16)m1;
+    const _Float16 r0 = (_Float16)(m0 - (float)h0), r1 = (_Float16)(m1 - (float)h1);
+    hp[v / 2] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+    lp[v / 2] = (uint32_t)__builtin_bit_cast(uint16_t, r0) | ((uint32_t)__builtin_bit_cast(uint16_t, r1) << 16);
   }
+  /* back to the operand layout: lane (q4, n) needs slots 0..7 of column n */
+  /* (all cross-lane moves run on every lane before the selects) */
+  u32x4 pw;
+  if constexpr (CF == 2) {
+    /* slots 0..3 live in the lower half, 4..7 in the upper one */
+    const uint32_t l0 = dpp_mov_u<kRor8>(lp[0]), l1 = dpp_mov_u<kRor8>(lp[1]);
+    const uint32_t h0 = dpp_mov_u<kRor8>(hp[0]), h1 = dpp_mov_u<kRor8>(hp[1]);
+    pw[0] = upper ? l0 : hp[0];
+    pw[1] = upper ? l1 : hp[1];
+    pw[2] = upper ? lp[0] : h0;
+    pw[3] = upper ? lp[1] : h1;
+  } else {
+    /* slot pair w of head g lives in lane 4 w + g; columns 0..3 read the
+     * fp16 parts, 8..11 the remainders (4..7 and 12..15 are unused) */
+    const uint32_t l8 = dpp_mov_u<kShr8>(lp[0]), l4 = dpp_mov_u<kShr4>(lp[0]);
+    const uint32_t lu = dpp_mov_u<kShl4>(lp[0]);
+    const uint32_t h4 = dpp_mov_u<kShl4>(hp[0]), h8 = dpp_mov_u<kShl8>(hp[0]);
+    const uint32_t h12 = dpp_mov_u<kShl12>(hp[0]);
+    pw[0] = upper ? l8 : hp[0];
+    pw[1] = upper ? l4 : h4;
+    pw[2] = upper ? lp[0] : h8;
+    pw[3] = upper ? lu : h12;
+  }
+  const half8 pb = __builtin_bit_cast(half8, pw);
   if constexpr (VTab<BV>::QUAD) {
     /* a value word holds two 16-bit fields; each byte of one is four tokens'
      * codes, looked up as four fp16 levels at once */
@@ -427,7 +527,7 @@ __device__ inline void tile_step(const TileRegs<DG>& r,
   }
 }
 
-template <int D, int BK, int BV>
+template <int D, int BK, int BV, int CF>
 __global__ void __launch_bounds__(64 * waves_for(D, BK, BV))
 decode_kernel(DecArgs a) {
   using DG = DecGeo<D, BK, BV>;
@@ -456,6 +556,39 @@ decode_kernel(DecArgs a) {
    * and load bases live in scalar registers */
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64), lane = threadIdx.x % 64;
   const int q4 = lane / 16, n = lane % 16;
+
+  int len = a.seq_lens[b];
+  len = len < 0 ? 0 : (len > a.max_len ? a.max_len : len);
+  const int ntiles = (len + 31) / 32;
+  const int t_begin = split * a.tiles_per_split;
+  int t_end = t_begin + a.tiles_per_split;
+  if (t_end > ntiles) t_end = ntiles;
+
+  const int64_t sh = (int64_t)b * a.kv_heads + kv;
+  TileAddr ad;
+  ad.k = a.k_codes + layer * a.ls_kc + sh * a.capacity * DG::RB;
+  ad.v = a.v_codes + layer * a.ls_vc + sh * (a.capacity / 32) * DG::TILE;
+  ad.kn = a.k_norms + layer * a.ls_kn + sh * a.capacity * 2;
+  ad.vn = a.v_norms + layer * a.ls_vn + sh * a.capacity * 2;
+  ad.koff = (uint32_t)(n * DG::RB + q4 * DG::KB);
+  ad.voff = (uint32_t)(lane * DG::SEG);
+  /* norms of the tokens this lane's softmax covers (see tile_step) */
+  ad.noff = (uint32_t)(2 * tok_of(q4, CF == 2 ? 4 * (n >> 3) : 2 * (n >> 2)));
+  const uint32_t lo = (uint32_t)lane << 2;           /* value tables, 4-byte entries */
+  const uint32_t lo8 = (uint32_t)(lane & 31) << 3;   /* value tables, 8-byte entries */
+  const uint32_t lok = (KTab<BK>::SPLIT ? lo8 : lo) | KPAGE; /* key table */
+
+  /* the first tiles' loads go out before the tables are built, so their
+   * latency overlaps the prologue (issued on every path, clamped to a tile
+   * that exists, so that the loop's waits stay exact) */
+  const int full_end = (len / 32) < t_end ? (len / 32) : t_end;
+  int tile = t_begin + wave;
+  constexpr int W = kWaves;  /* tile stride between a wave's tiles */
+  const int last = full_end > 0 ? full_end - 1 : 0;
+  auto pf = [&](TileRegs<DG, CF>& r, int t) { load_tile<DG, CF>(r, ad, t < last ? t : last); };
+  TileRegs<DG, CF> ra, rb, rc;
+  pf(ra, tile);
+  if constexpr (DG::DEPTH == 3) pf(rb, tile + W);
 
   if constexpr (KTab<BK>::SPLIT)
     fill_pairs<KTab<BK>::ENTRIES, kWaves>(lut_k, a.lut_k, a.lut_k_lo, 1);
@@ -510,27 +643,6 @@ decode_kernel(DecArgs a) {
     }
   }
 
-  int len = a.seq_lens[b];
-  len = len < 0 ? 0 : (len > a.max_len ? a.max_len : len);
-  const int ntiles = (len + 31) / 32;
-  const int t_begin = split * a.tiles_per_split;
-  int t_end = t_begin + a.tiles_per_split;
-  if (t_end > ntiles) t_end = ntiles;
-
-  const int64_t sh = (int64_t)b * a.kv_heads + kv;
-  TileAddr ad;
-  ad.k = a.k_codes + layer * a.ls_kc + sh * a.capacity * DG::RB;
-  ad.v = a.v_codes + layer * a.ls_vc + sh * (a.capacity / 32) * DG::TILE;
-  ad.kn = a.k_norms + layer * a.ls_kn + sh * a.capacity * 2;
-  ad.vn = a.v_norms + layer * a.ls_vn + sh * a.capacity * 2;
-  ad.koff = (uint32_t)(n * DG::RB + q4 * DG::KB);
-  ad.voff = (uint32_t)(lane * DG::SEG);
-  ad.noff = (uint32_t)(8 * q4);
-  const uint32_t lo = (uint32_t)lane << 2;           /* value tables, 4-byte entries */
-  const uint32_t lo8 = (uint32_t)(lane & 31) << 3;   /* value tables, 8-byte entries */
-  const uint32_t lok = (KTab<BK>::SPLIT ? lo8 : lo) | KPAGE; /* key table */
-  const float lo_col = n < 8 ? 0.0f : 1.0f; /* this lane's column holds remainders */
-
   floatx4 acc[DG::VM];
 #pragma unroll
   for (int m = 0; m < DG::VM; ++m) acc[m] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -544,22 +656,12 @@ decode_kernel(DecArgs a) {
    * (past the end they re-read the wave's last tile) so the number of loads
    * in flight is the same everywhere and each wait covers only the tile
    * about to be used. */
-  const int full_end = (len / 32) < t_end ? (len / 32) : t_end;
-  int tile = t_begin + wave;
-  constexpr int W = kWaves;  /* tile stride between a wave's tiles */
   if (tile < full_end) {
-    const int last = full_end - 1;
-    auto pf = [&](TileRegs<DG>& r, int t) {
-      load_tile<DG>(r, ad, t < last ? t : last);
-    };
-    auto step = [&](const TileRegs<DG>& r) {
-      tile_step<DG, BK, BV, false>(r, bq, lut_k_rd, lut_v, lo, lo8, lok, lo_col, acc, m_run,
-                                   l_run, first, tile * 32, len, q4);
+    auto step = [&](const TileRegs<DG, CF>& r) {
+      tile_step<DG, BK, BV, false, CF>(r, bq, lut_k_rd, lut_v, lo, lo8, lok, acc, m_run, l_run,
+                                       first, tile * 32, len, q4, n);
     };
     if constexpr (DG::DEPTH == 3) {
-      TileRegs<DG> ra, rb, rc;
-      pf(ra, tile);
-      pf(rb, tile + W);
       for (;;) {
         pf(rc, tile + 2 * W);
         step(ra);
@@ -572,8 +674,6 @@ decode_kernel(DecArgs a) {
         if ((tile += W) >= full_end) break;
       }
     } else {
-      TileRegs<DG> ra, rb;
-      pf(ra, tile);
       for (;;) {
         pf(rb, tile + W);
         step(ra);
@@ -586,13 +686,16 @@ decode_kernel(DecArgs a) {
   }
   /* the ragged last tile, if this wave owns it */
   if (tile < t_end) {
-    TileRegs<DG> rp;
-    load_tile<DG>(rp, ad, tile);
-    tile_step<DG, BK, BV, true>(rp, bq, lut_k_rd, lut_v, lo, lo8, lok, lo_col, acc, m_run, l_run,
-                                first, tile * 32, len, q4);
+    TileRegs<DG, CF> rp;
+    load_tile<DG, CF>(rp, ad, tile);
+    tile_step<DG, BK, BV, true, CF>(rp, bq, lut_k_rd, lut_v, lo, lo8, lok, acc, m_run, l_run,
+                                    first, tile * 32, len, q4, n);
   }
   if (first) m_run = -1e30f; /* no tiles: contributes nothing to the merge */
+  /* the lanes of a head hold disjoint tokens' sums */
   l_run = rows_sum(l_run);
+  if constexpr (CF == 4) l_run = add_ror4(l_run);
+  l_run += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(l_run), kRor8, 0xF, 0xF, false));
   /* value sums: column g (< 8) += column g + 8 (the fp16 remainders of p m) */
 #pragma unroll
   for (int m = 0; m < DG::VM; ++m)
@@ -703,11 +806,16 @@ decode_kernel(DecArgs a) {
   }
 }
 
+/* Groups of up to 4 query heads compact their softmax 4 ways, up to 8 2 ways. */
 template <int D, int BK, int BV>
 tq_status launch_decode_t(const DecArgs& a, hipStream_t s) {
   const int64_t blocks = (int64_t)a.n_layers * a.batch * a.kv_heads * a.splits;
-  hipLaunchKernelGGL((decode_kernel<D, BK, BV>), dim3((unsigned)blocks), dim3(64 * waves_for(D, BK, BV)), 0, s,
-                     a);
+  if (a.group <= 4)
+    hipLaunchKernelGGL((decode_kernel<D, BK, BV, 4>), dim3((unsigned)blocks),
+                       dim3(64 * waves_for(D, BK, BV)), 0, s, a);
+  else
+    hipLaunchKernelGGL((decode_kernel<D, BK, BV, 2>), dim3((unsigned)blocks),
+                       dim3(64 * waves_for(D, BK, BV)), 0, s, a);
   return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_DEVICE;
 }
 
@@ -722,7 +830,7 @@ int concurrent_blocks_t() {
     int dev = 0, cus = 0, per = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, decode_kernel<D, BK, BV>, 64 * waves_for(D, BK, BV),
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, decode_kernel<D, BK, BV, 2>, 64 * waves_for(D, BK, BV),
                                                      0) != hipSuccess ||
         cus <= 0 || per <= 0) {
       (void)hipGetLastError();

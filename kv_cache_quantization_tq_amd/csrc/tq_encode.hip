@@ -446,21 +446,24 @@ encode_rows_kernel(const uint16_t* __restrict__ x, int64_t n, int64_t stride,
   extern __shared__ __align__(16) char smem[];
   tq_enc_entry* tab = (tq_enc_entry*)smem;
   const int lane = threadIdx.x % 64, q4 = lane / 16, nl = lane % 16;
-  load_table(tab, table, entries);
-  __syncthreads();
-  const char* mytab = (const char*)tab + (lane & (kEncRep - 1)) * sizeof(tq_enc_entry);
-  uint32_t sm[G::J][4];
-  sign_masks<D>(sign_bits, q4, sm);
-  const HTiles ht = h_tiles(nl, q4);
   const int64_t passes = (n + kVec - 1) / kVec;
   const int64_t wstride = (int64_t)gridDim.x * kRowsWaves;
   int64_t ps = (int64_t)blockIdx.x * kRowsWaves + __builtin_amdgcn_readfirstlane(threadIdx.x / 64);
-  if (ps >= passes) return;
   /* this lane's row in pass p, clamped to a real row */
   auto row_of = [&](int64_t p) -> int64_t {
     const int64_t r = p * kVec + nl;
     return r < n ? r : n - 1;
   };
+  /* the first pass's loads go out before the table is built */
+  XRegs<D> xa, xb;
+  load_x<D>(xa, x + row_of(ps < passes ? ps : passes - 1) * stride, q4);
+  load_table(tab, table, entries);
+  __syncthreads();
+  if (ps >= passes) return;
+  const char* mytab = (const char*)tab + (lane & (kEncRep - 1)) * sizeof(tq_enc_entry);
+  uint32_t sm[G::J][4];
+  sign_masks<D>(sign_bits, q4, sm);
+  const HTiles ht = h_tiles(nl, q4);
   auto body = [&](const XRegs<D>& xr, int64_t p) {
     const int64_t r = p * kVec + nl;
     const bool valid = r < n;
@@ -474,8 +477,6 @@ encode_rows_kernel(const uint16_t* __restrict__ x, int64_t n, int64_t stride,
       if (q4 == 0) norms[r] = (uint16_t)n16;
     }
   };
-  XRegs<D> xa, xb;
-  load_x<D>(xa, x + row_of(ps) * stride, q4);
   for (;;) {
     const int64_t p1 = ps + wstride;
     load_x<D>(xb, x + row_of(p1 < passes ? p1 : ps) * stride, q4);
@@ -671,8 +672,6 @@ append_kernel(AppendArgs a) {
   /* tile codes [row][coord], rows padded by 16 bytes so that the 64 lanes'
    * 4-byte writes of one output block fall on distinct banks */
   uint8_t* vbuf = (uint8_t*)(smem + tb) + slot_in_block * 32 * kVPitch<D>;
-  load_table(tab, is_v ? a.tab_v : a.tab_k, ent);
-  __syncthreads();
   const char* mytab = (const char*)tab + (lane & (kEncRep - 1)) * sizeof(tq_enc_entry);
   const float nbh = is_v ? a.nbh_v : a.nbh_k;
   const uint16_t* src_all = is_v ? a.v_new : a.k_new;
@@ -765,10 +764,13 @@ append_kernel(AppendArgs a) {
   };
 
   /* every wave of the block runs the same iterations (barriers inside) */
+  /* the first pair's loads go out before the table is built */
   XRegs<D> xa, xb;
   TaskIter tnext = task_at(a, first * kTPB + slot_in_block);
   TaskGeo ga = setup(tnext);
   load_x<D>(xa, lane_src(ga), q4);
+  load_table(tab, is_v ? a.tab_v : a.tab_k, ent);
+  __syncthreads();
   /* the geometry of the pair after `it` (the same pair again at the end,
    * so the prefetch loads are issued on every path) */
   auto next_geo = [&](int64_t it, const TaskGeo& same) -> TaskGeo {
