@@ -203,10 +203,10 @@ def main():
         "encode_gbs": enc_gbs,
         "encode_pct_hbm_peak": 100 * enc_gbs / HBM_PEAK_GBS,
         "append_us": app_ms * 1e3,
-        "roofline": {"bound": "hbm", "kernel": "decode_kernel<128,4,2>",
+        "roofline": {"bound": "hbm", "kernel": "decode_kernel<128,4,2,4>",
                      "achieved": dec_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": dec_gbs / HBM_PEAK_GBS,
-                     "traffic": measured_traffic("decode_kernel<128,4,2>"),
+                     "traffic": measured_traffic("decode_kernel<128,4,2,4>"),
                      "bytes_per_launch": dec_bytes, "avg_launch_us": dec_ms * 1e3},
         "roofline_encode": {"bound": "hbm", "kernel": "append_kernel<128,4,2>",
                             "achieved": enc_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
