@@ -179,24 +179,39 @@ __device__ inline uint32_t field(const uint32_t (&w)[NW], int s) {
   return (uint32_t)(v >> sh) & ((1u << (8 * B)) - 1u);
 }
 
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+/* Streaming (non-temporal) loads: the packed cache is read once per step. */
+template <class T>
+__device__ inline T ld_nt(const uint8_t* p);
+template <>
+__device__ inline uint32_t ld_nt<uint32_t>(const uint8_t* p) {
+  return __builtin_nontemporal_load((const uint32_t*)p);
+}
+template <>
+__device__ inline uint2 ld_nt<uint2>(const uint8_t* p) {
+  const u32x2 t = __builtin_nontemporal_load((const u32x2*)p);
+  return make_uint2(t.x, t.y);
+}
+
 /* Load N bytes (N % 4 == 0 or N == 6) from p, aligned to A bytes. */
 template <int N, int A>
 __device__ inline void load_words(const uint8_t* p, uint32_t (&w)[(N + 3) / 4]) {
   if constexpr (A >= 16 && N % 16 == 0) {
 #pragma unroll
     for (int k = 0; k < N / 16; ++k) {
-      uint4 t = *(const uint4*)(p + 16 * k);
+      u32x4 t = __builtin_nontemporal_load((const u32x4*)(p + 16 * k));
       w[4 * k] = t.x; w[4 * k + 1] = t.y; w[4 * k + 2] = t.z; w[4 * k + 3] = t.w;
     }
   } else if constexpr (A >= 8 && N % 8 == 0) {
 #pragma unroll
     for (int k = 0; k < N / 8; ++k) {
-      uint2 t = *(const uint2*)(p + 8 * k);
+      u32x2 t = __builtin_nontemporal_load((const u32x2*)(p + 8 * k));
       w[2 * k] = t.x; w[2 * k + 1] = t.y;
     }
   } else if constexpr (A >= 4 && N % 4 == 0) {
 #pragma unroll
-    for (int k = 0; k < N / 4; ++k) w[k] = *(const uint32_t*)(p + 4 * k);
+    for (int k = 0; k < N / 4; ++k) w[k] = __builtin_nontemporal_load((const uint32_t*)(p + 4 * k));
   } else {
     static_assert(N == 6, "unsupported load");
     const uint16_t* h = (const uint16_t*)p;
@@ -327,8 +342,8 @@ __device__ inline void load_tile(TileRegs<DG, CF>& r, const TileAddr& ad, int ti
   load_words<DG::KB, DG::KA>(kt + ad.koff, r.kw0);
   load_words<DG::KB, DG::KA>(kt + 16 * DG::RB + ad.koff, r.kw1);
   load_words<DG::SEG, DG::VA>(ad.v + (int64_t)tile * DG::TILE + ad.voff, r.vw);
-  r.kn = *(const NT*)(ad.kn + (int64_t)tile * 64 + ad.noff);
-  r.vn = *(const NT*)(ad.vn + (int64_t)tile * 64 + ad.noff);
+  r.kn = ld_nt<NT>(ad.kn + (int64_t)tile * 64 + ad.noff);
+  r.vn = ld_nt<NT>(ad.vn + (int64_t)tile * 64 + ad.noff);
 }
 
 /* Tile token (0..31) of slot u (0..7) of a lane in row q4 of the products. */
