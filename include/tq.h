@@ -119,9 +119,11 @@ tq_status tq_encode(tq_codebook cb, const uint16_t* x, int64_t n, int64_t x_stri
  *   k_codes: [batch][kv_heads][capacity][d*bits_k/8]     row layout
  *   v_codes: [batch][kv_heads][capacity/32][32*d*bits_v/8] value-tile layout
  *   k_norms, v_norms: fp16 [batch][kv_heads][capacity]
- * capacity % 32 == 0.  Code arrays 16-byte aligned, norm arrays 8-byte
- * aligned, layer strides multiples of 16.  Rows at or past a sequence's
- * length are never read by decode. */
+ * capacity % 32 == 0, and capacity * d * max(bits_k, bits_v) / 8 < 2^31 (one
+ * (sequence, head) stream of codes is addressed with 32-bit offsets; larger
+ * caches return TQ_ERR_UNSUPPORTED).  Code arrays 16-byte aligned, norm
+ * arrays 8-byte aligned, layer strides multiples of 16.  Rows at or past a
+ * sequence's length are never read by decode. */
 typedef struct {
   uint8_t* k_codes;
   uint8_t* v_codes;

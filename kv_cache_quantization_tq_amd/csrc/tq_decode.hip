@@ -180,45 +180,67 @@ __device__ inline uint32_t field(const uint32_t (&w)[NW], int s) {
 }
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 
-/* Streaming (non-temporal) loads: the packed cache is read once per step. */
-template <class T>
-__device__ inline T ld_nt(const uint8_t* p);
-template <>
-__device__ inline uint32_t ld_nt<uint32_t>(const uint8_t* p) {
-  return __builtin_nontemporal_load((const uint32_t*)p);
-}
-template <>
-__device__ inline uint2 ld_nt<uint2>(const uint8_t* p) {
-  const u32x2 t = __builtin_nontemporal_load((const u32x2*)p);
-  return make_uint2(t.x, t.y);
+/* Loads of the packed cache go through buffer resources: a wave-uniform
+ * stream base and size in scalar registers, a constant per-lane offset and a
+ * scalar per-tile offset, so no vector address arithmetic is needed per
+ * tile.  They are non-temporal (streaming): the cache is read once per step. */
+constexpr int kNT = 2; /* cache-policy bits of a streaming load */
+
+__device__ inline __amdgpu_buffer_rsrc_t make_stream(const uint8_t* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, 0x00020000);
 }
 
-/* Load N bytes (N % 4 == 0 or N == 6) from p, aligned to A bytes. */
+/* Load N bytes (N % 4 == 0 or N == 6) at voff + soff of a stream, aligned to
+ * A bytes. */
 template <int N, int A>
-__device__ inline void load_words(const uint8_t* p, uint32_t (&w)[(N + 3) / 4]) {
+__device__ inline void load_words(__amdgpu_buffer_rsrc_t rs, uint32_t voff, int32_t soff,
+                                  uint32_t (&w)[(N + 3) / 4]) {
   if constexpr (A >= 16 && N % 16 == 0) {
 #pragma unroll
     for (int k = 0; k < N / 16; ++k) {
-      u32x4 t = __builtin_nontemporal_load((const u32x4*)(p + 16 * k));
+      const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(rs, voff + 16 * k, soff, kNT);
       w[4 * k] = t.x; w[4 * k + 1] = t.y; w[4 * k + 2] = t.z; w[4 * k + 3] = t.w;
     }
   } else if constexpr (A >= 8 && N % 8 == 0) {
 #pragma unroll
     for (int k = 0; k < N / 8; ++k) {
-      u32x2 t = __builtin_nontemporal_load((const u32x2*)(p + 8 * k));
+      const u32x2 t = __builtin_amdgcn_raw_buffer_load_b64(rs, voff + 8 * k, soff, kNT);
       w[2 * k] = t.x; w[2 * k + 1] = t.y;
+    }
+  } else if constexpr (A >= 4 && N % 12 == 0) {
+#pragma unroll
+    for (int k = 0; k < N / 12; ++k) {
+      const u32x3 t = __builtin_amdgcn_raw_buffer_load_b96(rs, voff + 12 * k, soff, kNT);
+      w[3 * k] = t.x; w[3 * k + 1] = t.y; w[3 * k + 2] = t.z;
     }
   } else if constexpr (A >= 4 && N % 4 == 0) {
 #pragma unroll
-    for (int k = 0; k < N / 4; ++k) w[k] = __builtin_nontemporal_load((const uint32_t*)(p + 4 * k));
+    for (int k = 0; k < N / 4; ++k) w[k] = __builtin_amdgcn_raw_buffer_load_b32(rs, voff + 4 * k, soff, kNT);
   } else {
     static_assert(N == 6, "unsupported load");
-    const uint16_t* h = (const uint16_t*)p;
-    w[0] = h[0] | ((uint32_t)h[1] << 16);
-    w[1] = h[2];
+    const uint32_t h0 = __builtin_amdgcn_raw_buffer_load_b16(rs, voff, soff, kNT);
+    const uint32_t h1 = __builtin_amdgcn_raw_buffer_load_b16(rs, voff + 2, soff, kNT);
+    const uint32_t h2 = __builtin_amdgcn_raw_buffer_load_b16(rs, voff + 4, soff, kNT);
+    w[0] = h0 | (h1 << 16);
+    w[1] = h2;
   }
 }
+
+template <class T>
+__device__ inline T load_norms(__amdgpu_buffer_rsrc_t rs, uint32_t voff, int32_t soff);
+template <>
+__device__ inline uint32_t load_norms<uint32_t>(__amdgpu_buffer_rsrc_t rs, uint32_t voff, int32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(rs, voff, soff, kNT);
+}
+template <>
+__device__ inline uint2 load_norms<uint2>(__amdgpu_buffer_rsrc_t rs, uint32_t voff, int32_t soff) {
+  const u32x2 t = __builtin_amdgcn_raw_buffer_load_b64(rs, voff, soff, kNT);
+  return make_uint2(t.x, t.y);
+}
+
 
 /* v + v of the lane 8 places along in the same row (a single v_add_f32_dpp) */
 __device__ inline float ror8_add(float v) {
@@ -304,7 +326,6 @@ __device__ inline void lds_fwht(float* buf, int G) {
   }
 }
 
-/* One 32-token tile's loads for one lane. */
 /* One 32-token tile's loads for one lane.  The norms are only those of the
  * tokens whose softmax this lane computes (see tile_step): four consecutive
  * tokens (CF 2) or two (CF 4). */
@@ -325,25 +346,24 @@ struct TileRegs {
   typename NormWords<CF>::T kn, vn;
 };
 
-/* Addresses of one wave's loads: wave-uniform bases (scalar registers; the
- * per-tile advance is scalar arithmetic) plus constant per-lane offsets. */
+/* The four streams of one (layer, sequence, KV head) and a lane's offsets. */
 struct TileAddr {
-  const uint8_t* k;   /* key rows of the stream */
-  const uint8_t* v;   /* value tiles of the stream */
-  const uint8_t* kn;  /* key norms (bytes) */
-  const uint8_t* vn;  /* value norms (bytes) */
+  __amdgpu_buffer_rsrc_t k;   /* key rows */
+  __amdgpu_buffer_rsrc_t v;   /* value tiles */
+  __amdgpu_buffer_rsrc_t kn;  /* key norms */
+  __amdgpu_buffer_rsrc_t vn;  /* value norms */
   uint32_t koff, voff, noff;
 };
 
 template <class DG, int CF>
 __device__ inline void load_tile(TileRegs<DG, CF>& r, const TileAddr& ad, int tile) {
   typedef typename NormWords<CF>::T NT;
-  const uint8_t* kt = ad.k + (int64_t)tile * (32 * DG::RB);
-  load_words<DG::KB, DG::KA>(kt + ad.koff, r.kw0);
-  load_words<DG::KB, DG::KA>(kt + 16 * DG::RB + ad.koff, r.kw1);
-  load_words<DG::SEG, DG::VA>(ad.v + (int64_t)tile * DG::TILE + ad.voff, r.vw);
-  r.kn = ld_nt<NT>(ad.kn + (int64_t)tile * 64 + ad.noff);
-  r.vn = ld_nt<NT>(ad.vn + (int64_t)tile * 64 + ad.noff);
+  const int32_t kt = tile * (32 * DG::RB);
+  load_words<DG::KB, DG::KA>(ad.k, ad.koff, kt, r.kw0);
+  load_words<DG::KB, DG::KA>(ad.k, ad.koff, kt + 16 * DG::RB, r.kw1);
+  load_words<DG::SEG, DG::VA>(ad.v, ad.voff, tile * DG::TILE, r.vw);
+  r.kn = load_norms<NT>(ad.kn, ad.noff, tile * 64);
+  r.vn = load_norms<NT>(ad.vn, ad.noff, tile * 64);
 }
 
 /* Tile token (0..31) of slot u (0..7) of a lane in row q4 of the products. */
@@ -470,12 +490,14 @@ __device__ inline void tile_step(const TileRegs<DG, CF>& r,
     }
     mt = fmaxf(mt, sc[v]);
   }
-  /* max over the lanes that share the head, then over the rows */
-  if constexpr (CF == 4) mt = max_ror4(mt);
-  mt = rows_max(max_ror8(mt));
   /* a new maximum (or the wave's first tile, which sets it): move the
-   * reference and rescale the running sums; rare after the first tiles */
+   * reference and rescale the running sums; rare after the first tiles.
+   * Any lane's score above its head's reference decides it; only then is
+   * the head's maximum reduced, over the lanes that share the head and
+   * over the rows. */
   if (__builtin_expect(__any(mt > 0.0f) || first, 0)) {
+    if constexpr (CF == 4) mt = max_ror4(mt);
+    mt = rows_max(max_ror8(mt));
     const float dm = first ? mt : fmaxf(mt, 0.0f);
     const float alpha = first ? 0.0f : __builtin_amdgcn_exp2f(-dm);
     l_run *= alpha;
@@ -493,11 +515,16 @@ __device__ inline void tile_step(const TileRegs<DG, CF>& r,
   for (int v = 0; v < V; v += 2) {
     const float p0 = __builtin_amdgcn_exp2f(sc[v]), p1 = __builtin_amdgcn_exp2f(sc[v + 1]);
     l_run += p0 + p1;
-    const float m0 = mul_h(p0, vnh[v]), m1 = mul_h(p1, vnh[v + 1]);
-    const _Float16 h0 = (_Float16)m0, h1 = (_Float16)m1;
-    const _Float16 r0 = (_Float16)(m0 - (float)h0), r1 = (_Float16)(m1 - (float)h1);
-    hp[v / 2] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
-    lp[v / 2] = (uint32_t)__builtin_bit_cast(uint16_t, r0) | ((uint32_t)__builtin_bit_cast(uint16_t, r1) << 16);
+    /* fp16(p m) and the fp16 of the exact remainder p m - fp16(p m), each
+     * one mixed-precision FMA */
+    const float vn0 = (float)__builtin_bit_cast(_Float16, (uint16_t)vnh[v]);
+    const float vn1 = (float)__builtin_bit_cast(_Float16, (uint16_t)vnh[v + 1]);
+    const _Float16 h0 = (_Float16)__builtin_fmaf(p0, vn0, 0.0f);
+    const _Float16 h1 = (_Float16)__builtin_fmaf(p1, vn1, 0.0f);
+    const _Float16 r0 = (_Float16)__builtin_fmaf(p0, vn0, -(float)h0);
+    const _Float16 r1 = (_Float16)__builtin_fmaf(p1, vn1, -(float)h1);
+    hp[v / 2] = __builtin_bit_cast(uint32_t, half2v{h0, h1});
+    lp[v / 2] = __builtin_bit_cast(uint32_t, half2v{r0, r1});
   }
   /* back to the operand layout: lane (q4, n) needs slots 0..7 of column n */
   /* (all cross-lane moves run on every lane before the selects) */
@@ -581,10 +608,12 @@ decode_kernel(DecArgs a) {
 
   const int64_t sh = (int64_t)b * a.kv_heads + kv;
   TileAddr ad;
-  ad.k = a.k_codes + layer * a.ls_kc + sh * a.capacity * DG::RB;
-  ad.v = a.v_codes + layer * a.ls_vc + sh * (a.capacity / 32) * DG::TILE;
-  ad.kn = a.k_norms + layer * a.ls_kn + sh * a.capacity * 2;
-  ad.vn = a.v_norms + layer * a.ls_vn + sh * a.capacity * 2;
+  ad.k = make_stream(a.k_codes + layer * a.ls_kc + sh * a.capacity * DG::RB,
+                     (int64_t)a.capacity * DG::RB);
+  ad.v = make_stream(a.v_codes + layer * a.ls_vc + sh * (a.capacity / 32) * DG::TILE,
+                     (int64_t)(a.capacity / 32) * DG::TILE);
+  ad.kn = make_stream(a.k_norms + layer * a.ls_kn + sh * a.capacity * 2, (int64_t)a.capacity * 2);
+  ad.vn = make_stream(a.v_norms + layer * a.ls_vn + sh * a.capacity * 2, (int64_t)a.capacity * 2);
   ad.koff = (uint32_t)(n * DG::RB + q4 * DG::KB);
   ad.voff = (uint32_t)(lane * DG::SEG);
   /* norms of the tokens this lane's softmax covers (see tile_step) */

@@ -283,6 +283,10 @@ static tq_status check_cache(const tq_kv_cache* c) {
     return TQ_ERR_UNSUPPORTED;
   if (c->batch <= 0 || c->kv_heads <= 0 || c->capacity <= 0 || c->capacity % 32 != 0)
     return TQ_ERR_ARG;
+  /* one (sequence, head) stream of codes is addressed with 32-bit offsets */
+  if ((int64_t)c->capacity * c->head_dim * (c->bits_k > c->bits_v ? c->bits_k : c->bits_v) / 8 >=
+      ((int64_t)1 << 31))
+    return TQ_ERR_UNSUPPORTED;
   if (!c->k_codes || !c->v_codes || !c->k_norms || !c->v_norms) return TQ_ERR_ARG;
   if (!aligned(c->k_codes, 16) || !aligned(c->v_codes, 16) || !aligned(c->k_norms, 8) ||
       !aligned(c->v_norms, 8))

@@ -68,7 +68,8 @@ def test_validation_before_device_work():
     L = tq.lib()
     vp = ctypes.c_void_p
     bad = [dict(capacity=1000), dict(head_dim=96), dict(bits_k=5), dict(batch=0),
-           dict(k_codes=(1 << 20) + 4), dict(layer_stride_k_codes=8)]
+           dict(k_codes=(1 << 20) + 4), dict(layer_stride_k_codes=8),
+           dict(capacity=1 << 25)]  # one stream of key codes reaches 2 GiB
     for kw in bad:
         s = _fake_cache(**kw)
         rc = L.tq_append(ctypes.byref(s), None, None, vp(1), vp(16), vp(16), 1, vp(4), 0, 1, None)
