@@ -318,26 +318,39 @@ __device__ inline uint32_t encode_pass(const XRegs<D>& xr,
     b[j] = __builtin_bit_cast(half8, u32x4{x[j][0], x[j][1], x[j][2], x[j][3]});
   const float scale = S > 0.0f ? nbh * __builtin_amdgcn_rsqf(S * (float)D) : 0.0f;
   const float off = nbh + 1.0f;
+  floatx4 y[G::OB];
 #pragma unroll
   for (int ob = 0; ob < G::OB; ++ob) {
-    floatx4 y = {0.0f, 0.0f, 0.0f, 0.0f};
+    y[ob] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int j = 0; j < G::J; ++j) {
       const bool neg = __builtin_popcount((ob >> 1) & j) & 1;
-      y = __builtin_amdgcn_mfma_f32_16x16x32_f16(neg ? ht.m[ob & 1] : ht.p[ob & 1], b[j], y, 0,
-                                                 0, 0);
+      y[ob] = __builtin_amdgcn_mfma_f32_16x16x32_f16(neg ? ht.m[ob & 1] : ht.p[ob & 1], b[j],
+                                                     y[ob], 0, 0, 0);
     }
-    /* quantize: u = (y + 1) * nbh + 1, bucket floor(u) */
-    uint32_t pc = 0u;
+  }
+  /* quantize: u = (y + 1) * nbh + 1, bucket floor(u); the table reads of
+   * QB output blocks go out together */
+  constexpr int QB = 2;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float u = __builtin_fmaf(y[i], scale, off);
-      const uint32_t bk = (uint32_t)u;
-      const tq_enc_entry e = *(const tq_enc_entry*)(tab + bk * (kEncRep * sizeof(tq_enc_entry)));
-      const uint32_t code = e.base + (u > e.thr ? 1u : 0u);
-      pc |= code << (BYTES ? 8 * i : BITS * i);
+  for (int ob0 = 0; ob0 < G::OB; ob0 += QB) {
+    float u[4 * QB];
+    tq_enc_entry e[4 * QB];
+#pragma unroll
+    for (int k = 0; k < 4 * QB; ++k) u[k] = __builtin_fmaf(y[ob0 + k / 4][k % 4], scale, off);
+#pragma unroll
+    for (int k = 0; k < 4 * QB; ++k)
+      e[k] = *(const tq_enc_entry*)(tab + (uint32_t)u[k] * (kEncRep * sizeof(tq_enc_entry)));
+#pragma unroll
+    for (int q = 0; q < QB; ++q) {
+      uint32_t pc = 0u;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t code = e[4 * q + i].base + (u[4 * q + i] > e[4 * q + i].thr ? 1u : 0u);
+        pc |= code << (BYTES ? 8 * i : BITS * i);
+      }
+      piece[ob0 + q] = pc;
     }
-    piece[ob] = pc;
   }
   return n16;
 }
