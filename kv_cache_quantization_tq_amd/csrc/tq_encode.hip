@@ -418,11 +418,18 @@ __device__ inline void gather_row_chunk(const uint32_t (&piece)[EGeo<D>::OB],
 }
 
 /* Store a lane's packed row chunk at dst (dst aligned to 8 bytes when the
- * chunk size is a multiple of 8, else to 2). */
-template <int D, int BITS>
+ * chunk size is a multiple of 8, else to 2; A16: aligned to 16, and then
+ * 16-byte chunks go out as single non-temporal stores, since the cache is
+ * written once and read back much later). */
+template <int D, int BITS, bool A16 = false>
 __device__ inline void store_chunk(uint8_t* dst, const uint32_t (&p)[Chunk<D, BITS>::NW]) {
   constexpr int NB = Chunk<D, BITS>::BYTES;
-  if constexpr (NB % 8 == 0) {
+  if constexpr (A16 && NB % 16 == 0) {
+#pragma unroll
+    for (int k = 0; k < NB / 16; ++k)
+      __builtin_nontemporal_store(u32x4{p[4 * k], p[4 * k + 1], p[4 * k + 2], p[4 * k + 3]},
+                                  (u32x4*)(dst + 16 * k));
+  } else if constexpr (NB % 8 == 0) {
 #pragma unroll
     for (int k = 0; k < NB / 8; ++k) *(uint2*)(dst + 8 * k) = make_uint2(p[2 * k], p[2 * k + 1]);
   } else if constexpr (NB % 4 == 0) {
@@ -567,7 +574,7 @@ __device__ inline void build_value_tile(const uint8_t* vbuf, int lane, int jlo, 
   uint32_t* dst = (uint32_t*)(tile_dst + (int64_t)lane * (D * BV / 16));
   if (jlo == 0 && jhi == 32) {
 #pragma unroll
-    for (int k = 0; k < SW; ++k) dst[k] = seg[k];
+    for (int k = 0; k < SW; ++k) __builtin_nontemporal_store(seg[k], dst + k);
   } else {
     /* keep the other tokens' bits */
     uint32_t mask[SW];
@@ -753,8 +760,8 @@ append_kernel(AppendArgs a) {
       uint32_t out[Chunk<D, BK>::NW];
       gather_row_chunk<D, BK>(piece, out);
       if (mine) {
-        store_chunk<D, BK>(a.k_codes + g.layer * a.ls_kc + row * (D * BK / 8) +
-                               q4 * Chunk<D, BK>::BYTES, out);
+        store_chunk<D, BK, true>(a.k_codes + g.layer * a.ls_kc + row * (D * BK / 8) +
+                                     q4 * Chunk<D, BK>::BYTES, out);
         if (q4 == 0) *(uint16_t*)((uint8_t*)a.k_norms + g.layer * a.ls_kn + row * 2) = (uint16_t)n16;
       }
     } else {
