@@ -31,10 +31,11 @@
  * midpoints; otherwise the inputs are re-summed in fp64 and, if still
  * ambiguous, exactly in 128-bit integers.
  *
- * Quantizer: u = (y + 1) * nb_half + 1 = fma(h, scale, nb_half + 1) selects
- * one of the codebook's buckets in LDS (at most one threshold per bucket),
- * code = base + (u > thr).  The comparison happens in fp32 on u; it differs
- * from the exact decision only for coordinates within ~1e-7 of a threshold.
+ * Quantizer: u = (y + 1) * nb_half + 1/2 = fma(h, scale, nb_half + 1/2)
+ * selects, rounded to an integer, one of the codebook's buckets in LDS (at
+ * most one threshold per bucket), code = base + (u > thr).  The comparison
+ * happens in fp32 on u; it differs from the exact decision only for
+ * coordinates within ~1e-7 of a threshold.
  *
  * Output.  Key rows: the four lanes of a vector exchange their 4-code pieces
  * with 4 x 4 word transposes (permlane swaps), after which each lane owns d/4
@@ -268,8 +269,8 @@ __device__ inline void load_x(XRegs<D>& x, const uint16_t* vec, int q4) {
 template <int D, int BITS, bool BYTES>
 __device__ inline uint32_t encode_pass(const XRegs<D>& xr,
                                        const uint32_t (&sm)[EGeo<D>::J][4], const HTiles& ht,
-                                       const char* tab, float nbh, const uint16_t* vec,
-                                       uint32_t (&piece)[EGeo<D>::OB]) {
+                                       const char* tab, uint32_t lane_off, float nbh,
+                                       const uint16_t* vec, uint32_t (&piece)[EGeo<D>::OB]) {
   using G = EGeo<D>;
   uint32_t x[G::J][4];
 #pragma unroll
@@ -317,7 +318,7 @@ __device__ inline uint32_t encode_pass(const XRegs<D>& xr,
   for (int j = 0; j < G::J; ++j)
     b[j] = __builtin_bit_cast(half8, u32x4{x[j][0], x[j][1], x[j][2], x[j][3]});
   const float scale = S > 0.0f ? nbh * __builtin_amdgcn_rsqf(S * (float)D) : 0.0f;
-  const float off = nbh + 1.0f;
+  const float off = nbh + 0.5f;
   floatx4 y[G::OB];
 #pragma unroll
   for (int ob = 0; ob < G::OB; ++ob) {
@@ -329,8 +330,11 @@ __device__ inline uint32_t encode_pass(const XRegs<D>& xr,
                                                      y[ob], 0, 0, 0);
     }
   }
-  /* quantize: u = (y + 1) * nbh + 1, bucket floor(u); the table reads of
-   * QB output blocks go out together */
+  /* quantize: u = (y + 1) * nb_half + 1/2; bucket r = u rounded to the
+   * nearest integer (clamped to 0..255), so r - 1/2 <= u <= r + 1/2.  One
+   * conversion writes r into byte 1 of the lane's table offset, i.e. the
+   * address of row r, copy lane % 32.  The table reads of QB output blocks go
+   * out together. */
   constexpr int QB = 2;
 #pragma unroll
   for (int ob0 = 0; ob0 < G::OB; ob0 += QB) {
@@ -340,7 +344,7 @@ __device__ inline uint32_t encode_pass(const XRegs<D>& xr,
     for (int k = 0; k < 4 * QB; ++k) u[k] = __builtin_fmaf(y[ob0 + k / 4][k % 4], scale, off);
 #pragma unroll
     for (int k = 0; k < 4 * QB; ++k)
-      e[k] = *(const tq_enc_entry*)(tab + (uint32_t)u[k] * (kEncRep * sizeof(tq_enc_entry)));
+      e[k] = *(const tq_enc_entry*)(tab + __builtin_amdgcn_cvt_pk_u8_f32(u[k], 1, lane_off));
 #pragma unroll
     for (int q = 0; q < QB; ++q) {
       uint32_t pc = 0u;
@@ -447,10 +451,6 @@ __device__ inline void load_table(tq_enc_entry* dst, const tq_enc_entry* src, in
   for (int i = threadIdx.x; i < entries * kEncRep; i += blockDim.x) dst[i] = src[i / kEncRep];
 }
 
-__host__ __device__ inline int table_bytes(int entries) {
-  return (entries * kEncRep * (int)sizeof(tq_enc_entry) + 15) & ~15;
-}
-
 constexpr int kRowsWaves = 4;
 
 /* tq_encode: n vectors, row layout.  Each wave takes passes grid-stride and
@@ -463,8 +463,9 @@ encode_rows_kernel(const uint16_t* __restrict__ x, int64_t n, int64_t stride,
                    int entries, float nbh, uint8_t* __restrict__ codes,
                    uint16_t* __restrict__ norms) {
   using G = EGeo<D>;
-  extern __shared__ __align__(16) char smem[];
-  tq_enc_entry* tab = (tq_enc_entry*)smem;
+  /* static LDS: the table's address is a constant, folded into the reads */
+  constexpr int kRows = tq_enc_rows_max(D, BITS);
+  __shared__ __align__(16) tq_enc_entry tab[kRows * kEncRep];
   const int lane = threadIdx.x % 64, q4 = lane / 16, nl = lane % 16;
   const int64_t passes = (n + kVec - 1) / kVec;
   const int64_t wstride = (int64_t)gridDim.x * kRowsWaves;
@@ -477,10 +478,10 @@ encode_rows_kernel(const uint16_t* __restrict__ x, int64_t n, int64_t stride,
   /* the first pass's loads go out before the table is built */
   XRegs<D> xa, xb;
   load_x<D>(xa, x + row_of(ps < passes ? ps : passes - 1) * stride, q4);
-  load_table(tab, table, entries);
+  load_table(tab, table, entries < kRows ? entries : kRows);
   __syncthreads();
   if (ps >= passes) return;
-  const char* mytab = (const char*)tab + (lane & (kEncRep - 1)) * sizeof(tq_enc_entry);
+  const uint32_t tab_off = (uint32_t)(lane & (kEncRep - 1)) * sizeof(tq_enc_entry);
   uint32_t sm[G::J][4];
   sign_masks<D>(sign_bits, q4, sm);
   const HTiles ht = h_tiles(nl, q4);
@@ -488,7 +489,7 @@ encode_rows_kernel(const uint16_t* __restrict__ x, int64_t n, int64_t stride,
     const int64_t r = p * kVec + nl;
     const bool valid = r < n;
     uint32_t piece[G::OB];
-    const uint32_t n16 = encode_pass<D, BITS, false>(xr, sm, ht, mytab, nbh,
+    const uint32_t n16 = encode_pass<D, BITS, false>(xr, sm, ht, (const char*)tab, tab_off, nbh,
                                                      x + row_of(p) * stride, piece);
     uint32_t out[Chunk<D, BITS>::NW];
     gather_row_chunk<D, BITS>(piece, out);
@@ -681,18 +682,21 @@ template <int D, int BK, int BV>
 __global__ void __launch_bounds__(64 * kAppendWaves) __attribute__((amdgpu_waves_per_eu(D == 256 ? 2 : TQ_ENC_WPE)))
 append_kernel(AppendArgs a) {
   using G = EGeo<D>;
-  extern __shared__ __align__(16) char smem[];
+  /* static LDS: the table's address is a constant, folded into the reads */
+  constexpr int kRows = tq_enc_rows_max(D, BK) > tq_enc_rows_max(D, BV) ? tq_enc_rows_max(D, BK)
+                                                                       : tq_enc_rows_max(D, BV);
+  __shared__ __align__(16) tq_enc_entry tab[kRows * kEncRep];
+  __shared__ __align__(16) uint8_t vbuf_all[kTPB * 32 * kVPitch<D>];
   const bool is_v = blockIdx.y == 1;
-  const int ent = is_v ? a.ent_v : a.ent_k;
-  const int tb = table_bytes(a.ent_k > a.ent_v ? a.ent_k : a.ent_v);
-  tq_enc_entry* tab = (tq_enc_entry*)smem;
+  int ent = is_v ? a.ent_v : a.ent_k;
+  if (ent > kRows) ent = kRows;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64), lane = threadIdx.x % 64;
   const int q4 = lane / 16, nl = lane % 16;
   const int slot_in_block = wave / 2, sub = wave % 2;
   /* tile codes [row][coord], rows padded by 16 bytes so that the 64 lanes'
    * 4-byte writes of one output block fall on distinct banks */
-  uint8_t* vbuf = (uint8_t*)(smem + tb) + slot_in_block * 32 * kVPitch<D>;
-  const char* mytab = (const char*)tab + (lane & (kEncRep - 1)) * sizeof(tq_enc_entry);
+  uint8_t* vbuf = vbuf_all + slot_in_block * 32 * kVPitch<D>;
+  const uint32_t tab_off = (uint32_t)(lane & (kEncRep - 1)) * sizeof(tq_enc_entry);
   const float nbh = is_v ? a.nbh_v : a.nbh_k;
   const uint16_t* src_all = is_v ? a.v_new : a.k_new;
   const int64_t tasks = (int64_t)a.n_layers * a.batch * a.heads * a.slots;
@@ -756,7 +760,8 @@ append_kernel(AppendArgs a) {
     const uint16_t* vec = lane_src(g);
     uint32_t piece[G::OB];
     if (!is_v) {
-      const uint32_t n16 = encode_pass<D, BK, false>(xr, sm, ht, mytab, nbh, vec, piece);
+      const uint32_t n16 = encode_pass<D, BK, false>(xr, sm, ht, (const char*)tab, tab_off, nbh, vec,
+                                                     piece);
       uint32_t out[Chunk<D, BK>::NW];
       gather_row_chunk<D, BK>(piece, out);
       if (mine) {
@@ -765,7 +770,8 @@ append_kernel(AppendArgs a) {
         if (q4 == 0) *(uint16_t*)((uint8_t*)a.k_norms + g.layer * a.ls_kn + row * 2) = (uint16_t)n16;
       }
     } else {
-      const uint32_t n16 = encode_pass<D, BV, true>(xr, sm, ht, mytab, nbh, vec, piece);
+      const uint32_t n16 = encode_pass<D, BV, true>(xr, sm, ht, (const char*)tab, tab_off, nbh, vec,
+                                                    piece);
       /* code bytes of coordinates 16 ob + 4 q4 .. +3 -> vbuf[jrow] */
 #pragma unroll
       for (int ob = 0; ob < G::OB; ++ob)
@@ -817,9 +823,8 @@ tq_status launch_rows_t(const tq_codebook_s* cb, const uint16_t* x, int64_t n, i
   const int64_t passes = (n + kVec - 1) / kVec;
   int64_t blocks = (passes + kRowsWaves - 1) / kRowsWaves;
   if (blocks > 4096) blocks = 4096;
-  const size_t lds = table_bytes(cb->enc_entries);
   hipLaunchKernelGGL((encode_rows_kernel<D, BITS>), dim3((unsigned)blocks), dim3(64 * kRowsWaves),
-                     lds, s, x, n, stride, sb, cb->enc_table, cb->enc_entries,
+                     0, s, x, n, stride, sb, cb->enc_table, cb->enc_entries,
                      (float)cb->nb_half, codes, norms);
   return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_DEVICE;
 }
@@ -831,10 +836,8 @@ tq_status launch_append_t(AppendArgs a, hipStream_t s) {
   int64_t blocks = pairs < 2048 ? pairs : 2048;
   a.chunk = (pairs + blocks - 1) / blocks;
   blocks = (pairs + a.chunk - 1) / a.chunk;
-  const size_t lds = table_bytes(a.ent_k > a.ent_v ? a.ent_k : a.ent_v) +
-                     (size_t)kTPB * 32 * kVPitch<D>;
   hipLaunchKernelGGL((append_kernel<D, BK, BV>), dim3((unsigned)blocks, 2), dim3(64 * kAppendWaves),
-                     lds, s, a);
+                     0, s, a);
   return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_DEVICE;
 }
 

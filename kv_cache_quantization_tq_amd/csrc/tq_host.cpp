@@ -168,16 +168,22 @@ extern "C" tq_status tq_codebook_init(int head_dim, int bits, tq_codebook* out) 
   const int ne = cb->enc_entries;
   tq_enc_entry* et = (tq_enc_entry*)calloc((size_t)ne, sizeof(tq_enc_entry));
   float thr_u[15];
-  for (int k = 0; k + 1 < L; ++k) thr_u[k] = (float)((cb->bounds64[k] + 1.0) * cb->nb_half + 1.0);
+  for (int k = 0; k + 1 < L; ++k) thr_u[k] = (float)((cb->bounds64[k] + 1.0) * cb->nb_half + 0.5);
   for (int j = 0; j < ne; ++j) {
     uint32_t base = 0;
-    float thr = (float)(j + 1);
+    float thr = INFINITY;
     int inside = 0;
     for (int k = 0; k + 1 < L; ++k) {
-      if (thr_u[k] < (float)j) ++base;
-      else if (thr_u[k] < (float)(j + 1)) { thr = thr_u[k]; ++inside; }
+      if (thr_u[k] < (float)j - 0.5f) ++base;
+      else if (thr_u[k] < (float)j + 0.5f) { thr = thr_u[k]; ++inside; }
     }
-    if (inside > 1) { free(et); free(cb); return TQ_ERR_UNSUPPORTED; }
+    /* one threshold per bucket; none where the device clamps the bucket or
+     * past the rows the kernels keep */
+    if (inside > 1 || (inside && (j >= 255 || j >= tq_enc_rows_max(head_dim, bits)))) {
+      free(et);
+      free(cb);
+      return TQ_ERR_UNSUPPORTED;
+    }
     et[j].thr = thr;
     et[j].base = base;
   }
