@@ -43,9 +43,10 @@
  *     into 64 segments of d*bits/16 bytes.  Segment l = 16*q + r (q in 0..3,
  *     r in 0..15) is a little-endian bit string holding, for m in 0..d/16-1 and
  *     u in 0..7, at bit offset (8*m + u)*bits, the code of coordinate
- *     r*(d/16) + m of tile token tok(q,u) = 4q + u (u < 4) or 16 + 4q + u - 4
- *     (u >= 4).  The order matches the matrix-core operand layout of the
- *     decode kernel, so one 16-byte load per lane feeds its value products.
+ *     r*(d/16) + m of tile token tok(q,u) = 8q + u.  The order matches the
+ *     matrix-core operand layout of the decode kernel, so one load per lane
+ *     feeds its value products, and each half tile (16 tokens) is a
+ *     contiguous half of the bytes.
  *   Norms: fp16 (RNE of the exact Euclidean norm), one per vector.
  *   Sign bits: d bits per layer, LSB-first in d/8 bytes; bit i set means
  *     D_ii = -1.

@@ -27,9 +27,10 @@
  * minimise their fp16 rounding; sigma is divided out of the query and output.
  *
  * Lane roles in a wave (lane = 16 q4 + n):
- *   K operand: token n of a 16-token block, coordinates [q4 d/4, (q4+1) d/4)
- *              of its row, which is one contiguous d*bits/32-byte load;
- *   score out: tokens 4 q4 .. 4 q4 + 3 of the block, column n;
+ *   K operand: tile token 8 (n / 4) + n % 4 (first product) or that + 4
+ *              (second), coordinates [q4 d/4, (q4+1) d/4) of its row, one
+ *              contiguous d*bits/32-byte load;
+ *   score out: tile tokens 8 q4 .. 8 q4 + 7 (four per product), column n;
  *   V operand: segment lane of the 32-token value tile (see tq.h);
  *   value out: coordinates [q4 d/4, (q4+1) d/4) of head n.
  */
@@ -360,14 +361,14 @@ __device__ inline void load_tile(TileRegs<DG, CF>& r, const TileAddr& ad, int ti
   typedef typename NormWords<CF>::T NT;
   const int32_t kt = tile * (32 * DG::RB);
   load_words<DG::KB, DG::KA>(ad.k, ad.koff, kt, r.kw0);
-  load_words<DG::KB, DG::KA>(ad.k, ad.koff, kt + 16 * DG::RB, r.kw1);
+  load_words<DG::KB, DG::KA>(ad.k, ad.koff, kt + 4 * DG::RB, r.kw1);
   load_words<DG::SEG, DG::VA>(ad.v, ad.voff, tile * DG::TILE, r.vw);
   r.kn = load_norms<NT>(ad.kn, ad.noff, tile * 64);
   r.vn = load_norms<NT>(ad.vn, ad.noff, tile * 64);
 }
 
 /* Tile token (0..31) of slot u (0..7) of a lane in row q4 of the products. */
-__device__ inline int tok_of(int q4, int u) { return u < 4 ? 4 * q4 + u : 16 + 4 * q4 + (u - 4); }
+__device__ inline int tok_of(int q4, int u) { return 8 * q4 + u; }
 
 /* DPP move within 16-lane rows (lanes whose source lies outside the row
  * read 0). */
@@ -614,7 +615,9 @@ decode_kernel(DecArgs a) {
                      (int64_t)(a.capacity / 32) * DG::TILE);
   ad.kn = make_stream(a.k_norms + layer * a.ls_kn + sh * a.capacity * 2, (int64_t)a.capacity * 2);
   ad.vn = make_stream(a.v_norms + layer * a.ls_vn + sh * a.capacity * 2, (int64_t)a.capacity * 2);
-  ad.koff = (uint32_t)(n * DG::RB + q4 * DG::KB);
+  /* score rows: row 4 i + j of the first product is tile token 8 i + j, of
+   * the second 8 i + 4 + j (so that slot u of row group q4 is token 8 q4 + u) */
+  ad.koff = (uint32_t)((8 * (n >> 2) + (n & 3)) * DG::RB + q4 * DG::KB);
   ad.voff = (uint32_t)(lane * DG::SEG);
   /* norms of the tokens this lane's softmax covers (see tile_step) */
   ad.noff = (uint32_t)(2 * tok_of(q4, CF == 2 ? 4 * (n >> 3) : 2 * (n >> 2)));

@@ -39,8 +39,9 @@
  *
  * Output.  Key rows: the four lanes of a vector exchange their 4-code pieces
  * with 4 x 4 word transposes (permlane swaps), after which each lane owns d/4
- * consecutive coordinates and stores them packed.  Value tiles: code bytes go
- * to an LDS tile buffer from which the tile's 64 segments are built.
+ * consecutive coordinates and stores them packed.  Value tiles: a wave's 16
+ * tokens are one contiguous half of a tile; their code bytes go to the wave's
+ * own LDS rows, from which each lane packs half a segment (no block barrier).
  */
 #include <hip/hip_runtime.h>
 
@@ -55,6 +56,7 @@ namespace {
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kVec = 16;     /* vectors per wave pass (the matrix-core N) */
 constexpr int kEncRep = 32;  /* copies of the bucket table (lane % 32): a 64-bit LDS read
@@ -331,7 +333,7 @@ __device__ inline uint32_t encode_pass(const XRegs<D>& xr,
     }
   }
   /* quantize: u = (y + 1) * nb_half + 1/2; bucket r = u rounded to the
-   * nearest integer (clamped to 0..255), so r - 1/2 <= u <= r + 1/2.  One
+   * nearest integer, so r - 1/2 <= u <= r + 1/2.  One (saturating)
    * conversion writes r into byte 1 of the lane's table offset, i.e. the
    * address of row r, copy lane % 32.  The table reads of QB output blocks go
    * out together. */
@@ -478,7 +480,7 @@ encode_rows_kernel(const uint16_t* __restrict__ x, int64_t n, int64_t stride,
   /* the first pass's loads go out before the table is built */
   XRegs<D> xa, xb;
   load_x<D>(xa, x + row_of(ps < passes ? ps : passes - 1) * stride, q4);
-  load_table(tab, table, entries < kRows ? entries : kRows);
+  load_table(tab, table, entries);
   __syncthreads();
   if (ps >= passes) return;
   const uint32_t tab_off = (uint32_t)(lane & (kEncRep - 1)) * sizeof(tq_enc_entry);
@@ -514,85 +516,134 @@ encode_rows_kernel(const uint16_t* __restrict__ x, int64_t n, int64_t stride,
 
 /* ------------------------------------------------------------- append -- */
 
-__device__ inline int tile_token(int q, int u) { return u < 4 ? 4 * q + u : 16 + 4 * q + (u - 4); }
-
-/* Row pitch of the value-tile code buffer. */
+/* Row pitch of a wave's value-code buffer (16 rows, one per token; the
+ * padding puts the 64 lanes' 4-byte writes of one output block on distinct
+ * banks). */
 template <int D>
 constexpr int kVPitch = D + 16;
 
-/* The codes of one token's coordinates r M .. r M + M - 1 (M = d/16 bytes). */
-template <int D>
-struct TokCodes {
-  uint32_t w[D / 64];
-};
-template <int D>
-__device__ inline TokCodes<D> read_tok(const uint8_t* p) {
-  TokCodes<D> t;
-  if constexpr (D == 64) {
-    t.w[0] = *(const uint32_t*)p;
-  } else if constexpr (D == 128) {
-    const uint2 v = *(const uint2*)p;
-    t.w[0] = v.x;
-    t.w[1] = v.y;
+/* N bytes (2, 4 or 8) of LDS as words. */
+template <int N>
+__device__ inline void read_codes(const uint8_t* p, uint32_t (&w)[(N + 3) / 4]) {
+  if constexpr (N == 2) {
+    w[0] = *(const uint16_t*)p;
+  } else if constexpr (N == 4) {
+    w[0] = *(const uint32_t*)p;
   } else {
-    const uint4 v = *(const uint4*)p;
-    t.w[0] = v.x;
-    t.w[1] = v.y;
-    t.w[2] = v.z;
-    t.w[3] = v.w;
+    const uint2 v = *(const uint2*)p;
+    w[0] = v.x;
+    w[1] = v.y;
   }
-  return t;
 }
 
-/* Build segment `lane` (q = lane / 16, r = lane % 16) of a value tile from
- * the code bytes in vbuf (rows = tile tokens, kVPitch bytes apart) and store
- * it at tile_dst: for m < d/16 and u < 8, the code of coordinate r d/16 + m of
- * token tile_token(q, u) at bit (8 m + u) BV.  Tokens outside [jlo, jhi) keep
- * the bits already in memory. */
+/* Build this wave's half of a value tile.  The wave's 16 tokens are tile
+ * tokens 16 sub .. 16 sub + 15, i.e. segments 32 sub .. 32 sub + 31 (the
+ * segment l = 16 q + r holds, for m < d/16 and u < 8, the code of coordinate
+ * r d/16 + m of tile token 8 q + u at bit (8 m + u) BV).  Lane L writes half
+ * L % 2 of local segment L / 2: fields m in [h d/32, (h + 1) d/32), i.e. one
+ * contiguous run of d/32 code bytes from each of the segment's 8 token rows
+ * of vbuf (the wave's 16 rows of code bytes, kVPitch apart).  Tokens outside
+ * [lo, hi) (wave-local rows) keep the bits already in memory; dst is the
+ * wave's half tile. */
 template <int D, int BV>
-__device__ inline void build_value_tile(const uint8_t* vbuf, int lane, int jlo, int jhi,
-                                        uint8_t* tile_dst) {
-  constexpr int M = D / 16;
-  constexpr int SW = D * BV / 64; /* segment words */
-  const int q = lane / 16, rr = lane % 16;
-  uint32_t seg[SW];
+__device__ inline void build_value_half(const uint8_t* vbuf, int lane, int lo, int hi,
+                                        uint8_t* dst) {
+  constexpr int MH = D / 32;               /* fields (coordinates) per lane */
+  constexpr int NW = (MH + 3) / 4;         /* words per token row read */
+  constexpr int OB = MH * BV;              /* output bytes per lane (8 tokens x MH x BV bits) */
+  constexpr int OW = (OB + 3) / 4;
+  const int s = lane >> 1, h = lane & 1, ql = s >> 4, r = s & 15;
+  uint32_t x[8][NW];
 #pragma unroll
-  for (int k = 0; k < SW; ++k) seg[k] = 0u;
-  uint32_t valid_u = 0u; /* bit u: token u of the segment is being written */
+  for (int u = 0; u < 8; ++u)
+    read_codes<MH>(vbuf + (8 * ql + u) * kVPitch<D> + r * (D / 16) + h * MH, x[u]);
+  uint32_t out[OW];
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const int tj = tile_token(q, u);
-    valid_u |= (tj >= jlo && tj < jhi ? 1u : 0u) << u;
-    const TokCodes<D> t = read_tok<D>(vbuf + tj * kVPitch<D> + rr * M);
+  for (int k = 0; k < OW; ++k) out[k] = 0u;
+  if constexpr (BV == 2) {
+    /* bytes of A (B): tokens 0..3 (4..7) of one field, two bits each; field
+     * i = 16 bits [A_i, B_i] */
 #pragma unroll
-    for (int m = 0; m < M; ++m) {
-      const uint32_t c = __builtin_amdgcn_ubfe(t.w[m / 4], 8 * (m % 4), 8);
-      const int bit = (8 * m + u) * BV;
-      seg[bit / 32] |= c << (bit % 32);
-      if ((bit % 32) + BV > 32) seg[bit / 32 + 1] |= c >> (32 - bit % 32);
+    for (int w = 0; w < NW; ++w) {
+      const uint32_t A = (x[0][w] | (x[1][w] << 2)) | ((x[2][w] | (x[3][w] << 2)) << 4);
+      const uint32_t B = (x[4][w] | (x[5][w] << 2)) | ((x[6][w] | (x[7][w] << 2)) << 4);
+      out[2 * w] = __builtin_amdgcn_perm(B, A, 0x05010400u);
+      if (2 * w + 1 < OW) out[2 * w + 1] = __builtin_amdgcn_perm(B, A, 0x07030602u);
+    }
+  } else if constexpr (BV == 4) {
+    /* bytes of t_k: tokens 2k, 2k + 1 of one field; field i = 32 bits
+     * [t0_i, t1_i, t2_i, t3_i] */
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      uint32_t t[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) t[k] = x[2 * k][w] | (x[2 * k + 1][w] << 4);
+      const uint32_t P = __builtin_amdgcn_perm(t[1], t[0], 0x05010400u);
+      const uint32_t Q = __builtin_amdgcn_perm(t[3], t[2], 0x05010400u);
+      const uint32_t R = __builtin_amdgcn_perm(t[1], t[0], 0x07030602u);
+      const uint32_t S = __builtin_amdgcn_perm(t[3], t[2], 0x07030602u);
+      const uint32_t f[4] = {__builtin_amdgcn_perm(Q, P, 0x05040100u),
+                             __builtin_amdgcn_perm(Q, P, 0x07060302u),
+                             __builtin_amdgcn_perm(S, R, 0x05040100u),
+                             __builtin_amdgcn_perm(S, R, 0x07060302u)};
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if (4 * w + k < MH) out[4 * w + k] = f[k];
+    }
+  } else {
+    /* 3 bits: field i = 24 bits, tokens u at 3 u */
+#pragma unroll
+    for (int i = 0; i < MH; ++i) {
+      uint32_t f = 0u;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) f |= __builtin_amdgcn_ubfe(x[u][i / 4], 8 * (i % 4), 3) << (3 * u);
+      const int bit = 24 * i;
+      out[bit / 32] |= f << (bit % 32);
+      if ((bit % 32) + 24 > 32) out[bit / 32 + 1] |= f >> (32 - bit % 32);
     }
   }
-  uint32_t* dst = (uint32_t*)(tile_dst + (int64_t)lane * (D * BV / 16));
-  if (jlo == 0 && jhi == 32) {
+  uint8_t* d = dst + lane * OB;
+  const int t0 = 8 * ql; /* wave-local row of token u = 0 */
+  if (lo <= t0 && t0 + 8 <= hi) {
+    if constexpr (OB % 16 == 0) {
 #pragma unroll
-    for (int k = 0; k < SW; ++k) __builtin_nontemporal_store(seg[k], dst + k);
+      for (int k = 0; k < OB / 16; ++k)
+        __builtin_nontemporal_store(u32x4{out[4 * k], out[4 * k + 1], out[4 * k + 2], out[4 * k + 3]},
+                                    (u32x4*)(d + 16 * k));
+    } else if constexpr (OB % 8 == 0) {
+#pragma unroll
+      for (int k = 0; k < OB / 8; ++k)
+        __builtin_nontemporal_store(u32x2{out[2 * k], out[2 * k + 1]}, (u32x2*)(d + 8 * k));
+    } else if constexpr (OB % 4 == 0) {
+#pragma unroll
+      for (int k = 0; k < OB / 4; ++k) __builtin_nontemporal_store(out[k], (uint32_t*)(d + 4 * k));
+    } else {
+#pragma unroll
+      for (int k = 0; k < OB / 2; ++k)
+        *(uint16_t*)(d + 2 * k) = (uint16_t)(out[k / 2] >> (16 * (k & 1)));
+    }
   } else {
-    /* keep the other tokens' bits */
-    uint32_t mask[SW];
+    /* partly covered: keep the other tokens' bits (16-bit pieces; OB is even) */
+    uint32_t mask[OW];
 #pragma unroll
-    for (int k = 0; k < SW; ++k) mask[k] = 0u;
+    for (int k = 0; k < OW; ++k) mask[k] = 0u;
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const uint32_t f = (valid_u >> u) & 1u ? ((1u << BV) - 1u) : 0u;
+      const uint32_t f = (t0 + u >= lo && t0 + u < hi) ? ((1u << BV) - 1u) : 0u;
 #pragma unroll
-      for (int m = 0; m < M; ++m) {
-        const int bit = (8 * m + u) * BV;
+      for (int i = 0; i < MH; ++i) {
+        const int bit = (8 * i + u) * BV;
         mask[bit / 32] |= f << (bit % 32);
         if ((bit % 32) + BV > 32) mask[bit / 32 + 1] |= f >> (32 - bit % 32);
       }
     }
 #pragma unroll
-    for (int k = 0; k < SW; ++k) dst[k] = (dst[k] & ~mask[k]) | (seg[k] & mask[k]);
+    for (int k = 0; k < OB / 2; ++k) {
+      const uint32_t sh = 16 * (k & 1);
+      const uint32_t m = (mask[k / 2] >> sh) & 0xFFFFu;
+      uint16_t* p = (uint16_t*)(d + 2 * k);
+      *p = (uint16_t)((*p & ~m) | ((out[k / 2] >> sh) & m));
+    }
   }
 }
 
@@ -686,16 +737,14 @@ append_kernel(AppendArgs a) {
   constexpr int kRows = tq_enc_rows_max(D, BK) > tq_enc_rows_max(D, BV) ? tq_enc_rows_max(D, BK)
                                                                        : tq_enc_rows_max(D, BV);
   __shared__ __align__(16) tq_enc_entry tab[kRows * kEncRep];
-  __shared__ __align__(16) uint8_t vbuf_all[kTPB * 32 * kVPitch<D>];
+  __shared__ __align__(16) uint8_t vbuf_all[kAppendWaves * kVec * kVPitch<D>];
   const bool is_v = blockIdx.y == 1;
-  int ent = is_v ? a.ent_v : a.ent_k;
-  if (ent > kRows) ent = kRows;
+  const int ent = is_v ? a.ent_v : a.ent_k; /* <= kRows (checked by the codebook build) */
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64), lane = threadIdx.x % 64;
   const int q4 = lane / 16, nl = lane % 16;
   const int slot_in_block = wave / 2, sub = wave % 2;
-  /* tile codes [row][coord], rows padded by 16 bytes so that the 64 lanes'
-   * 4-byte writes of one output block fall on distinct banks */
-  uint8_t* vbuf = vbuf_all + slot_in_block * 32 * kVPitch<D>;
+  /* the wave's value codes [row][coord], one row per token of its pass */
+  uint8_t* vbuf = vbuf_all + wave * kVec * kVPitch<D>;
   const uint32_t tab_off = (uint32_t)(lane & (kEncRep - 1)) * sizeof(tq_enc_entry);
   const float nbh = is_v ? a.nbh_v : a.nbh_k;
   const uint16_t* src_all = is_v ? a.v_new : a.k_new;
@@ -772,24 +821,30 @@ append_kernel(AppendArgs a) {
     } else {
       const uint32_t n16 = encode_pass<D, BV, true>(xr, sm, ht, (const char*)tab, tab_off, nbh, vec,
                                                     piece);
-      /* code bytes of coordinates 16 ob + 4 q4 .. +3 -> vbuf[jrow] */
+      /* code bytes of coordinates 16 ob + 4 q4 .. +3 -> the wave's row nl */
 #pragma unroll
       for (int ob = 0; ob < G::OB; ++ob)
-        *(uint32_t*)(vbuf + jrow * kVPitch<D> + 16 * ob + 4 * q4) = piece[ob];
+        *(uint32_t*)(vbuf + nl * kVPitch<D> + 16 * ob + 4 * q4) = piece[ob];
       if (mine && q4 == 0)
         *(uint16_t*)((uint8_t*)a.v_norms + g.layer * a.ls_vn + row * 2) = (uint16_t)n16;
-      __syncthreads();
-      /* the first wave of each tile builds the 64 segments of its tile */
-      if (g.live && sub == 0)
-        build_value_tile<D, BV>(vbuf, lane, g.jlo, g.jhi,
+      /* the wave's own rows only: a wave-level fence orders the writes and
+       * the reads of other lanes (LDS operations of a wave run in order) */
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      if (g.live && g.jhi > j0 && g.jlo < j0 + kVec)
+        build_value_half<D, BV>(vbuf, lane, g.jlo - j0, g.jhi - j0,
                                 a.v_codes + g.layer * a.ls_vc +
                                     (((int64_t)g.b * a.heads + g.h) * (a.capacity / 32) + g.tile) *
-                                        (32 * D * BV / 8));
-      __syncthreads(); /* vbuf is reused by the next task */
+                                        (32 * D * BV / 8) +
+                                    sub * (16 * D * BV / 8));
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
   };
 
-  /* every wave of the block runs the same iterations (barriers inside) */
+  /* every wave of the block runs the same iterations */
   /* the first pair's loads go out before the table is built */
   XRegs<D> xa, xb;
   TaskIter tnext = task_at(a, first * kTPB + slot_in_block);

@@ -144,11 +144,12 @@ static tq_status build_codebook(int d, int bits, tq_codebook_s* cb) {
   tq_lloyd_max_host(d, bits, cb->centroids64, cb->bounds64);
   for (int k = 0; k < L; ++k) cb->centroids[k] = (float)cb->centroids64[k];
   for (int k = 0; k + 1 < L; ++k) cb->bounds[k] = (float)cb->bounds64[k];
-  /* bucket width <= 0.8 of the closest threshold gap */
+  /* bucket width below 1/1.02 of the closest threshold gap, so that no
+   * bucket holds two thresholds */
   double gap = 1e300;
   for (int k = 0; k + 2 < L; ++k) gap = fmin(gap, cb->bounds64[k + 1] - cb->bounds64[k]);
   int nbh = 1;
-  while (nbh * gap < 1.25) nbh *= 2;
+  while (nbh * gap <= 1.02) nbh *= 2;
   cb->nb_half = nbh;
   cb->enc_entries = 2 * nbh + 2;
   cb->sigma = lut_scale(cb->centroids64, L);
@@ -177,9 +178,8 @@ extern "C" tq_status tq_codebook_init(int head_dim, int bits, tq_codebook* out) 
       if (thr_u[k] < (float)j - 0.5f) ++base;
       else if (thr_u[k] < (float)j + 0.5f) { thr = thr_u[k]; ++inside; }
     }
-    /* one threshold per bucket; none where the device clamps the bucket or
-     * past the rows the kernels keep */
-    if (inside > 1 || (inside && (j >= 255 || j >= tq_enc_rows_max(head_dim, bits)))) {
+    /* one threshold per bucket, and no more rows than the kernels keep */
+    if (inside > 1 || ne > tq_enc_rows_max(head_dim, bits)) {
       free(et);
       free(cb);
       return TQ_ERR_UNSUPPORTED;

@@ -12,26 +12,27 @@
 
 /* Encoder bucket table: the rotated, normalised coordinate y in [-1, 1] maps
  * to u = (y + 1) * nb_half + 1/2 and bucket r = u rounded to an integer (any
- * rounding that keeps r - 1/2 <= u <= r + 1/2), r in 0 .. 2*nb_half + 1, and
- * clamped to 255.  Bucket r holds the thresholds in [r - 1/2, r + 1/2) of u,
- * at most one: code = base + (u > thr), base the number of thresholds below
- * r - 1/2; that count is right on the closed interval too.  Buckets without a
- * threshold store thr = +inf.  No threshold lies in a bucket at or past 255,
- * so the clamp never changes a code. */
+ * rounding that keeps r - 1/2 <= u <= r + 1/2), r in 0 .. 2*nb_half + 1 (a
+ * few ulps beyond |y| = 1 still round into that range).  Bucket r holds the
+ * thresholds in [r - 1/2, r + 1/2) of u, at most one: code = base +
+ * (u > thr), base the number of thresholds below r - 1/2; that count is right
+ * on the closed interval too.  Buckets without a threshold store
+ * thr = +inf. */
 struct tq_enc_entry {
   float thr;
   uint32_t base;
 };
 
 /* Rows of the encoder table a kernel keeps for (d, bits): 2 * nb_half + 2 for
- * the nb_half the codebook build picks (16 / 32 / 64 buckets per unit of y for
- * 2 / 3 / 4 bits at d <= 128, twice that at d = 256), capped at 256 since
- * rows past 255 are never addressed.  The codebook build checks its table
- * against this bound. */
+ * the nb_half the codebook build picks (the smallest power of two whose
+ * buckets are narrower than the closest pair of thresholds with a 2% margin:
+ * 16 / 32 / 32 buckets per unit of y for 2 / 3 / 4 bits at d = 64,
+ * 16 / 32 / 64 at d = 128, 32 / 64 / 64 at d = 256).  The codebook build
+ * checks its table against this bound. */
 __host__ __device__ constexpr int tq_enc_rows_max(int d, int bits) {
-  return (2 * ((d == 256 ? 2 : 1) * (bits == 2 ? 16 : bits == 3 ? 32 : 64)) + 2) > 256
-             ? 256
-             : 2 * ((d == 256 ? 2 : 1) * (bits == 2 ? 16 : bits == 3 ? 32 : 64)) + 2;
+  return 2 * (bits == 2 ? (d == 256 ? 32 : 16)
+                        : bits == 3 ? (d == 256 ? 64 : 32) : (d == 64 ? 32 : 64)) +
+         2;
 }
 
 struct tq_codebook_s {

@@ -262,9 +262,9 @@ void orc_unpack_rows(const uint8_t* packed, int64_t n, int d, int bits, uint8_t*
  * 32*d*bits/8 bytes, cut into 64 segments of d*bits/16 bytes.  Segment
  * l = 16 q + r (q in 0..3, r in 0..15) is a little-endian bit string holding,
  * for m in 0..d/16-1 and u in 0..7, at bit offset (8 m + u) * bits, the code of
- * coordinate r * (d/16) + m of tile token tok(q, u) = 4 q + u (u < 4) or
- * 16 + 4 q + (u - 4) (u >= 4).  codes[32][d] are the tile's tokens in order. */
-static int tile_token(int q, int u) { return u < 4 ? 4 * q + u : 16 + 4 * q + (u - 4); }
+ * coordinate r * (d/16) + m of tile token tok(q, u) = 8 q + u.  codes[32][d]
+ * are the tile's tokens in order. */
+static int tile_token(int q, int u) { return 8 * q + u; }
 
 void orc_pack_vtile(const uint8_t* codes, int d, int bits, uint8_t* tile) {
   const int seg = d * bits / 16, M = d / 16;

@@ -338,8 +338,8 @@ def test_vtile_bit_positions():
     at bit (8m + u) * b; check one hand-placed code."""
     d, bits = 128, 2
     c = np.zeros((32, d), np.uint8)
-    # token 21 = 16 + 4*1 + 1 -> q = 1, u = 5; coordinate 3*8 + 2 -> r = 3, m = 2
-    c[21, 26] = 3
+    # token 13 = 8*1 + 5 -> q = 1, u = 5; coordinate 3*8 + 2 -> r = 3, m = 2
+    c[13, 26] = 3
     t = oracle.pack_vtiles(c, bits)[0]
     seg = d * bits // 16
     bit = (8 * 2 + 5) * bits
