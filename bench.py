@@ -97,6 +97,236 @@ def cpu_baseline(seconds_budget=20.0):
     }
 
 
+def _report(workload, metric, value, unit, higher, extra, args, ms_per_step):
+    line = {"metric": metric, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": higher,
+            "scaling": "weak", "vs_baseline": None,
+            "data": "synthetic (seeded fp16 K/V with outlier channels and lognormal token scale)",
+            "config": workload}
+    line.update(extra)
+    print(json.dumps(line), flush=True)
+
+
+def _timed(torch, fn, steps, warmup):
+    """Median over `steps` timed calls of fn (after `warmup` calls), in ms."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    ts.sort()
+    return ts[len(ts) // 2]
+
+
+def _fill_cache(torch, tq, synth, cache, cbk, cbv, sbd, seed, L, B, H, T, d):
+    """Encode the seeded prefill of every layer into `cache`, one layer at a
+    time (bounded device memory)."""
+    zero = torch.zeros(B, dtype=torch.int32, device="cuda")
+    for l in range(L):
+        k = torch.empty((1, B, H, T, d), dtype=torch.int16, device="cuda")
+        v = torch.empty_like(k)
+        synth.kv_dev(seed, 0, l, k[0])
+        synth.kv_dev(seed, 1, l, v[0])
+        tq.append(cache, cbk, cbv, sbd[l:l + 1], k, v, zero, host_max_pos=0, layer0=l, n_layers=1)
+        del k, v
+    torch.cuda.synchronize()
+
+
+def workload_batched_decode(args):
+    """32 layers, 32 query / 8 KV heads, d 128, batch 16, 8192-token context,
+    K3/V2: 64 consecutive steps, each appending one token per sequence to all
+    layers (one tq_append) and attending over all layers (one tq_decode_attn).
+    Reports decode tokens/s (batch x steps / time) and GB/s of packed cache
+    read over the 64 steps."""
+    import numpy as np
+    import torch
+    import kv_cache_quantization_tq_amd as tq
+    import synth
+    seed, L, B, H, HQ, d, T0, steps, bk, bv = 1003, 32, 16, 8, 32, 128, 8192, 64, 3, 2
+    torch.cuda.set_device(0)
+    cap = ((T0 + steps + 31) // 32) * 32
+    cache = tq.KVCache(L, B, H, d, bk, bv, cap)
+    cbk, cbv = tq.Codebook(d, bk), tq.Codebook(d, bv)
+    sbd = torch.from_numpy(np.stack([synth.sign_bits(seed, l, d) for l in range(L)])).cuda()
+    _fill_cache(torch, tq, synth, cache, cbk, cbv, sbd, seed, L, B, H, T0, d)
+    kn = torch.empty((steps, L, B, H, 1, d), dtype=torch.int16, device="cuda")
+    vn = torch.empty_like(kn)
+    q = torch.empty((steps, L, B, HQ, d), dtype=torch.int16, device="cuda")
+    for s in range(steps):
+        for l in range(L):
+            synth.kv_dev(seed, 0, l, kn[s, l], t0=T0 + s)
+            synth.kv_dev(seed, 1, l, vn[s, l], t0=T0 + s)
+            synth.q_dev(seed, s, l, q[s, l])
+    pos = [torch.full((B,), T0 + s, dtype=torch.int32, device="cuda") for s in range(steps)]
+    lens = [torch.full((B,), T0 + s + 1, dtype=torch.int32, device="cuda") for s in range(steps)]
+    out = torch.empty((L, B, HQ, d), dtype=torch.float32, device="cuda")
+    ws = tq.workspace(cache, HQ, cap)
+    torch.cuda.synchronize()
+
+    def run64():
+        for s in range(steps):
+            tq.append(cache, cbk, cbv, sbd, kn[s], vn[s], pos[s], host_max_pos=T0 + s)
+            tq.decode(cache, cbk, cbv, sbd, q[s], lens[s], T0 + s + 1, out, ws)
+
+    ms = _timed(torch, run64, args.steps, args.warmup)
+    nbytes = sum(L * B * H * (T0 + s + 1) * per_token_head_bytes(d, bk, bv) for s in range(steps))
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    _report({"workload": "batched decode, 64 steps with appends", "layers": L, "q_heads": HQ,
+             "kv_heads": H, "head_dim": d, "batch": B, "context": f"{T0 + 1}..{T0 + steps}",
+             "bits_k": bk, "bits_v": bv},
+            "decode tokens/s (batch x 64 steps, append + decode per step)", B * steps / (ms * 1e-3),
+            "tokens/s", True,
+            {"dtype": "f32 (f16 matrix-core operands; packed 3-bit K, 2-bit V)",
+             "ms_per_64_steps": ms, "packed_gbs": gbs, "pct_hbm_peak": 100 * gbs / HBM_PEAK_GBS,
+             "packed_bytes_64_steps": nbytes}, args, ms / steps)
+
+
+def workload_encode_48l(args):
+    """48 layers, 8 KV heads, d 128, 32768 tokens, K4/V3: one tq_append of the
+    whole prefill over all layers (timed), and the same prefill as 16 chunked
+    appends of 2048 tokens (timed separately)."""
+    import numpy as np
+    import torch
+    import kv_cache_quantization_tq_amd as tq
+    import synth
+    seed, L, B, H, d, T, bk, bv, chunk = 1004, 48, 1, 8, 128, 32768, 4, 3, 2048
+    torch.cuda.set_device(0)
+    cache = tq.KVCache(L, B, H, d, bk, bv, T)
+    cbk, cbv = tq.Codebook(d, bk), tq.Codebook(d, bv)
+    sbd = torch.from_numpy(np.stack([synth.sign_bits(seed, l, d) for l in range(L)])).cuda()
+    kp = torch.empty((L, B, H, T, d), dtype=torch.int16, device="cuda")
+    vp = torch.empty_like(kp)
+    for l in range(L):
+        synth.kv_dev(seed, 0, l, kp[l])
+        synth.kv_dev(seed, 1, l, vp[l])
+    kc = [kp[:, :, :, c * chunk:(c + 1) * chunk].contiguous() for c in range(T // chunk)]
+    vc = [vp[:, :, :, c * chunk:(c + 1) * chunk].contiguous() for c in range(T // chunk)]
+    zero = torch.zeros(B, dtype=torch.int32, device="cuda")
+    cpos = [torch.full((B,), c * chunk, dtype=torch.int32, device="cuda") for c in range(T // chunk)]
+    torch.cuda.synchronize()
+    bulk_ms = _timed(torch, lambda: tq.append(cache, cbk, cbv, sbd, kp, vp, zero, host_max_pos=0),
+                     args.steps, args.warmup)
+
+    def chunked():
+        for c in range(T // chunk):
+            tq.append(cache, cbk, cbv, sbd, kc[c], vc[c], cpos[c], host_max_pos=c * chunk)
+
+    chunk_ms = _timed(torch, chunked, args.steps, args.warmup)
+    nbytes = L * B * H * T * encode_bytes_per_token_head(d, bk, bv)
+    gbs = nbytes / (bulk_ms * 1e-3) / 1e9
+    _report({"workload": "48-layer 32K prefill encode", "layers": L, "kv_heads": H,
+             "head_dim": d, "batch": B, "tokens": T, "bits_k": bk, "bits_v": bv},
+            "encode tokens/s (32K prefill, all 48 layers, one tq_append)", T * B / (bulk_ms * 1e-3),
+            "tokens/s", True,
+            {"dtype": "f32 (f16 matrix-core transform; packed 4-bit K, 3-bit V)",
+             "encode_ms": bulk_ms, "encode_gbs": gbs, "pct_hbm_peak": 100 * gbs / HBM_PEAK_GBS,
+             "bytes_per_launch": nbytes, "chunked_16x2048_ms": chunk_ms,
+             "chunked_gbs": nbytes / (chunk_ms * 1e-3) / 1e9}, args, bulk_ms)
+
+
+def workload_70b_128k(args):
+    """80 layers, 64 query / 8 KV heads (group 8), d 128, batch 4, 131072-token
+    context, K4/V2 (33.5 GB packed cache): one decode step over all layers
+    (timed); plus one layer at d 64 and one at d 256 with the same batch,
+    heads and context (timed on their own)."""
+    import numpy as np
+    import torch
+    import kv_cache_quantization_tq_amd as tq
+    import synth
+    seed, L, B, H, HQ, d, T, bk, bv = 1005, 80, 4, 8, 64, 128, 131072, 4, 2
+    torch.cuda.set_device(0)
+    res = {}
+    for dd, layers, first in ((d, L, 0), (64, 1, 80), (256, 1, 81)):
+        cache = tq.KVCache(layers, B, H, dd, bk, bv, T)
+        cbk, cbv = tq.Codebook(dd, bk), tq.Codebook(dd, bv)
+        sbd = torch.from_numpy(np.stack([synth.sign_bits(seed, first + l, dd)
+                                         for l in range(layers)])).cuda()
+        zero = torch.zeros(B, dtype=torch.int32, device="cuda")
+        for l in range(layers):
+            k = torch.empty((1, B, H, T, dd), dtype=torch.int16, device="cuda")
+            v = torch.empty_like(k)
+            synth.kv_dev(seed, 0, first + l, k[0])
+            synth.kv_dev(seed, 1, first + l, v[0])
+            tq.append(cache, cbk, cbv, sbd[l:l + 1], k, v, zero, host_max_pos=0, layer0=l,
+                      n_layers=1)
+            del k, v
+        q = torch.empty((layers, B, HQ, dd), dtype=torch.int16, device="cuda")
+        for l in range(layers):
+            synth.q_dev(seed, 0, first + l, q[l])
+        lens = torch.full((B,), T, dtype=torch.int32, device="cuda")
+        out = torch.empty((layers, B, HQ, dd), dtype=torch.float32, device="cuda")
+        ws = tq.workspace(cache, HQ, T)
+        torch.cuda.synchronize()
+        ms = _timed(torch, lambda: tq.decode(cache, cbk, cbv, sbd, q, lens, T, out, ws),
+                    args.steps, args.warmup)
+        nbytes = layers * B * H * T * per_token_head_bytes(dd, bk, bv)
+        res[dd] = (ms, nbytes)
+        del cache, q, out, ws
+        torch.cuda.synchronize()
+        print(f"70b-128k: d {dd}: {ms * 1e3:.1f} us per step", file=sys.stderr, flush=True)
+    ms, nbytes = res[d]
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    extra = {"dtype": "f32 (f16 matrix-core operands; packed 4-bit K, 2-bit V)",
+             "decode_us": ms * 1e3, "packed_gbs": gbs, "pct_hbm_peak": 100 * gbs / HBM_PEAK_GBS,
+             "bytes_per_step": nbytes}
+    for dd in (64, 256):
+        m2, b2 = res[dd]
+        extra[f"d{dd}_layer_decode_us"] = m2 * 1e3
+        extra[f"d{dd}_layer_pct_hbm_peak"] = 100 * b2 / (m2 * 1e-3) / 1e9 / HBM_PEAK_GBS
+    _report({"workload": "70b-shaped 128K-context decode", "layers": L, "q_heads": HQ,
+             "kv_heads": H, "head_dim": d, "batch": B, "context": T, "bits_k": bk, "bits_v": bv},
+            "decode tokens/s (batch / step time, all 80 layers)", B / (ms * 1e-3), "tokens/s",
+            True, extra, args, ms)
+
+
+def workload_tiny(args):
+    """1 layer, 2 KV and 2 query heads, d 128, 512 tokens, K4/V2: encode of
+    the 512 tokens and one decode step, timed (latency-bound)."""
+    import numpy as np
+    import torch
+    import kv_cache_quantization_tq_amd as tq
+    import synth
+    seed, L, B, H, HQ, d, T, bk, bv = 1001, 1, 1, 2, 2, 128, 512, 4, 2
+    torch.cuda.set_device(0)
+    cache = tq.KVCache(L, B, H, d, bk, bv, T)
+    cbk, cbv = tq.Codebook(d, bk), tq.Codebook(d, bv)
+    sbd = torch.from_numpy(synth.sign_bits(seed, 0, d)[None]).cuda()
+    k = torch.empty((1, B, H, T, d), dtype=torch.int16, device="cuda")
+    v = torch.empty_like(k)
+    synth.kv_dev(seed, 0, 0, k[0])
+    synth.kv_dev(seed, 1, 0, v[0])
+    q = torch.empty((1, B, HQ, d), dtype=torch.int16, device="cuda")
+    synth.q_dev(seed, 0, 0, q[0])
+    zero = torch.zeros(B, dtype=torch.int32, device="cuda")
+    lens = torch.full((B,), T, dtype=torch.int32, device="cuda")
+    out = torch.empty((1, B, HQ, d), dtype=torch.float32, device="cuda")
+    ws = tq.workspace(cache, HQ, T)
+    enc_ms = _timed(torch, lambda: tq.append(cache, cbk, cbv, sbd, k, v, zero, host_max_pos=0),
+                    args.steps, args.warmup)
+    dec_ms = _timed(torch, lambda: tq.decode(cache, cbk, cbv, sbd, q, lens, T, out, ws),
+                    args.steps, args.warmup)
+    _report({"workload": "tiny single layer", "layers": L, "q_heads": HQ, "kv_heads": H,
+             "head_dim": d, "batch": B, "context": T, "bits_k": bk, "bits_v": bv},
+            "decode-step latency (us, latency-bound; no roofline claim)", dec_ms * 1e3, "us", False,
+            {"dtype": "f32 (f16 matrix-core operands; packed 4-bit K, 2-bit V)",
+             "encode_us": enc_ms * 1e3, "decode_us": dec_ms * 1e3}, args, enc_ms + dec_ms)
+
+
+WORKLOADS = {
+    "llama8b-32k": None,
+    "tiny": workload_tiny,
+    "batched-decode-b16-8k": workload_batched_decode,
+    "encode-48l-32k": workload_encode_48l,
+    "70b-128k-b4": workload_70b_128k,
+}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -105,11 +335,18 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run one plain 1 GiB device copy (HBM counter calibration)")
+    ap.add_argument("--workload", default="llama8b-32k", choices=sorted(WORKLOADS),
+                    help="llama8b-32k (the metric's workload, default) or one of the other "
+                         "workload shapes, timed and reported on a line of its own")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
               "(the path shards by KV head with no exchange; see DESIGN.md)", file=sys.stderr)
         sys.exit(2)
+
+    if args.workload != "llama8b-32k":
+        WORKLOADS[args.workload](args)
+        return
 
     import torch
     import kv_cache_quantization_tq_amd as tq

@@ -59,7 +59,9 @@ constexpr int waves_for(int d, int bk, int bv) {
  *   Word tables (4-byte entries): the fp16 levels of two codes, indexed by a
  *     byte (bits 4), 6 bits (bits 3) or a nibble (bits 2).
  *   Split key tables (bits 3 and 4, 8-byte entries): {fp16 pair, fp16 pair
- *     of (level - fp16 level) * 2^11}.  Key scores reach tens of nats at
+ *     of (level - fp16 level) * 2^11}, indexed by a byte: for bits 3 its low
+ *     6 bits (two codes; the rows repeat every 64), so that a pair of codes
+ *     anywhere in the packed row is one funnel shift and one byte permute away.  Key scores reach tens of nats at
  *     long context, where the ~1e-4 relative fp16 rounding of a level would
  *     move the softmax visibly; the remainder, multiplied by q * 2^-11 in the
  *     same matrix product, makes the level exact to ~2^-22.
@@ -68,7 +70,8 @@ constexpr int waves_for(int d, int bk, int bv) {
 template <int B>
 struct KTab {
   static constexpr bool SPLIT = B >= 3;
-  static constexpr int ENTRIES = B == 4 ? 256 : (B == 3 ? 64 : 16);
+  static constexpr int ENTRIES = B >= 3 ? 256 : 16; /* rows */
+  static constexpr int SRC = B == 4 ? 256 : (B == 3 ? 64 : 16); /* distinct entries */
   static constexpr int BYTES = ENTRIES * 256;
 };
 template <int B>
@@ -98,8 +101,8 @@ __device__ inline void fill_words(uint32_t* dst, const uint32_t* src) {
 }
 
 /* Fill an 8-byte-entry table: 32 copies of {a[e * stride], b[e * stride]}
- * per row (loads batched as above). */
-template <int ENTRIES, int WAVES>
+ * per row, e the row index modulo SRC (loads batched as above). */
+template <int ENTRIES, int WAVES, int SRC = ENTRIES>
 __device__ inline void fill_pairs(uint32_t* dst, const uint32_t* a, const uint32_t* b,
                                   int stride) {
   constexpr int N = ENTRIES * 32, T = 64 * WAVES, IT = (N + T - 1) / T;
@@ -107,7 +110,8 @@ __device__ inline void fill_pairs(uint32_t* dst, const uint32_t* a, const uint32
 #pragma unroll
   for (int k = 0; k < IT; ++k) {
     const int i = threadIdx.x + k * T;
-    v[k] = i < N ? make_uint2(a[(i >> 5) * stride], b[(i >> 5) * stride]) : make_uint2(0u, 0u);
+    const int e = (i >> 5) % SRC;
+    v[k] = i < N ? make_uint2(a[e * stride], b[e * stride]) : make_uint2(0u, 0u);
   }
   uint2* d2 = (uint2*)dst;
 #pragma unroll
@@ -167,6 +171,26 @@ __device__ inline void deq8_split(const uint32_t* lut, uint32_t f, uint32_t lo8,
   }
   a0 = u32x4{w[0].x, w[0].y, w[1].x, w[1].y};
   a1 = u32x4{w[2].x, w[2].y, w[3].x, w[3].y};
+}
+
+/* Split key lookups of all pairs of 3-bit codes in a lane's packed row piece
+ * w (F fields of 8 codes): e[s][j] = entry of codes 8 s + 2 j, 8 s + 2 j + 1.
+ * The pair at bit p = 24 s + 6 j is the low 6 bits of byte 0 of the string
+ * shifted right by p, and the pair of field s + 1 is byte 3 of the same shift. */
+template <int NW, int F>
+__device__ inline void deq_split3(const uint32_t* lut, const uint32_t (&w)[NW], uint32_t lo8,
+                                  uint2 (&e)[F][4]) {
+  static_assert(F % 2 == 0, "fields come in pairs");
+#pragma unroll
+  for (int g = 0; g < F / 2; ++g)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int p = 48 * g + 6 * j, i = p / 32, sh = p % 32;
+      const uint32_t hi = i + 1 < NW ? w[i + 1] : 0u;
+      const uint32_t x = sh == 0 ? w[i] : __builtin_amdgcn_alignbit(hi, w[i], sh);
+      e[2 * g][j] = lut_at2(lut, __builtin_amdgcn_perm(x, lo8, sel_byte(0)));
+      e[2 * g + 1][j] = lut_at2(lut, __builtin_amdgcn_perm(x, lo8, sel_byte(3)));
+    }
 }
 
 /* Bits [8*B*s, 8*B*(s+1)) of a little-endian bit string held in words. */
@@ -414,6 +438,22 @@ __device__ inline void tile_step(const TileRegs<DG, CF>& r,
                                  float& m_run, float& l_run, bool& first, int tok0, int len,
                                  int q4, int n) {
   floatx4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (BK == 3) {
+    uint2 e0[DG::KS][4], e1[DG::KS][4];
+    deq_split3<DG::KW, DG::KS>(lk, r.kw0, lok, e0);
+    deq_split3<DG::KW, DG::KS>(lk, r.kw1, lok, e1);
+#pragma unroll
+    for (int s = 0; s < DG::KS; ++s) {
+      const u32x4 a0 = {e0[s][0].x, e0[s][0].y, e0[s][1].x, e0[s][1].y};
+      const u32x4 a1 = {e0[s][2].x, e0[s][2].y, e0[s][3].x, e0[s][3].y};
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, a0), bq[2 * s], s0, 0, 0, 0);
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, a1), bq[2 * s + 1], s0, 0, 0, 0);
+      const u32x4 b0 = {e1[s][0].x, e1[s][0].y, e1[s][1].x, e1[s][1].y};
+      const u32x4 b1 = {e1[s][2].x, e1[s][2].y, e1[s][3].x, e1[s][3].y};
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, b0), bq[2 * s], s1, 0, 0, 0);
+      s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, b1), bq[2 * s + 1], s1, 0, 0, 0);
+    }
+  } else
 #pragma unroll
   for (int s = 0; s < DG::KS; ++s) {
     if constexpr (KTab<BK>::SPLIT) {
@@ -638,7 +678,7 @@ decode_kernel(DecArgs a) {
   if constexpr (DG::DEPTH == 3) pf(rb, tile + W);
 
   if constexpr (KTab<BK>::SPLIT)
-    fill_pairs<KTab<BK>::ENTRIES, kWaves>(lut_k, a.lut_k, a.lut_k_lo, 1);
+    fill_pairs<KTab<BK>::ENTRIES, kWaves, KTab<BK>::SRC>(lut_k, a.lut_k, a.lut_k_lo, 1);
   else
     fill_words<KTab<BK>::ENTRIES, kWaves>(lut_k, a.lut_k);
   if constexpr (VTab<BV>::QUAD)
