@@ -329,26 +329,42 @@ struct DecArgs {
 /* LDS of one decode block. */
 template <int D, int BK, int BV>
 constexpr size_t decode_lds_bytes() {
-  return (size_t)((KTab<BK>::BYTES + VTab<BV>::BYTES) > waves_for(D, BK, BV) * (8 * D + 16) * 4
+  return (size_t)((KTab<BK>::BYTES + VTab<BV>::BYTES) > waves_for(D, BK, BV) * (8 * (D + 4) + 16) * 4
                       ? (KTab<BK>::BYTES + VTab<BV>::BYTES)
-                      : waves_for(D, BK, BV) * (8 * D + 16) * 4) +
+                      : waves_for(D, BK, BV) * (8 * (D + 4) + 16) * 4) +
          8 * D * 4;
 }
 
-/* In-LDS Walsh-Hadamard transform of G rows of D floats (block-wide). */
+/* Walsh-Hadamard transform of one row of D floats by one wave: lane l holds
+ * coordinates l + 64 j; butterflies of stride >= 64 stay in the lane, the
+ * others pair lanes l and l ^ h.  Returns the lane's transformed values. */
 template <int D>
-__device__ inline void lds_fwht(float* buf, int G) {
-  for (int h = 1; h < D; h <<= 1) {
-    for (int t = threadIdx.x; t < G * D / 2; t += blockDim.x) {
-      const int g = t / (D / 2), k = t % (D / 2);
-      const int i = (k / h) * 2 * h + (k % h);
-      float* r = buf + g * D;
-      const float a = r[i], b = r[i + h];
-      r[i] = a + b;
-      r[i + h] = a - b;
+struct RowRegs {
+  float v[D >= 64 ? D / 64 : 1];
+};
+template <int D>
+__device__ inline RowRegs<D> wave_fwht(const float* row, int lane) {
+  constexpr int J = D >= 64 ? D / 64 : 1;
+  RowRegs<D> r;
+#pragma unroll
+  for (int j = 0; j < J; ++j) r.v[j] = row[lane + 64 * j];
+#pragma unroll
+  for (int hj = 1; hj < J; hj <<= 1)
+#pragma unroll
+    for (int j = 0; j < J; ++j)
+      if (!(j & hj)) {
+        const float x = r.v[j], y = r.v[j | hj];
+        r.v[j] = x + y;
+        r.v[j | hj] = x - y;
+      }
+#pragma unroll
+  for (int h = 1; h < 64 && h < D; h <<= 1)
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const float y = __shfl_xor(r.v[j], h);
+      r.v[j] = (lane & h) ? y - r.v[j] : r.v[j] + y;
     }
-    __syncthreads();
-  }
+  return r;
 }
 
 /* One 32-token tile's loads for one lane.  The norms are only those of the
@@ -694,7 +710,13 @@ decode_kernel(DecArgs a) {
     qbuf[t] = ((sb[i >> 3] >> (i & 7)) & 1) ? -v : v;
   }
   __syncthreads();
-  lds_fwht<D>(qbuf, G);
+  /* one wave per head transforms its row in registers */
+  if (wave < G) {
+    const RowRegs<D> t = wave_fwht<D>(qbuf + wave * D, lane);
+#pragma unroll
+    for (int j = 0; j < (D >= 64 ? D / 64 : 1); ++j) qbuf[wave * D + lane + 64 * j] = t.v[j];
+  }
+  __syncthreads();
 
   /* B operands of the score products: fp16(q'') in columns 0..7 (one per
    * head), the fp16 remainder q'' - fp16(q'') in columns 8..15.  With split
@@ -789,9 +811,11 @@ decode_kernel(DecArgs a) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[m][i] = ror8_add(acc[m][i]);
 
-  /* merge the waves: mbuf[w] = {m[8], l[8], acc[8][D]} */
+  /* merge the waves: mbuf[w] = {m[8], l[8], acc[8][D + 4]} (rows padded so
+   * that the lanes' writes spread over the banks) */
+  constexpr int MR = D + 4, MW = 8 * MR + 16;
   __syncthreads(); /* tables are dead from here on */
-  float* mw = mbuf + wave * (8 * D + 16);
+  float* mw = mbuf + wave * MW;
   if (n < 8) {
     if (q4 == 0) {
       mw[n] = m_run;
@@ -800,20 +824,23 @@ decode_kernel(DecArgs a) {
 #pragma unroll
     for (int m = 0; m < DG::VM; ++m)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) mw[16 + n * D + (4 * q4 + i) * DG::VM + m] = acc[m][i];
+      for (int i = 0; i < 4; ++i) mw[16 + n * MR + (4 * q4 + i) * DG::VM + m] = acc[m][i];
   }
   __syncthreads();
-  /* merged record per head in qbuf (reused): qbuf[g][i] */
+  /* merged record per head in qbuf (reused): qbuf[g][i]; wsc[w][g] = the
+   * weight of wave w's sums, exp2(m_w - M) */
   float* res = qbuf;
-  __shared__ float mg[8], lg[8];
+  __shared__ float mg[8], lg[8], wsc[kWaves][8];
   if (threadIdx.x < G) {
     const int g = threadIdx.x;
     float M = -1e30f;
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, mbuf[w * (8 * D + 16) + g]);
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, mbuf[w * MW + g]);
     float L = 0.0f;
     for (int w = 0; w < kWaves; ++w) {
-      const float* r = mbuf + w * (8 * D + 16);
-      L += __builtin_amdgcn_exp2f(r[g] - M) * r[8 + g];
+      const float* r = mbuf + w * MW;
+      const float e = __builtin_amdgcn_exp2f(r[g] - M);
+      wsc[w][g] = e;
+      L += e * r[8 + g];
     }
     mg[g] = M;
     lg[g] = L;
@@ -822,22 +849,26 @@ decode_kernel(DecArgs a) {
   for (int t = threadIdx.x; t < G * D; t += blockDim.x) {
     const int g = t / D, i = t % D;
     float s = 0.0f;
-    for (int w = 0; w < kWaves; ++w) {
-      const float* r = mbuf + w * (8 * D + 16);
-      s += __builtin_amdgcn_exp2f(r[g] - mg[g]) * r[16 + g * D + i];
-    }
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) s += wsc[w][g] * mbuf[w * MW + 16 + g * MR + i];
     res[t] = s;
   }
   __syncthreads();
   const int64_t head0 = ((int64_t)layer * a.batch + b) * a.q_heads + (int64_t)kv * G;
   if (a.splits == 1) {
-    lds_fwht<D>(res, G);
-    for (int t = threadIdx.x; t < G * D; t += blockDim.x) {
-      const int g = t / D, i = t % D;
-      const float L = lg[g];
-      float v = L > 0.0f ? res[t] * a.oscale / L : 0.0f;
-      if ((sb[i >> 3] >> (i & 7)) & 1) v = -v;
-      a.out[head0 * D + t] = v;
+    if (wave < G) {
+      /* head `wave`: inverse rotation, 1/l and the scales, straight out */
+      const RowRegs<D> t = wave_fwht<D>(res + wave * D, lane);
+      const float L = lg[wave];
+      const float f = L > 0.0f ? a.oscale / L : 0.0f;
+#pragma unroll
+      for (int j = 0; j < (D >= 64 ? D / 64 : 1); ++j) {
+        const int i = lane + 64 * j;
+        if (i < D) {
+          const float v = t.v[j] * f;
+          a.out[(head0 + wave) * D + i] = ((sb[i >> 3] >> (i & 7)) & 1) ? -v : v;
+        }
+      }
     }
   } else {
     /* partial record per (head, split): {m, l, acc[D]}, after the counters */
@@ -882,13 +913,19 @@ decode_kernel(DecArgs a) {
       res[t] = s;
     }
     __syncthreads();
-    lds_fwht<D>(res, G);
-    for (int t = threadIdx.x; t < G * D; t += blockDim.x) {
-      const int g = t / D, i = t % D;
-      const float L = lg[g];
-      float v = L > 0.0f ? res[t] * a.oscale / L : 0.0f;
-      if ((sb[i >> 3] >> (i & 7)) & 1) v = -v;
-      a.out[head0 * D + t] = v;
+    if (wave < G) {
+      /* head `wave`: inverse rotation, 1/l and the scales, straight out */
+      const RowRegs<D> t = wave_fwht<D>(res + wave * D, lane);
+      const float L = lg[wave];
+      const float f = L > 0.0f ? a.oscale / L : 0.0f;
+#pragma unroll
+      for (int j = 0; j < (D >= 64 ? D / 64 : 1); ++j) {
+        const int i = lane + 64 * j;
+        if (i < D) {
+          const float v = t.v[j] * f;
+          a.out[(head0 + wave) * D + i] = ((sb[i >> 3] >> (i & 7)) & 1) ? -v : v;
+        }
+      }
     }
   }
 }
