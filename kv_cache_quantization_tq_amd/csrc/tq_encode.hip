@@ -591,15 +591,31 @@ __device__ inline void build_value_half(const uint8_t* vbuf, int lane, int lo, i
         if (4 * w + k < MH) out[4 * w + k] = f[k];
     }
   } else {
-    /* 3 bits: field i = 24 bits, tokens u at 3 u */
+    /* 3 bits: field i = 24 bits, tokens u at 3 u.  Bytes of p_k: tokens 2k,
+     * 2k + 1 (6 bits); the even and odd fields of a word then go to 16-bit
+     * halves, where four tokens fit (12 bits), and two halves make a field. */
 #pragma unroll
-    for (int i = 0; i < MH; ++i) {
-      uint32_t f = 0u;
+    for (int w = 0; w < NW; ++w) {
+      uint32_t p[4];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) f |= __builtin_amdgcn_ubfe(x[u][i / 4], 8 * (i % 4), 3) << (3 * u);
-      const int bit = 24 * i;
-      out[bit / 32] |= f << (bit % 32);
-      if ((bit % 32) + 24 > 32) out[bit / 32 + 1] |= f >> (32 - bit % 32);
+      for (int k = 0; k < 4; ++k) p[k] = x[2 * k][w] | (x[2 * k + 1][w] << 3);
+      const uint32_t e01 = (p[0] & 0x00FF00FFu) | ((p[1] & 0x00FF00FFu) << 6);
+      const uint32_t e23 = (p[2] & 0x00FF00FFu) | ((p[3] & 0x00FF00FFu) << 6);
+      const uint32_t o01 = ((p[0] >> 8) & 0x00FF00FFu) | (((p[1] >> 8) & 0x00FF00FFu) << 6);
+      const uint32_t o23 = ((p[2] >> 8) & 0x00FF00FFu) | (((p[3] >> 8) & 0x00FF00FFu) << 6);
+      const uint32_t f[4] = {(e01 & 0xFFFu) | ((e23 & 0xFFFu) << 12),
+                             (o01 & 0xFFFu) | ((o23 & 0xFFFu) << 12),
+                             (e01 >> 16) | ((e23 >> 16) << 12),
+                             (o01 >> 16) | ((o23 >> 16) << 12)};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int i = 4 * w + k;
+        if (i < MH) {
+          const int bit = 24 * i;
+          out[bit / 32] |= f[k] << (bit % 32);
+          if ((bit % 32) + 24 > 32) out[bit / 32 + 1] |= f[k] >> (32 - bit % 32);
+        }
+      }
     }
   }
   uint8_t* d = dst + lane * OB;
