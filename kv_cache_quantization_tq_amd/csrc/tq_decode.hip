@@ -156,23 +156,6 @@ __device__ inline u32x4 deq8(const uint32_t* lut, uint32_t f, uint32_t lo) {
   return o;
 }
 
-/* The split key lookup of an 8*B-bit field (8 codes): two matrix operands,
- * each {fp16 pair, remainder pair, fp16 pair, remainder pair} of 4 codes.
- * lo8: the lane's copy offset ((lane & 31) * 8). */
-template <int B>
-__device__ inline void deq8_split(const uint32_t* lut, uint32_t f, uint32_t lo8, u32x4& a0,
-                                  u32x4& a1) {
-  uint2 w[4];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const uint32_t a = B == 4 ? __builtin_amdgcn_perm(f, lo8, sel_byte(k))
-                              : ((((f >> (6 * k)) & 0x3Fu) << 8) | lo8);
-    w[k] = lut_at2(lut, a);
-  }
-  a0 = u32x4{w[0].x, w[0].y, w[1].x, w[1].y};
-  a1 = u32x4{w[2].x, w[2].y, w[3].x, w[3].y};
-}
-
 /* Split key lookups of all pairs of 3-bit codes in a lane's packed row piece
  * w (F fields of 8 codes): e[s][j] = entry of codes 8 s + 2 j, 8 s + 2 j + 1.
  * The pair at bit p = 24 s + 6 j is the low 6 bits of byte 0 of the string
@@ -454,10 +437,24 @@ __device__ inline void tile_step(const TileRegs<DG, CF>& r,
                                  float& m_run, float& l_run, bool& first, int tok0, int len,
                                  int q4, int n) {
   floatx4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-  if constexpr (BK == 3) {
+  if constexpr (KTab<BK>::SPLIT) {
+    /* split tables (3 and 4 bits): all lookups of the tile's keys first, so
+     * that many are in flight, then the products; an operand is {fp16 pair,
+     * remainder pair} of two codes twice */
     uint2 e0[DG::KS][4], e1[DG::KS][4];
-    deq_split3<DG::KW, DG::KS>(lk, r.kw0, lok, e0);
-    deq_split3<DG::KW, DG::KS>(lk, r.kw1, lok, e1);
+    if constexpr (BK == 3) {
+      deq_split3<DG::KW, DG::KS>(lk, r.kw0, lok, e0);
+      deq_split3<DG::KW, DG::KS>(lk, r.kw1, lok, e1);
+    } else {
+#pragma unroll
+      for (int s = 0; s < DG::KS; ++s)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) e0[s][k] = lut_at2(lk, __builtin_amdgcn_perm(r.kw0[s], lok, sel_byte(k)));
+#pragma unroll
+      for (int s = 0; s < DG::KS; ++s)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) e1[s][k] = lut_at2(lk, __builtin_amdgcn_perm(r.kw1[s], lok, sel_byte(k)));
+    }
 #pragma unroll
     for (int s = 0; s < DG::KS; ++s) {
       const u32x4 a0 = {e0[s][0].x, e0[s][0].y, e0[s][1].x, e0[s][1].y};
@@ -469,18 +466,10 @@ __device__ inline void tile_step(const TileRegs<DG, CF>& r,
       s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, b0), bq[2 * s], s1, 0, 0, 0);
       s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, b1), bq[2 * s + 1], s1, 0, 0, 0);
     }
-  } else
+  } else {
+    /* 2-bit keys: word tables (fp16 pairs, no remainder) */
 #pragma unroll
-  for (int s = 0; s < DG::KS; ++s) {
-    if constexpr (KTab<BK>::SPLIT) {
-      u32x4 a0, a1;
-      deq8_split<BK>(lk, field<BK>(r.kw0, s), lok, a0, a1);
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, a0), bq[2 * s], s0, 0, 0, 0);
-      s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, a1), bq[2 * s + 1], s0, 0, 0, 0);
-      deq8_split<BK>(lk, field<BK>(r.kw1, s), lok, a0, a1);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, a0), bq[2 * s], s1, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, a1), bq[2 * s + 1], s1, 0, 0, 0);
-    } else {
+    for (int s = 0; s < DG::KS; ++s) {
       const u32x4 a0 = deq8<BK>(lk, field<BK>(r.kw0, s), lok);
       s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, a0), bq[s], s0, 0, 0, 0);
       const u32x4 a1 = deq8<BK>(lk, field<BK>(r.kw1, s), lok);
