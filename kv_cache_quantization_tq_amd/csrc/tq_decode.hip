@@ -860,35 +860,44 @@ decode_kernel(DecArgs a) {
       }
     }
   } else {
-    /* partial record per (head, split): {m, l, acc[D]}, after the counters */
+    /* partial record per (head, split): {m, l, acc[D]}, after the counters.
+     * Records and counters are exchanged between blocks (possibly on other
+     * XCDs) with device-scope relaxed atomic stores and loads, which go to
+     * the coherent level directly; a wait for this block's stores orders them
+     * before its counter increment.  (Device-scope fences would write back
+     * and invalidate the whole L2 instead, stalling every block's streams.) */
     const int64_t uid = blockIdx.x / a.splits;
     float* recs = (float*)((char*)a.ws + a.ctr_bytes);
     for (int t = threadIdx.x; t < G * (D + 2); t += blockDim.x) {
       const int g = t / (D + 2), k = t % (D + 2);
       float* rec = recs + ((head0 + g) * a.splits + split) * (D + 2);
-      rec[k] = k == 0 ? mg[g] : (k == 1 ? lg[g] : res[g * D + (k - 2)]);
+      const float v = k == 0 ? mg[g] : (k == 1 ? lg[g] : res[g * D + (k - 2)]);
+      __hip_atomic_store(rec + k, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    /* the last split of the unit to finish merges all of them */
-    __threadfence();
+    __builtin_amdgcn_s_waitcnt(0); /* this wave's records are written */
     __syncthreads();
+    /* the last split of the unit to finish merges all of them */
     __shared__ int last;
     if (threadIdx.x == 0) {
       int* ctr = (int*)a.ws + uid;
-      const int ticket = atomicAdd(ctr, 1);
+      const int ticket = __hip_atomic_fetch_add(ctr, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       last = ticket == a.splits - 1;
-      if (last) *ctr = 0; /* every split has arrived: ready for the next call */
+      /* every split has arrived: ready for the next call */
+      if (last) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     __syncthreads();
     if (!last) return;
-    __threadfence();
+    auto rd = [](const float* p) {
+      return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
     if (threadIdx.x < G) {
       const int g = threadIdx.x;
       const float* r = recs + (head0 + g) * a.splits * (D + 2);
       float M = -1e30f;
-      for (int sp = 0; sp < a.splits; ++sp) M = fmaxf(M, r[sp * (D + 2)]);
+      for (int sp = 0; sp < a.splits; ++sp) M = fmaxf(M, rd(r + sp * (D + 2)));
       float L = 0.0f;
       for (int sp = 0; sp < a.splits; ++sp)
-        L += __builtin_amdgcn_exp2f(r[sp * (D + 2)] - M) * r[sp * (D + 2) + 1];
+        L += __builtin_amdgcn_exp2f(rd(r + sp * (D + 2)) - M) * rd(r + sp * (D + 2) + 1);
       mg[g] = M;
       lg[g] = L;
     }
@@ -898,7 +907,7 @@ decode_kernel(DecArgs a) {
       const float* r = recs + (head0 + g) * a.splits * (D + 2);
       float s = 0.0f;
       for (int sp = 0; sp < a.splits; ++sp)
-        s += __builtin_amdgcn_exp2f(r[sp * (D + 2)] - mg[g]) * r[sp * (D + 2) + 2 + i];
+        s += __builtin_amdgcn_exp2f(rd(r + sp * (D + 2)) - mg[g]) * rd(r + sp * (D + 2) + 2 + i);
       res[t] = s;
     }
     __syncthreads();
