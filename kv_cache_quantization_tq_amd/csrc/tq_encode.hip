@@ -686,6 +686,10 @@ struct AppendArgs {
 constexpr int kAppendWaves = 4;
 constexpr int kTPB = 2;
 
+/* Whether key and value blocks alternate in one grid dimension. */
+template <int BV>
+constexpr bool kMixKV = BV == 2;
+
 /* Rows of tile `tile` receiving tokens of this append, [jlo, jhi). */
 __device__ inline bool tile_range(const AppendArgs& a, int p0, int tile, int* jlo, int* jhi) {
   int lo = p0 - 32 * tile, hi = p0 + a.t_new - 32 * tile;
@@ -741,7 +745,11 @@ struct TaskGeo {
   const uint16_t* src; /* fp16 input row of tile row j0 (the wave's first row) */
 };
 
-/* blockIdx.y = 0: keys (rows); 1: values (tiles).  Block k takes the tile
+/* Key (row) and value (tile) blocks: with 2-bit values they alternate
+ * (blockIdx.x odd: values), which mixes the two write streams evenly and
+ * measured faster; otherwise blockIdx.y = 1 marks the value blocks, all
+ * dispatched after the key blocks, which measured faster for 3- and 4-bit
+ * values.  Block k of a kind takes the tile
  * pairs [k chunk, (k + 1) chunk) in order (consecutive tiles of a stream, so
  * the layer and its sign flip rarely change), loading the next pair's
  * vectors while encoding the current one. */
@@ -754,7 +762,8 @@ append_kernel(AppendArgs a) {
                                                                        : tq_enc_rows_max(D, BV);
   __shared__ __align__(16) tq_enc_entry tab[kRows * kEncRep];
   __shared__ __align__(16) uint8_t vbuf_all[kAppendWaves * kVec * kVPitch<D>];
-  const bool is_v = blockIdx.y == 1;
+  constexpr bool kMix = kMixKV<BV>;
+  const bool is_v = kMix ? (blockIdx.x & 1) != 0 : blockIdx.y == 1;
   const int ent = is_v ? a.ent_v : a.ent_k; /* <= kRows (checked by the codebook build) */
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64), lane = threadIdx.x % 64;
   const int q4 = lane / 16, nl = lane % 16;
@@ -806,7 +815,7 @@ append_kernel(AppendArgs a) {
   };
 
   const int64_t pairs = (tasks + kTPB - 1) / kTPB;
-  const int64_t first = (int64_t)blockIdx.x * a.chunk;
+  const int64_t first = (int64_t)(kMix ? blockIdx.x >> 1 : blockIdx.x) * a.chunk;
   int64_t last = first + a.chunk;
   if (last > pairs) last = pairs;
   if (first >= last) return;
@@ -907,8 +916,8 @@ tq_status launch_append_t(AppendArgs a, hipStream_t s) {
   int64_t blocks = pairs < 2048 ? pairs : 2048;
   a.chunk = (pairs + blocks - 1) / blocks;
   blocks = (pairs + a.chunk - 1) / a.chunk;
-  hipLaunchKernelGGL((append_kernel<D, BK, BV>), dim3((unsigned)blocks, 2), dim3(64 * kAppendWaves),
-                     0, s, a);
+  const dim3 grid = kMixKV<BV> ? dim3((unsigned)(2 * blocks)) : dim3((unsigned)blocks, 2);
+  hipLaunchKernelGGL((append_kernel<D, BK, BV>), grid, dim3(64 * kAppendWaves), 0, s, a);
   return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_DEVICE;
 }
 
