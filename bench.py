@@ -318,12 +318,63 @@ def workload_tiny(args):
              "encode_us": enc_ms * 1e3, "decode_us": dec_ms * 1e3}, args, enc_ms + dec_ms)
 
 
+def workload_paged_llama8b(args):
+    """The 32K workload (32 layers, 32 query / 8 KV heads, d 128, K4/V2) in
+    paged storage: 256-token pages, the pool's pages assigned to the batch in
+    shuffled order.  Times the 32K prefill append and one decode step, as the
+    default line does, so the two layouts can be compared."""
+    import numpy as np
+    import torch
+    import kv_cache_quantization_tq_amd as tq
+    import synth
+    P = 256
+    torch.cuda.set_device(0)
+    cap = T + 256
+    maxp = cap // P
+    rng = np.random.default_rng(7)
+    num_pages = B * maxp
+    table = rng.permutation(num_pages).reshape(B, maxp).astype(np.int32)
+    cache = tq.PagedKVCache(L, B, HKV, D, BK, BV, P, maxp, num_pages, table)
+    cbk, cbv = tq.Codebook(D, BK), tq.Codebook(D, BV)
+    sbs = torch.from_numpy(np.stack([synth.sign_bits(SEED, l, D) for l in range(L)])).cuda()
+    k = torch.empty((L, B, HKV, T, D), dtype=torch.int16, device="cuda")
+    v = torch.empty_like(k)
+    for l in range(L):
+        synth.kv_dev(SEED, 0, l, k[l])
+        synth.kv_dev(SEED, 1, l, v[l])
+    q = torch.empty((L, B, HQ, D), dtype=torch.int16, device="cuda")
+    for l in range(L):
+        synth.q_dev(SEED, 0, l, q[l])
+    zero = torch.zeros(B, dtype=torch.int32, device="cuda")
+    lens = torch.full((B,), T, dtype=torch.int32, device="cuda")
+    out = torch.empty((L, B, HQ, D), dtype=torch.float32, device="cuda")
+    ws = tq.workspace(cache, HQ, T)
+    torch.cuda.synchronize()
+    enc_ms = _timed(torch, lambda: tq.append(cache, cbk, cbv, sbs, k, v, zero, host_max_pos=0),
+                    args.steps, args.warmup)
+    dec_ms = _timed(torch, lambda: tq.decode(cache, cbk, cbv, sbs, q, lens, T, out, ws),
+                    args.steps, args.warmup)
+    dec_bytes = L * B * HKV * T * per_token_head_bytes()
+    enc_bytes = L * B * HKV * T * encode_bytes_per_token_head()
+    dec_gbs = dec_bytes / (dec_ms * 1e-3) / 1e9
+    _report({"workload": "llama3-8b-shaped 32K decode + prefill, paged (256-token pages, "
+                         "shuffled)", "layers": L, "q_heads": HQ, "kv_heads": HKV, "head_dim": D,
+             "batch": B, "context": T, "bits_k": BK, "bits_v": BV, "page_tokens": P},
+            "decode-attn GB/s over packed KV, paged storage", dec_gbs, "GB/s", True,
+            {"dtype": "f32 (f16 matrix-core operands; packed 4-bit K, 2-bit V)",
+             "decode_us": dec_ms * 1e3, "decode_pct_hbm_peak": 100 * dec_gbs / HBM_PEAK_GBS,
+             "encode_ms": enc_ms,
+             "encode_pct_hbm_peak": 100 * enc_bytes / (enc_ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
+            args, enc_ms + dec_ms)
+
+
 WORKLOADS = {
     "llama8b-32k": None,
     "tiny": workload_tiny,
     "batched-decode-b16-8k": workload_batched_decode,
     "encode-48l-32k": workload_encode_48l,
     "70b-128k-b4": workload_70b_128k,
+    "paged-llama8b-32k": workload_paged_llama8b,
 }
 
 

@@ -117,14 +117,32 @@ tq_status tq_encode(tq_codebook cb, const uint16_t* x, int64_t n, int64_t x_stri
 
 /* One compressed KV cache layer; layer i of a multi-layer call lives at the
  * base pointers plus i * layer_stride (bytes) of each array.
+ *
+ * Contiguous storage (block_table == NULL):
  *   k_codes: [batch][kv_heads][capacity][d*bits_k/8]     row layout
  *   v_codes: [batch][kv_heads][capacity/32][32*d*bits_v/8] value-tile layout
  *   k_norms, v_norms: fp16 [batch][kv_heads][capacity]
  * capacity % 32 == 0, and capacity * d * max(bits_k, bits_v) / 8 < 2^31 (one
  * (sequence, head) stream of codes is addressed with 32-bit offsets; larger
- * caches return TQ_ERR_UNSUPPORTED).  Code arrays 16-byte aligned, norm
- * arrays 8-byte aligned, layer strides multiples of 16.  Rows at or past a
- * sequence's length are never read by decode. */
+ * caches return TQ_ERR_UNSUPPORTED).
+ *
+ * Paged storage (block_table != NULL): each layer's arrays are a pool of
+ * num_pages pages of page_tokens tokens, shared by all sequences:
+ *   k_codes: [num_pages][kv_heads][page_tokens][d*bits_k/8]
+ *   v_codes: [num_pages][kv_heads][page_tokens/32][32*d*bits_v/8]
+ *   k_norms, v_norms: fp16 [num_pages][kv_heads][page_tokens]
+ * block_table (device int32 [batch][max_pages], 4-byte aligned, the same for
+ * every layer) maps page p of sequence b (its tokens p*page_tokens ..
+ * (p+1)*page_tokens - 1) to a pool page.  page_tokens is a power of two
+ * >= 32, capacity == max_pages * page_tokens (tokens per sequence), and each
+ * pool array of a layer is < 2^31 bytes (else TQ_ERR_UNSUPPORTED).  Entries
+ * outside [0, num_pages) make appends skip those rows and decode read page 0
+ * or num_pages - 1 instead (no access outside the pool).
+ *
+ * Both: code arrays 16-byte aligned, norm arrays 8-byte aligned, layer
+ * strides multiples of 16.  Rows at or past a sequence's length are never
+ * read by decode.  Paging fields are ignored (and may be zero) when
+ * block_table is NULL. */
 typedef struct {
   uint8_t* k_codes;
   uint8_t* v_codes;
@@ -133,9 +151,12 @@ typedef struct {
   int batch, kv_heads, head_dim, bits_k, bits_v, capacity;
   int64_t layer_stride_k_codes, layer_stride_v_codes;
   int64_t layer_stride_k_norms, layer_stride_v_norms;
+  const int32_t* block_table; /* NULL: contiguous storage */
+  int page_tokens, max_pages, num_pages;
 } tq_kv_cache;
 
-/* Bytes of each array for one layer (host helper, no device work). */
+/* Bytes of each array for one layer (host helper, no device work): the
+ * contiguous arrays, or the page pools. */
 tq_status tq_cache_layer_bytes(const tq_kv_cache* c, int64_t* k_codes, int64_t* v_codes,
                                int64_t* k_norms, int64_t* v_norms);
 

@@ -37,6 +37,8 @@ class KVCacheStruct(ctypes.Structure):
         ("bits_k", ctypes.c_int), ("bits_v", ctypes.c_int), ("capacity", ctypes.c_int),
         ("layer_stride_k_codes", ctypes.c_int64), ("layer_stride_v_codes", ctypes.c_int64),
         ("layer_stride_k_norms", ctypes.c_int64), ("layer_stride_v_norms", ctypes.c_int64),
+        ("block_table", ctypes.c_void_p),
+        ("page_tokens", ctypes.c_int), ("max_pages", ctypes.c_int), ("num_pages", ctypes.c_int),
     ]
 
 
@@ -180,6 +182,61 @@ class KVCache:
         if lengths is None:
             lengths = [self.capacity] * self.batch
         return self.n_layers * self.kv_heads * per_tok * sum(lengths)
+
+
+class PagedKVCache:
+    """Paged compressed cache of n_layers layers: per layer a pool of
+    num_pages pages of page_tokens tokens, shared by the batch's sequences
+    through block_table (int32 [batch][max_pages], the same for every layer).
+
+    k_codes [L][num_pages][H][P][d*bk/8], v_codes [L][num_pages][H][P/32][32*d*bv/8],
+    k_norms / v_norms [L][num_pages][H][P] (fp16 bits as int16)."""
+
+    def __init__(self, n_layers, batch, kv_heads, head_dim, bits_k, bits_v, page_tokens,
+                 max_pages, num_pages, block_table, device="cuda"):
+        import torch
+        self.n_layers, self.batch, self.kv_heads = n_layers, batch, kv_heads
+        self.head_dim, self.bits_k, self.bits_v = head_dim, bits_k, bits_v
+        self.page_tokens, self.max_pages, self.num_pages = page_tokens, max_pages, num_pages
+        self.capacity = page_tokens * max_pages
+        self.block_table = torch.as_tensor(block_table, dtype=torch.int32, device=device).contiguous()
+        assert tuple(self.block_table.shape) == (batch, max_pages)
+        d, P = head_dim, page_tokens
+        self.k_codes = torch.zeros((n_layers, num_pages, kv_heads, P, d * bits_k // 8),
+                                   dtype=torch.uint8, device=device)
+        self.v_codes = torch.zeros((n_layers, num_pages, kv_heads, P // 32, 32 * d * bits_v // 8),
+                                   dtype=torch.uint8, device=device)
+        self.k_norms = torch.zeros((n_layers, num_pages, kv_heads, P), dtype=torch.int16,
+                                   device=device)
+        self.v_norms = torch.zeros_like(self.k_norms)
+
+    def struct(self, layer=0):
+        s = KVCacheStruct()
+        s.k_codes = self.k_codes[layer].data_ptr()
+        s.v_codes = self.v_codes[layer].data_ptr()
+        s.k_norms = self.k_norms[layer].data_ptr()
+        s.v_norms = self.v_norms[layer].data_ptr()
+        s.batch, s.kv_heads, s.head_dim = self.batch, self.kv_heads, self.head_dim
+        s.bits_k, s.bits_v, s.capacity = self.bits_k, self.bits_v, self.capacity
+        s.layer_stride_k_codes = self.k_codes.stride(0)
+        s.layer_stride_v_codes = self.v_codes.stride(0)
+        s.layer_stride_k_norms = self.k_norms.stride(0) * 2
+        s.layer_stride_v_norms = self.v_norms.stride(0) * 2
+        s.block_table = self.block_table.data_ptr()
+        s.page_tokens, s.max_pages, s.num_pages = self.page_tokens, self.max_pages, self.num_pages
+        return s
+
+    def gather(self, layer, b, h):
+        """The (layer, sequence b, head h) stream in contiguous layout: key rows
+        [capacity][d*bk/8], value tiles [capacity/32][...], norms [capacity]
+        (torch tensors, for comparisons)."""
+        import torch
+        pages = self.block_table[b].long()
+        kc = self.k_codes[layer][pages, h].reshape(self.capacity, -1)
+        vc = self.v_codes[layer][pages, h].reshape(self.capacity // 32, -1)
+        kn = self.k_norms[layer][pages, h].reshape(self.capacity)
+        vn = self.v_norms[layer][pages, h].reshape(self.capacity)
+        return kc, vc, kn, vn
 
 
 def append(cache, cbk, cbv, sign_bits, k_new, v_new, pos, host_max_pos=-1, layer0=0,

@@ -295,6 +295,8 @@ struct DecArgs {
   int64_t ls_kc, ls_vc, ls_kn, ls_vn;
   int batch, kv_heads, capacity, q_heads, group, n_layers;
   int max_len, splits, tiles_per_split;
+  const int32_t* block_table; /* paged storage: [batch][max_pages] */
+  int lg_tpp, max_pages, num_pages; /* log2(tiles per page), table row, pool pages */
   const uint8_t* sign_bits;
   const uint16_t* q;
   const int32_t* seq_lens;
@@ -379,15 +381,27 @@ struct TileAddr {
   uint32_t koff, voff, noff;
 };
 
+/* Byte offsets of one tile in the four streams (first key row, value tile,
+ * first norm). */
+struct TileOff {
+  int32_t k, v, n;
+};
+
 template <class DG, int CF>
-__device__ inline void load_tile(TileRegs<DG, CF>& r, const TileAddr& ad, int tile) {
+__device__ inline void load_tile(TileRegs<DG, CF>& r, const TileAddr& ad, TileOff o) {
   typedef typename NormWords<CF>::T NT;
-  const int32_t kt = tile * (32 * DG::RB);
-  load_words<DG::KB, DG::KA>(ad.k, ad.koff, kt, r.kw0);
-  load_words<DG::KB, DG::KA>(ad.k, ad.koff, kt + 4 * DG::RB, r.kw1);
-  load_words<DG::SEG, DG::VA>(ad.v, ad.voff, tile * DG::TILE, r.vw);
-  r.kn = load_norms<NT>(ad.kn, ad.noff, tile * 64);
-  r.vn = load_norms<NT>(ad.vn, ad.noff, tile * 64);
+  load_words<DG::KB, DG::KA>(ad.k, ad.koff, o.k, r.kw0);
+  load_words<DG::KB, DG::KA>(ad.k, ad.koff, o.k + 4 * DG::RB, r.kw1);
+  load_words<DG::SEG, DG::VA>(ad.v, ad.voff, o.v, r.vw);
+  r.kn = load_norms<NT>(ad.kn, ad.noff, o.n);
+  r.vn = load_norms<NT>(ad.vn, ad.noff, o.n);
+}
+
+/* Read-only kernel inputs read through the constant address space, so that
+ * uniform reads become scalar loads. */
+template <class T>
+__device__ inline T ld_const(const T* p) {
+  return *(const __attribute__((address_space(4))) T*)p;
 }
 
 /* Tile token (0..31) of slot u (0..7) of a lane in row q4 of the products. */
@@ -615,7 +629,7 @@ __device__ inline void tile_step(const TileRegs<DG, CF>& r,
   }
 }
 
-template <int D, int BK, int BV, int CF>
+template <int D, int BK, int BV, int CF, bool PAGED>
 __global__ void __launch_bounds__(64 * waves_for(D, BK, BV))
 decode_kernel(DecArgs a) {
   using DG = DecGeo<D, BK, BV>;
@@ -652,14 +666,17 @@ decode_kernel(DecArgs a) {
   int t_end = t_begin + a.tiles_per_split;
   if (t_end > ntiles) t_end = ntiles;
 
-  const int64_t sh = (int64_t)b * a.kv_heads + kv;
+  /* streams: the (sequence, head) rows of the layer (contiguous), or the
+   * layer's whole page pool (paged, tile offsets then go through the block
+   * table) */
+  const int64_t sh = PAGED ? 0 : (int64_t)b * a.kv_heads + kv;
+  const int64_t srows = PAGED ? (int64_t)a.num_pages * a.kv_heads * (32 << a.lg_tpp) : a.capacity;
   TileAddr ad;
-  ad.k = make_stream(a.k_codes + layer * a.ls_kc + sh * a.capacity * DG::RB,
-                     (int64_t)a.capacity * DG::RB);
+  ad.k = make_stream(a.k_codes + layer * a.ls_kc + sh * a.capacity * DG::RB, srows * DG::RB);
   ad.v = make_stream(a.v_codes + layer * a.ls_vc + sh * (a.capacity / 32) * DG::TILE,
-                     (int64_t)(a.capacity / 32) * DG::TILE);
-  ad.kn = make_stream(a.k_norms + layer * a.ls_kn + sh * a.capacity * 2, (int64_t)a.capacity * 2);
-  ad.vn = make_stream(a.v_norms + layer * a.ls_vn + sh * a.capacity * 2, (int64_t)a.capacity * 2);
+                     srows / 32 * DG::TILE);
+  ad.kn = make_stream(a.k_norms + layer * a.ls_kn + sh * a.capacity * 2, srows * 2);
+  ad.vn = make_stream(a.v_norms + layer * a.ls_vn + sh * a.capacity * 2, srows * 2);
   /* score rows: row 4 i + j of the first product is tile token 8 i + j, of
    * the second 8 i + 4 + j (so that slot u of row group q4 is token 8 q4 + u) */
   ad.koff = (uint32_t)((8 * (n >> 2) + (n & 3)) * DG::RB + q4 * DG::KB);
@@ -677,7 +694,23 @@ decode_kernel(DecArgs a) {
   int tile = t_begin + wave;
   constexpr int W = kWaves;  /* tile stride between a wave's tiles */
   const int last = full_end > 0 ? full_end - 1 : 0;
-  auto pf = [&](TileRegs<DG, CF>& r, int t) { load_tile<DG, CF>(r, ad, t < last ? t : last); };
+  /* tile t's offsets: tile t of the stream, or tile t % tpp of the pool page
+   * the block table gives for page t / tpp (clamped into the pool) */
+  auto toff = [&](int t) -> TileOff {
+    if constexpr (PAGED) {
+      const int tpp = 1 << a.lg_tpp, pg = t >> a.lg_tpp, w = t & (tpp - 1);
+      int phys = ld_const(a.block_table + (int64_t)b * a.max_pages + pg);
+      phys = phys < 0 ? 0 : (phys >= a.num_pages ? a.num_pages - 1 : phys);
+      const int pb = phys * a.kv_heads + kv;
+      return TileOff{pb * (tpp * 32 * DG::RB) + w * (32 * DG::RB), pb * (tpp * DG::TILE) + w * DG::TILE,
+                     pb * (tpp * 64) + w * 64};
+    } else {
+      return TileOff{t * (32 * DG::RB), t * DG::TILE, t * 64};
+    }
+  };
+  auto pf = [&](TileRegs<DG, CF>& r, int t) {
+    load_tile<DG, CF>(r, ad, toff(t < last ? t : last));
+  };
   TileRegs<DG, CF> ra, rb, rc;
   pf(ra, tile);
   if constexpr (DG::DEPTH == 3) pf(rb, tile + W);
@@ -785,7 +818,7 @@ decode_kernel(DecArgs a) {
   /* the ragged last tile, if this wave owns it */
   if (tile < t_end) {
     TileRegs<DG, CF> rp;
-    load_tile<DG, CF>(rp, ad, tile);
+    load_tile<DG, CF>(rp, ad, toff(tile));
     tile_step<DG, BK, BV, true, CF>(rp, bq, lut_k_rd, lut_v, lo, lo8, lok, acc, m_run, l_run,
                                     first, tile * 32, len, q4, n);
   }
@@ -932,12 +965,18 @@ decode_kernel(DecArgs a) {
 template <int D, int BK, int BV>
 tq_status launch_decode_t(const DecArgs& a, hipStream_t s) {
   const int64_t blocks = (int64_t)a.n_layers * a.batch * a.kv_heads * a.splits;
-  if (a.group <= 4)
-    hipLaunchKernelGGL((decode_kernel<D, BK, BV, 4>), dim3((unsigned)blocks),
-                       dim3(64 * waves_for(D, BK, BV)), 0, s, a);
-  else
-    hipLaunchKernelGGL((decode_kernel<D, BK, BV, 2>), dim3((unsigned)blocks),
-                       dim3(64 * waves_for(D, BK, BV)), 0, s, a);
+  const dim3 grid((unsigned)blocks), block(64 * waves_for(D, BK, BV));
+  if (a.block_table) {
+    if (a.group <= 4)
+      hipLaunchKernelGGL((decode_kernel<D, BK, BV, 4, true>), grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL((decode_kernel<D, BK, BV, 2, true>), grid, block, 0, s, a);
+  } else {
+    if (a.group <= 4)
+      hipLaunchKernelGGL((decode_kernel<D, BK, BV, 4, false>), grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL((decode_kernel<D, BK, BV, 2, false>), grid, block, 0, s, a);
+  }
   return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_DEVICE;
 }
 
@@ -952,7 +991,7 @@ int concurrent_blocks_t() {
     int dev = 0, cus = 0, per = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, decode_kernel<D, BK, BV, 2>, 64 * waves_for(D, BK, BV),
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, decode_kernel<D, BK, BV, 2, false>, 64 * waves_for(D, BK, BV),
                                                      0) != hipSuccess ||
         cus <= 0 || per <= 0) {
       (void)hipGetLastError();
@@ -1041,6 +1080,12 @@ tq_status tq_launch_decode(const tq_kv_cache* c, const tq_codebook_s* cbk,
   a.out = out;
   a.ws = ws;
   a.ctr_bytes = (int64_t)plan.ctr_bytes;
+  a.block_table = c->block_table;
+  a.lg_tpp = 0;
+  if (c->block_table)
+    while ((32 << a.lg_tpp) < c->page_tokens) ++a.lg_tpp;
+  a.max_pages = c->block_table ? c->max_pages : 0;
+  a.num_pages = c->block_table ? c->num_pages : 0;
 #define TQ_DEC(DD, KK, VV) \
   if (c->head_dim == DD && c->bits_k == KK && c->bits_v == VV) return launch_decode_t<DD, KK, VV>(a, s);
 #define TQ_DEC_D(DD) \

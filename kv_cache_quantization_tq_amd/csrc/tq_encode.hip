@@ -671,6 +671,8 @@ struct AppendArgs {
   int64_t ls_kc, ls_vc, ls_kn, ls_vn; /* layer strides, bytes */
   int batch, heads, capacity, t_new, n_layers, slots;
   int64_t chunk;                      /* tile pairs per block */
+  const int32_t* block_table;         /* paged storage: [batch][max_pages], else null */
+  int lg_tpp, max_pages, num_pages;   /* log2(tiles per page), table row, pool pages */
   const uint16_t* k_new;
   const uint16_t* v_new;
   const uint8_t* sign_bits;
@@ -742,6 +744,8 @@ __device__ inline TaskIter task_advance(const AppendArgs& a, TaskIter t, int ste
 struct TaskGeo {
   bool live;
   int layer, b, h, tile, jlo, jhi;
+  int64_t rbase;       /* row index (within the layer's rows) of the tile's row 0 */
+  int64_t vt;          /* value-tile index within the layer's tiles */
   const uint16_t* src; /* fp16 input row of tile row j0 (the wave's first row) */
 };
 
@@ -784,6 +788,7 @@ append_kernel(AppendArgs a) {
     g.b = t.b;
     g.h = t.h;
     g.tile = g.jlo = g.jhi = 0;
+    g.rbase = g.vt = 0;
     g.src = src_all;
     if (t.task >= tasks) return g;
     const int slot = t.slot;
@@ -793,6 +798,20 @@ append_kernel(AppendArgs a) {
     if (p0 < 0) return g;
     g.tile = p0 / 32 + slot;
     if (!tile_range(a, p0, g.tile, &g.jlo, &g.jhi)) return g;
+    if (a.block_table) {
+      /* paged: the pool page of this tile's page (rows of pages outside the
+       * pool are skipped) */
+      const int tpp = 1 << a.lg_tpp;
+      const int phys = ld_const(a.block_table + (int64_t)g.b * a.max_pages + (g.tile >> a.lg_tpp));
+      if (phys < 0 || phys >= a.num_pages) return g;
+      const int64_t pb = (int64_t)phys * a.heads + g.h;
+      g.rbase = pb * (32 * tpp) + 32 * (g.tile & (tpp - 1));
+      g.vt = pb * tpp + (g.tile & (tpp - 1));
+    } else {
+      const int64_t sh = (int64_t)g.b * a.heads + g.h;
+      g.rbase = sh * a.capacity + 32 * (int64_t)g.tile;
+      g.vt = sh * (a.capacity / 32) + g.tile;
+    }
     /* this wave's 16 rows must meet the appended ones */
     if (g.jhi <= j0 || g.jlo >= j0 + kVec) {
       g.src = src_all;
@@ -830,7 +849,7 @@ append_kernel(AppendArgs a) {
     }
     const int jrow = j0 + nl;
     const bool mine = g.live && jrow >= g.jlo && jrow < g.jhi;
-    const int64_t row = ((int64_t)g.b * a.heads + g.h) * a.capacity + 32 * (int64_t)g.tile + jrow;
+    const int64_t row = g.rbase + jrow;
     const uint16_t* vec = lane_src(g);
     uint32_t piece[G::OB];
     if (!is_v) {
@@ -859,9 +878,7 @@ append_kernel(AppendArgs a) {
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       if (g.live && g.jhi > j0 && g.jlo < j0 + kVec)
         build_value_half<D, BV>(vbuf, lane, g.jlo - j0, g.jhi - j0,
-                                a.v_codes + g.layer * a.ls_vc +
-                                    (((int64_t)g.b * a.heads + g.h) * (a.capacity / 32) + g.tile) *
-                                        (32 * D * BV / 8) +
+                                a.v_codes + g.layer * a.ls_vc + g.vt * (32 * D * BV / 8) +
                                     sub * (16 * D * BV / 8));
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
@@ -956,6 +973,12 @@ tq_status tq_launch_append(const tq_kv_cache* c, const tq_codebook_s* cbk,
   a.n_layers = n_layers;
   a.slots = (t_new + 31) / 32 + 1;
   a.chunk = 1;
+  a.block_table = c->block_table;
+  a.lg_tpp = 0;
+  if (c->block_table)
+    while ((32 << a.lg_tpp) < c->page_tokens) ++a.lg_tpp;
+  a.max_pages = c->block_table ? c->max_pages : 0;
+  a.num_pages = c->block_table ? c->num_pages : 0;
   a.k_new = k_new;
   a.v_new = v_new;
   a.sign_bits = sign_bits;

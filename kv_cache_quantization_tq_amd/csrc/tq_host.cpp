@@ -283,16 +283,39 @@ extern "C" tq_status tq_encode(tq_codebook cb, const uint16_t* x, int64_t n, int
                                (hipStream_t)stream);
 }
 
-static tq_status check_cache(const tq_kv_cache* c) {
+/* Rows of one layer's storage: batch * heads * capacity (contiguous), or the
+ * pool's num_pages * heads * page_tokens (paged). */
+static int64_t storage_rows(const tq_kv_cache* c) {
+  return c->block_table ? (int64_t)c->num_pages * c->kv_heads * c->page_tokens
+                        : (int64_t)c->batch * c->kv_heads * c->capacity;
+}
+
+/* Shape checks shared by the entry points and tq_cache_layer_bytes. */
+static tq_status check_shape(const tq_kv_cache* c) {
   if (!c) return TQ_ERR_ARG;
   if (!supported_dim(c->head_dim) || !supported_bits(c->bits_k) || !supported_bits(c->bits_v))
     return TQ_ERR_UNSUPPORTED;
   if (c->batch <= 0 || c->kv_heads <= 0 || c->capacity <= 0 || c->capacity % 32 != 0)
     return TQ_ERR_ARG;
-  /* one (sequence, head) stream of codes is addressed with 32-bit offsets */
-  if ((int64_t)c->capacity * c->head_dim * (c->bits_k > c->bits_v ? c->bits_k : c->bits_v) / 8 >=
-      ((int64_t)1 << 31))
-    return TQ_ERR_UNSUPPORTED;
+  const int maxbits = c->bits_k > c->bits_v ? c->bits_k : c->bits_v;
+  if (c->block_table) {
+    const int p = c->page_tokens;
+    if (p < 32 || (p & (p - 1)) != 0 || c->max_pages <= 0 || c->num_pages <= 0 ||
+        (int64_t)c->max_pages * p != c->capacity || !aligned(c->block_table, 4))
+      return TQ_ERR_ARG;
+    /* a layer's pool is addressed with 32-bit offsets */
+    if (storage_rows(c) * c->head_dim * maxbits / 8 >= ((int64_t)1 << 31)) return TQ_ERR_UNSUPPORTED;
+  } else {
+    /* one (sequence, head) stream of codes is addressed with 32-bit offsets */
+    if ((int64_t)c->capacity * c->head_dim * maxbits / 8 >= ((int64_t)1 << 31))
+      return TQ_ERR_UNSUPPORTED;
+  }
+  return TQ_OK;
+}
+
+static tq_status check_cache(const tq_kv_cache* c) {
+  const tq_status st = check_shape(c);
+  if (st != TQ_OK) return st;
   if (!c->k_codes || !c->v_codes || !c->k_norms || !c->v_norms) return TQ_ERR_ARG;
   if (!aligned(c->k_codes, 16) || !aligned(c->v_codes, 16) || !aligned(c->k_norms, 8) ||
       !aligned(c->v_norms, 8))
@@ -306,12 +329,9 @@ static tq_status check_cache(const tq_kv_cache* c) {
 extern "C" tq_status tq_cache_layer_bytes(const tq_kv_cache* c, int64_t* k_codes,
                                           int64_t* v_codes, int64_t* k_norms,
                                           int64_t* v_norms) {
-  if (!c) return TQ_ERR_ARG;
-  if (!supported_dim(c->head_dim) || !supported_bits(c->bits_k) || !supported_bits(c->bits_v))
-    return TQ_ERR_UNSUPPORTED;
-  if (c->batch <= 0 || c->kv_heads <= 0 || c->capacity <= 0 || c->capacity % 32 != 0)
-    return TQ_ERR_ARG;
-  int64_t rows = (int64_t)c->batch * c->kv_heads * c->capacity;
+  const tq_status st = check_shape(c);
+  if (st != TQ_OK) return st;
+  const int64_t rows = storage_rows(c);
   if (k_codes) *k_codes = rows * c->head_dim * c->bits_k / 8;
   if (v_codes) *v_codes = rows * c->head_dim * c->bits_v / 8;
   if (k_norms) *k_norms = rows * 2;

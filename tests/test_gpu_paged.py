@@ -1,0 +1,113 @@
+"""Paged (block-table) storage: appends and decode through a shuffled block
+table agree with the contiguous layout (the same bytes per sequence, the same
+attention), and decode agrees with the oracle."""
+import numpy as np
+import pytest
+
+import kv_cache_quantization_tq_amd as tq
+import synth
+from helpers import attention_errors, check_attention, oracle_attention_with_bound, require_gpu
+
+pytestmark = pytest.mark.gpu
+SEED = 1011
+
+
+def _fill(torch, caches, cbk, cbv, sbd, L, B, H, d, chunks):
+    """The same appends (t_new tokens at per-sequence positions) to every cache."""
+    for pos, t_new in chunks:
+        kh = np.empty((L, B, H, t_new, d), dtype=np.uint16)
+        vh = np.empty_like(kh)
+        for l in range(L):
+            for b in range(B):
+                for h in range(H):
+                    kh[l, b, h] = synth.kv_host(SEED, 0, l, b, h, d, pos[b], t_new)
+                    vh[l, b, h] = synth.kv_host(SEED, 1, l, b, h, d, pos[b], t_new)
+        k = torch.from_numpy(kh.view(np.int16)).cuda()
+        v = torch.from_numpy(vh.view(np.int16)).cuda()
+        p = torch.tensor(pos, dtype=torch.int32, device="cuda")
+        for c in caches:
+            tq.append(c, cbk, cbv, sbd, k, v, p, host_max_pos=max(pos))
+
+
+@pytest.mark.parametrize("d,bk,bv,P", [(128, 4, 2, 32), (128, 4, 2, 256), (64, 3, 3, 64),
+                                       (256, 2, 4, 128)])
+def test_paged_equals_contiguous(d, bk, bv, P):
+    torch = require_gpu()
+    L, B, H, G, cap = 2, 3, 2, 4, 1024
+    maxp = cap // P
+    rng = np.random.default_rng(P + d)
+    num_pages = B * maxp + 5
+    table = rng.permutation(num_pages)[:B * maxp].reshape(B, maxp).astype(np.int32)
+    cont = tq.KVCache(L, B, H, d, bk, bv, cap)
+    paged = tq.PagedKVCache(L, B, H, d, bk, bv, P, maxp, num_pages, table)
+    cbk, cbv = tq.Codebook(d, bk), tq.Codebook(d, bv)
+    sbs = np.stack([synth.sign_bits(SEED, l, d) for l in range(L)])
+    sbd = torch.from_numpy(sbs).cuda()
+    # ragged per-sequence positions; chunks cross page and tile boundaries
+    lens = [700, 37, 1000]
+    chunks = [([0, 0, 0], 37), ([37, 37, 37], 300), ([337, 337, 337], 363)]
+    _fill(torch, (cont, paged), cbk, cbv, sbd, L, B, H, d, chunks)
+    _fill(torch, (cont, paged), cbk, cbv, sbd, L, B, H, d, [([700, 37, 700], 300)])
+    torch.cuda.synchronize()
+    for l in range(L):
+        for b in range(B):
+            for h in range(H):
+                kc, vc, kn, vn = paged.gather(l, b, h)
+                assert torch.equal(kc, cont.k_codes[l, b, h]), (l, b, h)
+                assert torch.equal(vc, cont.v_codes[l, b, h]), (l, b, h)
+                assert torch.equal(kn, cont.k_norms[l, b, h]), (l, b, h)
+                assert torch.equal(vn, cont.v_norms[l, b, h]), (l, b, h)
+    # pool pages no sequence maps stay untouched
+    unused = sorted(set(range(num_pages)) - set(table.ravel().tolist()))
+    assert not paged.k_codes[:, unused].any() and not paged.v_codes[:, unused].any()
+    # decode: the same output as the contiguous cache, and the oracle's
+    lens = [1000, 337, 1000]
+    q = torch.empty((L, B, H * G, d), dtype=torch.int16, device="cuda")
+    for l in range(L):
+        synth.q_dev(SEED, 3, l, q[l])
+    ld = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    outs = []
+    for c in (cont, paged):
+        o = torch.empty((L, B, H * G, d), dtype=torch.float32, device="cuda")
+        tq.decode(c, cbk, cbv, sbd, q, ld, cap, o, tq.workspace(c, H * G, cap))
+        outs.append(o)
+    torch.cuda.synchronize()
+    rel, mx = attention_errors(outs[1].cpu().numpy(), outs[0].cpu().numpy())
+    assert rel <= 1e-6 and mx <= 1e-5, (rel, mx)
+    q16 = q.cpu().numpy().view(np.uint16)
+    got, ref, bnd = [], [], []
+    for (l, b, h) in ((0, 0, 1), (1, 1, 0), (1, 2, 1)):
+        n = lens[b]
+        # the sequence's tokens in order of position (chunks wrote them at their positions)
+        k = synth.kv_host(SEED, 0, l, b, h, d, 0, n)
+        v = synth.kv_host(SEED, 1, l, b, h, d, 0, n)
+        o, bound, _ = oracle_attention_with_bound(k, v, q16[l, b, h * G:(h + 1) * G], bk, bv, sbs[l])
+        got.append(outs[1].cpu().numpy()[l, b, h * G:(h + 1) * G])
+        ref.append(o)
+        bnd.append(bound)
+    check_attention(np.stack(got), np.stack(ref), np.stack(bnd), f"paged d={d} P={P}")
+
+
+def test_paged_invalid_entries_skip_rows():
+    """Rows whose page the table maps outside the pool are not written; the
+    other rows are."""
+    torch = require_gpu()
+    L, B, H, d, bk, bv, P, maxp = 1, 2, 2, 128, 4, 2, 64, 4
+    num_pages = 8
+    table = np.array([[3, -1, 5, 0], [7, 2, 9, 1]], dtype=np.int32)
+    paged = tq.PagedKVCache(L, B, H, d, bk, bv, P, maxp, num_pages, table)
+    cont = tq.KVCache(L, B, H, d, bk, bv, P * maxp)
+    cbk, cbv = tq.Codebook(d, bk), tq.Codebook(d, bv)
+    sbd = torch.from_numpy(synth.sign_bits(SEED, 0, d)[None]).cuda()
+    _fill(torch, (cont, paged), cbk, cbv, sbd, L, B, H, d, [([0, 0], 256)])
+    torch.cuda.synchronize()
+    for h in range(H):
+        # sequence 0: pages 0, 2, 3 written, page 1 (entry -1) skipped
+        for pg, phys in ((0, 3), (2, 5), (3, 0)):
+            assert torch.equal(paged.k_codes[0, phys, h], cont.k_codes[0, 0, h, pg * P:(pg + 1) * P])
+        # sequence 1: page 2 maps to 9 (outside the pool): skipped
+        for pg, phys in ((0, 7), (1, 2), (3, 1)):
+            assert torch.equal(paged.k_codes[0, phys, h], cont.k_codes[0, 1, h, pg * P:(pg + 1) * P])
+    written = {3, 5, 0, 7, 2, 1}
+    for phys in set(range(num_pages)) - written:
+        assert not paged.k_codes[0, phys].any() and not paged.v_codes[0, phys].any()

@@ -107,3 +107,42 @@ def test_workspace_planning():
     assert L.tq_cache_layer_bytes(ctypes.byref(s), ctypes.byref(k), ctypes.byref(v),
                                   ctypes.byref(kn), ctypes.byref(vn)) == 0
     assert (k.value + v.value + kn.value + vn.value) // 32 == 100
+
+
+def _paged(**kw):
+    s = _fake_cache(capacity=1024)
+    s.block_table = 1 << 16
+    s.page_tokens, s.max_pages, s.num_pages = 256, 4, 10
+    for k, v in kw.items():
+        setattr(s, k, v)
+    return s
+
+
+def test_paged_cache_layer_bytes():
+    """Paged storage: the layer arrays are the page pools."""
+    L = tq.lib()
+    s = _paged()
+    kc, vc, kn, vn = (ctypes.c_int64() for _ in range(4))
+    assert L.tq_cache_layer_bytes(ctypes.byref(s), ctypes.byref(kc), ctypes.byref(vc),
+                                  ctypes.byref(kn), ctypes.byref(vn)) == 0
+    rows = 10 * 8 * 256
+    assert (kc.value, vc.value, kn.value, vn.value) == (rows * 64, rows * 32, rows * 2, rows * 2)
+
+
+def test_paged_validation():
+    """Bad paging parameters are rejected on the host."""
+    L = tq.lib()
+    vp = ctypes.c_void_p
+    bad = [dict(page_tokens=96), dict(page_tokens=16, max_pages=64), dict(max_pages=3),
+           dict(num_pages=0), dict(block_table=(1 << 16) + 2)]
+    for kw in bad:
+        s = _paged(**kw)
+        rc = L.tq_append(ctypes.byref(s), None, None, vp(1), vp(16), vp(16), 1, vp(4), 0, 1, None)
+        assert rc == 1, kw
+        rc = L.tq_decode_attn(ctypes.byref(s), None, None, vp(1), vp(16), 8, vp(4), 16, 1, vp(16),
+                              None, 0, None)
+        assert rc == 1, kw
+    # a layer's pool of 2 GiB or more is unsupported
+    s = _paged(num_pages=1 << 17)
+    assert L.tq_decode_attn(ctypes.byref(s), None, None, vp(1), vp(16), 8, vp(4), 16, 1, vp(16),
+                            None, 0, None) == 2
