@@ -44,6 +44,7 @@ def _L():
         lib.orc_unpack_vtile.argtypes = [vp, i32, i32, vp]
         lib.orc_dequant.argtypes = [vp, vp, i64, i32, vp, vp, vp]
         lib.orc_attention.argtypes = [vp, i32, vp, vp, i64, i32, vp]
+        lib.orc_attention_sparse.argtypes = [vp, i32, vp, vp, i64, i32, dbl, vp, vp, vp]
         _lib = lib
     return _lib
 
@@ -183,6 +184,26 @@ def attention(q, K, V):
     out = np.zeros((G, d))
     _L().orc_attention(_p(qb), G, _p(Kb), _p(Vb), T, d, _p(out))
     return out
+
+
+def attention_sparse(q, K, V, eps, want_weights=False):
+    """Attention with the Sparse V gate (tq_oracle.c, orc_attention_sparse):
+    positions whose weight exp(s_j - max s) is below eps are left out of the
+    value sum, the denominator keeps them.  Returns (out[G][d], bound[G][d])
+    and, with want_weights, the relative weights [G][T] as well."""
+    qb = _c(q, np.float64)
+    G, d = qb.shape
+    Kb = _c(K, np.float64)
+    Vb = _c(V, np.float64)
+    T = Kb.shape[0]
+    out = np.zeros((G, d))
+    bound = np.zeros((G, d))
+    w = np.zeros((G, max(T, 1))) if want_weights else None
+    _L().orc_attention_sparse(_p(qb), G, _p(Kb), _p(Vb), T, d, float(eps), _p(out), _p(bound),
+                              _p(w) if want_weights else None)
+    if want_weights:
+        return out, bound, w[:, :T]
+    return out, bound
 
 
 def halves_to_double(x):

@@ -342,3 +342,49 @@ void orc_attention(const double* q, int G, const double* K, const double* V, int
   }
   free(s);
 }
+
+/* Sparse V ("TurboQuant+ ...", section "Sparse V": value positions whose
+ * attention weight is negligible are left out).  The page gives no
+ * threshold; the reading here: position j is left out of the value sum when
+ * its weight relative to the largest one, exp(s_j - max_k s_k), is below eps.
+ * The softmax denominator keeps every position (all scores are computed; only
+ * the value side is skipped).  eps <= 0 keeps everything (plain attention).
+ *   out[g]   = sum_{j kept} p_j V[j] / l,   l = sum_j p_j,  p_j = exp(s_j - max)
+ *   bound[g] = sum_{j left out} p_j |V[j]| / l   (coordinate-wise)
+ * A computation that leaves out any subset of the left-out positions (and
+ * nothing else) differs from out and from plain attention by at most bound,
+ * coordinate by coordinate.  weights (optional, [G][T]) receives
+ * exp(s_j - max). */
+void orc_attention_sparse(const double* q, int G, const double* K, const double* V, int64_t T,
+                          int d, double eps, double* out, double* bound, double* weights) {
+  double* s = (double*)malloc(sizeof(double) * (size_t)(T > 0 ? T : 1));
+  double scale = 1.0 / sqrt((double)d);
+  for (int g = 0; g < G; ++g) {
+    for (int i = 0; i < d; ++i) out[g * d + i] = bound[g * d + i] = 0.0;
+    if (T == 0) continue;
+    double mx = -INFINITY;
+    for (int64_t j = 0; j < T; ++j) {
+      double a = 0.0;
+      for (int i = 0; i < d; ++i) a += q[g * d + i] * K[j * d + i];
+      s[j] = a * scale;
+      if (s[j] > mx) mx = s[j];
+    }
+    double l = 0.0;
+    for (int64_t j = 0; j < T; ++j) {
+      s[j] = exp(s[j] - mx);
+      l += s[j];
+      if (weights) weights[(int64_t)g * T + j] = s[j];
+    }
+    for (int64_t j = 0; j < T; ++j) {
+      if (s[j] >= eps)
+        for (int i = 0; i < d; ++i) out[g * d + i] += s[j] * V[j * d + i];
+      else
+        for (int i = 0; i < d; ++i) bound[g * d + i] += s[j] * fabs(V[j * d + i]);
+    }
+    for (int i = 0; i < d; ++i) {
+      out[g * d + i] /= l;
+      bound[g * d + i] /= l;
+    }
+  }
+  free(s);
+}

@@ -406,6 +406,71 @@ def test_attention_special_cases():
     assert np.array_equal(oracle.attention(q, K[:0], V[:0]), np.zeros((3, d)))
 
 
+def test_sparse_v_hand_example():
+    """Scores 0, -1, -20 (d = 2): with eps = 1e-6 the third position (relative
+    weight e^-20 ~ 2e-9) leaves the value sum but stays in the denominator;
+    the bound is its weighted |V|."""
+    r2 = math.sqrt(2.0)
+    q = np.array([[r2, 0.0]])
+    K = np.array([[0.0, 1.0], [-1.0, 3.0], [-20.0, -2.0]])  # q.k / sqrt 2 = first coordinate
+    V = np.array([[1.0, 0.0], [0.0, 1.0], [5.0, -7.0]])
+    l = 1 + math.exp(-1) + math.exp(-20)
+    out, bound, w = oracle.attention_sparse(q, K, V, 1e-6, want_weights=True)
+    assert np.allclose(w[0], [1.0, math.exp(-1), math.exp(-20)], rtol=1e-14, atol=0)
+    assert np.allclose(out[0], [1 / l, math.exp(-1) / l], rtol=1e-14, atol=0)
+    assert np.allclose(bound[0], [5 * math.exp(-20) / l, 7 * math.exp(-20) / l], rtol=1e-14, atol=0)
+    # a threshold between e^-20 and e^-1 gives the same; above e^-1 the
+    # second position leaves too
+    out2, _ = oracle.attention_sparse(q, K, V, 0.3)
+    assert np.allclose(out2[0], out[0], rtol=1e-14, atol=0)
+    out3, b3 = oracle.attention_sparse(q, K, V, 0.5)
+    assert np.allclose(out3[0], [1 / l, 0.0], rtol=1e-14, atol=1e-300)
+    assert np.allclose(b3[0], [5 * math.exp(-20) / l, (math.exp(-1) + 7 * math.exp(-20)) / l],
+                       rtol=1e-14, atol=0)
+
+
+def test_sparse_v_special_cases():
+    rng = np.random.default_rng(15)
+    d, T = 64, 53
+    K = rng.standard_normal((T, d))
+    V = rng.standard_normal((T, d))
+    q = rng.standard_normal((3, d)) * 4
+    dense = oracle.attention(q, K, V)
+    # eps <= 0 keeps every position: plain attention, zero bound
+    for eps in (0.0, -1.0):
+        o, b = oracle.attention_sparse(q, K, V, eps)
+        assert np.allclose(o, dense, rtol=0, atol=1e-15) and not b.any()
+    # eps = 1 keeps only the maximum (both of a tie): output = V_max / l
+    s = q @ K.T / math.sqrt(d)
+    o, b = oracle.attention_sparse(q, K, V, 1.0)
+    for g in range(3):
+        j = int(np.argmax(s[g]))
+        l = np.exp(s[g] - s[g, j]).sum()
+        assert np.allclose(o[g], V[j] / l, rtol=1e-12, atol=0)
+    K2 = np.vstack([K, K[:1]])
+    V2 = np.vstack([V, V[5:6]])
+    qt = K[:1] * 3  # position 0 and its copy hold the maximum
+    o, _ = oracle.attention_sparse(qt, K2, V2, 1.0)
+    st = qt @ K2.T / math.sqrt(d)
+    l = np.exp(st[0] - st[0].max()).sum()
+    assert np.allclose(o[0], (V[0] + V[5]) / l, rtol=1e-12, atol=0)
+    # eps above 1 leaves everything out
+    o, b = oracle.attention_sparse(q, K, V, 1.5)
+    assert not o.any()
+    # the bound holds for the dense result, and dense - sparse is exactly the
+    # left-out part: |dense - sparse| <= bound, with equality where the
+    # left-out values share a sign
+    for eps in (1e-3, 1e-2, 0.1):
+        o, b = oracle.attention_sparse(q, K, V, eps)
+        assert (np.abs(dense - o) <= b + 1e-15).all()
+    Vp = np.abs(V)
+    o, b = oracle.attention_sparse(q, K, Vp, 1e-2)
+    assert np.allclose(oracle.attention(q, K, Vp) - o, b, rtol=1e-12, atol=1e-16)
+    # no positions: zeros
+    o, b = oracle.attention_sparse(q, K[:0], V[:0], 1e-6)
+    assert not o.any() and not b.any()
+
+
 def test_rotated_domain_evaluation_matches_plain():
     """Attention evaluated in the rotated domain (scores (Rq).c, values summed
     as levels, one R^T at the end) equals the oracle's plain evaluation over
