@@ -368,6 +368,55 @@ def workload_paged_llama8b(args):
             args, enc_ms + dec_ms)
 
 
+def workload_sparse_v(args):
+    """The 32K decode (32 layers, 32 query / 8 KV heads, d 128, K4/V2) with the
+    Sparse V gate at thresholds 1e-6, 1e-4 and 1e-3 against the dense decode
+    on the same cache; reports the tiles skipped and the time of each."""
+    import numpy as np
+    import torch
+    import kv_cache_quantization_tq_amd as tq
+    import synth
+    torch.cuda.set_device(0)
+    cache = tq.KVCache(L, B, HKV, D, BK, BV, T + 32)
+    cbk, cbv = tq.Codebook(D, BK), tq.Codebook(D, BV)
+    sbs = torch.from_numpy(np.stack([synth.sign_bits(SEED, l, D) for l in range(L)])).cuda()
+    _fill_cache(torch, tq, synth, cache, cbk, cbv, sbs, SEED, L, B, HKV, T, D)
+    q = torch.empty((L, B, HQ, D), dtype=torch.int16, device="cuda")
+    for l in range(L):
+        synth.q_dev(SEED, 0, l, q[l])
+    lens = torch.full((B,), T, dtype=torch.int32, device="cuda")
+    out = torch.empty((L, B, HQ, D), dtype=torch.float32, device="cuda")
+    ws = tq.workspace(cache, HQ, T)
+    torch.cuda.synchronize()
+    dense_ms = _timed(torch, lambda: tq.decode(cache, cbk, cbv, sbs, q, lens, T, out, ws),
+                      args.steps, args.warmup)
+    dec_bytes = L * B * HKV * T * per_token_head_bytes()
+    tiles = L * B * HKV * (T // 32)
+    v_tile_bytes = 32 * (D * BV // 8 + 2)
+    res = {"dense_us": dense_ms * 1e3}
+    best = None
+    for eps in (1e-6, 1e-4, 1e-3):
+        cnt = torch.zeros((L, B, HKV), dtype=torch.int32, device="cuda")
+        tq.decode_sparse(cache, cbk, cbv, sbs, q, lens, T, out, eps, ws, skip_counts=cnt)
+        torch.cuda.synchronize()
+        skipped = int(cnt.sum().item())
+        ms = _timed(torch, lambda e=eps: tq.decode_sparse(cache, cbk, cbv, sbs, q, lens, T, out,
+                                                           e, ws), args.steps, args.warmup)
+        key = f"eps_{eps:g}"
+        res[key + "_us"] = ms * 1e3
+        res[key + "_skipped_tile_frac"] = skipped / tiles
+        res[key + "_bytes_read_gbs"] = (dec_bytes - skipped * v_tile_bytes) / (ms * 1e-3) / 1e9
+        if eps == 1e-3:
+            best = ms
+    _report({"workload": "llama3-8b-shaped 32K decode with the Sparse V gate", "layers": L,
+             "q_heads": HQ, "kv_heads": HKV, "head_dim": D, "batch": B, "context": T,
+             "bits_k": BK, "bits_v": BV, "eps": 1e-3},
+            "decode-attn dense-equivalent GB/s (packed KV bytes a dense decode reads / time), "
+            "Sparse V at eps 1e-3", dec_bytes / (best * 1e-3) / 1e9, "GB/s", True,
+            dict(dtype="f32 (f16 matrix-core operands; packed 4-bit K, 2-bit V)", **res),
+            args, best)
+
+
 WORKLOADS = {
     "llama8b-32k": None,
     "tiny": workload_tiny,
@@ -375,6 +424,7 @@ WORKLOADS = {
     "encode-48l-32k": workload_encode_48l,
     "70b-128k-b4": workload_70b_128k,
     "paged-llama8b-32k": workload_paged_llama8b,
+    "sparse-v-llama8b-32k": workload_sparse_v,
 }
 
 

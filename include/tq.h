@@ -205,6 +205,31 @@ tq_status tq_decode_attn(const tq_kv_cache* c, tq_codebook cbk, tq_codebook cbv,
                          const int32_t* seq_lens, int max_len, int n_layers, float* out,
                          void* ws, size_t ws_bytes, void* stream);
 
+/* tq_decode_attn with the Sparse V gate ("TurboQuant+: Compresion de Cache KV
+ * 6.4x para LLMs", section "Sparse V": the value work of positions with
+ * negligible attention weight is skipped; the page gives no threshold).
+ * Per 32-token tile of a (layer, sequence, KV head): the tile's value codes
+ * are neither read nor accumulated when, for every query head of the group
+ * and every token of the tile, the weight exp(s - m) is below eps, where m
+ * is a running maximum of that head's scores (never above the final one).
+ * So every skipped token has final weight exp(s - max s) < eps, and every
+ * token at or above eps is accumulated; which tokens below eps are skipped
+ * depends on the order tiles are visited in.  The softmax denominator keeps
+ * every token.  The output therefore differs from tq_decode_attn's by at most
+ * sum over tokens with weight < eps of p |v| / l per coordinate.  A
+ * sequence's ragged last tile is never skipped.
+ * eps:         0 gives tq_decode_attn exactly; > 0 and finite (above 1 every
+ *              full tile is skipped); NaN, negative or infinite: TQ_ERR_ARG.
+ * skip_counts: device uint32 [n_layers][batch][kv_heads], 4-byte aligned, or
+ *              NULL; the number of tiles skipped for each (layer, sequence,
+ *              KV head) is ADDED to it (the caller zeroes it).
+ * Other arguments as tq_decode_attn (same workspace). */
+tq_status tq_decode_attn_sparse(const tq_kv_cache* c, tq_codebook cbk, tq_codebook cbv,
+                                const uint8_t* sign_bits, const uint16_t* q, int q_heads,
+                                const int32_t* seq_lens, int max_len, int n_layers, float eps,
+                                uint32_t* skip_counts, float* out, void* ws, size_t ws_bytes,
+                                void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -19,6 +19,7 @@ EXPORTS = (
     "tq_status_str", "tq_codebook_compute", "tq_codebook_init", "tq_codebook_read",
     "tq_codebook_head_dim", "tq_codebook_bits", "tq_codebook_free", "tq_encode",
     "tq_cache_layer_bytes", "tq_append", "tq_decode_workspace_bytes", "tq_decode_attn",
+    "tq_decode_attn_sparse",
 )
 
 
@@ -71,8 +72,10 @@ def lib():
         L.tq_decode_workspace_bytes.restype = sz
         L.tq_decode_attn.argtypes = [P(KVCacheStruct), vp, vp, vp, vp, i32, vp, i32, i32, vp,
                                      vp, sz, vp]
+        L.tq_decode_attn_sparse.argtypes = [P(KVCacheStruct), vp, vp, vp, vp, i32, vp, i32, i32,
+                                            ctypes.c_float, vp, vp, vp, sz, vp]
         for f in ("tq_codebook_compute", "tq_codebook_init", "tq_codebook_read", "tq_encode",
-                  "tq_cache_layer_bytes", "tq_append", "tq_decode_attn"):
+                  "tq_cache_layer_bytes", "tq_append", "tq_decode_attn", "tq_decode_attn_sparse"):
             getattr(L, f).restype = i32
         _lib = L
     return _lib
@@ -269,6 +272,21 @@ def decode(cache, cbk, cbv, sign_bits, q, seq_lens, max_len, out, ws=None, layer
     _check("tq_decode_attn", lib().tq_decode_attn(
         ctypes.byref(s), cbk.handle, cbv.handle, _ptr(sign_bits), _ptr(q), q_heads,
         _ptr(seq_lens), max_len, n_layers, _ptr(out), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def decode_sparse(cache, cbk, cbv, sign_bits, q, seq_lens, max_len, out, eps, ws=None,
+                  skip_counts=None, layer0=0, n_layers=None, stream=None):
+    """tq_decode_attn_sparse: decode with the Sparse V gate at threshold eps;
+    skip_counts (optional) uint32/int32 [n_layers][B][Hkv] receives added
+    per-unit counts of skipped tiles.  Other arguments as decode()."""
+    n_layers = n_layers if n_layers is not None else q.shape[0]
+    q_heads = q.shape[2]
+    s = cache.struct(layer0)
+    ws_bytes = ws.numel() if ws is not None else 0
+    _check("tq_decode_attn_sparse", lib().tq_decode_attn_sparse(
+        ctypes.byref(s), cbk.handle, cbv.handle, _ptr(sign_bits), _ptr(q), q_heads,
+        _ptr(seq_lens), max_len, n_layers, float(eps), _ptr(skip_counts), _ptr(out), _ptr(ws),
+        ws_bytes, _stream(stream)))
 
 
 def workspace(cache, q_heads, max_len, n_layers=None, layer0=0, device="cuda"):

@@ -273,6 +273,7 @@ __device__ inline float h2f(uint32_t h) { return (float)__builtin_bit_cast(_Floa
 
 template <int D, int BK, int BV>
 struct DecGeo {
+  static constexpr int DIM = D, BITS_K = BK, BITS_V = BV;
   static constexpr int KQ = D / 4;              /* coordinates per lane quarter */
   static constexpr int KS = D / 32;             /* score MFMAs per block */
   static constexpr int VM = D / 16;             /* value MFMAs per tile */
@@ -297,6 +298,9 @@ struct DecArgs {
   int max_len, splits, tiles_per_split;
   const int32_t* block_table; /* paged storage: [batch][max_pages] */
   int lg_tpp, max_pages, num_pages; /* log2(tiles per page), table row, pool pages */
+  float sparse_eps;      /* Sparse V threshold (sparse kernels only) */
+  float sparse_lg_eps;   /* log2 of it */
+  uint32_t* skip_counts; /* optional [n_layers][batch][kv_heads] skipped-tile counts */
   const uint8_t* sign_bits;
   const uint16_t* q;
   const int32_t* seq_lens;
@@ -370,6 +374,7 @@ template <class DG, int CF>
 struct TileRegs {
   uint32_t kw0[DG::KW], kw1[DG::KW], vw[DG::VW];
   typename NormWords<CF>::T kn, vn;
+  int32_t vt, nt; /* the tile's value-tile and norm offsets, when its values load later */
 };
 
 /* The four streams of one (layer, sequence, KV head) and a lane's offsets. */
@@ -387,15 +392,21 @@ struct TileOff {
   int32_t k, v, n;
 };
 
-template <class DG, int CF>
+template <class DG, int CF, bool WITH_V = true>
 __device__ inline void load_tile(TileRegs<DG, CF>& r, const TileAddr& ad, TileOff o) {
   typedef typename NormWords<CF>::T NT;
   load_words<DG::KB, DG::KA>(ad.k, ad.koff, o.k, r.kw0);
   load_words<DG::KB, DG::KA>(ad.k, ad.koff, o.k + 4 * DG::RB, r.kw1);
-  load_words<DG::SEG, DG::VA>(ad.v, ad.voff, o.v, r.vw);
+  if constexpr (WITH_V) load_words<DG::SEG, DG::VA>(ad.v, ad.voff, o.v, r.vw);
+  r.vt = o.v;
+  r.nt = o.n;
   r.kn = load_norms<NT>(ad.kn, ad.noff, o.n);
-  r.vn = load_norms<NT>(ad.vn, ad.noff, o.n);
+  if constexpr (WITH_V) r.vn = load_norms<NT>(ad.vn, ad.noff, o.n);
 }
+
+/* A lane offset past every stream's end: buffer loads from it return zeros
+ * without touching memory. */
+constexpr uint32_t kNoLoad = 0x80000000u;
 
 /* Read-only kernel inputs read through the constant address space, so that
  * uniform reads become scalar loads. */
@@ -441,15 +452,20 @@ __device__ inline float mul_h(float x, uint32_t h) {
   return __builtin_fmaf(x, (float)__builtin_bit_cast(_Float16, (uint16_t)h), 0.0f);
 }
 
-/* Score, softmax-update and accumulate one tile.  PARTIAL: some of its tokens
- * lie at or past len and are masked out. */
-template <class DG, int BK, int BV, bool PARTIAL, int CF>
-__device__ inline void tile_step(const TileRegs<DG, CF>& r,
-                                 const half8 (&bq)[KTab<BK>::SPLIT ? 2 * DG::KS : DG::KS],
-                                 const uint32_t* lk, const uint32_t* lv, uint32_t lo,
-                                 uint32_t lo8, uint32_t lok, floatx4 (&acc)[DG::VM],
-                                 float& m_run, float& l_run, bool& first, int tok0, int len,
-                                 int q4, int n) {
+/* Score one tile and update the online softmax: p[v] receives the weights
+ * (relative to the updated running max) of the lane's 8 / CF (token, head)
+ * slots, l_run their sum.  PARTIAL: some of its tokens lie at or past len
+ * and are masked out.  When the max moves, the running sums are rescaled by
+ * alpha: acc here (DEFER false), or by the caller (DEFER true: alpha is
+ * returned and the result says whether it moved), for a caller that still
+ * has an earlier tile's values to add at the old reference. */
+template <class DG, int BK, bool PARTIAL, int CF, bool DEFER>
+__device__ inline bool score_part(const TileRegs<DG, CF>& r,
+                                  const half8 (&bq)[KTab<BK>::SPLIT ? 2 * DG::KS : DG::KS],
+                                  const uint32_t* lk, uint32_t lok, floatx4 (&acc)[DG::VM],
+                                  float& m_run, float& l_run, bool& first, int tok0, int len,
+                                  int q4, int n, float (&p)[8 / CF], float& alpha,
+                                  float* smax = nullptr) {
   floatx4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
   if constexpr (KTab<BK>::SPLIT) {
     /* split tables (3 and 4 bits): all lookups of the tile's keys first, so
@@ -531,14 +547,13 @@ __device__ inline void tile_step(const TileRegs<DG, CF>& r,
     }
   }
   /* scores relative to the running max: w = s - m_run in one fma */
-  uint32_t knh[V], vnh[V];
+  uint32_t knh[V];
   if constexpr (CF == 2) {
     knh[0] = r.kn.x & 0xFFFFu; knh[1] = r.kn.x >> 16; knh[2] = r.kn.y & 0xFFFFu; knh[3] = r.kn.y >> 16;
-    vnh[0] = r.vn.x & 0xFFFFu; vnh[1] = r.vn.x >> 16; vnh[2] = r.vn.y & 0xFFFFu; vnh[3] = r.vn.y >> 16;
   } else {
     knh[0] = r.kn & 0xFFFFu; knh[1] = r.kn >> 16;
-    vnh[0] = r.vn & 0xFFFFu; vnh[1] = r.vn >> 16;
   }
+  bool moved = false;
   float mt = -INFINITY;
 #pragma unroll
   for (int v = 0; v < V; ++v) {
@@ -559,22 +574,56 @@ __device__ inline void tile_step(const TileRegs<DG, CF>& r,
     if constexpr (CF == 4) mt = max_ror4(mt);
     mt = rows_max(max_ror8(mt));
     const float dm = first ? mt : fmaxf(mt, 0.0f);
-    const float alpha = first ? 0.0f : __builtin_amdgcn_exp2f(-dm);
-    l_run *= alpha;
+    const float al = first ? 0.0f : __builtin_amdgcn_exp2f(-dm);
+    l_run *= al;
+    if constexpr (DEFER) {
+      alpha = al;
+      moved = true;
+    } else {
 #pragma unroll
-    for (int m = 0; m < DG::VM; ++m) acc[m] *= alpha;
+      for (int m = 0; m < DG::VM; ++m) acc[m] *= al;
+    }
     m_run += dm;
 #pragma unroll
     for (int v = 0; v < V; ++v) sc[v] -= dm;
     first = false;
   }
-  /* p, then P' = p m split into fp16(p m) (columns 0..7) and the fp16
-   * remainder (columns 8..15), as fp16 pairs of consecutive slots */
+#pragma unroll
+  for (int v = 0; v < V; v += 2) {
+    p[v] = __builtin_amdgcn_exp2f(sc[v]);
+    p[v + 1] = __builtin_amdgcn_exp2f(sc[v + 1]);
+    l_run += p[v] + p[v + 1];
+  }
+  if constexpr (DEFER) {
+    /* the largest of the lane's scores relative to the running max */
+    float m = sc[0];
+#pragma unroll
+    for (int v = 1; v < V; ++v) m = fmaxf(m, sc[v]);
+    *smax = m;
+  }
+  return moved;
+}
+
+/* Accumulate one tile's values with its weights p (from score_part), the
+ * value norms vn and the value words vw of the tile. */
+template <class DG, int BV, int CF>
+__device__ inline void value_part(const float (&p)[8 / CF], typename NormWords<CF>::T vn,
+                                  const uint32_t (&vw)[DG::VW], const uint32_t* lv, uint32_t lo,
+                                  uint32_t lo8, floatx4 (&acc)[DG::VM], int n) {
+  constexpr int V = 8 / CF;
+  const bool upper = n >= 8; /* lane-constant selectors */
+  uint32_t vnh[V];
+  if constexpr (CF == 2) {
+    vnh[0] = vn.x & 0xFFFFu; vnh[1] = vn.x >> 16; vnh[2] = vn.y & 0xFFFFu; vnh[3] = vn.y >> 16;
+  } else {
+    vnh[0] = vn & 0xFFFFu; vnh[1] = vn >> 16;
+  }
+  /* P' = p m split into fp16(p m) (columns 0..7) and the fp16 remainder
+   * (columns 8..15), as fp16 pairs of consecutive slots */
   uint32_t hp[V / 2], lp[V / 2];
 #pragma unroll
   for (int v = 0; v < V; v += 2) {
-    const float p0 = __builtin_amdgcn_exp2f(sc[v]), p1 = __builtin_amdgcn_exp2f(sc[v + 1]);
-    l_run += p0 + p1;
+    const float p0 = p[v], p1 = p[v + 1];
     /* fp16(p m) and the fp16 of the exact remainder p m - fp16(p m), each
      * one mixed-precision FMA */
     const float vn0 = (float)__builtin_bit_cast(_Float16, (uint16_t)vnh[v]);
@@ -615,21 +664,168 @@ __device__ inline void tile_step(const TileRegs<DG, CF>& r,
      * codes, looked up as four fp16 levels at once */
 #pragma unroll
     for (int m = 0; m < DG::VM; ++m) {
-      const uint2 w0 = lut_at2(lv, __builtin_amdgcn_perm(r.vw[m / 2], lo8, sel_byte(2 * (m & 1))));
-      const uint2 w1 = lut_at2(lv, __builtin_amdgcn_perm(r.vw[m / 2], lo8, sel_byte(2 * (m & 1) + 1)));
+      const uint2 w0 = lut_at2(lv, __builtin_amdgcn_perm(vw[m / 2], lo8, sel_byte(2 * (m & 1))));
+      const uint2 w1 = lut_at2(lv, __builtin_amdgcn_perm(vw[m / 2], lo8, sel_byte(2 * (m & 1) + 1)));
       const u32x4 av = {w0.x, w0.y, w1.x, w1.y};
       acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, av), pb, acc[m], 0, 0, 0);
     }
   } else {
 #pragma unroll
     for (int m = 0; m < DG::VM; ++m) {
-      const u32x4 av = deq8<BV>(lv, field<BV>(r.vw, m), lo);
+      const u32x4 av = deq8<BV>(lv, field<BV>(vw, m), lo);
       acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, av), pb, acc[m], 0, 0, 0);
     }
   }
 }
 
-template <int D, int BK, int BV, int CF, bool PAGED>
+/* Score, softmax-update and accumulate one tile whose values came with it. */
+template <class DG, int BK, int BV, bool PARTIAL, int CF>
+__device__ inline void tile_step(const TileRegs<DG, CF>& r,
+                                 const half8 (&bq)[KTab<BK>::SPLIT ? 2 * DG::KS : DG::KS],
+                                 const uint32_t* lk, const uint32_t* lv, uint32_t lo,
+                                 uint32_t lo8, uint32_t lok, floatx4 (&acc)[DG::VM],
+                                 float& m_run, float& l_run, bool& first, int tok0, int len,
+                                 int q4, int n) {
+  float p[8 / CF], alpha;
+  score_part<DG, BK, PARTIAL, CF, false>(r, bq, lk, lok, acc, m_run, l_run, first, tok0, len, q4,
+                                         n, p, alpha);
+  value_part<DG, BV, CF>(p, r.vn, r.vw, lv, lo, lo8, acc, n);
+}
+
+/* The full tiles of a wave with the Sparse V gate ("TurboQuant+ ...",
+ * "Sparse V": value work of positions with negligible attention weight is
+ * skipped).  A tile's values are loaded and accumulated unless, for every
+ * query head of the group and every token of the tile, the weight relative
+ * to the block's largest running max of that head is below eps.  That
+ * reference never exceeds the final max, so a skipped token's final weight
+ * is below eps too; the softmax denominator keeps every token.
+ *
+ * To skip the value bytes, a tile's values are requested only after its
+ * scores: the wave scores one tile ahead.  Per step, with tile t scored and
+ * its value load in flight: score tile t + W (its keys and norms came
+ * through the ring), request its values (or a no-memory load past the
+ * stream's end when skipped, so that the wait counts stay static), refill
+ * the freed ring slot, then accumulate tile t's values, and only then apply
+ * the rescale that the scoring of t + W may have asked for (t's weights are
+ * still at the old reference).  On entry ra holds tile (and rb tile + W
+ * with a depth-3 ring); the rest of the ring is loaded here. */
+template <class DG, int BK, int BV, int CF, class PF>
+__device__ inline void sparse_tiles(const DecArgs& a, const TileAddr& ad, TileRegs<DG, CF>& ra,
+                                    TileRegs<DG, CF>& rb, TileRegs<DG, CF>& rc, PF& pf,
+                                    const half8 (&bq)[KTab<BK>::SPLIT ? 2 * DG::KS : DG::KS],
+                                    const uint32_t* lk, const uint32_t* lv, uint32_t lo,
+                                    uint32_t lo8, uint32_t lok, floatx4 (&acc)[DG::VM],
+                                    float& m_run, float& l_run, bool& first, int& tile,
+                                    int full_end, int len, int q4, int n, int lane, float* mref,
+                                    int layer, int b, int kv) {
+  typedef typename NormWords<CF>::T NT;
+  constexpr int V = 8 / CF, W = waves_for(DG::DIM, BK, BV), NH = CF == 4 ? 4 : 8;
+  const int head = n & (NH - 1);
+  const bool voter = head < a.group; /* padding columns do not vote */
+  const float lg_eps = a.sparse_lg_eps;
+  /* the block's reference grows through plain stores of running maxima (a
+   * lost race leaves a smaller one, which is still a valid reference) */
+  auto publish = [&]() {
+    if (lane < NH && lane < a.group &&
+        m_run > __hip_atomic_load(&mref[lane], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP))
+      __hip_atomic_store(&mref[lane], m_run, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  };
+  /* does any (token, head) weight of the tile reach eps against the larger
+   * of the block's reference and the wave's running max?  smax is the
+   * lane's largest score relative to m_run (log2) */
+  auto keep_of = [&](float smax) -> bool {
+    const float ref =
+        __hip_atomic_load(&mref[head], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    return __any(voter && smax - fmaxf(ref - m_run, 0.0f) >= lg_eps);
+  };
+  /* a tile's value codes and norms go to its own ring slot, whose key
+   * refills leave them alone, so no register copy ever waits on an
+   * in-flight load */
+  auto load_v = [&](TileRegs<DG, CF>& r, bool keep) {
+    load_words<DG::SEG, DG::VA>(ad.v, keep ? ad.voff : kNoLoad, r.vt, r.vw);
+    r.vn = load_norms<NT>(ad.vn, keep ? ad.noff : kNoLoad, r.nt);
+  };
+  uint32_t nskip = 0;
+  if constexpr (DG::DEPTH == 3)
+    pf(rc, tile + 2 * W);
+  else
+    pf(rb, tile + W);
+  /* the first tile: scored here (it sets the running max) */
+  float pc[V], alpha = 1.0f, sm;
+  if (score_part<DG, BK, false, CF, true>(ra, bq, lk, lok, acc, m_run, l_run, first, tile * 32,
+                                          len, q4, n, pc, alpha, &sm))
+    publish();
+  bool keepc = keep_of(sm);
+  load_v(ra, keepc);
+  pf(ra, tile + DG::DEPTH * W);
+  /* the value half of a step: tile's values (in slot cur) at weights pc */
+  auto values = [&](TileRegs<DG, CF>& cur) {
+    if (keepc)
+      value_part<DG, BV, CF>(pc, cur.vn, cur.vw, lv, lo, lo8, acc, n);
+    else
+      ++nskip;
+  };
+  /* one step: cur holds the values of tile, nxt the keys of tile + W (which
+   * exists) */
+  auto step = [&](TileRegs<DG, CF>& cur, TileRegs<DG, CF>& nxt) {
+    float pn[V], al = 1.0f, smn;
+    const bool moved = score_part<DG, BK, false, CF, true>(nxt, bq, lk, lok, acc, m_run, l_run,
+                                                           first, (tile + W) * 32, len, q4, n,
+                                                           pn, al, &smn);
+    if (moved) publish();
+    const bool keepn = keep_of(smn);
+    load_v(nxt, keepn);
+    pf(nxt, tile + W + DG::DEPTH * W);
+    values(cur);
+    if (moved) {
+#pragma unroll
+      for (int m = 0; m < DG::VM; ++m) acc[m] *= al;
+    }
+    tile += W;
+#pragma unroll
+    for (int v = 0; v < V; ++v) pc[v] = pn[v];
+    keepc = keepn;
+  };
+  /* the wave's full tiles are tile, tile + W, ..., cnt of them; whole ring
+   * turns first (no exits inside, so the wait counts stay those of the
+   * steady state), then the rest, then the last tile's values */
+  const int cnt = (full_end - 1 - tile) / W + 1;
+  int k = 1;
+  if constexpr (DG::DEPTH == 3) {
+    for (; k + 3 <= cnt; k += 3) {
+      step(ra, rb);
+      step(rb, rc);
+      step(rc, ra);
+    }
+    if (k < cnt) {
+      step(ra, rb);
+      if (k + 1 < cnt) {
+        step(rb, rc);
+        values(rc);
+      } else {
+        values(rb);
+      }
+    } else {
+      values(ra);
+    }
+  } else {
+    for (; k + 2 <= cnt; k += 2) {
+      step(ra, rb);
+      step(rb, ra);
+    }
+    if (k < cnt) {
+      step(ra, rb);
+      values(rb);
+    } else {
+      values(ra);
+    }
+  }
+  tile += W;
+  if (a.skip_counts && lane == 0 && nskip)
+    atomicAdd(a.skip_counts + ((int64_t)layer * a.batch + b) * a.kv_heads + kv, nskip);
+}
+
+template <int D, int BK, int BV, int CF, bool PAGED, bool SPARSE>
 __global__ void __launch_bounds__(64 * waves_for(D, BK, BV))
 decode_kernel(DecArgs a) {
   using DG = DecGeo<D, BK, BV>;
@@ -708,8 +904,10 @@ decode_kernel(DecArgs a) {
       return TileOff{t * (32 * DG::RB), t * DG::TILE, t * 64};
     }
   };
+  /* with Sparse V the tile's values load only once its scores say they are
+   * needed (see below) */
   auto pf = [&](TileRegs<DG, CF>& r, int t) {
-    load_tile<DG, CF>(r, ad, toff(t < last ? t : last));
+    load_tile<DG, CF, !SPARSE>(r, ad, toff(t < last ? t : last));
   };
   TileRegs<DG, CF> ra, rb, rc;
   pf(ra, tile);
@@ -731,6 +929,11 @@ decode_kernel(DecArgs a) {
     const float v = h2f(qg[t]);
     qbuf[t] = ((sb[i >> 3] >> (i & 7)) & 1) ? -v : v;
   }
+  /* Sparse V: a running max per head shared by the block's waves, so that
+   * each gates against the largest one seen */
+  __shared__ float mref[8];
+  if constexpr (SPARSE)
+    if (threadIdx.x < 8) mref[threadIdx.x] = -INFINITY;
   __syncthreads();
   /* one wave per head transforms its row in registers */
   if (wave < G) {
@@ -787,7 +990,12 @@ decode_kernel(DecArgs a) {
    * (past the end they re-read the wave's last tile) so the number of loads
    * in flight is the same everywhere and each wait covers only the tile
    * about to be used. */
-  if (tile < full_end) {
+  if constexpr (SPARSE) {
+    if (tile < full_end)
+      sparse_tiles<DG, BK, BV, CF>(a, ad, ra, rb, rc, pf, bq, lut_k_rd, lut_v, lo, lo8, lok, acc,
+                                   m_run, l_run, first, tile, full_end, len, q4, n, lane, mref,
+                                   layer, b, kv);
+  } else if (tile < full_end) {
     auto step = [&](const TileRegs<DG, CF>& r) {
       tile_step<DG, BK, BV, false, CF>(r, bq, lut_k_rd, lut_v, lo, lo8, lok, acc, m_run, l_run,
                                        first, tile * 32, len, q4, n);
@@ -966,17 +1174,22 @@ template <int D, int BK, int BV>
 tq_status launch_decode_t(const DecArgs& a, hipStream_t s) {
   const int64_t blocks = (int64_t)a.n_layers * a.batch * a.kv_heads * a.splits;
   const dim3 grid((unsigned)blocks), block(64 * waves_for(D, BK, BV));
+#define TQ_LAUNCH(CF, PG, SP) hipLaunchKernelGGL((decode_kernel<D, BK, BV, CF, PG, SP>), grid, block, 0, s, a)
+  const bool sp = a.sparse_eps > 0.0f;
   if (a.block_table) {
-    if (a.group <= 4)
-      hipLaunchKernelGGL((decode_kernel<D, BK, BV, 4, true>), grid, block, 0, s, a);
-    else
-      hipLaunchKernelGGL((decode_kernel<D, BK, BV, 2, true>), grid, block, 0, s, a);
+    if (a.group <= 4) {
+      if (sp) TQ_LAUNCH(4, true, true); else TQ_LAUNCH(4, true, false);
+    } else {
+      if (sp) TQ_LAUNCH(2, true, true); else TQ_LAUNCH(2, true, false);
+    }
   } else {
-    if (a.group <= 4)
-      hipLaunchKernelGGL((decode_kernel<D, BK, BV, 4, false>), grid, block, 0, s, a);
-    else
-      hipLaunchKernelGGL((decode_kernel<D, BK, BV, 2, false>), grid, block, 0, s, a);
+    if (a.group <= 4) {
+      if (sp) TQ_LAUNCH(4, false, true); else TQ_LAUNCH(4, false, false);
+    } else {
+      if (sp) TQ_LAUNCH(2, false, true); else TQ_LAUNCH(2, false, false);
+    }
   }
+#undef TQ_LAUNCH
   return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_DEVICE;
 }
 
@@ -991,7 +1204,7 @@ int concurrent_blocks_t() {
     int dev = 0, cus = 0, per = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, decode_kernel<D, BK, BV, 2, false>, 64 * waves_for(D, BK, BV),
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, decode_kernel<D, BK, BV, 2, false, false>, 64 * waves_for(D, BK, BV),
                                                      0) != hipSuccess ||
         cus <= 0 || per <= 0) {
       (void)hipGetLastError();
@@ -1048,8 +1261,12 @@ tq_status tq_launch_decode(const tq_kv_cache* c, const tq_codebook_s* cbk,
                            const tq_codebook_s* cbv, const uint8_t* sign_bits,
                            const uint16_t* q, int q_heads, const int32_t* seq_lens,
                            int max_len, int n_layers, float* out, void* ws,
-                           const tq_decode_plan& plan, hipStream_t s) {
+                           const tq_decode_plan& plan, float sparse_eps, uint32_t* skip_counts,
+                           hipStream_t s) {
   DecArgs a;
+  a.sparse_eps = sparse_eps;
+  a.sparse_lg_eps = sparse_eps > 0.0f ? (float)log2((double)sparse_eps) : -INFINITY;
+  a.skip_counts = skip_counts;
   a.k_codes = c->k_codes;
   a.v_codes = c->v_codes;
   a.k_norms = (const uint8_t*)c->k_norms;

@@ -378,10 +378,11 @@ extern "C" size_t tq_decode_workspace_bytes(const tq_kv_cache* c, int q_heads, i
   return tq_plan_decode(c, q_heads, max_len, n_layers).ws_bytes;
 }
 
-extern "C" tq_status tq_decode_attn(const tq_kv_cache* c, tq_codebook cbk, tq_codebook cbv,
-                                    const uint8_t* sign_bits, const uint16_t* q, int q_heads,
-                                    const int32_t* seq_lens, int max_len, int n_layers,
-                                    float* out, void* ws, size_t ws_bytes, void* stream) {
+static tq_status decode_common(const tq_kv_cache* c, tq_codebook cbk, tq_codebook cbv,
+                               const uint8_t* sign_bits, const uint16_t* q, int q_heads,
+                               const int32_t* seq_lens, int max_len, int n_layers, float* out,
+                               void* ws, size_t ws_bytes, float sparse_eps,
+                               uint32_t* skip_counts, void* stream) {
   tq_status st = check_decode(c, q_heads, max_len, n_layers);
   if (st != TQ_OK) return st;
   if (!codebook_matches(cbk, c->head_dim, c->bits_k) ||
@@ -393,5 +394,25 @@ extern "C" tq_status tq_decode_attn(const tq_kv_cache* c, tq_codebook cbk, tq_co
   if (plan.ws_bytes > 0 && (!ws || ws_bytes < plan.ws_bytes || !aligned(ws, 256)))
     return TQ_ERR_WORKSPACE;
   return tq_launch_decode(c, cbk, cbv, sign_bits, q, q_heads, seq_lens, max_len, n_layers, out,
-                          ws, plan, (hipStream_t)stream);
+                          ws, plan, sparse_eps, skip_counts, (hipStream_t)stream);
+}
+
+extern "C" tq_status tq_decode_attn(const tq_kv_cache* c, tq_codebook cbk, tq_codebook cbv,
+                                    const uint8_t* sign_bits, const uint16_t* q, int q_heads,
+                                    const int32_t* seq_lens, int max_len, int n_layers,
+                                    float* out, void* ws, size_t ws_bytes, void* stream) {
+  return decode_common(c, cbk, cbv, sign_bits, q, q_heads, seq_lens, max_len, n_layers, out, ws,
+                       ws_bytes, 0.0f, nullptr, stream);
+}
+
+extern "C" tq_status tq_decode_attn_sparse(const tq_kv_cache* c, tq_codebook cbk,
+                                           tq_codebook cbv, const uint8_t* sign_bits,
+                                           const uint16_t* q, int q_heads,
+                                           const int32_t* seq_lens, int max_len, int n_layers,
+                                           float eps, uint32_t* skip_counts, float* out,
+                                           void* ws, size_t ws_bytes, void* stream) {
+  if (!(eps >= 0.0f) || eps == INFINITY) return TQ_ERR_ARG; /* NaN, negative or infinite */
+  if (skip_counts && !aligned(skip_counts, 4)) return TQ_ERR_ARG;
+  return decode_common(c, cbk, cbv, sign_bits, q, q_heads, seq_lens, max_len, n_layers, out, ws,
+                       ws_bytes, eps, skip_counts, stream);
 }

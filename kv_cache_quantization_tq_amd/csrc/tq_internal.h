@@ -78,6 +78,7 @@ tq_status tq_launch_decode(const tq_kv_cache* c, const tq_codebook_s* cbk,
                            const tq_codebook_s* cbv, const uint8_t* sign_bits,
                            const uint16_t* q, int q_heads, const int32_t* seq_lens,
                            int max_len, int n_layers, float* out, void* ws,
-                           const tq_decode_plan& plan, hipStream_t stream);
+                           const tq_decode_plan& plan, float sparse_eps, uint32_t* skip_counts,
+                           hipStream_t stream);
 
 #endif

@@ -1,0 +1,175 @@
+"""GPU parity of decode attention with the Sparse V gate (tq_decode_attn_sparse)
+against the oracle's sparse attention ("TurboQuant+ ...", "Sparse V").
+
+The kernel decides per 32-token tile against a running maximum, so which
+tokens below the threshold it leaves out depends on the visiting order; the
+oracle's bound on what the left-out tokens can contribute (per coordinate)
+widens the bars, and the per-unit skip counts are checked against the tiles
+the oracle says may be skipped."""
+import math
+
+import numpy as np
+import pytest
+
+import kv_cache_quantization_tq_amd as tq
+import oracle
+import synth
+from helpers import band_flip_bound, check_attention, require_gpu
+
+pytestmark = pytest.mark.gpu
+SEED = 1001
+
+
+def _case(torch, d, bk, bv, G, lens, Lyr=2, H=2, seed=SEED, paged_tokens=None):
+    B = len(lens)
+    T = max(lens)
+    cap = ((T + 31) // 32) * 32 + 32
+    if paged_tokens:
+        P = paged_tokens
+        cap = (cap + P - 1) // P * P
+        maxp = cap // P
+        rng = np.random.default_rng(seed)
+        table = rng.permutation(B * maxp).reshape(B, maxp).astype(np.int32)
+        cache = tq.PagedKVCache(Lyr, B, H, d, bk, bv, P, maxp, B * maxp, table)
+    else:
+        cache = tq.KVCache(Lyr, B, H, d, bk, bv, cap)
+    sbs = np.stack([synth.sign_bits(seed, l, d) for l in range(Lyr)])
+    sbd = torch.from_numpy(sbs).cuda()
+    cbk, cbv = tq.Codebook(d, bk), tq.Codebook(d, bv)
+    for l in range(Lyr):
+        k = torch.empty((1, B, H, T, d), dtype=torch.int16, device="cuda")
+        v = torch.empty_like(k)
+        synth.kv_dev(seed, 0, l, k[0])
+        synth.kv_dev(seed, 1, l, v[0])
+        tq.append(cache, cbk, cbv, sbd[l:l + 1], k, v,
+                  torch.zeros(B, dtype=torch.int32, device="cuda"), host_max_pos=0, layer0=l,
+                  n_layers=1)
+    q = torch.empty((Lyr, B, G * H, d), dtype=torch.int16, device="cuda")
+    for l in range(Lyr):
+        synth.q_dev(seed, 0, l, q[l])
+    lens_d = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    ws = tq.workspace(cache, G * H, T)
+    torch.cuda.synchronize()
+    return dict(cache=cache, sbs=sbs, sbd=sbd, cbk=cbk, cbv=cbv, q=q, lens_d=lens_d, T=T, ws=ws,
+                Lyr=Lyr, B=B, H=H, G=G, d=d, bk=bk, bv=bv, lens=lens, seed=seed)
+
+
+def _run_sparse(torch, c, eps):
+    out = torch.empty((c["Lyr"], c["B"], c["G"] * c["H"], c["d"]), dtype=torch.float32,
+                      device="cuda")
+    counts = torch.zeros((c["Lyr"], c["B"], c["H"]), dtype=torch.int32, device="cuda")
+    if c["ws"] is not None:
+        c["ws"].zero_()
+    tq.decode_sparse(c["cache"], c["cbk"], c["cbv"], c["sbd"], c["q"], c["lens_d"], c["T"], out,
+                     eps, c["ws"], skip_counts=counts)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), counts.cpu().numpy()
+
+
+def _oracle(c, eps, units=None):
+    """Oracle sparse output, bound (band flips + left-out tokens) and, per
+    unit, the number of full tiles whose every (token, head) weight lies
+    below eps (with a relative margin for rounding) relative to the final
+    max: the most the kernel may skip."""
+    d, G, H = c["d"], c["G"], c["H"]
+    q16 = c["q"].cpu().numpy().view(np.uint16)
+    shape = (c["Lyr"], c["B"], G * H, d)
+    ref, bound = np.zeros(shape), np.zeros(shape)
+    may_skip = np.zeros((c["Lyr"], c["B"], H), dtype=np.int64)
+    for l in range(c["Lyr"]):
+        for b, n in enumerate(c["lens"]):
+            for h in range(H):
+                if units is not None and (l, b, h) not in units:
+                    continue
+                k = synth.kv_host(c["seed"], 0, l, b, h, d, 0, n)
+                v = synth.kv_host(c["seed"], 1, l, b, h, d, 0, n)
+                qq = q16[l, b, h * G:(h + 1) * G]
+                st = oracle.decode_stream(k, v, qq, c["bk"], c["bv"], c["sbs"][l], full=True)
+                q64 = oracle.halves_to_double(qq)
+                bf, _ = band_flip_bound(q64, k, v, st, c["bk"], c["bv"], c["sbs"][l])
+                o, bs, w = oracle.attention_sparse(q64, st["K"], st["V"], eps, want_weights=True)
+                sl = slice(h * G, (h + 1) * G)
+                ref[l, b, sl], bound[l, b, sl] = o, bf + bs
+                nf = n // 32
+                if nf:
+                    tmax = w[:, :nf * 32].reshape(G, nf, 32).max(axis=(0, 2))
+                    may_skip[l, b, h] = int((tmax < eps * (1 + 1e-3)).sum())
+    return ref, bound, may_skip
+
+
+def test_sparse_eps0_equals_dense():
+    """eps = 0 runs the dense kernel: bit-identical output, nothing counted."""
+    torch = require_gpu()
+    c = _case(torch, 128, 4, 2, 4, [700, 257])
+    out_s, counts = _run_sparse(torch, c, 0.0)
+    out_d = torch.empty((c["Lyr"], c["B"], c["G"] * c["H"], c["d"]), dtype=torch.float32,
+                        device="cuda")
+    c["ws"] is not None and c["ws"].zero_()
+    tq.decode(c["cache"], c["cbk"], c["cbv"], c["sbd"], c["q"], c["lens_d"], c["T"], out_d, c["ws"])
+    torch.cuda.synchronize()
+    assert np.array_equal(out_s, out_d.cpu().numpy())
+    assert not counts.any()
+
+
+@pytest.mark.parametrize("d,bk,bv,G,lens", [
+    (128, 4, 2, 4, [4000, 257]),
+    (128, 3, 2, 8, [2049, 33]),
+    (128, 4, 3, 1, [1500]),
+    (64, 4, 2, 4, [3000, 96]),
+    (256, 4, 2, 2, [1200, 31]),
+    (64, 3, 4, 8, [900]),
+])
+@pytest.mark.parametrize("eps", [1e-6, 1e-3])
+def test_sparse_parity(d, bk, bv, G, lens, eps):
+    torch = require_gpu()
+    c = _case(torch, d, bk, bv, G, lens)
+    out, counts = _run_sparse(torch, c, eps)
+    ref, bound, may_skip = _oracle(c, eps)
+    what = f"sparse d={d} K{bk}/V{bv} G={G} lens={lens} eps={eps}"
+    check_attention(out, ref, bound, what)
+    print(f"{what}: skipped {counts.sum()} of {may_skip.sum()} skippable tiles", flush=True)
+    assert (counts >= 0).all() and (counts <= may_skip).all(), (counts, may_skip)
+
+
+def test_sparse_everything_skipped():
+    """eps above 1: every full tile is skipped (the count is exact), so a
+    length that is a multiple of 32 gives a zero output, and the ragged tail
+    alone is accumulated otherwise (within the bound)."""
+    torch = require_gpu()
+    c = _case(torch, 128, 4, 2, 4, [640, 300], Lyr=1)
+    out, counts = _run_sparse(torch, c, 2.0)
+    assert np.array_equal(counts[0, 0], [20, 20]) and np.array_equal(counts[0, 1], [9, 9])
+    assert not out[0, 0].any()
+    ref, bound, _ = _oracle(c, 2.0)
+    assert not ref.any()
+    assert (np.abs(out - ref) <= bound + 1e-5).all()
+
+
+def test_sparse_skips_on_long_context():
+    """A 32K-token context of the benchmark's data (8 KV heads, G = 4): the
+    gate skips a good part of the tiles the oracle allows (the block shares
+    its running maxima), and the sampled units stay within the bars."""
+    torch = require_gpu()
+    eps = 1e-4
+    c = _case(torch, 128, 4, 2, 4, [32768], Lyr=32, H=8)
+    out, counts = _run_sparse(torch, c, eps)
+    units = {(0, 0, 0), (17, 0, 5)}
+    ref, bound, may_skip = _oracle(c, eps, units)
+    for (l, b, h) in units:
+        sl = slice(h * 4, h * 4 + 4)
+        check_attention(out[l, b, sl], ref[l, b, sl], bound[l, b, sl], f"32K unit {h}")
+        print(f"unit {h}: skipped {counts[l, b, h]} of {may_skip[l, b, h]} skippable tiles",
+              flush=True)
+        assert counts[l, b, h] <= may_skip[l, b, h]
+        assert counts[l, b, h] >= 0.3 * may_skip[l, b, h]
+
+
+@pytest.mark.parametrize("P", [32, 256])
+def test_sparse_paged(P):
+    torch = require_gpu()
+    eps = 1e-3
+    c = _case(torch, 128, 4, 2, 4, [3000, 700], paged_tokens=P)
+    out, counts = _run_sparse(torch, c, eps)
+    ref, bound, may_skip = _oracle(c, eps)
+    check_attention(out, ref, bound, f"sparse paged P={P}")
+    assert (counts <= may_skip).all()

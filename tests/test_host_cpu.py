@@ -92,6 +92,25 @@ def test_validation_before_device_work():
                        None) == 1
 
 
+def test_sparse_decode_validation():
+    """tq_decode_attn_sparse rejects a NaN, negative or infinite threshold and a
+    misaligned count array before anything else (an unsupported head dim
+    would otherwise answer TQ_ERR_UNSUPPORTED); valid thresholds reach the
+    ordinary checks."""
+    L = tq.lib()
+    vp = ctypes.c_void_p
+    s = _fake_cache(head_dim=96)
+    def call(eps, counts=None):
+        return L.tq_decode_attn_sparse(ctypes.byref(s), None, None, vp(1), vp(16), 8, vp(4), 16,
+                                       1, eps, counts, vp(16), None, 0, None)
+    for eps in (float("nan"), -1e-6, float("inf")):
+        assert call(eps) == 1, eps
+    assert call(1e-6, vp(2)) == 1
+    for eps in (0.0, 1e-6, 1.0, 3.0):
+        assert call(eps) == 2, eps
+        assert call(eps, vp(4)) == 2, eps
+
+
 def test_workspace_planning():
     L = tq.lib()
     s = _fake_cache(capacity=32768)
