@@ -108,19 +108,19 @@ def _report(workload, metric, value, unit, higher, extra, args, ms_per_step):
 
 
 def _timed(torch, fn, steps, warmup):
-    """Median over `steps` timed calls of fn (after `warmup` calls), in ms."""
+    """Median over `steps` calls of fn issued back to back (after `warmup`
+    calls), each bracketed by its own events, in ms."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    ts = []
-    for _ in range(steps):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for e0, e1 in evs:
         e0.record()
         fn()
         e1.record()
-        torch.cuda.synchronize()
-        ts.append(e0.elapsed_time(e1))
-    ts.sort()
+    torch.cuda.synchronize()
+    ts = sorted(e0.elapsed_time(e1) for e0, e1 in evs)
     return ts[len(ts) // 2]
 
 
