@@ -205,6 +205,24 @@ tq_status tq_decode_attn(const tq_kv_cache* c, tq_codebook cbk, tq_codebook cbv,
                          const int32_t* seq_lens, int max_len, int n_layers, float* out,
                          void* ws, size_t ws_bytes, void* stream);
 
+/* Prefill (extend) attention over the compressed cache: t_new query tokens
+ * per sequence, already written to the cache (e.g. by tq_append), each
+ * attending causally to its sequence's cached tokens ("We Built ...", "Test
+ * Suite": softmax(Q K^T / sqrt d) V; AdapTQ page, step 3, with many queries;
+ * the prefill the TurboQuant+ page times).  Query i of sequence b sits at
+ * position pos[b] + i and attends to cache rows 0 .. pos[b] + i, the result
+ * equalling tq_decode_attn with that query and length pos[b] + i + 1.
+ * q:    device fp16 [n_layers][batch][q_heads][t_new][d], 16-byte aligned.
+ * pos:  device int32 [batch], 4-byte aligned; negative values count as 0,
+ *       rows at or past capacity are never read.
+ * out:  device fp32 [n_layers][batch][q_heads][t_new][d], 16-byte aligned,
+ *       in the original domain.
+ * Query head h reads KV head h / (q_heads / kv_heads); group sizes 1 .. 8.
+ * Contiguous or paged cache.  t_new == 0 is a no-op.  No workspace. */
+tq_status tq_prefill_attn(const tq_kv_cache* c, tq_codebook cbk, tq_codebook cbv,
+                          const uint8_t* sign_bits, const uint16_t* q, int q_heads, int t_new,
+                          const int32_t* pos, int n_layers, float* out, void* stream);
+
 /* tq_decode_attn with the Sparse V gate ("TurboQuant+: Compresion de Cache KV
  * 6.4x para LLMs", section "Sparse V": the value work of positions with
  * negligible attention weight is skipped; the page gives no threshold).

@@ -19,7 +19,7 @@ EXPORTS = (
     "tq_status_str", "tq_codebook_compute", "tq_codebook_init", "tq_codebook_read",
     "tq_codebook_head_dim", "tq_codebook_bits", "tq_codebook_free", "tq_encode",
     "tq_cache_layer_bytes", "tq_append", "tq_decode_workspace_bytes", "tq_decode_attn",
-    "tq_decode_attn_sparse",
+    "tq_decode_attn_sparse", "tq_prefill_attn",
 )
 
 
@@ -74,8 +74,10 @@ def lib():
                                      vp, sz, vp]
         L.tq_decode_attn_sparse.argtypes = [P(KVCacheStruct), vp, vp, vp, vp, i32, vp, i32, i32,
                                             ctypes.c_float, vp, vp, vp, sz, vp]
+        L.tq_prefill_attn.argtypes = [P(KVCacheStruct), vp, vp, vp, vp, i32, i32, vp, i32, vp, vp]
         for f in ("tq_codebook_compute", "tq_codebook_init", "tq_codebook_read", "tq_encode",
-                  "tq_cache_layer_bytes", "tq_append", "tq_decode_attn", "tq_decode_attn_sparse"):
+                  "tq_cache_layer_bytes", "tq_append", "tq_decode_attn", "tq_decode_attn_sparse",
+                  "tq_prefill_attn"):
             getattr(L, f).restype = i32
         _lib = L
     return _lib
@@ -287,6 +289,17 @@ def decode_sparse(cache, cbk, cbv, sign_bits, q, seq_lens, max_len, out, eps, ws
         ctypes.byref(s), cbk.handle, cbv.handle, _ptr(sign_bits), _ptr(q), q_heads,
         _ptr(seq_lens), max_len, n_layers, float(eps), _ptr(skip_counts), _ptr(out), _ptr(ws),
         ws_bytes, _stream(stream)))
+
+
+def prefill(cache, cbk, cbv, sign_bits, q, pos, out, layer0=0, n_layers=None, stream=None):
+    """tq_prefill_attn: q fp16 [n_layers][B][Hq][t_new][d], pos int32 [B]
+    (CUDA), out fp32 [n_layers][B][Hq][t_new][d]."""
+    n_layers = n_layers if n_layers is not None else q.shape[0]
+    q_heads, t_new = q.shape[2], q.shape[3]
+    s = cache.struct(layer0)
+    _check("tq_prefill_attn", lib().tq_prefill_attn(
+        ctypes.byref(s), cbk.handle, cbv.handle, _ptr(sign_bits), _ptr(q), q_heads, t_new,
+        _ptr(pos), n_layers, _ptr(out), _stream(stream)))
 
 
 def workspace(cache, q_heads, max_len, n_layers=None, layer0=0, device="cuda"):

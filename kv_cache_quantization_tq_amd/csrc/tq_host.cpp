@@ -405,6 +405,23 @@ extern "C" tq_status tq_decode_attn(const tq_kv_cache* c, tq_codebook cbk, tq_co
                        ws_bytes, 0.0f, nullptr, stream);
 }
 
+extern "C" tq_status tq_prefill_attn(const tq_kv_cache* c, tq_codebook cbk, tq_codebook cbv,
+                                     const uint8_t* sign_bits, const uint16_t* q, int q_heads,
+                                     int t_new, const int32_t* pos, int n_layers, float* out,
+                                     void* stream) {
+  tq_status st = check_decode(c, q_heads, 0, n_layers);
+  if (st != TQ_OK) return st;
+  if (t_new < 0) return TQ_ERR_ARG;
+  if (!codebook_matches(cbk, c->head_dim, c->bits_k) ||
+      !codebook_matches(cbv, c->head_dim, c->bits_v))
+    return TQ_ERR_ARG;
+  if (!sign_bits || !q || !pos || !out) return TQ_ERR_ARG;
+  if (!aligned(q, 16) || !aligned(out, 16) || !aligned(pos, 4)) return TQ_ERR_ARG;
+  if (t_new == 0) return TQ_OK;
+  return tq_launch_prefill(c, cbk, cbv, sign_bits, q, q_heads, t_new, pos, n_layers, out,
+                           (hipStream_t)stream);
+}
+
 extern "C" tq_status tq_decode_attn_sparse(const tq_kv_cache* c, tq_codebook cbk,
                                            tq_codebook cbv, const uint8_t* sign_bits,
                                            const uint16_t* q, int q_heads,

@@ -65,6 +65,11 @@ tq_status tq_launch_append(const tq_kv_cache* c, const tq_codebook_s* cbk,
                            const uint16_t* k_new, const uint16_t* v_new, int t_new,
                            const int32_t* pos, int n_layers, hipStream_t stream);
 
+tq_status tq_launch_prefill(const tq_kv_cache* c, const tq_codebook_s* cbk,
+                            const tq_codebook_s* cbv, const uint8_t* sign_bits,
+                            const uint16_t* q, int q_heads, int t_new, const int32_t* pos,
+                            int n_layers, float* out, hipStream_t stream);
+
 /* Split count and workspace layout of one decode call. */
 struct tq_decode_plan {
   int splits;          /* token splits per (layer, seq, kv head) */

@@ -1,0 +1,462 @@
+/*
+ * gfx950 prefill (extend) attention over the compressed cache: a chunk of new
+ * query tokens, already appended to the cache, attends causally to the
+ * sequence's cached tokens, reading the packed codes directly.
+ *
+ * Math (per layer, sequence, KV head; the G query heads of the group share
+ * every dequantized tile), as in the decode step, one query at a time:
+ *   q'' = H D q * log2(e) / (d * sigma_K)
+ *   s_j = n_j * sum_i q''_i * (sigma_K c_K[code_ji])        (base-2 logits)
+ *   online softmax in base 2 over j <= the query's position;
+ *   o = D H (sum_j p_j m_j sigma_V c_V[code_j]) / (sqrt(d) sigma_V l)
+ * ("We Built a Python Library That Cuts LLM Memory Usage by 80%", "Test
+ * Suite": softmax(Q K^T / sqrt d) V; AdapTQ page, "How it works (HAR + VQ)",
+ * step 3: queries rotated once and scored against the codebook levels; the
+ * many-query case is the prefill the TurboQuant+ page times, "Paridad de
+ * Velocidad Alcanzada".)
+ *
+ * With many queries per tile the products are dense contractions, so they run
+ * on the matrix cores (v_mfma_f32_16x16x32_f16), and each 32-token tile is
+ * dequantized once per block into LDS for all its queries:
+ *   keys:   fp16 levels and fp16 remainders (level - fp16 level) * 2^11, token
+ *           rows; S^T[16 tokens x 16 queries] = Khi Qhi + Khi Qlo + Klo Qrem,
+ *           Qhi + Qlo = q'' split into fp16 parts, Qrem = fp16(q'' 2^-11),
+ *           which carries the level to ~2^-22 (scores reach tens of nats);
+ *   values: fp16 levels, coordinate rows with the tile's tokens in the order
+ *           the score output leaves them in the lanes, so P^T feeds the value
+ *           product without moving: O^T[16 coords x 16 queries] +=
+ *           V^T[16 x 32 tokens] P'^T, P' = p * m_j split into two fp16 parts.
+ * A block is 8 waves x 16 (head, query) columns: 128 / Gp queries of each of
+ * the G heads (Gp = G rounded up to a power of two).  The next tile's codes
+ * are loaded into registers while the current one is multiplied.
+ */
+#include <hip/hip_runtime.h>
+
+#include "tq_internal.h"
+
+namespace {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWaves = 8;
+constexpr int kCols = 16 * kWaves; /* (head, query) columns per block */
+
+struct PreArgs {
+  const uint8_t* k_codes;
+  const uint8_t* v_codes;
+  const uint8_t* k_norms;
+  const uint8_t* v_norms;
+  int64_t ls_kc, ls_vc, ls_kn, ls_vn;
+  int batch, kv_heads, capacity, q_heads, group, qc, t_new, chunks;
+  const int32_t* block_table; /* paged storage: [batch][max_pages] */
+  int lg_tpp, max_pages, num_pages;
+  const uint8_t* sign_bits;
+  const uint16_t* q;
+  const int32_t* pos;
+  const uint32_t* lut_k;    /* pair table: two fp16 levels per index */
+  const uint32_t* lut_k_lo; /* pair table: two fp16 remainders * 2^11 */
+  const uint32_t* lut_v;
+  float qscale, oscale;
+  float* out;
+};
+
+__device__ inline float h2f(uint32_t h) { return (float)__builtin_bit_cast(_Float16, (uint16_t)h); }
+
+__device__ inline __amdgpu_buffer_rsrc_t make_stream(const uint8_t* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, 0x00020000);
+}
+
+/* The 8 codes (8 * B bits, little-endian) at byte offset off of a stream: two
+ * aligned words and a funnel shift (bytes past the stream read as 0). */
+template <int B>
+__device__ inline uint32_t load_codes8(__amdgpu_buffer_rsrc_t rs, int32_t off) {
+  const uint32_t a = (uint32_t)off & ~3u;
+  const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b32(rs, a, 0, 0);
+  if constexpr (B == 3) {
+    const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b32(rs, a + 4, 0, 0);
+    return __builtin_amdgcn_alignbit(hi, lo, (uint32_t)(off & 3) * 8u);
+  } else {
+    /* 2 or 4 bytes at an even offset: inside the aligned word */
+    return lo >> ((off & 3) * 8);
+  }
+}
+
+/* Walsh-Hadamard transform of one LDS row of D floats by one wave (lane l
+ * holds coordinates l + 64 j on return). */
+template <int D>
+struct Row {
+  float v[D >= 64 ? D / 64 : 1];
+};
+template <int D>
+__device__ inline Row<D> row_fwht(const float* row, int lane) {
+  constexpr int J = D / 64;
+  Row<D> r;
+#pragma unroll
+  for (int j = 0; j < J; ++j) r.v[j] = row[lane + 64 * j];
+#pragma unroll
+  for (int hj = 1; hj < J; hj <<= 1)
+#pragma unroll
+    for (int j = 0; j < J; ++j)
+      if (!(j & hj)) {
+        const float x = r.v[j], y = r.v[j | hj];
+        r.v[j] = x + y;
+        r.v[j | hj] = x - y;
+      }
+#pragma unroll
+  for (int h = 1; h < 64; h <<= 1)
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+      const float y = __shfl_xor(r.v[j], h);
+      r.v[j] = (lane & h) ? y - r.v[j] : r.v[j] + y;
+    }
+  return r;
+}
+
+template <int D, int BK, int BV>
+struct PreGeo {
+  static constexpr int RBK = D * BK / 8;        /* key row bytes */
+  static constexpr int SEG = D * BV / 16;       /* value segment bytes */
+  static constexpr int TILE_V = 32 * D * BV / 8;
+  static constexpr int KP = D + 8;              /* key tile pitch (halfs) */
+  static constexpr int VP = 32 + 8;             /* value tile pitch (halfs) */
+  static constexpr int PWK = 1 << (2 * BK), PWV = 1 << (2 * BV); /* pair table words */
+  static constexpr int ITEMS = 4 * D;           /* 8-code items per tile (keys; values too) */
+  static constexpr int PER = (ITEMS + 64 * kWaves - 1) / (64 * kWaves);
+  /* LDS: [query / output rows (fp32) | tiles] union, then tables */
+  static constexpr int QBYTES = kCols * D * 4;
+  static constexpr int TBYTES = 2 * 32 * KP * 2 + D * VP * 2 + 2 * 32 * 4;
+  static constexpr int UBYTES = QBYTES > TBYTES ? QBYTES : TBYTES;
+  static constexpr int BYTES = UBYTES + (2 * PWK + PWV) * 4;
+};
+
+/* Token order of the value tile's k index (see the header): k = 8 kq + j holds
+ * token 4 kq + j (j < 4) or 16 + 4 kq + j - 4. */
+__device__ inline int kpos(int t) { return t < 16 ? 8 * (t >> 2) + (t & 3) : 8 * ((t - 16) >> 2) + 4 + (t & 3); }
+
+template <int D, int BK, int BV, bool PAGED>
+__global__ void __launch_bounds__(64 * kWaves) prefill_kernel(PreArgs a) {
+  using PG = PreGeo<D, BK, BV>;
+  __shared__ __align__(16) char smem[PG::BYTES];
+  float* qbuf = (float*)smem;                            /* [kCols][D] */
+  _Float16* khi = (_Float16*)smem;                       /* [32][KP] */
+  _Float16* klo = khi + 32 * PG::KP;                     /* [32][KP] */
+  _Float16* vt = klo + 32 * PG::KP;                      /* [D][VP] */
+  float* nk = (float*)(vt + D * PG::VP);                 /* [32] */
+  float* nv = nk + 32;                                   /* [32] */
+  uint32_t* tk = (uint32_t*)(smem + PG::UBYTES);         /* key pairs, then remainders */
+  uint32_t* tv = tk + 2 * PG::PWK;
+
+  const int tid = threadIdx.x, lane = tid % 64;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+  const int n = lane % 16, kq = lane / 16;
+  const int chunk = blockIdx.x % a.chunks;
+  int64_t unit = blockIdx.x / a.chunks;
+  const int kv = (int)(unit % a.kv_heads);
+  unit /= a.kv_heads;
+  const int b = (int)(unit % a.batch);
+  const int layer = (int)(unit / a.batch);
+  const int q0 = chunk * a.qc;
+  const int qn = (a.t_new - q0) < a.qc ? (a.t_new - q0) : a.qc; /* queries of this chunk */
+  int p0 = a.pos[b];
+  p0 = p0 < 0 ? 0 : p0;
+
+  /* tables */
+  for (int i = tid; i < PG::PWK; i += blockDim.x) {
+    tk[i] = a.lut_k[i];
+    tk[PG::PWK + i] = a.lut_k_lo[i];
+  }
+  for (int i = tid; i < PG::PWV; i += blockDim.x) tv[i] = a.lut_v[i];
+
+  /* queries: column c = head g * qc + query i; q'' = H D q, scaled */
+  const uint8_t* sb = a.sign_bits + (int64_t)layer * (D / 8);
+  for (int t = tid; t < kCols * D; t += blockDim.x) {
+    const int c = t / D, i = t % D;
+    const int g = c / a.qc, qi = c % a.qc;
+    float v = 0.0f;
+    if (g < a.group && qi < qn) {
+      const int64_t row = (((int64_t)layer * a.batch + b) * a.q_heads + (int64_t)kv * a.group + g) *
+                              a.t_new + q0 + qi;
+      v = h2f(a.q[row * D + i]);
+      v = ((sb[i >> 3] >> (i & 7)) & 1) ? -v : v;
+    }
+    qbuf[t] = v;
+  }
+  __syncthreads();
+  for (int r = 0; r < 16; ++r) {
+    float* row = qbuf + (16 * wave + r) * D;
+    const Row<D> t = row_fwht<D>(row, lane);
+#pragma unroll
+    for (int j = 0; j < D / 64; ++j) row[lane + 64 * j] = t.v[j] * a.qscale;
+  }
+  __syncthreads();
+  /* B operands: lane (n, kq) holds coordinates 32 s + 8 kq + 0..7 of column
+   * 16 wave + n: fp16 part, fp16 remainder, fp16(q'' 2^-11) */
+  constexpr int KS = D / 32;
+  half8 qhi[KS], qlo[KS], qrm[KS];
+  {
+    const float* row = qbuf + (16 * wave + n) * D;
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float v = row[32 * s + 8 * kq + j];
+        const _Float16 h = (_Float16)v;
+        qhi[s][j] = h;
+        qlo[s][j] = (_Float16)(v - (float)h);
+        qrm[s][j] = (_Float16)(v * 0x1p-11f);
+      }
+  }
+  /* this lane's column: its causal limit (tokens < lim are attended) */
+  const int col = 16 * wave + n;
+  const int cg = col / a.qc, ci = col % a.qc;
+  const bool live = cg < a.group && ci < qn;
+  int lim = p0 + q0 + ci + 1;
+  lim = lim > a.capacity ? a.capacity : lim;
+  lim = live ? lim : 1; /* padding columns attend token 0 only */
+  int blk_lim = p0 + q0 + qn;
+  blk_lim = blk_lim > a.capacity ? a.capacity : blk_lim;
+  const int ntiles = (blk_lim + 31) / 32;
+  __syncthreads(); /* qbuf is dead: the tiles take its place */
+
+  /* streams of this (layer, sequence, head), or of the layer's page pool */
+  const int64_t sh = PAGED ? 0 : (int64_t)b * a.kv_heads + kv;
+  const int64_t srows = PAGED ? (int64_t)a.num_pages * a.kv_heads * (32 << a.lg_tpp) : a.capacity;
+  const __amdgpu_buffer_rsrc_t rk =
+      make_stream(a.k_codes + layer * a.ls_kc + sh * a.capacity * PG::RBK, srows * PG::RBK);
+  const __amdgpu_buffer_rsrc_t rv = make_stream(
+      a.v_codes + layer * a.ls_vc + sh * (a.capacity / 32) * PG::TILE_V, srows / 32 * PG::TILE_V);
+  const __amdgpu_buffer_rsrc_t rkn = make_stream(a.k_norms + layer * a.ls_kn + sh * a.capacity * 2, srows * 2);
+  const __amdgpu_buffer_rsrc_t rvn = make_stream(a.v_norms + layer * a.ls_vn + sh * a.capacity * 2, srows * 2);
+  /* tile t's first key row, value tile and first norm, as stream offsets in
+   * units of rows / tiles */
+  auto tile_rows = [&](int t) -> int32_t {
+    if constexpr (PAGED) {
+      const int tpp = 1 << a.lg_tpp;
+      int phys = a.block_table[(int64_t)b * a.max_pages + (t >> a.lg_tpp)];
+      phys = phys < 0 ? 0 : (phys >= a.num_pages ? a.num_pages - 1 : phys);
+      return (phys * a.kv_heads + kv) * (tpp * 32) + (t & (tpp - 1)) * 32;
+    } else {
+      return t * 32;
+    }
+  };
+
+  /* raw codes of one tile, per thread: PER key items and PER value items */
+  uint32_t kraw[PG::PER], vraw[PG::PER], nraw = 0;
+  auto fetch = [&](int t) {
+    const int32_t r0 = tile_rows(t);
+#pragma unroll
+    for (int u = 0; u < PG::PER; ++u) {
+      const int it = tid + u * 64 * kWaves;
+      kraw[u] = 0;
+      vraw[u] = 0;
+      if (it < PG::ITEMS) {
+        const int tok = it / (D / 8), grp = it % (D / 8);
+        kraw[u] = load_codes8<BK>(rk, (r0 + tok) * PG::RBK + grp * BK);
+        const int seg = it / (D / 16), m = it % (D / 16);
+        vraw[u] = load_codes8<BV>(rv, (r0 / 32) * PG::TILE_V + seg * PG::SEG + m * BV);
+      }
+    }
+    if (tid < 32)
+      nraw = __builtin_amdgcn_raw_buffer_load_b16(rkn, (uint32_t)(r0 + tid) * 2u, 0, 0);
+    else if (tid < 64)
+      nraw = __builtin_amdgcn_raw_buffer_load_b16(rvn, (uint32_t)(r0 + tid - 32) * 2u, 0, 0);
+  };
+  /* dequantize the fetched tile into LDS */
+  auto spill = [&]() {
+#pragma unroll
+    for (int u = 0; u < PG::PER; ++u) {
+      const int it = tid + u * 64 * kWaves;
+      if (it < PG::ITEMS) {
+        const int tok = it / (D / 8), grp = it % (D / 8);
+        u32x4 h, l;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const uint32_t e = (kraw[u] >> (2 * BK * p)) & (PG::PWK - 1);
+          h[p] = tk[e];
+          l[p] = tk[PG::PWK + e];
+        }
+        *(u32x4*)(khi + tok * PG::KP + 8 * grp) = h;
+        *(u32x4*)(klo + tok * PG::KP + 8 * grp) = l;
+        /* value segment seg = 16 q + r, field m: coordinate r (d/16) + m of
+         * tokens 8 q + 0..7, pairs of consecutive tokens adjacent in kpos */
+        const int seg = it / (D / 16), m = it % (D / 16);
+        const int qq = seg >> 4, rr = seg & 15;
+        _Float16* vrow = vt + (rr * (D / 16) + m) * PG::VP;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const uint32_t e = (vraw[u] >> (2 * BV * p)) & (PG::PWV - 1);
+          *(uint32_t*)(vrow + kpos(8 * qq + 2 * p)) = tv[e];
+        }
+      }
+    }
+    if (tid < 32) nk[tid] = h2f(nraw);
+    else if (tid < 64) nv[tid - 32] = h2f(nraw);
+  };
+
+  floatx4 acc[D / 16];
+#pragma unroll
+  for (int m = 0; m < D / 16; ++m) acc[m] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.0f;
+
+  if (ntiles > 0) fetch(0);
+  for (int t = 0; t < ntiles; ++t) {
+    spill();
+    __syncthreads();
+    if (t + 1 < ntiles) fetch(t + 1);
+    /* scores of the two 16-token halves */
+    floatx4 s[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      s[h] = floatx4{0.f, 0.f, 0.f, 0.f};
+      const _Float16* kr = khi + (16 * h + n) * PG::KP + 8 * kq;
+      const _Float16* kl = klo + (16 * h + n) * PG::KP + 8 * kq;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const half8 ah = *(const half8*)(kr + 32 * ks);
+        const half8 al = *(const half8*)(kl + 32 * ks);
+        s[h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, qhi[ks], s[h], 0, 0, 0);
+        s[h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, qlo[ks], s[h], 0, 0, 0);
+        s[h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, qrm[ks], s[h], 0, 0, 0);
+      }
+    }
+    /* lane (n, kq) holds tokens 16 h + 4 kq + i of column n */
+    float sc[8];
+    const int tok0 = 32 * t;
+    const bool edge = tok0 + 32 > p0 + q0 + 1; /* some column may stop inside */
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tt = 16 * h + 4 * kq + i;
+        float v = s[h][i] * nk[tt];
+        if (edge && tok0 + tt >= lim) v = -INFINITY;
+        sc[4 * h + i] = v;
+      }
+    float mt = sc[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) mt = fmaxf(mt, sc[i]);
+    mt = fmaxf(mt, __shfl_xor(mt, 16));
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    if (__any(mt > m_run)) {
+      const float mn = fmaxf(m_run, mt);
+      const float al = __builtin_amdgcn_exp2f(m_run - mn); /* 0 on the first tile */
+      l_run *= al;
+#pragma unroll
+      for (int m = 0; m < D / 16; ++m) acc[m] *= al;
+      m_run = mn;
+    }
+    /* P' = p m_j as fp16 parts, in the value product's k order */
+    half8 ph, pl;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = __builtin_amdgcn_exp2f(sc[4 * h + i] - m_run);
+        l_run += p;
+        const float pm = p * nv[16 * h + 4 * kq + i];
+        const _Float16 hh = (_Float16)pm;
+        ph[4 * h + i] = hh;
+        pl[4 * h + i] = (_Float16)(pm - (float)hh);
+      }
+#pragma unroll
+    for (int m = 0; m < D / 16; ++m) {
+      const half8 av = *(const half8*)(vt + (16 * m + n) * PG::VP + 8 * kq);
+      acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, ph, acc[m], 0, 0, 0);
+      acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pl, acc[m], 0, 0, 0);
+    }
+    __syncthreads();
+  }
+
+  /* column sums over the four lane groups, then o'' = acc / l into LDS rows */
+  l_run += __shfl_xor(l_run, 16);
+  l_run += __shfl_xor(l_run, 32);
+  const float inv = a.oscale / l_run;
+  float* obuf = qbuf;
+#pragma unroll
+  for (int m = 0; m < D / 16; ++m)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) obuf[col * D + 16 * m + 4 * kq + i] = acc[m][i] * inv;
+  __syncthreads();
+  /* o = D H o'': one wave per row of its 16 columns */
+  for (int r = 0; r < 16; ++r) {
+    const int c = 16 * wave + r;
+    const int g = c / a.qc, qi = c % a.qc;
+    const Row<D> t = row_fwht<D>(obuf + c * D, lane);
+    if (g < a.group && qi < qn) {
+      const int64_t row = (((int64_t)layer * a.batch + b) * a.q_heads + (int64_t)kv * a.group + g) *
+                              a.t_new + q0 + qi;
+#pragma unroll
+      for (int j = 0; j < D / 64; ++j) {
+        const int i = lane + 64 * j;
+        const float v = t.v[j];
+        a.out[row * D + i] = ((sb[i >> 3] >> (i & 7)) & 1) ? -v : v;
+      }
+    }
+  }
+}
+
+template <int D, int BK, int BV>
+tq_status launch_prefill_t(const PreArgs& a, int64_t blocks, hipStream_t s) {
+  if (a.block_table)
+    hipLaunchKernelGGL((prefill_kernel<D, BK, BV, true>), dim3((unsigned)blocks), dim3(64 * kWaves), 0, s, a);
+  else
+    hipLaunchKernelGGL((prefill_kernel<D, BK, BV, false>), dim3((unsigned)blocks), dim3(64 * kWaves), 0, s, a);
+  return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_DEVICE;
+}
+
+}  // namespace
+
+tq_status tq_launch_prefill(const tq_kv_cache* c, const tq_codebook_s* cbk,
+                            const tq_codebook_s* cbv, const uint8_t* sign_bits,
+                            const uint16_t* q, int q_heads, int t_new, const int32_t* pos,
+                            int n_layers, float* out, hipStream_t s) {
+  PreArgs a;
+  a.k_codes = c->k_codes;
+  a.v_codes = c->v_codes;
+  a.k_norms = (const uint8_t*)c->k_norms;
+  a.v_norms = (const uint8_t*)c->v_norms;
+  a.ls_kc = c->layer_stride_k_codes;
+  a.ls_vc = c->layer_stride_v_codes;
+  a.ls_kn = c->layer_stride_k_norms;
+  a.ls_vn = c->layer_stride_v_norms;
+  a.batch = c->batch;
+  a.kv_heads = c->kv_heads;
+  a.capacity = c->capacity;
+  a.q_heads = q_heads;
+  a.group = q_heads / c->kv_heads;
+  int gp = 1;
+  while (gp < a.group) gp *= 2;
+  a.qc = kCols / gp;
+  a.t_new = t_new;
+  a.chunks = (t_new + a.qc - 1) / a.qc;
+  a.block_table = c->block_table;
+  a.lg_tpp = 0;
+  if (c->block_table)
+    while ((32 << a.lg_tpp) < c->page_tokens) ++a.lg_tpp;
+  a.max_pages = c->block_table ? c->max_pages : 0;
+  a.num_pages = c->block_table ? c->num_pages : 0;
+  a.sign_bits = sign_bits;
+  a.q = q;
+  a.pos = pos;
+  a.lut_k = cbk->dec_lut;
+  a.lut_k_lo = cbk->dec_lut_lo;
+  a.lut_v = cbv->dec_lut;
+  const double d = c->head_dim;
+  a.qscale = (float)(1.4426950408889634 / (d * cbk->sigma));
+  a.oscale = (float)(1.0 / (sqrt(d) * cbv->sigma));
+  a.out = out;
+  const int64_t blocks = (int64_t)n_layers * c->batch * c->kv_heads * a.chunks;
+  if (blocks == 0) return TQ_OK;
+#define TQ_PRE(DD, KK, VV) \
+  if (c->head_dim == DD && c->bits_k == KK && c->bits_v == VV) return launch_prefill_t<DD, KK, VV>(a, blocks, s);
+#define TQ_PRE_D(DD) \
+  TQ_PRE(DD, 2, 2) TQ_PRE(DD, 2, 3) TQ_PRE(DD, 2, 4) TQ_PRE(DD, 3, 2) TQ_PRE(DD, 3, 3) \
+  TQ_PRE(DD, 3, 4) TQ_PRE(DD, 4, 2) TQ_PRE(DD, 4, 3) TQ_PRE(DD, 4, 4)
+  TQ_PRE_D(64) TQ_PRE_D(128) TQ_PRE_D(256)
+#undef TQ_PRE_D
+#undef TQ_PRE
+  return TQ_ERR_UNSUPPORTED;
+}

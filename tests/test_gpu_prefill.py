@@ -1,0 +1,124 @@
+"""GPU parity of prefill (extend) attention over the compressed cache
+(tq_prefill_attn) against the oracle: every new query attends causally to its
+sequence's cached tokens, so query i of sequence b is the oracle's attention
+over the first pos[b] + i + 1 dequantized tokens.  Shapes span several query
+chunks and key tiles with ragged ends, every group size class (including a
+group that is not a power of two), all head dims, plain prefill (pos 0) and
+extension of an existing context, and paged storage."""
+import numpy as np
+import pytest
+
+import kv_cache_quantization_tq_amd as tq
+import oracle
+import synth
+from helpers import band_flip_bound, check_attention, prefix, require_gpu
+
+pytestmark = pytest.mark.gpu
+SEED = 1003
+
+
+def _case(torch, d, bk, bv, G, H, pos, t_new, Lyr=1, paged_tokens=None, seed=SEED):
+    B = len(pos)
+    T = max(pos) + t_new
+    cap = ((T + 31) // 32) * 32
+    if paged_tokens:
+        P = paged_tokens
+        cap = (cap + P - 1) // P * P
+        maxp = cap // P
+        rng = np.random.default_rng(seed)
+        table = rng.permutation(B * maxp).reshape(B, maxp).astype(np.int32)
+        cache = tq.PagedKVCache(Lyr, B, H, d, bk, bv, P, maxp, B * maxp, table)
+    else:
+        cache = tq.KVCache(Lyr, B, H, d, bk, bv, cap)
+    sbs = np.stack([synth.sign_bits(seed, l, d) for l in range(Lyr)])
+    sbd = torch.from_numpy(sbs).cuda()
+    cbk, cbv = tq.Codebook(d, bk), tq.Codebook(d, bv)
+    for l in range(Lyr):
+        k = torch.empty((1, B, H, T, d), dtype=torch.int16, device="cuda")
+        v = torch.empty_like(k)
+        synth.kv_dev(seed, 0, l, k[0])
+        synth.kv_dev(seed, 1, l, v[0])
+        tq.append(cache, cbk, cbv, sbd[l:l + 1], k, v,
+                  torch.zeros(B, dtype=torch.int32, device="cuda"), host_max_pos=0, layer0=l,
+                  n_layers=1)
+    q16 = np.empty((Lyr, B, G * H, t_new, d), dtype=np.uint16)
+    for l in range(Lyr):
+        for b in range(B):
+            for hq in range(G * H):
+                for i in range(t_new):
+                    q16[l, b, hq, i] = synth.q_host(seed, i, l, b, hq, d)
+    qd = torch.from_numpy(q16.view(np.int16)).cuda()
+    posd = torch.tensor(pos, dtype=torch.int32, device="cuda")
+    out = torch.empty((Lyr, B, G * H, t_new, d), dtype=torch.float32, device="cuda")
+    tq.prefill(cache, cbk, cbv, sbd, qd, posd, out)
+    torch.cuda.synchronize()
+    return dict(cache=cache, sbs=sbs, sbd=sbd, cbk=cbk, cbv=cbv, q16=q16, qd=qd, posd=posd,
+                out=out.cpu().numpy(), Lyr=Lyr, B=B, H=H, G=G, d=d, bk=bk, bv=bv, pos=pos,
+                t_new=t_new, seed=seed)
+
+
+def _oracle(c):
+    d, G, H, t_new = c["d"], c["G"], c["H"], c["t_new"]
+    ref = np.zeros(c["out"].shape)
+    bound = np.zeros_like(ref)
+    for l in range(c["Lyr"]):
+        for b, p in enumerate(c["pos"]):
+            for h in range(H):
+                n_all = p + t_new
+                k = synth.kv_host(c["seed"], 0, l, b, h, d, 0, n_all)
+                v = synth.kv_host(c["seed"], 1, l, b, h, d, 0, n_all)
+                sl = slice(h * G, (h + 1) * G)
+                st = oracle.decode_stream(k, v, c["q16"][l, b, sl, 0], c["bk"], c["bv"],
+                                          c["sbs"][l], full=True)
+                for i in range(t_new):
+                    n = p + i + 1
+                    q64 = oracle.halves_to_double(c["q16"][l, b, sl, i])
+                    o = oracle.attention(q64, st["K"][:n], st["V"][:n])
+                    sp = prefix(st, n)
+                    sp["out"] = o
+                    bd, _ = band_flip_bound(q64, k[:n], v[:n], sp, c["bk"], c["bv"], c["sbs"][l])
+                    ref[l, b, sl, i] = o
+                    bound[l, b, sl, i] = bd
+    return ref, bound
+
+
+@pytest.mark.parametrize("d,bk,bv,G,H,pos,t_new,Lyr", [
+    (128, 4, 2, 4, 2, [0, 300], 77, 2),
+    (64, 3, 3, 8, 1, [5], 40, 1),
+    (256, 2, 4, 1, 2, [1000], 130, 1),
+    (128, 4, 3, 3, 2, [33], 50, 1),
+    (128, 3, 2, 2, 1, [62, 0, 17], 33, 1),
+])
+def test_prefill_parity(d, bk, bv, G, H, pos, t_new, Lyr):
+    torch = require_gpu()
+    c = _case(torch, d, bk, bv, G, H, pos, t_new, Lyr)
+    ref, bound = _oracle(c)
+    check_attention(c["out"], ref, bound,
+                    f"prefill d={d} K{bk}/V{bv} G={G} pos={pos} t_new={t_new}")
+
+
+@pytest.mark.parametrize("P", [32, 128])
+def test_prefill_paged(P):
+    torch = require_gpu()
+    c = _case(torch, 128, 4, 2, 4, 2, [0, 300], 77, 2, paged_tokens=P)
+    ref, bound = _oracle(c)
+    check_attention(c["out"], ref, bound, f"prefill paged P={P}")
+
+
+def test_prefill_row_equals_decode():
+    """Query i of the prefill equals a decode step with that query and
+    length pos + i + 1 (both on the GPU, same cache)."""
+    torch = require_gpu()
+    c = _case(torch, 128, 4, 2, 4, 2, [200, 40], 70, 1)
+    for i in (0, 1, 31, 32, 69):
+        q = c["qd"][:, :, :, i].contiguous()
+        lens = c["posd"] + (i + 1)
+        out = torch.empty((1, c["B"], c["G"] * c["H"], c["d"]), dtype=torch.float32, device="cuda")
+        ws = tq.workspace(c["cache"], c["G"] * c["H"], max(c["pos"]) + i + 1)
+        tq.decode(c["cache"], c["cbk"], c["cbv"], c["sbd"], q, lens, max(c["pos"]) + i + 1, out,
+                  ws)
+        torch.cuda.synchronize()
+        got = c["out"][:, :, :, i]
+        want = out.cpu().numpy()
+        rel = np.linalg.norm(got - want) / np.linalg.norm(want)
+        assert rel < 1e-4 and np.abs(got - want).max() < 1e-3, (i, rel)
