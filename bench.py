@@ -417,6 +417,49 @@ def workload_sparse_v(args):
             args, best)
 
 
+def workload_prefill(args):
+    """Causal prefill attention over the compressed cache for the 32K workload
+    (32 layers, 32 query / 8 KV heads, d 128, K4/V2): the whole 32768-token
+    prompt is appended, then every prompt token attends to its prefix
+    (tq_prefill_attn, one call for all layers).  Matrix-core bound: reported
+    against the fp16 dense peak with the algorithmic flops of causal
+    attention, 4 d per (query, key) pair."""
+    import numpy as np
+    import torch
+    import kv_cache_quantization_tq_amd as tq
+    import synth
+    torch.cuda.set_device(0)
+    Tp = int(os.environ.get("TQ_PREFILL_TOKENS", T))
+    cache = tq.KVCache(L, B, HKV, D, BK, BV, Tp)
+    cbk, cbv = tq.Codebook(D, BK), tq.Codebook(D, BV)
+    sbs = torch.from_numpy(np.stack([synth.sign_bits(SEED, l, D) for l in range(L)])).cuda()
+    _fill_cache(torch, tq, synth, cache, cbk, cbv, sbs, SEED, L, B, HKV, Tp, D)
+    # queries: the decode query generator, one step per prompt position
+    q = torch.empty((L, B, HQ, Tp, D), dtype=torch.int16, device="cuda")
+    qs = torch.empty((B, HQ, D), dtype=torch.int16, device="cuda")
+    for l in range(L):
+        synth.q_dev(SEED, 0, l, qs)
+        q[l] = qs[:, :, None, :]
+    pos = torch.zeros(B, dtype=torch.int32, device="cuda")
+    out = torch.empty((L, B, HQ, Tp, D), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    ms = _timed(torch, lambda: tq.prefill(cache, cbk, cbv, sbs, q, pos, out), args.steps,
+                args.warmup)
+    pairs = Tp * (Tp + 1) // 2
+    flops = 4.0 * D * pairs * HQ * L * B
+    tfs = flops / (ms * 1e-3) / 1e12
+    _report({"workload": "llama3-8b-shaped 32K causal prefill attention over the packed cache",
+             "layers": L, "q_heads": HQ, "kv_heads": HKV, "head_dim": D, "batch": B,
+             "prompt": Tp, "bits_k": BK, "bits_v": BV},
+            "prefill-attn TFLOP/s (4 d flops per causal query-key pair)", tfs, "TFLOP/s", True,
+            {"dtype": "f32 (f16 matrix-core operands; packed 4-bit K, 2-bit V)",
+             "prefill_ms": ms, "tokens_per_s": Tp * B / (ms * 1e-3),
+             "roofline": {"bound": "mfma", "kernel": "prefill_kernel<128,4,2>", "achieved": tfs,
+                          "peak": 2500.0, "unit": "TFLOP/s", "frac": tfs / 2500.0,
+                          "traffic": None}},
+            args, ms)
+
+
 WORKLOADS = {
     "llama8b-32k": None,
     "tiny": workload_tiny,
@@ -425,6 +468,7 @@ WORKLOADS = {
     "70b-128k-b4": workload_70b_128k,
     "paged-llama8b-32k": workload_paged_llama8b,
     "sparse-v-llama8b-32k": workload_sparse_v,
+    "prefill-llama8b-32k": workload_prefill,
 }
 
 

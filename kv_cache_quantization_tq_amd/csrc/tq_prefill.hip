@@ -26,9 +26,11 @@
  *           the score output leaves them in the lanes, so P^T feeds the value
  *           product without moving: O^T[16 coords x 16 queries] +=
  *           V^T[16 x 32 tokens] P'^T, P' = p * m_j split into two fp16 parts.
- * A block is 8 waves x 16 (head, query) columns: 128 / Gp queries of each of
- * the G heads (Gp = G rounded up to a power of two).  The next tile's codes
- * are loaded into registers while the current one is multiplied.
+ * A block has 128 (head, query) columns: 128 / Gp queries of each of the G
+ * heads (Gp = G rounded up to a power of two), 32 per wave (16 with 256-dim
+ * heads), so that each operand read from LDS feeds two products.  Two LDS tile buffers:
+ * while tile t is multiplied, tile t + 1 is dequantized into the other one
+ * and tile t + 2's codes are loaded into registers (one barrier a tile).
  */
 #include <hip/hip_runtime.h>
 
@@ -41,8 +43,12 @@ typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = 8;
-constexpr int kCols = 16 * kWaves; /* (head, query) columns per block */
+constexpr int kCols = 128; /* (head, query) columns per block */
+
+/* 16-column groups per wave: two (each key and value operand read from LDS
+ * feeds two products) unless the registers of 256-dim heads forbid it */
+constexpr int groups_for(int d) { return d == 256 ? 1 : 2; }
+constexpr int waves_for(int d) { return kCols / (16 * groups_for(d)); }
 
 struct PreArgs {
   const uint8_t* k_codes;
@@ -64,6 +70,20 @@ struct PreArgs {
 };
 
 __device__ inline float h2f(uint32_t h) { return (float)__builtin_bit_cast(_Float16, (uint16_t)h); }
+
+/* max / sum over the four 16-lane rows (lanes n, n+16, n+32, n+48) */
+__device__ inline float rows_max(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ inline float rows_sum(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
 
 __device__ inline __amdgpu_buffer_rsrc_t make_stream(const uint8_t* base, int64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, 0x00020000);
@@ -124,11 +144,12 @@ struct PreGeo {
   static constexpr int VP = 32 + 8;             /* value tile pitch (halfs) */
   static constexpr int PWK = 1 << (2 * BK), PWV = 1 << (2 * BV); /* pair table words */
   static constexpr int ITEMS = 4 * D;           /* 8-code items per tile (keys; values too) */
-  static constexpr int PER = (ITEMS + 64 * kWaves - 1) / (64 * kWaves);
-  /* LDS: [query / output rows (fp32) | tiles] union, then tables */
+  static constexpr int NG = groups_for(D), WAVES = waves_for(D);
+  static constexpr int PER = (ITEMS + 64 * WAVES - 1) / (64 * WAVES);
+  /* LDS: [query / output rows (fp32) | two tile buffers] union, then tables */
   static constexpr int QBYTES = kCols * D * 4;
-  static constexpr int TBYTES = 2 * 32 * KP * 2 + D * VP * 2 + 2 * 32 * 4;
-  static constexpr int UBYTES = QBYTES > TBYTES ? QBYTES : TBYTES;
+  static constexpr int TBYTES = 2 * 32 * KP * 2 + D * VP * 2 + 2 * 32 * 4; /* one tile */
+  static constexpr int UBYTES = QBYTES > 2 * TBYTES ? QBYTES : 2 * TBYTES;
   static constexpr int BYTES = UBYTES + (2 * PWK + PWV) * 4;
 };
 
@@ -137,15 +158,18 @@ struct PreGeo {
 __device__ inline int kpos(int t) { return t < 16 ? 8 * (t >> 2) + (t & 3) : 8 * ((t - 16) >> 2) + 4 + (t & 3); }
 
 template <int D, int BK, int BV, bool PAGED>
-__global__ void __launch_bounds__(64 * kWaves) prefill_kernel(PreArgs a) {
+__global__ void __launch_bounds__(64 * waves_for(D)) prefill_kernel(PreArgs a) {
   using PG = PreGeo<D, BK, BV>;
+  constexpr int NG = PG::NG, KS = D / 32, VM = D / 16;
   __shared__ __align__(16) char smem[PG::BYTES];
   float* qbuf = (float*)smem;                            /* [kCols][D] */
-  _Float16* khi = (_Float16*)smem;                       /* [32][KP] */
-  _Float16* klo = khi + 32 * PG::KP;                     /* [32][KP] */
-  _Float16* vt = klo + 32 * PG::KP;                      /* [D][VP] */
-  float* nk = (float*)(vt + D * PG::VP);                 /* [32] */
-  float* nv = nk + 32;                                   /* [32] */
+  /* tile buffer u: khi [32][KP], klo [32][KP], vt [D][VP] (halfs), nk [32],
+   * nv [32] (floats) */
+  auto khi_of = [&](int u) { return (_Float16*)(smem + u * PG::TBYTES); };
+  auto klo_of = [&](int u) { return khi_of(u) + 32 * PG::KP; };
+  auto vt_of = [&](int u) { return khi_of(u) + 64 * PG::KP; };
+  auto nk_of = [&](int u) { return (float*)(vt_of(u) + D * PG::VP); };
+  auto nv_of = [&](int u) { return nk_of(u) + 32; };
   uint32_t* tk = (uint32_t*)(smem + PG::UBYTES);         /* key pairs, then remainders */
   uint32_t* tv = tk + 2 * PG::PWK;
 
@@ -185,37 +209,42 @@ __global__ void __launch_bounds__(64 * kWaves) prefill_kernel(PreArgs a) {
     qbuf[t] = v;
   }
   __syncthreads();
-  for (int r = 0; r < 16; ++r) {
-    float* row = qbuf + (16 * wave + r) * D;
+  /* wave w owns columns 16 NG w .. 16 NG w + 16 NG - 1 */
+  const int c0 = 16 * NG * wave;
+  for (int r = 0; r < 16 * NG; ++r) {
+    float* row = qbuf + (c0 + r) * D;
     const Row<D> t = row_fwht<D>(row, lane);
 #pragma unroll
     for (int j = 0; j < D / 64; ++j) row[lane + 64 * j] = t.v[j] * a.qscale;
   }
   __syncthreads();
-  /* B operands: lane (n, kq) holds coordinates 32 s + 8 kq + 0..7 of column
-   * 16 wave + n: fp16 part, fp16 remainder, fp16(q'' 2^-11) */
-  constexpr int KS = D / 32;
-  half8 qhi[KS], qlo[KS], qrm[KS];
-  {
-    const float* row = qbuf + (16 * wave + n) * D;
+  /* B operands: lane (n, kq) of group e holds coordinates 32 s + 8 kq + 0..7
+   * of column c0 + 16 e + n: fp16 part, fp16 remainder, fp16(q'' 2^-11) */
+  half8 qhi[NG][KS], qlo[NG][KS], qrm[NG][KS];
+#pragma unroll
+  for (int e = 0; e < NG; ++e) {
+    const float* row = qbuf + (c0 + 16 * e + n) * D;
 #pragma unroll
     for (int s = 0; s < KS; ++s)
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const float v = row[32 * s + 8 * kq + j];
         const _Float16 h = (_Float16)v;
-        qhi[s][j] = h;
-        qlo[s][j] = (_Float16)(v - (float)h);
-        qrm[s][j] = (_Float16)(v * 0x1p-11f);
+        qhi[e][s][j] = h;
+        qlo[e][s][j] = (_Float16)(v - (float)h);
+        qrm[e][s][j] = (_Float16)(v * 0x1p-11f);
       }
   }
-  /* this lane's column: its causal limit (tokens < lim are attended) */
-  const int col = 16 * wave + n;
-  const int cg = col / a.qc, ci = col % a.qc;
-  const bool live = cg < a.group && ci < qn;
-  int lim = p0 + q0 + ci + 1;
-  lim = lim > a.capacity ? a.capacity : lim;
-  lim = live ? lim : 1; /* padding columns attend token 0 only */
+  /* the lane's columns: causal limits (tokens < lim are attended) */
+  int lim[NG];
+#pragma unroll
+  for (int e = 0; e < NG; ++e) {
+    const int col = c0 + 16 * e + n;
+    const int cg = col / a.qc, ci = col % a.qc;
+    int l = p0 + q0 + ci + 1;
+    l = l > a.capacity ? a.capacity : l;
+    lim[e] = (cg < a.group && ci < qn) ? l : 1; /* padding columns attend token 0 only */
+  }
   int blk_lim = p0 + q0 + qn;
   blk_lim = blk_lim > a.capacity ? a.capacity : blk_lim;
   const int ntiles = (blk_lim + 31) / 32;
@@ -230,8 +259,7 @@ __global__ void __launch_bounds__(64 * kWaves) prefill_kernel(PreArgs a) {
       a.v_codes + layer * a.ls_vc + sh * (a.capacity / 32) * PG::TILE_V, srows / 32 * PG::TILE_V);
   const __amdgpu_buffer_rsrc_t rkn = make_stream(a.k_norms + layer * a.ls_kn + sh * a.capacity * 2, srows * 2);
   const __amdgpu_buffer_rsrc_t rvn = make_stream(a.v_norms + layer * a.ls_vn + sh * a.capacity * 2, srows * 2);
-  /* tile t's first key row, value tile and first norm, as stream offsets in
-   * units of rows / tiles */
+  /* tile t's first row in the streams (value tiles: that / 32) */
   auto tile_rows = [&](int t) -> int32_t {
     if constexpr (PAGED) {
       const int tpp = 1 << a.lg_tpp;
@@ -249,7 +277,7 @@ __global__ void __launch_bounds__(64 * kWaves) prefill_kernel(PreArgs a) {
     const int32_t r0 = tile_rows(t);
 #pragma unroll
     for (int u = 0; u < PG::PER; ++u) {
-      const int it = tid + u * 64 * kWaves;
+      const int it = tid + u * 64 * PG::WAVES;
       kraw[u] = 0;
       vraw[u] = 0;
       if (it < PG::ITEMS) {
@@ -264,17 +292,22 @@ __global__ void __launch_bounds__(64 * kWaves) prefill_kernel(PreArgs a) {
     else if (tid < 64)
       nraw = __builtin_amdgcn_raw_buffer_load_b16(rvn, (uint32_t)(r0 + tid - 32) * 2u, 0, 0);
   };
-  /* dequantize the fetched tile into LDS */
-  auto spill = [&]() {
+  /* dequantize the fetched tile into LDS buffer u */
+  auto spill = [&](int u) {
+    _Float16* khi = khi_of(u);
+    _Float16* klo = klo_of(u);
+    _Float16* vt = vt_of(u);
+    float* nk = nk_of(u);
+    float* nv = nv_of(u);
 #pragma unroll
-    for (int u = 0; u < PG::PER; ++u) {
-      const int it = tid + u * 64 * kWaves;
+    for (int w = 0; w < PG::PER; ++w) {
+      const int it = tid + w * 64 * PG::WAVES;
       if (it < PG::ITEMS) {
         const int tok = it / (D / 8), grp = it % (D / 8);
         u32x4 h, l;
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-          const uint32_t e = (kraw[u] >> (2 * BK * p)) & (PG::PWK - 1);
+          const uint32_t e = (kraw[w] >> (2 * BK * p)) & (PG::PWK - 1);
           h[p] = tk[e];
           l[p] = tk[PG::PWK + e];
         }
@@ -287,7 +320,7 @@ __global__ void __launch_bounds__(64 * kWaves) prefill_kernel(PreArgs a) {
         _Float16* vrow = vt + (rr * (D / 16) + m) * PG::VP;
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-          const uint32_t e = (vraw[u] >> (2 * BV * p)) & (PG::PWV - 1);
+          const uint32_t e = (vraw[w] >> (2 * BV * p)) & (PG::PWV - 1);
           *(uint32_t*)(vrow + kpos(8 * qq + 2 * p)) = tv[e];
         }
       }
@@ -296,93 +329,130 @@ __global__ void __launch_bounds__(64 * kWaves) prefill_kernel(PreArgs a) {
     else if (tid < 64) nv[tid - 32] = h2f(nraw);
   };
 
-  floatx4 acc[D / 16];
+  floatx4 acc[NG][VM];
 #pragma unroll
-  for (int m = 0; m < D / 16; ++m) acc[m] = floatx4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.0f;
+  for (int e = 0; e < NG; ++e)
+#pragma unroll
+    for (int m = 0; m < VM; ++m) acc[e][m] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float m_run[NG], l_run[NG];
+#pragma unroll
+  for (int e = 0; e < NG; ++e) {
+    m_run[e] = -INFINITY;
+    l_run[e] = 0.0f;
+  }
 
-  if (ntiles > 0) fetch(0);
+  /* tile t is multiplied from buffer t % 2 while tile t + 1 is dequantized
+   * into the other one and tile t + 2's codes are loaded: one barrier a tile */
+  fetch(0);
+  spill(0);
+  if (ntiles > 1) fetch(1);
+  __syncthreads();
   for (int t = 0; t < ntiles; ++t) {
-    spill();
-    __syncthreads();
-    if (t + 1 < ntiles) fetch(t + 1);
-    /* scores of the two 16-token halves */
-    floatx4 s[2];
+    const int u = t & 1;
+    const _Float16* khi = khi_of(u);
+    const _Float16* klo = klo_of(u);
+    const _Float16* vt = vt_of(u);
+    const float* nk = nk_of(u);
+    const float* nv = nv_of(u);
+    if (t + 1 < ntiles) {
+      spill(u ^ 1);
+      if (t + 2 < ntiles) fetch(t + 2);
+    }
+    /* scores of the two 16-token halves, every key operand read once for the
+     * NG column groups */
+    floatx4 s[NG][2];
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      s[h] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int e = 0; e < NG; ++e) s[e][h] = floatx4{0.f, 0.f, 0.f, 0.f};
       const _Float16* kr = khi + (16 * h + n) * PG::KP + 8 * kq;
       const _Float16* kl = klo + (16 * h + n) * PG::KP + 8 * kq;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const half8 ah = *(const half8*)(kr + 32 * ks);
         const half8 al = *(const half8*)(kl + 32 * ks);
-        s[h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, qhi[ks], s[h], 0, 0, 0);
-        s[h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, qlo[ks], s[h], 0, 0, 0);
-        s[h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, qrm[ks], s[h], 0, 0, 0);
+#pragma unroll
+        for (int e = 0; e < NG; ++e) {
+          s[e][h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, qhi[e][ks], s[e][h], 0, 0, 0);
+          s[e][h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, qlo[e][ks], s[e][h], 0, 0, 0);
+          s[e][h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, qrm[e][ks], s[e][h], 0, 0, 0);
+        }
       }
     }
-    /* lane (n, kq) holds tokens 16 h + 4 kq + i of column n */
-    float sc[8];
+    /* lane (n, kq) holds tokens 16 h + 4 kq + i of its columns */
+    float nkv[8], nvv[8];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        nkv[4 * h + i] = nk[16 * h + 4 * kq + i];
+        nvv[4 * h + i] = nv[16 * h + 4 * kq + i];
+      }
     const int tok0 = 32 * t;
     const bool edge = tok0 + 32 > p0 + q0 + 1; /* some column may stop inside */
+    half8 ph[NG], pl[NG];
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int e = 0; e < NG; ++e) {
+      float sc[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int tt = 16 * h + 4 * kq + i;
-        float v = s[h][i] * nk[tt];
-        if (edge && tok0 + tt >= lim) v = -INFINITY;
-        sc[4 * h + i] = v;
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int tt = 16 * h + 4 * kq + i;
+          float v = s[e][h][i] * nkv[4 * h + i];
+          if (edge && tok0 + tt >= lim[e]) v = -INFINITY;
+          sc[4 * h + i] = v;
+        }
+      float mt = sc[0];
+#pragma unroll
+      for (int i = 1; i < 8; ++i) mt = fmaxf(mt, sc[i]);
+      mt = rows_max(mt);
+      if (__any(mt > m_run[e])) {
+        const float mn = fmaxf(m_run[e], mt);
+        const float al = __builtin_amdgcn_exp2f(m_run[e] - mn); /* 0 on the first tile */
+        l_run[e] *= al;
+#pragma unroll
+        for (int m = 0; m < VM; ++m) acc[e][m] *= al;
+        m_run[e] = mn;
       }
-    float mt = sc[0];
+      /* P' = p m_j as fp16 parts, in the value product's k order */
 #pragma unroll
-    for (int i = 1; i < 8; ++i) mt = fmaxf(mt, sc[i]);
-    mt = fmaxf(mt, __shfl_xor(mt, 16));
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    if (__any(mt > m_run)) {
-      const float mn = fmaxf(m_run, mt);
-      const float al = __builtin_amdgcn_exp2f(m_run - mn); /* 0 on the first tile */
-      l_run *= al;
-#pragma unroll
-      for (int m = 0; m < D / 16; ++m) acc[m] *= al;
-      m_run = mn;
-    }
-    /* P' = p m_j as fp16 parts, in the value product's k order */
-    half8 ph, pl;
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float p = __builtin_amdgcn_exp2f(sc[4 * h + i] - m_run);
-        l_run += p;
-        const float pm = p * nv[16 * h + 4 * kq + i];
+      for (int j = 0; j < 8; ++j) {
+        const float p = __builtin_amdgcn_exp2f(sc[j] - m_run[e]);
+        l_run[e] += p;
+        const float pm = p * nvv[j];
         const _Float16 hh = (_Float16)pm;
-        ph[4 * h + i] = hh;
-        pl[4 * h + i] = (_Float16)(pm - (float)hh);
+        ph[e][j] = hh;
+        pl[e][j] = (_Float16)(pm - (float)hh);
       }
+    }
 #pragma unroll
-    for (int m = 0; m < D / 16; ++m) {
+    for (int m = 0; m < VM; ++m) {
       const half8 av = *(const half8*)(vt + (16 * m + n) * PG::VP + 8 * kq);
-      acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, ph, acc[m], 0, 0, 0);
-      acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pl, acc[m], 0, 0, 0);
+#pragma unroll
+      for (int e = 0; e < NG; ++e) {
+        acc[e][m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, ph[e], acc[e][m], 0, 0, 0);
+        acc[e][m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, pl[e], acc[e][m], 0, 0, 0);
+      }
     }
     __syncthreads();
   }
 
   /* column sums over the four lane groups, then o'' = acc / l into LDS rows */
-  l_run += __shfl_xor(l_run, 16);
-  l_run += __shfl_xor(l_run, 32);
-  const float inv = a.oscale / l_run;
   float* obuf = qbuf;
 #pragma unroll
-  for (int m = 0; m < D / 16; ++m)
+  for (int e = 0; e < NG; ++e) {
+    const float inv = a.oscale / rows_sum(l_run[e]);
+    const int col = c0 + 16 * e + n;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) obuf[col * D + 16 * m + 4 * kq + i] = acc[m][i] * inv;
+    for (int m = 0; m < VM; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) obuf[col * D + 16 * m + 4 * kq + i] = acc[e][m][i] * inv;
+  }
   __syncthreads();
-  /* o = D H o'': one wave per row of its 16 columns */
-  for (int r = 0; r < 16; ++r) {
-    const int c = 16 * wave + r;
+  /* o = D H o'': one wave per row of its columns */
+  for (int r = 0; r < 16 * NG; ++r) {
+    const int c = c0 + r;
     const int g = c / a.qc, qi = c % a.qc;
     const Row<D> t = row_fwht<D>(obuf + c * D, lane);
     if (g < a.group && qi < qn) {
@@ -401,9 +471,9 @@ __global__ void __launch_bounds__(64 * kWaves) prefill_kernel(PreArgs a) {
 template <int D, int BK, int BV>
 tq_status launch_prefill_t(const PreArgs& a, int64_t blocks, hipStream_t s) {
   if (a.block_table)
-    hipLaunchKernelGGL((prefill_kernel<D, BK, BV, true>), dim3((unsigned)blocks), dim3(64 * kWaves), 0, s, a);
+    hipLaunchKernelGGL((prefill_kernel<D, BK, BV, true>), dim3((unsigned)blocks), dim3(64 * waves_for(D)), 0, s, a);
   else
-    hipLaunchKernelGGL((prefill_kernel<D, BK, BV, false>), dim3((unsigned)blocks), dim3(64 * kWaves), 0, s, a);
+    hipLaunchKernelGGL((prefill_kernel<D, BK, BV, false>), dim3((unsigned)blocks), dim3(64 * waves_for(D)), 0, s, a);
   return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_DEVICE;
 }
 
