@@ -45,6 +45,10 @@ def _L():
         lib.orc_dequant.argtypes = [vp, vp, i64, i32, vp, vp, vp]
         lib.orc_attention.argtypes = [vp, i32, vp, vp, i64, i32, vp]
         lib.orc_attention_sparse.argtypes = [vp, i32, vp, vp, i64, i32, dbl, vp, vp, vp]
+        lib.orc_qjl_project.argtypes = [vp, i32, vp, i32, vp, vp, vp]
+        lib.orc_qjl_encode.argtypes = [vp, i64, i32, i32, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp]
+        lib.orc_qjl_estimate.argtypes = [vp, i32, vp, vp, vp, dbl, dbl, vp, vp, i32]
+        lib.orc_qjl_estimate.restype = dbl
         _lib = lib
     return _lib
 
@@ -204,6 +208,58 @@ def attention_sparse(q, K, V, eps, want_weights=False):
     if want_weights:
         return out, bound, w[:, :T]
     return out, bound
+
+
+def qjl_project(r, S):
+    """Signs of S r as m bits (uint8 [m/8], LSB first), gamma = ||r||, and S r
+    (tq_oracle.c, orc_qjl_project)."""
+    rb = _c(r, np.float64)
+    Sb = _c(S, np.float64)
+    m, d = Sb.shape
+    bits = np.zeros((m + 7) // 8, dtype=np.uint8)
+    gamma = np.zeros(1)
+    proj = np.zeros(m)
+    _L().orc_qjl_project(_p(rb), d, _p(Sb), m, _p(bits), _p(gamma), _p(proj))
+    return bits, float(gamma[0]), proj
+
+
+def qjl_encode(x, bits, sign_bits, S):
+    """Stage 1 and the QJL sketch of fp16 vectors x[n][d] with the m x d
+    matrix S: (codes [n][d], norms uint16 [n], signs uint8 [n][m/8],
+    gamma float64 [n], projections float64 [n][m])."""
+    xb = _c(x, np.uint16)
+    n, d = xb.shape
+    Sb = _c(S, np.float64)
+    m = Sb.shape[0]
+    R = rotation(d, sign_bits)
+    c, t = codebook(d, bits)
+    codes = np.zeros((n, d), dtype=np.uint8)
+    norms = np.zeros(n, dtype=np.uint16)
+    signs = np.zeros((n, (m + 7) // 8), dtype=np.uint8)
+    gamma = np.zeros(n)
+    proj = np.zeros((n, m))
+    _L().orc_qjl_encode(_p(xb), n, d, bits, _p(R), _p(_c(c, np.float64)), _p(_c(t, np.float64)),
+                        _p(Sb), m, _p(codes), _p(norms), _p(signs), _p(gamma), _p(proj))
+    return codes, norms, signs, gamma, proj
+
+
+def qjl_estimate(q, codes, n16, gamma16, signs, S, R, c):
+    """Estimates of <q, x_j> for one query q[d] (float64) over encoded keys:
+    codes [T][d], n16 / gamma16 float64 [T] (the stored fp16 values), signs
+    [T][m/8]; R the rotation, c the levels (tq_oracle.c, orc_qjl_estimate)."""
+    qb = _c(q, np.float64)
+    d = qb.shape[0]
+    Sb = _c(S, np.float64)
+    m = Sb.shape[0]
+    Rb = _c(R, np.float64)
+    cb = _c(c, np.float64)
+    cd = _c(codes, np.uint8)
+    sg = _c(signs, np.uint8)
+    out = np.zeros(cd.shape[0])
+    for j in range(cd.shape[0]):
+        out[j] = _L().orc_qjl_estimate(_p(qb), d, _p(Rb), _p(cb), _p(cd[j]), float(n16[j]),
+                                       float(gamma16[j]), _p(sg[j]), _p(Sb), m)
+    return out
 
 
 def halves_to_double(x):

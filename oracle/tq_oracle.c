@@ -388,3 +388,84 @@ void orc_attention_sparse(const double* q, int G, const double* K, const double*
   }
   free(s);
 }
+
+/* ------------------------------------------------------------------ QJL -- */
+
+/* Stage 2 of the method ("We Built a Python Library That Cuts LLM Memory
+ * Usage by 80%", "Why not both stages?": a 1-bit residual correction for
+ * unbiased inner products, which that library skips).  The page gives no
+ * more; the reading here is the quantized Johnson-Lindenstrauss sketch of the
+ * stage-1 residual of a key, in the rotated unit domain:
+ *   r = R x / ||x|| - c[codes],   gamma = ||r||,
+ *   z_i = sign((S r)_i), i < m    (bit i set iff (S r)_i >= 0),
+ * S an m x d matrix of i.i.d. N(0,1) draws given by the caller, and an inner
+ * product with a query q estimated as
+ *   <q, x> ~= n16 * ( <R q, c[codes]> + sqrt(pi/2) / m * gamma * <S R q, z> ),
+ * whose second term is unbiased for n16 <R q, r> over the draw of S, because
+ * E[sign(s.r) (s.u)] = sqrt(2/pi) <u, r> / ||r|| for s ~ N(0, I). */
+
+/* Signs of S r (m x d, row-major) as m bits LSB-first, and gamma = ||r||;
+ * proj (optional, m values) receives S r. */
+void orc_qjl_project(const double* r, int d, const double* S, int m, uint8_t* bits,
+                     double* gamma, double* proj) {
+  double g = 0.0;
+  for (int j = 0; j < d; ++j) g += r[j] * r[j];
+  *gamma = sqrt(g);
+  memset(bits, 0, (size_t)(m + 7) / 8);
+  for (int i = 0; i < m; ++i) {
+    double t = 0.0;
+    for (int j = 0; j < d; ++j) t += S[i * d + j] * r[j];
+    if (proj) proj[i] = t;
+    if (t >= 0.0) bits[i / 8] |= (uint8_t)(1u << (i % 8));
+  }
+}
+
+/* Stage 1 and 2 of n fp16 vectors x[n][d]: codes (unpacked, as orc_encode),
+ * norms, the sign bits [n][m/8], gamma [n] and the projections [n][m]. */
+void orc_qjl_encode(const uint16_t* x, int64_t n, int d, int bits, const double* R,
+                    const double* c, const double* t, const double* S, int m, uint8_t* codes,
+                    uint16_t* norms, uint8_t* signs, double* gamma, double* proj) {
+  orc_encode(x, n, d, bits, R, c, t, codes, norms, NULL);
+  double* xv = (double*)malloc(sizeof(double) * d);
+  double* r = (double*)malloc(sizeof(double) * d);
+  for (int64_t v = 0; v < n; ++v) {
+    double nrm;
+    orc_norm16(x + v * d, d, &nrm);
+    for (int j = 0; j < d; ++j) xv[j] = orc_half_to_double(x[v * d + j]);
+    for (int i = 0; i < d; ++i) {
+      double y = 0.0;
+      if (nrm > 0.0) {
+        for (int j = 0; j < d; ++j) y += R[i * d + j] * xv[j];
+        y /= nrm;
+      }
+      r[i] = y - c[codes[v * d + i]];
+    }
+    orc_qjl_project(r, d, S, m, signs + v * ((m + 7) / 8), gamma + v, proj ? proj + v * m : NULL);
+  }
+  free(xv);
+  free(r);
+}
+
+/* The estimate of <q, x> for one query q[d] (original domain) and one encoded
+ * key: codes[d] (unpacked), its fp16 norm n16 and fp16 gamma16 (as values),
+ * its m sign bits; R, c, S as above. */
+double orc_qjl_estimate(const double* q, int d, const double* R, const double* c,
+                        const uint8_t* codes, double n16, double gamma16, const uint8_t* signs,
+                        const double* S, int m) {
+  double* rq = (double*)malloc(sizeof(double) * d);
+  for (int i = 0; i < d; ++i) {
+    double a = 0.0;
+    for (int j = 0; j < d; ++j) a += R[i * d + j] * q[j];
+    rq[i] = a;
+  }
+  double mse = 0.0;
+  for (int i = 0; i < d; ++i) mse += rq[i] * c[codes[i]];
+  double corr = 0.0;
+  for (int k = 0; k < m; ++k) {
+    double sq = 0.0;
+    for (int j = 0; j < d; ++j) sq += S[k * d + j] * rq[j];
+    corr += ((signs[k / 8] >> (k % 8)) & 1) ? sq : -sq;
+  }
+  free(rq);
+  return n16 * (mse + sqrt(acos(-1.0) / 2.0) / m * gamma16 * corr);
+}

@@ -471,6 +471,71 @@ def test_sparse_v_special_cases():
     assert not o.any() and not b.any()
 
 
+def test_qjl_hand_examples():
+    """d = m = 2: S r = (-1, 4) gives bits (0, 1) and gamma = sqrt 5; with
+    R = I, levels (-1/2, 1/2), codes (0, 1), n16 = 2 and q = (3, 1) the
+    estimate is 2 (-1 + sqrt(pi/2) / 2 * sqrt 5 * <S q, z>), <S q, z> = -4 + 5."""
+    S = np.array([[1.0, 1.0], [2.0, -1.0]])
+    bits, gamma, proj = oracle.qjl_project(np.array([1.0, -2.0]), S)
+    assert bits.tolist() == [2] and abs(gamma - math.sqrt(5)) < 1e-15
+    assert proj.tolist() == [-1.0, 4.0]
+    # a zero projection counts as non-negative
+    bits0, _, _ = oracle.qjl_project(np.array([1.0, -1.0]), np.array([[1.0, 1.0], [0.0, 1.0]]))
+    assert bits0.tolist() == [1]
+    est = oracle.qjl_estimate(np.array([3.0, 1.0]), np.array([[0, 1]]), np.array([2.0]),
+                              np.array([math.sqrt(5)]), np.array([[2]]), S, np.eye(2),
+                              np.array([-0.5, 0.5]))
+    want = 2 * (-1 + math.sqrt(math.pi / 2) / 2 * math.sqrt(5) * 1.0)
+    assert abs(est[0] - want) < 1e-14
+
+
+def test_qjl_term_unbiased():
+    """Over draws of S (i.i.d. N(0,1), m = d = 64) the QJL term
+    sqrt(pi/2)/m gamma <S u, z> averages to <u, r>; a wrong constant or sign
+    convention moves the mean by many standard errors."""
+    rng = np.random.default_rng(21)
+    d = 64
+    r = rng.standard_normal(d) * 0.05
+    u = r / np.linalg.norm(r) * 10 + rng.standard_normal(d)
+    est = []
+    for _ in range(3000):
+        S = rng.standard_normal((d, d))
+        bits, gamma, _ = oracle.qjl_project(r, S)
+        z = np.where((bits[np.arange(d) // 8] >> (np.arange(d) % 8)) & 1, 1.0, -1.0)
+        est.append(math.sqrt(math.pi / 2) / d * gamma * float((S @ u) @ z))
+    est = np.array(est)
+    se = est.std() / math.sqrt(len(est))
+    assert abs(est.mean() - u @ r) < 5 * se, (est.mean(), u @ r, se)
+    assert abs(u @ r) > 20 * se  # the test can see a constant off by a few percent
+
+
+def test_qjl_estimate_unbiased_on_encoded_keys():
+    """The whole estimate (stage 1 plus the QJL term) of <q, x> for encoded
+    fp16 keys averages, over draws of S, to <q, x> n16 / ||x|| (the stored
+    norm against the exact one), while stage 1 alone stays biased."""
+    rng = np.random.default_rng(22)
+    d = 64
+    sb = _rand_signs(rng, d)
+    x = (rng.standard_normal((3, d)) * 2).astype(np.float16).view(np.uint16)
+    xf = x.view(np.float16).astype(np.float64)
+    q = xf[0] * 0.7 + rng.standard_normal(d)
+    R = oracle.rotation(d, sb)
+    c, _ = oracle.codebook(d, 2)
+    draws = []
+    for _ in range(400):
+        S = rng.standard_normal((d, d))
+        codes, norms, signs, gamma, _ = oracle.qjl_encode(x, 2, sb, S)
+        n16 = oracle.halves_to_double(norms)
+        g16 = np.float16(gamma).astype(np.float64)
+        draws.append(oracle.qjl_estimate(q, codes, n16, g16, signs, S, R, c))
+    draws = np.array(draws)
+    exact = xf @ q * n16 / np.linalg.norm(xf, axis=1)
+    mean, se = draws.mean(0), draws.std(0) / math.sqrt(len(draws))
+    assert np.all(np.abs(mean - exact) < 5 * se + 1e-3 * np.abs(exact)), (mean, exact, se)
+    stage1 = n16 * ((R @ q) @ c[codes].T)
+    assert np.abs(stage1 - exact).max() > 10 * se.max()
+
+
 def test_rotated_domain_evaluation_matches_plain():
     """Attention evaluated in the rotated domain (scores (Rq).c, values summed
     as levels, one R^T at the end) equals the oracle's plain evaluation over
