@@ -223,6 +223,35 @@ tq_status tq_prefill_attn(const tq_kv_cache* c, tq_codebook cbk, tq_codebook cbv
                           const uint8_t* sign_bits, const uint16_t* q, int q_heads, int t_new,
                           const int32_t* pos, int n_layers, float* out, void* stream);
 
+/* ------------------------------------------------------------------ QJL -- */
+
+/* The method's second stage, the 1-bit residual sketch of keys ("We Built
+ * ...", "Why not both stages?": a 1-bit residual correction for unbiased
+ * inner products; that page skips it in attention).  For each key x with
+ * stage-1 codes (from tq_encode, row layout) the residual in the rotated unit
+ * domain is r = R x / ||x|| - c[codes]; the sketch is gamma = fp16(||r||)
+ * and d sign bits of S r, bit i set iff (S r)_i >= 0 (LSB first, d/8 bytes).
+ * x, x_stride, sign_bits: as tq_encode (x 16-byte aligned, stride % 8 == 0).
+ * S:     device fp16 [d][d] row-major, 16-byte aligned: the caller's draw of
+ *        i.i.d. N(0,1) entries (fixed per layer, like the sign bits).
+ * codes: device, the keys' tq_encode rows [n][d*bits/8].
+ * signs: device [n][d/8], 4-byte aligned.  gamma: device fp16 [n].
+ * The codebook gives d and bits.  n == 0 is a no-op. */
+tq_status tq_qjl_encode(tq_codebook cb, const uint16_t* x, int64_t n, int64_t x_stride,
+                        const uint8_t* sign_bits, const uint16_t* S, const uint8_t* codes,
+                        uint8_t* signs, uint16_t* gamma, void* stream);
+
+/* Estimates of <q_g, x_t> for n_q (1..8) queries q (device fp16 [n_q][d],
+ * original domain) over n_keys sketched keys:
+ *   n16_t * ( <R q, c[codes_t]> + sqrt(pi/2) / d * gamma_t * <S R q, z_t> ),
+ * z_t = +-1 from the sign bits; unbiased for <q, x_t> n16_t / ||x_t|| over
+ * the draw of S.  codes [n_keys][d*bits/8], norms fp16 [n_keys] (tq_encode),
+ * signs, gamma as tq_qjl_encode; out: device fp32 [n_q][n_keys]. */
+tq_status tq_qjl_scores(tq_codebook cb, const uint16_t* q, int n_q, const uint8_t* sign_bits,
+                        const uint16_t* S, const uint8_t* codes, const uint16_t* norms,
+                        const uint8_t* signs, const uint16_t* gamma, int64_t n_keys, float* out,
+                        void* stream);
+
 /* tq_decode_attn with the Sparse V gate ("TurboQuant+: Compresion de Cache KV
  * 6.4x para LLMs", section "Sparse V": the value work of positions with
  * negligible attention weight is skipped; the page gives no threshold).

@@ -19,7 +19,7 @@ EXPORTS = (
     "tq_status_str", "tq_codebook_compute", "tq_codebook_init", "tq_codebook_read",
     "tq_codebook_head_dim", "tq_codebook_bits", "tq_codebook_free", "tq_encode",
     "tq_cache_layer_bytes", "tq_append", "tq_decode_workspace_bytes", "tq_decode_attn",
-    "tq_decode_attn_sparse", "tq_prefill_attn",
+    "tq_decode_attn_sparse", "tq_prefill_attn", "tq_qjl_encode", "tq_qjl_scores",
 )
 
 
@@ -75,9 +75,11 @@ def lib():
         L.tq_decode_attn_sparse.argtypes = [P(KVCacheStruct), vp, vp, vp, vp, i32, vp, i32, i32,
                                             ctypes.c_float, vp, vp, vp, sz, vp]
         L.tq_prefill_attn.argtypes = [P(KVCacheStruct), vp, vp, vp, vp, i32, i32, vp, i32, vp, vp]
+        L.tq_qjl_encode.argtypes = [vp, vp, i64, i64, vp, vp, vp, vp, vp, vp]
+        L.tq_qjl_scores.argtypes = [vp, vp, i32, vp, vp, vp, vp, vp, vp, i64, vp, vp]
         for f in ("tq_codebook_compute", "tq_codebook_init", "tq_codebook_read", "tq_encode",
                   "tq_cache_layer_bytes", "tq_append", "tq_decode_attn", "tq_decode_attn_sparse",
-                  "tq_prefill_attn"):
+                  "tq_prefill_attn", "tq_qjl_encode", "tq_qjl_scores"):
             getattr(L, f).restype = i32
         _lib = L
     return _lib
@@ -300,6 +302,21 @@ def prefill(cache, cbk, cbv, sign_bits, q, pos, out, layer0=0, n_layers=None, st
     _check("tq_prefill_attn", lib().tq_prefill_attn(
         ctypes.byref(s), cbk.handle, cbv.handle, _ptr(sign_bits), _ptr(q), q_heads, t_new,
         _ptr(pos), n_layers, _ptr(out), _stream(stream)))
+
+
+def qjl_encode(cb, x, sign_bits, S, codes, signs, gamma, stream=None):
+    """tq_qjl_encode: x fp16 [n][>= d] (CUDA), S fp16 [d][d], codes [n][d*bits/8]
+    (tq_encode rows); writes signs uint8 [n][d/8] and gamma fp16 [n]."""
+    _check("tq_qjl_encode", lib().tq_qjl_encode(
+        cb.handle, _ptr(x), x.shape[0], x.stride(0), _ptr(sign_bits), _ptr(S), _ptr(codes),
+        _ptr(signs), _ptr(gamma), _stream(stream)))
+
+
+def qjl_scores(cb, q, sign_bits, S, codes, norms, signs, gamma, out, stream=None):
+    """tq_qjl_scores: q fp16 [n_q][d]; out fp32 [n_q][n_keys]."""
+    _check("tq_qjl_scores", lib().tq_qjl_scores(
+        cb.handle, _ptr(q), q.shape[0], _ptr(sign_bits), _ptr(S), _ptr(codes), _ptr(norms),
+        _ptr(signs), _ptr(gamma), codes.shape[0], _ptr(out), _stream(stream)))
 
 
 def workspace(cache, q_heads, max_len, n_layers=None, layer0=0, device="cuda"):

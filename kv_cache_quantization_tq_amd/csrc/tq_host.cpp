@@ -422,6 +422,37 @@ extern "C" tq_status tq_prefill_attn(const tq_kv_cache* c, tq_codebook cbk, tq_c
                            (hipStream_t)stream);
 }
 
+extern "C" tq_status tq_qjl_encode(tq_codebook cb, const uint16_t* x, int64_t n,
+                                   int64_t x_stride, const uint8_t* sign_bits, const uint16_t* S,
+                                   const uint8_t* codes, uint8_t* signs, uint16_t* gamma,
+                                   void* stream) {
+  if (!cb || n < 0) return TQ_ERR_ARG;
+  if (n == 0) return TQ_OK;
+  const int d = cb->d;
+  if (!x || !sign_bits || !S || !codes || !signs || !gamma) return TQ_ERR_ARG;
+  if (x_stride < d || x_stride % 8 != 0 || !aligned(x, 16) || !aligned(S, 16) ||
+      !aligned(signs, 4) || !aligned(gamma, 2))
+    return TQ_ERR_ARG;
+  return tq_launch_qjl_encode(cb, x, n, x_stride, sign_bits, S, codes, signs, gamma,
+                              (hipStream_t)stream);
+}
+
+extern "C" tq_status tq_qjl_scores(tq_codebook cb, const uint16_t* q, int n_q,
+                                   const uint8_t* sign_bits, const uint16_t* S,
+                                   const uint8_t* codes, const uint16_t* norms,
+                                   const uint8_t* signs, const uint16_t* gamma, int64_t n_keys,
+                                   float* out, void* stream) {
+  if (!cb || n_keys < 0) return TQ_ERR_ARG;
+  if (n_q < 1 || n_q > 8) return TQ_ERR_UNSUPPORTED;
+  if (n_keys == 0) return TQ_OK;
+  if (!q || !sign_bits || !S || !codes || !norms || !signs || !gamma || !out) return TQ_ERR_ARG;
+  if (!aligned(q, 2) || !aligned(norms, 2) || !aligned(gamma, 2) || !aligned(out, 4) ||
+      !aligned(S, 2))
+    return TQ_ERR_ARG;
+  return tq_launch_qjl_scores(cb, q, n_q, sign_bits, S, codes, norms, signs, gamma, n_keys, out,
+                              (hipStream_t)stream);
+}
+
 extern "C" tq_status tq_decode_attn_sparse(const tq_kv_cache* c, tq_codebook cbk,
                                            tq_codebook cbv, const uint8_t* sign_bits,
                                            const uint16_t* q, int q_heads,

@@ -70,6 +70,15 @@ tq_status tq_launch_prefill(const tq_kv_cache* c, const tq_codebook_s* cbk,
                             const uint16_t* q, int q_heads, int t_new, const int32_t* pos,
                             int n_layers, float* out, hipStream_t stream);
 
+tq_status tq_launch_qjl_encode(const tq_codebook_s* cb, const uint16_t* x, int64_t n,
+                               int64_t stride, const uint8_t* sign_bits, const uint16_t* S,
+                               const uint8_t* codes, uint8_t* signs, uint16_t* gamma,
+                               hipStream_t stream);
+tq_status tq_launch_qjl_scores(const tq_codebook_s* cb, const uint16_t* q, int G,
+                               const uint8_t* sign_bits, const uint16_t* S, const uint8_t* codes,
+                               const uint16_t* norms, const uint8_t* signs,
+                               const uint16_t* gamma, int64_t T, float* out, hipStream_t stream);
+
 /* Split count and workspace layout of one decode call. */
 struct tq_decode_plan {
   int splits;          /* token splits per (layer, seq, kv head) */

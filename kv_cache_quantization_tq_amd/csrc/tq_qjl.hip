@@ -1,0 +1,290 @@
+/*
+ * gfx950 kernels of the QJL stage: the 1-bit residual sketch of keys and the
+ * inner-product estimate that uses it ("We Built a Python Library That Cuts
+ * LLM Memory Usage by 80%", "Why not both stages?": the method's second
+ * stage adds a 1-bit residual correction for unbiased inner products).
+ *
+ * For a key x with stage-1 codes (tq_encode) the residual in the rotated unit
+ * domain is r = R x / ||x|| - c[codes]; its sketch is gamma = fp16(||r||) and
+ * the signs of S r (m = d rows of the caller's fp16 matrix S, bit set iff the
+ * projection is >= 0).  The estimate of <q, x> is
+ *   n16 * ( <R q, c[codes]> + sqrt(pi/2) / d * gamma * <S R q, z> ).
+ *
+ * qjl_encode_kernel: a wave sketches 16 keys.  Lane (n, kq) holds
+ * coordinates 32 s + 8 kq + 0..7 of key n, so the residual it computes is
+ * exactly its slice of the B operand of S R^T on the matrix cores
+ * (v_mfma_f32_16x16x32_f16, r split into two fp16 parts; S is exact in fp16).
+ * The rotation is the butterfly Walsh-Hadamard transform: in-lane strides
+ * 1, 2, 4 and >= 32, lane-xor 16 and 32 for strides 8 and 16.
+ * qjl_scores_kernel: one thread per key, the group's rotated queries and
+ * their projections in LDS (plain VALU: 2 G multiply-adds per coordinate).
+ */
+#include <hip/hip_runtime.h>
+
+#include "tq_internal.h"
+
+namespace {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+constexpr float kSqrtHalfPi = 1.2533141373155003f; /* sqrt(pi / 2) */
+
+struct QjlEncArgs {
+  const uint16_t* x;
+  int64_t n, stride;
+  const uint8_t* sign_bits;
+  const uint16_t* S; /* fp16 [d][d] */
+  const uint8_t* codes;
+  uint8_t* signs;
+  uint16_t* gamma;
+  float levels[16];
+};
+
+__device__ inline float h2f(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
+__device__ inline uint16_t f2h(float f) { return __builtin_bit_cast(uint16_t, (_Float16)f); }
+
+/* sum over the four 16-lane rows (lanes n, n+16, n+32, n+48) */
+__device__ inline float rows_sum(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+/* The B = bits-bit code of coordinate i of a packed row. */
+template <int B>
+__device__ inline uint32_t code_at(const uint8_t* row, int i) {
+  const int bit = i * B;
+  uint32_t w = row[bit >> 3];
+  if ((bit & 7) + B > 8) w |= (uint32_t)row[(bit >> 3) + 1] << 8;
+  return (w >> (bit & 7)) & ((1u << B) - 1);
+}
+
+template <int D, int B>
+__global__ void __launch_bounds__(256) qjl_encode_kernel(QjlEncArgs a) {
+  constexpr int KS = D / 32;
+  const int lane = threadIdx.x % 64, n = lane % 16, kq = lane / 16;
+  const int64_t v0 = ((int64_t)blockIdx.x * 4 + threadIdx.x / 64) * 16;
+  if (v0 >= a.n) return; /* whole waves only: every lane of a live wave stays */
+  const int64_t v = v0 + n;
+  const bool live = v < a.n;
+  /* x slice, sign flips D, squares for the norm */
+  float y[KS][8];
+  float ss = 0.0f;
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    const int i0 = 32 * s + 8 * kq;
+    uint4 w = make_uint4(0, 0, 0, 0);
+    if (live) w = *(const uint4*)(a.x + v * a.stride + i0);
+    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+    const uint32_t flips = a.sign_bits[i0 >> 3];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float f = h2f((uint16_t)(ww[j / 2] >> (16 * (j & 1))));
+      ss += f * f;
+      y[s][j] = ((flips >> j) & 1) ? -f : f;
+    }
+  }
+  ss = rows_sum(ss);
+  /* Walsh-Hadamard: coordinate 32 s + 8 kq + j */
+#pragma unroll
+  for (int h = 1; h < 8; h <<= 1)
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (!(j & h)) {
+          const float p = y[s][j], q = y[s][j | h];
+          y[s][j] = p + q;
+          y[s][j | h] = p - q;
+        }
+#pragma unroll
+  for (int h = 16; h <= 32; h <<= 1)
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float o = __shfl_xor(y[s][j], h);
+        y[s][j] = (lane & h) ? o - y[s][j] : y[s][j] + o;
+      }
+#pragma unroll
+  for (int h = 1; h < KS; h <<= 1)
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      if (!(s & h))
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float p = y[s][j], q = y[s | h][j];
+          y[s][j] = p + q;
+          y[s | h][j] = p - q;
+        }
+  /* residual in the rotated unit domain: y / (sqrt(d) ||x||) - c[code] */
+  const float scale = ss > 0.0f ? 1.0f / (sqrtf((float)D) * sqrtf(ss)) : 0.0f;
+  const uint8_t* row = a.codes + (live ? v : 0) * (D * B / 8);
+  float g2 = 0.0f;
+  half8 rhi[KS], rlo[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float r = live ? y[s][j] * scale - a.levels[code_at<B>(row, 32 * s + 8 * kq + j)] : 0.0f;
+      g2 += r * r;
+      const _Float16 hi = (_Float16)r;
+      rhi[s][j] = hi;
+      rlo[s][j] = (_Float16)(r - (float)hi);
+    }
+  g2 = rows_sum(g2);
+  if (live && kq == 0) a.gamma[v] = f2h(sqrtf(g2));
+  /* S r on the matrix cores: rows 16 mt .. 16 mt + 15 of S per product;
+   * lane (n, kq) gets projections 16 mt + 4 kq + 0..3 of key n */
+  uint32_t packed[D / 32]; /* the key's D sign bits, for lane kq == 0 */
+#pragma unroll
+  for (int mt = 0; mt < D / 16; ++mt) {
+    floatx4 t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const half8 sa = *(const half8*)(a.S + (16 * mt + n) * D + 32 * s + 8 * kq);
+      t = __builtin_amdgcn_mfma_f32_16x16x32_f16(sa, rhi[s], t, 0, 0, 0);
+      t = __builtin_amdgcn_mfma_f32_16x16x32_f16(sa, rlo[s], t, 0, 0, 0);
+    }
+    uint32_t nib = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) nib |= (t[i] >= 0.0f ? 1u : 0u) << i;
+    const uint32_t n1 = __shfl_xor(nib, 16), n2 = __shfl_xor(nib, 32), n3 = __shfl_xor(nib, 48);
+    const uint32_t bits16 = nib | (n1 << 4) | (n2 << 8) | (n3 << 12);
+    if (mt & 1) packed[mt / 2] |= bits16 << 16;
+    else packed[mt / 2] = bits16;
+  }
+  if (live && kq == 0) {
+    uint32_t* dst = (uint32_t*)(a.signs + v * (D / 8));
+#pragma unroll
+    for (int k = 0; k < D / 32; ++k) dst[k] = packed[k];
+  }
+}
+
+struct QjlScoreArgs {
+  const uint16_t* q; /* fp16 [G][d] */
+  int G;
+  const uint8_t* sign_bits;
+  const uint16_t* S;
+  const uint8_t* codes;
+  const uint16_t* norms;
+  const uint8_t* signs;
+  const uint16_t* gamma;
+  int64_t T;
+  float* out; /* [G][T] */
+  float levels[16];
+};
+
+template <int D, int B>
+__global__ void __launch_bounds__(256) qjl_scores_kernel(QjlScoreArgs a) {
+  __shared__ float rq[8][D];  /* R q */
+  __shared__ float sq[8][D];  /* S R q * sqrt(pi/2) / d */
+  __shared__ float lev[16];
+  const int tid = threadIdx.x;
+  if (tid < 16) lev[tid] = a.levels[tid];
+  /* R q = H D q / sqrt(d), one thread per (query, coordinate), by a plain
+   * O(d log d) pass through LDS */
+  for (int t = tid; t < a.G * D; t += blockDim.x) {
+    const int g = t / D, i = t % D;
+    const float f = h2f(a.q[g * D + i]);
+    rq[g][i] = ((a.sign_bits[i >> 3] >> (i & 7)) & 1) ? -f : f;
+  }
+  __syncthreads();
+  for (int h = 1; h < D; h <<= 1) {
+    float nv[(8 * D + 255) / 256];
+    int k = 0;
+    for (int t = tid; t < a.G * D; t += blockDim.x, ++k) {
+      const int g = t / D, i = t % D;
+      const float p = rq[g][i & ~h], q = rq[g][i | h];
+      nv[k] = (i & h) ? p - q : p + q;
+    }
+    __syncthreads();
+    k = 0;
+    for (int t = tid; t < a.G * D; t += blockDim.x, ++k) rq[t / D][t % D] = nv[k];
+    __syncthreads();
+  }
+  for (int t = tid; t < a.G * D; t += blockDim.x) rq[t / D][t % D] *= 1.0f / sqrtf((float)D);
+  __syncthreads();
+  for (int t = tid; t < a.G * D; t += blockDim.x) {
+    const int g = t / D, i = t % D;
+    float acc = 0.0f;
+    for (int j = 0; j < D; ++j) acc += h2f(a.S[i * D + j]) * rq[g][j];
+    sq[g][i] = acc * (kSqrtHalfPi / D);
+  }
+  __syncthreads();
+  const int64_t key = (int64_t)blockIdx.x * blockDim.x + tid;
+  if (key >= a.T) return;
+  const uint8_t* row = a.codes + key * (D * B / 8);
+  const uint8_t* sg = a.signs + key * (D / 8);
+  float mse[8], cor[8];
+#pragma unroll
+  for (int g = 0; g < 8; ++g) mse[g] = cor[g] = 0.0f;
+  for (int i = 0; i < D; ++i) {
+    const float c = lev[code_at<B>(row, i)];
+    const bool z = (sg[i >> 3] >> (i & 7)) & 1;
+#pragma unroll
+    for (int g = 0; g < 8; ++g)
+      if (g < a.G) {
+        mse[g] += rq[g][i] * c;
+        cor[g] += z ? sq[g][i] : -sq[g][i];
+      }
+  }
+  const float n16 = h2f(a.norms[key]), g16 = h2f(a.gamma[key]);
+#pragma unroll
+  for (int g = 0; g < 8; ++g)
+    if (g < a.G) a.out[g * a.T + key] = n16 * (mse[g] + g16 * cor[g]);
+}
+
+}  // namespace
+
+tq_status tq_launch_qjl_encode(const tq_codebook_s* cb, const uint16_t* x, int64_t n,
+                               int64_t stride, const uint8_t* sign_bits, const uint16_t* S,
+                               const uint8_t* codes, uint8_t* signs, uint16_t* gamma,
+                               hipStream_t s) {
+  QjlEncArgs a;
+  a.x = x;
+  a.n = n;
+  a.stride = stride;
+  a.sign_bits = sign_bits;
+  a.S = S;
+  a.codes = codes;
+  a.signs = signs;
+  a.gamma = gamma;
+  for (int k = 0; k < 16; ++k) a.levels[k] = k < (1 << cb->bits) ? cb->centroids[k] : 0.0f;
+  const int64_t blocks = (n + 63) / 64;
+#define TQ_QE(DD, BB) \
+  if (cb->d == DD && cb->bits == BB) \
+    hipLaunchKernelGGL((qjl_encode_kernel<DD, BB>), dim3((unsigned)blocks), dim3(256), 0, s, a); else
+  TQ_QE(64, 2) TQ_QE(64, 3) TQ_QE(64, 4) TQ_QE(128, 2) TQ_QE(128, 3) TQ_QE(128, 4)
+  TQ_QE(256, 2) TQ_QE(256, 3) TQ_QE(256, 4) return TQ_ERR_UNSUPPORTED;
+#undef TQ_QE
+  return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_DEVICE;
+}
+
+tq_status tq_launch_qjl_scores(const tq_codebook_s* cb, const uint16_t* q, int G,
+                               const uint8_t* sign_bits, const uint16_t* S, const uint8_t* codes,
+                               const uint16_t* norms, const uint8_t* signs,
+                               const uint16_t* gamma, int64_t T, float* out, hipStream_t s) {
+  QjlScoreArgs a;
+  a.q = q;
+  a.G = G;
+  a.sign_bits = sign_bits;
+  a.S = S;
+  a.codes = codes;
+  a.norms = norms;
+  a.signs = signs;
+  a.gamma = gamma;
+  a.T = T;
+  a.out = out;
+  for (int k = 0; k < 16; ++k) a.levels[k] = k < (1 << cb->bits) ? cb->centroids[k] : 0.0f;
+  const int64_t blocks = (T + 255) / 256;
+#define TQ_QS(DD, BB) \
+  if (cb->d == DD && cb->bits == BB) \
+    hipLaunchKernelGGL((qjl_scores_kernel<DD, BB>), dim3((unsigned)blocks), dim3(256), 0, s, a); else
+  TQ_QS(64, 2) TQ_QS(64, 3) TQ_QS(64, 4) TQ_QS(128, 2) TQ_QS(128, 3) TQ_QS(128, 4)
+  TQ_QS(256, 2) TQ_QS(256, 3) TQ_QS(256, 4) return TQ_ERR_UNSUPPORTED;
+#undef TQ_QS
+  return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_DEVICE;
+}

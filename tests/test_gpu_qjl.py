@@ -1,0 +1,84 @@
+"""GPU parity of the QJL stage (tq_qjl_encode, tq_qjl_scores) against the
+oracle ("We Built ...", "Why not both stages?"): the residual sketch (sign
+bits of S r, gamma = ||r||) and the inner-product estimate.
+
+S is the caller's draw (fp16 N(0,1) entries), passed to both sides.  Keys
+whose stage-1 codes differ between the two sides (a coordinate within 1e-6
+of a decision threshold, where either code is correct) are left out of the
+sketch comparisons and counted; projections within a relative 1e-4 of zero
+may take either sign (fp32 against fp64 residuals)."""
+import math
+
+import numpy as np
+import pytest
+
+import kv_cache_quantization_tq_amd as tq
+import oracle
+import synth
+from helpers import require_gpu
+
+pytestmark = pytest.mark.gpu
+SEED = 1004
+
+
+def _draw_S(rng, d):
+    return rng.standard_normal((d, d)).astype(np.float16)
+
+
+@pytest.mark.parametrize("d,bits,n", [(128, 4, 300), (64, 2, 77), (256, 3, 130), (128, 3, 1000)])
+def test_qjl_parity(d, bits, n):
+    torch = require_gpu()
+    rng = np.random.default_rng(d * 10 + bits)
+    x16 = synth.kv_host(SEED, 0, 0, 0, 0, d, 0, n)
+    sb = synth.sign_bits(SEED, 0, d)
+    S16 = _draw_S(rng, d)
+    cb = tq.Codebook(d, bits)
+    xd = torch.from_numpy(x16.view(np.int16)).cuda()
+    sbd = torch.from_numpy(sb).cuda()
+    Sd = torch.from_numpy(S16.view(np.int16)).cuda()
+    codes = torch.empty((n, d * bits // 8), dtype=torch.uint8, device="cuda")
+    norms = torch.empty(n, dtype=torch.int16, device="cuda")
+    signs = torch.empty((n, d // 8), dtype=torch.uint8, device="cuda")
+    gamma = torch.empty(n, dtype=torch.int16, device="cuda")
+    tq.encode(cb, xd, sbd, codes, norms)
+    tq.qjl_encode(cb, xd, sbd, Sd, codes, signs, gamma)
+    G = 4
+    q16 = np.stack([synth.q_host(SEED, 0, 0, 0, g, d) for g in range(G)])
+    qd = torch.from_numpy(q16.view(np.int16)).cuda()
+    out = torch.empty((G, n), dtype=torch.float32, device="cuda")
+    tq.qjl_scores(cb, qd, sbd, Sd, codes, norms, signs, gamma, out)
+    torch.cuda.synchronize()
+
+    S64 = S16.astype(np.float64)
+    oc, on, osg, og, proj = oracle.qjl_encode(x16, bits, sb, S64)
+    gc = oracle.unpack_rows(codes.cpu().numpy(), d, bits)
+    same = np.all(gc == oc, axis=1) & (norms.cpu().numpy().view(np.uint16) == on)
+    excluded = int((~same).sum())
+    print(f"QJL d={d} b={bits} n={n}: {excluded} keys with a band code left out", flush=True)
+    assert excluded <= max(2, n // 50)
+    # gamma: fp16 of the residual norm, within one fp16 rounding
+    gg = gamma.cpu().numpy().view(np.float16).astype(np.float64)
+    assert np.all(np.abs(gg[same] - og[same]) <= 2.0 ** -10 * og[same] + 1e-7)
+    # signs: bit-exact away from zero projections
+    gbits = np.unpackbits(signs.cpu().numpy(), axis=1, bitorder="little").astype(bool)
+    obits = np.unpackbits(osg, axis=1, bitorder="little").astype(bool)
+    rown = np.linalg.norm(S64, axis=1)
+    near = np.abs(proj) < 1e-4 * rown[None, :] * og[:, None]
+    bad = (gbits != obits) & ~near & same[:, None]
+    assert not bad.any(), np.argwhere(bad)[:5]
+    # estimates: against the oracle's estimate from its own sketch
+    R = oracle.rotation(d, sb)
+    c, _ = oracle.codebook(d, bits)
+    n16 = oracle.halves_to_double(on)
+    g16 = np.float16(og).astype(np.float64)
+    got = out.cpu().numpy()
+    for g in range(G):
+        q64 = oracle.halves_to_double(q16[g])
+        want = oracle.qjl_estimate(q64, oc, n16, g16, osg, S64, R, c)
+        rq = R @ q64
+        qjl_scale = n16 * math.sqrt(math.pi / 2) / d * g16 * np.abs(S64 @ rq).sum()
+        scale = n16 * (np.abs(rq) @ np.abs(c[oc]).T) + qjl_scale
+        err = np.abs(got[g] - want)
+        # fp32 sums, plus one fp16 rounding of gamma either way
+        assert np.all(err[same] <= 1e-5 * scale[same] + 2.0 ** -10 * qjl_scale[same]), (
+            err[same].max(), scale[same].max())

@@ -111,6 +111,17 @@ def test_sparse_decode_validation():
         assert call(eps, vp(4)) == 2, eps
 
 
+def test_qjl_validation():
+    """The QJL entry points reject null handles and pointers, misaligned
+    buffers and unsupported query counts before any device work."""
+    L = tq.lib()
+    vp = ctypes.c_void_p
+    assert L.tq_qjl_encode(None, vp(16), 4, 128, vp(4), vp(16), vp(16), vp(16), vp(16), None) == 1
+    assert L.tq_qjl_scores(None, vp(16), 4, vp(4), vp(16), vp(16), vp(16), vp(16), vp(16), 8,
+                           vp(16), None) == 1
+    assert L.tq_qjl_encode(None, vp(16), -1, 128, vp(4), vp(16), vp(16), vp(16), vp(16), None) == 1
+
+
 def test_workspace_planning():
     L = tq.lib()
     s = _fake_cache(capacity=32768)
