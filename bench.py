@@ -460,6 +460,61 @@ def workload_prefill(args):
             args, ms)
 
 
+def workload_qjl(args):
+    """The QJL stage on the keys of the 32K workload (32 layers x 8 KV heads x
+    32768 tokens, d 128, 4-bit keys): tq_qjl_encode over all 8.4M keys (after
+    tq_encode), then tq_qjl_scores of 4 queries against all of them.  Both
+    stream HBM: per key the sketch reads the fp16 key and its codes and
+    writes d/8 sign bytes and gamma; the estimate reads codes, signs, norm and
+    gamma and writes 4 floats."""
+    import numpy as np
+    import torch
+    import kv_cache_quantization_tq_amd as tq
+    import synth
+    torch.cuda.set_device(0)
+    n = L * B * HKV * T
+    x = torch.empty((L, B, HKV, T, D), dtype=torch.int16, device="cuda")
+    for l in range(L):
+        synth.kv_dev(SEED, 0, l, x[l])
+    x = x.view(n, D)
+    cb = tq.Codebook(D, BK)
+    sb = torch.from_numpy(synth.sign_bits(SEED, 0, D)).cuda()
+    rng = np.random.default_rng(SEED)
+    S = torch.from_numpy(rng.standard_normal((D, D)).astype(np.float16).view(np.int16)).cuda()
+    codes = torch.empty((n, D * BK // 8), dtype=torch.uint8, device="cuda")
+    norms = torch.empty(n, dtype=torch.int16, device="cuda")
+    signs = torch.empty((n, D // 8), dtype=torch.uint8, device="cuda")
+    gamma = torch.empty(n, dtype=torch.int16, device="cuda")
+    tq.encode(cb, x, sb, codes, norms)
+    q = torch.empty((1, 4, D), dtype=torch.int16, device="cuda")
+    synth.q_dev(SEED, 0, 0, q)
+    q = q.view(4, D)
+    out = torch.empty((4, n), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    enc_ms = _timed(torch, lambda: tq.qjl_encode(cb, x, sb, S, codes, signs, gamma), args.steps,
+                    args.warmup)
+    sc_ms = _timed(torch, lambda: tq.qjl_scores(cb, q, sb, S, codes, norms, signs, gamma, out),
+                   args.steps, args.warmup)
+    enc_b = n * (2 * D + D * BK // 8 + D // 8 + 2)
+    sc_b = n * (D * BK // 8 + D // 8 + 2 + 2 + 4 * 4)
+    enc_gbs = enc_b / (enc_ms * 1e-3) / 1e9
+    sc_gbs = sc_b / (sc_ms * 1e-3) / 1e9
+    _report({"workload": "QJL sketch and estimate over the keys of the 32K workload",
+             "keys": n, "head_dim": D, "bits_k": BK, "queries": 4},
+            "QJL sketch GB/s (fp16 keys + codes read, signs + gamma written)", enc_gbs, "GB/s",
+            True,
+            {"dtype": "f32 (f16 matrix-core operands for S r)",
+             "qjl_encode_ms": enc_ms, "qjl_encode_keys_per_s": n / (enc_ms * 1e-3),
+             "qjl_scores_ms": sc_ms, "qjl_scores_gbs": sc_gbs,
+             "roofline": {"bound": "hbm", "kernel": "qjl_encode_kernel<128,4>",
+                          "achieved": enc_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                          "frac": enc_gbs / HBM_PEAK_GBS, "traffic": None},
+             "roofline_scores": {"bound": "hbm", "kernel": "qjl_scores_kernel<128,4>",
+                                 "achieved": sc_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                 "frac": sc_gbs / HBM_PEAK_GBS, "traffic": None}},
+            args, enc_ms + sc_ms)
+
+
 WORKLOADS = {
     "llama8b-32k": None,
     "tiny": workload_tiny,
@@ -469,6 +524,7 @@ WORKLOADS = {
     "paged-llama8b-32k": workload_paged_llama8b,
     "sparse-v-llama8b-32k": workload_sparse_v,
     "prefill-llama8b-32k": workload_prefill,
+    "qjl-llama8b-32k": workload_qjl,
 }
 
 

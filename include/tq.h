@@ -245,8 +245,9 @@ tq_status tq_qjl_encode(tq_codebook cb, const uint16_t* x, int64_t n, int64_t x_
  * original domain) over n_keys sketched keys:
  *   n16_t * ( <R q, c[codes_t]> + sqrt(pi/2) / d * gamma_t * <S R q, z_t> ),
  * z_t = +-1 from the sign bits; unbiased for <q, x_t> n16_t / ||x_t|| over
- * the draw of S.  codes [n_keys][d*bits/8], norms fp16 [n_keys] (tq_encode),
- * signs, gamma as tq_qjl_encode; out: device fp32 [n_q][n_keys]. */
+ * the draw of S.  codes [n_keys][d*bits/8] (8-byte aligned), norms fp16
+ * [n_keys] (tq_encode), signs (4-byte aligned), gamma as tq_qjl_encode; out:
+ * device fp32 [n_q][n_keys]. */
 tq_status tq_qjl_scores(tq_codebook cb, const uint16_t* q, int n_q, const uint8_t* sign_bits,
                         const uint16_t* S, const uint8_t* codes, const uint16_t* norms,
                         const uint8_t* signs, const uint16_t* gamma, int64_t n_keys, float* out,

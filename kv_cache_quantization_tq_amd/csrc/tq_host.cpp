@@ -447,7 +447,7 @@ extern "C" tq_status tq_qjl_scores(tq_codebook cb, const uint16_t* q, int n_q,
   if (n_keys == 0) return TQ_OK;
   if (!q || !sign_bits || !S || !codes || !norms || !signs || !gamma || !out) return TQ_ERR_ARG;
   if (!aligned(q, 2) || !aligned(norms, 2) || !aligned(gamma, 2) || !aligned(out, 4) ||
-      !aligned(S, 2))
+      !aligned(S, 2) || !aligned(codes, 8) || !aligned(signs, 4))
     return TQ_ERR_ARG;
   return tq_launch_qjl_scores(cb, q, n_q, sign_bits, S, codes, norms, signs, gamma, n_keys, out,
                               (hipStream_t)stream);

@@ -52,13 +52,14 @@ __device__ inline float rows_sum(float v) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-/* The B = bits-bit code of coordinate i of a packed row. */
+/* 8 consecutive B-bit codes starting at a byte boundary (B bytes, read as
+ * bytes: the rows are only byte-aligned for B = 3). */
 template <int B>
-__device__ inline uint32_t code_at(const uint8_t* row, int i) {
-  const int bit = i * B;
-  uint32_t w = row[bit >> 3];
-  if ((bit & 7) + B > 8) w |= (uint32_t)row[(bit >> 3) + 1] << 8;
-  return (w >> (bit & 7)) & ((1u << B) - 1);
+__device__ inline uint32_t codes8(const uint8_t* p) {
+  uint32_t w = 0;
+#pragma unroll
+  for (int k = 0; k < B; ++k) w |= (uint32_t)p[k] << (8 * k);
+  return w;
 }
 
 template <int D, int B>
@@ -125,15 +126,18 @@ __global__ void __launch_bounds__(256) qjl_encode_kernel(QjlEncArgs a) {
   float g2 = 0.0f;
   half8 rhi[KS], rlo[KS];
 #pragma unroll
-  for (int s = 0; s < KS; ++s)
+  for (int s = 0; s < KS; ++s) {
+    /* the 8 codes of coordinates 32 s + 8 kq + 0..7: B bytes of the row */
+    const uint32_t cw = live ? codes8<B>(row + (32 * s + 8 * kq) * B / 8) : 0u;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const float r = live ? y[s][j] * scale - a.levels[code_at<B>(row, 32 * s + 8 * kq + j)] : 0.0f;
+      const float r = live ? y[s][j] * scale - a.levels[(cw >> (B * j)) & ((1u << B) - 1)] : 0.0f;
       g2 += r * r;
       const _Float16 hi = (_Float16)r;
       rhi[s][j] = hi;
       rlo[s][j] = (_Float16)(r - (float)hi);
     }
+  }
   g2 = rows_sum(g2);
   if (live && kq == 0) a.gamma[v] = f2h(sqrtf(g2));
   /* S r on the matrix cores: rows 16 mt .. 16 mt + 15 of S per product;
@@ -216,14 +220,30 @@ __global__ void __launch_bounds__(256) qjl_scores_kernel(QjlScoreArgs a) {
   __syncthreads();
   const int64_t key = (int64_t)blockIdx.x * blockDim.x + tid;
   if (key >= a.T) return;
-  const uint8_t* row = a.codes + key * (D * B / 8);
-  const uint8_t* sg = a.signs + key * (D / 8);
+  /* the key's row and sign bits in registers (rows are 8 * B-byte aligned:
+   * d * B / 8 is a multiple of 8 for d >= 64) */
+  constexpr int RW = D * B / 32; /* 32-bit words per row */
+  uint32_t cw[RW], zw[D / 32];
+  const uint2* row = (const uint2*)(a.codes + key * (D * B / 8));
+#pragma unroll
+  for (int k = 0; k < RW / 2; ++k) {
+    const uint2 t = row[k];
+    cw[2 * k] = t.x;
+    cw[2 * k + 1] = t.y;
+  }
+  const uint32_t* sg = (const uint32_t*)(a.signs + key * (D / 8));
+#pragma unroll
+  for (int k = 0; k < D / 32; ++k) zw[k] = sg[k];
   float mse[8], cor[8];
 #pragma unroll
   for (int g = 0; g < 8; ++g) mse[g] = cor[g] = 0.0f;
+#pragma unroll
   for (int i = 0; i < D; ++i) {
-    const float c = lev[code_at<B>(row, i)];
-    const bool z = (sg[i >> 3] >> (i & 7)) & 1;
+    const int bit = i * B;
+    uint32_t code = cw[bit >> 5] >> (bit & 31);
+    if ((bit & 31) + B > 32) code |= cw[(bit >> 5) + 1] << (32 - (bit & 31));
+    const float c = lev[code & ((1u << B) - 1)];
+    const bool z = (zw[i >> 5] >> (i & 31)) & 1;
 #pragma unroll
     for (int g = 0; g < 8; ++g)
       if (g < a.G) {
