@@ -111,6 +111,26 @@ def test_sparse_decode_validation():
         assert call(eps, vp(4)) == 2, eps
 
 
+def test_prefill_validation():
+    """tq_prefill_attn checks the cache, the group size and t_new before any
+    device work."""
+    L = tq.lib()
+    vp = ctypes.c_void_p
+    for kw in (dict(capacity=1000), dict(head_dim=96), dict(bits_v=1)):
+        s = _fake_cache(**kw)
+        assert L.tq_prefill_attn(ctypes.byref(s), None, None, vp(1), vp(16), 8, 4, vp(4), 1,
+                                 vp(16), None) in (1, 2), kw
+    s = _fake_cache()
+    assert L.tq_prefill_attn(ctypes.byref(s), None, None, vp(1), vp(16), 12, 4, vp(4), 1,
+                             vp(16), None) == 1          # q_heads not a multiple of kv_heads
+    assert L.tq_prefill_attn(ctypes.byref(s), None, None, vp(1), vp(16), 128, 4, vp(4), 1,
+                             vp(16), None) == 2          # group of 16
+    assert L.tq_prefill_attn(ctypes.byref(s), None, None, vp(1), vp(16), 8, -1, vp(4), 1,
+                             vp(16), None) == 1          # negative t_new
+    assert L.tq_prefill_attn(ctypes.byref(s), None, None, vp(1), vp(16), 8, 4, vp(4), 0,
+                             vp(16), None) == 1          # no layers
+
+
 def test_qjl_validation():
     """The QJL entry points reject null handles and pointers, misaligned
     buffers and unsupported query counts before any device work."""
