@@ -16,8 +16,10 @@
  * (v_mfma_f32_16x16x32_f16, r split into two fp16 parts; S is exact in fp16).
  * The rotation is the butterfly Walsh-Hadamard transform: in-lane strides
  * 1, 2, 4 and >= 32, lane-xor 16 and 32 for strides 8 and 16.
- * qjl_scores_kernel: one thread per key, the group's rotated queries and
- * their projections in LDS (plain VALU: 2 G multiply-adds per coordinate).
+ * qjl_scores_kernel: 16 keys per wave on the matrix cores, like the decode's
+ * scores: A = the keys' fp16 levels (plus their fp16 remainders against
+ * q 2^-11) and their signs as +-1, B = the group's rotated queries and their
+ * projections split into two fp16 parts (columns 0..7 and 8..15).
  */
 #include <hip/hip_runtime.h>
 
@@ -181,13 +183,26 @@ struct QjlScoreArgs {
   float levels[16];
 };
 
+/* Row reduction partner: the value of the lane 8 places along in the
+ * 16-lane row. */
+__device__ inline float ror8(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));
+}
+
 template <int D, int B>
 __global__ void __launch_bounds__(256) qjl_scores_kernel(QjlScoreArgs a) {
-  __shared__ float rq[8][D];  /* R q */
-  __shared__ float sq[8][D];  /* S R q * sqrt(pi/2) / d */
-  __shared__ float lev[16];
-  const int tid = threadIdx.x;
-  if (tid < 16) lev[tid] = a.levels[tid];
+  constexpr int KS = D / 32;
+  __shared__ float rq[8][D];   /* R q */
+  __shared__ float sq[8][D];   /* S R q * sqrt(pi/2) / d */
+  __shared__ uint32_t lev[64]; /* level c as {fp16 c, fp16 (c - fp16 c) 2^11}, 4 copies */
+  const int tid = threadIdx.x, lane = tid % 64, n = lane % 16, kq = lane / 16;
+  if (tid < 64) {
+    const float c = a.levels[tid / 4];
+    const _Float16 h = (_Float16)c;
+    const _Float16 l = (_Float16)((c - (float)h) * 2048.0f);
+    lev[tid] = (uint32_t)__builtin_bit_cast(uint16_t, h) |
+               ((uint32_t)__builtin_bit_cast(uint16_t, l) << 16);
+  }
   /* R q = H D q / sqrt(d), one thread per (query, coordinate), by a plain
    * O(d log d) pass through LDS */
   for (int t = tid; t < a.G * D; t += blockDim.x) {
@@ -218,43 +233,83 @@ __global__ void __launch_bounds__(256) qjl_scores_kernel(QjlScoreArgs a) {
     sq[g][i] = acc * (kSqrtHalfPi / D);
   }
   __syncthreads();
-  const int64_t key = (int64_t)blockIdx.x * blockDim.x + tid;
-  if (key >= a.T) return;
-  /* the key's row and sign bits in registers (rows are 8 * B-byte aligned:
-   * d * B / 8 is a multiple of 8 for d >= 64) */
-  constexpr int RW = D * B / 32; /* 32-bit words per row */
-  uint32_t cw[RW], zw[D / 32];
-  const uint2* row = (const uint2*)(a.codes + key * (D * B / 8));
+  /* B operands, lane (n, kq), coordinates 32 s + 8 kq + 0..7: columns 0..7
+   * the fp16 parts of query n, 8..15 their fp16 remainders (levels and sign
+   * products); for the level remainders fp16(R q 2^-11) in columns 0..7 */
+  half8 bl[KS], br[KS], bs[KS];
+  {
+    const int g = n & 7;
+    const bool hiCol = n < 8, ok = g < a.G;
 #pragma unroll
-  for (int k = 0; k < RW / 2; ++k) {
-    const uint2 t = row[k];
-    cw[2 * k] = t.x;
-    cw[2 * k + 1] = t.y;
-  }
-  const uint32_t* sg = (const uint32_t*)(a.signs + key * (D / 8));
+    for (int s = 0; s < KS; ++s)
 #pragma unroll
-  for (int k = 0; k < D / 32; ++k) zw[k] = sg[k];
-  float mse[8], cor[8];
-#pragma unroll
-  for (int g = 0; g < 8; ++g) mse[g] = cor[g] = 0.0f;
-#pragma unroll
-  for (int i = 0; i < D; ++i) {
-    const int bit = i * B;
-    uint32_t code = cw[bit >> 5] >> (bit & 31);
-    if ((bit & 31) + B > 32) code |= cw[(bit >> 5) + 1] << (32 - (bit & 31));
-    const float c = lev[code & ((1u << B) - 1)];
-    const bool z = (zw[i >> 5] >> (i & 31)) & 1;
-#pragma unroll
-    for (int g = 0; g < 8; ++g)
-      if (g < a.G) {
-        mse[g] += rq[g][i] * c;
-        cor[g] += z ? sq[g][i] : -sq[g][i];
+      for (int j = 0; j < 8; ++j) {
+        const int i = 32 * s + 8 * kq + j;
+        const float r = ok ? rq[g][i] : 0.0f, z = ok ? sq[g][i] : 0.0f;
+        const _Float16 rh = (_Float16)r, zh = (_Float16)z;
+        bl[s][j] = hiCol ? rh : (_Float16)(r - (float)rh);
+        br[s][j] = hiCol ? (_Float16)(r * 0x1p-11f) : (_Float16)0.0f;
+        bs[s][j] = hiCol ? zh : (_Float16)(z - (float)zh);
       }
   }
-  const float n16 = h2f(a.norms[key]), g16 = h2f(a.gamma[key]);
+  /* 16-key tiles, one per wave at a time: lane (m = n, kq) supplies key
+   * k0 + m's coordinates 32 s + 8 kq + 0..7 of the A operands (levels, level
+   * remainders, signs as +-1) */
+  const int wave = tid / 64;
+  const uint32_t cpy = (uint32_t)lane & 3u;
+  const int64_t ntile = (a.T + 15) / 16;
+  for (int64_t tile = (int64_t)blockIdx.x * 4 + wave; tile < ntile; tile += (int64_t)gridDim.x * 4) {
+    const int64_t k0 = tile * 16, key = k0 + n;
+    const bool live = key < a.T;
+    const uint8_t* row = a.codes + (live ? key : 0) * (D * B / 8);
+    const uint8_t* sg = a.signs + (live ? key : 0) * (D / 8);
+    floatx4 c1 = {0.f, 0.f, 0.f, 0.f}, c2 = {0.f, 0.f, 0.f, 0.f};
+    /* the key's sign bits in one go (d/8 bytes, 4-byte aligned) */
+    uint32_t zw[D / 32];
 #pragma unroll
-  for (int g = 0; g < 8; ++g)
-    if (g < a.G) a.out[g * a.T + key] = n16 * (mse[g] + g16 * cor[g]);
+    for (int k = 0; k < D / 32; ++k) zw[k] = live ? ((const uint32_t*)sg)[k] : 0u;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      /* the 8 codes at byte (32 s + 8 kq) B / 8 from aligned words (rows are
+       * a multiple of 4 bytes, so the word holding the last byte ends inside
+       * the row) */
+      uint32_t cw = 0;
+      if (live) {
+        const int off = (32 * s + 8 * kq) * B / 8;
+        const uint32_t* w = (const uint32_t*)(row + (off & ~3));
+        if constexpr (B == 3)
+          cw = (off & 3) + 3 > 4 ? __builtin_amdgcn_alignbit(w[1], w[0], (uint32_t)(off & 3) * 8u)
+                                 : w[0] >> ((off & 3) * 8);
+        else
+          cw = w[0] >> ((off & 3) * 8);
+      }
+      const uint32_t zb = (zw[s] >> (8 * kq)) & 0xFFu;
+      uint32_t e[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) e[j] = lev[((cw >> (B * j)) & ((1u << B) - 1)) * 4 + cpy];
+      half8 ah, al, az;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        ah[j] = __builtin_bit_cast(_Float16, (uint16_t)(e[j] & 0xFFFFu));
+        al[j] = __builtin_bit_cast(_Float16, (uint16_t)(e[j] >> 16));
+        az[j] = ((zb >> j) & 1) ? (_Float16)1.0f : (_Float16)-1.0f;
+      }
+      c1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bl[s], c1, 0, 0, 0);
+      c1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, br[s], c1, 0, 0, 0);
+      c2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(az, bs[s], c2, 0, 0, 0);
+    }
+    /* lane (n, kq) holds keys k0 + 4 kq + i of column n; join the fp16
+     * parts (column n + 8) into columns n < 8 */
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float m1 = c1[i] + ror8(c1[i]), m2 = c2[i] + ror8(c2[i]);
+      const int64_t kk = k0 + 4 * kq + i;
+      if (n < a.G && kk < a.T) {
+        const float n16 = h2f(a.norms[kk]), g16 = h2f(a.gamma[kk]);
+        a.out[n * a.T + kk] = n16 * (m1 + g16 * m2);
+      }
+    }
+  }
 }
 
 }  // namespace
@@ -299,7 +354,8 @@ tq_status tq_launch_qjl_scores(const tq_codebook_s* cb, const uint16_t* q, int G
   a.T = T;
   a.out = out;
   for (int k = 0; k < 16; ++k) a.levels[k] = k < (1 << cb->bits) ? cb->centroids[k] : 0.0f;
-  const int64_t blocks = (T + 255) / 256;
+  int64_t blocks = (T + 63) / 64; /* 4 waves of 16 keys; capped, the waves then stride */
+  if (blocks > 4096) blocks = 4096;
 #define TQ_QS(DD, BB) \
   if (cb->d == DD && cb->bits == BB) \
     hipLaunchKernelGGL((qjl_scores_kernel<DD, BB>), dim3((unsigned)blocks), dim3(256), 0, s, a); else
