@@ -10,7 +10,8 @@
  * projection is >= 0).  The estimate of <q, x> is
  *   n16 * ( <R q, c[codes]> + sqrt(pi/2) / d * gamma * <S R q, z> ).
  *
- * qjl_encode_kernel: a wave sketches 16 keys.  Lane (n, kq) holds
+ * qjl_encode_kernel: a wave sketches 16 keys at a time (S staged in LDS
+ * per block for d <= 128).  Lane (n, kq) holds
  * coordinates 32 s + 8 kq + 0..7 of key n, so the residual it computes is
  * exactly its slice of the B operand of S R^T on the matrix cores
  * (v_mfma_f32_16x16x32_f16, r split into two fp16 parts; S is exact in fp16).
@@ -64,12 +65,31 @@ __device__ inline uint32_t codes8(const uint8_t* p) {
   return w;
 }
 
+/* S in LDS (rows padded against bank conflicts) for d <= 128; 256-dim heads
+ * read it through the caches */
+template <int D>
+struct SLds {
+  static constexpr bool ON = D <= 128;
+  static constexpr int P = D + 8; /* row pitch, halfs */
+  static constexpr int HALFS = ON ? D * P : 8;
+};
+
 template <int D, int B>
 __global__ void __launch_bounds__(256) qjl_encode_kernel(QjlEncArgs a) {
   constexpr int KS = D / 32;
+  using SL = SLds<D>;
+  __shared__ __align__(16) _Float16 sl[SL::HALFS];
   const int lane = threadIdx.x % 64, n = lane % 16, kq = lane / 16;
-  const int64_t v0 = ((int64_t)blockIdx.x * 4 + threadIdx.x / 64) * 16;
-  if (v0 >= a.n) return; /* whole waves only: every lane of a live wave stays */
+  if constexpr (SL::ON) {
+    for (int t = threadIdx.x; t < D * D / 8; t += blockDim.x) {
+      const int r = t / (D / 8), c = t % (D / 8);
+      *(uint4*)(sl + r * SL::P + 8 * c) = *(const uint4*)(a.S + r * D + 8 * c);
+    }
+    __syncthreads();
+  }
+  /* each wave sketches groups of 16 keys, striding over the grid */
+  for (int64_t v0 = ((int64_t)blockIdx.x * 4 + threadIdx.x / 64) * 16; v0 < a.n;
+       v0 += (int64_t)gridDim.x * 64) {
   const int64_t v = v0 + n;
   const bool live = v < a.n;
   /* x slice, sign flips D, squares for the norm */
@@ -150,7 +170,8 @@ __global__ void __launch_bounds__(256) qjl_encode_kernel(QjlEncArgs a) {
     floatx4 t = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      const half8 sa = *(const half8*)(a.S + (16 * mt + n) * D + 32 * s + 8 * kq);
+      const half8 sa = SL::ON ? *(const half8*)(sl + (16 * mt + n) * SL::P + 32 * s + 8 * kq)
+                              : *(const half8*)(a.S + (16 * mt + n) * D + 32 * s + 8 * kq);
       t = __builtin_amdgcn_mfma_f32_16x16x32_f16(sa, rhi[s], t, 0, 0, 0);
       t = __builtin_amdgcn_mfma_f32_16x16x32_f16(sa, rlo[s], t, 0, 0, 0);
     }
@@ -166,6 +187,7 @@ __global__ void __launch_bounds__(256) qjl_encode_kernel(QjlEncArgs a) {
     uint32_t* dst = (uint32_t*)(a.signs + v * (D / 8));
 #pragma unroll
     for (int k = 0; k < D / 32; ++k) dst[k] = packed[k];
+  }
   }
 }
 
@@ -328,7 +350,8 @@ tq_status tq_launch_qjl_encode(const tq_codebook_s* cb, const uint16_t* x, int64
   a.signs = signs;
   a.gamma = gamma;
   for (int k = 0; k < 16; ++k) a.levels[k] = k < (1 << cb->bits) ? cb->centroids[k] : 0.0f;
-  const int64_t blocks = (n + 63) / 64;
+  int64_t blocks = (n + 63) / 64; /* 4 waves of 16 keys; capped, the waves then stride */
+  if (blocks > 2048) blocks = 2048;
 #define TQ_QE(DD, BB) \
   if (cb->d == DD && cb->bits == BB) \
     hipLaunchKernelGGL((qjl_encode_kernel<DD, BB>), dim3((unsigned)blocks), dim3(256), 0, s, a); else
