@@ -6,7 +6,9 @@ import pytest
 
 import kv_cache_quantization_tq_amd as tq
 import synth
-from helpers import attention_errors, check_attention, oracle_attention_with_bound, require_gpu
+import oracle
+from helpers import (attention_errors, band_flip_bound, check_attention, compare_codes,
+                     oracle_attention_with_bound, require_gpu)
 
 pytestmark = pytest.mark.gpu
 SEED = 1011
@@ -111,3 +113,50 @@ def test_paged_invalid_entries_skip_rows():
     written = {3, 5, 0, 7, 2, 1}
     for phys in set(range(num_pages)) - written:
         assert not paged.k_codes[0, phys].any() and not paged.v_codes[0, phys].any()
+
+
+def test_paged_full_size_sampled():
+    """The paged benchmark's shapes (32K context, 8 KV heads, groups of 4,
+    d 128, K4/V2, 256-token pages in shuffled order; two layers: the launch
+    configuration per block does not depend on the layer count): sampled
+    units' codes, norms and decode outputs against the oracle."""
+    torch = require_gpu()
+    d, bk, bv, G, H, T, Lyr, P = 128, 4, 2, 4, 8, 32768, 2, 256
+    seed = 1002
+    cap = T + 256
+    maxp = cap // P
+    table = np.random.default_rng(7).permutation(maxp).reshape(1, maxp).astype(np.int32)
+    cache = tq.PagedKVCache(Lyr, 1, H, d, bk, bv, P, maxp, maxp, table)
+    sbs = np.stack([synth.sign_bits(seed, l, d) for l in range(Lyr)])
+    sbd = torch.from_numpy(sbs).cuda()
+    cbk, cbv = tq.Codebook(d, bk), tq.Codebook(d, bv)
+    for l in range(Lyr):
+        k = torch.empty((1, 1, H, T, d), dtype=torch.int16, device="cuda")
+        v = torch.empty_like(k)
+        synth.kv_dev(seed, 0, l, k[0])
+        synth.kv_dev(seed, 1, l, v[0])
+        tq.append(cache, cbk, cbv, sbd[l:l + 1], k, v,
+                  torch.zeros(1, dtype=torch.int32, device="cuda"), host_max_pos=0, layer0=l,
+                  n_layers=1)
+    q = torch.empty((Lyr, 1, G * H, d), dtype=torch.int16, device="cuda")
+    for l in range(Lyr):
+        synth.q_dev(seed, 0, l, q[l])
+    lens = torch.full((1,), T, dtype=torch.int32, device="cuda")
+    out = torch.empty((Lyr, 1, G * H, d), dtype=torch.float32, device="cuda")
+    tq.decode(cache, cbk, cbv, sbd, q, lens, T, out, tq.workspace(cache, G * H, T))
+    torch.cuda.synchronize()
+    q16 = q.cpu().numpy().view(np.uint16)
+    for (l, h) in ((0, 0), (1, 6)):
+        kk = synth.kv_host(seed, 0, l, 0, h, d, 0, T)
+        vv = synth.kv_host(seed, 1, l, 0, h, d, 0, T)
+        sl = slice(h * G, (h + 1) * G)
+        st = oracle.decode_stream(kk, vv, q16[l, 0, sl], bk, bv, sbs[l], full=True)
+        kc, vc, kn, vn = cache.gather(l, 0, h)
+        kc = kc[:T].cpu().numpy()
+        kn = kn[:T].cpu().numpy().view(np.uint16)
+        compare_codes(oracle.unpack_rows(kc, d, bk), st["k_codes"], st["k_band"],
+                      f"paged 32K layer {l} head {h} keys")
+        assert np.array_equal(kn, st["k_norms"])
+        q64 = oracle.halves_to_double(q16[l, 0, sl])
+        bd, _ = band_flip_bound(q64, kk, vv, st, bk, bv, sbs[l])
+        check_attention(out[l, 0, sl].cpu().numpy(), st["out"], bd, f"paged 32K layer {l} head {h}")

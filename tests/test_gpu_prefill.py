@@ -122,3 +122,52 @@ def test_prefill_row_equals_decode():
         want = out.cpu().numpy()
         rel = np.linalg.norm(got - want) / np.linalg.norm(want)
         assert rel < 1e-4 and np.abs(got - want).max() < 1e-3, (i, rel)
+
+
+def test_prefill_full_size_sampled():
+    """The benchmark's prefill launch at its full prompt (32768 tokens, 8 KV
+    heads, groups of 4, d 128, K4/V2; one layer: the launch configuration per
+    block does not depend on the layer count), checked on sampled query rows
+    of two KV heads against the oracle's attention over their whole prefix."""
+    torch = require_gpu()
+    d, bk, bv, G, H, T = 128, 4, 2, 4, 8, 32768
+    seed = 1002
+    cache = tq.KVCache(1, 1, H, d, bk, bv, T)
+    sbs = np.stack([synth.sign_bits(seed, 0, d)])
+    sbd = torch.from_numpy(sbs).cuda()
+    cbk, cbv = tq.Codebook(d, bk), tq.Codebook(d, bv)
+    k = torch.empty((1, 1, H, T, d), dtype=torch.int16, device="cuda")
+    v = torch.empty_like(k)
+    synth.kv_dev(seed, 0, 0, k[0])
+    synth.kv_dev(seed, 1, 0, v[0])
+    tq.append(cache, cbk, cbv, sbd, k, v, torch.zeros(1, dtype=torch.int32, device="cuda"),
+              host_max_pos=0)
+    del k, v
+    rows = [0, 31, 32, 4095, 16384, 32767]
+    q16 = np.empty((1, 1, G * H, T, d), dtype=np.uint16)
+    qs = np.stack([synth.q_host(seed, 0, 0, 0, hq, d) for hq in range(G * H)])
+    q16[0, 0] = qs[:, None, :]
+    for hq in range(G * H):  # distinct queries on the sampled rows
+        for i in rows:
+            q16[0, 0, hq, i] = synth.q_host(seed, i + 1, 0, 0, hq, d)
+    qd = torch.from_numpy(q16.view(np.int16)).cuda()
+    out = torch.empty((1, 1, G * H, T, d), dtype=torch.float32, device="cuda")
+    tq.prefill(cache, cbk, cbv, sbd, qd, torch.zeros(1, dtype=torch.int32, device="cuda"), out)
+    torch.cuda.synchronize()
+    for h in (0, 5):
+        kk = synth.kv_host(seed, 0, 0, 0, h, d, 0, T)
+        vv = synth.kv_host(seed, 1, 0, 0, h, d, 0, T)
+        sl = slice(h * G, (h + 1) * G)
+        st = oracle.decode_stream(kk, vv, q16[0, 0, sl, 0], bk, bv, sbs[0], full=True)
+        got = np.stack([out[0, 0, sl, i].cpu().numpy() for i in rows])
+        ref = np.zeros_like(got, dtype=np.float64)
+        bound = np.zeros_like(ref)
+        for r, i in enumerate(rows):
+            n = i + 1
+            q64 = oracle.halves_to_double(q16[0, 0, sl, i])
+            o = oracle.attention(q64, st["K"][:n], st["V"][:n])
+            sp = prefix(st, n)
+            sp["out"] = o
+            bd, _ = band_flip_bound(q64, kk[:n], vv[:n], sp, bk, bv, sbs[0])
+            ref[r], bound[r] = o, bd
+        check_attention(got, ref, bound, f"prefill 32K, KV head {h}, rows {rows}")
