@@ -82,3 +82,59 @@ def test_qjl_parity(d, bits, n):
         # fp32 sums, plus one fp16 rounding of gamma either way
         assert np.all(err[same] <= 1e-5 * scale[same] + 2.0 ** -10 * qjl_scale[same]), (
             err[same].max(), scale[same].max())
+
+
+def test_qjl_large_sampled():
+    """655,360 keys (8 heads x 81,920 tokens, d 128, 4 bits): more than one
+    grid-stride pass of both kernels; sampled keys (including the last ones)
+    against the oracle."""
+    torch = require_gpu()
+    d, bits, H, T = 128, 4, 8, 81920
+    n = H * T
+    rng = np.random.default_rng(5)
+    S16 = _draw_S(rng, d)
+    sb = synth.sign_bits(SEED, 0, d)
+    cb = tq.Codebook(d, bits)
+    x = torch.empty((1, H, T, d), dtype=torch.int16, device="cuda")
+    synth.kv_dev(SEED, 0, 0, x)
+    xd = x.view(n, d)
+    sbd = torch.from_numpy(sb).cuda()
+    Sd = torch.from_numpy(S16.view(np.int16)).cuda()
+    codes = torch.empty((n, d * bits // 8), dtype=torch.uint8, device="cuda")
+    norms = torch.empty(n, dtype=torch.int16, device="cuda")
+    signs = torch.empty((n, d // 8), dtype=torch.uint8, device="cuda")
+    gamma = torch.empty(n, dtype=torch.int16, device="cuda")
+    tq.encode(cb, xd, sbd, codes, norms)
+    tq.qjl_encode(cb, xd, sbd, Sd, codes, signs, gamma)
+    G = 3
+    q16 = np.stack([synth.q_host(SEED, 0, 0, 0, g, d) for g in range(G)])
+    out = torch.empty((G, n), dtype=torch.float32, device="cuda")
+    tq.qjl_scores(cb, torch.from_numpy(q16.view(np.int16)).cuda(), sbd, Sd, codes, norms, signs,
+                  gamma, out)
+    torch.cuda.synchronize()
+    picks = np.unique(np.concatenate([rng.integers(0, n, 120), np.arange(n - 40, n)]))
+    x16 = np.stack([synth.kv_host(SEED, 0, 0, 0, int(k // T), d, int(k % T), 1)[0] for k in picks])
+    S64 = S16.astype(np.float64)
+    oc, on, osg, og, proj = oracle.qjl_encode(x16, bits, sb, S64)
+    gc = oracle.unpack_rows(codes[picks].cpu().numpy(), d, bits)
+    same = np.all(gc == oc, axis=1) & (norms[picks].cpu().numpy().view(np.uint16) == on)
+    assert (~same).sum() <= 2
+    gg = gamma[picks].cpu().numpy().view(np.float16).astype(np.float64)
+    assert np.all(np.abs(gg[same] - og[same]) <= 2.0 ** -10 * og[same] + 1e-7)
+    gbits = np.unpackbits(signs[picks].cpu().numpy(), axis=1, bitorder="little").astype(bool)
+    obits = np.unpackbits(osg, axis=1, bitorder="little").astype(bool)
+    near = np.abs(proj) < 1e-4 * np.linalg.norm(S64, axis=1)[None, :] * og[:, None]
+    assert not ((gbits != obits) & ~near & same[:, None]).any()
+    R = oracle.rotation(d, sb)
+    c, _ = oracle.codebook(d, bits)
+    n16 = oracle.halves_to_double(on)
+    g16 = np.float16(og).astype(np.float64)
+    got = out[:, picks].cpu().numpy()
+    for g in range(G):
+        q64 = oracle.halves_to_double(q16[g])
+        want = oracle.qjl_estimate(q64, oc, n16, g16, osg, S64, R, c)
+        rq = R @ q64
+        qjl_scale = n16 * math.sqrt(math.pi / 2) / d * g16 * np.abs(S64 @ rq).sum()
+        scale = n16 * (np.abs(rq) @ np.abs(c[oc]).T) + qjl_scale
+        err = np.abs(got[g] - want)
+        assert np.all(err[same] <= 1e-5 * scale[same] + 2.0 ** -10 * qjl_scale[same])
