@@ -541,8 +541,9 @@ def main():
                          "workload shapes, timed and reported on a line of its own")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              "(the path shards by KV head with no exchange; see DESIGN.md)", file=sys.stderr)
+        print(f"bench.py: runs on one GPU only; --gpus {args.gpus} is not supported (across "
+              "GPUs the path would shard by KV head, with no exchange between them)",
+              file=sys.stderr)
         sys.exit(2)
 
     if args.workload != "llama8b-32k":
