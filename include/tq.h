@@ -226,8 +226,9 @@ tq_status tq_prefill_attn(const tq_kv_cache* c, tq_codebook cbk, tq_codebook cbv
 /* ------------------------------------------------------------------ QJL -- */
 
 /* The method's second stage, the 1-bit residual sketch of keys ("We Built
- * ...", "Why not both stages?": a 1-bit residual correction for unbiased
- * inner products; that page skips it in attention).  For each key x with
+ * ...", "Why not both stages?": a one-bit-per-coordinate correction of the
+ * residual that makes inner-product estimates unbiased; that page skips it in
+ * attention).  For each key x with
  * stage-1 codes (from tq_encode, row layout) the residual in the rotated unit
  * domain is r = R x / ||x|| - c[codes]; the sketch is gamma = fp16(||r||)
  * and d sign bits of S r, bit i set iff (S r)_i >= 0 (LSB first, d/8 bytes).

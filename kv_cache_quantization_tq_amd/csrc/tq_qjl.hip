@@ -2,7 +2,8 @@
  * gfx950 kernels of the QJL stage: the 1-bit residual sketch of keys and the
  * inner-product estimate that uses it ("We Built a Python Library That Cuts
  * LLM Memory Usage by 80%", "Why not both stages?": the method's second
- * stage adds a 1-bit residual correction for unbiased inner products).
+ * stage, one bit per coordinate of the residual, so that inner-product
+ * estimates are unbiased).
  *
  * For a key x with stage-1 codes (tq_encode) the residual in the rotated unit
  * domain is r = R x / ||x|| - c[codes]; its sketch is gamma = fp16(||r||) and

@@ -392,8 +392,9 @@ void orc_attention_sparse(const double* q, int G, const double* K, const double*
 /* ------------------------------------------------------------------ QJL -- */
 
 /* Stage 2 of the method ("We Built a Python Library That Cuts LLM Memory
- * Usage by 80%", "Why not both stages?": a 1-bit residual correction for
- * unbiased inner products, which that library skips).  The page gives no
+ * Usage by 80%", "Why not both stages?": a second stage of one bit per
+ * coordinate for the residual, making inner-product estimates unbiased,
+ * which that library skips).  The page gives no
  * more; the reading here is the quantized Johnson-Lindenstrauss sketch of the
  * stage-1 residual of a key, in the rotated unit domain:
  *   r = R x / ||x|| - c[codes],   gamma = ||r||,
