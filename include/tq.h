@@ -235,8 +235,11 @@ tq_status tq_prefill_attn(const tq_kv_cache* c, tq_codebook cbk, tq_codebook cbv
  * x, x_stride, sign_bits: as tq_encode (x 16-byte aligned, stride % 8 == 0).
  * S:     device fp16 [d][d] row-major, 16-byte aligned: the caller's draw of
  *        i.i.d. N(0,1) entries (fixed per layer, like the sign bits).
- * codes: device, the keys' tq_encode rows [n][d*bits/8].
- * signs: device [n][d/8], 4-byte aligned.  gamma: device fp16 [n].
+ * codes: device, the keys' tq_encode rows [n][d*bits/8], 8-byte aligned
+ *        (as tq_encode requires).
+ * signs: device [n][d/8], 4-byte aligned (16-byte alignment lets a key's
+ *        sign row go out in vector stores).  gamma: device fp16 [n].
+ * Misaligned pointers or a bad stride: TQ_ERR_ARG before any device work.
  * The codebook gives d and bits.  n == 0 is a no-op. */
 tq_status tq_qjl_encode(tq_codebook cb, const uint16_t* x, int64_t n, int64_t x_stride,
                         const uint8_t* sign_bits, const uint16_t* S, const uint8_t* codes,

@@ -431,7 +431,7 @@ extern "C" tq_status tq_qjl_encode(tq_codebook cb, const uint16_t* x, int64_t n,
   const int d = cb->d;
   if (!x || !sign_bits || !S || !codes || !signs || !gamma) return TQ_ERR_ARG;
   if (x_stride < d || x_stride % 8 != 0 || !aligned(x, 16) || !aligned(S, 16) ||
-      !aligned(signs, 4) || !aligned(gamma, 2))
+      !aligned(codes, 8) || !aligned(signs, 4) || !aligned(gamma, 2))
     return TQ_ERR_ARG;
   return tq_launch_qjl_encode(cb, x, n, x_stride, sign_bits, S, codes, signs, gamma,
                               (hipStream_t)stream);

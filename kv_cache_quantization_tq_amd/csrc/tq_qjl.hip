@@ -12,7 +12,8 @@
  *   n16 * ( <R q, c[codes]> + sqrt(pi/2) / d * gamma * <S R q, z> ).
  *
  * qjl_encode_kernel: a wave sketches 16 keys at a time (S staged in LDS
- * per block for d <= 128).  Lane (n, kq) holds
+ * per block for d <= 128; the two cross-lane stages of the transform and
+ * the gathering of sign nibbles use the permlane swaps, not LDS).  Lane (n, kq) holds
  * coordinates 32 s + 8 kq + 0..7 of key n, so the residual it computes is
  * exactly its slice of the B operand of S R^T on the matrix cores
  * (v_mfma_f32_16x16x32_f16, r split into two fp16 parts; S is exact in fp16).
@@ -21,7 +22,10 @@
  * qjl_scores_kernel: 16 keys per wave on the matrix cores, like the decode's
  * scores: A = the keys' fp16 levels (plus their fp16 remainders against
  * q 2^-11) and their signs as +-1, B = the group's rotated queries and their
- * projections split into two fp16 parts (columns 0..7 and 8..15).
+ * projections split into two fp16 parts (columns 0..7 and 8..15).  A lane
+ * takes a contiguous quarter of a key's coordinates, so a tile's codes and
+ * signs arrive in a few wide loads, and the next tile's are in flight while
+ * one is scored.
  */
 #include <hip/hip_runtime.h>
 
@@ -42,6 +46,7 @@ struct QjlEncArgs {
   const uint8_t* codes;
   uint8_t* signs;
   uint16_t* gamma;
+  int vec_signs; /* signs 16-byte aligned: a key's sign row goes out in vector stores */
   float levels[16];
 };
 
@@ -56,16 +61,6 @@ __device__ inline float rows_sum(float v) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-/* 8 consecutive B-bit codes starting at a byte boundary (B bytes, read as
- * bytes: the rows are only byte-aligned for B = 3). */
-template <int B>
-__device__ inline uint32_t codes8(const uint8_t* p) {
-  uint32_t w = 0;
-#pragma unroll
-  for (int k = 0; k < B; ++k) w |= (uint32_t)p[k] << (8 * k);
-  return w;
-}
-
 /* S in LDS (rows padded against bank conflicts) for d <= 128; 256-dim heads
  * read it through the caches */
 template <int D>
@@ -75,22 +70,61 @@ struct SLds {
   static constexpr int HALFS = ON ? D * P : 8;
 };
 
+/* Exchange with the lane 16 (X = 16) or 32 (X = 32) places away, as one
+ * butterfly stage: the lower lane of each pair gets own + other, the upper
+ * one other - own.  The permlane swaps hand every lane both values of its
+ * pair ({lower, upper}) on the VALU, with no LDS round trip. */
+template <int X>
+__device__ inline float xbutterfly(float v, float sg) {
+  const uint32_t u = __float_as_uint(v);
+  const auto p = X == 16 ? __builtin_amdgcn_permlane16_swap(u, u, false, false)
+                         : __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(p[0]) + sg * __uint_as_float(p[1]);
+}
+
+/* One wave's 16 keys: lane (n, kq) holds key n's fp16
+ * coordinates 32 s + 8 kq + 0..7 and their 8 codes each. */
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 template <int D, int B>
-__global__ void __launch_bounds__(256) qjl_encode_kernel(QjlEncArgs a) {
+struct EncSlot {
+  u32x4 xw[D / 32];
+  uint32_t cw[D / 32];
+};
+
+/* The 8 B-bit codes of coordinates 32 s + 8 kq + 0..7: B bytes at byte
+ * 4 B s + B kq of the row, read as the aligned words that hold them (rows
+ * are multiples of 8 bytes from an 8-byte aligned base, so a second word is
+ * read only when the bytes straddle two, and it lies inside the row). */
+template <int B>
+__device__ inline uint32_t enc_codes(const uint8_t* row, int off) {
+  const uint32_t* w = (const uint32_t*)(row + (off & ~3));
+  const uint32_t sh = (uint32_t)(off & 3) * 8u;
+  if constexpr (B == 4)
+    return w[0];
+  else if constexpr (B == 2)
+    return w[0] >> sh;
+  else
+    return (off & 3) + 3 > 4 ? __builtin_amdgcn_alignbit(w[1], w[0], sh) : w[0] >> sh;
+}
+
+template <int D, int B>
+__device__ inline void enc_load(EncSlot<D, B>& r, const QjlEncArgs& a, int64_t v0, int n, int kq) {
+  const int64_t v = v0 + n < a.n ? v0 + n : a.n - 1; /* ragged tail: the last key again */
+  const uint8_t* row = a.codes + v * (D * B / 8);
+#pragma unroll
+  for (int s = 0; s < D / 32; ++s) {
+    r.xw[s] = __builtin_nontemporal_load((const u32x4*)(a.x + v * a.stride + 32 * s + 8 * kq));
+    r.cw[s] = enc_codes<B>(row, (32 * s + 8 * kq) * B / 8);
+  }
+}
+
+/* Sketch the 16 keys v0 .. v0 + 15 held in r. */
+template <int D, int B>
+__device__ inline void enc_keys(const EncSlot<D, B>& r, const QjlEncArgs& a, const _Float16* sl,
+                                int64_t v0, int lane, int n, int kq) {
   constexpr int KS = D / 32;
   using SL = SLds<D>;
-  __shared__ __align__(16) _Float16 sl[SL::HALFS];
-  const int lane = threadIdx.x % 64, n = lane % 16, kq = lane / 16;
-  if constexpr (SL::ON) {
-    for (int t = threadIdx.x; t < D * D / 8; t += blockDim.x) {
-      const int r = t / (D / 8), c = t % (D / 8);
-      *(uint4*)(sl + r * SL::P + 8 * c) = *(const uint4*)(a.S + r * D + 8 * c);
-    }
-    __syncthreads();
-  }
-  /* each wave sketches groups of 16 keys, striding over the grid */
-  for (int64_t v0 = ((int64_t)blockIdx.x * 4 + threadIdx.x / 64) * 16; v0 < a.n;
-       v0 += (int64_t)gridDim.x * 64) {
   const int64_t v = v0 + n;
   const bool live = v < a.n;
   /* x slice, sign flips D, squares for the norm */
@@ -99,9 +133,7 @@ __global__ void __launch_bounds__(256) qjl_encode_kernel(QjlEncArgs a) {
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
     const int i0 = 32 * s + 8 * kq;
-    uint4 w = make_uint4(0, 0, 0, 0);
-    if (live) w = *(const uint4*)(a.x + v * a.stride + i0);
-    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+    const uint32_t ww[4] = {r.xw[s][0], r.xw[s][1], r.xw[s][2], r.xw[s][3]};
     const uint32_t flips = a.sign_bits[i0 >> 3];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -123,15 +155,13 @@ __global__ void __launch_bounds__(256) qjl_encode_kernel(QjlEncArgs a) {
           y[s][j] = p + q;
           y[s][j | h] = p - q;
         }
-#pragma unroll
-  for (int h = 16; h <= 32; h <<= 1)
+  {
+    const float sg16 = (lane & 16) ? -1.0f : 1.0f, sg32 = (lane & 32) ? -1.0f : 1.0f;
 #pragma unroll
     for (int s = 0; s < KS; ++s)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float o = __shfl_xor(y[s][j], h);
-        y[s][j] = (lane & h) ? o - y[s][j] : y[s][j] + o;
-      }
+      for (int j = 0; j < 8; ++j) y[s][j] = xbutterfly<32>(xbutterfly<16>(y[s][j], sg16), sg32);
+  }
 #pragma unroll
   for (int h = 1; h < KS; h <<= 1)
 #pragma unroll
@@ -145,27 +175,25 @@ __global__ void __launch_bounds__(256) qjl_encode_kernel(QjlEncArgs a) {
         }
   /* residual in the rotated unit domain: y / (sqrt(d) ||x||) - c[code] */
   const float scale = ss > 0.0f ? 1.0f / (sqrtf((float)D) * sqrtf(ss)) : 0.0f;
-  const uint8_t* row = a.codes + (live ? v : 0) * (D * B / 8);
   float g2 = 0.0f;
   half8 rhi[KS], rlo[KS];
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
-    /* the 8 codes of coordinates 32 s + 8 kq + 0..7: B bytes of the row */
-    const uint32_t cw = live ? codes8<B>(row + (32 * s + 8 * kq) * B / 8) : 0u;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const float r = live ? y[s][j] * scale - a.levels[(cw >> (B * j)) & ((1u << B) - 1)] : 0.0f;
-      g2 += r * r;
-      const _Float16 hi = (_Float16)r;
+      const float rr = y[s][j] * scale - a.levels[(r.cw[s] >> (B * j)) & ((1u << B) - 1)];
+      g2 += rr * rr;
+      const _Float16 hi = (_Float16)rr;
       rhi[s][j] = hi;
-      rlo[s][j] = (_Float16)(r - (float)hi);
+      rlo[s][j] = (_Float16)(rr - (float)hi);
     }
   }
   g2 = rows_sum(g2);
   if (live && kq == 0) a.gamma[v] = f2h(sqrtf(g2));
   /* S r on the matrix cores: rows 16 mt .. 16 mt + 15 of S per product;
-   * lane (n, kq) gets projections 16 mt + 4 kq + 0..3 of key n */
-  uint32_t packed[D / 32]; /* the key's D sign bits, for lane kq == 0 */
+   * lane (n, kq) gets projections 16 mt + 4 kq + 0..3 of key n, and the
+   * four nibbles of a key are joined by the same two swaps */
+  uint32_t packed[D / 32]; /* the key's D sign bits (every lane of the key) */
 #pragma unroll
   for (int mt = 0; mt < D / 16; ++mt) {
     floatx4 t = {0.f, 0.f, 0.f, 0.f};
@@ -179,16 +207,53 @@ __global__ void __launch_bounds__(256) qjl_encode_kernel(QjlEncArgs a) {
     uint32_t nib = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) nib |= (t[i] >= 0.0f ? 1u : 0u) << i;
-    const uint32_t n1 = __shfl_xor(nib, 16), n2 = __shfl_xor(nib, 32), n3 = __shfl_xor(nib, 48);
-    const uint32_t bits16 = nib | (n1 << 4) | (n2 << 8) | (n3 << 12);
+    const auto p16 = __builtin_amdgcn_permlane16_swap(nib, nib, false, false);
+    const uint32_t byte = p16[0] | (p16[1] << 4);
+    const auto p32 = __builtin_amdgcn_permlane32_swap(byte, byte, false, false);
+    const uint32_t bits16 = p32[0] | (p32[1] << 8);
     if (mt & 1) packed[mt / 2] |= bits16 << 16;
     else packed[mt / 2] = bits16;
   }
   if (live && kq == 0) {
-    uint32_t* dst = (uint32_t*)(a.signs + v * (D / 8));
+    uint8_t* dst = a.signs + v * (D / 8);
+    if (a.vec_signs) {
+      if constexpr (D == 64) {
+        *(uint2*)dst = make_uint2(packed[0], packed[1]);
+      } else {
 #pragma unroll
-    for (int k = 0; k < D / 32; ++k) dst[k] = packed[k];
+        for (int k = 0; k < D / 128; ++k)
+          ((uint4*)dst)[k] = make_uint4(packed[4 * k], packed[4 * k + 1], packed[4 * k + 2],
+                                        packed[4 * k + 3]);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < D / 32; ++k) ((uint32_t*)dst)[k] = packed[k];
+    }
   }
+}
+
+template <int D, int B>
+__global__ void __launch_bounds__(256) qjl_encode_kernel(QjlEncArgs a) {
+  using SL = SLds<D>;
+  __shared__ __align__(16) _Float16 sl[SL::HALFS];
+  const int lane = threadIdx.x % 64, n = lane % 16, kq = lane / 16;
+  if constexpr (SL::ON) {
+    for (int t = threadIdx.x; t < D * D / 8; t += blockDim.x) {
+      const int r = t / (D / 8), c = t % (D / 8);
+      *(uint4*)(sl + r * SL::P + 8 * c) = *(const uint4*)(a.S + r * D + 8 * c);
+    }
+    __syncthreads();
+  }
+  /* each wave sketches groups of 16 keys, striding over the grid (a second
+   * register slot to load the next group meanwhile would cost the second
+   * wave per SIMD, which hides more) */
+  const int64_t stride = (int64_t)gridDim.x * 64;
+  int64_t v0 = ((int64_t)blockIdx.x * 4 + threadIdx.x / 64) * 16;
+  if (v0 >= a.n) return;
+  for (; v0 < a.n; v0 += stride) {
+    EncSlot<D, B> ra;
+    enc_load<D, B>(ra, a, v0, n, kq);
+    enc_keys<D, B>(ra, a, sl, v0, lane, n, kq);
   }
 }
 
@@ -203,8 +268,11 @@ struct QjlScoreArgs {
   const uint16_t* gamma;
   int64_t T;
   float* out; /* [G][T] */
+  int vec_out; /* T % 4 == 0 and out 16-byte aligned: rows of 4 keys go out as one store */
   float levels[16];
 };
+
+typedef float floatv4 __attribute__((ext_vector_type(4)));
 
 /* Row reduction partner: the value of the lane 8 places along in the
  * 16-lane row. */
@@ -212,19 +280,164 @@ __device__ inline float ror8(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));
 }
 
+/* A lane's share of one 16-key tile.  Lane (n, kq) takes key k0 + n's
+ * coordinates kq d/4 + 0 .. d/4 - 1 (the dot products do not depend on how
+ * coordinates are dealt out, as long as A and B agree), so its codes and
+ * sign bits are one contiguous slice of the key's rows; plus the norms and
+ * gammas of keys k0 + 4 kq + 0..3, the rows its output column covers. */
+template <int D, int B>
+struct KeySlice {
+  static constexpr int KS = D / 32;          /* matrix-core steps per tile */
+  static constexpr int CB = KS * B;          /* code bytes per lane */
+  static constexpr int CW = (CB + 3) / 4;
+  static constexpr int ZW = (KS + 3) / 4;    /* KS sign bytes */
+  uint32_t cw[CW];
+  uint32_t zw[ZW];
+  uint16_t nm[4], gm[4];
+};
+
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+/* Streamed once: non-temporal loads.  Keys past the end are clamped to the
+ * last one (their rows of the product are never stored). */
+template <int D, int B>
+__device__ inline void load_slice(KeySlice<D, B>& r, const QjlScoreArgs& a, int64_t k0, int n,
+                                  int kq) {
+  typedef KeySlice<D, B> KSl;
+  const int64_t last = a.T - 1;
+  const int64_t key = k0 + n < last ? k0 + n : last;
+  /* rows are multiples of 8 bytes from an 8-byte aligned base */
+  const uint8_t* cp = a.codes + key * (D * B / 8) + kq * KSl::CB;
+  if constexpr (KSl::CB % 8 == 0) {
+#pragma unroll
+    for (int k = 0; k < KSl::CB / 8; ++k) {
+      const u32x2 w = __builtin_nontemporal_load((const u32x2*)cp + k);
+      r.cw[2 * k] = w[0];
+      r.cw[2 * k + 1] = w[1];
+    }
+  } else if constexpr (KSl::CB % 4 == 0) {
+#pragma unroll
+    for (int k = 0; k < KSl::CB / 4; ++k)
+      r.cw[k] = __builtin_nontemporal_load((const uint32_t*)cp + k);
+  } else { /* d = 64, 3 bits: 6 bytes at a 2-byte boundary */
+    const uint16_t* h = (const uint16_t*)cp;
+    r.cw[0] = (uint32_t)__builtin_nontemporal_load(h) |
+              ((uint32_t)__builtin_nontemporal_load(h + 1) << 16);
+    r.cw[1] = __builtin_nontemporal_load(h + 2);
+  }
+  const uint8_t* zp = a.signs + key * (D / 8) + kq * KSl::KS;
+  if constexpr (KSl::KS == 2)
+    r.zw[0] = __builtin_nontemporal_load((const uint16_t*)zp);
+  else
+#pragma unroll
+    for (int k = 0; k < KSl::ZW; ++k) r.zw[k] = __builtin_nontemporal_load((const uint32_t*)zp + k);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t kk = k0 + 4 * kq + i < last ? k0 + 4 * kq + i : last;
+    r.nm[i] = __builtin_nontemporal_load(a.norms + kk);
+    r.gm[i] = __builtin_nontemporal_load(a.gamma + kk);
+  }
+}
+
+/* The 8 B-bit codes of matrix-core step s from a lane's slice. */
+template <int D, int B>
+__device__ inline uint32_t step_codes(const KeySlice<D, B>& r, int s) {
+  if constexpr (B == 4) {
+    return r.cw[s];
+  } else if constexpr (B == 2) {
+    return (r.cw[s / 2] >> (16 * (s & 1))) & 0xFFFFu;
+  } else {
+    const int bit = 24 * s, w = bit / 32, sh = bit % 32;
+    return sh + 24 > 32 ? __builtin_amdgcn_alignbit(r.cw[w + 1], r.cw[w], (uint32_t)sh)
+                        : r.cw[w] >> sh;
+  }
+}
+
+/* LDS tables of the scores kernel.  plev: for each pair of B-bit codes
+ * (first code in the low bits) the words {fp16 c0 | fp16 c1 << 16} and
+ * {fp16 r0 | fp16 r1 << 16}, r = fp16((c - fp16 c) 2^11), in 4 copies
+ * (entry 4 p + lane % 4); zpm: for each byte of sign bits the 8 fp16 values
+ * +-1 (bit j set -> +1 in half j). */
+template <int B>
+struct ScoreLds {
+  static constexpr int PAIRS = 1 << (2 * B);
+  uint2 plev[PAIRS * 4];
+  uint4 zpm[256];
+};
+
+/* Estimates for one tile of 16 keys at k0 from the lane's slice r.  Step s
+ * covers the lane's coordinates 8 s + 0..7: the levels in two products
+ * (A = {c0, c1, r0, r1, c2, c3, r2, r3} fp16 straight from two table words,
+ * B = the query parts in the same order), the signs in one. */
+template <int D, int B>
+__device__ inline void score_tile(const KeySlice<D, B>& r, const half8 (&bv)[2 * (D / 32)],
+                                  const half8 (&bs)[D / 32], const ScoreLds<B>& tb,
+                                  uint32_t cpy, const QjlScoreArgs& a, int64_t k0, int n, int kq) {
+  constexpr int KS = D / 32;
+  floatx4 c1 = {0.f, 0.f, 0.f, 0.f}, c2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    const uint32_t cw = step_codes<D, B>(r, s);
+    const uint32_t zb = (r.zw[s / 4] >> (8 * (s % 4))) & 0xFFu;
+    const uint4 z = tb.zpm[zb];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint2 e0 = tb.plev[((cw >> (4 * B * h)) & ((1u << (2 * B)) - 1)) * 4 + cpy];
+      const uint2 e1 = tb.plev[((cw >> (4 * B * h + 2 * B)) & ((1u << (2 * B)) - 1)) * 4 + cpy];
+      const uint4 w = {e0.x, e0.y, e1.x, e1.y};
+      c1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, w), bv[2 * s + h], c1,
+                                                  0, 0, 0);
+    }
+    c2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, z), bs[s], c2, 0, 0, 0);
+  }
+  /* lane (n, kq) holds keys k0 + 4 kq + 0..3 of column n; join the fp16
+   * parts (column n + 8) into columns n < 8 */
+  floatv4 o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float m1 = c1[i] + ror8(c1[i]), m2 = c2[i] + ror8(c2[i]);
+    o[i] = h2f(r.nm[i]) * (m1 + h2f(r.gm[i]) * m2);
+  }
+  if (n < a.G) {
+    const int64_t kb = k0 + 4 * kq;
+    float* dst = a.out + n * a.T + kb;
+    if (a.vec_out && kb + 4 <= a.T) {
+      __builtin_nontemporal_store(o, (floatv4*)dst);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (kb + i < a.T) __builtin_nontemporal_store(o[i], dst + i);
+    }
+  }
+}
+
 template <int D, int B>
 __global__ void __launch_bounds__(256) qjl_scores_kernel(QjlScoreArgs a) {
   constexpr int KS = D / 32;
   __shared__ float rq[8][D];   /* R q */
   __shared__ float sq[8][D];   /* S R q * sqrt(pi/2) / d */
-  __shared__ uint32_t lev[64]; /* level c as {fp16 c, fp16 (c - fp16 c) 2^11}, 4 copies */
-  const int tid = threadIdx.x, lane = tid % 64, n = lane % 16, kq = lane / 16;
-  if (tid < 64) {
-    const float c = a.levels[tid / 4];
-    const _Float16 h = (_Float16)c;
-    const _Float16 l = (_Float16)((c - (float)h) * 2048.0f);
-    lev[tid] = (uint32_t)__builtin_bit_cast(uint16_t, h) |
-               ((uint32_t)__builtin_bit_cast(uint16_t, l) << 16);
+  __shared__ ScoreLds<B> tb;
+  const int tid = threadIdx.x, lane = tid % 64, n = lane % 16, kq = lane / 16, wave = tid / 64;
+  for (int e = tid; e < ScoreLds<B>::PAIRS * 4; e += blockDim.x) {
+    const int p = e / 4;
+    uint32_t hw = 0, lw = 0;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const float c = a.levels[(p >> (B * t)) & ((1 << B) - 1)];
+      const _Float16 h = (_Float16)c;
+      const _Float16 l = (_Float16)((c - (float)h) * 2048.0f);
+      hw |= (uint32_t)__builtin_bit_cast(uint16_t, h) << (16 * t);
+      lw |= (uint32_t)__builtin_bit_cast(uint16_t, l) << (16 * t);
+    }
+    tb.plev[e] = make_uint2(hw, lw);
+  }
+  {
+    uint32_t w[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      w[k] = (((tid >> (2 * k)) & 1) ? 0x3C00u : 0xBC00u) |
+             ((((tid >> (2 * k + 1)) & 1) ? 0x3C00u : 0xBC00u) << 16);
+    tb.zpm[tid] = make_uint4(w[0], w[1], w[2], w[3]);
   }
   /* R q = H D q / sqrt(d), one thread per (query, coordinate), by a plain
    * O(d log d) pass through LDS */
@@ -249,17 +462,36 @@ __global__ void __launch_bounds__(256) qjl_scores_kernel(QjlScoreArgs a) {
   }
   for (int t = tid; t < a.G * D; t += blockDim.x) rq[t / D][t % D] *= 1.0f / sqrtf((float)D);
   __syncthreads();
-  for (int t = tid; t < a.G * D; t += blockDim.x) {
-    const int g = t / D, i = t % D;
-    float acc = 0.0f;
-    for (int j = 0; j < D; ++j) acc += h2f(a.S[i * D + j]) * rq[g][j];
-    sq[g][i] = acc * (kSqrtHalfPi / D);
+  /* S R q on the matrix cores: 16-row tiles of S (exact in fp16; lane
+   * (m, kq) supplies row i0 + m, columns 32 s + 8 kq + 0..7) times the
+   * rotated queries in two fp16 parts (lane (g, kq) supplies query g's
+   * coordinates 32 s + 8 kq + 0..7), row tiles dealt out to the waves */
+  for (int i0 = 16 * wave; i0 < D; i0 += 64) {
+    floatx4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const uint16_t* srow = a.S + (i0 + n) * D + 32 * s + 8 * kq;
+      half8 av, bh, bm;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        av[j] = __builtin_bit_cast(_Float16, srow[j]);
+        const float r = n < a.G ? rq[n & 7][32 * s + 8 * kq + j] : 0.0f;
+        bh[j] = (_Float16)r;
+        bm[j] = (_Float16)(r - (float)bh[j]);
+      }
+      c = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bh, c, 0, 0, 0);
+      c = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bm, c, 0, 0, 0);
+    }
+    /* lane (g, kq) holds rows i0 + 4 kq + 0..3 of query g */
+    if (n < a.G)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sq[n][i0 + 4 * kq + i] = c[i] * (kSqrtHalfPi / D);
   }
   __syncthreads();
-  /* B operands, lane (n, kq), coordinates 32 s + 8 kq + 0..7: columns 0..7
+  /* B operands, lane (n, kq), coordinates kq d/4 + 8 s + 0..7: columns 0..7
    * the fp16 parts of query n, 8..15 their fp16 remainders (levels and sign
    * products); for the level remainders fp16(R q 2^-11) in columns 0..7 */
-  half8 bl[KS], br[KS], bs[KS];
+  half8 bv[2 * KS], bs[KS];
   {
     const int g = n & 7;
     const bool hiCol = n < 8, ok = g < a.G;
@@ -267,72 +499,55 @@ __global__ void __launch_bounds__(256) qjl_scores_kernel(QjlScoreArgs a) {
     for (int s = 0; s < KS; ++s)
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const int i = 32 * s + 8 * kq + j;
+        const int i = kq * (D / 4) + 8 * s + j;
         const float r = ok ? rq[g][i] : 0.0f, z = ok ? sq[g][i] : 0.0f;
         const _Float16 rh = (_Float16)r, zh = (_Float16)z;
-        bl[s][j] = hiCol ? rh : (_Float16)(r - (float)rh);
-        br[s][j] = hiCol ? (_Float16)(r * 0x1p-11f) : (_Float16)0.0f;
+        /* level products: coordinates j = 4 h + 2 u + t sit at half
+         * 4 u + t (level part) and 4 u + 2 + t (remainder part) of bv[2 s + h] */
+        const int h = j / 4, u = (j / 2) % 2, t = j % 2;
+        bv[2 * s + h][4 * u + t] = hiCol ? rh : (_Float16)(r - (float)rh);
+        bv[2 * s + h][4 * u + 2 + t] = hiCol ? (_Float16)(r * 0x1p-11f) : (_Float16)0.0f;
         bs[s][j] = hiCol ? zh : (_Float16)(z - (float)zh);
       }
   }
-  /* 16-key tiles, one per wave at a time: lane (m = n, kq) supplies key
-   * k0 + m's coordinates 32 s + 8 kq + 0..7 of the A operands (levels, level
-   * remainders, signs as +-1) */
-  const int wave = tid / 64;
+  /* 16-key tiles striding over the grid, two register slots: the next
+   * tile's loads are in flight while the current one is scored */
   const uint32_t cpy = (uint32_t)lane & 3u;
-  const int64_t ntile = (a.T + 15) / 16;
-  for (int64_t tile = (int64_t)blockIdx.x * 4 + wave; tile < ntile; tile += (int64_t)gridDim.x * 4) {
-    const int64_t k0 = tile * 16, key = k0 + n;
-    const bool live = key < a.T;
-    const uint8_t* row = a.codes + (live ? key : 0) * (D * B / 8);
-    const uint8_t* sg = a.signs + (live ? key : 0) * (D / 8);
-    floatx4 c1 = {0.f, 0.f, 0.f, 0.f}, c2 = {0.f, 0.f, 0.f, 0.f};
-    /* the key's sign bits in one go (d/8 bytes, 4-byte aligned) */
-    uint32_t zw[D / 32];
-#pragma unroll
-    for (int k = 0; k < D / 32; ++k) zw[k] = live ? ((const uint32_t*)sg)[k] : 0u;
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      /* the 8 codes at byte (32 s + 8 kq) B / 8 from aligned words (rows are
-       * a multiple of 4 bytes, so the word holding the last byte ends inside
-       * the row) */
-      uint32_t cw = 0;
-      if (live) {
-        const int off = (32 * s + 8 * kq) * B / 8;
-        const uint32_t* w = (const uint32_t*)(row + (off & ~3));
-        if constexpr (B == 3)
-          cw = (off & 3) + 3 > 4 ? __builtin_amdgcn_alignbit(w[1], w[0], (uint32_t)(off & 3) * 8u)
-                                 : w[0] >> ((off & 3) * 8);
-        else
-          cw = w[0] >> ((off & 3) * 8);
-      }
-      const uint32_t zb = (zw[s] >> (8 * kq)) & 0xFFu;
-      uint32_t e[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) e[j] = lev[((cw >> (B * j)) & ((1u << B) - 1)) * 4 + cpy];
-      half8 ah, al, az;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        ah[j] = __builtin_bit_cast(_Float16, (uint16_t)(e[j] & 0xFFFFu));
-        al[j] = __builtin_bit_cast(_Float16, (uint16_t)(e[j] >> 16));
-        az[j] = ((zb >> j) & 1) ? (_Float16)1.0f : (_Float16)-1.0f;
-      }
-      c1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bl[s], c1, 0, 0, 0);
-      c1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, br[s], c1, 0, 0, 0);
-      c2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(az, bs[s], c2, 0, 0, 0);
-    }
-    /* lane (n, kq) holds keys k0 + 4 kq + i of column n; join the fp16
-     * parts (column n + 8) into columns n < 8 */
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float m1 = c1[i] + ror8(c1[i]), m2 = c2[i] + ror8(c2[i]);
-      const int64_t kk = k0 + 4 * kq + i;
-      if (n < a.G && kk < a.T) {
-        const float n16 = h2f(a.norms[kk]), g16 = h2f(a.gamma[kk]);
-        a.out[n * a.T + kk] = n16 * (m1 + g16 * m2);
-      }
-    }
+  const int64_t ntile = (a.T + 15) / 16, stride = (int64_t)gridDim.x * 4;
+  int64_t t = (int64_t)blockIdx.x * 4 + wave;
+  if (t >= ntile) return;
+  const int64_t cnt = (ntile - 1 - t) / stride + 1;
+  KeySlice<D, B> ra, rb;
+  load_slice<D, B>(ra, a, t * 16, n, kq);
+  for (int64_t k = 0; k + 2 <= cnt; k += 2) {
+    load_slice<D, B>(rb, a, (t + stride) * 16, n, kq);
+    score_tile<D, B>(ra, bv, bs, tb, cpy, a, t * 16, n, kq);
+    t += stride;
+    if (k + 2 < cnt) load_slice<D, B>(ra, a, (t + stride) * 16, n, kq);
+    score_tile<D, B>(rb, bv, bs, tb, cpy, a, t * 16, n, kq);
+    t += stride;
   }
+  if (cnt & 1) score_tile<D, B>(ra, bv, bs, tb, cpy, a, t * 16, n, kq);
+}
+
+/* Blocks of a scores instantiation the device holds at once (occupancy x
+ * CUs), looked up once per process; 1024 when no device answers. */
+template <int D, int B>
+int scores_resident_blocks() {
+  static int cached = 0;
+  if (cached == 0) {
+    int dev = 0, cus = 0, per = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, qjl_scores_kernel<D, B>, 256, 0) !=
+            hipSuccess ||
+        cus <= 0 || per <= 0) {
+      (void)hipGetLastError();
+      return 1024;
+    }
+    cached = cus * per;
+  }
+  return cached;
 }
 
 }  // namespace
@@ -350,6 +565,7 @@ tq_status tq_launch_qjl_encode(const tq_codebook_s* cb, const uint16_t* x, int64
   a.codes = codes;
   a.signs = signs;
   a.gamma = gamma;
+  a.vec_signs = ((uintptr_t)signs & 15) == 0;
   for (int k = 0; k < 16; ++k) a.levels[k] = k < (1 << cb->bits) ? cb->centroids[k] : 0.0f;
   int64_t blocks = (n + 63) / 64; /* 4 waves of 16 keys; capped, the waves then stride */
   if (blocks > 2048) blocks = 2048;
@@ -377,12 +593,17 @@ tq_status tq_launch_qjl_scores(const tq_codebook_s* cb, const uint16_t* q, int G
   a.gamma = gamma;
   a.T = T;
   a.out = out;
+  a.vec_out = T % 4 == 0 && ((uintptr_t)out & 15) == 0;
   for (int k = 0; k < 16; ++k) a.levels[k] = k < (1 << cb->bits) ? cb->centroids[k] : 0.0f;
-  int64_t blocks = (T + 63) / 64; /* 4 waves of 16 keys; capped, the waves then stride */
-  if (blocks > 4096) blocks = 4096;
+  /* 4 waves of 16 keys a block; at most one round of resident blocks, whose
+   * waves then stride (each block projects the queries once) */
+  const int64_t need = (T + 63) / 64;
 #define TQ_QS(DD, BB) \
-  if (cb->d == DD && cb->bits == BB) \
-    hipLaunchKernelGGL((qjl_scores_kernel<DD, BB>), dim3((unsigned)blocks), dim3(256), 0, s, a); else
+  if (cb->d == DD && cb->bits == BB) { \
+    const int64_t cap = scores_resident_blocks<DD, BB>(); \
+    hipLaunchKernelGGL((qjl_scores_kernel<DD, BB>), dim3((unsigned)(need < cap ? need : cap)), \
+                       dim3(256), 0, s, a); \
+  } else
   TQ_QS(64, 2) TQ_QS(64, 3) TQ_QS(64, 4) TQ_QS(128, 2) TQ_QS(128, 3) TQ_QS(128, 4)
   TQ_QS(256, 2) TQ_QS(256, 3) TQ_QS(256, 4) return TQ_ERR_UNSUPPORTED;
 #undef TQ_QS

@@ -7,6 +7,7 @@ whose stage-1 codes differ between the two sides (a coordinate within 1e-6
 of a decision threshold, where either code is correct) are left out of the
 sketch comparisons and counted; projections within a relative 1e-4 of zero
 may take either sign (fp32 against fp64 residuals)."""
+import ctypes
 import math
 
 import numpy as np
@@ -25,8 +26,13 @@ def _draw_S(rng, d):
     return rng.standard_normal((d, d)).astype(np.float16)
 
 
-@pytest.mark.parametrize("d,bits,n", [(128, 4, 300), (64, 2, 77), (256, 3, 130), (128, 3, 1000)])
-def test_qjl_parity(d, bits, n):
+@pytest.mark.parametrize("d,bits,n,G", [(128, 4, 300, 4), (64, 2, 77, 4), (256, 3, 130, 4),
+                                        (128, 3, 1000, 4), (64, 3, 45, 8), (256, 4, 64, 1),
+                                        (128, 2, 33, 8), (64, 4, 200, 2)])
+def test_qjl_parity(d, bits, n, G):
+    """Sketch and estimate against the oracle: every head dim and bit width,
+    1 to 8 queries, key counts with and without a whole number of 4-key rows
+    and 16-key tiles."""
     torch = require_gpu()
     rng = np.random.default_rng(d * 10 + bits)
     x16 = synth.kv_host(SEED, 0, 0, 0, 0, d, 0, n)
@@ -42,7 +48,6 @@ def test_qjl_parity(d, bits, n):
     gamma = torch.empty(n, dtype=torch.int16, device="cuda")
     tq.encode(cb, xd, sbd, codes, norms)
     tq.qjl_encode(cb, xd, sbd, Sd, codes, signs, gamma)
-    G = 4
     q16 = np.stack([synth.q_host(SEED, 0, 0, 0, g, d) for g in range(G)])
     qd = torch.from_numpy(q16.view(np.int16)).cuda()
     out = torch.empty((G, n), dtype=torch.float32, device="cuda")
@@ -138,3 +143,39 @@ def test_qjl_large_sampled():
         scale = n16 * (np.abs(rq) @ np.abs(c[oc]).T) + qjl_scale
         err = np.abs(got[g] - want)
         assert np.all(err[same] <= 1e-5 * scale[same] + 2.0 ** -10 * qjl_scale[same])
+
+
+def test_qjl_encode_alignment_checks():
+    """Misaligned codes (the kernel reads them as aligned words), x or S are
+    rejected on the host, before any device work; signs aligned to 4 but not
+    16 bytes take the per-word store path and match the aligned result."""
+    torch = require_gpu()
+    d, bits, n = 128, 4, 40
+    L = tq.lib()
+    vp = ctypes.c_void_p
+    cb = tq.Codebook(d, bits)
+    x = torch.empty((1, 1, n, d), dtype=torch.int16, device="cuda")
+    synth.kv_dev(SEED, 0, 0, x)
+    x = x.view(n, d)
+    sbd = torch.from_numpy(synth.sign_bits(SEED, 0, d)).cuda()
+    Sd = torch.from_numpy(_draw_S(np.random.default_rng(3), d).view(np.int16)).cuda()
+    codes = torch.empty((n + 1) * d * bits // 8, dtype=torch.uint8, device="cuda")
+    norms = torch.empty(n, dtype=torch.int16, device="cuda")
+    tq.encode(cb, x, sbd, codes[: n * d * bits // 8].view(n, -1), norms)
+    signs = torch.zeros(n * d // 8 + 16, dtype=torch.uint8, device="cuda")
+    gamma = torch.empty(n, dtype=torch.int16, device="cuda")
+
+    def call(xp, Sp, cp, sp):
+        return L.tq_qjl_encode(cb.handle, vp(xp), n, d, vp(sbd.data_ptr()), vp(Sp), vp(cp),
+                               vp(sp), vp(gamma.data_ptr()), None)
+
+    base = (x.data_ptr(), Sd.data_ptr(), codes.data_ptr(), signs.data_ptr())
+    assert call(base[0], base[1], base[2] + 4, base[3]) == 1
+    assert call(base[0] + 8, base[1], base[2], base[3]) == 1
+    assert call(base[0], base[1] + 8, base[2], base[3]) == 1
+    assert call(*base) == 0
+    torch.cuda.synchronize()
+    want = signs[: n * d // 8].clone()
+    assert call(base[0], base[1], base[2], base[3] + 4) == 0
+    torch.cuda.synchronize()
+    assert torch.equal(signs[4: 4 + n * d // 8], want)
