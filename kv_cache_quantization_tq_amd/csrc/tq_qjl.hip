@@ -122,24 +122,27 @@ __device__ inline void enc_load(EncSlot<D, B>& r, const QjlEncArgs& a, int64_t v
 /* Sketch the 16 keys v0 .. v0 + 15 held in r. */
 template <int D, int B>
 __device__ inline void enc_keys(const EncSlot<D, B>& r, const QjlEncArgs& a, const _Float16* sl,
-                                int64_t v0, int lane, int n, int kq) {
+                                const float2* plev, const uint32_t (&fm)[D / 32][4], int64_t v0,
+                                int lane, int n, int kq) {
   constexpr int KS = D / 32;
   using SL = SLds<D>;
   const int64_t v = v0 + n;
   const bool live = v < a.n;
-  /* x slice, sign flips D, squares for the norm */
+  /* x slice with the sign flips D (an xor of the fp16 sign bits), squares
+   * for the norm */
   float y[KS][8];
   float ss = 0.0f;
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
-    const int i0 = 32 * s + 8 * kq;
-    const uint32_t ww[4] = {r.xw[s][0], r.xw[s][1], r.xw[s][2], r.xw[s][3]};
-    const uint32_t flips = a.sign_bits[i0 >> 3];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      float f = h2f((uint16_t)(ww[j / 2] >> (16 * (j & 1))));
-      ss += f * f;
-      y[s][j] = ((flips >> j) & 1) ? -f : f;
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t hw = r.xw[s][w] ^ fm[s][w];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const float f = h2f((uint16_t)(hw >> (16 * t)));
+        ss += f * f;
+        y[s][2 * w + t] = f;
+      }
     }
   }
   ss = rows_sum(ss);
@@ -177,15 +180,21 @@ __device__ inline void enc_keys(const EncSlot<D, B>& r, const QjlEncArgs& a, con
   const float scale = ss > 0.0f ? 1.0f / (sqrtf((float)D) * sqrtf(ss)) : 0.0f;
   float g2 = 0.0f;
   half8 rhi[KS], rlo[KS];
+  const uint32_t cpy = (uint32_t)lane & 3u;
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float rr = y[s][j] * scale - a.levels[(r.cw[s] >> (B * j)) & ((1u << B) - 1)];
-      g2 += rr * rr;
-      const _Float16 hi = (_Float16)rr;
-      rhi[s][j] = hi;
-      rlo[s][j] = (_Float16)(rr - (float)hi);
+    for (int u = 0; u < 4; ++u) {
+      const float2 c = plev[((r.cw[s] >> (2 * B * u)) & ((1u << (2 * B)) - 1)) * 4 + cpy];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int j = 2 * u + t;
+        const float rr = y[s][j] * scale - (t ? c.y : c.x);
+        g2 += rr * rr;
+        const _Float16 hi = (_Float16)rr;
+        rhi[s][j] = hi;
+        rlo[s][j] = (_Float16)(rr - (float)hi);
+      }
     }
   }
   g2 = rows_sum(g2);
@@ -236,13 +245,31 @@ template <int D, int B>
 __global__ void __launch_bounds__(256) qjl_encode_kernel(QjlEncArgs a) {
   using SL = SLds<D>;
   __shared__ __align__(16) _Float16 sl[SL::HALFS];
+  /* the levels of each pair of codes (first code in the low bits), 4 copies
+   * (entry 4 p + lane % 4) */
+  __shared__ float2 plev[(1 << (2 * B)) * 4];
   const int lane = threadIdx.x % 64, n = lane % 16, kq = lane / 16;
+  for (int e = threadIdx.x; e < (1 << (2 * B)) * 4; e += blockDim.x) {
+    const int p = e / 4;
+    plev[e] = make_float2(a.levels[p & ((1 << B) - 1)], a.levels[p >> B]);
+  }
+  __syncthreads();
   if constexpr (SL::ON) {
     for (int t = threadIdx.x; t < D * D / 8; t += blockDim.x) {
       const int r = t / (D / 8), c = t % (D / 8);
       *(uint4*)(sl + r * SL::P + 8 * c) = *(const uint4*)(a.S + r * D + 8 * c);
     }
     __syncthreads();
+  }
+  /* the lane's sign flips: coordinate 32 s + 8 kq + 2 w + t flips the fp16
+   * sign bit 16 t + 15 of word w of slice s */
+  uint32_t fm[D / 32][4];
+#pragma unroll
+  for (int s = 0; s < D / 32; ++s) {
+    const uint32_t fb = a.sign_bits[(32 * s + 8 * kq) >> 3];
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      fm[s][w] = (((fb >> (2 * w)) & 1u) << 15) | (((fb >> (2 * w + 1)) & 1u) << 31);
   }
   /* each wave sketches groups of 16 keys, striding over the grid (a second
    * register slot to load the next group meanwhile would cost the second
@@ -253,7 +280,7 @@ __global__ void __launch_bounds__(256) qjl_encode_kernel(QjlEncArgs a) {
   for (; v0 < a.n; v0 += stride) {
     EncSlot<D, B> ra;
     enc_load<D, B>(ra, a, v0, n, kq);
-    enc_keys<D, B>(ra, a, sl, v0, lane, n, kq);
+    enc_keys<D, B>(ra, a, sl, plev, fm, v0, lane, n, kq);
   }
 }
 
