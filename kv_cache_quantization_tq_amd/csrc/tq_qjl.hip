@@ -11,14 +11,15 @@
  * projection is >= 0).  The estimate of <q, x> is
  *   n16 * ( <R q, c[codes]> + sqrt(pi/2) / d * gamma * <S R q, z> ).
  *
- * qjl_encode_kernel: a wave sketches 16 keys at a time (S staged in LDS
- * per block for d <= 128; the two cross-lane stages of the transform and
- * the gathering of sign nibbles use the permlane swaps, not LDS).  Lane (n, kq) holds
- * coordinates 32 s + 8 kq + 0..7 of key n, so the residual it computes is
- * exactly its slice of the B operand of S R^T on the matrix cores
- * (v_mfma_f32_16x16x32_f16, r split into two fp16 parts; S is exact in fp16).
- * The rotation is the butterfly Walsh-Hadamard transform: in-lane strides
- * 1, 2, 4 and >= 32, lane-xor 16 and 32 for strides 8 and 16.
+ * qjl_encode_kernel: a wave sketches 16 keys at a time.  For d <= 128 both
+ * products run on the matrix cores (v_mfma_f32_16x16x32_f16): the rotation
+ * as a row-reordered Hadamard matrix (exact in fp16, staged in LDS with S)
+ * times the sign-flipped fp16 keys, which leaves each lane a contiguous
+ * quarter of the rotated coordinates, and S r with the residual in two fp16
+ * parts (S is exact in fp16).  For d = 256 the rotation is the butterfly
+ * Walsh-Hadamard transform in registers (in-lane strides 1, 2, 4 and >= 32;
+ * strides 8 and 16 through the permlane swaps) and S is read through the
+ * caches.  Sign nibbles are joined by permlane swaps, not LDS.
  * qjl_scores_kernel: 16 keys per wave on the matrix cores, like the decode's
  * scores: A = the keys' fp16 levels (plus their fp16 remainders against
  * q 2^-11) and their signs as +-1, B = the group's rotated queries and their
@@ -85,6 +86,7 @@ __device__ inline float xbutterfly(float v, float sg) {
 /* One wave's 16 keys: lane (n, kq) holds key n's fp16
  * coordinates 32 s + 8 kq + 0..7 and their 8 codes each. */
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 template <int D, int B>
 struct EncSlot {
@@ -116,6 +118,57 @@ __device__ inline void enc_load(EncSlot<D, B>& r, const QjlEncArgs& a, int64_t v
   for (int s = 0; s < D / 32; ++s) {
     r.xw[s] = __builtin_nontemporal_load((const u32x4*)(a.x + v * a.stride + 32 * s + 8 * kq));
     r.cw[s] = enc_codes<B>(row, (32 * s + 8 * kq) * B / 8);
+  }
+}
+
+/* S r on the matrix cores for 16 keys (r in two fp16 parts, lane (n, kq)
+ * holding key n's coordinates col0 + cstep s + 0..7 in rhi[s], rlo[s]):
+ * rows 16 mt .. 16 mt + 15 of S per product; lane (n, kq) gets projections
+ * 16 mt + 4 kq + 0..3 of key n, and the four nibbles of a key are joined by
+ * the two permlane swaps; the key's sign row goes out from lane kq == 0. */
+template <int D>
+__device__ inline void enc_project(const half8 (&rhi)[D / 32], const half8 (&rlo)[D / 32],
+                                   const _Float16* sl, const QjlEncArgs& a, int col0, int cstep,
+                                   int64_t v, bool live, int n, int kq) {
+  constexpr int KS = D / 32;
+  using SL = SLds<D>;
+  uint32_t packed[D / 32]; /* the key's D sign bits (every lane of the key) */
+#pragma unroll
+  for (int mt = 0; mt < D / 16; ++mt) {
+    floatx4 t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const int col = col0 + cstep * s;
+      const half8 sa = SL::ON ? *(const half8*)(sl + (16 * mt + n) * SL::P + col)
+                              : *(const half8*)(a.S + (16 * mt + n) * D + col);
+      t = __builtin_amdgcn_mfma_f32_16x16x32_f16(sa, rhi[s], t, 0, 0, 0);
+      t = __builtin_amdgcn_mfma_f32_16x16x32_f16(sa, rlo[s], t, 0, 0, 0);
+    }
+    uint32_t nib = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) nib |= (t[i] >= 0.0f ? 1u : 0u) << i;
+    const auto p16 = __builtin_amdgcn_permlane16_swap(nib, nib, false, false);
+    const uint32_t byte = p16[0] | (p16[1] << 4);
+    const auto p32 = __builtin_amdgcn_permlane32_swap(byte, byte, false, false);
+    const uint32_t bits16 = p32[0] | (p32[1] << 8);
+    if (mt & 1) packed[mt / 2] |= bits16 << 16;
+    else packed[mt / 2] = bits16;
+  }
+  if (live && kq == 0) {
+    uint8_t* dst = a.signs + v * (D / 8);
+    if (a.vec_signs) {
+      if constexpr (D == 64) {
+        *(uint2*)dst = make_uint2(packed[0], packed[1]);
+      } else {
+#pragma unroll
+        for (int k = 0; k < D / 128; ++k)
+          ((uint4*)dst)[k] = make_uint4(packed[4 * k], packed[4 * k + 1], packed[4 * k + 2],
+                                        packed[4 * k + 3]);
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < D / 32; ++k) ((uint32_t*)dst)[k] = packed[k];
+    }
   }
 }
 
@@ -199,46 +252,126 @@ __device__ inline void enc_keys(const EncSlot<D, B>& r, const QjlEncArgs& a, con
   }
   g2 = rows_sum(g2);
   if (live && kq == 0) a.gamma[v] = f2h(sqrtf(g2));
-  /* S r on the matrix cores: rows 16 mt .. 16 mt + 15 of S per product;
-   * lane (n, kq) gets projections 16 mt + 4 kq + 0..3 of key n, and the
-   * four nibbles of a key are joined by the same two swaps */
-  uint32_t packed[D / 32]; /* the key's D sign bits (every lane of the key) */
+  enc_project<D>(rhi, rlo, sl, a, 8 * kq, 32, v, live, n, kq);
+}
+
+/* d <= 128: the rotation on the matrix cores as well.  Hp is the Hadamard
+ * matrix (entries (-1)^popcount(a & c), exact in fp16) with its rows
+ * reordered so that row 16 mt + 4 kq + i of Hp is row (d/4) kq + 4 mt + i of
+ * H: then the product Hp (D x), with D x the key slices as loaded (B
+ * operand, lane (n, kq) supplying coordinates 32 s + 8 kq + 0..7 of key n),
+ * leaves lane (n, kq) the rotated coordinates (d/4) kq + 0 .. d/4 - 1 of
+ * key n.  That slice is contiguous, so its codes are one load, and it is,
+ * coordinate for coordinate, the lane's B operand slice of S r. */
+template <int D>
+__device__ inline int hp_row(int r) {
+  const int mt = r / 16, m = r % 16;
+  return (D / 4) * (m / 4) + 4 * mt + (m % 4);
+}
+
+template <int D, int B>
+struct EncSlotM {
+  static constexpr int CB = D * B / 32; /* code bytes of a lane's d/4 coordinates */
+  u32x4 xw[D / 32];
+  uint32_t cw[(CB + 3) / 4];
+};
+
+template <int D, int B>
+__device__ inline void enc_load_m(EncSlotM<D, B>& r, const QjlEncArgs& a, int64_t v0, int n,
+                                  int kq) {
+  constexpr int CB = EncSlotM<D, B>::CB;
+  const int64_t v = v0 + n < a.n ? v0 + n : a.n - 1; /* ragged tail: the last key again */
+#pragma unroll
+  for (int s = 0; s < D / 32; ++s)
+    r.xw[s] = __builtin_nontemporal_load((const u32x4*)(a.x + v * a.stride + 32 * s + 8 * kq));
+  /* rows are multiples of 8 bytes from an 8-byte aligned base */
+  const uint8_t* cp = a.codes + v * (D * B / 8) + kq * CB;
+  if constexpr (CB % 8 == 0) {
+#pragma unroll
+    for (int k = 0; k < CB / 8; ++k) {
+      const u32x2 w = __builtin_nontemporal_load((const u32x2*)cp + k);
+      r.cw[2 * k] = w[0];
+      r.cw[2 * k + 1] = w[1];
+    }
+  } else if constexpr (CB % 4 == 0) {
+#pragma unroll
+    for (int k = 0; k < CB / 4; ++k) r.cw[k] = __builtin_nontemporal_load((const uint32_t*)cp + k);
+  } else { /* d = 64, 3 bits: 6 bytes at a 2-byte boundary */
+    const uint16_t* h = (const uint16_t*)cp;
+    r.cw[0] = (uint32_t)__builtin_nontemporal_load(h) |
+              ((uint32_t)__builtin_nontemporal_load(h + 1) << 16);
+    r.cw[1] = __builtin_nontemporal_load(h + 2);
+  }
+}
+
+/* The 2 B-bit field of code pair p (coordinates 2 p, 2 p + 1 of the slice). */
+template <int B>
+__device__ inline uint32_t pair_field(const uint32_t* cw, int p) {
+  const int bit = 2 * B * p, w = bit / 32, sh = bit % 32;
+  const uint32_t v =
+      sh + 2 * B > 32 ? __builtin_amdgcn_alignbit(cw[w + 1], cw[w], (uint32_t)sh) : cw[w] >> sh;
+  return v & ((1u << (2 * B)) - 1);
+}
+
+template <int D, int B>
+__device__ inline void enc_keys_m(const EncSlotM<D, B>& r, const QjlEncArgs& a, const _Float16* sl,
+                                  const _Float16* hl, const float2* plev,
+                                  const uint32_t (&fm)[D / 32][4], int64_t v0, int lane, int n,
+                                  int kq) {
+  constexpr int KS = D / 32, NL = D / 4;
+  using SL = SLds<D>;
+  const int64_t v = v0 + n;
+  const bool live = v < a.n;
+  /* D x as fp16 operands (an xor of the sign bits), squares for the norm */
+  half8 xb[KS];
+  float ss = 0.0f;
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    u32x4 w;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) w[k] = r.xw[s][k] ^ fm[s][k];
+    xb[s] = __builtin_bit_cast(half8, w);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float f = (float)xb[s][j];
+      ss += f * f;
+    }
+  }
+  ss = rows_sum(ss);
+  /* H D x a 16-row tile at a time: lane (n, kq) gets rotated coordinates
+   * l = 4 mt + 0..3 of its slice, turned at once into the residual
+   * y / (sqrt(d) ||x||) - c[code] and its two fp16 parts */
+  const float scale = ss > 0.0f ? 1.0f / (sqrtf((float)D) * sqrtf(ss)) : 0.0f;
+  const uint32_t cpy = (uint32_t)lane & 3u;
+  float g2 = 0.0f;
+  half8 rhi[KS], rlo[KS];
 #pragma unroll
   for (int mt = 0; mt < D / 16; ++mt) {
     floatx4 t = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      const half8 sa = SL::ON ? *(const half8*)(sl + (16 * mt + n) * SL::P + 32 * s + 8 * kq)
-                              : *(const half8*)(a.S + (16 * mt + n) * D + 32 * s + 8 * kq);
-      t = __builtin_amdgcn_mfma_f32_16x16x32_f16(sa, rhi[s], t, 0, 0, 0);
-      t = __builtin_amdgcn_mfma_f32_16x16x32_f16(sa, rlo[s], t, 0, 0, 0);
-    }
-    uint32_t nib = 0;
+    for (int s = 0; s < KS; ++s)
+      t = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+          *(const half8*)(hl + (16 * mt + n) * SL::P + 32 * s + 8 * kq), xb[s], t, 0, 0, 0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) nib |= (t[i] >= 0.0f ? 1u : 0u) << i;
-    const auto p16 = __builtin_amdgcn_permlane16_swap(nib, nib, false, false);
-    const uint32_t byte = p16[0] | (p16[1] << 4);
-    const auto p32 = __builtin_amdgcn_permlane32_swap(byte, byte, false, false);
-    const uint32_t bits16 = p32[0] | (p32[1] << 8);
-    if (mt & 1) packed[mt / 2] |= bits16 << 16;
-    else packed[mt / 2] = bits16;
-  }
-  if (live && kq == 0) {
-    uint8_t* dst = a.signs + v * (D / 8);
-    if (a.vec_signs) {
-      if constexpr (D == 64) {
-        *(uint2*)dst = make_uint2(packed[0], packed[1]);
-      } else {
+    for (int h = 0; h < 2; ++h) {
+      const float2 c = plev[pair_field<B>(r.cw, 2 * mt + h) * 4 + cpy];
 #pragma unroll
-        for (int k = 0; k < D / 128; ++k)
-          ((uint4*)dst)[k] = make_uint4(packed[4 * k], packed[4 * k + 1], packed[4 * k + 2],
-                                        packed[4 * k + 3]);
+      for (int u = 0; u < 2; ++u) {
+        const int l = 4 * mt + 2 * h + u;
+        const float rr = t[2 * h + u] * scale - (u ? c.y : c.x);
+        g2 += rr * rr;
+        const _Float16 hi = (_Float16)rr;
+        rhi[l / 8][l % 8] = hi;
+        rlo[l / 8][l % 8] = (_Float16)(rr - (float)hi);
       }
-    } else {
-#pragma unroll
-      for (int k = 0; k < D / 32; ++k) ((uint32_t*)dst)[k] = packed[k];
     }
   }
+  g2 = rows_sum(g2);
+  if (live && kq == 0) a.gamma[v] = f2h(sqrtf(g2));
+  /* keep the S operand reads from being hoisted into the rotation (their
+   * registers on top of the rotation's would halve the waves per SIMD) */
+  __builtin_amdgcn_sched_barrier(0);
+  enc_project<D>(rhi, rlo, sl, a, NL * kq, 8, v, live, n, kq);
 }
 
 template <int D, int B>
@@ -248,7 +381,16 @@ __global__ void __launch_bounds__(256) qjl_encode_kernel(QjlEncArgs a) {
   /* the levels of each pair of codes (first code in the low bits), 4 copies
    * (entry 4 p + lane % 4) */
   __shared__ float2 plev[(1 << (2 * B)) * 4];
+  /* Hp (rows reordered Hadamard matrix, padded rows like S) for d <= 128 */
+  __shared__ __align__(16) _Float16 hl[SL::HALFS];
   const int lane = threadIdx.x % 64, n = lane % 16, kq = lane / 16;
+  if constexpr (SL::ON) {
+    for (int e = threadIdx.x; e < D * D; e += blockDim.x) {
+      const int rr = e / D, c = e % D;
+      hl[rr * SL::P + c] = (__builtin_popcount((unsigned)(hp_row<D>(rr) & c)) & 1)
+                               ? (_Float16)-1.0f : (_Float16)1.0f;
+    }
+  }
   for (int e = threadIdx.x; e < (1 << (2 * B)) * 4; e += blockDim.x) {
     const int p = e / 4;
     plev[e] = make_float2(a.levels[p & ((1 << B) - 1)], a.levels[p >> B]);
@@ -278,9 +420,15 @@ __global__ void __launch_bounds__(256) qjl_encode_kernel(QjlEncArgs a) {
   int64_t v0 = ((int64_t)blockIdx.x * 4 + threadIdx.x / 64) * 16;
   if (v0 >= a.n) return;
   for (; v0 < a.n; v0 += stride) {
-    EncSlot<D, B> ra;
-    enc_load<D, B>(ra, a, v0, n, kq);
-    enc_keys<D, B>(ra, a, sl, plev, fm, v0, lane, n, kq);
+    if constexpr (SL::ON) {
+      EncSlotM<D, B> ra;
+      enc_load_m<D, B>(ra, a, v0, n, kq);
+      enc_keys_m<D, B>(ra, a, sl, hl, plev, fm, v0, lane, n, kq);
+    } else {
+      EncSlot<D, B> ra;
+      enc_load<D, B>(ra, a, v0, n, kq);
+      enc_keys<D, B>(ra, a, sl, plev, fm, v0, lane, n, kq);
+    }
   }
 }
 
@@ -322,8 +470,6 @@ struct KeySlice {
   uint32_t zw[ZW];
   uint16_t nm[4], gm[4];
 };
-
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 /* Streamed once: non-temporal loads.  Keys past the end are clamped to the
  * last one (their rows of the product are never stored). */
@@ -557,18 +703,17 @@ __global__ void __launch_bounds__(256) qjl_scores_kernel(QjlScoreArgs a) {
   if (cnt & 1) score_tile<D, B>(ra, bv, bs, tb, cpy, a, t * 16, n, kq);
 }
 
-/* Blocks of a scores instantiation the device holds at once (occupancy x
+/* Blocks of kernel K (256 threads) the device holds at once (occupancy x
  * CUs), looked up once per process; 1024 when no device answers. */
-template <int D, int B>
-int scores_resident_blocks() {
+template <auto K>
+int resident_blocks() {
   static int cached = 0;
   if (cached == 0) {
     int dev = 0, cus = 0, per = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, qjl_scores_kernel<D, B>, 256, 0) !=
-            hipSuccess ||
-        cus <= 0 || per <= 0) {
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, K, 256, 0) != hipSuccess || cus <= 0 ||
+        per <= 0) {
       (void)hipGetLastError();
       return 1024;
     }
@@ -594,11 +739,16 @@ tq_status tq_launch_qjl_encode(const tq_codebook_s* cb, const uint16_t* x, int64
   a.gamma = gamma;
   a.vec_signs = ((uintptr_t)signs & 15) == 0;
   for (int k = 0; k < 16; ++k) a.levels[k] = k < (1 << cb->bits) ? cb->centroids[k] : 0.0f;
-  int64_t blocks = (n + 63) / 64; /* 4 waves of 16 keys; capped, the waves then stride */
-  if (blocks > 2048) blocks = 2048;
+  /* 4 waves of 16 keys a block; at most one round of resident blocks, whose
+   * waves then stride (each block stages S and the reordered Hadamard
+   * matrix once) */
+  const int64_t need = (n + 63) / 64;
 #define TQ_QE(DD, BB) \
-  if (cb->d == DD && cb->bits == BB) \
-    hipLaunchKernelGGL((qjl_encode_kernel<DD, BB>), dim3((unsigned)blocks), dim3(256), 0, s, a); else
+  if (cb->d == DD && cb->bits == BB) { \
+    const int64_t cap = resident_blocks<qjl_encode_kernel<DD, BB>>(); \
+    hipLaunchKernelGGL((qjl_encode_kernel<DD, BB>), dim3((unsigned)(need < cap ? need : cap)), \
+                       dim3(256), 0, s, a); \
+  } else
   TQ_QE(64, 2) TQ_QE(64, 3) TQ_QE(64, 4) TQ_QE(128, 2) TQ_QE(128, 3) TQ_QE(128, 4)
   TQ_QE(256, 2) TQ_QE(256, 3) TQ_QE(256, 4) return TQ_ERR_UNSUPPORTED;
 #undef TQ_QE
@@ -627,7 +777,7 @@ tq_status tq_launch_qjl_scores(const tq_codebook_s* cb, const uint16_t* q, int G
   const int64_t need = (T + 63) / 64;
 #define TQ_QS(DD, BB) \
   if (cb->d == DD && cb->bits == BB) { \
-    const int64_t cap = scores_resident_blocks<DD, BB>(); \
+    const int64_t cap = resident_blocks<qjl_scores_kernel<DD, BB>>(); \
     hipLaunchKernelGGL((qjl_scores_kernel<DD, BB>), dim3((unsigned)(need < cap ? need : cap)), \
                        dim3(256), 0, s, a); \
   } else
