@@ -413,18 +413,29 @@ __global__ void __launch_bounds__(256) qjl_encode_kernel(QjlEncArgs a) {
     for (int w = 0; w < 4; ++w)
       fm[s][w] = (((fb >> (2 * w)) & 1u) << 15) | (((fb >> (2 * w + 1)) & 1u) << 31);
   }
-  /* each wave sketches groups of 16 keys, striding over the grid (a second
-   * register slot to load the next group meanwhile would cost the second
-   * wave per SIMD, which hides more) */
+  /* each wave sketches groups of 16 keys, striding over the grid */
   const int64_t stride = (int64_t)gridDim.x * 64;
   int64_t v0 = ((int64_t)blockIdx.x * 4 + threadIdx.x / 64) * 16;
   if (v0 >= a.n) return;
-  for (; v0 < a.n; v0 += stride) {
-    if constexpr (SL::ON) {
-      EncSlotM<D, B> ra;
-      enc_load_m<D, B>(ra, a, v0, n, kq);
+  if constexpr (SL::ON) {
+    /* two register slots: the next group's keys and codes load while one
+     * is sketched (the LDS, not the registers, sets the waves per SIMD) */
+    const int64_t cnt = (a.n - 1 - v0) / stride + 1;
+    EncSlotM<D, B> ra, rb;
+    enc_load_m<D, B>(ra, a, v0, n, kq);
+    for (int64_t k = 0; k + 2 <= cnt; k += 2) {
+      enc_load_m<D, B>(rb, a, v0 + stride, n, kq);
       enc_keys_m<D, B>(ra, a, sl, hl, plev, fm, v0, lane, n, kq);
-    } else {
+      v0 += stride;
+      if (k + 2 < cnt) enc_load_m<D, B>(ra, a, v0 + stride, n, kq);
+      enc_keys_m<D, B>(rb, a, sl, hl, plev, fm, v0, lane, n, kq);
+      v0 += stride;
+    }
+    if (cnt & 1) enc_keys_m<D, B>(ra, a, sl, hl, plev, fm, v0, lane, n, kq);
+  } else {
+    /* one slot: with the rotation in registers a second one would cost the
+     * second wave per SIMD, which hides more */
+    for (; v0 < a.n; v0 += stride) {
       EncSlot<D, B> ra;
       enc_load<D, B>(ra, a, v0, n, kq);
       enc_keys<D, B>(ra, a, sl, plev, fm, v0, lane, n, kq);
