@@ -491,6 +491,12 @@ def workload_qjl(args):
     q = q.view(4, D)
     out = torch.empty((4, n), dtype=torch.float32, device="cuda")
     torch.cuda.synchronize()
+    if args.copy_probe:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     enc_ms = _timed(torch, lambda: tq.qjl_encode(cb, x, sb, S, codes, signs, gamma), args.steps,
                     args.warmup)
     sc_ms = _timed(torch, lambda: tq.qjl_scores(cb, q, sb, S, codes, norms, signs, gamma, out),
@@ -508,10 +514,12 @@ def workload_qjl(args):
              "qjl_scores_ms": sc_ms, "qjl_scores_gbs": sc_gbs,
              "roofline": {"bound": "hbm", "kernel": "qjl_encode_kernel<128,4>",
                           "achieved": enc_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                          "frac": enc_gbs / HBM_PEAK_GBS, "traffic": None},
+                          "frac": enc_gbs / HBM_PEAK_GBS,
+                          "traffic": measured_traffic("qjl_encode_kernel<128,4>")},
              "roofline_scores": {"bound": "hbm", "kernel": "qjl_scores_kernel<128,4>",
                                  "achieved": sc_gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                 "frac": sc_gbs / HBM_PEAK_GBS, "traffic": None}},
+                                 "frac": sc_gbs / HBM_PEAK_GBS,
+                                 "traffic": measured_traffic("qjl_scores_kernel<128,4>")}},
             args, enc_ms + sc_ms)
 
 
