@@ -388,6 +388,12 @@ def workload_sparse_v(args):
     out = torch.empty((L, B, HQ, D), dtype=torch.float32, device="cuda")
     ws = tq.workspace(cache, HQ, T)
     torch.cuda.synchronize()
+    if args.copy_probe:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     dense_ms = _timed(torch, lambda: tq.decode(cache, cbk, cbv, sbs, q, lens, T, out, ws),
                       args.steps, args.warmup)
     dec_bytes = L * B * HKV * T * per_token_head_bytes()
