@@ -350,6 +350,12 @@ def workload_paged_llama8b(args):
     out = torch.empty((L, B, HQ, D), dtype=torch.float32, device="cuda")
     ws = tq.workspace(cache, HQ, T)
     torch.cuda.synchronize()
+    if args.copy_probe:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     enc_ms = _timed(torch, lambda: tq.append(cache, cbk, cbv, sbs, k, v, zero, host_max_pos=0),
                     args.steps, args.warmup)
     dec_ms = _timed(torch, lambda: tq.decode(cache, cbk, cbv, sbs, q, lens, T, out, ws),
