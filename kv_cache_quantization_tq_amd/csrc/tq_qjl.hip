@@ -694,24 +694,27 @@ __global__ void __launch_bounds__(256) qjl_scores_kernel(QjlScoreArgs a) {
         bs[s][j] = hiCol ? zh : (_Float16)(z - (float)zh);
       }
   }
-  /* 16-key tiles striding over the grid, two register slots: the next
-   * tile's loads are in flight while the current one is scored */
+  /* pairs of adjacent 16-key tiles striding over the grid (a wave's two
+   * stores per query then cover 128 contiguous output bytes), two register
+   * slots: the next tile's loads are in flight while the current one is
+   * scored */
   const uint32_t cpy = (uint32_t)lane & 3u;
-  const int64_t ntile = (a.T + 15) / 16, stride = (int64_t)gridDim.x * 4;
-  int64_t t = (int64_t)blockIdx.x * 4 + wave;
-  if (t >= ntile) return;
-  const int64_t cnt = (ntile - 1 - t) / stride + 1;
+  const int64_t ntile = (a.T + 15) / 16, npair = (ntile + 1) / 2;
+  const int64_t stride = (int64_t)gridDim.x * 4, p0 = (int64_t)blockIdx.x * 4 + wave;
+  if (p0 >= npair) return;
+  const int64_t pcnt = (npair - 1 - p0) / stride + 1;
+  const int64_t cnt = 2 * pcnt - (2 * (p0 + (pcnt - 1) * stride) + 1 >= ntile ? 1 : 0);
+  /* the wave's k-th tile */
+  auto tile_of = [&](int64_t k) { return 2 * (p0 + (k >> 1) * stride) + (k & 1); };
   KeySlice<D, B> ra, rb;
-  load_slice<D, B>(ra, a, t * 16, n, kq);
+  load_slice<D, B>(ra, a, tile_of(0) * 16, n, kq);
   for (int64_t k = 0; k + 2 <= cnt; k += 2) {
-    load_slice<D, B>(rb, a, (t + stride) * 16, n, kq);
-    score_tile<D, B>(ra, bv, bs, tb, cpy, a, t * 16, n, kq);
-    t += stride;
-    if (k + 2 < cnt) load_slice<D, B>(ra, a, (t + stride) * 16, n, kq);
-    score_tile<D, B>(rb, bv, bs, tb, cpy, a, t * 16, n, kq);
-    t += stride;
+    load_slice<D, B>(rb, a, tile_of(k + 1) * 16, n, kq);
+    score_tile<D, B>(ra, bv, bs, tb, cpy, a, tile_of(k) * 16, n, kq);
+    if (k + 2 < cnt) load_slice<D, B>(ra, a, tile_of(k + 2) * 16, n, kq);
+    score_tile<D, B>(rb, bv, bs, tb, cpy, a, tile_of(k + 1) * 16, n, kq);
   }
-  if (cnt & 1) score_tile<D, B>(ra, bv, bs, tb, cpy, a, t * 16, n, kq);
+  if (cnt & 1) score_tile<D, B>(ra, bv, bs, tb, cpy, a, tile_of(cnt - 1) * 16, n, kq);
 }
 
 /* Blocks of kernel K (256 threads) the device holds at once (occupancy x
@@ -783,9 +786,9 @@ tq_status tq_launch_qjl_scores(const tq_codebook_s* cb, const uint16_t* q, int G
   a.out = out;
   a.vec_out = T % 4 == 0 && ((uintptr_t)out & 15) == 0;
   for (int k = 0; k < 16; ++k) a.levels[k] = k < (1 << cb->bits) ? cb->centroids[k] : 0.0f;
-  /* 4 waves of 16 keys a block; at most one round of resident blocks, whose
-   * waves then stride (each block projects the queries once) */
-  const int64_t need = (T + 63) / 64;
+  /* 4 waves of two 16-key tiles a block; at most one round of resident
+   * blocks, whose waves then stride (each block projects the queries once) */
+  const int64_t need = (T + 127) / 128;
 #define TQ_QS(DD, BB) \
   if (cb->d == DD && cb->bits == BB) { \
     const int64_t cap = resident_blocks<qjl_scores_kernel<DD, BB>>(); \
