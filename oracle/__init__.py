@@ -37,7 +37,7 @@ def _L():
         lib.orc_lloyd_max.restype = i32
         lib.orc_norm16.argtypes = [vp, i32, vp]
         lib.orc_norm16.restype = ctypes.c_uint16
-        lib.orc_encode.argtypes = [vp, i64, i32, i32, vp, vp, vp, vp, vp, vp]
+        lib.orc_encode.argtypes = [vp, i64, i32, i32, vp, vp, vp, vp, vp, vp, vp]
         lib.orc_pack_rows.argtypes = [vp, i64, i32, i32, vp]
         lib.orc_unpack_rows.argtypes = [vp, i64, i32, i32, vp]
         lib.orc_pack_vtile.argtypes = [vp, i32, i32, vp]
@@ -45,6 +45,7 @@ def _L():
         lib.orc_dequant.argtypes = [vp, vp, i64, i32, vp, vp, vp]
         lib.orc_attention.argtypes = [vp, i32, vp, vp, i64, i32, vp]
         lib.orc_attention_sparse.argtypes = [vp, i32, vp, vp, i64, i32, dbl, vp, vp, vp]
+        lib.orc_attention_keep.argtypes = [vp, i32, vp, vp, i64, i32, vp, vp, vp]
         lib.orc_qjl_project.argtypes = [vp, i32, vp, i32, vp, vp, vp]
         lib.orc_qjl_encode.argtypes = [vp, i64, i32, i32, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp]
         lib.orc_qjl_estimate.argtypes = [vp, i32, vp, vp, vp, dbl, dbl, vp, vp, i32]
@@ -108,10 +109,13 @@ def norm16(x):
     return h, float(ex[0])
 
 
-def encode(x, bits, sign_bits, want_band=True):
+def encode(x, bits, sign_bits, want_band=True, want_alt=False):
     """Encode fp16 vectors x[n][d] (uint16 bits).
 
-    Returns (codes uint8 [n][d] unpacked, norms uint16 [n], band float64 [n][d])."""
+    Returns (codes uint8 [n][d] unpacked, norms uint16 [n], band float64 [n][d])
+    and, with want_alt, the alternative codes uint8 [n][d] as a fourth item:
+    per coordinate, the code across its nearest threshold (tq_oracle.c,
+    orc_encode)."""
     xb = _c(x, np.uint16)
     n, d = xb.shape
     R = rotation(d, sign_bits)
@@ -119,8 +123,12 @@ def encode(x, bits, sign_bits, want_band=True):
     codes = np.zeros((n, d), dtype=np.uint8)
     norms = np.zeros(n, dtype=np.uint16)
     band = np.zeros((n, d)) if want_band else None
+    alt = np.zeros((n, d), dtype=np.uint8) if want_alt else None
     _L().orc_encode(_p(xb), n, d, bits, _p(R), _p(_c(c, np.float64)), _p(_c(t, np.float64)),
-                    _p(codes), _p(norms), _p(band) if want_band else None)
+                    _p(codes), _p(norms), _p(band) if want_band else None,
+                    _p(alt) if want_alt else None)
+    if want_alt:
+        return codes, norms, band, alt
     return codes, norms, band
 
 
@@ -208,6 +216,26 @@ def attention_sparse(q, K, V, eps, want_weights=False):
     if want_weights:
         return out, bound, w[:, :T]
     return out, bound
+
+
+def attention_keep(q, K, V, keep, want_weights=False):
+    """Attention whose value sum leaves out the positions with keep[j] == 0
+    (the denominator keeps them): out[G][d] (tq_oracle.c,
+    orc_attention_keep); with want_weights also exp(s_j - max s) [G][T]."""
+    qb = _c(q, np.float64)
+    G, d = qb.shape
+    Kb = _c(K, np.float64)
+    Vb = _c(V, np.float64)
+    T = Kb.shape[0]
+    kb = _c(np.asarray(keep, dtype=bool).astype(np.uint8), np.uint8)
+    assert kb.shape == (T,)
+    out = np.zeros((G, d))
+    w = np.zeros((G, max(T, 1))) if want_weights else None
+    _L().orc_attention_keep(_p(qb), G, _p(Kb), _p(Vb), T, d, _p(kb), _p(out),
+                            _p(w) if want_weights else None)
+    if want_weights:
+        return out, w[:, :T]
+    return out
 
 
 def qjl_project(r, S):

@@ -192,12 +192,17 @@ uint16_t orc_norm16(const uint16_t* x, int d, double* exact_norm) {
  *   norms[v]   = fp16 nearest to ||x|| (orc_norm16);
  *   y          = R x / ||x|| with the exact norm (y = 0 for the zero vector);
  *   codes[v*d+i] = argmin_k |y_i - c[k]|, the smaller k on a tie;
- *   band[v*d+i]  = min_k |y_i - t[k]|, distance to the nearest threshold.
+ *   band[v*d+i]  = min_k |y_i - t[k]|, distance to the nearest threshold;
+ *   alt[v*d+i]   = the code on the other side of that nearest threshold
+ *                  (t[k] separates levels k and k + 1; the first of equally
+ *                  near thresholds counts).  Within a tiny distance of a
+ *                  threshold either neighbouring code is a correct encoding.
  * c[2^bits], t[2^bits - 1] are the dimension-scaled codebook (levels and
- * thresholds divided by sqrt(d)); R is orc_rotation's matrix. */
+ * thresholds divided by sqrt(d)); R is orc_rotation's matrix.  band and alt
+ * may be NULL. */
 void orc_encode(const uint16_t* x, int64_t n, int d, int bits, const double* R,
                 const double* c, const double* t, uint8_t* codes, uint16_t* norms,
-                double* band) {
+                double* band, uint8_t* alt) {
   const int L = 1 << bits;
   double* xv = (double*)malloc(sizeof(double) * d);
   for (int64_t v = 0; v < n; ++v) {
@@ -218,12 +223,14 @@ void orc_encode(const uint16_t* x, int64_t n, int d, int bits, const double* R,
         if (dk < bd) { bd = dk; best = k; }
       }
       double md = INFINITY;
+      int kt = 0;
       for (int k = 0; k < L - 1; ++k) {
         double dk = fabs(y - t[k]);
-        if (dk < md) md = dk;
+        if (dk < md) { md = dk; kt = k; }
       }
       codes[v * d + i] = (uint8_t)best;
       if (band) band[v * d + i] = md;
+      if (alt) alt[v * d + i] = (uint8_t)(best == kt ? kt + 1 : kt);
     }
   }
   free(xv);
@@ -389,6 +396,40 @@ void orc_attention_sparse(const double* q, int G, const double* K, const double*
   free(s);
 }
 
+/* Attention with an explicit set of positions left out of the value sum
+ * (the Sparse V reading above, for a left-out set chosen by someone else):
+ *   out[g] = sum_{j : keep[j]} p_j V[j] / sum_j p_j,  p_j = exp(s_j - max s)
+ * for all G queries; the denominator keeps every position.  keep[T] holds 0
+ * or 1 per position.  weights (optional, [G][T]) receives exp(s_j - max s),
+ * so a caller can check that every left-out position was negligible. */
+void orc_attention_keep(const double* q, int G, const double* K, const double* V, int64_t T,
+                        int d, const uint8_t* keep, double* out, double* weights) {
+  double* s = (double*)malloc(sizeof(double) * (size_t)(T > 0 ? T : 1));
+  double scale = 1.0 / sqrt((double)d);
+  for (int g = 0; g < G; ++g) {
+    for (int i = 0; i < d; ++i) out[g * d + i] = 0.0;
+    if (T == 0) continue;
+    double mx = -INFINITY;
+    for (int64_t j = 0; j < T; ++j) {
+      double a = 0.0;
+      for (int i = 0; i < d; ++i) a += q[g * d + i] * K[j * d + i];
+      s[j] = a * scale;
+      if (s[j] > mx) mx = s[j];
+    }
+    double l = 0.0;
+    for (int64_t j = 0; j < T; ++j) {
+      s[j] = exp(s[j] - mx);
+      l += s[j];
+      if (weights) weights[(int64_t)g * T + j] = s[j];
+    }
+    for (int64_t j = 0; j < T; ++j)
+      if (keep[j])
+        for (int i = 0; i < d; ++i) out[g * d + i] += s[j] * V[j * d + i];
+    for (int i = 0; i < d; ++i) out[g * d + i] /= l;
+  }
+  free(s);
+}
+
 /* ------------------------------------------------------------------ QJL -- */
 
 /* Stage 2 of the method ("We Built a Python Library That Cuts LLM Memory
@@ -426,7 +467,7 @@ void orc_qjl_project(const double* r, int d, const double* S, int m, uint8_t* bi
 void orc_qjl_encode(const uint16_t* x, int64_t n, int d, int bits, const double* R,
                     const double* c, const double* t, const double* S, int m, uint8_t* codes,
                     uint16_t* norms, uint8_t* signs, double* gamma, double* proj) {
-  orc_encode(x, n, d, bits, R, c, t, codes, norms, NULL);
+  orc_encode(x, n, d, bits, R, c, t, codes, norms, NULL, NULL);
   double* xv = (double*)malloc(sizeof(double) * d);
   double* r = (double*)malloc(sizeof(double) * d);
   for (int64_t v = 0; v < n; ++v) {

@@ -243,6 +243,63 @@ def test_quantize_argmin_equals_threshold_count():
     assert np.allclose(band, np.abs(y[..., None] - t).min(-1), atol=1e-13)
 
 
+def test_alternative_code_against_textbook_thresholds():
+    """The alternative code (the neighbour across the nearest threshold) on a
+    spike input x = e_j at d = 64: every rotated coordinate is +-1/8 exactly
+    (R = H D / 8), so code, alternative and band follow from the thresholds
+    of the textbook table (midpoints of its levels, scaled by 1/8)."""
+    d = 64
+    rng = np.random.default_rng(5)
+    sb = _rand_signs(rng, d)
+    x = np.zeros((1, d), np.float16)
+    x[0, 9] = 1.0
+    R = oracle.rotation(d, sb)
+    sign = np.sign(R[:, 9])  # +-1/8 per coordinate: the sign is all that varies
+    assert np.allclose(np.abs(R[:, 9]), 1 / 8, rtol=0, atol=0)
+    for bits in (2, 3, 4):
+        lv = _golden_levels()[bits][1]
+        levels = np.r_[-np.array(lv[::-1]), np.array(lv)] / 8
+        thr = (levels[1:] + levels[:-1]) / 2
+        y = 1 / 8
+        code_pos = int(np.argmin(np.abs(y - levels)))
+        kt = int(np.argmin(np.abs(y - thr)))
+        # the table's 4-decimal levels decide these with a wide margin
+        dist = np.sort(np.abs(y - thr))
+        assert dist[0] > 1e-4 and dist[1] - dist[0] > 1e-4
+        alt_pos = kt + 1 if code_pos == kt else kt
+        L = 1 << bits
+        codes, _, band, alt = oracle.encode(x.view(np.uint16), bits, sb, want_alt=True)
+        want_c = np.where(sign > 0, code_pos, L - 1 - code_pos)
+        want_a = np.where(sign > 0, alt_pos, L - 1 - alt_pos)
+        assert np.array_equal(codes[0], want_c), bits
+        assert np.array_equal(alt[0], want_a), bits
+        assert np.allclose(band[0], dist[0], rtol=0, atol=2e-5)
+    # the hand values for 2 bits: y = 1/8 lies just above the threshold
+    # 0.9816 / 8 = 0.1227, so the code is the top level and the alternative
+    # the one below it
+    codes, _, _, alt = oracle.encode(x.view(np.uint16), 2, sb, want_alt=True)
+    assert set(zip(codes[0].tolist(), alt[0].tolist())) <= {(3, 2), (0, 1)}
+
+
+def test_alternative_code_is_the_neighbour_across_the_nearest_threshold():
+    """On random inputs: the alternative differs from the code by one level,
+    and the threshold between them is the nearest one (its distance is the
+    band)."""
+    d = 128
+    rng = np.random.default_rng(8)
+    sb = _rand_signs(rng, d)
+    x = rng.standard_normal((300, d)).astype(np.float16).view(np.uint16)
+    R = oracle.rotation(d, sb)
+    xf = x.view(np.float16).astype(np.float64)
+    y = (xf @ R.T) / np.linalg.norm(xf, axis=1, keepdims=True)
+    for bits in (2, 3, 4):
+        codes, _, band, alt = oracle.encode(x, bits, sb, want_alt=True)
+        _, t = oracle.codebook(d, bits)
+        assert (np.abs(alt.astype(int) - codes.astype(int)) == 1).all()
+        between = t[np.minimum(alt, codes)]
+        assert np.allclose(np.abs(y - between), band, rtol=0, atol=1e-13)
+
+
 @pytest.mark.parametrize("bits", [2, 3, 4])
 def test_code_histogram_matches_gaussian_cells(bits):
     """After rotation each coordinate is ~N(0, 1/d): code frequencies match the
@@ -346,6 +403,36 @@ def test_vtile_bit_positions():
     nz = np.flatnonzero(t)
     assert list(nz) == [(16 * 1 + 3) * seg + bit // 8]
     assert t[nz[0]] == 3 << (bit % 8)
+
+
+def test_vtile_fields_across_byte_boundaries():
+    """3-bit fields straddle bytes, 4-bit fields fill nibbles: hand-placed codes
+    land at the bytes the layout description gives (d = 128)."""
+    d = 128
+    # 3 bits: segments of 24 bytes
+    c = np.zeros((32, d), np.uint8)
+    # token 18 = 8*2 + 2 (q 2, u 2), coordinate 56 = 7*8 + 0 (r 7, m 0):
+    # segment 39, bits 6..8 of it; code 0b101 -> bit 6 and bit 8
+    c[18, 56] = 5
+    # token 5 (q 0, u 5), coordinate 2*8 + 2 = 18 (r 2, m 2): segment 2, bits
+    # (16 + 5) * 3 = 63..65; code 0b110 -> bits 64 and 65
+    c[5, 18] = 6
+    t = oracle.pack_vtiles(c, 3)[0]
+    want = {39 * 24 + 0: 0x40, 39 * 24 + 1: 0x01, 2 * 24 + 8: 0x03}
+    assert {int(i): int(t[i]) for i in np.flatnonzero(t)} == want
+    assert np.array_equal(oracle.unpack_vtiles(t[None], d, 3), c)
+    # 4 bits: segments of 32 bytes
+    c = np.zeros((32, d), np.uint8)
+    # token 27 = 8*3 + 3 (q 3, u 3), coordinate 1 (r 0, m 1): segment 48, bits
+    # (8 + 3) * 4 = 44..47, the high nibble of byte 5; code 9
+    c[27, 1] = 9
+    # token 8 (q 1, u 0), coordinate 15*8 + 7 = 127 (r 15, m 7): segment 31,
+    # bits 56 * 4 = 224..227, the low nibble of byte 28; code 14
+    c[8, 127] = 14
+    t = oracle.pack_vtiles(c, 4)[0]
+    want = {48 * 32 + 5: 0x90, 31 * 32 + 28: 0x0E}
+    assert {int(i): int(t[i]) for i in np.flatnonzero(t)} == want
+    assert np.array_equal(oracle.unpack_vtiles(t[None], d, 4), c)
 
 
 # ------------------------------------------------------------------ fidelity
@@ -469,6 +556,33 @@ def test_sparse_v_special_cases():
     # no positions: zeros
     o, b = oracle.attention_sparse(q, K[:0], V[:0], 1e-6)
     assert not o.any() and not b.any()
+
+
+def test_attention_keep_hand_example_and_reductions():
+    """Attention with an explicit left-out set: the hand example of the sparse
+    pin with its second position left out, then keep-all equal to plain
+    attention and the eps rule's set equal to the sparse reading."""
+    r2 = math.sqrt(2.0)
+    q = np.array([[r2, 0.0]])
+    K = np.array([[0.0, 1.0], [-1.0, 3.0], [-20.0, -2.0]])
+    V = np.array([[1.0, 0.0], [0.0, 1.0], [5.0, -7.0]])
+    l = 1 + math.exp(-1) + math.exp(-20)
+    out, w = oracle.attention_keep(q, K, V, [1, 0, 1], want_weights=True)
+    assert np.allclose(w[0], [1.0, math.exp(-1), math.exp(-20)], rtol=1e-14, atol=0)
+    assert np.allclose(out[0], [(1 + 5 * math.exp(-20)) / l, -7 * math.exp(-20) / l],
+                       rtol=1e-14, atol=0)
+    rng = np.random.default_rng(16)
+    d, T = 64, 70
+    K = rng.standard_normal((T, d))
+    V = rng.standard_normal((T, d))
+    q = rng.standard_normal((1, d)) * 4
+    assert np.allclose(oracle.attention_keep(q, K, V, np.ones(T)), oracle.attention(q, K, V),
+                       rtol=0, atol=1e-15)
+    for eps in (1e-3, 0.05):
+        o, _, w = oracle.attention_sparse(q, K, V, eps, want_weights=True)
+        assert np.allclose(oracle.attention_keep(q, K, V, w[0] >= eps), o, rtol=0, atol=1e-15)
+    assert not oracle.attention_keep(q, K, V, np.zeros(T)).any()
+    assert not oracle.attention_keep(q, K[:0], V[:0], np.zeros(0)).any()
 
 
 def test_qjl_hand_examples():
