@@ -45,6 +45,7 @@
  */
 #include <hip/hip_runtime.h>
 
+#include "tq_append_rows.h"
 #include "tq_internal.h"
 
 namespace {
@@ -692,17 +693,6 @@ constexpr int kTPB = 2;
 template <int BV>
 constexpr bool kMixKV = BV == 2;
 
-/* Rows of tile `tile` receiving tokens of this append, [jlo, jhi). */
-__device__ inline bool tile_range(const AppendArgs& a, int p0, int tile, int* jlo, int* jhi) {
-  int lo = p0 - 32 * tile, hi = p0 + a.t_new - 32 * tile;
-  if (lo < 0) lo = 0;
-  if (hi > 32) hi = 32;
-  if (32 * tile + hi > a.capacity) hi = a.capacity - 32 * tile;
-  *jlo = lo;
-  *jhi = hi;
-  return hi > lo;
-}
-
 /* Task coordinates (layer, seq, head, slot), slot the tile offset from the
  * first tile touched by the append; tasks are numbered with slot fastest.
  * The divisions happen once per block; later tasks advance by carries. */
@@ -795,9 +785,9 @@ append_kernel(AppendArgs a) {
     /* a scalar load: the index is uniform (a vector load here would make the
      * wave wait for all its outstanding memory operations) */
     const int p0 = ld_const(a.pos + g.b);
-    if (p0 < 0) return g;
-    g.tile = p0 / 32 + slot;
-    if (!tile_range(a, p0, g.tile, &g.jlo, &g.jhi)) return g;
+    /* the tile of this slot and its appended rows below capacity (nothing
+     * when p0 is negative or at or past capacity) */
+    if (!tq_append_tile_rows(p0, a.t_new, a.capacity, slot, &g.tile, &g.jlo, &g.jhi)) return g;
     if (a.block_table) {
       /* paged: the pool page of this tile's page (rows of pages outside the
        * pool are skipped) */

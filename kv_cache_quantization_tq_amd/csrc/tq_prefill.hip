@@ -183,8 +183,10 @@ __global__ void __launch_bounds__(64 * waves_for(D)) prefill_kernel(PreArgs a) {
   const int layer = (int)(unit / a.batch);
   const int q0 = chunk * a.qc;
   const int qn = (a.t_new - q0) < a.qc ? (a.t_new - q0) : a.qc; /* queries of this chunk */
+  /* first query position, clamped to [0, capacity] (queries at or past
+   * capacity attend the whole cache) */
   int p0 = a.pos[b];
-  p0 = p0 < 0 ? 0 : p0;
+  p0 = p0 < 0 ? 0 : (p0 > a.capacity ? a.capacity : p0);
 
   /* tables */
   for (int i = tid; i < PG::PWK; i += blockDim.x) {
@@ -240,12 +242,12 @@ __global__ void __launch_bounds__(64 * waves_for(D)) prefill_kernel(PreArgs a) {
   for (int e = 0; e < NG; ++e) {
     const int col = c0 + 16 * e + n;
     const int cg = col / a.qc, ci = col % a.qc;
-    int l = p0 + q0 + ci + 1;
-    l = l > a.capacity ? a.capacity : l;
-    lim[e] = (cg < a.group && ci < qn) ? l : 1; /* padding columns attend token 0 only */
+    const int64_t l = (int64_t)p0 + q0 + ci + 1;
+    lim[e] = (cg < a.group && ci < qn) ? (int)(l > a.capacity ? a.capacity : l)
+                                       : 1; /* padding columns attend token 0 only */
   }
-  int blk_lim = p0 + q0 + qn;
-  blk_lim = blk_lim > a.capacity ? a.capacity : blk_lim;
+  const int64_t blk_end = (int64_t)p0 + q0 + qn;
+  const int blk_lim = (int)(blk_end > a.capacity ? a.capacity : blk_end);
   const int ntiles = (blk_lim + 31) / 32;
   __syncthreads(); /* qbuf is dead: the tiles take its place */
 

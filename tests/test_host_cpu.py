@@ -94,21 +94,22 @@ def test_validation_before_device_work():
 
 def test_sparse_decode_validation():
     """tq_decode_attn_sparse rejects a NaN, negative or infinite threshold and a
-    misaligned count array before anything else (an unsupported head dim
-    would otherwise answer TQ_ERR_UNSUPPORTED); valid thresholds reach the
-    ordinary checks."""
+    misaligned count array or skip bitmap before anything else (an
+    unsupported head dim would otherwise answer TQ_ERR_UNSUPPORTED); valid
+    thresholds reach the ordinary checks."""
     L = tq.lib()
     vp = ctypes.c_void_p
     s = _fake_cache(head_dim=96)
-    def call(eps, counts=None):
+    def call(eps, counts=None, tiles=None):
         return L.tq_decode_attn_sparse(ctypes.byref(s), None, None, vp(1), vp(16), 8, vp(4), 16,
-                                       1, eps, counts, vp(16), None, 0, None)
+                                       1, eps, counts, tiles, vp(16), None, 0, None)
     for eps in (float("nan"), -1e-6, float("inf")):
         assert call(eps) == 1, eps
     assert call(1e-6, vp(2)) == 1
+    assert call(1e-6, None, vp(6)) == 1
     for eps in (0.0, 1e-6, 1.0, 3.0):
         assert call(eps) == 2, eps
-        assert call(eps, vp(4)) == 2, eps
+        assert call(eps, vp(4), vp(8)) == 2, eps
 
 
 def test_prefill_validation():
@@ -196,3 +197,65 @@ def test_paged_validation():
     s = _paged(num_pages=1 << 17)
     assert L.tq_decode_attn(ctypes.byref(s), None, None, vp(1), vp(16), 8, vp(4), 16, 1, vp(16),
                             None, 0, None) == 2
+
+
+_ROWS_HARNESS = r"""
+#define __host__
+#define __device__
+#include <stdio.h>
+#include "tq_append_rows.h"
+int main(void) {
+  long long p0, t_new, cap, slot;
+  while (scanf("%lld %lld %lld %lld", &p0, &t_new, &cap, &slot) == 4) {
+    int32_t tile, jlo, jhi;
+    bool ok = tq_append_tile_rows((int32_t)p0, (int32_t)t_new, (int32_t)cap, (int32_t)slot,
+                                  &tile, &jlo, &jhi);
+    printf("%d %d %d %d\n", ok ? 1 : 0, tile, jlo, jhi);
+  }
+  return 0;
+}
+"""
+
+
+def test_append_tile_rows_arithmetic(tmp_path):
+    """The append kernel's per-slot row arithmetic (tq_append_rows.h, compiled
+    here for the host) against a brute-force statement of what an append
+    writes: rows p0 .. p0 + t_new - 1 that are below capacity, cut into
+    32-token tiles.  Includes positions within 64 of INT32_MAX, where 32-bit
+    row arithmetic would wrap and write far past the stream."""
+    import subprocess
+    src = tmp_path / "rows.cpp"
+    src.write_text(_ROWS_HARNESS)
+    exe = tmp_path / "rows"
+    inc = os.path.join(ROOT, "kv_cache_quantization_tq_amd", "csrc")
+    subprocess.run(["g++", "-O1", "-std=c++17", "-I", inc, str(src), "-o", str(exe)], check=True)
+    imax = 2 ** 31 - 1
+    cases = []
+    rng = np.random.default_rng(9)
+    for cap in (32, 2048, 32768, 1 << 26):
+        starts = [0, 1, 31, 32, cap - 33, cap - 1, cap, cap + 5, -1, -40]
+        starts += list(range(imax - 64, imax + 1, 7)) + [imax - 4, imax]
+        starts += rng.integers(0, cap, 5).tolist()
+        for p0 in starts:
+            for t_new in (1, 7, 8, 32, 40, 2049, imax - 3):
+                nslots = min((t_new + 31) // 32 + 1, 70)
+                for slot in list(range(min(nslots, 4))) + [nslots - 1]:
+                    cases.append((p0, t_new, cap, slot))
+    inp = "\n".join(" ".join(map(str, c)) for c in cases) + "\n"
+    res = subprocess.run([str(exe)], input=inp, capture_output=True, text=True, check=True)
+    lines = res.stdout.split("\n")
+    for (p0, t_new, cap, slot), line in zip(cases, lines):
+        ok, tile, jlo, jhi = map(int, line.split())
+        # brute force: appended rows below capacity, within this slot's tile
+        want = None
+        if 0 <= p0 < cap:
+            t = p0 // 32 + slot
+            lo, hi = max(p0, 32 * t), min(p0 + t_new, 32 * t + 32, cap)
+            if hi > lo:
+                want = (t, lo - 32 * t, hi - 32 * t)
+        if want is None:
+            assert ok == 0, (p0, t_new, cap, slot, line)
+        else:
+            assert ok == 1 and (tile, jlo, jhi) == want, (p0, t_new, cap, slot, line, want)
+            assert 32 * tile + jhi <= cap and 0 <= jlo < jhi <= 32
+    assert len(lines) >= len(cases)
