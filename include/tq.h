@@ -275,12 +275,17 @@ tq_status tq_qjl_scores(tq_codebook cb, const uint16_t* q, int n_q, const uint8_
  * skip_counts: device uint32 [n_layers][batch][kv_heads], 4-byte aligned, or
  *              NULL; the number of tiles skipped for each (layer, sequence,
  *              KV head) is ADDED to it (the caller zeroes it).
+ * skip_tiles:  device uint32 [n_layers][batch][kv_heads][(max_len + 1023) /
+ *              1024], 4-byte aligned, or NULL; when tile t (tokens 32 t ..
+ *              32 t + 31) of a unit is skipped, bit t % 32 of that unit's word
+ *              t / 32 is OR-ed in (the caller zeroes it), so the exact set of
+ *              left-out positions is known.
  * Other arguments as tq_decode_attn (same workspace). */
 tq_status tq_decode_attn_sparse(const tq_kv_cache* c, tq_codebook cbk, tq_codebook cbv,
                                 const uint8_t* sign_bits, const uint16_t* q, int q_heads,
                                 const int32_t* seq_lens, int max_len, int n_layers, float eps,
-                                uint32_t* skip_counts, float* out, void* ws, size_t ws_bytes,
-                                void* stream);
+                                uint32_t* skip_counts, uint32_t* skip_tiles, float* out, void* ws,
+                                size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -73,7 +73,7 @@ def lib():
         L.tq_decode_attn.argtypes = [P(KVCacheStruct), vp, vp, vp, vp, i32, vp, i32, i32, vp,
                                      vp, sz, vp]
         L.tq_decode_attn_sparse.argtypes = [P(KVCacheStruct), vp, vp, vp, vp, i32, vp, i32, i32,
-                                            ctypes.c_float, vp, vp, vp, sz, vp]
+                                            ctypes.c_float, vp, vp, vp, vp, sz, vp]
         L.tq_prefill_attn.argtypes = [P(KVCacheStruct), vp, vp, vp, vp, i32, i32, vp, i32, vp, vp]
         L.tq_qjl_encode.argtypes = [vp, vp, i64, i64, vp, vp, vp, vp, vp, vp]
         L.tq_qjl_scores.argtypes = [vp, vp, i32, vp, vp, vp, vp, vp, vp, i64, vp, vp]
@@ -278,19 +278,26 @@ def decode(cache, cbk, cbv, sign_bits, q, seq_lens, max_len, out, ws=None, layer
         _ptr(seq_lens), max_len, n_layers, _ptr(out), _ptr(ws), ws_bytes, _stream(stream)))
 
 
+def skip_words(max_len):
+    """Words per (layer, sequence, KV head) of a Sparse V skip bitmap."""
+    return (max_len + 1023) // 1024
+
+
 def decode_sparse(cache, cbk, cbv, sign_bits, q, seq_lens, max_len, out, eps, ws=None,
-                  skip_counts=None, layer0=0, n_layers=None, stream=None):
+                  skip_counts=None, skip_tiles=None, layer0=0, n_layers=None, stream=None):
     """tq_decode_attn_sparse: decode with the Sparse V gate at threshold eps;
     skip_counts (optional) uint32/int32 [n_layers][B][Hkv] receives added
-    per-unit counts of skipped tiles.  Other arguments as decode()."""
+    per-unit counts of skipped tiles, skip_tiles (optional) int32
+    [n_layers][B][Hkv][skip_words(max_len)] the OR of one bit per skipped
+    tile.  Other arguments as decode()."""
     n_layers = n_layers if n_layers is not None else q.shape[0]
     q_heads = q.shape[2]
     s = cache.struct(layer0)
     ws_bytes = ws.numel() if ws is not None else 0
     _check("tq_decode_attn_sparse", lib().tq_decode_attn_sparse(
         ctypes.byref(s), cbk.handle, cbv.handle, _ptr(sign_bits), _ptr(q), q_heads,
-        _ptr(seq_lens), max_len, n_layers, float(eps), _ptr(skip_counts), _ptr(out), _ptr(ws),
-        ws_bytes, _stream(stream)))
+        _ptr(seq_lens), max_len, n_layers, float(eps), _ptr(skip_counts), _ptr(skip_tiles),
+        _ptr(out), _ptr(ws), ws_bytes, _stream(stream)))
 
 
 def prefill(cache, cbk, cbv, sign_bits, q, pos, out, layer0=0, n_layers=None, stream=None):

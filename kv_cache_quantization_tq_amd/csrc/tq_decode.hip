@@ -301,6 +301,8 @@ struct DecArgs {
   float sparse_eps;      /* Sparse V threshold (sparse kernels only) */
   float sparse_lg_eps;   /* log2 of it */
   uint32_t* skip_counts; /* optional [n_layers][batch][kv_heads] skipped-tile counts */
+  uint32_t* skip_tiles;  /* optional [n_layers][batch][kv_heads][skip_words] bitmaps */
+  int skip_words;        /* words per unit of skip_tiles: one bit per tile */
   const uint8_t* sign_bits;
   const uint16_t* q;
   const int32_t* seq_lens;
@@ -759,11 +761,16 @@ __device__ inline void sparse_tiles(const DecArgs& a, const TileAddr& ad, TileRe
   load_v(ra, keepc);
   pf(ra, tile + DG::DEPTH * W);
   /* the value half of a step: tile's values (in slot cur) at weights pc */
+  uint32_t* const skip_map =
+      a.skip_tiles ? a.skip_tiles + (((int64_t)layer * a.batch + b) * a.kv_heads + kv) * a.skip_words
+                   : nullptr;
   auto values = [&](TileRegs<DG, CF>& cur) {
-    if (keepc)
+    if (keepc) {
       value_part<DG, BV, CF>(pc, cur.vn, cur.vw, lv, lo, lo8, acc, n);
-    else
+    } else {
       ++nskip;
+      if (skip_map && lane == 0) atomicOr(skip_map + (tile >> 5), 1u << (tile & 31));
+    }
   };
   /* one step: cur holds the values of tile, nxt the keys of tile + W (which
    * exists) */
@@ -1262,11 +1269,13 @@ tq_status tq_launch_decode(const tq_kv_cache* c, const tq_codebook_s* cbk,
                            const uint16_t* q, int q_heads, const int32_t* seq_lens,
                            int max_len, int n_layers, float* out, void* ws,
                            const tq_decode_plan& plan, float sparse_eps, uint32_t* skip_counts,
-                           hipStream_t s) {
+                           uint32_t* skip_tiles, hipStream_t s) {
   DecArgs a;
   a.sparse_eps = sparse_eps;
   a.sparse_lg_eps = sparse_eps > 0.0f ? (float)log2((double)sparse_eps) : -INFINITY;
   a.skip_counts = skip_counts;
+  a.skip_tiles = skip_tiles;
+  a.skip_words = tq_skip_words(max_len);
   a.k_codes = c->k_codes;
   a.v_codes = c->v_codes;
   a.k_norms = (const uint8_t*)c->k_norms;

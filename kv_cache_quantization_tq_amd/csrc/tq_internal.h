@@ -93,6 +93,10 @@ tq_status tq_launch_decode(const tq_kv_cache* c, const tq_codebook_s* cbk,
                            const uint16_t* q, int q_heads, const int32_t* seq_lens,
                            int max_len, int n_layers, float* out, void* ws,
                            const tq_decode_plan& plan, float sparse_eps, uint32_t* skip_counts,
-                           hipStream_t stream);
+                           uint32_t* skip_tiles, hipStream_t stream);
+
+/* Words per (layer, sequence, KV head) of a Sparse V skip bitmap: one bit per
+ * 32-token tile of a context of up to max_len tokens. */
+inline int tq_skip_words(int max_len) { return (max_len + 1023) / 1024; }
 
 #endif

@@ -1,58 +1,78 @@
-"""The attention check's band-flip bound, tested on the CPU against brute
-force: each band coordinate's code is flipped alone in the oracle's cache, the
-attention recomputed, and the bound must be the sum of those exact changes."""
+"""The GPU tests' comparison helpers, tested on the CPU: the attention check
+resolves band codes only to the oracle's own neighbouring code, and rejects
+every other difference (a code outside the band, a band code two levels away,
+a norm off by one ulp).  The "GPU" inputs here are planted on the CPU."""
 import numpy as np
 import pytest
 
 import oracle
 import synth
-from helpers import band_flip_bound
+from helpers import check_attention, oracle_stream, resolve_codes
 
 
-@pytest.mark.parametrize("d,bk,bv", [(64, 4, 2), (128, 3, 3)])
-def test_band_flip_bound_matches_single_flips(d, bk, bv):
-    seed, T, G = 77, 40, 3
+def _stream(seed=77, d=64, T=40):
     k = synth.kv_host(seed, 0, 0, 0, 0, d, 0, T)
     v = synth.kv_host(seed, 1, 0, 0, 0, d, 0, T)
-    q16 = np.stack([synth.q_host(seed, 0, 0, 0, g, d) for g in range(G)])
-    sb = synth.sign_bits(seed, 0, d)
-    st = oracle.decode_stream(k, v, q16, bk, bv, sb, full=True)
-    q64 = oracle.halves_to_double(q16)
-    thr = 4e-3  # wide enough that a few coordinates of this tiny stream are "band"
-    bound, nb = band_flip_bound(q64, k, v, st, bk, bv, sb, threshold=thr)
-    assert nb > 0
-    ck, tk = oracle.codebook(d, bk)
-    cv, tv = oracle.codebook(d, bv)
-    R = oracle.rotation(d, sb)
-    total = np.zeros_like(bound)
-    for kind, codes, band, x16, t in (("k", st["k_codes"], st["k_band"], k, tk),
-                                      ("v", st["v_codes"], st["v_band"], v, tv)):
-        for j, i in np.argwhere(band < thr):
-            x = x16[j].view(np.float16).astype(np.float64)
-            y = R[i] @ x / np.linalg.norm(x)
-            near = int(np.argmin(np.abs(y - t)))
-            c2 = codes.copy()
-            c2[j, i] = near + 1 if codes[j, i] == near else near
-            if kind == "k":
-                K2 = oracle.dequant(c2, st["k_norms"], bk, sb)
-                o2 = oracle.attention(q64, K2, st["V"])
-            else:
-                V2 = oracle.dequant(c2, st["v_norms"], bv, sb)
-                o2 = oracle.attention(q64, st["K"], V2)
-            assert abs(int(c2[j, i]) - int(codes[j, i])) == 1
-            total += np.abs(o2 - st["out"])
-    np.testing.assert_allclose(bound, total, rtol=1e-9, atol=1e-15)
+    return k, v, synth.sign_bits(seed, 0, d)
 
 
-def test_band_flip_bound_empty_and_bandless():
-    d = 64
-    sb = synth.sign_bits(5, 0, d)
-    q16 = np.stack([synth.q_host(5, 0, 0, 0, 0, d)])
-    k = synth.kv_host(5, 0, 0, 0, 0, d, 0, 8)
-    st = oracle.decode_stream(k, k, q16, 2, 2, sb, full=True)
-    b, nb = band_flip_bound(oracle.halves_to_double(q16), k, k, st, 2, 2, sb, threshold=0.0)
-    assert nb == 0 and not b.any()
-    e = k[:0]
-    st0 = oracle.decode_stream(e, e, q16, 2, 2, sb, full=True)
-    b0, nb0 = band_flip_bound(oracle.halves_to_double(q16), e, e, st0, 2, 2, sb)
-    assert nb0 == 0 and b0.shape == (1, d) and not b0.any()
+def test_resolve_takes_the_oracles_neighbour_at_band_coordinates():
+    k, _, sb = _stream()
+    codes, _, band, alt = oracle.encode(k, 4, sb, want_alt=True)
+    # a coordinate nearest its threshold stands in for a band coordinate
+    j, i = np.unravel_index(int(np.argmin(band)), band.shape)
+    gpu = codes.copy()
+    gpu[j, i] = alt[j, i]
+    band_wide = band.copy()
+    band_wide[j, i] = 0.0
+    out, n = resolve_codes(gpu, codes, band_wide, alt)
+    assert n == 1 and np.array_equal(out, gpu) and out is not codes
+    same, n0 = resolve_codes(codes.copy(), codes, band, alt)
+    assert n0 == 0 and np.array_equal(same, codes)
+
+
+def test_resolve_rejects_codes_that_are_not_correct_encodings():
+    k, _, sb = _stream()
+    codes, _, band, alt = oracle.encode(k, 4, sb, want_alt=True)
+    # outside the band: any difference fails
+    far = np.argwhere(band > 1e-3)[0]
+    gpu = codes.copy()
+    gpu[tuple(far)] = alt[tuple(far)]
+    with pytest.raises(AssertionError):
+        resolve_codes(gpu, codes, band, alt)
+    # in the band, but two levels away from the oracle's code
+    j, i = np.unravel_index(int(np.argmin(band)), band.shape)
+    band_wide = band.copy()
+    band_wide[j, i] = 0.0
+    gpu = codes.copy()
+    gpu[j, i] = (int(alt[j, i]) * 2 - int(codes[j, i])) % 16
+    with pytest.raises(AssertionError):
+        resolve_codes(gpu, codes, band_wide, alt)
+
+
+def test_oracle_stream_checks_norms_and_dequantizes():
+    k, v, sb = _stream()
+    d = k.shape[1]
+    kc, kn, _ = oracle.encode(k, 4, sb)
+    vc, vn, _ = oracle.encode(v, 2, sb)
+    gpu = dict(k_codes=kc, k_norms=kn, v_codes=vc, v_norms=vn)
+    st = oracle_stream(k, v, 4, 2, sb, gpu, "cpu")
+    assert st["n_alt"] == 0 and st["n_coords"] == 2 * k.size
+    assert np.array_equal(st["K"], oracle.dequant(kc, kn, 4, sb))
+    assert np.array_equal(st["V"], oracle.dequant(vc, vn, 2, sb))
+    bad = dict(gpu, v_norms=vn + np.uint16(1))
+    with pytest.raises(AssertionError):
+        oracle_stream(k, v, 4, 2, sb, bad, "cpu")
+    assert st["K"].shape == (k.shape[0], d)
+
+
+def test_check_attention_plain_bars():
+    rng = np.random.default_rng(1)
+    ref = rng.standard_normal((4, 64))
+    check_attention(ref + 1e-4, ref, "within")
+    with pytest.raises(AssertionError):
+        check_attention(ref * (1 + 3e-3), ref, "rel-L2 above 2e-3")
+    off = ref.copy()
+    off[0, 0] += 0.02
+    with pytest.raises(AssertionError):
+        check_attention(off, ref, "max-abs above 1e-2")

@@ -9,8 +9,8 @@ import pytest
 import kv_cache_quantization_tq_amd as tq
 import oracle
 import synth
-from helpers import (attention_errors, check_attention, compare_codes,
-                     oracle_attention_with_bound, require_gpu)
+from helpers import (attention_errors, check_attention, check_mismatch_fraction, compare_codes,
+                     gpu_stream, oracle_attention_stream, require_gpu)
 
 pytestmark = pytest.mark.gpu
 SEED = 1001
@@ -179,19 +179,23 @@ def _decode_case(torch, d, bk, bv, G, lens, Lyr=2, H=2, seed=SEED):
     return cache, sbs, q.cpu().numpy().view(np.uint16), out.cpu().numpy(), (cbk, cbv, sbd, lens_d, T)
 
 
-def _oracle_decode(seed, d, bk, bv, G, lens, sbs, q16, Lyr=2, H=2):
+def _oracle_decode(cache, seed, d, bk, bv, G, lens, sbs, q16, Lyr=2, H=2, what=""):
+    """The oracle's attention of every unit over the cache resolved against
+    the GPU's codes; returns (ref, band codes resolved)."""
     ref = np.zeros((Lyr, len(lens), G * H, d))
-    bound = np.zeros_like(ref)
+    n_alt = n_coords = 0
     for l in range(Lyr):
         for b, n in enumerate(lens):
             for h in range(H):
-                k = synth.kv_host(seed, 0, l, b, h, d, 0, n)
-                v = synth.kv_host(seed, 1, l, b, h, d, 0, n)
-                o, bd, _ = oracle_attention_with_bound(k, v, q16[l, b, h * G:(h + 1) * G], bk, bv,
-                                                       sbs[l])
+                o, na, nc = oracle_attention_stream(seed, l, b, h, n, bk, bv, sbs[l],
+                                                    q16[l, b, h * G:(h + 1) * G],
+                                                    gpu_stream(cache, l, b, h, n),
+                                                    f"{what} unit {l},{b},{h}")
                 ref[l, b, h * G:(h + 1) * G] = o
-                bound[l, b, h * G:(h + 1) * G] = bd
-    return ref, bound
+                n_alt += na
+                n_coords += nc
+    check_mismatch_fraction(n_alt, n_coords, what)
+    return ref, n_alt
 
 
 @pytest.mark.parametrize("d,bk,bv,G,lens", [
@@ -206,9 +210,10 @@ def _oracle_decode(seed, d, bk, bv, G, lens, sbs, q16, Lyr=2, H=2):
 ])
 def test_decode_parity(d, bk, bv, G, lens):
     torch = require_gpu()
-    _, sbs, q16, out, _ = _decode_case(torch, d, bk, bv, G, lens)
-    ref, bound = _oracle_decode(SEED, d, bk, bv, G, lens, sbs, q16)
-    check_attention(out, ref, bound, f"decode d={d} K{bk}/V{bv} G={G} lens={lens}")
+    cache, sbs, q16, out, _ = _decode_case(torch, d, bk, bv, G, lens)
+    what = f"decode d={d} K{bk}/V{bv} G={G} lens={lens}"
+    ref, n_alt = _oracle_decode(cache, SEED, d, bk, bv, G, lens, sbs, q16, what=what)
+    check_attention(out, ref, what, n_alt)
     for b, n in enumerate(lens):
         if n == 0:
             assert np.all(out[:, b] == 0)
@@ -229,3 +234,86 @@ def test_decode_split_invariance():
         torch.cuda.synchronize()
         rel, mx = attention_errors(o.cpu().numpy()[0], out[l])
         assert rel < 1e-5 and mx < 1e-4, (rel, mx)
+
+
+def _guarded(torch, shape, dtype, gen, guard=4096):
+    """A tensor of `shape` in the middle of a larger buffer whose `guard` bytes
+    on each side, like the tensor itself, hold seeded random values."""
+    item = torch.empty(0, dtype=dtype).element_size()
+    n = int(np.prod(shape))
+    g = guard // item
+    if dtype == torch.uint8:
+        buf = torch.randint(0, 256, (n + 2 * g,), dtype=dtype, device="cuda", generator=gen)
+    else:
+        buf = torch.randint(-2 ** 15, 2 ** 15, (n + 2 * g,), dtype=dtype, device="cuda",
+                            generator=gen)
+    return buf, buf[g:g + n].view(shape)
+
+
+def test_append_capacity_skip_guard_bytes():
+    """host_max_pos = -1: rows at or past capacity are skipped on the device.
+    Appends straddling capacity write exactly the rows below it (equal to
+    tq_encode of those tokens); an append starting at or past capacity, or
+    near INT32_MAX, writes nothing; every other byte of the cache, and the
+    guard bytes around each array, stay unchanged."""
+    torch = require_gpu()
+    d, bk, bv, Lyr, B, H, cap, t_new = 128, 4, 3, 2, 4, 2, 256, 40
+    gen = torch.Generator(device="cuda").manual_seed(5)
+    cache = tq.KVCache(Lyr, B, H, d, bk, bv, cap)
+    bufs = {}
+    for name in ("k_codes", "v_codes", "k_norms", "v_norms"):
+        t = getattr(cache, name)
+        bufs[name], view = _guarded(torch, tuple(t.shape), t.dtype, gen)
+        setattr(cache, name, view)
+    before = {k: b.clone() for k, b in bufs.items()}
+    sbs = np.stack([synth.sign_bits(SEED, l, d) for l in range(Lyr)])
+    sbd = torch.from_numpy(sbs).cuda()
+    cbk, cbv = tq.Codebook(d, bk), tq.Codebook(d, bv)
+    kn = torch.stack([_dev_kv(torch, SEED, 0, l, B, H, t_new, d) for l in range(Lyr)])
+    vn = torch.stack([_dev_kv(torch, SEED, 1, l, B, H, t_new, d) for l in range(Lyr)])
+    imax = 2 ** 31 - 1
+    # nothing lands for starts at or past capacity (the last call's starts sit
+    # where 32-bit row arithmetic would wrap)
+    for pos in ([240, 250, 300, 225], [imax - 4, imax, cap, 2 ** 30]):
+        tq.append(cache, cbk, cbv, sbd, kn, vn, torch.tensor(pos, dtype=torch.int32,
+                                                               device="cuda"), host_max_pos=-1)
+    torch.cuda.synchronize()
+    g = 4096
+    for name, buf in bufs.items():
+        item = buf.element_size()
+        assert torch.equal(buf[:g // item], before[name][:g // item]), f"{name}: guard before"
+        assert torch.equal(buf[-(g // item):], before[name][-(g // item):]), f"{name}: guard after"
+    pos = [240, 250, 300, 225]
+    for l in range(Lyr):
+        for b in range(B):
+            for h in range(H):
+                w0, w1 = min(pos[b], cap), min(pos[b] + t_new, cap)
+                keep = np.ones(cap, bool)
+                keep[w0:w1] = False
+                for kind, cb, bits in ((0, cbk, bk), (1, cbv, bv)):
+                    src = (kn if kind == 0 else vn)[l, b, h]
+                    codes = torch.empty((t_new, d * bits // 8), dtype=torch.uint8, device="cuda")
+                    norms = torch.empty(t_new, dtype=torch.int16, device="cuda")
+                    tq.encode(cb, src, sbd[l], codes, norms)
+                    torch.cuda.synchronize()
+                    ref_c = codes.cpu().numpy()[:w1 - w0]
+                    ref_n = norms.cpu().numpy()[:w1 - w0]
+                    nname = "k_norms" if kind == 0 else "v_norms"
+                    old_n = before[nname][g // 2:g // 2 + cache.k_norms.numel()].view(
+                        cache.k_norms.shape)[l, b, h].cpu().numpy()
+                    got_n = getattr(cache, nname)[l, b, h].cpu().numpy()
+                    assert np.array_equal(got_n[w0:w1], ref_n)
+                    assert np.array_equal(got_n[keep], old_n[keep])
+                    if kind == 0:
+                        old = before["k_codes"][g:g + cache.k_codes.numel()].view(
+                            cache.k_codes.shape)[l, b, h].cpu().numpy()
+                        got = cache.k_codes[l, b, h].cpu().numpy()
+                        assert np.array_equal(got[w0:w1], ref_c)
+                        assert np.array_equal(got[keep], old[keep])
+                    else:
+                        old = before["v_codes"][g:g + cache.v_codes.numel()].view(
+                            cache.v_codes.shape)[l, b, h].cpu().numpy()
+                        got = oracle.unpack_vtiles(cache.v_codes[l, b, h].cpu().numpy(), d, bits)
+                        old = oracle.unpack_vtiles(old, d, bits)
+                        assert np.array_equal(got[w0:w1], oracle.unpack_rows(ref_c, d, bits))
+                        assert np.array_equal(got[keep], old[keep])

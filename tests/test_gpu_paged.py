@@ -7,8 +7,8 @@ import pytest
 import kv_cache_quantization_tq_amd as tq
 import synth
 import oracle
-from helpers import (attention_errors, band_flip_bound, check_attention, compare_codes,
-                     oracle_attention_with_bound, require_gpu)
+from helpers import (attention_errors, check_attention, check_mismatch_fraction, compare_codes,
+                     gpu_stream, oracle_attention_stream, require_gpu)
 
 pytestmark = pytest.mark.gpu
 SEED = 1011
@@ -77,17 +77,19 @@ def test_paged_equals_contiguous(d, bk, bv, P):
     rel, mx = attention_errors(outs[1].cpu().numpy(), outs[0].cpu().numpy())
     assert rel <= 1e-6 and mx <= 1e-5, (rel, mx)
     q16 = q.cpu().numpy().view(np.uint16)
-    got, ref, bnd = [], [], []
+    got, ref, n_alt, n_coords = [], [], 0, 0
+    what = f"paged d={d} P={P}"
     for (l, b, h) in ((0, 0, 1), (1, 1, 0), (1, 2, 1)):
-        n = lens[b]
         # the sequence's tokens in order of position (chunks wrote them at their positions)
-        k = synth.kv_host(SEED, 0, l, b, h, d, 0, n)
-        v = synth.kv_host(SEED, 1, l, b, h, d, 0, n)
-        o, bound, _ = oracle_attention_with_bound(k, v, q16[l, b, h * G:(h + 1) * G], bk, bv, sbs[l])
+        o, na, nc = oracle_attention_stream(SEED, l, b, h, lens[b], bk, bv, sbs[l],
+                                            q16[l, b, h * G:(h + 1) * G],
+                                            gpu_stream(paged, l, b, h, lens[b]), what)
         got.append(outs[1].cpu().numpy()[l, b, h * G:(h + 1) * G])
         ref.append(o)
-        bnd.append(bound)
-    check_attention(np.stack(got), np.stack(ref), np.stack(bnd), f"paged d={d} P={P}")
+        n_alt += na
+        n_coords += nc
+    check_mismatch_fraction(n_alt, n_coords, what)
+    check_attention(np.stack(got), np.stack(ref), what, n_alt)
 
 
 def test_paged_invalid_entries_skip_rows():
@@ -147,16 +149,10 @@ def test_paged_full_size_sampled():
     torch.cuda.synchronize()
     q16 = q.cpu().numpy().view(np.uint16)
     for (l, h) in ((0, 0), (1, 6)):
-        kk = synth.kv_host(seed, 0, l, 0, h, d, 0, T)
-        vv = synth.kv_host(seed, 1, l, 0, h, d, 0, T)
         sl = slice(h * G, (h + 1) * G)
-        st = oracle.decode_stream(kk, vv, q16[l, 0, sl], bk, bv, sbs[l], full=True)
-        kc, vc, kn, vn = cache.gather(l, 0, h)
-        kc = kc[:T].cpu().numpy()
-        kn = kn[:T].cpu().numpy().view(np.uint16)
-        compare_codes(oracle.unpack_rows(kc, d, bk), st["k_codes"], st["k_band"],
-                      f"paged 32K layer {l} head {h} keys")
-        assert np.array_equal(kn, st["k_norms"])
-        q64 = oracle.halves_to_double(q16[l, 0, sl])
-        bd, _ = band_flip_bound(q64, kk, vv, st, bk, bv, sbs[l])
-        check_attention(out[l, 0, sl].cpu().numpy(), st["out"], bd, f"paged 32K layer {l} head {h}")
+        what = f"paged 32K layer {l} head {h}"
+        # every code and norm of the stream is checked on the way
+        o, na, nc = oracle_attention_stream(seed, l, 0, h, T, bk, bv, sbs[l], q16[l, 0, sl],
+                                            gpu_stream(cache, l, 0, h, T), what)
+        check_mismatch_fraction(na, nc, what)
+        check_attention(out[l, 0, sl].cpu().numpy(), o, what, na)

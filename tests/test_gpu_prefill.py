@@ -11,7 +11,8 @@ import pytest
 import kv_cache_quantization_tq_amd as tq
 import oracle
 import synth
-from helpers import band_flip_bound, check_attention, prefix, require_gpu
+from helpers import (check_attention, check_mismatch_fraction, gpu_stream, oracle_stream,
+                     require_gpu)
 
 pytestmark = pytest.mark.gpu
 SEED = 1003
@@ -57,10 +58,12 @@ def _case(torch, d, bk, bv, G, H, pos, t_new, Lyr=1, paged_tokens=None, seed=SEE
                 t_new=t_new, seed=seed)
 
 
-def _oracle(c):
+def _oracle(c, what=""):
+    """Every query row's attention over its causal prefix of the cache,
+    resolved against the GPU's codes; returns (ref, band codes resolved)."""
     d, G, H, t_new = c["d"], c["G"], c["H"], c["t_new"]
     ref = np.zeros(c["out"].shape)
-    bound = np.zeros_like(ref)
+    n_alt = n_coords = 0
     for l in range(c["Lyr"]):
         for b, p in enumerate(c["pos"]):
             for h in range(H):
@@ -68,18 +71,16 @@ def _oracle(c):
                 k = synth.kv_host(c["seed"], 0, l, b, h, d, 0, n_all)
                 v = synth.kv_host(c["seed"], 1, l, b, h, d, 0, n_all)
                 sl = slice(h * G, (h + 1) * G)
-                st = oracle.decode_stream(k, v, c["q16"][l, b, sl, 0], c["bk"], c["bv"],
-                                          c["sbs"][l], full=True)
+                st = oracle_stream(k, v, c["bk"], c["bv"], c["sbs"][l],
+                                   gpu_stream(c["cache"], l, b, h, n_all), f"{what} {l},{b},{h}")
+                n_alt += st["n_alt"]
+                n_coords += st["n_coords"]
                 for i in range(t_new):
                     n = p + i + 1
                     q64 = oracle.halves_to_double(c["q16"][l, b, sl, i])
-                    o = oracle.attention(q64, st["K"][:n], st["V"][:n])
-                    sp = prefix(st, n)
-                    sp["out"] = o
-                    bd, _ = band_flip_bound(q64, k[:n], v[:n], sp, c["bk"], c["bv"], c["sbs"][l])
-                    ref[l, b, sl, i] = o
-                    bound[l, b, sl, i] = bd
-    return ref, bound
+                    ref[l, b, sl, i] = oracle.attention(q64, st["K"][:n], st["V"][:n])
+    check_mismatch_fraction(n_alt, n_coords, what)
+    return ref, n_alt
 
 
 @pytest.mark.parametrize("d,bk,bv,G,H,pos,t_new,Lyr", [
@@ -92,17 +93,17 @@ def _oracle(c):
 def test_prefill_parity(d, bk, bv, G, H, pos, t_new, Lyr):
     torch = require_gpu()
     c = _case(torch, d, bk, bv, G, H, pos, t_new, Lyr)
-    ref, bound = _oracle(c)
-    check_attention(c["out"], ref, bound,
-                    f"prefill d={d} K{bk}/V{bv} G={G} pos={pos} t_new={t_new}")
+    what = f"prefill d={d} K{bk}/V{bv} G={G} pos={pos} t_new={t_new}"
+    ref, n_alt = _oracle(c, what)
+    check_attention(c["out"], ref, what, n_alt)
 
 
 @pytest.mark.parametrize("P", [32, 128])
 def test_prefill_paged(P):
     torch = require_gpu()
     c = _case(torch, 128, 4, 2, 4, 2, [0, 300], 77, 2, paged_tokens=P)
-    ref, bound = _oracle(c)
-    check_attention(c["out"], ref, bound, f"prefill paged P={P}")
+    ref, n_alt = _oracle(c, f"prefill paged P={P}")
+    check_attention(c["out"], ref, f"prefill paged P={P}", n_alt)
 
 
 def test_prefill_row_equals_decode():
@@ -158,16 +159,12 @@ def test_prefill_full_size_sampled():
         kk = synth.kv_host(seed, 0, 0, 0, h, d, 0, T)
         vv = synth.kv_host(seed, 1, 0, 0, h, d, 0, T)
         sl = slice(h * G, (h + 1) * G)
-        st = oracle.decode_stream(kk, vv, q16[0, 0, sl, 0], bk, bv, sbs[0], full=True)
+        what = f"prefill 32K, KV head {h}, rows {rows}"
+        st = oracle_stream(kk, vv, bk, bv, sbs[0], gpu_stream(cache, 0, 0, h, T), what)
+        check_mismatch_fraction(st["n_alt"], st["n_coords"], what)
         got = np.stack([out[0, 0, sl, i].cpu().numpy() for i in rows])
         ref = np.zeros_like(got, dtype=np.float64)
-        bound = np.zeros_like(ref)
         for r, i in enumerate(rows):
-            n = i + 1
             q64 = oracle.halves_to_double(q16[0, 0, sl, i])
-            o = oracle.attention(q64, st["K"][:n], st["V"][:n])
-            sp = prefix(st, n)
-            sp["out"] = o
-            bd, _ = band_flip_bound(q64, kk[:n], vv[:n], sp, bk, bv, sbs[0])
-            ref[r], bound[r] = o, bd
-        check_attention(got, ref, bound, f"prefill 32K, KV head {h}, rows {rows}")
+            ref[r] = oracle.attention(q64, st["K"][:i + 1], st["V"][:i + 1])
+        check_attention(got, ref, what, st["n_alt"])

@@ -1,11 +1,15 @@
 """GPU parity of decode attention with the Sparse V gate (tq_decode_attn_sparse)
-against the oracle's sparse attention ("TurboQuant+ ...", "Sparse V").
+against the oracle ("TurboQuant+ ...", "Sparse V").
 
 The kernel decides per 32-token tile against a running maximum, so which
-tokens below the threshold it leaves out depends on the visiting order; the
-oracle's bound on what the left-out tokens can contribute (per coordinate)
-widens the bars, and the per-unit skip counts are checked against the tiles
-the oracle says may be skipped."""
+tokens below the threshold it leaves out depends on the visiting order.  It
+reports the exact set of tiles it skipped (a bitmap per unit); the oracle
+leaves out exactly those positions and the output must then meet the plain
+bars (2e-3 relative L2, 1e-2 max-abs).  Separately, every skipped tile must be
+one the rule allows: each of its (token, head) weights relative to the final
+maximum is below eps (with a 1e-3 relative margin for the kernel's fp32
+scores), only full tiles are skipped, and the per-unit counts equal the
+bitmaps' popcounts."""
 import math
 
 import numpy as np
@@ -14,7 +18,7 @@ import pytest
 import kv_cache_quantization_tq_amd as tq
 import oracle
 import synth
-from helpers import band_flip_bound, check_attention, require_gpu
+from helpers import check_attention, check_mismatch_fraction, gpu_stream, oracle_stream, require_gpu
 
 pytestmark = pytest.mark.gpu
 SEED = 1001
@@ -58,24 +62,34 @@ def _run_sparse(torch, c, eps):
     out = torch.empty((c["Lyr"], c["B"], c["G"] * c["H"], c["d"]), dtype=torch.float32,
                       device="cuda")
     counts = torch.zeros((c["Lyr"], c["B"], c["H"]), dtype=torch.int32, device="cuda")
+    tiles = torch.zeros((c["Lyr"], c["B"], c["H"], tq.skip_words(c["T"])), dtype=torch.int32,
+                        device="cuda")
     if c["ws"] is not None:
         c["ws"].zero_()
     tq.decode_sparse(c["cache"], c["cbk"], c["cbv"], c["sbd"], c["q"], c["lens_d"], c["T"], out,
-                     eps, c["ws"], skip_counts=counts)
+                     eps, c["ws"], skip_counts=counts, skip_tiles=tiles)
     torch.cuda.synchronize()
-    return out.cpu().numpy(), counts.cpu().numpy()
+    return out.cpu().numpy(), counts.cpu().numpy(), tiles.cpu().numpy().view(np.uint32)
 
 
-def _oracle(c, eps, units=None):
-    """Oracle sparse output, bound (band flips + left-out tokens) and, per
-    unit, the number of full tiles whose every (token, head) weight lies
-    below eps (with a relative margin for rounding) relative to the final
-    max: the most the kernel may skip."""
+def _skipped_tiles(words, n_tiles):
+    """Indices of the tiles set in one unit's bitmap words (tiles < n_tiles)."""
+    bits = np.unpackbits(words.astype("<u4").view(np.uint8), bitorder="little")
+    assert not bits[n_tiles:].any(), "a bit past the unit's tiles is set"
+    return np.flatnonzero(bits[:n_tiles])
+
+
+def _oracle(c, eps, counts, tiles, units=None, what=""):
+    """Per unit: the oracle's attention with exactly the kernel's skipped
+    tiles left out (over the cache resolved against the GPU's codes), and
+    checks that those tiles were skippable.  Returns (ref, may_skip, n_alt):
+    may_skip[l, b, h] is the number of full tiles whose every (token, head)
+    weight is below eps relative to the final max."""
     d, G, H = c["d"], c["G"], c["H"]
     q16 = c["q"].cpu().numpy().view(np.uint16)
-    shape = (c["Lyr"], c["B"], G * H, d)
-    ref, bound = np.zeros(shape), np.zeros(shape)
+    ref = np.zeros((c["Lyr"], c["B"], G * H, d))
     may_skip = np.zeros((c["Lyr"], c["B"], H), dtype=np.int64)
+    n_alt = n_coords = 0
     for l in range(c["Lyr"]):
         for b, n in enumerate(c["lens"]):
             for h in range(H):
@@ -83,32 +97,42 @@ def _oracle(c, eps, units=None):
                     continue
                 k = synth.kv_host(c["seed"], 0, l, b, h, d, 0, n)
                 v = synth.kv_host(c["seed"], 1, l, b, h, d, 0, n)
-                qq = q16[l, b, h * G:(h + 1) * G]
-                st = oracle.decode_stream(k, v, qq, c["bk"], c["bv"], c["sbs"][l], full=True)
-                q64 = oracle.halves_to_double(qq)
-                bf, _ = band_flip_bound(q64, k, v, st, c["bk"], c["bv"], c["sbs"][l])
-                o, bs, w = oracle.attention_sparse(q64, st["K"], st["V"], eps, want_weights=True)
-                sl = slice(h * G, (h + 1) * G)
-                ref[l, b, sl], bound[l, b, sl] = o, bf + bs
+                st = oracle_stream(k, v, c["bk"], c["bv"], c["sbs"][l],
+                                   gpu_stream(c["cache"], l, b, h, n), f"{what} {l},{b},{h}")
+                n_alt += st["n_alt"]
+                n_coords += st["n_coords"]
                 nf = n // 32
+                skipped = _skipped_tiles(tiles[l, b, h], (n + 31) // 32)
+                assert (skipped < nf).all(), "a ragged last tile was skipped"
+                assert len(skipped) == counts[l, b, h], (len(skipped), counts[l, b, h])
+                keep = np.ones(n, bool)
+                for t in skipped:
+                    keep[32 * t:32 * t + 32] = False
+                q64 = oracle.halves_to_double(q16[l, b, h * G:(h + 1) * G])
+                o, w = oracle.attention_keep(q64, st["K"], st["V"], keep, want_weights=True)
+                ref[l, b, h * G:(h + 1) * G] = o
                 if nf:
                     tmax = w[:, :nf * 32].reshape(G, nf, 32).max(axis=(0, 2))
-                    may_skip[l, b, h] = int((tmax < eps * (1 + 1e-3)).sum())
-    return ref, bound, may_skip
+                    allowed = tmax < eps * (1 + 1e-3)
+                    may_skip[l, b, h] = int(allowed.sum())
+                    assert allowed[skipped].all(), \
+                        f"unit {l},{b},{h}: tiles {skipped[~allowed[skipped]]} were not skippable"
+    check_mismatch_fraction(n_alt, n_coords, what)
+    return ref, may_skip, n_alt
 
 
 def test_sparse_eps0_equals_dense():
     """eps = 0 runs the dense kernel: bit-identical output, nothing counted."""
     torch = require_gpu()
     c = _case(torch, 128, 4, 2, 4, [700, 257])
-    out_s, counts = _run_sparse(torch, c, 0.0)
+    out_s, counts, tiles = _run_sparse(torch, c, 0.0)
     out_d = torch.empty((c["Lyr"], c["B"], c["G"] * c["H"], c["d"]), dtype=torch.float32,
                         device="cuda")
     c["ws"] is not None and c["ws"].zero_()
     tq.decode(c["cache"], c["cbk"], c["cbv"], c["sbd"], c["q"], c["lens_d"], c["T"], out_d, c["ws"])
     torch.cuda.synchronize()
     assert np.array_equal(out_s, out_d.cpu().numpy())
-    assert not counts.any()
+    assert not counts.any() and not tiles.any()
 
 
 @pytest.mark.parametrize("d,bk,bv,G,lens", [
@@ -123,10 +147,10 @@ def test_sparse_eps0_equals_dense():
 def test_sparse_parity(d, bk, bv, G, lens, eps):
     torch = require_gpu()
     c = _case(torch, d, bk, bv, G, lens)
-    out, counts = _run_sparse(torch, c, eps)
-    ref, bound, may_skip = _oracle(c, eps)
+    out, counts, tiles = _run_sparse(torch, c, eps)
     what = f"sparse d={d} K{bk}/V{bv} G={G} lens={lens} eps={eps}"
-    check_attention(out, ref, bound, what)
+    ref, may_skip, n_alt = _oracle(c, eps, counts, tiles, what=what)
+    check_attention(out, ref, what, n_alt)
     print(f"{what}: skipped {counts.sum()} of {may_skip.sum()} skippable tiles", flush=True)
     assert (counts >= 0).all() and (counts <= may_skip).all(), (counts, may_skip)
 
@@ -134,30 +158,30 @@ def test_sparse_parity(d, bk, bv, G, lens, eps):
 def test_sparse_everything_skipped():
     """eps above 1: every full tile is skipped (the count is exact), so a
     length that is a multiple of 32 gives a zero output, and the ragged tail
-    alone is accumulated otherwise (within the bound)."""
+    alone is accumulated otherwise."""
     torch = require_gpu()
     c = _case(torch, 128, 4, 2, 4, [640, 300], Lyr=1)
-    out, counts = _run_sparse(torch, c, 2.0)
+    out, counts, tiles = _run_sparse(torch, c, 2.0)
     assert np.array_equal(counts[0, 0], [20, 20]) and np.array_equal(counts[0, 1], [9, 9])
     assert not out[0, 0].any()
-    ref, bound, _ = _oracle(c, 2.0)
-    assert not ref.any()
-    assert (np.abs(out - ref) <= bound + 1e-5).all()
+    ref, _, n_alt = _oracle(c, 2.0, counts, tiles, what="eps 2")
+    assert not ref[0, 0].any()
+    check_attention(out, ref, "sparse eps 2", n_alt)
 
 
 def test_sparse_skips_on_long_context():
     """A 32K-token context of the benchmark's data (8 KV heads, G = 4): the
     gate skips a good part of the tiles the oracle allows (the block shares
-    its running maxima), and the sampled units stay within the bars."""
+    its running maxima), and the sampled units meet the bars."""
     torch = require_gpu()
     eps = 1e-4
     c = _case(torch, 128, 4, 2, 4, [32768], Lyr=32, H=8)
-    out, counts = _run_sparse(torch, c, eps)
+    out, counts, tiles = _run_sparse(torch, c, eps)
     units = {(0, 0, 0), (17, 0, 5)}
-    ref, bound, may_skip = _oracle(c, eps, units)
+    ref, may_skip, n_alt = _oracle(c, eps, counts, tiles, units, "32K")
     for (l, b, h) in units:
         sl = slice(h * 4, h * 4 + 4)
-        check_attention(out[l, b, sl], ref[l, b, sl], bound[l, b, sl], f"32K unit {h}")
+        check_attention(out[l, b, sl], ref[l, b, sl], f"32K unit {l},{b},{h}", n_alt)
         print(f"unit {h}: skipped {counts[l, b, h]} of {may_skip[l, b, h]} skippable tiles",
               flush=True)
         assert counts[l, b, h] <= may_skip[l, b, h]
@@ -169,7 +193,7 @@ def test_sparse_paged(P):
     torch = require_gpu()
     eps = 1e-3
     c = _case(torch, 128, 4, 2, 4, [3000, 700], paged_tokens=P)
-    out, counts = _run_sparse(torch, c, eps)
-    ref, bound, may_skip = _oracle(c, eps)
-    check_attention(out, ref, bound, f"sparse paged P={P}")
+    out, counts, tiles = _run_sparse(torch, c, eps)
+    ref, may_skip, n_alt = _oracle(c, eps, counts, tiles, what=f"sparse paged P={P}")
+    check_attention(out, ref, f"sparse paged P={P}", n_alt)
     assert (counts <= may_skip).all()
