@@ -12,8 +12,10 @@ step of attention over the 32769-token compressed cache of all 32 layers
 
 ``value`` is the decode-attention throughput in GB/s of packed cache bytes
 (codes + norms) per step; the line also carries encode tokens/s, the decode
-kernel's roofline fraction against the 8 TB/s HBM peak, and the CPU oracle
-timed on a bounded sample on this host.
+kernel's roofline fraction against the 8 TB/s HBM peak, the 48-layer K4/V3
+32K prefill encode (timed after the steps, bulk and in 16 chunks of 2048
+tokens), and the CPU oracle timed on a bounded sample on this host's cores,
+with the same sample's GPU codes and outputs compared against it.
 """
 import argparse
 import json
@@ -57,44 +59,147 @@ def measured_traffic(kernel):
     return rec["traffic_bytes"] if h.hexdigest() == rec["source_sha256"] else None
 
 
-def cpu_baseline(seconds_budget=20.0):
-    """The oracle (single thread, plain loops, fp64) on a sample of the same
-    workload: whole (layer 0, KV head h) streams, 32768 tokens each, encoded and
-    then attended by their 4 query heads; streams are added until the budget is
-    spent.  Scaled to the metric's units."""
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_threads():
+    """Threads for the oracle: the cores in this process's affinity mask, at
+    most 16 (one GPU's share of a host's cores)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    return max(1, min(16, n)), n
+
+
+def cpu_baseline(gpu=None, seconds_budget=20.0):
+    """The oracle (plain loops, fp64) on this host's cores, on a sample of the
+    same workload: whole (layer, KV head) streams of the decoded context (the
+    32768-token prefill plus the appended token), each encoded (keys and
+    values: norm, explicit rotation, argmin), then dequantized and attended by
+    its 4 query heads.  One stream per thread, rounds of `threads` streams
+    (streams spread over the layers) until the budget is spent; each phase is
+    timed by the wall clock over a round.  Rates are scaled to the metric's
+    units: decode GB/s of packed bytes, encode tokens/s over all layers and
+    heads.
+
+    With `gpu` = (cache, out, q) the same streams are also compared with the
+    GPU's: norms bit for bit, codes (any difference must lie within 1e-6 of a
+    threshold; those are counted), and the attention outputs against the
+    oracle's over its cache, resolved to the GPU's neighbouring code at those
+    band coordinates."""
     import numpy as np
+    from concurrent.futures import ThreadPoolExecutor
     import oracle
     import synth
-    sb = synth.sign_bits(SEED, 0, D)
+    ctx = T + 1
+    threads, n_aff = _oracle_threads()
+    order = np.random.default_rng(SEED).permutation(L * HKV)
+    units = [(int(u) // HKV, int(u) % HKV) for u in order]
+    sbs = {l: synth.sign_bits(SEED, l, D) for l in range(L)}
     enc_s = dec_s = 0.0
-    n_streams = 0
+    done = 0
+    par = dict(streams=0, codes=0, band_diff=0, outside_band_diff=0, norms_diff=0,
+               num=0.0, den=0.0, max_abs=0.0)
+
+    def inputs_unit(u):
+        l, h = u
+        return [synth.kv_host(SEED, kind, l, 0, h, D, 0, ctx) for kind in (0, 1)]
+
+    def encode_unit(args):
+        (l, h), xs = args
+        return [oracle.encode(x, bits, sbs[l], want_alt=True) for x, bits in zip(xs, (BK, BV))]
+
+    def decode_unit(args):
+        (l, h), enc, resolved = args
+        (kc, kn, _, _), (vc, vn, _, _) = enc
+        K = oracle.dequant(resolved[0] if resolved else kc, kn, BK, sbs[l])
+        V = oracle.dequant(resolved[1] if resolved else vc, vn, BV, sbs[l])
+        q = np.stack([synth.q_host(SEED, 0, l, 0, h * (HQ // HKV) + g, D)
+                      for g in range(HQ // HKV)])
+        return oracle.attention(oracle.halves_to_double(q), K, V)
+
+    # the oracle's codebooks (Lloyd iterations, computed once and kept) are
+    # built before timing
+    oracle.codebook(D, BK)
+    oracle.codebook(D, BV)
     t_start = time.perf_counter()
-    for h in range(HKV):
-        k = synth.kv_host(SEED, 0, 0, 0, h, D, 0, T)
-        v = synth.kv_host(SEED, 1, 0, 0, h, D, 0, T)
-        q = np.stack([synth.q_host(SEED, 0, 0, 0, h * 4 + g, D) for g in range(4)])
-        t0 = time.perf_counter()
-        kc, kn, _ = oracle.encode(k, BK, sb, want_band=False)
-        vc, vn, _ = oracle.encode(v, BV, sb, want_band=False)
-        t1 = time.perf_counter()
-        K = oracle.dequant(kc, kn, BK, sb)
-        V = oracle.dequant(vc, vn, BV, sb)
-        oracle.attention(oracle.halves_to_double(q), K, V)
-        t2 = time.perf_counter()
-        enc_s += t1 - t0
-        dec_s += t2 - t1
-        n_streams += 1
-        if time.perf_counter() - t_start > seconds_budget:
-            break
-    dec_gbs = n_streams * T * per_token_head_bytes() / dec_s / 1e9
-    enc_tok_s = n_streams * T / enc_s / (L * HKV)  # context tokens/s over all layers and heads
-    return {
-        "value": dec_gbs, "unit": "GB/s", "cores": 1, "kind": "oracle",
-        "sample": f"{n_streams} of {L * HKV} (layer, KV head) streams, {T} tokens each, "
-                  f"encode + dequantize + attention by 4 query heads",
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        while done < len(units) and time.perf_counter() - t_start < seconds_budget:
+            batch = units[done:done + threads]
+            xs = list(ex.map(inputs_unit, batch))  # the seeded inputs, not timed
+            t0 = time.perf_counter()
+            encs = list(ex.map(encode_unit, zip(batch, xs)))
+            t1 = time.perf_counter()
+            del xs
+            resolved = []
+            for (l, h), enc in zip(batch, encs):
+                if gpu is None:
+                    resolved.append(None)
+                    continue
+                cache = gpu[0]
+                g_k = oracle.unpack_rows(cache.k_codes[l, 0, h, :ctx].cpu().numpy(), D, BK)
+                g_v = oracle.unpack_vtiles(cache.v_codes[l, 0, h, :(ctx + 31) // 32].cpu().numpy(),
+                                           D, BV)[:ctx]
+                g_norms = (cache.k_norms[l, 0, h, :ctx].cpu().numpy().view(np.uint16),
+                           cache.v_norms[l, 0, h, :ctx].cpu().numpy().view(np.uint16))
+                res = []
+                for (codes, norms, band, alt), gc, gn in zip(enc, (g_k, g_v), g_norms):
+                    diff = gc != codes
+                    inside = diff & (band < 1e-6) & (gc == alt)
+                    par["codes"] += codes.size
+                    par["band_diff"] += int(inside.sum())
+                    par["outside_band_diff"] += int((diff & ~inside).sum())
+                    par["norms_diff"] += int((gn != norms).sum())
+                    rc = codes.copy()
+                    rc[inside] = alt[inside]
+                    res.append(rc)
+                resolved.append(res)
+            t2 = time.perf_counter()
+            outs = list(ex.map(decode_unit, zip(batch, encs, resolved)))
+            t3 = time.perf_counter()
+            enc_s += t1 - t0
+            dec_s += t3 - t2
+            done += len(batch)
+            if gpu is not None:
+                out_gpu = gpu[1]
+                G = HQ // HKV
+                for (l, h), o in zip(batch, outs):
+                    g = out_gpu[l, 0, h * G:(h + 1) * G].cpu().numpy().astype(np.float64)
+                    par["num"] += float(((g - o) ** 2).sum())
+                    par["den"] += float((o ** 2).sum())
+                    par["max_abs"] = max(par["max_abs"], float(np.abs(g - o).max()))
+                par["streams"] = done
+    dec_gbs = done * ctx * per_token_head_bytes() / dec_s / 1e9
+    enc_tok_s = done * ctx / enc_s / (L * HKV)  # context tokens/s over all layers and heads
+    r = {
+        "value": dec_gbs, "unit": "GB/s", "cores": threads, "kind": "oracle",
+        "sample": f"{done} of {L * HKV} (layer, KV head) streams of the {ctx}-token context, "
+                  f"each encoded (keys and values), dequantized and attended by "
+                  f"{HQ // HKV} query heads; {threads} streams at a time, one per thread",
+        "cpu_model": _cpu_model(), "cores_in_affinity_mask": n_aff,
         "encode_tokens_per_s": enc_tok_s,
         "seconds": enc_s + dec_s,
     }
+    if gpu is not None:
+        r["parity"] = {
+            "streams": par["streams"], "codes": par["codes"],
+            "band_codes_gpu_took_other_neighbour": par["band_diff"],
+            "codes_differing_outside_band": par["outside_band_diff"],
+            "norms_differing": par["norms_diff"],
+            "attention_rel_l2": (par["num"] / par["den"]) ** 0.5 if par["den"] else 0.0,
+            "attention_max_abs": par["max_abs"],
+            "bars": "codes: differences only within 1e-6 of a threshold, under 1e-5 of codes; "
+                    "norms bit-exact; attention rel-L2 <= 2e-3, max-abs <= 1e-2"}
+    return r
 
 
 def _report(workload, metric, value, unit, higher, extra, args, ms_per_step):
@@ -187,47 +292,65 @@ def workload_batched_decode(args):
              "packed_bytes_64_steps": nbytes}, args, ms / steps)
 
 
-def workload_encode_48l(args):
-    """48 layers, 8 KV heads, d 128, 32768 tokens, K4/V3: one tq_append of the
-    whole prefill over all layers (timed), and the same prefill as 16 chunked
-    appends of 2048 tokens (timed separately)."""
+def encode_48l(args):
+    """48 layers, 8 KV heads, d 128, 32768 tokens, K4/V3: the whole prefill in
+    one tq_append over all layers, and the same prefill as 16 chunked appends
+    of 2048 tokens, each timed (median of `steps` after `warmup`).  Returns
+    the figures; the inputs are freed before returning."""
     import numpy as np
     import torch
     import kv_cache_quantization_tq_amd as tq
     import synth
-    seed, L, B, H, d, T, bk, bv, chunk = 1004, 48, 1, 8, 128, 32768, 4, 3, 2048
-    torch.cuda.set_device(0)
-    cache = tq.KVCache(L, B, H, d, bk, bv, T)
+    seed, L4, B4, H, d, T4, bk, bv, chunk = 1004, 48, 1, 8, 128, 32768, 4, 3, 2048
+    cache = tq.KVCache(L4, B4, H, d, bk, bv, T4)
     cbk, cbv = tq.Codebook(d, bk), tq.Codebook(d, bv)
-    sbd = torch.from_numpy(np.stack([synth.sign_bits(seed, l, d) for l in range(L)])).cuda()
-    kp = torch.empty((L, B, H, T, d), dtype=torch.int16, device="cuda")
+    sbd = torch.from_numpy(np.stack([synth.sign_bits(seed, l, d) for l in range(L4)])).cuda()
+    kp = torch.empty((L4, B4, H, T4, d), dtype=torch.int16, device="cuda")
     vp = torch.empty_like(kp)
-    for l in range(L):
+    for l in range(L4):
         synth.kv_dev(seed, 0, l, kp[l])
         synth.kv_dev(seed, 1, l, vp[l])
-    kc = [kp[:, :, :, c * chunk:(c + 1) * chunk].contiguous() for c in range(T // chunk)]
-    vc = [vp[:, :, :, c * chunk:(c + 1) * chunk].contiguous() for c in range(T // chunk)]
-    zero = torch.zeros(B, dtype=torch.int32, device="cuda")
-    cpos = [torch.full((B,), c * chunk, dtype=torch.int32, device="cuda") for c in range(T // chunk)]
+    kc = [kp[:, :, :, c * chunk:(c + 1) * chunk].contiguous() for c in range(T4 // chunk)]
+    vc = [vp[:, :, :, c * chunk:(c + 1) * chunk].contiguous() for c in range(T4 // chunk)]
+    zero = torch.zeros(B4, dtype=torch.int32, device="cuda")
+    cpos = [torch.full((B4,), c * chunk, dtype=torch.int32, device="cuda")
+            for c in range(T4 // chunk)]
     torch.cuda.synchronize()
     bulk_ms = _timed(torch, lambda: tq.append(cache, cbk, cbv, sbd, kp, vp, zero, host_max_pos=0),
                      args.steps, args.warmup)
 
     def chunked():
-        for c in range(T // chunk):
+        for c in range(T4 // chunk):
             tq.append(cache, cbk, cbv, sbd, kc[c], vc[c], cpos[c], host_max_pos=c * chunk)
 
     chunk_ms = _timed(torch, chunked, args.steps, args.warmup)
-    nbytes = L * B * H * T * encode_bytes_per_token_head(d, bk, bv)
+    nbytes = L4 * B4 * H * T4 * encode_bytes_per_token_head(d, bk, bv)
     gbs = nbytes / (bulk_ms * 1e-3) / 1e9
-    _report({"workload": "48-layer 32K prefill encode", "layers": L, "kv_heads": H,
-             "head_dim": d, "batch": B, "tokens": T, "bits_k": bk, "bits_v": bv},
-            "encode tokens/s (32K prefill, all 48 layers, one tq_append)", T * B / (bulk_ms * 1e-3),
-            "tokens/s", True,
+    del kp, vp, kc, vc, cache
+    torch.cuda.synchronize()
+    return {"layers": L4, "kv_heads": H, "head_dim": d, "batch": B4, "tokens": T4,
+            "bits_k": bk, "bits_v": bv, "encode_ms": bulk_ms,
+            "encode_tokens_per_s": T4 * B4 / (bulk_ms * 1e-3), "encode_gbs": gbs,
+            "pct_hbm_peak": 100 * gbs / HBM_PEAK_GBS, "bytes_per_launch": nbytes,
+            "chunked_16x2048_ms": chunk_ms,
+            "chunked_pct_hbm_peak": 100 * nbytes / (chunk_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+
+
+def workload_encode_48l(args):
+    """The 48-layer K4/V3 prefill encode on a line of its own (encode_48l)."""
+    import torch
+    torch.cuda.set_device(0)
+    r = encode_48l(args)
+    _report({"workload": "48-layer 32K prefill encode", "layers": r["layers"],
+             "kv_heads": r["kv_heads"], "head_dim": r["head_dim"], "batch": r["batch"],
+             "tokens": r["tokens"], "bits_k": r["bits_k"], "bits_v": r["bits_v"]},
+            "encode tokens/s (32K prefill, all 48 layers, one tq_append)",
+            r["encode_tokens_per_s"], "tokens/s", True,
             {"dtype": "f32 (f16 matrix-core transform; packed 4-bit K, 3-bit V)",
-             "encode_ms": bulk_ms, "encode_gbs": gbs, "pct_hbm_peak": 100 * gbs / HBM_PEAK_GBS,
-             "bytes_per_launch": nbytes, "chunked_16x2048_ms": chunk_ms,
-             "chunked_gbs": nbytes / (chunk_ms * 1e-3) / 1e9}, args, bulk_ms)
+             "encode_ms": r["encode_ms"], "encode_gbs": r["encode_gbs"],
+             "pct_hbm_peak": r["pct_hbm_peak"], "bytes_per_launch": r["bytes_per_launch"],
+             "chunked_16x2048_ms": r["chunked_16x2048_ms"],
+             "chunked_pct_hbm_peak": r["chunked_pct_hbm_peak"]}, args, r["encode_ms"])
 
 
 def workload_70b_128k(args):
@@ -673,8 +796,19 @@ def main():
                             "traffic": measured_traffic("append_kernel<128,4,2>"),
                             "bytes_per_launch": enc_bytes, "avg_launch_us": enc_ms * 1e3},
     }
+    # the 48-layer K4/V3 prefill encode (the dedicated encode workload), timed
+    # after the steps above
+    e48 = encode_48l(args)
+    line["encode_48l_k4v3"] = {k: e48[k] for k in (
+        "encode_ms", "encode_tokens_per_s", "pct_hbm_peak", "chunked_16x2048_ms",
+        "chunked_pct_hbm_peak")}
+    line["roofline_encode_48l"] = {
+        "bound": "hbm", "kernel": "append_kernel<128,4,3>", "achieved": e48["encode_gbs"],
+        "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": e48["encode_gbs"] / HBM_PEAK_GBS,
+        "traffic": measured_traffic("append_kernel<128,4,3>"),
+        "bytes_per_launch": e48["bytes_per_launch"], "avg_launch_us": e48["encode_ms"] * 1e3}
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline()
+        line["cpu_baseline"] = cpu_baseline((cache, out, q))
     print(json.dumps(line), flush=True)
 
 
