@@ -31,11 +31,14 @@
  * midpoints; otherwise the inputs are re-summed in fp64 and, if still
  * ambiguous, exactly in 128-bit integers.
  *
- * Quantizer: u = (y + 1) * nb_half + 1/2 = fma(h, scale, nb_half + 1/2)
+ * Quantizer: u = (y + 1) * nb_half + 1/2 + shift = fma(h, scale, off)
  * selects, rounded to an integer, one of the codebook's buckets in LDS (at
- * most one threshold per bucket), code = base + (u > thr).  The comparison
- * happens in fp32 on u; it differs from the exact decision only for
- * coordinates within ~1e-7 of a threshold.
+ * most one threshold t per bucket, kept clear of the bucket edges by the
+ * shift), code = base + (fma(h, scale, -t nb_half) > 0).  That fma rounds
+ * once, so its sign is the exact sign of y nb_half - t nb_half for the fp32
+ * h and scale: the decision differs from the exact one only through the
+ * rounding of the transform sums and of the norm (~1e-8 in y), not through
+ * the ~1e-7 spacing of fp32 values near u.
  *
  * Output.  Key rows: the four lanes of a vector exchange their 4-code pieces
  * with 4 x 4 word transposes (permlane swaps), after which each lane owns d/4
@@ -273,7 +276,8 @@ template <int D, int BITS, bool BYTES>
 __device__ inline uint32_t encode_pass(const XRegs<D>& xr,
                                        const uint32_t (&sm)[EGeo<D>::J][4], const HTiles& ht,
                                        const char* tab, uint32_t lane_off, float nbh,
-                                       const uint16_t* vec, uint32_t (&piece)[EGeo<D>::OB]) {
+                                       float off, const uint16_t* vec,
+                                       uint32_t (&piece)[EGeo<D>::OB]) {
   using G = EGeo<D>;
   uint32_t x[G::J][4];
 #pragma unroll
@@ -321,7 +325,6 @@ __device__ inline uint32_t encode_pass(const XRegs<D>& xr,
   for (int j = 0; j < G::J; ++j)
     b[j] = __builtin_bit_cast(half8, u32x4{x[j][0], x[j][1], x[j][2], x[j][3]});
   const float scale = S > 0.0f ? nbh * __builtin_amdgcn_rsqf(S * (float)D) : 0.0f;
-  const float off = nbh + 0.5f;
   floatx4 y[G::OB];
 #pragma unroll
   for (int ob = 0; ob < G::OB; ++ob) {
@@ -333,11 +336,11 @@ __device__ inline uint32_t encode_pass(const XRegs<D>& xr,
                                                      y[ob], 0, 0, 0);
     }
   }
-  /* quantize: u = (y + 1) * nb_half + 1/2; bucket r = u rounded to the
-   * nearest integer, so r - 1/2 <= u <= r + 1/2.  One (saturating)
-   * conversion writes r into byte 1 of the lane's table offset, i.e. the
-   * address of row r, copy lane % 32.  The table reads of QB output blocks go
-   * out together. */
+  /* quantize: u = (y + 1) * nb_half + 1/2 + shift; bucket r = u rounded to
+   * the nearest integer.  One (saturating) conversion writes r into byte 1
+   * of the lane's table offset, i.e. the address of row r, copy lane % 32.
+   * The table reads of QB output blocks go out together; each code is then
+   * decided by the sign of one fma against the bucket's threshold. */
   constexpr int QB = 2;
 #pragma unroll
   for (int ob0 = 0; ob0 < G::OB; ob0 += QB) {
@@ -353,7 +356,8 @@ __device__ inline uint32_t encode_pass(const XRegs<D>& xr,
       uint32_t pc = 0u;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const uint32_t code = e[4 * q + i].base + (u[4 * q + i] > e[4 * q + i].thr ? 1u : 0u);
+        const float side = __builtin_fmaf(y[ob0 + q][i], scale, e[4 * q + i].neg_t);
+        const uint32_t code = e[4 * q + i].base + (side > 0.0f ? 1u : 0u);
         pc |= code << (BYTES ? 8 * i : BITS * i);
       }
       piece[ob0 + q] = pc;
@@ -463,7 +467,7 @@ template <int D, int BITS>
 __global__ void __launch_bounds__(64 * kRowsWaves) __attribute__((amdgpu_waves_per_eu(D == 256 ? 2 : TQ_ENC_WPE)))
 encode_rows_kernel(const uint16_t* __restrict__ x, int64_t n, int64_t stride,
                    const uint8_t* __restrict__ sign_bits, const tq_enc_entry* __restrict__ table,
-                   int entries, float nbh, uint8_t* __restrict__ codes,
+                   int entries, float nbh, float off, uint8_t* __restrict__ codes,
                    uint16_t* __restrict__ norms) {
   using G = EGeo<D>;
   /* static LDS: the table's address is a constant, folded into the reads */
@@ -493,7 +497,7 @@ encode_rows_kernel(const uint16_t* __restrict__ x, int64_t n, int64_t stride,
     const bool valid = r < n;
     uint32_t piece[G::OB];
     const uint32_t n16 = encode_pass<D, BITS, false>(xr, sm, ht, (const char*)tab, tab_off, nbh,
-                                                     x + row_of(p) * stride, piece);
+                                                     off, x + row_of(p) * stride, piece);
     uint32_t out[Chunk<D, BITS>::NW];
     gather_row_chunk<D, BITS>(piece, out);
     if (valid) {
@@ -682,6 +686,7 @@ struct AppendArgs {
   const tq_enc_entry* tab_v;
   int ent_k, ent_v;
   float nbh_k, nbh_v;
+  float off_k, off_v; /* nb_half + 1/2 + the codebook's bucket shift */
 };
 
 /* A 32-token tile takes two waves (16 vectors each); a block of 4 waves
@@ -766,6 +771,7 @@ append_kernel(AppendArgs a) {
   uint8_t* vbuf = vbuf_all + wave * kVec * kVPitch<D>;
   const uint32_t tab_off = (uint32_t)(lane & (kEncRep - 1)) * sizeof(tq_enc_entry);
   const float nbh = is_v ? a.nbh_v : a.nbh_k;
+  const float off = is_v ? a.off_v : a.off_k;
   const uint16_t* src_all = is_v ? a.v_new : a.k_new;
   const int64_t tasks = (int64_t)a.n_layers * a.batch * a.heads * a.slots;
   const int j0 = sub * kVec; /* this wave's first tile row */
@@ -843,8 +849,8 @@ append_kernel(AppendArgs a) {
     const uint16_t* vec = lane_src(g);
     uint32_t piece[G::OB];
     if (!is_v) {
-      const uint32_t n16 = encode_pass<D, BK, false>(xr, sm, ht, (const char*)tab, tab_off, nbh, vec,
-                                                     piece);
+      const uint32_t n16 = encode_pass<D, BK, false>(xr, sm, ht, (const char*)tab, tab_off, nbh,
+                                                     off, vec, piece);
       uint32_t out[Chunk<D, BK>::NW];
       gather_row_chunk<D, BK>(piece, out);
       if (mine) {
@@ -853,8 +859,8 @@ append_kernel(AppendArgs a) {
         if (q4 == 0) *(uint16_t*)((uint8_t*)a.k_norms + g.layer * a.ls_kn + row * 2) = (uint16_t)n16;
       }
     } else {
-      const uint32_t n16 = encode_pass<D, BV, true>(xr, sm, ht, (const char*)tab, tab_off, nbh, vec,
-                                                    piece);
+      const uint32_t n16 = encode_pass<D, BV, true>(xr, sm, ht, (const char*)tab, tab_off, nbh,
+                                                    off, vec, piece);
       /* code bytes of coordinates 16 ob + 4 q4 .. +3 -> the wave's row nl */
 #pragma unroll
       for (int ob = 0; ob < G::OB; ++ob)
@@ -912,7 +918,7 @@ tq_status launch_rows_t(const tq_codebook_s* cb, const uint16_t* x, int64_t n, i
   if (blocks > 4096) blocks = 4096;
   hipLaunchKernelGGL((encode_rows_kernel<D, BITS>), dim3((unsigned)blocks), dim3(64 * kRowsWaves),
                      0, s, x, n, stride, sb, cb->enc_table, cb->enc_entries,
-                     (float)cb->nb_half, codes, norms);
+                     (float)cb->nb_half, (float)cb->nb_half + 0.5f + cb->enc_shift, codes, norms);
   return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_DEVICE;
 }
 
@@ -979,6 +985,8 @@ tq_status tq_launch_append(const tq_kv_cache* c, const tq_codebook_s* cbk,
   a.ent_v = cbv->enc_entries;
   a.nbh_k = (float)cbk->nb_half;
   a.nbh_v = (float)cbv->nb_half;
+  a.off_k = (float)cbk->nb_half + 0.5f + cbk->enc_shift;
+  a.off_v = (float)cbv->nb_half + 0.5f + cbv->enc_shift;
 #define TQ_APP(DD, KK, VV) \
   if (c->head_dim == DD && c->bits_k == KK && c->bits_v == VV) return launch_append_t<DD, KK, VV>(a, s);
 #define TQ_APP_D(DD) \

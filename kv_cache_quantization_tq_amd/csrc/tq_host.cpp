@@ -165,26 +165,40 @@ extern "C" tq_status tq_codebook_init(int head_dim, int bits, tq_codebook* out) 
   build_codebook(head_dim, bits, cb);
   const int L = 1 << bits;
 
-  /* encoder bucket table */
+  /* encoder bucket table: the grid offset that keeps the thresholds
+   * farthest from bucket edges (edges at half-integers of u) */
   const int ne = cb->enc_entries;
+  const double nbh = cb->nb_half;
+  double best_gap = -1.0;
+  for (int i = 0; i < 90; ++i) {
+    const double shift = 0.005 * i;
+    double gap = 0.5;
+    for (int k = 0; k + 1 < L; ++k) {
+      const double g = (cb->bounds64[k] + 1.0) * nbh + shift; /* u - 1/2 */
+      gap = fmin(gap, fabs(g - nearbyint(g)));
+    }
+    if (gap > best_gap) { best_gap = gap; cb->enc_shift = (float)shift; }
+  }
   tq_enc_entry* et = (tq_enc_entry*)calloc((size_t)ne, sizeof(tq_enc_entry));
-  float thr_u[15];
-  for (int k = 0; k + 1 < L; ++k) thr_u[k] = (float)((cb->bounds64[k] + 1.0) * cb->nb_half + 0.5);
+  double thr_u[15];
+  for (int k = 0; k + 1 < L; ++k)
+    thr_u[k] = (cb->bounds64[k] + 1.0) * nbh + 0.5 + (double)cb->enc_shift;
   for (int j = 0; j < ne; ++j) {
     uint32_t base = 0;
-    float thr = INFINITY;
+    float neg_t = -INFINITY;
     int inside = 0;
     for (int k = 0; k + 1 < L; ++k) {
-      if (thr_u[k] < (float)j - 0.5f) ++base;
-      else if (thr_u[k] < (float)j + 0.5f) { thr = thr_u[k]; ++inside; }
+      if (thr_u[k] < j - 0.5) ++base;
+      else if (thr_u[k] < j + 0.5) { neg_t = (float)(-cb->bounds64[k] * nbh); ++inside; }
     }
-    /* one threshold per bucket, and no more rows than the kernels keep */
-    if (inside > 1 || ne > tq_enc_rows_max(head_dim, bits)) {
+    /* one threshold per bucket, thresholds clear of the bucket edges, and no
+     * more rows than the kernels keep */
+    if (inside > 1 || best_gap < 1.0 / 64 || ne > tq_enc_rows_max(head_dim, bits)) {
       free(et);
       free(cb);
       return TQ_ERR_UNSUPPORTED;
     }
-    et[j].thr = thr;
+    et[j].neg_t = neg_t;
     et[j].base = base;
   }
   /* decoder lookup table: fp16(level * sigma) */

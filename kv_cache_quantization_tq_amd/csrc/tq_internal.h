@@ -10,16 +10,20 @@
 
 #include "tq.h"
 
-/* Encoder bucket table: the rotated, normalised coordinate y in [-1, 1] maps
- * to u = (y + 1) * nb_half + 1/2 and bucket r = u rounded to an integer (any
- * rounding that keeps r - 1/2 <= u <= r + 1/2), r in 0 .. 2*nb_half + 1 (a
- * few ulps beyond |y| = 1 still round into that range).  Bucket r holds the
- * thresholds in [r - 1/2, r + 1/2) of u, at most one: code = base +
- * (u > thr), base the number of thresholds below r - 1/2; that count is right
- * on the closed interval too.  Buckets without a threshold store
- * thr = +inf. */
+/* Encoder bucket table.  The rotated, normalised coordinate y in [-1, 1]
+ * maps to u = (y + 1) * nb_half + 1/2 + enc_shift and bucket r = u rounded to
+ * an integer, r in 0 .. 2*nb_half + 1 (enc_shift < 0.45, so a few ulps beyond
+ * |y| = 1 still round into that range).  Bucket r holds the thresholds whose
+ * u lies in [r - 1/2, r + 1/2), at most one, and base = the number of
+ * thresholds below r - 1/2.  The code is base + (y nb_half > t nb_half), the
+ * comparison decided exactly as the sign of one fused multiply-add
+ * h * scale - t nb_half (h * scale = y nb_half), with neg_t = fp32(-t nb_half)
+ * (-inf for buckets without a threshold).  enc_shift keeps every threshold's
+ * u at least 1/64 of a bucket away from the bucket edges, so that the fp32
+ * rounding of u never puts a coordinate in a bucket on the far side of a
+ * threshold it lies close to. */
 struct tq_enc_entry {
-  float thr;
+  float neg_t;
   uint32_t base;
 };
 
@@ -39,6 +43,7 @@ struct tq_codebook_s {
   int d, bits;
   int nb_half;           /* buckets per unit of y */
   int enc_entries;       /* 2 * nb_half + 2 */
+  float enc_shift;       /* bucket grid offset in [0, 0.45) */
   float sigma;           /* decoder lookup-table scale (levels stored as fp16(c * sigma)) */
   double centroids64[16];
   double bounds64[15];
