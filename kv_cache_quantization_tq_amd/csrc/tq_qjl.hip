@@ -178,7 +178,6 @@ __device__ inline void enc_keys(const EncSlot<D, B>& r, const QjlEncArgs& a, con
                                 const float2* plev, const uint32_t (&fm)[D / 32][4], int64_t v0,
                                 int lane, int n, int kq) {
   constexpr int KS = D / 32;
-  using SL = SLds<D>;
   const int64_t v = v0 + n;
   const bool live = v < a.n;
   /* x slice with the sign flips D (an xor of the fp16 sign bits), squares
