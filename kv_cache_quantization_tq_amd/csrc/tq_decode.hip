@@ -449,10 +449,6 @@ __device__ inline float fma_h(float x, uint32_t h, float c) {
   return __builtin_fmaf(x, (float)__builtin_bit_cast(_Float16, (uint16_t)h), c);
 }
 
-/* fp32 x times an fp16 value given by its bits (one mixed-precision FMA). */
-__device__ inline float mul_h(float x, uint32_t h) {
-  return __builtin_fmaf(x, (float)__builtin_bit_cast(_Float16, (uint16_t)h), 0.0f);
-}
 
 /* Score one tile and update the online softmax: p[v] receives the weights
  * (relative to the updated running max) of the lane's 8 / CF (token, head)
