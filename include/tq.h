@@ -205,6 +205,21 @@ tq_status tq_decode_attn(const tq_kv_cache* c, tq_codebook cbk, tq_codebook cbv,
                          const int32_t* seq_lens, int max_len, int n_layers, float* out,
                          void* ws, size_t ws_bytes, void* stream);
 
+/* tq_decode_attn for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same computation and kernels, with the split workspace held by the
+ * library, one array of 16 MiB per GPU that stays until the process ends (its
+ * address is looked up, and the array cleared, on the first call on a
+ * device).  Allocates nothing.  Calls whose workspace
+ * (tq_decode_workspace_bytes) exceeds 16 MiB return TQ_ERR_WORKSPACE before
+ * anything is launched.  Every call on a GPU shares that GPU's array; calls
+ * that overlap on one GPU (other streams, other threads) race and must not
+ * be issued.  Arguments as tq_decode_attn, without ws and ws_bytes. */
+tq_status tq_decode_attn_noalloc(const tq_kv_cache* c, tq_codebook cbk, tq_codebook cbv,
+                                 const uint8_t* sign_bits, const uint16_t* q, int q_heads,
+                                 const int32_t* seq_lens, int max_len, int n_layers, float* out,
+                                 void* stream);
+
 /* Prefill (extend) attention over the compressed cache: t_new query tokens
  * per sequence, already written to the cache (e.g. by tq_append), each
  * attending causally to its sequence's cached tokens ("We Built ...", "Test

@@ -19,7 +19,8 @@ EXPORTS = (
     "tq_status_str", "tq_codebook_compute", "tq_codebook_init", "tq_codebook_read",
     "tq_codebook_head_dim", "tq_codebook_bits", "tq_codebook_free", "tq_encode",
     "tq_cache_layer_bytes", "tq_append", "tq_decode_workspace_bytes", "tq_decode_attn",
-    "tq_decode_attn_sparse", "tq_prefill_attn", "tq_qjl_encode", "tq_qjl_scores",
+    "tq_decode_attn_sparse", "tq_decode_attn_noalloc", "tq_prefill_attn", "tq_qjl_encode",
+    "tq_qjl_scores",
 )
 
 
@@ -74,12 +75,14 @@ def lib():
                                      vp, sz, vp]
         L.tq_decode_attn_sparse.argtypes = [P(KVCacheStruct), vp, vp, vp, vp, i32, vp, i32, i32,
                                             ctypes.c_float, vp, vp, vp, vp, sz, vp]
+        L.tq_decode_attn_noalloc.argtypes = [P(KVCacheStruct), vp, vp, vp, vp, i32, vp, i32, i32,
+                                             vp, vp]
         L.tq_prefill_attn.argtypes = [P(KVCacheStruct), vp, vp, vp, vp, i32, i32, vp, i32, vp, vp]
         L.tq_qjl_encode.argtypes = [vp, vp, i64, i64, vp, vp, vp, vp, vp, vp]
         L.tq_qjl_scores.argtypes = [vp, vp, i32, vp, vp, vp, vp, vp, vp, i64, vp, vp]
         for f in ("tq_codebook_compute", "tq_codebook_init", "tq_codebook_read", "tq_encode",
                   "tq_cache_layer_bytes", "tq_append", "tq_decode_attn", "tq_decode_attn_sparse",
-                  "tq_prefill_attn", "tq_qjl_encode", "tq_qjl_scores"):
+                  "tq_decode_attn_noalloc", "tq_prefill_attn", "tq_qjl_encode", "tq_qjl_scores"):
             getattr(L, f).restype = i32
         _lib = L
     return _lib
@@ -276,6 +279,18 @@ def decode(cache, cbk, cbv, sign_bits, q, seq_lens, max_len, out, ws=None, layer
     _check("tq_decode_attn", lib().tq_decode_attn(
         ctypes.byref(s), cbk.handle, cbv.handle, _ptr(sign_bits), _ptr(q), q_heads,
         _ptr(seq_lens), max_len, n_layers, _ptr(out), _ptr(ws), ws_bytes, _stream(stream)))
+
+
+def decode_noalloc(cache, cbk, cbv, sign_bits, q, seq_lens, max_len, out, layer0=0,
+                   n_layers=None, stream=None):
+    """tq_decode_attn_noalloc: decode() with the library's own workspace (no
+    allocation; calls on one GPU must not overlap)."""
+    n_layers = n_layers if n_layers is not None else q.shape[0]
+    q_heads = q.shape[2]
+    s = cache.struct(layer0)
+    _check("tq_decode_attn_noalloc", lib().tq_decode_attn_noalloc(
+        ctypes.byref(s), cbk.handle, cbv.handle, _ptr(sign_bits), _ptr(q), q_heads,
+        _ptr(seq_lens), max_len, n_layers, _ptr(out), _stream(stream)))
 
 
 def skip_words(max_len):

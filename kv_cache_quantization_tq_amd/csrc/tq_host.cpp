@@ -419,6 +419,29 @@ extern "C" tq_status tq_decode_attn(const tq_kv_cache* c, tq_codebook cbk, tq_co
                        ws_bytes, 0.0f, nullptr, nullptr, stream);
 }
 
+extern "C" tq_status tq_decode_attn_noalloc(const tq_kv_cache* c, tq_codebook cbk,
+                                            tq_codebook cbv, const uint8_t* sign_bits,
+                                            const uint16_t* q, int q_heads,
+                                            const int32_t* seq_lens, int max_len, int n_layers,
+                                            float* out, void* stream) {
+  tq_status st = check_decode(c, q_heads, max_len, n_layers);
+  if (st != TQ_OK) return st;
+  if (!codebook_matches(cbk, c->head_dim, c->bits_k) ||
+      !codebook_matches(cbv, c->head_dim, c->bits_v))
+    return TQ_ERR_ARG;
+  if (!sign_bits || !q || !seq_lens || !out) return TQ_ERR_ARG;
+  if (!aligned(q, 16) || !aligned(out, 16) || !aligned(seq_lens, 4)) return TQ_ERR_ARG;
+  const tq_decode_plan plan = tq_plan_decode(c, q_heads, max_len, n_layers);
+  if (plan.ws_bytes > TQ_NOALLOC_SCRATCH_BYTES) return TQ_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (plan.ws_bytes > 0) {
+    st = tq_noalloc_scratch(&ws, (hipStream_t)stream);
+    if (st != TQ_OK) return st;
+  }
+  return tq_launch_decode(c, cbk, cbv, sign_bits, q, q_heads, seq_lens, max_len, n_layers, out,
+                          ws, plan, 0.0f, nullptr, nullptr, (hipStream_t)stream);
+}
+
 extern "C" tq_status tq_prefill_attn(const tq_kv_cache* c, tq_codebook cbk, tq_codebook cbv,
                                      const uint8_t* sign_bits, const uint16_t* q, int q_heads,
                                      int t_new, const int32_t* pos, int n_layers, float* out,

@@ -100,6 +100,14 @@ tq_status tq_launch_decode(const tq_kv_cache* c, const tq_codebook_s* cbk,
                            const tq_decode_plan& plan, float sparse_eps, uint32_t* skip_counts,
                            uint32_t* skip_tiles, hipStream_t stream);
 
+/* Bytes of the library-held decode workspace of tq_decode_attn_noalloc (one
+ * array per GPU, held until the process ends). */
+#define TQ_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/* This device's library-held workspace (tq_noalloc.hip): its address, looked
+ * up (and the array cleared on `stream`) on the first call on a device. */
+tq_status tq_noalloc_scratch(void** out, hipStream_t stream);
+
 /* Words per (layer, sequence, KV head) of a Sparse V skip bitmap: one bit per
  * 32-token tile of a context of up to max_len tokens. */
 inline int tq_skip_words(int max_len) { return (max_len + 1023) / 1024; }

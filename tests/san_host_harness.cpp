@@ -64,6 +64,13 @@ tq_status tq_launch_decode(const tq_kv_cache*, const tq_codebook_s*, const tq_co
   return TQ_OK;
 }
 
+static int scratch_lookups = 0;
+tq_status tq_noalloc_scratch(void** out, hipStream_t) {
+  ++scratch_lookups;
+  *out = (void*)(uintptr_t)0x200000;
+  return TQ_OK;
+}
+
 #define CHECK(c)                                                     \
   do {                                                               \
     if (!(c)) {                                                      \
@@ -193,9 +200,15 @@ int main() {
                               fake(256), ws2, nullptr) == TQ_ERR_ARG);
   CHECK(tq_decode_attn_sparse(&c, &ck, &cv, sb, q, 16, lens, 8192, 2, 1e-4f, nullptr,
                               (uint32_t*)fake(2), out, fake(256), ws2, nullptr) == TQ_ERR_ARG);
+  CHECK(tq_decode_attn_noalloc(&c, &ck, &cv, sb, q, 16, lens, 8192, 2, out, nullptr) == TQ_OK);
+  CHECK(scratch_lookups == 1);
+  CHECK(tq_decode_attn_noalloc(&c, &ck, &cv, sb, q, 10, lens, 8192, 2, out, nullptr) == TQ_ERR_ARG);
+  CHECK(tq_decode_attn_noalloc(&c, &ck, &cv, sb, q, 16, lens, 8192, 4096, out, nullptr) ==
+        TQ_ERR_WORKSPACE); /* records of 4096 layers exceed the library's array */
+  CHECK(scratch_lookups == 1);
   CHECK(tq_prefill_attn(&c, &ck, &cv, sb, q, 16, 7, pos, 2, out, nullptr) == TQ_OK);
   CHECK(tq_prefill_attn(&c, &ck, &cv, sb, q, 16, -1, pos, 2, out, nullptr) == TQ_ERR_ARG);
-  CHECK(launches == before + 4);
+  CHECK(launches == before + 5);
 
   /* paged caches */
   tq_kv_cache p = cache(128, 4, 2, 1024);
