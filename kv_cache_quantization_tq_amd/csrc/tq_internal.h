@@ -22,7 +22,7 @@
  * u at least 1/64 of a bucket away from the bucket edges, so that the fp32
  * rounding of u never puts a coordinate in a bucket on the far side of a
  * threshold it lies close to. */
-struct tq_enc_entry {
+struct alignas(8) tq_enc_entry {
   float neg_t;
   uint32_t base;
 };
