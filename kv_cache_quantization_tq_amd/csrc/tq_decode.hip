@@ -296,6 +296,8 @@ struct DecArgs {
   int64_t ls_kc, ls_vc, ls_kn, ls_vn;
   int batch, kv_heads, capacity, q_heads, group, n_layers;
   int max_len, splits, tiles_per_split;
+  int upb;         /* units per block (> 1 only with one split and no Sparse V) */
+  int64_t units;   /* (layer, sequence, KV head) units of the call */
   const int32_t* block_table; /* paged storage: [batch][max_pages] */
   int lg_tpp, max_pages, num_pages; /* log2(tiles per page), table row, pool pages */
   float sparse_eps;      /* Sparse V threshold (sparse kernels only) */
@@ -317,13 +319,17 @@ struct DecArgs {
   int64_t ctr_bytes;
 };
 
+/* Rows of rotated queries (and merged sums) a block keeps: the heads of all
+ * its units (units per block x group size <= 16). */
+constexpr int kQRows = 16;
+
 /* LDS of one decode block. */
 template <int D, int BK, int BV>
 constexpr size_t decode_lds_bytes() {
   return (size_t)((KTab<BK>::BYTES + VTab<BV>::BYTES) > waves_for(D, BK, BV) * (8 * (D + 4) + 16) * 4
                       ? (KTab<BK>::BYTES + VTab<BV>::BYTES)
                       : waves_for(D, BK, BV) * (8 * (D + 4) + 16) * 4) +
-         8 * D * 4;
+         kQRows * D * 4;
 }
 
 /* Walsh-Hadamard transform of one row of D floats by one wave: lane l holds
@@ -828,7 +834,7 @@ __device__ inline void sparse_tiles(const DecArgs& a, const TileAddr& ad, TileRe
     atomicAdd(a.skip_counts + ((int64_t)layer * a.batch + b) * a.kv_heads + kv, nskip);
 }
 
-template <int D, int BK, int BV, int CF, bool PAGED, bool SPARSE>
+template <int D, int BK, int BV, int CF, bool PAGED, bool SPARSE, bool MULTI>
 __global__ void __launch_bounds__(64 * waves_for(D, BK, BV))
 decode_kernel(DecArgs a) {
   using DG = DecGeo<D, BK, BV>;
@@ -844,21 +850,29 @@ decode_kernel(DecArgs a) {
    * lane-offset operand of the address permute (no extra add per lookup). */
   constexpr uint32_t KPAGE = VTab<BV>::BYTES & ~0xFFFFu;
   const uint32_t* lut_k_rd = (const uint32_t*)(smem + (VTab<BV>::BYTES - KPAGE));
-  float* qbuf = (float*)(smem + decode_lds_bytes<D, BK, BV>() - 8 * D * 4);
+  float* qbuf = (float*)(smem + decode_lds_bytes<D, BK, BV>() - kQRows * D * 4);
   float* mbuf = (float*)smem; /* aliases the tables after the token loop */
   const int G = a.group;
-  const int split = blockIdx.x % a.splits;
-  int64_t unit = blockIdx.x / a.splits;
-  const int kv = (int)(unit % a.kv_heads);
-  unit /= a.kv_heads;
-  const int b = (int)(unit % a.batch);
-  const int layer = (int)(unit / a.batch);
   /* the wave index is uniform within a wave: say so, so that tile indices
    * and load bases live in scalar registers */
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64), lane = threadIdx.x % 64;
   const int q4 = lane / 16, n = lane % 16;
+  /* A block takes one split of one (layer, sequence, KV head) unit, or (with
+   * one split) upb whole units, each streamed by kWaves / upb of its waves,
+   * all sharing the block's lookup tables.  ug: this wave's unit in the
+   * block, wu: its index among that unit's waves. */
+  const int upb = MULTI ? a.upb : 1, wpu = MULTI ? kWaves / upb : kWaves;
+  const int ug = wave / wpu, wu = wave - ug * wpu;
+  const int split = upb == 1 ? (int)(blockIdx.x % a.splits) : 0;
+  const int64_t unit_id = upb == 1 ? (int64_t)(blockIdx.x / a.splits) : (int64_t)blockIdx.x * upb + ug;
+  const bool unit_ok = unit_id < a.units; /* the last block's spare waves stream nothing */
+  int64_t unit = unit_ok ? unit_id : a.units - 1;
+  const int kv = (int)(unit % a.kv_heads);
+  unit /= a.kv_heads;
+  const int b = (int)(unit % a.batch);
+  const int layer = (int)(unit / a.batch);
 
-  int len = a.seq_lens[b];
+  int len = unit_ok ? a.seq_lens[b] : 0;
   len = len < 0 ? 0 : (len > a.max_len ? a.max_len : len);
   const int ntiles = (len + 31) / 32;
   const int t_begin = split * a.tiles_per_split;
@@ -890,8 +904,8 @@ decode_kernel(DecArgs a) {
    * latency overlaps the prologue (issued on every path, clamped to a tile
    * that exists, so that the loop's waits stay exact) */
   const int full_end = (len / 32) < t_end ? (len / 32) : t_end;
-  int tile = t_begin + wave;
-  constexpr int W = kWaves;  /* tile stride between a wave's tiles */
+  int tile = t_begin + wu;
+  const int W = MULTI ? wpu : kWaves;  /* tile stride between a wave's tiles */
   const int last = full_end > 0 ? full_end - 1 : 0;
   /* tile t's offsets: tile t of the stream, or tile t % tpp of the pool page
    * the block table gives for page t / tpp (clamped into the pool) */
@@ -924,13 +938,28 @@ decode_kernel(DecArgs a) {
     fill_pairs<VTab<BV>::ENTRIES, kWaves>(lut_v, a.lut_v_quad, a.lut_v_quad + 1, 2);
   else
     fill_words<VTab<BV>::ENTRIES, kWaves>(lut_v, a.lut_v);
-  /* rotated queries: qbuf[g][i] = (D q_g)_i, then FWHT, then scale */
+  /* rotated queries: qbuf[u G + g][i] = (D q_g)_i of the block's unit u,
+   * then FWHT, then scale */
   const uint8_t* sb = a.sign_bits + (int64_t)layer * (D / 8);
-  const uint16_t* qg = a.q + (((int64_t)layer * a.batch + b) * a.q_heads + (int64_t)kv * G) * D;
-  for (int t = threadIdx.x; t < G * D; t += blockDim.x) {
-    const int i = t % D;
-    const float v = h2f(qg[t]);
-    qbuf[t] = ((sb[i >> 3] >> (i & 7)) & 1) ? -v : v;
+  auto unit_of = [&](int u, int& ul, int& ub, int& ukv) -> bool {
+    int64_t id = upb == 1 ? (int64_t)(blockIdx.x / a.splits) : (int64_t)blockIdx.x * upb + u;
+    const bool ok = id < a.units;
+    if (!ok) id = a.units - 1;
+    ukv = (int)(id % a.kv_heads);
+    id /= a.kv_heads;
+    ub = (int)(id % a.batch);
+    ul = (int)(id / a.batch);
+    return ok;
+  };
+  for (int t = threadIdx.x; t < upb * G * D; t += blockDim.x) {
+    const int r = t / D, i = t % D, u = r / G, g = r % G;
+    int ul, ub, ukv;
+    float v = 0.0f;
+    if (unit_of(u, ul, ub, ukv)) {
+      v = h2f(a.q[((((int64_t)ul * a.batch + ub) * a.q_heads + (int64_t)ukv * G + g) * D) + i]);
+      if ((a.sign_bits[(int64_t)ul * (D / 8) + (i >> 3)] >> (i & 7)) & 1) v = -v;
+    }
+    qbuf[t] = v;
   }
   /* Sparse V: a running max per head shared by the block's waves, so that
    * each gates against the largest one seen */
@@ -939,10 +968,10 @@ decode_kernel(DecArgs a) {
     if (threadIdx.x < 8) mref[threadIdx.x] = -INFINITY;
   __syncthreads();
   /* one wave per head transforms its row in registers */
-  if (wave < G) {
-    const RowRegs<D> t = wave_fwht<D>(qbuf + wave * D, lane);
+  for (int r = wave; r < upb * G; r += kWaves) {
+    const RowRegs<D> t = wave_fwht<D>(qbuf + r * D, lane);
 #pragma unroll
-    for (int j = 0; j < (D >= 64 ? D / 64 : 1); ++j) qbuf[wave * D + lane + 64 * j] = t.v[j];
+    for (int j = 0; j < (D >= 64 ? D / 64 : 1); ++j) qbuf[r * D + lane + 64 * j] = t.v[j];
   }
   __syncthreads();
 
@@ -955,7 +984,7 @@ decode_kernel(DecArgs a) {
   half8 bq[NB];
   {
     const int g = n & 7;
-    const float* qg = qbuf + g * D + q4 * DG::KQ;
+    const float* qg = qbuf + (ug * G + g) * D + q4 * DG::KQ;
 #pragma unroll
     for (int t = 0; t < NB; ++t) {
 #pragma unroll
@@ -1060,46 +1089,51 @@ decode_kernel(DecArgs a) {
       for (int i = 0; i < 4; ++i) mw[16 + n * MR + (4 * q4 + i) * DG::VM + m] = acc[m][i];
   }
   __syncthreads();
-  /* merged record per head in qbuf (reused): qbuf[g][i]; wsc[w][g] = the
-   * weight of wave w's sums, exp2(m_w - M) */
+  /* merged record per head of each unit in qbuf (reused): qbuf[u G + g][i];
+   * wsc[w][g] = the weight of wave w's sums, exp2(m_w - M) (a wave belongs
+   * to one unit, waves u wpu .. u wpu + wpu - 1) */
   float* res = qbuf;
-  __shared__ float mg[8], lg[8], wsc[kWaves][8];
-  if (threadIdx.x < G) {
-    const int g = threadIdx.x;
+  __shared__ float mg[kQRows], lg[kQRows], wsc[kWaves][8];
+  if (threadIdx.x < upb * G) {
+    const int u = threadIdx.x / G, g = threadIdx.x % G;
     float M = -1e30f;
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, mbuf[w * MW + g]);
+    for (int w = u * wpu; w < (u + 1) * wpu; ++w) M = fmaxf(M, mbuf[w * MW + g]);
     float L = 0.0f;
-    for (int w = 0; w < kWaves; ++w) {
+    for (int w = u * wpu; w < (u + 1) * wpu; ++w) {
       const float* r = mbuf + w * MW;
       const float e = __builtin_amdgcn_exp2f(r[g] - M);
       wsc[w][g] = e;
       L += e * r[8 + g];
     }
-    mg[g] = M;
-    lg[g] = L;
+    mg[threadIdx.x] = M;
+    lg[threadIdx.x] = L;
   }
   __syncthreads();
-  for (int t = threadIdx.x; t < G * D; t += blockDim.x) {
-    const int g = t / D, i = t % D;
+  for (int t = threadIdx.x; t < upb * G * D; t += blockDim.x) {
+    const int r = t / D, i = t % D, u = r / G, g = r % G;
     float s = 0.0f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) s += wsc[w][g] * mbuf[w * MW + 16 + g * MR + i];
+    for (int w = u * wpu; w < (u + 1) * wpu; ++w) s += wsc[w][g] * mbuf[w * MW + 16 + g * MR + i];
     res[t] = s;
   }
   __syncthreads();
   const int64_t head0 = ((int64_t)layer * a.batch + b) * a.q_heads + (int64_t)kv * G;
   if (a.splits == 1) {
-    if (wave < G) {
-      /* head `wave`: inverse rotation, 1/l and the scales, straight out */
-      const RowRegs<D> t = wave_fwht<D>(res + wave * D, lane);
-      const float L = lg[wave];
+    /* one wave per head of each unit: inverse rotation, 1/l and the scales,
+     * straight out */
+    for (int r = wave; r < upb * G; r += kWaves) {
+      int ul, ub, ukv;
+      if (!unit_of(r / G, ul, ub, ukv)) continue;
+      const int64_t h0 = ((int64_t)ul * a.batch + ub) * a.q_heads + (int64_t)ukv * G + r % G;
+      const uint8_t* usb = a.sign_bits + (int64_t)ul * (D / 8);
+      const RowRegs<D> t = wave_fwht<D>(res + r * D, lane);
+      const float L = lg[r];
       const float f = L > 0.0f ? a.oscale / L : 0.0f;
 #pragma unroll
       for (int j = 0; j < (D >= 64 ? D / 64 : 1); ++j) {
         const int i = lane + 64 * j;
         if (i < D) {
           const float v = t.v[j] * f;
-          a.out[(head0 + wave) * D + i] = ((sb[i >> 3] >> (i & 7)) & 1) ? -v : v;
+          a.out[h0 * D + i] = ((usb[i >> 3] >> (i & 7)) & 1) ? -v : v;
         }
       }
     }
@@ -1172,24 +1206,30 @@ decode_kernel(DecArgs a) {
   }
 }
 
-/* Groups of up to 4 query heads compact their softmax 4 ways, up to 8 2 ways. */
+/* Groups of up to 4 query heads compact their softmax 4 ways, up to 8 2 ways;
+ * several units per block only in the dense, contiguous form. */
 template <int D, int BK, int BV>
 tq_status launch_decode_t(const DecArgs& a, hipStream_t s) {
-  const int64_t blocks = (int64_t)a.n_layers * a.batch * a.kv_heads * a.splits;
+  const int64_t blocks = a.upb > 1 ? (a.units + a.upb - 1) / a.upb : a.units * a.splits;
   const dim3 grid((unsigned)blocks), block(64 * waves_for(D, BK, BV));
-#define TQ_LAUNCH(CF, PG, SP) hipLaunchKernelGGL((decode_kernel<D, BK, BV, CF, PG, SP>), grid, block, 0, s, a)
-  const bool sp = a.sparse_eps > 0.0f;
+#define TQ_LAUNCH(CF, PG, SP, MU) \
+  hipLaunchKernelGGL((decode_kernel<D, BK, BV, CF, PG, SP, MU>), grid, block, 0, s, a)
+  const bool sp = a.sparse_eps > 0.0f, mu = a.upb > 1;
   if (a.block_table) {
     if (a.group <= 4) {
-      if (sp) TQ_LAUNCH(4, true, true); else TQ_LAUNCH(4, true, false);
+      if (sp) TQ_LAUNCH(4, true, true, false); else TQ_LAUNCH(4, true, false, false);
     } else {
-      if (sp) TQ_LAUNCH(2, true, true); else TQ_LAUNCH(2, true, false);
+      if (sp) TQ_LAUNCH(2, true, true, false); else TQ_LAUNCH(2, true, false, false);
     }
   } else {
     if (a.group <= 4) {
-      if (sp) TQ_LAUNCH(4, false, true); else TQ_LAUNCH(4, false, false);
+      if (sp) TQ_LAUNCH(4, false, true, false);
+      else if (mu) TQ_LAUNCH(4, false, false, true);
+      else TQ_LAUNCH(4, false, false, false);
     } else {
-      if (sp) TQ_LAUNCH(2, false, true); else TQ_LAUNCH(2, false, false);
+      if (sp) TQ_LAUNCH(2, false, true, false);
+      else if (mu) TQ_LAUNCH(2, false, false, true);
+      else TQ_LAUNCH(2, false, false, false);
     }
   }
 #undef TQ_LAUNCH
@@ -1207,7 +1247,7 @@ int concurrent_blocks_t() {
     int dev = 0, cus = 0, per = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, decode_kernel<D, BK, BV, 2, false, false>, 64 * waves_for(D, BK, BV),
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, decode_kernel<D, BK, BV, 2, false, false, false>, 64 * waves_for(D, BK, BV),
                                                      0) != hipSuccess ||
         cus <= 0 || per <= 0) {
       (void)hipGetLastError();
@@ -1253,6 +1293,23 @@ tq_decode_plan tq_plan_decode(const tq_kv_cache* c, int q_heads, int max_len, in
   }
   p.splits = splits;
   p.tiles_per_split = tiles > 0 ? (tiles + splits - 1) / splits : 0;
+  /* With one split, up to 4 units share a block (its waves split between
+   * them, one table fill for all) when the rounds of blocks stay >= 90%
+   * full: many-round workloads pay the block's fixed cost (launch, first
+   * loads, table fill, merge) once per upb units. */
+  p.upb = 1;
+  if (splits == 1) {
+    const int G = q_heads / c->kv_heads;
+    for (int u = 4; u >= 2; --u) {
+      if (waves % u != 0 || u * G > kQRows) continue;
+      const int64_t blocks = (units + u - 1) / u;
+      const int64_t rounds = (blocks + conc - 1) / conc;
+      if ((double)blocks / (double)(rounds * conc) >= 0.9) {
+        p.upb = u;
+        break;
+      }
+    }
+  }
   p.ctr_bytes = ((size_t)units * sizeof(int) + 255) & ~(size_t)255;
   p.ws_bytes = splits > 1 ? p.ctr_bytes + (size_t)n_layers * c->batch * q_heads * splits *
                                               (c->head_dim + 2) * sizeof(float)
@@ -1289,6 +1346,9 @@ tq_status tq_launch_decode(const tq_kv_cache* c, const tq_codebook_s* cbk,
   a.max_len = max_len;
   a.splits = plan.splits;
   a.tiles_per_split = plan.tiles_per_split;
+  /* Sparse V and paged storage keep one unit per block */
+  a.upb = (sparse_eps > 0.0f || c->block_table) ? 1 : plan.upb;
+  a.units = (int64_t)n_layers * c->batch * c->kv_heads;
   a.sign_bits = sign_bits;
   a.q = q;
   a.seq_lens = seq_lens;

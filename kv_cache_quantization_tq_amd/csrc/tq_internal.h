@@ -88,6 +88,7 @@ tq_status tq_launch_qjl_scores(const tq_codebook_s* cb, const uint16_t* q, int G
 struct tq_decode_plan {
   int splits;          /* token splits per (layer, seq, kv head) */
   int tiles_per_split; /* 32-token tiles per split */
+  int upb;             /* (layer, seq, kv head) units per block; > 1 only with one split */
   size_t ctr_bytes;    /* per-unit arrival counters, 256-byte padded */
   size_t ws_bytes;     /* counters + (m, l, acc[d]) records; 0 when splits == 1 */
 };

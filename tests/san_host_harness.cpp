@@ -49,6 +49,7 @@ tq_status tq_launch_qjl_scores(const tq_codebook_s*, const uint16_t*, int, const
 tq_decode_plan tq_plan_decode(const tq_kv_cache* c, int q_heads, int max_len, int n_layers) {
   tq_decode_plan p;
   p.splits = max_len > 4096 ? 4 : 1;
+  p.upb = 1;
   p.tiles_per_split = (max_len + 31) / 32;
   p.ctr_bytes = 256;
   p.ws_bytes = p.splits > 1 ? 256 + (size_t)n_layers * c->batch * q_heads * p.splits *

@@ -317,3 +317,58 @@ def test_append_capacity_skip_guard_bytes():
                         old = oracle.unpack_vtiles(old, d, bits)
                         assert np.array_equal(got[w0:w1], oracle.unpack_rows(ref_c, d, bits))
                         assert np.array_equal(got[keep], old[keep])
+
+
+@pytest.mark.parametrize("L,B,H,G,d,bk,bv,maxlen", [
+    (4, 16, 8, 4, 128, 3, 2, 700),    # 512 units
+    (2, 509, 1, 4, 64, 4, 2, 300),    # 1018 units: the last block is not full
+    (2, 64, 4, 8, 256, 2, 4, 200),    # 512 units, groups of 8
+])
+def test_decode_many_units(L, B, H, G, d, bk, bv, maxlen):
+    """Calls with many (layer, sequence, KV head) units, where several units
+    share a block: ragged lengths (some zero), units sampled at every
+    position inside a block and at the end of the grid, against the oracle."""
+    torch = require_gpu()
+    rng = np.random.default_rng(L * B + d)
+    lens = rng.integers(0, maxlen + 1, B).tolist()
+    lens[0], lens[-1] = maxlen, 0
+    T = max(lens)
+    cap = ((T + 31) // 32) * 32 + 32
+    cache = tq.KVCache(L, B, H, d, bk, bv, cap)
+    sbs = np.stack([synth.sign_bits(SEED, l, d) for l in range(L)])
+    sbd = torch.from_numpy(sbs).cuda()
+    cbk, cbv = tq.Codebook(d, bk), tq.Codebook(d, bv)
+    kall = torch.stack([_dev_kv(torch, SEED, 0, l, B, H, T, d) for l in range(L)])
+    vall = torch.stack([_dev_kv(torch, SEED, 1, l, B, H, T, d) for l in range(L)])
+    tq.append(cache, cbk, cbv, sbd, kall, vall, torch.zeros(B, dtype=torch.int32, device="cuda"),
+              host_max_pos=0)
+    del kall, vall
+    q = torch.empty((L, B, G * H, d), dtype=torch.int16, device="cuda")
+    for l in range(L):
+        synth.q_dev(SEED, 0, l, q[l])
+    lens_d = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    out = torch.full((L, B, G * H, d), float("nan"), dtype=torch.float32, device="cuda")
+    tq.decode(cache, cbk, cbv, sbd, q, lens_d, T, out, tq.workspace(cache, G * H, T))
+    torch.cuda.synchronize()
+    outh = out.cpu().numpy()
+    q16 = q.cpu().numpy().view(np.uint16)
+    assert np.isfinite(outh).all()
+    units = L * B * H
+    picks = sorted(set(list(range(5)) + list(range(units // 2 - 2, units // 2 + 3)) +
+                   list(range(units - 6, units))))
+    got, ref, n_alt, n_coords = [], [], 0, 0
+    what = f"many units L={L} B={B} H={H} G={G} d={d}"
+    for u in picks:
+        h, b, l = u % H, (u // H) % B, u // (H * B)
+        sl = slice(h * G, (h + 1) * G)
+        if lens[b] == 0:
+            assert not outh[l, b, sl].any()
+            continue
+        o, na, nc = oracle_attention_stream(SEED, l, b, h, lens[b], bk, bv, sbs[l], q16[l, b, sl],
+                                            gpu_stream(cache, l, b, h, lens[b]), what)
+        got.append(outh[l, b, sl])
+        ref.append(o)
+        n_alt += na
+        n_coords += nc
+    check_mismatch_fraction(n_alt, n_coords, what)
+    check_attention(np.stack(got), np.stack(ref), what, n_alt)
