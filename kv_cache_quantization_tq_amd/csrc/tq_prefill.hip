@@ -421,10 +421,11 @@ __global__ void __launch_bounds__(64 * waves_for(D)) prefill_kernel(PreArgs a) {
       for (int j = 0; j < 8; ++j) {
         const float p = __builtin_amdgcn_exp2f(sc[j] - m_run[e]);
         l_run[e] += p;
-        const float pm = p * nvv[j];
-        const _Float16 hh = (_Float16)pm;
+        /* fp16(p m) and the fp16 of the exact remainder p m - fp16(p m), one
+         * mixed-precision FMA each */
+        const _Float16 hh = (_Float16)__builtin_fmaf(p, nvv[j], 0.0f);
         ph[e][j] = hh;
-        pl[e][j] = (_Float16)(pm - (float)hh);
+        pl[e][j] = (_Float16)__builtin_fmaf(p, nvv[j], -(float)hh);
       }
     }
 #pragma unroll
