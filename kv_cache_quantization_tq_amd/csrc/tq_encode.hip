@@ -910,6 +910,174 @@ append_kernel(AppendArgs a) {
   }
 }
 
+/* ------------------------------------------------- one-token append -- */
+
+/* Sign-flip masks as sign_masks, for a layer that may differ between the
+ * lanes of a wave (vector loads). */
+template <int D>
+__device__ inline void sign_masks_lane(const uint8_t* sb, int q4, uint32_t (&m)[EGeo<D>::J][4]) {
+#pragma unroll
+  for (int j = 0; j < EGeo<D>::J; ++j) {
+    const uint32_t b = (((const uint32_t*)sb)[j] >> (8 * q4)) & 0xFFu;
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+      m[j][w] = (((b >> (2 * w)) & 1u) << 15) | (((b >> (2 * w + 1)) & 1u) << 31);
+  }
+}
+
+/* An append of one token per stream (a decode step).  The n_layers batch
+ * heads new vectors of a kind are then one row-major matrix, encoded 16 per
+ * wave pass as in tq_encode (lanes of one pass may belong to different
+ * layers and sequences).  Key codes and norms go straight to the stream's
+ * row.  A value token owns BV bits of every field of 16 segments of its tile
+ * (tile row 8 q + u: segments 16 q + r, field m at bit (8 m + u) BV); lane
+ * (token, segment) pairs merge those bits into the words already in memory.
+ * One token per stream means no two vectors of a launch share a tile, so no
+ * two merges touch one word.  blockIdx.y = 1 marks the value blocks. */
+template <int D, int BK, int BV>
+__global__ void __launch_bounds__(64 * kRowsWaves) __attribute__((amdgpu_waves_per_eu(D == 256 ? 2 : TQ_ENC_WPE)))
+append_token_kernel(AppendArgs a) {
+  using G = EGeo<D>;
+  constexpr int kRows = tq_enc_rows_max(D, BK) > tq_enc_rows_max(D, BV) ? tq_enc_rows_max(D, BK)
+                                                                       : tq_enc_rows_max(D, BV);
+  constexpr int MS = D / 16;      /* fields per value segment */
+  constexpr int SB = D * BV / 16; /* bytes per value segment (a multiple of 4) */
+  constexpr int SW = SB / 4;
+  __shared__ __align__(16) tq_enc_entry tab[kRows * kEncRep];
+  __shared__ __align__(16) uint8_t vbuf_all[kRowsWaves * kVec * kVPitch<D>];
+  /* per wave and token: byte offset of the value tile (-1: nothing to
+   * write) and the token's tile row */
+  __shared__ int64_t tbase_all[kRowsWaves * kVec];
+  __shared__ int trow_all[kRowsWaves * kVec];
+  const bool is_v = blockIdx.y == 1;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / 64), lane = threadIdx.x % 64;
+  const int q4 = lane / 16, nl = lane % 16;
+  uint8_t* vbuf = vbuf_all + wave * kVec * kVPitch<D>;
+  int64_t* tbase = tbase_all + wave * kVec;
+  int* trow = trow_all + wave * kVec;
+  const uint32_t tab_off = (uint32_t)(lane & (kEncRep - 1)) * sizeof(tq_enc_entry);
+  const float nbh = is_v ? a.nbh_v : a.nbh_k;
+  const float off = is_v ? a.off_v : a.off_k;
+  const uint16_t* src_all = is_v ? a.v_new : a.k_new;
+  const int64_t per_layer = (int64_t)a.batch * a.heads;
+  const int64_t n = (int64_t)a.n_layers * per_layer;
+  const int64_t passes = (n + kVec - 1) / kVec;
+  const int64_t wstride = (int64_t)gridDim.x * kRowsWaves;
+  int64_t ps = (int64_t)blockIdx.x * kRowsWaves + wave;
+  load_table(tab, is_v ? a.tab_v : a.tab_k, is_v ? a.ent_v : a.ent_k);
+  __syncthreads();
+  const HTiles ht = h_tiles(nl, q4);
+  for (; ps < passes; ps += wstride) {
+    /* the lane's vector, clamped to a real one */
+    const int64_t v = ps * kVec + nl;
+    const int64_t vc = v < n ? v : n - 1;
+    const int layer = (int)(vc / per_layer);
+    const int64_t sh = vc - (int64_t)layer * per_layer; /* b heads + h */
+    const int b = (int)(sh / a.heads), h = (int)(sh - (int64_t)b * a.heads);
+    const uint16_t* vec = src_all + vc * D;
+    XRegs<D> xr;
+    load_x<D>(xr, vec, q4);
+    uint32_t sm[G::J][4];
+    sign_masks_lane<D>(a.sign_bits + (int64_t)layer * (D / 8), q4, sm);
+    /* the token's row: tile p0 / 32, tile row p0 % 32 (nothing when p0 is
+     * outside [0, capacity) or, paged, its page is outside the pool) */
+    const int p0 = a.pos[b];
+    int tile = 0, jlo = 0, jhi = 0;
+    bool mine = v < n && tq_append_tile_rows(p0, 1, a.capacity, 0, &tile, &jlo, &jhi);
+    int64_t rbase = 0, vt = 0;
+    if (mine) {
+      if (a.block_table) {
+        const int tpp = 1 << a.lg_tpp;
+        const int phys = a.block_table[(int64_t)b * a.max_pages + (tile >> a.lg_tpp)];
+        mine = phys >= 0 && phys < a.num_pages;
+        const int64_t pb = (int64_t)phys * a.heads + h;
+        rbase = pb * (32 * tpp) + 32 * (tile & (tpp - 1));
+        vt = pb * tpp + (tile & (tpp - 1));
+      } else {
+        rbase = sh * a.capacity + 32 * (int64_t)tile;
+        vt = sh * (a.capacity / 32) + tile;
+      }
+    }
+    const int64_t row = rbase + jlo;
+    uint32_t piece[G::OB];
+    if (!is_v) {
+      const uint32_t n16 = encode_pass<D, BK, false>(xr, sm, ht, (const char*)tab, tab_off, nbh,
+                                                     off, vec, piece);
+      uint32_t out[Chunk<D, BK>::NW];
+      gather_row_chunk<D, BK>(piece, out);
+      if (mine) {
+        store_chunk<D, BK, true>(a.k_codes + layer * a.ls_kc + row * (D * BK / 8) +
+                                     q4 * Chunk<D, BK>::BYTES, out);
+        if (q4 == 0) *(uint16_t*)((uint8_t*)a.k_norms + layer * a.ls_kn + row * 2) = (uint16_t)n16;
+      }
+      continue;
+    }
+    const uint32_t n16 = encode_pass<D, BV, true>(xr, sm, ht, (const char*)tab, tab_off, nbh,
+                                                  off, vec, piece);
+#pragma unroll
+    for (int ob = 0; ob < G::OB; ++ob)
+      *(uint32_t*)(vbuf + nl * kVPitch<D> + 16 * ob + 4 * q4) = piece[ob];
+    if (q4 == 0) {
+      tbase[nl] = mine ? layer * a.ls_vc + vt * (32 * D * BV / 8) : (int64_t)-1;
+      trow[nl] = jlo;
+      if (mine) *(uint16_t*)((uint8_t*)a.v_norms + layer * a.ls_vn + row * 2) = (uint16_t)n16;
+    }
+    /* the wave's own LDS rows: a wave-level fence orders the writes and the
+     * other lanes' reads (LDS operations of a wave run in order) */
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int r = lane % 16;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = lane / 16 + 4 * i; /* the pass's token */
+      const int64_t base = tbase[t];
+      if (base < 0) continue;
+      const int j = trow[t], u = j % 8;
+      /* the token's codes of segment r (coordinates r MS .. r MS + MS - 1)
+       * at field bits 8 m BV, then moved up to token u's place: u BV < 32,
+       * and each code stays inside its own field */
+      uint32_t cw[MS / 4];
+#pragma unroll
+      for (int k = 0; k < MS / 4; ++k)
+        cw[k] = *(const uint32_t*)(vbuf + t * kVPitch<D> + r * MS + 4 * k);
+      uint32_t bits0[SW], mask0[SW];
+#pragma unroll
+      for (int w = 0; w < SW; ++w) bits0[w] = mask0[w] = 0u;
+#pragma unroll
+      for (int m = 0; m < MS; ++m) {
+        const uint32_t code = (cw[m / 4] >> (8 * (m % 4))) & ((1u << BV) - 1u);
+        put_bits(bits0, 8 * m * BV, code, BV);
+        put_bits(mask0, 8 * m * BV, (1u << BV) - 1u, BV);
+      }
+      const uint32_t s = (uint32_t)(u * BV);
+      uint32_t* seg = (uint32_t*)(a.v_codes + base + (int64_t)(16 * (j / 8) + r) * SB);
+#pragma unroll
+      for (int w = 0; w < SW; ++w) {
+        const uint32_t lo_b = w > 0 ? bits0[w - 1] : 0u, lo_m = w > 0 ? mask0[w - 1] : 0u;
+        const uint32_t bw = (uint32_t)((((uint64_t)bits0[w] << 32) | lo_b) >> (32 - s));
+        const uint32_t mw = (uint32_t)((((uint64_t)mask0[w] << 32) | lo_m) >> (32 - s));
+        seg[w] = (seg[w] & ~mw) | bw;
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+}
+
+template <int D, int BK, int BV>
+tq_status launch_append_token_t(const AppendArgs& a, hipStream_t s) {
+  const int64_t n = (int64_t)a.n_layers * a.batch * a.heads;
+  const int64_t passes = (n + kVec - 1) / kVec;
+  int64_t blocks = (passes + kRowsWaves - 1) / kRowsWaves;
+  if (blocks < 1) return TQ_OK;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL((append_token_kernel<D, BK, BV>), dim3((unsigned)blocks, 2),
+                     dim3(64 * kRowsWaves), 0, s, a);
+  return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_DEVICE;
+}
+
 template <int D, int BITS>
 tq_status launch_rows_t(const tq_codebook_s* cb, const uint16_t* x, int64_t n, int64_t stride,
                         const uint8_t* sb, uint8_t* codes, uint16_t* norms, hipStream_t s) {
@@ -988,7 +1156,8 @@ tq_status tq_launch_append(const tq_kv_cache* c, const tq_codebook_s* cbk,
   a.off_k = (float)cbk->nb_half + 0.5f + cbk->enc_shift;
   a.off_v = (float)cbv->nb_half + 0.5f + cbv->enc_shift;
 #define TQ_APP(DD, KK, VV) \
-  if (c->head_dim == DD && c->bits_k == KK && c->bits_v == VV) return launch_append_t<DD, KK, VV>(a, s);
+  if (c->head_dim == DD && c->bits_k == KK && c->bits_v == VV) \
+    return t_new == 1 ? launch_append_token_t<DD, KK, VV>(a, s) : launch_append_t<DD, KK, VV>(a, s);
 #define TQ_APP_D(DD) \
   TQ_APP(DD, 2, 2) TQ_APP(DD, 2, 3) TQ_APP(DD, 2, 4) TQ_APP(DD, 3, 2) TQ_APP(DD, 3, 3) \
   TQ_APP(DD, 3, 4) TQ_APP(DD, 4, 2) TQ_APP(DD, 4, 3) TQ_APP(DD, 4, 4)

@@ -319,6 +319,115 @@ def test_append_capacity_skip_guard_bytes():
                         assert np.array_equal(got[keep], old[keep])
 
 
+@pytest.mark.parametrize("d,bk,bv", [(128, 3, 2), (128, 4, 3), (64, 2, 4), (256, 4, 3),
+                                     (64, 3, 3)])
+def test_append_one_token(d, bk, bv):
+    """One-token appends (decode steps) to 5 layers x 3 sequences x 2 heads,
+    so that the new vectors of one wave pass come from different layers and
+    sequences: each step writes exactly tq_encode's codes and norm of its
+    token at the sequence's position (across a tile and a page boundary, up
+    to the last row), in the contiguous and the paged layout alike;
+    positions outside [0, capacity) write nothing; every other byte, and the
+    guard bytes around each contiguous array, stay unchanged."""
+    torch = require_gpu()
+    Lyr, B, H, cap, P, steps = 5, 3, 2, 256, 64, 4
+    gen = torch.Generator(device="cuda").manual_seed(11)
+    cache = tq.KVCache(Lyr, B, H, d, bk, bv, cap)
+    bufs = {}
+    for name in ("k_codes", "v_codes", "k_norms", "v_norms"):
+        t = getattr(cache, name)
+        bufs[name], view = _guarded(torch, tuple(t.shape), t.dtype, gen)
+        setattr(cache, name, view)
+    before = {k: b.clone() for k, b in bufs.items()}
+    maxp = cap // P
+    rng = np.random.default_rng(d + 10 * bk + bv)
+    num_pages = B * maxp + 3
+    table = rng.permutation(num_pages)[:B * maxp].reshape(B, maxp).astype(np.int32)
+    paged = tq.PagedKVCache(Lyr, B, H, d, bk, bv, P, maxp, num_pages, table)
+    for t in (paged.k_codes, paged.v_codes):
+        t.copy_(torch.randint(0, 256, t.shape, dtype=torch.uint8, device="cuda", generator=gen))
+    for t in (paged.k_norms, paged.v_norms):
+        t.copy_(torch.randint(-2 ** 15, 2 ** 15, t.shape, dtype=torch.int16, device="cuda",
+                              generator=gen))
+    pbefore = {(l, b, h): [x.clone() for x in paged.gather(l, b, h)]
+               for l in range(Lyr) for b in range(B) for h in range(H)}
+    unused = sorted(set(range(num_pages)) - set(table.ravel().tolist()))
+    pool = ("k_codes", "v_codes", "k_norms", "v_norms")
+    unused_before = [getattr(paged, n)[:, unused].clone() for n in pool]
+    sbs = np.stack([synth.sign_bits(SEED, l, d) for l in range(Lyr)])
+    sbd = torch.from_numpy(sbs).cuda()
+    cbk, cbv = tq.Codebook(d, bk), tq.Codebook(d, bv)
+    kn = torch.stack([_dev_kv(torch, SEED, 0, l, B, H, steps, d) for l in range(Lyr)])
+    vn = torch.stack([_dev_kv(torch, SEED, 1, l, B, H, steps, d) for l in range(Lyr)])
+    # sequence 1 crosses a tile and a page boundary, sequence 2 runs into
+    # capacity (its last two steps write nothing)
+    pos = [[s, 62 + s, cap - 2 + s] for s in range(steps)]
+    for s in range(steps):
+        k1 = kn[:, :, :, s:s + 1].contiguous()
+        v1 = vn[:, :, :, s:s + 1].contiguous()
+        p = torch.tensor(pos[s], dtype=torch.int32, device="cuda")
+        for c in (cache, paged):
+            tq.append(c, cbk, cbv, sbd, k1, v1, p, host_max_pos=-1)
+    # starts outside [0, capacity) write nothing
+    p = torch.tensor([-1, 2 ** 31 - 1, cap], dtype=torch.int32, device="cuda")
+    for c in (cache, paged):
+        tq.append(c, cbk, cbv, sbd, kn[:, :, :, :1].contiguous(), vn[:, :, :, :1].contiguous(),
+                  p, host_max_pos=-1)
+    torch.cuda.synchronize()
+    g = 4096
+    for name, buf in bufs.items():
+        item = buf.element_size()
+        assert torch.equal(buf[:g // item], before[name][:g // item]), f"{name}: guard before"
+        assert torch.equal(buf[-(g // item):], before[name][-(g // item):]), f"{name}: guard after"
+
+    def old_of(name, l, b, h):
+        item = bufs[name].element_size()
+        t = getattr(cache, name)
+        return before[name][g // item:g // item + t.numel()].view(t.shape)[l, b, h].cpu().numpy()
+
+    for l in range(Lyr):
+        for b in range(B):
+            for h in range(H):
+                written = [(s, pos[s][b]) for s in range(steps) if 0 <= pos[s][b] < cap]
+                steps_w = [s for s, _ in written]
+                rows = [r for _, r in written]
+                keep = np.ones(cap, bool)
+                keep[rows] = False
+                pk, pv, pkn, pvn = [x.cpu().numpy() for x in paged.gather(l, b, h)]
+                ok, ov, okn, ovn = [x.cpu().numpy() for x in pbefore[(l, b, h)]]
+                for kind, cb, bits in ((0, cbk, bk), (1, cbv, bv)):
+                    src = (kn if kind == 0 else vn)[l, b, h]
+                    codes = torch.empty((steps, d * bits // 8), dtype=torch.uint8, device="cuda")
+                    norms = torch.empty(steps, dtype=torch.int16, device="cuda")
+                    tq.encode(cb, src, sbd[l], codes, norms)
+                    torch.cuda.synchronize()
+                    ref_c = codes.cpu().numpy()[steps_w]
+                    ref_n = norms.cpu().numpy()[steps_w]
+                    what = f"l{l} b{b} h{h} {'kv'[kind]}"
+                    nname = "k_norms" if kind == 0 else "v_norms"
+                    for got_n, old_n in ((getattr(cache, nname)[l, b, h].cpu().numpy(),
+                                          old_of(nname, l, b, h)),
+                                         (pkn if kind == 0 else pvn, okn if kind == 0 else ovn)):
+                        assert np.array_equal(got_n[rows], ref_n), what
+                        assert np.array_equal(got_n[keep], old_n[keep]), what
+                    if kind == 0:
+                        for got, old in ((cache.k_codes[l, b, h].cpu().numpy(),
+                                          old_of("k_codes", l, b, h)), (pk, ok)):
+                            assert np.array_equal(got[rows], ref_c), what
+                            assert np.array_equal(got[keep], old[keep]), what
+                    else:
+                        want = oracle.unpack_rows(ref_c, d, bits)
+                        for got, old in ((cache.v_codes[l, b, h].cpu().numpy(),
+                                          old_of("v_codes", l, b, h)), (pv, ov)):
+                            gu = oracle.unpack_vtiles(got, d, bits)
+                            ou = oracle.unpack_vtiles(old, d, bits)
+                            assert np.array_equal(gu[rows], want), what
+                            assert np.array_equal(gu[keep], ou[keep]), what
+    # pool pages no sequence maps stay untouched
+    for n, was in zip(pool, unused_before):
+        assert torch.equal(getattr(paged, n)[:, unused], was), n
+
+
 @pytest.mark.parametrize("L,B,H,G,d,bk,bv,maxlen", [
     (4, 16, 8, 4, 128, 3, 2, 700),    # 512 units
     (2, 509, 1, 4, 64, 4, 2, 300),    # 1018 units: the last block is not full
