@@ -224,7 +224,7 @@ extern "C" tq_status tq_codebook_init(int head_dim, int bits, tq_codebook* out) 
   }
   const size_t pw = bits == 2 ? 16 : (bits == 3 ? 64 : 256);
   const size_t qw = bits == 2 ? 512 : 0;
-  uint32_t* lut = (uint32_t*)calloc(2 * pw + qw, 4);
+  uint32_t* lut = (uint32_t*)calloc(2 * pw + qw + 16, 4);
   for (size_t e = 0; e < pw; ++e) {
     lut[e] = h[e & (L - 1)] | ((uint32_t)h[e >> bits] << 16);
     lut[pw + e] = r16[e & (L - 1)] | ((uint32_t)r16[e >> bits] << 16);
@@ -233,7 +233,23 @@ extern "C" tq_status tq_codebook_init(int head_dim, int bits, tq_codebook* out) 
     lut[2 * pw + 2 * e] = h[e & 3] | ((uint32_t)h[(e >> 2) & 3] << 16);
     lut[2 * pw + 2 * e + 1] = h[(e >> 4) & 3] | ((uint32_t)h[(e >> 6) & 3] << 16);
   }
-  const size_t lut_words = 2 * pw + qw;
+  /*  pre[k]:     per code, fp16(level * sigma * 2^e) and the fp16 of the
+   *              exact remainder, e putting the largest level in [16, 32)
+   *              (the many-query products add the remainder term in full
+   *              precision instead of scaling it) */
+  int pe = 0;
+  {
+    const double top = fabs(cb->centroids64[L - 1] * cb->sigma);
+    while (top * ldexp(1.0, pe) < 16.0) ++pe;
+    while (top * ldexp(1.0, pe) >= 32.0) --pe;
+  }
+  cb->pre_exp = pe;
+  for (int k = 0; k < L; ++k) {
+    const double v = ldexp(cb->centroids64[k] * cb->sigma, pe);
+    const uint16_t hi = half_rne(v);
+    lut[2 * pw + qw + k] = hi | ((uint32_t)half_rne(v - half_value(hi)) << 16);
+  }
+  const size_t lut_words = 2 * pw + qw + 16;
   size_t enc_bytes = ((size_t)ne * sizeof(tq_enc_entry) + 255) & ~(size_t)255;
   size_t total = enc_bytes + lut_words * 4;
   tq_status st = TQ_OK;
@@ -253,6 +269,7 @@ extern "C" tq_status tq_codebook_init(int head_dim, int bits, tq_codebook* out) 
   cb->dec_lut = (const uint32_t*)((char*)cb->dev_mem + enc_bytes);
   cb->dec_lut_lo = cb->dec_lut + (bits == 2 ? 16 : (bits == 3 ? 64 : 256));
   cb->dec_quad = bits == 2 ? cb->dec_lut + 32 : nullptr;
+  cb->pre_klut = cb->dec_lut + 2 * pw + qw;
   *out = cb;
   return TQ_OK;
 }

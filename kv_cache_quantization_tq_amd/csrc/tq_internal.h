@@ -55,6 +55,12 @@ struct tq_codebook_s {
   const uint32_t* dec_lut; /* one word (two fp16 levels) per pair of codes: 2^(2*bits) words */
   const uint32_t* dec_lut_lo; /* same shape: two fp16 remainders (level - fp16 level) * 2^11 */
   const uint32_t* dec_quad;   /* bits 2: four fp16 levels (two words) per byte of codes */
+  /* one word per code: fp16(level * sigma * 2^pre_exp) in the low half, the
+   * fp16 of its remainder (unscaled) in the high half; pre_exp puts the
+   * largest level in [16, 32), so every remainder is far above fp16's
+   * absolute rounding step */
+  const uint32_t* pre_klut;
+  int pre_exp;
 };
 
 /* Host-side Lloyd-Max (levels / thresholds in fp64, N(0, 1/d)). */

@@ -41,6 +41,7 @@ namespace {
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 constexpr int kCols = 128; /* (head, query) columns per block */
 
@@ -64,7 +65,9 @@ struct PreArgs {
   const uint32_t* lut_k;    /* pair table: two fp16 levels per index */
   const uint32_t* lut_k_lo; /* pair table: two fp16 remainders * 2^11 */
   const uint32_t* lut_v;
+  const uint32_t* lut_k1;   /* per code: fp16 level * 2^e | fp16 remainder << 16 */
   float qscale, oscale;
+  float kscale;             /* 2^-e: key norms against the per-code table */
   float* out;
 };
 
@@ -157,7 +160,7 @@ struct PreGeo {
 __device__ inline int kpos(int t) { return t < 16 ? 8 * (t >> 2) + (t & 3) : 8 * ((t - 16) >> 2) + 4 + (t & 3); }
 
 template <int D, int BK, int BV, bool PAGED>
-__global__ void __launch_bounds__(64 * waves_for(D)) prefill_kernel(PreArgs a) {
+__global__ void __launch_bounds__(64 * waves_for(D)) prefill16_kernel(PreArgs a) {
   using PG = PreGeo<D, BK, BV>;
   constexpr int NG = PG::NG, KS = D / 32, VM = D / 16;
   __shared__ __align__(16) char smem[PG::BYTES];
@@ -470,12 +473,375 @@ __global__ void __launch_bounds__(64 * waves_for(D)) prefill_kernel(PreArgs a) {
   }
 }
 
+/* ------------------------------------------------ 32 x 32 product form -- */
+
+/* Heads of 64 and 128 coordinates: v_mfma_f32_32x32x16_f16, one wave per 32
+ * (head, query) columns, so that a lane holds 16 of the 32 scores of one
+ * column (the other 16 sit in lane l ^ 32).  Operand layouts (lane l, h =
+ * l / 32): A[l % 32][8 h + j], B[8 h + j][l % 32], j < 8; the result C[8 (r
+ * / 4) + 4 h + r % 4][l % 32], r < 16.
+ *
+ * Precision with fewer products than the 16-wide form:
+ *   keys:   level v = hi + lo, hi = fp16(v), lo = fp16(v - hi) (levels
+ *           scaled by 2^e so that lo stays far above fp16's absolute step,
+ *           2^-e folded into the key norms: the query keeps its own scale,
+ *           so its small coordinates do not become subnormal); query q = qh
+ *           + ql in fp16 parts; S^T = Khi Qh + Klo Qh + Khi Ql (the dropped
+ *           Klo Ql is ~2^-22 of the score);
+ *   values: P' = p m / 2^E as fp16 part and fp16 remainder, two products
+ *           with the value levels as the codebook's fp16 table (its scale
+ *           minimises their rounding); E is the running maximum of the
+ *           value-norm exponents, so P' <= 2 and the remainders of the
+ *           weights that matter stay far above fp16's absolute step; the
+ *           accumulator is rescaled when E grows, like the softmax maximum.
+ * The value tile's k index follows the score layout: in each 16-token step,
+ * k = 8 h + j holds token 4 h + (j % 4) + 8 (j / 4), so the P' registers feed
+ * the value product as they are. */
+constexpr int kWaves32 = 4;
+
+template <int D, int BK, int BV>
+struct Geo32 {
+  static constexpr int RBK = D * BK / 8;
+  static constexpr int SEG = D * BV / 16;
+  static constexpr int TILE_V = 32 * D * BV / 8;
+  static constexpr int KP = D + 8;  /* key tile pitch (halfs) */
+  static constexpr int VP = 32 + 8; /* value tile pitch (halfs) */
+  static constexpr int OP = D + 4;  /* query / output row pitch (floats) */
+  static constexpr int LK = 1 << BK, PWV = 1 << (2 * BV);
+  static constexpr int ITEMS = 4 * D; /* 8-code items per tile, keys and values alike */
+  static constexpr int PER = ITEMS / (64 * kWaves32);
+  static constexpr int QBYTES = kCols * OP * 4;
+  /* one tile: khi, klo [32][KP], vt [D][VP] (halfs), nk, nv [32], E */
+  static constexpr int TBYTES = 2 * 32 * KP * 2 + D * VP * 2 + 2 * 32 * 4 + 16;
+  static constexpr int UBYTES = QBYTES > 2 * TBYTES ? QBYTES : 2 * TBYTES;
+  static constexpr int BYTES = UBYTES + (LK + PWV) * 4;
+};
+
+/* k index of tile token t within the value tile rows */
+__device__ inline int kpos32(int t) {
+  const int u = t & 15;
+  return (t & 16) + 8 * ((u >> 2) & 1) + (u & 3) + 4 * (u >> 3);
+}
+
+/* max over the lane pair (l, l ^ 32) */
+__device__ inline float pair_max(float v) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+}
+__device__ inline float pair_sum(float v) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(a[0]) + __uint_as_float(a[1]);
+}
+
+template <int D, int BK, int BV, bool PAGED>
+__global__ void __launch_bounds__(64 * kWaves32) prefill32_kernel(PreArgs a) {
+  using PG = Geo32<D, BK, BV>;
+  constexpr int KS = D / 16, VM = D / 32;
+  __shared__ __align__(16) char smem[PG::BYTES];
+  float* qbuf = (float*)smem; /* [kCols][OP] */
+  auto khi_of = [&](int u) { return (_Float16*)(smem + u * PG::TBYTES); };
+  auto klo_of = [&](int u) { return khi_of(u) + 32 * PG::KP; };
+  auto vt_of = [&](int u) { return khi_of(u) + 64 * PG::KP; };
+  auto nk_of = [&](int u) { return (float*)(vt_of(u) + D * PG::VP); };
+  auto nv_of = [&](int u) { return nk_of(u) + 32; };
+  auto ev_of = [&](int u) { return (int*)(nk_of(u) + 64); };
+  uint32_t* tk = (uint32_t*)(smem + PG::UBYTES); /* per code: hi | lo << 16 */
+  uint32_t* tv = tk + PG::LK;                    /* per pair of codes: two fp16 levels */
+
+  const int tid = threadIdx.x, lane = tid % 64;
+  const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
+  const int cl = lane % 32, hh = lane / 32;
+  const int chunk = blockIdx.x % a.chunks;
+  int64_t unit = blockIdx.x / a.chunks;
+  const int kv = (int)(unit % a.kv_heads);
+  unit /= a.kv_heads;
+  const int b = (int)(unit % a.batch);
+  const int layer = (int)(unit / a.batch);
+  const int q0 = chunk * a.qc;
+  const int qn = (a.t_new - q0) < a.qc ? (a.t_new - q0) : a.qc;
+  int p0 = a.pos[b];
+  p0 = p0 < 0 ? 0 : (p0 > a.capacity ? a.capacity : p0);
+
+  for (int i = tid; i < PG::LK; i += blockDim.x) tk[i] = a.lut_k1[i];
+  for (int i = tid; i < PG::PWV; i += blockDim.x) tv[i] = a.lut_v[i];
+
+  /* queries: column c = head g * qc + query i; q'' = H D q, scaled */
+  const uint8_t* sb = a.sign_bits + (int64_t)layer * (D / 8);
+  for (int t = tid; t < kCols * D; t += blockDim.x) {
+    const int c = t / D, i = t % D;
+    const int g = c / a.qc, qi = c % a.qc;
+    float v = 0.0f;
+    if (g < a.group && qi < qn) {
+      const int64_t row = (((int64_t)layer * a.batch + b) * a.q_heads + (int64_t)kv * a.group + g) *
+                              a.t_new + q0 + qi;
+      v = h2f(a.q[row * D + i]);
+      v = ((sb[i >> 3] >> (i & 7)) & 1) ? -v : v;
+    }
+    qbuf[c * PG::OP + i] = v;
+  }
+  __syncthreads();
+  const int c0 = 32 * wave; /* the wave's columns */
+  for (int r = 0; r < 32; ++r) {
+    float* row = qbuf + (c0 + r) * PG::OP;
+    const Row<D> t = row_fwht<D>(row, lane);
+#pragma unroll
+    for (int j = 0; j < D / 64; ++j) row[lane + 64 * j] = t.v[j] * a.qscale;
+  }
+  __syncthreads();
+  /* B operands: lane (cl, hh) holds coordinates 16 s + 8 hh + 0..7 of column
+   * c0 + cl, as fp16 part and fp16 remainder */
+  half8 qh[KS], ql[KS];
+  {
+    const float* row = qbuf + (c0 + cl) * PG::OP;
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float v = row[16 * s + 8 * hh + j];
+        const _Float16 h = (_Float16)v;
+        qh[s][j] = h;
+        ql[s][j] = (_Float16)(v - (float)h);
+      }
+  }
+  /* causal limit of the lane's column (tokens < lim are attended) */
+  int lim;
+  {
+    const int col = c0 + cl;
+    const int cg = col / a.qc, ci = col % a.qc;
+    const int64_t l = (int64_t)p0 + q0 + ci + 1;
+    lim = (cg < a.group && ci < qn) ? (int)(l > a.capacity ? a.capacity : l) : 1;
+  }
+  const int64_t blk_end = (int64_t)p0 + q0 + qn;
+  const int blk_lim = (int)(blk_end > a.capacity ? a.capacity : blk_end);
+  const int ntiles = (blk_lim + 31) / 32;
+  __syncthreads(); /* qbuf is dead: the tiles take its place */
+
+  const int64_t sh = PAGED ? 0 : (int64_t)b * a.kv_heads + kv;
+  const int64_t srows = PAGED ? (int64_t)a.num_pages * a.kv_heads * (32 << a.lg_tpp) : a.capacity;
+  const __amdgpu_buffer_rsrc_t rk =
+      make_stream(a.k_codes + layer * a.ls_kc + sh * a.capacity * PG::RBK, srows * PG::RBK);
+  const __amdgpu_buffer_rsrc_t rv = make_stream(
+      a.v_codes + layer * a.ls_vc + sh * (a.capacity / 32) * PG::TILE_V, srows / 32 * PG::TILE_V);
+  const __amdgpu_buffer_rsrc_t rkn = make_stream(a.k_norms + layer * a.ls_kn + sh * a.capacity * 2, srows * 2);
+  const __amdgpu_buffer_rsrc_t rvn = make_stream(a.v_norms + layer * a.ls_vn + sh * a.capacity * 2, srows * 2);
+  auto tile_rows = [&](int t) -> int32_t {
+    if constexpr (PAGED) {
+      const int tpp = 1 << a.lg_tpp;
+      int phys = a.block_table[(int64_t)b * a.max_pages + (t >> a.lg_tpp)];
+      phys = phys < 0 ? 0 : (phys >= a.num_pages ? a.num_pages - 1 : phys);
+      return (phys * a.kv_heads + kv) * (tpp * 32) + (t & (tpp - 1)) * 32;
+    } else {
+      return t * 32;
+    }
+  };
+
+  /* raw codes of one tile: PER key items and PER value items per thread;
+   * threads 0..31 load the key norms, 32..63 the value norms */
+  uint32_t kraw[PG::PER], vraw[PG::PER], nraw = 0;
+  auto fetch = [&](int t) {
+    const int32_t r0 = tile_rows(t);
+#pragma unroll
+    for (int u = 0; u < PG::PER; ++u) {
+      const int it = tid + u * 64 * kWaves32;
+      const int tok = it / (D / 8), grp = it % (D / 8);
+      kraw[u] = load_codes8<BK>(rk, (r0 + tok) * PG::RBK + grp * BK);
+      const int seg = it / (D / 16), m = it % (D / 16);
+      vraw[u] = load_codes8<BV>(rv, (r0 / 32) * PG::TILE_V + seg * PG::SEG + m * BV);
+    }
+    if (tid < 32)
+      nraw = __builtin_amdgcn_raw_buffer_load_b16(rkn, (uint32_t)(r0 + tid) * 2u, 0, 0);
+    else if (tid < 64)
+      nraw = __builtin_amdgcn_raw_buffer_load_b16(rvn, (uint32_t)(r0 + tid - 32) * 2u, 0, 0);
+  };
+  /* running value-norm exponent (meaningful in threads 32..63) */
+  int e_run = -25;
+  auto spill = [&](int u) {
+    _Float16* khi = khi_of(u);
+    _Float16* klo = klo_of(u);
+    _Float16* vt = vt_of(u);
+#pragma unroll
+    for (int w = 0; w < PG::PER; ++w) {
+      const int it = tid + w * 64 * kWaves32;
+      const int tok = it / (D / 8), grp = it % (D / 8);
+      uint32_t e[8];
+#pragma unroll
+      for (int p = 0; p < 8; ++p) e[p] = tk[(kraw[w] >> (BK * p)) & (PG::LK - 1)];
+      u32x4 hv, lv;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        hv[p] = __builtin_amdgcn_perm(e[2 * p + 1], e[2 * p], 0x05040100u);
+        lv[p] = __builtin_amdgcn_perm(e[2 * p + 1], e[2 * p], 0x07060302u);
+      }
+      *(u32x4*)(khi + tok * PG::KP + 8 * grp) = hv;
+      *(u32x4*)(klo + tok * PG::KP + 8 * grp) = lv;
+      /* value segment seg = 16 q + r, field m: coordinate r (d/16) + m of
+       * tokens 8 q + 0..7; tokens 8 q + 0..3 and 8 q + 4..7 are runs of 4
+       * in the row's k order */
+      const int seg = it / (D / 16), m = it % (D / 16);
+      const int qq = seg >> 4, rr = seg & 15;
+      _Float16* vrow = vt + (rr * (D / 16) + m) * PG::VP + 16 * (qq >> 1) + 4 * (qq & 1);
+      uint32_t pv[4];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) pv[p] = tv[(vraw[w] >> (2 * BV * p)) & (PG::PWV - 1)];
+      *(uint2*)vrow = make_uint2(pv[0], pv[1]);
+      *(uint2*)(vrow + 8) = make_uint2(pv[2], pv[3]);
+    }
+    /* norms; the value norms scaled by 2^-E, E the running maximum of the
+     * tiles' largest value-norm exponents */
+    const float nf = h2f(nraw);
+    float mx = nf;
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 32));
+    const int et = ((int)(__float_as_uint(mx) >> 23) & 255) - 127;
+    e_run = et > e_run ? et : e_run;
+    if (tid < 32) nk_of(u)[tid] = nf * a.kscale;
+    else if (tid < 64) nv_of(u)[tid - 32] = __builtin_ldexpf(nf, -e_run);
+    if (tid == 32) *ev_of(u) = e_run;
+  };
+
+  floatx16 acc[VM];
+#pragma unroll
+  for (int m = 0; m < VM; ++m)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[m][i] = 0.0f;
+  float m_run = -INFINITY, l_run = 0.0f;
+  int e_cur = -25;
+
+  /* tile t is multiplied from buffer t % 2 while tile t + 1 is dequantized
+   * into the other one and tile t + 2's codes are loaded (past the last
+   * tile, the last tile again): one barrier a tile */
+  fetch(0);
+  spill(0);
+  fetch(ntiles > 1 ? 1 : 0);
+  __syncthreads();
+  for (int t = 0; t < ntiles; ++t) {
+    const int u = t & 1;
+    const _Float16* khi = khi_of(u);
+    const _Float16* klo = klo_of(u);
+    const _Float16* vt = vt_of(u);
+    const float* nk = nk_of(u);
+    const float* nv = nv_of(u);
+    const int et = *ev_of(u);
+    floatx16 S;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) S[i] = 0.0f;
+    const _Float16* kr = khi + cl * PG::KP + 8 * hh;
+    const _Float16* kl = klo + cl * PG::KP + 8 * hh;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const half8 ah = *(const half8*)(kr + 16 * ks);
+      const half8 al = *(const half8*)(kl + 16 * ks);
+      S = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, qh[ks], S, 0, 0, 0);
+      S = __builtin_amdgcn_mfma_f32_32x32x16_f16(al, qh[ks], S, 0, 0, 0);
+      S = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah, ql[ks], S, 0, 0, 0);
+    }
+    spill(u ^ 1);
+    fetch(t + 2 < ntiles ? t + 2 : ntiles - 1);
+    /* S[r]: token 8 (r / 4) + 4 hh + r % 4 of the lane's column */
+    float nkv[16], nvv[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 a4 = *(const float4*)(nk + 8 * q + 4 * hh);
+      const float4 b4 = *(const float4*)(nv + 8 * q + 4 * hh);
+      nkv[4 * q] = a4.x, nkv[4 * q + 1] = a4.y, nkv[4 * q + 2] = a4.z, nkv[4 * q + 3] = a4.w;
+      nvv[4 * q] = b4.x, nvv[4 * q + 1] = b4.y, nvv[4 * q + 2] = b4.z, nvv[4 * q + 3] = b4.w;
+    }
+    if (et > e_cur) {
+      /* uniform over the block: a larger value-norm scale */
+      const float f = __builtin_ldexpf(1.0f, e_cur - et);
+#pragma unroll
+      for (int m = 0; m < VM; ++m) acc[m] *= f;
+      e_cur = et;
+    }
+    const int tok0 = 32 * t;
+    const bool edge = tok0 + 32 > p0 + q0 + 1; /* some column may stop inside */
+    float sc[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float v = S[r] * nkv[r];
+      if (edge && tok0 + 8 * (r >> 2) + 4 * hh + (r & 3) >= lim) v = -INFINITY;
+      sc[r] = v;
+    }
+    float mt = sc[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mt = fmaxf(mt, sc[r]);
+    mt = pair_max(mt);
+    if (__any(mt > m_run)) {
+      const float mn = fmaxf(m_run, mt);
+      const float al = __builtin_amdgcn_exp2f(m_run - mn); /* 0 on the first tile */
+      l_run *= al;
+#pragma unroll
+      for (int m = 0; m < VM; ++m) acc[m] *= al;
+      m_run = mn;
+    }
+    half8 ph[2], pl[2];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p = __builtin_amdgcn_exp2f(sc[r] - m_run);
+      l_run += p;
+      /* fp16(p m) and the fp16 of the exact remainder, one fma each */
+      const _Float16 h = (_Float16)__builtin_fmaf(p, nvv[r], 0.0f);
+      ph[r >> 3][r & 7] = h;
+      pl[r >> 3][r & 7] = (_Float16)__builtin_fmaf(p, nvv[r], -(float)h);
+    }
+#pragma unroll
+    for (int m = 0; m < VM; ++m) {
+      const _Float16* vr = vt + (32 * m + cl) * PG::VP + 8 * hh;
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const half8 av = *(const half8*)(vr + 16 * k);
+        acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, ph[k], acc[m], 0, 0, 0);
+        acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, pl[k], acc[m], 0, 0, 0);
+      }
+    }
+    __syncthreads();
+  }
+
+  /* o'' = acc 2^E / l into LDS rows, then o = D H o'' per row */
+  float* obuf = qbuf;
+  {
+    const float inv = __builtin_ldexpf(a.oscale, e_cur) / pair_sum(l_run);
+    float* orow = obuf + (c0 + cl) * PG::OP;
+#pragma unroll
+    for (int m = 0; m < VM; ++m)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *(float4*)(orow + 32 * m + 8 * q + 4 * hh) =
+            make_float4(acc[m][4 * q] * inv, acc[m][4 * q + 1] * inv, acc[m][4 * q + 2] * inv,
+                        acc[m][4 * q + 3] * inv);
+  }
+  __syncthreads();
+  for (int r = 0; r < 32; ++r) {
+    const int c = c0 + r;
+    const int g = c / a.qc, qi = c % a.qc;
+    const Row<D> t = row_fwht<D>(obuf + c * PG::OP, lane);
+    if (g < a.group && qi < qn) {
+      const int64_t row = (((int64_t)layer * a.batch + b) * a.q_heads + (int64_t)kv * a.group + g) *
+                              a.t_new + q0 + qi;
+#pragma unroll
+      for (int j = 0; j < D / 64; ++j) {
+        const int i = lane + 64 * j;
+        const float v = t.v[j];
+        a.out[row * D + i] = ((sb[i >> 3] >> (i & 7)) & 1) ? -v : v;
+      }
+    }
+  }
+}
+
 template <int D, int BK, int BV>
 tq_status launch_prefill_t(const PreArgs& a, int64_t blocks, hipStream_t s) {
-  if (a.block_table)
-    hipLaunchKernelGGL((prefill_kernel<D, BK, BV, true>), dim3((unsigned)blocks), dim3(64 * waves_for(D)), 0, s, a);
-  else
-    hipLaunchKernelGGL((prefill_kernel<D, BK, BV, false>), dim3((unsigned)blocks), dim3(64 * waves_for(D)), 0, s, a);
+  const dim3 grid((unsigned)blocks);
+  if constexpr (D == 256) {
+    if (a.block_table)
+      hipLaunchKernelGGL((prefill16_kernel<D, BK, BV, true>), grid, dim3(64 * waves_for(D)), 0, s, a);
+    else
+      hipLaunchKernelGGL((prefill16_kernel<D, BK, BV, false>), grid, dim3(64 * waves_for(D)), 0, s, a);
+  } else {
+    if (a.block_table)
+      hipLaunchKernelGGL((prefill32_kernel<D, BK, BV, true>), grid, dim3(64 * kWaves32), 0, s, a);
+    else
+      hipLaunchKernelGGL((prefill32_kernel<D, BK, BV, false>), grid, dim3(64 * kWaves32), 0, s, a);
+  }
   return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_DEVICE;
 }
 
@@ -516,8 +882,10 @@ tq_status tq_launch_prefill(const tq_kv_cache* c, const tq_codebook_s* cbk,
   a.lut_k = cbk->dec_lut;
   a.lut_k_lo = cbk->dec_lut_lo;
   a.lut_v = cbv->dec_lut;
+  a.lut_k1 = cbk->pre_klut;
   const double d = c->head_dim;
   a.qscale = (float)(1.4426950408889634 / (d * cbk->sigma));
+  a.kscale = (float)ldexp(1.0, -cbk->pre_exp);
   a.oscale = (float)(1.0 / (sqrt(d) * cbv->sigma));
   a.out = out;
   const int64_t blocks = (int64_t)n_layers * c->batch * c->kv_heads * a.chunks;
