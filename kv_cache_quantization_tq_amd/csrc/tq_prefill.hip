@@ -34,6 +34,8 @@
  */
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "tq_internal.h"
 
 namespace {
@@ -688,15 +690,17 @@ __global__ void __launch_bounds__(64 * kWaves32) prefill32_kernel(PreArgs a) {
     }
     /* norms; the value norms scaled by 2^-E, E the running maximum of the
      * tiles' largest value-norm exponents */
-    const float nf = h2f(nraw);
-    float mx = nf;
+    if (wave == 0) {
+      const float nf = h2f(nraw);
+      float mx = tid >= 32 ? nf : 0.0f;
 #pragma unroll
-    for (int o = 1; o < 32; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 32));
-    const int et = ((int)(__float_as_uint(mx) >> 23) & 255) - 127;
-    e_run = et > e_run ? et : e_run;
-    if (tid < 32) nk_of(u)[tid] = nf * a.kscale;
-    else if (tid < 64) nv_of(u)[tid - 32] = __builtin_ldexpf(nf, -e_run);
-    if (tid == 32) *ev_of(u) = e_run;
+      for (int o = 1; o < 32; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 32));
+      const int et = ((int)(__float_as_uint(mx) >> 23) & 255) - 127;
+      e_run = et > e_run ? et : e_run;
+      if (tid < 32) nk_of(u)[tid] = nf * a.kscale;
+      else nv_of(u)[tid - 32] = __builtin_ldexpf(nf, -e_run);
+      if (tid == 32) *ev_of(u) = e_run;
+    }
   };
 
   floatx16 acc[VM];
@@ -714,7 +718,12 @@ __global__ void __launch_bounds__(64 * kWaves32) prefill32_kernel(PreArgs a) {
   spill(0);
   fetch(ntiles > 1 ? 1 : 0);
   __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
+  /* tiles below t_edge end at or before every real column's first query
+   * (padding columns attend token 0 only, but their outputs are not
+   * written, so they need no mask there either) */
+  const int t_edge = (p0 + q0 + 1) / 32 < ntiles ? (p0 + q0 + 1) / 32 : ntiles;
+  auto step = [&](const int t, auto edge_tag) {
+    constexpr bool EDGE = decltype(edge_tag)::value;
     const int u = t & 1;
     const _Float16* khi = khi_of(u);
     const _Float16* klo = klo_of(u);
@@ -753,13 +762,11 @@ __global__ void __launch_bounds__(64 * kWaves32) prefill32_kernel(PreArgs a) {
       for (int m = 0; m < VM; ++m) acc[m] *= f;
       e_cur = et;
     }
-    const int tok0 = 32 * t;
-    const bool edge = tok0 + 32 > p0 + q0 + 1; /* some column may stop inside */
     float sc[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       float v = S[r] * nkv[r];
-      if (edge && tok0 + 8 * (r >> 2) + 4 * hh + (r & 3) >= lim) v = -INFINITY;
+      if (EDGE && 32 * t + 8 * (r >> 2) + 4 * hh + (r & 3) >= lim) v = -INFINITY;
       sc[r] = v;
     }
     float mt = sc[0];
@@ -795,7 +802,10 @@ __global__ void __launch_bounds__(64 * kWaves32) prefill32_kernel(PreArgs a) {
       }
     }
     __syncthreads();
-  }
+  };
+  int t = 0;
+  for (; t < t_edge; ++t) step(t, std::false_type{});
+  for (; t < ntiles; ++t) step(t, std::true_type{});
 
   /* o'' = acc 2^E / l into LDS rows, then o = D H o'' per row */
   float* obuf = qbuf;
