@@ -314,7 +314,7 @@ __device__ inline uint32_t pair_field(const uint32_t* cw, int p) {
 
 template <int D, int B>
 __device__ inline void enc_keys_m(const EncSlotM<D, B>& r, const QjlEncArgs& a, const _Float16* sl,
-                                  const _Float16* hl, const float2* plev,
+                                  const u32x4* hpt, const float2* plev,
                                   const uint32_t (&fm)[D / 32][4], int64_t v0, int lane, int n,
                                   int kq) {
   constexpr int KS = D / 32, NL = D / 4;
@@ -347,10 +347,18 @@ __device__ inline void enc_keys_m(const EncSlotM<D, B>& r, const QjlEncArgs& a, 
 #pragma unroll
   for (int mt = 0; mt < D / 16; ++mt) {
     floatx4 t = {0.f, 0.f, 0.f, 0.f};
+    /* row R of Hp held by the lane: (-1)^popcount(R & c) for columns c =
+     * 32 s + 8 kq + j splits over disjoint bits into the pattern of R & 7
+     * over j, one sign for R & 8 kq (both from the table) and one for
+     * R & 32 s (a sign flip of all eight entries) */
+    const int R = hp_row<D>(16 * mt + n);
+    const u32x4 base = hpt[(R & 7) | ((__builtin_popcount((unsigned)(R & (8 * kq))) & 1) << 3)];
 #pragma unroll
-    for (int s = 0; s < KS; ++s)
-      t = __builtin_amdgcn_mfma_f32_16x16x32_f16(
-          *(const half8*)(hl + (16 * mt + n) * SL::P + 32 * s + 8 * kq), xb[s], t, 0, 0, 0);
+    for (int s = 0; s < KS; ++s) {
+      const uint32_t f = (__builtin_popcount((unsigned)(R & (32 * s))) & 1) ? 0x80008000u : 0u;
+      const u32x4 hw = {base[0] ^ f, base[1] ^ f, base[2] ^ f, base[3] ^ f};
+      t = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, hw), xb[s], t, 0, 0, 0);
+    }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const float2 c = plev[pair_field<B>(r.cw, 2 * mt + h) * 4 + cpy];
@@ -374,21 +382,26 @@ __device__ inline void enc_keys_m(const EncSlotM<D, B>& r, const QjlEncArgs& a, 
 }
 
 template <int D, int B>
-__global__ void __launch_bounds__(256) qjl_encode_kernel(QjlEncArgs a) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 3 : 1)))
+qjl_encode_kernel(QjlEncArgs a) {
   using SL = SLds<D>;
   __shared__ __align__(16) _Float16 sl[SL::HALFS];
   /* the levels of each pair of codes (first code in the low bits), 4 copies
    * (entry 4 p + lane % 4) */
   __shared__ float2 plev[(1 << (2 * B)) * 4];
-  /* Hp (rows reordered Hadamard matrix, padded rows like S) for d <= 128 */
-  __shared__ __align__(16) _Float16 hl[SL::HALFS];
+  /* for d <= 128, the rows of Hp (rows reordered Hadamard matrix) over 8
+   * consecutive columns 8 k + j: entry p + 8 c holds the fp16 +-1 values
+   * (-1)^(popcount(p & j) + c), j = 0..7 */
+  __shared__ u32x4 hpt[16];
   const int lane = threadIdx.x % 64, n = lane % 16, kq = lane / 16;
-  if constexpr (SL::ON) {
-    for (int e = threadIdx.x; e < D * D; e += blockDim.x) {
-      const int rr = e / D, c = e % D;
-      hl[rr * SL::P + c] = (__builtin_popcount((unsigned)(hp_row<D>(rr) & c)) & 1)
-                               ? (_Float16)-1.0f : (_Float16)1.0f;
-    }
+  if (threadIdx.x < 16) {
+    const int p = threadIdx.x & 7, c = threadIdx.x >> 3;
+    u32x4 w;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      w[k] = 0x3C003C00u | ((uint32_t)((__builtin_popcount((unsigned)(p & (2 * k))) + c) & 1) << 15) |
+             ((uint32_t)((__builtin_popcount((unsigned)(p & (2 * k + 1))) + c) & 1) << 31);
+    hpt[threadIdx.x] = w;
   }
   for (int e = threadIdx.x; e < (1 << (2 * B)) * 4; e += blockDim.x) {
     const int p = e / 4;
@@ -424,13 +437,13 @@ __global__ void __launch_bounds__(256) qjl_encode_kernel(QjlEncArgs a) {
     enc_load_m<D, B>(ra, a, v0, n, kq);
     for (int64_t k = 0; k + 2 <= cnt; k += 2) {
       enc_load_m<D, B>(rb, a, v0 + stride, n, kq);
-      enc_keys_m<D, B>(ra, a, sl, hl, plev, fm, v0, lane, n, kq);
+      enc_keys_m<D, B>(ra, a, sl, hpt, plev, fm, v0, lane, n, kq);
       v0 += stride;
       if (k + 2 < cnt) enc_load_m<D, B>(ra, a, v0 + stride, n, kq);
-      enc_keys_m<D, B>(rb, a, sl, hl, plev, fm, v0, lane, n, kq);
+      enc_keys_m<D, B>(rb, a, sl, hpt, plev, fm, v0, lane, n, kq);
       v0 += stride;
     }
-    if (cnt & 1) enc_keys_m<D, B>(ra, a, sl, hl, plev, fm, v0, lane, n, kq);
+    if (cnt & 1) enc_keys_m<D, B>(ra, a, sl, hpt, plev, fm, v0, lane, n, kq);
   } else {
     /* one slot: with the rotation in registers a second one would cost the
      * second wave per SIMD, which hides more */
