@@ -467,6 +467,7 @@ struct QjlScoreArgs {
   int64_t T;
   float* out; /* [G][T] */
   int vec_out; /* T % 4 == 0 and out 16-byte aligned: rows of 4 keys go out as one store */
+  int vec_ng;  /* norms and gamma 8-byte aligned: 4 keys' values in one load each */
   float levels[16];
 };
 
@@ -491,7 +492,7 @@ struct KeySlice {
   static constexpr int ZW = (KS + 3) / 4;    /* KS sign bytes */
   uint32_t cw[CW];
   uint32_t zw[ZW];
-  uint16_t nm[4], gm[4];
+  uint32_t nm[2], gm[2]; /* fp16 norms / gammas of the 4 keys, two per word */
 };
 
 /* Streamed once: non-temporal loads.  Keys past the end are clamped to the
@@ -527,11 +528,22 @@ __device__ inline void load_slice(KeySlice<D, B>& r, const QjlScoreArgs& a, int6
   else
 #pragma unroll
     for (int k = 0; k < KSl::ZW; ++k) r.zw[k] = __builtin_nontemporal_load((const uint32_t*)zp + k);
+  const int64_t k4 = k0 + 4 * kq;
+  if (a.vec_ng && k4 + 3 <= last) {
+    /* the 4 keys' norms and gammas as one 8-byte load each */
+    const u32x2 nw = __builtin_nontemporal_load((const u32x2*)(a.norms + k4));
+    const u32x2 gw = __builtin_nontemporal_load((const u32x2*)(a.gamma + k4));
+    r.nm[0] = nw[0], r.nm[1] = nw[1], r.gm[0] = gw[0], r.gm[1] = gw[1];
+  } else {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int64_t kk = k0 + 4 * kq + i < last ? k0 + 4 * kq + i : last;
-    r.nm[i] = __builtin_nontemporal_load(a.norms + kk);
-    r.gm[i] = __builtin_nontemporal_load(a.gamma + kk);
+    for (int i = 0; i < 2; ++i) {
+      const int64_t k = k4 + 2 * i < last ? k4 + 2 * i : last;
+      const int64_t k1 = k4 + 2 * i + 1 < last ? k4 + 2 * i + 1 : last;
+      r.nm[i] = (uint32_t)__builtin_nontemporal_load(a.norms + k) |
+                ((uint32_t)__builtin_nontemporal_load(a.norms + k1) << 16);
+      r.gm[i] = (uint32_t)__builtin_nontemporal_load(a.gamma + k) |
+                ((uint32_t)__builtin_nontemporal_load(a.gamma + k1) << 16);
+    }
   }
 }
 
@@ -592,7 +604,9 @@ __device__ inline void score_tile(const KeySlice<D, B>& r, const half8 (&bv)[2 *
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const float m1 = c1[i] + ror8(c1[i]), m2 = c2[i] + ror8(c2[i]);
-    o[i] = h2f(r.nm[i]) * (m1 + h2f(r.gm[i]) * m2);
+    const uint16_t nh = (uint16_t)(r.nm[i / 2] >> (16 * (i & 1)));
+    const uint16_t gh = (uint16_t)(r.gm[i / 2] >> (16 * (i & 1)));
+    o[i] = h2f(nh) * (m1 + h2f(gh) * m2);
   }
   if (n < a.G) {
     const int64_t kb = k0 + 4 * kq;
@@ -608,7 +622,8 @@ __device__ inline void score_tile(const KeySlice<D, B>& r, const half8 (&bv)[2 *
 }
 
 template <int D, int B>
-__global__ void __launch_bounds__(256) qjl_scores_kernel(QjlScoreArgs a) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D <= 128 ? 4 : 1)))
+qjl_scores_kernel(QjlScoreArgs a) {
   constexpr int KS = D / 32;
   __shared__ float rq[8][D];   /* R q */
   __shared__ float sq[8][D];   /* S R q * sqrt(pi/2) / d */
@@ -718,15 +733,23 @@ __global__ void __launch_bounds__(256) qjl_scores_kernel(QjlScoreArgs a) {
   const int64_t cnt = 2 * pcnt - (2 * (p0 + (pcnt - 1) * stride) + 1 >= ntile ? 1 : 0);
   /* the wave's k-th tile */
   auto tile_of = [&](int64_t k) { return 2 * (p0 + (k >> 1) * stride) + (k & 1); };
-  KeySlice<D, B> ra, rb;
-  load_slice<D, B>(ra, a, tile_of(0) * 16, n, kq);
-  for (int64_t k = 0; k + 2 <= cnt; k += 2) {
-    load_slice<D, B>(rb, a, tile_of(k + 1) * 16, n, kq);
-    score_tile<D, B>(ra, bv, bs, tb, cpy, a, tile_of(k) * 16, n, kq);
-    if (k + 2 < cnt) load_slice<D, B>(ra, a, tile_of(k + 2) * 16, n, kq);
-    score_tile<D, B>(rb, bv, bs, tb, cpy, a, tile_of(k + 1) * 16, n, kq);
+  /* three register slots: two tiles' loads in flight while one is scored
+   * (tiles past the wave's last load its last tile again, unscored) */
+  KeySlice<D, B> ra, rb, rc;
+  auto tl = [&](int64_t k) { return tile_of(k < cnt ? k : cnt - 1) * 16; };
+  load_slice<D, B>(ra, a, tl(0), n, kq);
+  load_slice<D, B>(rb, a, tl(1), n, kq);
+  int64_t k = 0;
+  for (; k + 3 <= cnt; k += 3) {
+    load_slice<D, B>(rc, a, tl(k + 2), n, kq);
+    score_tile<D, B>(ra, bv, bs, tb, cpy, a, tl(k), n, kq);
+    load_slice<D, B>(ra, a, tl(k + 3), n, kq);
+    score_tile<D, B>(rb, bv, bs, tb, cpy, a, tl(k + 1), n, kq);
+    load_slice<D, B>(rb, a, tl(k + 4), n, kq);
+    score_tile<D, B>(rc, bv, bs, tb, cpy, a, tl(k + 2), n, kq);
   }
-  if (cnt & 1) score_tile<D, B>(ra, bv, bs, tb, cpy, a, tile_of(cnt - 1) * 16, n, kq);
+  if (k < cnt) score_tile<D, B>(ra, bv, bs, tb, cpy, a, tl(k), n, kq);
+  if (k + 1 < cnt) score_tile<D, B>(rb, bv, bs, tb, cpy, a, tl(k + 1), n, kq);
 }
 
 /* Blocks of kernel K (256 threads) the device holds at once (occupancy x
@@ -797,6 +820,7 @@ tq_status tq_launch_qjl_scores(const tq_codebook_s* cb, const uint16_t* q, int G
   a.T = T;
   a.out = out;
   a.vec_out = T % 4 == 0 && ((uintptr_t)out & 15) == 0;
+  a.vec_ng = ((uintptr_t)norms & 7) == 0 && ((uintptr_t)gamma & 7) == 0;
   for (int k = 0; k < 16; ++k) a.levels[k] = k < (1 << cb->bits) ? cb->centroids[k] : 0.0f;
   /* 4 waves of two 16-key tiles a block; at most one round of resident
    * blocks, whose waves then stride (each block projects the queries once) */
