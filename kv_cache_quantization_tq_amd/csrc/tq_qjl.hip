@@ -578,9 +578,9 @@ struct ScoreLds {
  * (A = {c0, c1, r0, r1, c2, c3, r2, r3} fp16 straight from two table words,
  * B = the query parts in the same order), the signs in one. */
 template <int D, int B>
-__device__ inline void score_tile(const KeySlice<D, B>& r, const half8 (&bv)[2 * (D / 32)],
-                                  const half8 (&bs)[D / 32], const ScoreLds<B>& tb,
-                                  uint32_t cpy, const QjlScoreArgs& a, int64_t k0, int n, int kq) {
+__device__ inline floatv4 score_tile(const KeySlice<D, B>& r, const half8 (&bv)[2 * (D / 32)],
+                                     const half8 (&bs)[D / 32], const ScoreLds<B>& tb,
+                                     uint32_t cpy, int n) {
   constexpr int KS = D / 32;
   floatx4 c1 = {0.f, 0.f, 0.f, 0.f}, c2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -608,15 +608,22 @@ __device__ inline void score_tile(const KeySlice<D, B>& r, const half8 (&bv)[2 *
     const uint16_t gh = (uint16_t)(r.gm[i / 2] >> (16 * (i & 1)));
     o[i] = h2f(nh) * (m1 + h2f(gh) * m2);
   }
+  return o;
+}
+
+/* Store one tile's estimates: lane (n, kq) holds keys k0 + 4 kq + 0..3 of
+ * query n. */
+__device__ inline void store_tile(const QjlScoreArgs& a, floatv4 o, int64_t k0, int n, int kq) {
   if (n < a.G) {
     const int64_t kb = k0 + 4 * kq;
     float* dst = a.out + n * a.T + kb;
+    /* ordinary stores: the two halves of a line meet in the cache */
     if (a.vec_out && kb + 4 <= a.T) {
-      __builtin_nontemporal_store(o, (floatv4*)dst);
+      *(floatv4*)dst = o;
     } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        if (kb + i < a.T) __builtin_nontemporal_store(o[i], dst + i);
+        if (kb + i < a.T) dst[i] = o[i];
     }
   }
 }
@@ -734,22 +741,33 @@ qjl_scores_kernel(QjlScoreArgs a) {
   /* the wave's k-th tile */
   auto tile_of = [&](int64_t k) { return 2 * (p0 + (k >> 1) * stride) + (k & 1); };
   /* three register slots: two tiles' loads in flight while one is scored
-   * (tiles past the wave's last load its last tile again, unscored) */
+   * (tiles past the wave's last load its last tile again, unscored).  The
+   * estimates of the first tile of a pair wait for the second's, so that
+   * the two halves of each 128-byte output line go out back to back. */
   KeySlice<D, B> ra, rb, rc;
   auto tl = [&](int64_t k) { return tile_of(k < cnt ? k : cnt - 1) * 16; };
+  floatv4 held = {0.f, 0.f, 0.f, 0.f};
+  auto emit = [&](int64_t k, floatv4 o) {
+    if (!(k & 1) && k + 1 < cnt) {
+      held = o;
+    } else {
+      if (k & 1) store_tile(a, held, tl(k - 1), n, kq);
+      store_tile(a, o, tl(k), n, kq);
+    }
+  };
   load_slice<D, B>(ra, a, tl(0), n, kq);
   load_slice<D, B>(rb, a, tl(1), n, kq);
   int64_t k = 0;
   for (; k + 3 <= cnt; k += 3) {
     load_slice<D, B>(rc, a, tl(k + 2), n, kq);
-    score_tile<D, B>(ra, bv, bs, tb, cpy, a, tl(k), n, kq);
+    emit(k, score_tile<D, B>(ra, bv, bs, tb, cpy, n));
     load_slice<D, B>(ra, a, tl(k + 3), n, kq);
-    score_tile<D, B>(rb, bv, bs, tb, cpy, a, tl(k + 1), n, kq);
+    emit(k + 1, score_tile<D, B>(rb, bv, bs, tb, cpy, n));
     load_slice<D, B>(rb, a, tl(k + 4), n, kq);
-    score_tile<D, B>(rc, bv, bs, tb, cpy, a, tl(k + 2), n, kq);
+    emit(k + 2, score_tile<D, B>(rc, bv, bs, tb, cpy, n));
   }
-  if (k < cnt) score_tile<D, B>(ra, bv, bs, tb, cpy, a, tl(k), n, kq);
-  if (k + 1 < cnt) score_tile<D, B>(rb, bv, bs, tb, cpy, a, tl(k + 1), n, kq);
+  if (k < cnt) emit(k, score_tile<D, B>(ra, bv, bs, tb, cpy, n));
+  if (k + 1 < cnt) emit(k + 1, score_tile<D, B>(rb, bv, bs, tb, cpy, n));
 }
 
 /* Blocks of kernel K (256 threads) the device holds at once (occupancy x
