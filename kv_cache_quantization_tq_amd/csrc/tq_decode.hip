@@ -77,21 +77,25 @@ struct KTab {
 template <int B>
 struct VTab {
   static constexpr bool QUAD = B == 2;
-  static constexpr int ENTRIES = B == 3 ? 64 : 256;
+  /* 3 bits: the 64 pair entries in 256 rows repeating every 64, so that the
+   * index is the low 6 bits of a byte */
+  static constexpr int ENTRIES = 256;
+  static constexpr int SRC = B == 3 ? 64 : 256;
   static constexpr int BYTES = ENTRIES * 256;
 };
 
-/* Fill a word table: 64 copies of src[e] per row.  All of a thread's source
- * words are loaded before any is stored, so the block waits for one round of
- * (L2-resident) loads rather than one per iteration. */
-template <int ENTRIES, int WAVES>
+/* Fill a word table: 64 copies of src[e] per row, e the row index modulo
+ * SRC.  All of a thread's source words are loaded before any is stored, so
+ * the block waits for one round of (L2-resident) loads rather than one per
+ * iteration. */
+template <int ENTRIES, int WAVES, int SRC = ENTRIES>
 __device__ inline void fill_words(uint32_t* dst, const uint32_t* src) {
   constexpr int N = ENTRIES * 64, T = 64 * WAVES, IT = (N + T - 1) / T;
   uint32_t v[IT];
 #pragma unroll
   for (int k = 0; k < IT; ++k) {
     const int i = threadIdx.x + k * T;
-    v[k] = i < N ? src[i >> 6] : 0u;
+    v[k] = i < N ? src[(i >> 6) % SRC] : 0u;
   }
 #pragma unroll
   for (int k = 0; k < IT; ++k) {
@@ -673,6 +677,27 @@ __device__ inline void value_part(const float (&p)[8 / CF], typename NormWords<C
       const u32x4 av = {w0.x, w0.y, w1.x, w1.y};
       acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, av), pb, acc[m], 0, 0, 0);
     }
+  } else if constexpr (BV == 3) {
+    /* fields m, m + 1 (m even) are the 48 bits from bit 24 m: shifted right
+     * by 24 m + 6 k, the string holds pair k of field m in the low 6 bits of
+     * byte 0 and pair k of field m + 1 in those of byte 3 (the table's rows
+     * repeat every 64), so one funnel shift serves two lookups */
+#pragma unroll
+    for (int g = 0; g < DG::VM / 2; ++g) {
+      u32x4 a0, a1;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int p = 48 * g + 6 * k, i = p / 32, sh = p % 32;
+        const uint32_t hi = i + 1 < DG::VW ? vw[i + 1] : 0u;
+        const uint32_t x = sh == 0 ? vw[i] : __builtin_amdgcn_alignbit(hi, vw[i], (uint32_t)sh);
+        a0[k] = lut_at(lv, __builtin_amdgcn_perm(x, lo, sel_byte(0)));
+        a1[k] = lut_at(lv, __builtin_amdgcn_perm(x, lo, sel_byte(3)));
+      }
+      acc[2 * g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, a0), pb,
+                                                          acc[2 * g], 0, 0, 0);
+      acc[2 * g + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, a1), pb,
+                                                              acc[2 * g + 1], 0, 0, 0);
+    }
   } else {
 #pragma unroll
     for (int m = 0; m < DG::VM; ++m) {
@@ -937,7 +962,7 @@ decode_kernel(DecArgs a) {
   if constexpr (VTab<BV>::QUAD)
     fill_pairs<VTab<BV>::ENTRIES, kWaves>(lut_v, a.lut_v_quad, a.lut_v_quad + 1, 2);
   else
-    fill_words<VTab<BV>::ENTRIES, kWaves>(lut_v, a.lut_v);
+    fill_words<VTab<BV>::ENTRIES, kWaves, VTab<BV>::SRC>(lut_v, a.lut_v);
   /* rotated queries: qbuf[u G + g][i] = (D q_g)_i of the block's unit u,
    * then FWHT, then scale */
   const uint8_t* sb = a.sign_bits + (int64_t)layer * (D / 8);
