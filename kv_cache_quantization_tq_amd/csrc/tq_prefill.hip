@@ -498,32 +498,42 @@ __global__ void __launch_bounds__(64 * waves_for(D)) prefill16_kernel(PreArgs a)
  *           accumulator is rescaled when E grows, like the softmax maximum.
  * The value tile's k index follows the score layout: in each 16-token step,
  * k = 8 h + j holds token 4 h + (j % 4) + 8 (j / 4), so the P' registers feed
- * the value product as they are. */
+ * the value product as they are.
+ *
+ * Coordinates live in the lanes the way the value product leaves them: lane
+ * (c, h) holds coordinates 32 m + 8 r + 4 h + i (r, i < 4) of column c.  The
+ * query is loaded in that layout and both rotations (q'' = H D q, o = D H o'')
+ * run in registers: butterflies within the lane for coordinate bits 0, 1 and
+ * 3 and up, one exchange with lane l ^ 32 for bit 2.  The score product's k
+ * index is the same permutation of the coordinates (step s, k = 8 h + j:
+ * coordinate 32 (s / 2) + 8 (2 (s % 2) + j / 4) + 4 h + j % 4), so the key
+ * rows are stored in that order.  With no fp32 query or output rows in LDS,
+ * a block needs only its two tile buffers (~49 KB at d = 128): three blocks,
+ * three waves per SIMD, share a CU. */
 constexpr int kWaves32 = 4;
+constexpr float kLazy = 8.0f; /* base-2 slack of the softmax reference */
 
 template <int D, int BK, int BV>
 struct Geo32 {
+  static_assert(D == 64 || D == 128, "32 x 32 form: heads of 64 or 128 coordinates");
   static constexpr int RBK = D * BK / 8;
   static constexpr int SEG = D * BV / 16;
   static constexpr int TILE_V = 32 * D * BV / 8;
-  static constexpr int KP = D + 8;  /* key tile pitch (halfs) */
-  static constexpr int VP = 32 + 8; /* value tile pitch (halfs) */
-  static constexpr int OP = D + 4;  /* query / output row pitch (floats) */
   static constexpr int LK = 1 << BK, PWV = 1 << (2 * BV);
   static constexpr int ITEMS = 4 * D; /* 8-code items per tile, keys and values alike */
   static constexpr int PER = ITEMS / (64 * kWaves32);
-  static constexpr int QBYTES = kCols * OP * 4;
-  /* one tile: khi, klo [32][KP], vt [D][VP] (halfs), nk, nv [32], E */
-  static constexpr int TBYTES = 2 * 32 * KP * 2 + D * VP * 2 + 2 * 32 * 4 + 16;
-  static constexpr int UBYTES = QBYTES > 2 * TBYTES ? QBYTES : 2 * TBYTES;
-  static constexpr int BYTES = UBYTES + (LK + PWV) * 4;
+  static constexpr int KP = D + 8; /* key row pitch (halfs): rows 16 bytes apart in the banks */
+  /* one tile: khi, klo [32][KP], vt [4][D][8] (halfs: chunk k holds k-index
+   * 8 k..8 k+7 of every coordinate row), nk, nv [32], E */
+  static constexpr int TBYTES = 2 * 32 * KP * 2 + D * 32 * 2 + 2 * 32 * 4 + 16;
+  static constexpr int BYTES = 2 * TBYTES + (LK + PWV) * 4;
 };
 
-/* k index of tile token t within the value tile rows */
-__device__ inline int kpos32(int t) {
-  const int u = t & 15;
-  return (t & 16) + 8 * ((u >> 2) & 1) + (u & 3) + 4 * (u >> 3);
-}
+/* Bank spread of the LDS tiles (64 banks of 4 bytes; a 16-byte read serves
+ * 16 lanes per cycle, the 16 lanes of a half-wave reading rows 0..15 of one
+ * 16-byte chunk): key rows are padded by one chunk, and the value tile is
+ * stored chunk-major, so that those 16 reads are consecutive; the addresses
+ * of every step stay constant offsets from one register. */
 
 /* max over the lane pair (l, l ^ 32) */
 __device__ inline float pair_max(float v) {
@@ -535,20 +545,41 @@ __device__ inline float pair_sum(float v) {
   return __uint_as_float(a[0]) + __uint_as_float(a[1]);
 }
 
+/* Unnormalised Walsh-Hadamard transform of one column held by a lane pair:
+ * x[16 m + 4 r + i] is coordinate 32 m + 8 r + 4 h + i, h = lane / 32. */
+template <int N>
+__device__ inline void pair_fwht(float (&x)[N], int hh) {
+#pragma unroll
+  for (int b = 1; b < N; b <<= 1)
+#pragma unroll
+    for (int k = 0; k < N; ++k)
+      if (!(k & b)) {
+        const float u = x[k], w = x[k | b];
+        x[k] = u + w;
+        x[k | b] = u - w;
+      }
+  /* coordinate bit 2: lane l < 32 holds the first of each pair */
+  const float sg = hh ? -1.0f : 1.0f;
+#pragma unroll
+  for (int k = 0; k < N; ++k) {
+    auto p = __builtin_amdgcn_permlane32_swap(__float_as_uint(x[k]), __float_as_uint(x[k]), false, false);
+    x[k] = __builtin_fmaf(sg, __uint_as_float(p[1]), __uint_as_float(p[0]));
+  }
+}
+
 template <int D, int BK, int BV, bool PAGED>
 __global__ void __launch_bounds__(64 * kWaves32) prefill32_kernel(PreArgs a) {
   using PG = Geo32<D, BK, BV>;
-  constexpr int KS = D / 16, VM = D / 32;
+  constexpr int KS = D / 16, VM = D / 32, NX = D / 2;
   __shared__ __align__(16) char smem[PG::BYTES];
-  float* qbuf = (float*)smem; /* [kCols][OP] */
   auto khi_of = [&](int u) { return (_Float16*)(smem + u * PG::TBYTES); };
   auto klo_of = [&](int u) { return khi_of(u) + 32 * PG::KP; };
   auto vt_of = [&](int u) { return khi_of(u) + 64 * PG::KP; };
-  auto nk_of = [&](int u) { return (float*)(vt_of(u) + D * PG::VP); };
+  auto nk_of = [&](int u) { return (float*)(vt_of(u) + D * 32); };
   auto nv_of = [&](int u) { return nk_of(u) + 32; };
   auto ev_of = [&](int u) { return (int*)(nk_of(u) + 64); };
-  uint32_t* tk = (uint32_t*)(smem + PG::UBYTES); /* per code: hi | lo << 16 */
-  uint32_t* tv = tk + PG::LK;                    /* per pair of codes: two fp16 levels */
+  uint32_t* tk = (uint32_t*)(smem + 2 * PG::TBYTES); /* per code: hi | lo << 16 */
+  uint32_t* tv = tk + PG::LK;                        /* per pair of codes: two fp16 levels */
 
   const int tid = threadIdx.x, lane = tid % 64;
   const int wave = __builtin_amdgcn_readfirstlane(tid / 64);
@@ -567,39 +598,43 @@ __global__ void __launch_bounds__(64 * kWaves32) prefill32_kernel(PreArgs a) {
   for (int i = tid; i < PG::LK; i += blockDim.x) tk[i] = a.lut_k1[i];
   for (int i = tid; i < PG::PWV; i += blockDim.x) tv[i] = a.lut_v[i];
 
-  /* queries: column c = head g * qc + query i; q'' = H D q, scaled */
+  /* the lane's column c = head g * qc + query i; padding columns (no such
+   * head or query) hold zeros and are not written */
+  const int c0 = 32 * wave;
+  const int col = c0 + cl;
+  const int cg = col / a.qc, ci = col % a.qc;
+  const bool real = cg < a.group && ci < qn;
+  const int64_t orow =
+      (((int64_t)layer * a.batch + b) * a.q_heads + (int64_t)kv * a.group + (real ? cg : 0)) * a.t_new +
+      q0 + (real ? ci : 0);
   const uint8_t* sb = a.sign_bits + (int64_t)layer * (D / 8);
-  for (int t = tid; t < kCols * D; t += blockDim.x) {
-    const int c = t / D, i = t % D;
-    const int g = c / a.qc, qi = c % a.qc;
-    float v = 0.0f;
-    if (g < a.group && qi < qn) {
-      const int64_t row = (((int64_t)layer * a.batch + b) * a.q_heads + (int64_t)kv * a.group + g) *
-                              a.t_new + q0 + qi;
-      v = h2f(a.q[row * D + i]);
-      v = ((sb[i >> 3] >> (i & 7)) & 1) ? -v : v;
-    }
-    qbuf[c * PG::OP + i] = v;
-  }
-  __syncthreads();
-  const int c0 = 32 * wave; /* the wave's columns */
-  for (int r = 0; r < 32; ++r) {
-    float* row = qbuf + (c0 + r) * PG::OP;
-    const Row<D> t = row_fwht<D>(row, lane);
-#pragma unroll
-    for (int j = 0; j < D / 64; ++j) row[lane + 64 * j] = t.v[j] * a.qscale;
-  }
-  __syncthreads();
-  /* B operands: lane (cl, hh) holds coordinates 16 s + 8 hh + 0..7 of column
-   * c0 + cl, as fp16 part and fp16 remainder */
+
+  /* q'' = H D q, scaled, split into the B operands: lane (cl, hh) of step s
+   * holds coordinates 32 (s / 2) + 8 (2 (s % 2) + j / 4) + 4 hh + j % 4 */
   half8 qh[KS], ql[KS];
   {
-    const float* row = qbuf + (c0 + cl) * PG::OP;
+    float x[NX];
+    const uint16_t* qr = a.q + orow * D + 4 * hh;
+#pragma unroll
+    for (int m = 0; m < VM; ++m)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        uint2 w = make_uint2(0u, 0u);
+        if (real) w = *(const uint2*)(qr + 32 * m + 8 * r);
+        const uint32_t sgn = __builtin_amdgcn_readfirstlane((uint32_t)sb[4 * m + r]) >> (4 * hh);
+        const uint32_t h4[4] = {w.x & 0xffffu, w.x >> 16, w.y & 0xffffu, w.y >> 16};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float v = h2f(h4[i]);
+          x[16 * m + 4 * r + i] = ((sgn >> i) & 1) ? -v : v;
+        }
+      }
+    pair_fwht(x, hh);
 #pragma unroll
     for (int s = 0; s < KS; ++s)
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const float v = row[16 * s + 8 * hh + j];
+        const float v = x[16 * (s >> 1) + 8 * (s & 1) + j] * a.qscale;
         const _Float16 h = (_Float16)v;
         qh[s][j] = h;
         ql[s][j] = (_Float16)(v - (float)h);
@@ -608,15 +643,13 @@ __global__ void __launch_bounds__(64 * kWaves32) prefill32_kernel(PreArgs a) {
   /* causal limit of the lane's column (tokens < lim are attended) */
   int lim;
   {
-    const int col = c0 + cl;
-    const int cg = col / a.qc, ci = col % a.qc;
     const int64_t l = (int64_t)p0 + q0 + ci + 1;
-    lim = (cg < a.group && ci < qn) ? (int)(l > a.capacity ? a.capacity : l) : 1;
+    lim = real ? (int)(l > a.capacity ? a.capacity : l) : 1;
   }
   const int64_t blk_end = (int64_t)p0 + q0 + qn;
   const int blk_lim = (int)(blk_end > a.capacity ? a.capacity : blk_end);
   const int ntiles = (blk_lim + 31) / 32;
-  __syncthreads(); /* qbuf is dead: the tiles take its place */
+  __syncthreads(); /* the code tables are in place */
 
   const int64_t sh = PAGED ? 0 : (int64_t)b * a.kv_heads + kv;
   const int64_t srows = PAGED ? (int64_t)a.num_pages * a.kv_heads * (32 << a.lg_tpp) : a.capacity;
@@ -668,25 +701,33 @@ __global__ void __launch_bounds__(64 * kWaves32) prefill32_kernel(PreArgs a) {
       uint32_t e[8];
 #pragma unroll
       for (int p = 0; p < 8; ++p) e[p] = tk[(kraw[w] >> (BK * p)) & (PG::LK - 1)];
-      u32x4 hv, lv;
+      uint32_t hv[4], lv[4];
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
         hv[p] = __builtin_amdgcn_perm(e[2 * p + 1], e[2 * p], 0x05040100u);
         lv[p] = __builtin_amdgcn_perm(e[2 * p + 1], e[2 * p], 0x07060302u);
       }
-      *(u32x4*)(khi + tok * PG::KP + 8 * grp) = hv;
-      *(u32x4*)(klo + tok * PG::KP + 8 * grp) = lv;
+      /* coordinates 8 grp + 0..3 and + 4..7 (m = grp / 4, r = grp % 4) go to
+       * row positions 32 m + 16 (r / 2) + 4 (r % 2) and 8 further on */
+      const int pos = 32 * (grp >> 2) + 16 * ((grp >> 1) & 1) + 4 * (grp & 1);
+      _Float16* kh = khi + tok * PG::KP + pos;
+      _Float16* kl = klo + tok * PG::KP + pos;
+      *(uint2*)kh = make_uint2(hv[0], hv[1]);
+      *(uint2*)(kh + 8) = make_uint2(hv[2], hv[3]);
+      *(uint2*)kl = make_uint2(lv[0], lv[1]);
+      *(uint2*)(kl + 8) = make_uint2(lv[2], lv[3]);
       /* value segment seg = 16 q + r, field m: coordinate r (d/16) + m of
        * tokens 8 q + 0..7; tokens 8 q + 0..3 and 8 q + 4..7 are runs of 4
-       * in the row's k order */
+       * in the row's k order (chunks 2 (q / 2) and 2 (q / 2) + 1, at 4 (q % 2)) */
       const int seg = it / (D / 16), m = it % (D / 16);
       const int qq = seg >> 4, rr = seg & 15;
-      _Float16* vrow = vt + (rr * (D / 16) + m) * PG::VP + 16 * (qq >> 1) + 4 * (qq & 1);
+      const int vrow = rr * (D / 16) + m;
+      _Float16* vr = vt + (2 * (qq >> 1) * D + vrow) * 8 + 4 * (qq & 1);
       uint32_t pv[4];
 #pragma unroll
       for (int p = 0; p < 4; ++p) pv[p] = tv[(vraw[w] >> (2 * BV * p)) & (PG::PWV - 1)];
-      *(uint2*)vrow = make_uint2(pv[0], pv[1]);
-      *(uint2*)(vrow + 8) = make_uint2(pv[2], pv[3]);
+      *(uint2*)vr = make_uint2(pv[0], pv[1]);
+      *(uint2*)(vr + 8 * D) = make_uint2(pv[2], pv[3]);
     }
     /* norms; the value norms scaled by 2^-E, E the running maximum of the
      * tiles' largest value-norm exponents */
@@ -747,56 +788,58 @@ __global__ void __launch_bounds__(64 * kWaves32) prefill32_kernel(PreArgs a) {
     spill(u ^ 1);
     fetch(t + 2 < ntiles ? t + 2 : ntiles - 1);
     /* S[r]: token 8 (r / 4) + 4 hh + r % 4 of the lane's column */
-    float nkv[16], nvv[16];
+    float mt = -INFINITY;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const float4 a4 = *(const float4*)(nk + 8 * q + 4 * hh);
-      const float4 b4 = *(const float4*)(nv + 8 * q + 4 * hh);
-      nkv[4 * q] = a4.x, nkv[4 * q + 1] = a4.y, nkv[4 * q + 2] = a4.z, nkv[4 * q + 3] = a4.w;
-      nvv[4 * q] = b4.x, nvv[4 * q + 1] = b4.y, nvv[4 * q + 2] = b4.z, nvv[4 * q + 3] = b4.w;
-    }
-    if (et > e_cur) {
-      /* uniform over the block: a larger value-norm scale */
-      const float f = __builtin_ldexpf(1.0f, e_cur - et);
+      const float n4[4] = {a4.x, a4.y, a4.z, a4.w};
 #pragma unroll
-      for (int m = 0; m < VM; ++m) acc[m] *= f;
-      e_cur = et;
+      for (int i = 0; i < 4; ++i) {
+        float v = S[4 * q + i] * n4[i];
+        if (EDGE && 32 * t + 8 * q + 4 * hh + i >= lim) v = -INFINITY;
+        S[4 * q + i] = v;
+        mt = fmaxf(mt, v);
+      }
     }
-    float sc[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float v = S[r] * nkv[r];
-      if (EDGE && 32 * t + 8 * (r >> 2) + 4 * hh + (r & 3) >= lim) v = -INFINITY;
-      sc[r] = v;
-    }
-    float mt = sc[0];
-#pragma unroll
-    for (int r = 1; r < 16; ++r) mt = fmaxf(mt, sc[r]);
     mt = pair_max(mt);
-    if (__any(mt > m_run)) {
-      const float mn = fmaxf(m_run, mt);
-      const float al = __builtin_amdgcn_exp2f(m_run - mn); /* 0 on the first tile */
+    /* One rescale for both running scales, and only when needed: the
+     * softmax reference m_run moves only when a column's maximum passes it
+     * by more than kLazy (so p = 2^(s - m_run) <= 2^kLazy: the products
+     * are the same up to the common factor, which l_run carries too), and
+     * E moves when a tile brings a larger value-norm exponent (uniform). */
+    const bool grow = mt > m_run + kLazy;
+    if (__any(grow) || et > e_cur) {
+      const float mn = grow ? mt : m_run;
+      float al = __builtin_amdgcn_exp2f(m_run - mn); /* 0 on the first tile */
       l_run *= al;
+      if (et > e_cur) al = __builtin_ldexpf(al, e_cur - et);
 #pragma unroll
       for (int m = 0; m < VM; ++m) acc[m] *= al;
       m_run = mn;
+      e_cur = et > e_cur ? et : e_cur;
     }
     half8 ph[2], pl[2];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float p = __builtin_amdgcn_exp2f(sc[r] - m_run);
-      l_run += p;
-      /* fp16(p m) and the fp16 of the exact remainder, one fma each */
-      const _Float16 h = (_Float16)__builtin_fmaf(p, nvv[r], 0.0f);
-      ph[r >> 3][r & 7] = h;
-      pl[r >> 3][r & 7] = (_Float16)__builtin_fmaf(p, nvv[r], -(float)h);
+    for (int q = 0; q < 4; ++q) {
+      const float4 b4 = *(const float4*)(nv + 8 * q + 4 * hh);
+      const float n4[4] = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 4 * q + i;
+        const float p = __builtin_amdgcn_exp2f(S[r] - m_run);
+        l_run += p;
+        /* fp16(p m) and the fp16 of the exact remainder, one fma each */
+        const _Float16 h = (_Float16)__builtin_fmaf(p, n4[i], 0.0f);
+        ph[r >> 3][r & 7] = h;
+        pl[r >> 3][r & 7] = (_Float16)__builtin_fmaf(p, n4[i], -(float)h);
+      }
     }
 #pragma unroll
     for (int m = 0; m < VM; ++m) {
-      const _Float16* vr = vt + (32 * m + cl) * PG::VP + 8 * hh;
+      const _Float16* vr = vt + (hh * D + 32 * m + cl) * 8;
 #pragma unroll
       for (int k = 0; k < 2; ++k) {
-        const half8 av = *(const half8*)(vr + 16 * k);
+        const half8 av = *(const half8*)(vr + 16 * k * D);
         acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, ph[k], acc[m], 0, 0, 0);
         acc[m] = __builtin_amdgcn_mfma_f32_32x32x16_f16(av, pl[k], acc[m], 0, 0, 0);
       }
@@ -807,33 +850,30 @@ __global__ void __launch_bounds__(64 * kWaves32) prefill32_kernel(PreArgs a) {
   for (; t < t_edge; ++t) step(t, std::false_type{});
   for (; t < ntiles; ++t) step(t, std::true_type{});
 
-  /* o'' = acc 2^E / l into LDS rows, then o = D H o'' per row */
-  float* obuf = qbuf;
+  /* o = D H (acc 2^E / l), the lane's coordinates written as runs of 4 */
   {
     const float inv = __builtin_ldexpf(a.oscale, e_cur) / pair_sum(l_run);
-    float* orow = obuf + (c0 + cl) * PG::OP;
+    float x[NX];
 #pragma unroll
     for (int m = 0; m < VM; ++m)
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        *(float4*)(orow + 32 * m + 8 * q + 4 * hh) =
-            make_float4(acc[m][4 * q] * inv, acc[m][4 * q + 1] * inv, acc[m][4 * q + 2] * inv,
-                        acc[m][4 * q + 3] * inv);
-  }
-  __syncthreads();
-  for (int r = 0; r < 32; ++r) {
-    const int c = c0 + r;
-    const int g = c / a.qc, qi = c % a.qc;
-    const Row<D> t = row_fwht<D>(obuf + c * PG::OP, lane);
-    if (g < a.group && qi < qn) {
-      const int64_t row = (((int64_t)layer * a.batch + b) * a.q_heads + (int64_t)kv * a.group + g) *
-                              a.t_new + q0 + qi;
+      for (int r = 0; r < 16; ++r) x[16 * m + r] = acc[m][r] * inv;
+    pair_fwht(x, hh);
+    if (real) {
+      float* orp = a.out + orow * D + 4 * hh;
 #pragma unroll
-      for (int j = 0; j < D / 64; ++j) {
-        const int i = lane + 64 * j;
-        const float v = t.v[j];
-        a.out[row * D + i] = ((sb[i >> 3] >> (i & 7)) & 1) ? -v : v;
-      }
+      for (int m = 0; m < VM; ++m)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const uint32_t sgn = __builtin_amdgcn_readfirstlane((uint32_t)sb[4 * m + r]) >> (4 * hh);
+          float o4[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float v = x[16 * m + 4 * r + i];
+            o4[i] = ((sgn >> i) & 1) ? -v : v;
+          }
+          *(float4*)(orp + 32 * m + 8 * r) = make_float4(o4[0], o4[1], o4[2], o4[3]);
+        }
     }
   }
 }
