@@ -89,6 +89,20 @@ __device__ inline float rows_sum(float v) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+/* max over all 64 lanes on the VALU: within each 16-lane row by DPP (quad
+ * swaps, then rotations by 4 and 8), then across the rows */
+template <int CTRL>
+__device__ inline float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ inline float wave_max(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));  /* quad_perm [1, 0, 3, 2] */
+  v = fmaxf(v, dpp_f<0x4E>(v));  /* quad_perm [2, 3, 0, 1] */
+  v = fmaxf(v, dpp_f<0x124>(v)); /* row_ror:4 */
+  v = fmaxf(v, dpp_f<0x128>(v)); /* row_ror:8 */
+  return rows_max(v);
+}
+
 __device__ inline __amdgpu_buffer_rsrc_t make_stream(const uint8_t* base, int64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, 0x00020000);
 }
@@ -670,8 +684,14 @@ __global__ void __launch_bounds__(64 * kWaves32) prefill32_kernel(PreArgs a) {
     }
   };
 
-  /* raw codes of one tile: PER key items and PER value items per thread;
-   * threads 0..31 load the key norms, 32..63 the value norms */
+  /* raw codes of one tile: PER key items and PER value items per thread
+   * (with two value items, the pair q = 2 j, 2 j + 1 of one coordinate row,
+   * so that the thread's stores fill whole 16-byte chunks); lanes 0..31 of
+   * wave 0 load the key norms, of wave 1 the value norms */
+  constexpr bool VPAIR = PG::PER == 2;
+  auto vitem = [&](int u) {
+    return VPAIR ? (tid & 127) + 256 * (tid >> 7) + 128 * u : tid + u * 64 * kWaves32;
+  };
   uint32_t kraw[PG::PER], vraw[PG::PER], nraw = 0;
   auto fetch = [&](int t) {
     const int32_t r0 = tile_rows(t);
@@ -680,15 +700,16 @@ __global__ void __launch_bounds__(64 * kWaves32) prefill32_kernel(PreArgs a) {
       const int it = tid + u * 64 * kWaves32;
       const int tok = it / (D / 8), grp = it % (D / 8);
       kraw[u] = load_codes8<BK>(rk, (r0 + tok) * PG::RBK + grp * BK);
-      const int seg = it / (D / 16), m = it % (D / 16);
+      const int iv = vitem(u);
+      const int seg = iv / (D / 16), m = iv % (D / 16);
       vraw[u] = load_codes8<BV>(rv, (r0 / 32) * PG::TILE_V + seg * PG::SEG + m * BV);
     }
-    if (tid < 32)
-      nraw = __builtin_amdgcn_raw_buffer_load_b16(rkn, (uint32_t)(r0 + tid) * 2u, 0, 0);
-    else if (tid < 64)
-      nraw = __builtin_amdgcn_raw_buffer_load_b16(rvn, (uint32_t)(r0 + tid - 32) * 2u, 0, 0);
+    if (lane < 32) {
+      if (wave == 0) nraw = __builtin_amdgcn_raw_buffer_load_b16(rkn, (uint32_t)(r0 + lane) * 2u, 0, 0);
+      else if (wave == 1) nraw = __builtin_amdgcn_raw_buffer_load_b16(rvn, (uint32_t)(r0 + lane) * 2u, 0, 0);
+    }
   };
-  /* running value-norm exponent (meaningful in threads 32..63) */
+  /* running value-norm exponent (meaningful in wave 1) */
   int e_run = -25;
   auto spill = [&](int u) {
     _Float16* khi = khi_of(u);
@@ -716,31 +737,45 @@ __global__ void __launch_bounds__(64 * kWaves32) prefill32_kernel(PreArgs a) {
       *(uint2*)(kh + 8) = make_uint2(hv[2], hv[3]);
       *(uint2*)kl = make_uint2(lv[0], lv[1]);
       *(uint2*)(kl + 8) = make_uint2(lv[2], lv[3]);
-      /* value segment seg = 16 q + r, field m: coordinate r (d/16) + m of
-       * tokens 8 q + 0..7; tokens 8 q + 0..3 and 8 q + 4..7 are runs of 4
-       * in the row's k order (chunks 2 (q / 2) and 2 (q / 2) + 1, at 4 (q % 2)) */
-      const int seg = it / (D / 16), m = it % (D / 16);
-      const int qq = seg >> 4, rr = seg & 15;
-      const int vrow = rr * (D / 16) + m;
-      _Float16* vr = vt + (2 * (qq >> 1) * D + vrow) * 8 + 4 * (qq & 1);
-      uint32_t pv[4];
+    }
+    /* value segment seg = 16 q + r, field m: coordinate r (d/16) + m of
+     * tokens 8 q + 0..7; tokens 8 q + 0..3 and 8 q + 4..7 are runs of 4 in
+     * the row's k order (chunks 2 (q / 2) and 2 (q / 2) + 1, at 4 (q % 2)) */
+    uint32_t pv[PG::PER][4];
 #pragma unroll
-      for (int p = 0; p < 4; ++p) pv[p] = tv[(vraw[w] >> (2 * BV * p)) & (PG::PWV - 1)];
-      *(uint2*)vr = make_uint2(pv[0], pv[1]);
-      *(uint2*)(vr + 8 * D) = make_uint2(pv[2], pv[3]);
+    for (int w = 0; w < PG::PER; ++w)
+#pragma unroll
+      for (int p = 0; p < 4; ++p) pv[w][p] = tv[(vraw[w] >> (2 * BV * p)) & (PG::PWV - 1)];
+    if constexpr (VPAIR) {
+      const int iv = vitem(0);
+      const int seg = iv / (D / 16), m = iv % (D / 16);
+      const int vrow = (seg & 15) * (D / 16) + m;
+      _Float16* vr = vt + (2 * (seg >> 5) * D + vrow) * 8;
+      *(u32x4*)vr = u32x4{pv[0][0], pv[0][1], pv[1][0], pv[1][1]};
+      *(u32x4*)(vr + 8 * D) = u32x4{pv[0][2], pv[0][3], pv[1][2], pv[1][3]};
+    } else {
+#pragma unroll
+      for (int w = 0; w < PG::PER; ++w) {
+        const int iv = vitem(w);
+        const int seg = iv / (D / 16), m = iv % (D / 16);
+        const int qq = seg >> 4, rr = seg & 15;
+        const int vrow = rr * (D / 16) + m;
+        _Float16* vr = vt + (2 * (qq >> 1) * D + vrow) * 8 + 4 * (qq & 1);
+        *(uint2*)vr = make_uint2(pv[w][0], pv[w][1]);
+        *(uint2*)(vr + 8 * D) = make_uint2(pv[w][2], pv[w][3]);
+      }
     }
     /* norms; the value norms scaled by 2^-E, E the running maximum of the
      * tiles' largest value-norm exponents */
     if (wave == 0) {
-      const float nf = h2f(nraw);
-      float mx = tid >= 32 ? nf : 0.0f;
-#pragma unroll
-      for (int o = 1; o < 32; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 32));
+      if (lane < 32) nk_of(u)[lane] = h2f(nraw) * a.kscale;
+    } else if (wave == 1) {
+      const float nf = h2f(nraw); /* 0 in lanes 32..63 */
+      const float mx = wave_max(nf);
       const int et = ((int)(__float_as_uint(mx) >> 23) & 255) - 127;
       e_run = et > e_run ? et : e_run;
-      if (tid < 32) nk_of(u)[tid] = nf * a.kscale;
-      else nv_of(u)[tid - 32] = __builtin_ldexpf(nf, -e_run);
-      if (tid == 32) *ev_of(u) = e_run;
+      if (lane < 32) nv_of(u)[lane] = __builtin_ldexpf(nf, -e_run);
+      if (lane == 0) *ev_of(u) = e_run;
     }
   };
 
