@@ -18,7 +18,23 @@ pytestmark = pytest.mark.gpu
 SEED = 1003
 
 
-def _case(torch, d, bk, bv, G, H, pos, t_new, Lyr=1, paged_tokens=None, seed=SEED):
+def _grow_exps(n, grow):
+    """Per-token power-of-two scale exponents of K and V (zero unless grow):
+    keys double every 20 tokens, values every 48 (outputs stay in the range
+    the absolute max-abs bar is meant for)."""
+    t = np.arange(n)
+    return (t // 20, t // 48) if grow else (0 * t, 0 * t)
+
+
+def _scaled(h16, e):
+    """fp16 bits times 2^e per row (exact: no value leaves the normal range)."""
+    x = h16.view(np.float16).astype(np.float32) * np.exp2(e)[:, None].astype(np.float32)
+    y = x.astype(np.float16)
+    assert np.all(np.isfinite(y)) and np.array_equal(y.astype(np.float32), x)
+    return y.view(np.uint16)
+
+
+def _case(torch, d, bk, bv, G, H, pos, t_new, Lyr=1, paged_tokens=None, seed=SEED, grow=False):
     B = len(pos)
     T = max(pos) + t_new
     cap = ((T + 31) // 32) * 32
@@ -39,6 +55,11 @@ def _case(torch, d, bk, bv, G, H, pos, t_new, Lyr=1, paged_tokens=None, seed=SEE
         v = torch.empty_like(k)
         synth.kv_dev(seed, 0, l, k[0])
         synth.kv_dev(seed, 1, l, v[0])
+        if grow:
+            ke, ve = _grow_exps(T, True)
+            for x, e in ((k, ke), (v, ve)):
+                sc = torch.from_numpy(np.exp2(e).astype(np.float16)).cuda()
+                x.view(torch.float16).mul_(sc[:, None])
         tq.append(cache, cbk, cbv, sbd[l:l + 1], k, v,
                   torch.zeros(B, dtype=torch.int32, device="cuda"), host_max_pos=0, layer0=l,
                   n_layers=1)
@@ -55,7 +76,7 @@ def _case(torch, d, bk, bv, G, H, pos, t_new, Lyr=1, paged_tokens=None, seed=SEE
     torch.cuda.synchronize()
     return dict(cache=cache, sbs=sbs, sbd=sbd, cbk=cbk, cbv=cbv, q16=q16, qd=qd, posd=posd,
                 out=out.cpu().numpy(), Lyr=Lyr, B=B, H=H, G=G, d=d, bk=bk, bv=bv, pos=pos,
-                t_new=t_new, seed=seed)
+                t_new=t_new, seed=seed, grow=grow)
 
 
 def _oracle(c, what=""):
@@ -70,6 +91,9 @@ def _oracle(c, what=""):
                 n_all = p + t_new
                 k = synth.kv_host(c["seed"], 0, l, b, h, d, 0, n_all)
                 v = synth.kv_host(c["seed"], 1, l, b, h, d, 0, n_all)
+                if c["grow"]:
+                    ke, ve = _grow_exps(n_all, True)
+                    k, v = _scaled(k, ke), _scaled(v, ve)
                 sl = slice(h * G, (h + 1) * G)
                 st = oracle_stream(k, v, c["bk"], c["bv"], c["sbs"][l],
                                    gpu_stream(c["cache"], l, b, h, n_all), f"{what} {l},{b},{h}")
@@ -104,6 +128,21 @@ def test_prefill_paged(P):
     c = _case(torch, 128, 4, 2, 4, 2, [0, 300], 77, 2, paged_tokens=P)
     ref, n_alt = _oracle(c, f"prefill paged P={P}")
     check_attention(c["out"], ref, f"prefill paged P={P}", n_alt)
+
+
+@pytest.mark.parametrize("d,bk,bv,G,pos,t_new", [
+    (128, 4, 2, 4, [0, 40], 100),
+    (64, 3, 3, 8, [5], 90),
+])
+def test_prefill_growing_scales(d, bk, bv, G, pos, t_new):
+    """Key and value scales that double every 20 and 48 tokens: each column's
+    running softmax reference moves many times, by more than the rescale
+    threshold within a tile too, and the block's value-norm exponent moves."""
+    torch = require_gpu()
+    c = _case(torch, d, bk, bv, G, 1, pos, t_new, grow=True)
+    what = f"prefill growing scales d={d}"
+    ref, n_alt = _oracle(c, what)
+    check_attention(c["out"], ref, what, n_alt)
 
 
 def test_prefill_row_equals_decode():
