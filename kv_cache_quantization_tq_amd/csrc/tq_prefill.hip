@@ -522,8 +522,9 @@ __global__ void __launch_bounds__(64 * waves_for(D)) prefill16_kernel(PreArgs a)
  * index is the same permutation of the coordinates (step s, k = 8 h + j:
  * coordinate 32 (s / 2) + 8 (2 (s % 2) + j / 4) + 4 h + j % 4), so the key
  * rows are stored in that order.  With no fp32 query or output rows in LDS,
- * a block needs only its two tile buffers (~49 KB at d = 128): three blocks,
- * three waves per SIMD, share a CU. */
+ * a block needs only its two tile buffers and the code tables (~51 KB at
+ * d = 128); the registers (the accumulators and the query's two fp16 parts
+ * alone take 128) hold the kernel at two waves per SIMD. */
 constexpr int kWaves32 = 4;
 constexpr float kLazy = 8.0f; /* base-2 slack of the softmax reference */
 
