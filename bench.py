@@ -589,7 +589,7 @@ def workload_prefill(args):
             "prefill-attn TFLOP/s (4 d flops per causal query-key pair)", tfs, "TFLOP/s", True,
             {"dtype": "f32 (f16 matrix-core operands; packed 4-bit K, 2-bit V)",
              "prefill_ms": ms, "tokens_per_s": Tp * B / (ms * 1e-3),
-             "roofline": {"bound": "mfma", "kernel": "prefill_kernel<128,4,2>", "achieved": tfs,
+             "roofline": {"bound": "mfma", "kernel": "prefill32_kernel<128,4,2>", "achieved": tfs,
                           "peak": 2500.0, "unit": "TFLOP/s", "frac": tfs / 2500.0,
                           "traffic": None}},
             args, ms)
