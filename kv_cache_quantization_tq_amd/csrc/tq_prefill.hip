@@ -687,8 +687,8 @@ __global__ void __launch_bounds__(64 * kWaves32) prefill32_kernel(PreArgs a) {
 
   /* raw codes of one tile: PER key items and PER value items per thread
    * (with two value items, the pair q = 2 j, 2 j + 1 of one coordinate row,
-   * so that the thread's stores fill whole 16-byte chunks); lanes 0..31 of
-   * wave 0 load the key norms, of wave 1 the value norms */
+   * so that the thread's stores fill whole 16-byte chunks); threads 0..31
+   * load the key norms, 32..63 the value norms */
   constexpr bool VPAIR = PG::PER == 2;
   auto vitem = [&](int u) {
     return VPAIR ? (tid & 127) + 256 * (tid >> 7) + 128 * u : tid + u * 64 * kWaves32;
@@ -705,12 +705,12 @@ __global__ void __launch_bounds__(64 * kWaves32) prefill32_kernel(PreArgs a) {
       const int seg = iv / (D / 16), m = iv % (D / 16);
       vraw[u] = load_codes8<BV>(rv, (r0 / 32) * PG::TILE_V + seg * PG::SEG + m * BV);
     }
-    if (lane < 32) {
-      if (wave == 0) nraw = __builtin_amdgcn_raw_buffer_load_b16(rkn, (uint32_t)(r0 + lane) * 2u, 0, 0);
-      else if (wave == 1) nraw = __builtin_amdgcn_raw_buffer_load_b16(rvn, (uint32_t)(r0 + lane) * 2u, 0, 0);
-    }
+    if (tid < 32)
+      nraw = __builtin_amdgcn_raw_buffer_load_b16(rkn, (uint32_t)(r0 + tid) * 2u, 0, 0);
+    else if (tid < 64)
+      nraw = __builtin_amdgcn_raw_buffer_load_b16(rvn, (uint32_t)(r0 + tid - 32) * 2u, 0, 0);
   };
-  /* running value-norm exponent (meaningful in wave 1) */
+  /* running value-norm exponent (meaningful in wave 0) */
   int e_run = -25;
   auto spill = [&](int u) {
     _Float16* khi = khi_of(u);
@@ -769,14 +769,13 @@ __global__ void __launch_bounds__(64 * kWaves32) prefill32_kernel(PreArgs a) {
     /* norms; the value norms scaled by 2^-E, E the running maximum of the
      * tiles' largest value-norm exponents */
     if (wave == 0) {
-      if (lane < 32) nk_of(u)[lane] = h2f(nraw) * a.kscale;
-    } else if (wave == 1) {
-      const float nf = h2f(nraw); /* 0 in lanes 32..63 */
-      const float mx = wave_max(nf);
+      const float nf = h2f(nraw);
+      const float mx = wave_max(tid >= 32 ? nf : 0.0f);
       const int et = ((int)(__float_as_uint(mx) >> 23) & 255) - 127;
       e_run = et > e_run ? et : e_run;
-      if (lane < 32) nv_of(u)[lane] = __builtin_ldexpf(nf, -e_run);
-      if (lane == 0) *ev_of(u) = e_run;
+      if (tid < 32) nk_of(u)[tid] = nf * a.kscale;
+      else nv_of(u)[tid - 32] = __builtin_ldexpf(nf, -e_run);
+      if (tid == 32) *ev_of(u) = e_run;
     }
   };
 

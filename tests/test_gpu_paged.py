@@ -76,6 +76,25 @@ def test_paged_equals_contiguous(d, bk, bv, P):
     torch.cuda.synchronize()
     rel, mx = attention_errors(outs[1].cpu().numpy(), outs[0].cpu().numpy())
     assert rel <= 1e-6 and mx <= 1e-5, (rel, mx)
+    # prefill: the last 37 tokens of each sequence as new queries; the same
+    # kernel runs on both layouts (only the row addressing differs), so the
+    # outputs must be bit-identical
+    t_new = 37
+    pp = torch.tensor([lens[b] - t_new for b in range(B)], dtype=torch.int32, device="cuda")
+    qp = torch.empty((L, B, H * G, t_new, d), dtype=torch.int16, device="cuda")
+    qs = torch.empty((B, H * G, d), dtype=torch.int16, device="cuda")
+    for l in range(L):
+        for i in range(t_new):
+            synth.q_dev(SEED, 100 + i, l, qs)
+            qp[l, :, :, i] = qs
+    pouts = []
+    for c in (cont, paged):
+        o = torch.empty((L, B, H * G, t_new, d), dtype=torch.float32, device="cuda")
+        tq.prefill(c, cbk, cbv, sbd, qp, pp, o)
+        pouts.append(o)
+    torch.cuda.synchronize()
+    assert torch.isfinite(pouts[0]).all()
+    assert torch.equal(pouts[0], pouts[1]), float((pouts[0] - pouts[1]).abs().max())
     q16 = q.cpu().numpy().view(np.uint16)
     got, ref, n_alt, n_coords = [], [], 0, 0
     what = f"paged d={d} P={P}"

@@ -113,6 +113,10 @@ def _oracle(c, what=""):
     (256, 2, 4, 1, 2, [1000], 130, 1),
     (128, 4, 3, 3, 2, [33], 50, 1),
     (128, 3, 2, 2, 1, [62, 0, 17], 33, 1),
+    # one new query; a chunk whose first query is the last token of a tile
+    (128, 4, 2, 4, 1, [40, 0], 1, 1),
+    (128, 2, 4, 4, 1, [31, 63], 2, 1),
+    (64, 4, 2, 2, 2, [95], 70, 1),
 ])
 def test_prefill_parity(d, bk, bv, G, H, pos, t_new, Lyr):
     torch = require_gpu()
@@ -122,12 +126,16 @@ def test_prefill_parity(d, bk, bv, G, H, pos, t_new, Lyr):
     check_attention(c["out"], ref, what, n_alt)
 
 
-@pytest.mark.parametrize("P", [32, 128])
-def test_prefill_paged(P):
+@pytest.mark.parametrize("P,d", [(32, 128), (128, 128), (64, 64)])
+def test_prefill_paged(P, d):
+    """Shuffled pages: the oracle's bars, and bit for bit the contiguous
+    cache's output (the kernels differ only in row addressing)."""
     torch = require_gpu()
-    c = _case(torch, 128, 4, 2, 4, 2, [0, 300], 77, 2, paged_tokens=P)
-    ref, n_alt = _oracle(c, f"prefill paged P={P}")
-    check_attention(c["out"], ref, f"prefill paged P={P}", n_alt)
+    c = _case(torch, d, 4, 2, 4, 2, [0, 300], 77, 2, paged_tokens=P)
+    ref, n_alt = _oracle(c, f"prefill paged P={P} d={d}")
+    check_attention(c["out"], ref, f"prefill paged P={P} d={d}", n_alt)
+    cc = _case(torch, d, 4, 2, 4, 2, [0, 300], 77, 2)
+    assert np.array_equal(c["out"], cc["out"]), float(np.abs(c["out"] - cc["out"]).max())
 
 
 @pytest.mark.parametrize("d,bk,bv,G,pos,t_new", [
