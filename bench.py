@@ -500,7 +500,10 @@ def workload_paged_llama8b(args):
 def workload_sparse_v(args):
     """The 32K decode (32 layers, 32 query / 8 KV heads, d 128, K4/V2) with the
     Sparse V gate at thresholds 1e-6, 1e-4 and 1e-3 against the dense decode
-    on the same cache; reports the tiles skipped and the time of each."""
+    on the same cache; reports the tiles skipped and the time of each.  Each
+    threshold (and the dense decode) gets at least 20 warm-up launches and 20
+    timed ones: after a change of kernel the launch times drift for about ten
+    launches (~1.5 ms, the clock settling to the new load) before they hold."""
     import numpy as np
     import torch
     import kv_cache_quantization_tq_amd as tq
@@ -523,8 +526,9 @@ def workload_sparse_v(args):
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    steps, warmup = max(args.steps, 20), max(args.warmup, 20)
     dense_ms = _timed(torch, lambda: tq.decode(cache, cbk, cbv, sbs, q, lens, T, out, ws),
-                      args.steps, args.warmup)
+                      steps, warmup)
     dec_bytes = L * B * HKV * T * per_token_head_bytes()
     tiles = L * B * HKV * (T // 32)
     v_tile_bytes = 32 * (D * BV // 8 + 2)
@@ -536,7 +540,7 @@ def workload_sparse_v(args):
         torch.cuda.synchronize()
         skipped = int(cnt.sum().item())
         ms = _timed(torch, lambda e=eps: tq.decode_sparse(cache, cbk, cbv, sbs, q, lens, T, out,
-                                                           e, ws), args.steps, args.warmup)
+                                                           e, ws), steps, warmup)
         key = f"eps_{eps:g}"
         res[key + "_us"] = ms * 1e3
         res[key + "_skipped_tile_frac"] = skipped / tiles
@@ -549,7 +553,7 @@ def workload_sparse_v(args):
             "decode-attn dense-equivalent GB/s (packed KV bytes a dense decode reads / time), "
             "Sparse V at eps 1e-3", dec_bytes / (best * 1e-3) / 1e9, "GB/s", True,
             dict(dtype="f32 (f16 matrix-core operands; packed 4-bit K, 2-bit V)", **res),
-            args, best)
+            argparse.Namespace(steps=steps, warmup=warmup), best)
 
 
 def workload_prefill(args):

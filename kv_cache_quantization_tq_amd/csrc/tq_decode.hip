@@ -737,8 +737,14 @@ __device__ inline void tile_step(const TileRegs<DG, CF>& r,
  * the freed ring slot, then accumulate tile t's values, and only then apply
  * the rescale that the scoring of t + W may have asked for (t's weights are
  * still at the old reference).  On entry ra holds tile (and rb tile + W
- * with a depth-3 ring); the rest of the ring is loaded here. */
-template <class DG, int BK, int BV, int CF, class PF>
+ * with a depth-3 ring); the rest of the ring is loaded here.
+ *
+ * A skipped tile's value load reads zeros (codes and norms), so its weights
+ * P' = p m are zero and its value products add nothing.  SKIPWORK false runs
+ * them anyway, with no branch around the accumulators (such a branch makes
+ * every kept tile copy them); SKIPWORK true branches around them, which pays
+ * off only when most tiles are skipped. */
+template <class DG, int BK, int BV, int CF, bool SKIPWORK, class PF>
 __device__ inline void sparse_tiles(const DecArgs& a, const TileAddr& ad, TileRegs<DG, CF>& ra,
                                     TileRegs<DG, CF>& rb, TileRegs<DG, CF>& rc, PF& pf,
                                     const half8 (&bq)[KTab<BK>::SPLIT ? 2 * DG::KS : DG::KS],
@@ -792,9 +798,8 @@ __device__ inline void sparse_tiles(const DecArgs& a, const TileAddr& ad, TileRe
       a.skip_tiles ? a.skip_tiles + (((int64_t)layer * a.batch + b) * a.kv_heads + kv) * a.skip_words
                    : nullptr;
   auto values = [&](TileRegs<DG, CF>& cur) {
-    if (keepc) {
-      value_part<DG, BV, CF>(pc, cur.vn, cur.vw, lv, lo, lo8, acc, n);
-    } else {
+    if (!SKIPWORK || keepc) value_part<DG, BV, CF>(pc, cur.vn, cur.vw, lv, lo, lo8, acc, n);
+    if (!keepc) {
       ++nskip;
       if (skip_map && lane == 0) atomicOr(skip_map + (tile >> 5), 1u << (tile & 31));
     }
@@ -859,7 +864,9 @@ __device__ inline void sparse_tiles(const DecArgs& a, const TileAddr& ad, TileRe
     atomicAdd(a.skip_counts + ((int64_t)layer * a.batch + b) * a.kv_heads + kv, nskip);
 }
 
-template <int D, int BK, int BV, int CF, bool PAGED, bool SPARSE, bool MULTI>
+/* SPARSE: 0 dense; 1 the Sparse V gate, skipped tiles still running their
+ * value products; 2 the gate, skipped tiles leaving them out */
+template <int D, int BK, int BV, int CF, bool PAGED, int SPARSE, bool MULTI>
 __global__ void __launch_bounds__(64 * waves_for(D, BK, BV))
 decode_kernel(DecArgs a) {
   using DG = DecGeo<D, BK, BV>;
@@ -1049,9 +1056,9 @@ decode_kernel(DecArgs a) {
    * about to be used. */
   if constexpr (SPARSE) {
     if (tile < full_end)
-      sparse_tiles<DG, BK, BV, CF>(a, ad, ra, rb, rc, pf, bq, lut_k_rd, lut_v, lo, lo8, lok, acc,
-                                   m_run, l_run, first, tile, full_end, len, q4, n, lane, mref,
-                                   layer, b, kv);
+      sparse_tiles<DG, BK, BV, CF, SPARSE == 2>(a, ad, ra, rb, rc, pf, bq, lut_k_rd, lut_v, lo,
+                                                lo8, lok, acc, m_run, l_run, first, tile,
+                                                full_end, len, q4, n, lane, mref, layer, b, kv);
   } else if (tile < full_end) {
     auto step = [&](const TileRegs<DG, CF>& r) {
       tile_step<DG, BK, BV, false, CF>(r, bq, lut_k_rd, lut_v, lo, lo8, lok, acc, m_run, l_run,
@@ -1239,22 +1246,27 @@ tq_status launch_decode_t(const DecArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)blocks), block(64 * waves_for(D, BK, BV));
 #define TQ_LAUNCH(CF, PG, SP, MU) \
   hipLaunchKernelGGL((decode_kernel<D, BK, BV, CF, PG, SP, MU>), grid, block, 0, s, a)
-  const bool sp = a.sparse_eps > 0.0f, mu = a.upb > 1;
+  /* Sparse V: from eps 1e-3 on, most tiles of a long context are skipped,
+   * and leaving out their value products is worth the branch (contiguous
+   * storage only; paged storage always runs them) */
+  const bool sp = a.sparse_eps > 0.0f, mu = a.upb > 1, skipwork = a.sparse_eps >= 1e-3f;
   if (a.block_table) {
     if (a.group <= 4) {
-      if (sp) TQ_LAUNCH(4, true, true, false); else TQ_LAUNCH(4, true, false, false);
+      if (sp) TQ_LAUNCH(4, true, 1, false); else TQ_LAUNCH(4, true, 0, false);
     } else {
-      if (sp) TQ_LAUNCH(2, true, true, false); else TQ_LAUNCH(2, true, false, false);
+      if (sp) TQ_LAUNCH(2, true, 1, false); else TQ_LAUNCH(2, true, 0, false);
     }
   } else {
     if (a.group <= 4) {
-      if (sp) TQ_LAUNCH(4, false, true, false);
-      else if (mu) TQ_LAUNCH(4, false, false, true);
-      else TQ_LAUNCH(4, false, false, false);
+      if (sp && skipwork) TQ_LAUNCH(4, false, 2, false);
+      else if (sp) TQ_LAUNCH(4, false, 1, false);
+      else if (mu) TQ_LAUNCH(4, false, 0, true);
+      else TQ_LAUNCH(4, false, 0, false);
     } else {
-      if (sp) TQ_LAUNCH(2, false, true, false);
-      else if (mu) TQ_LAUNCH(2, false, false, true);
-      else TQ_LAUNCH(2, false, false, false);
+      if (sp && skipwork) TQ_LAUNCH(2, false, 2, false);
+      else if (sp) TQ_LAUNCH(2, false, 1, false);
+      else if (mu) TQ_LAUNCH(2, false, 0, true);
+      else TQ_LAUNCH(2, false, 0, false);
     }
   }
 #undef TQ_LAUNCH
@@ -1272,7 +1284,7 @@ int concurrent_blocks_t() {
     int dev = 0, cus = 0, per = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, decode_kernel<D, BK, BV, 2, false, false, false>, 64 * waves_for(D, BK, BV),
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, decode_kernel<D, BK, BV, 2, false, 0, false>, 64 * waves_for(D, BK, BV),
                                                      0) != hipSuccess ||
         cus <= 0 || per <= 0) {
       (void)hipGetLastError();
