@@ -500,10 +500,13 @@ def workload_paged_llama8b(args):
 def workload_sparse_v(args):
     """The 32K decode (32 layers, 32 query / 8 KV heads, d 128, K4/V2) with the
     Sparse V gate at thresholds 1e-6, 1e-4 and 1e-3 against the dense decode
-    on the same cache; reports the tiles skipped and the time of each.  Each
-    threshold (and the dense decode) gets at least 20 warm-up launches and 20
-    timed ones: after a change of kernel the launch times drift for about ten
-    launches (~1.5 ms, the clock settling to the new load) before they hold."""
+    on the same cache; reports the tiles skipped and the time of each.  The
+    four are timed interleaved: in each round every one runs 5 launches
+    (order reversed every other round), and the reported time is the median
+    over the rounds of the per-launch mean.  Launch times drift by up to ~50%
+    over runs of a few milliseconds of back-to-back decodes (the clock
+    following the load), so timing the thresholds one after another would
+    compare different clock states."""
     import numpy as np
     import torch
     import kv_cache_quantization_tq_amd as tq
@@ -526,34 +529,50 @@ def workload_sparse_v(args):
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    steps, warmup = max(args.steps, 20), max(args.warmup, 20)
-    dense_ms = _timed(torch, lambda: tq.decode(cache, cbk, cbv, sbs, q, lens, T, out, ws),
-                      steps, warmup)
     dec_bytes = L * B * HKV * T * per_token_head_bytes()
     tiles = L * B * HKV * (T // 32)
     v_tile_bytes = 32 * (D * BV // 8 + 2)
-    res = {"dense_us": dense_ms * 1e3}
-    best = None
-    for eps in (1e-6, 1e-4, 1e-3):
+    thresholds = (1e-6, 1e-4, 1e-3)
+    skipped = {}
+    for eps in thresholds:
         cnt = torch.zeros((L, B, HKV), dtype=torch.int32, device="cuda")
         tq.decode_sparse(cache, cbk, cbv, sbs, q, lens, T, out, eps, ws, skip_counts=cnt)
         torch.cuda.synchronize()
-        skipped = int(cnt.sum().item())
-        ms = _timed(torch, lambda e=eps: tq.decode_sparse(cache, cbk, cbv, sbs, q, lens, T, out,
-                                                           e, ws), steps, warmup)
+        skipped[eps] = int(cnt.sum().item())
+    runs = [(0.0, lambda: tq.decode(cache, cbk, cbv, sbs, q, lens, T, out, ws))]
+    runs += [(eps, lambda e=eps: tq.decode_sparse(cache, cbk, cbv, sbs, q, lens, T, out, e, ws))
+             for eps in thresholds]
+    per, rounds = 5, max(args.steps, 10)
+    times = {eps: [] for eps, _ in runs}
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for r in range(args.warmup + rounds):
+        for eps, fn in (runs if r % 2 == 0 else runs[::-1]):
+            ev0.record()
+            for _ in range(per):
+                fn()
+            ev1.record()
+            torch.cuda.synchronize()
+            if r >= args.warmup:
+                times[eps].append(ev0.elapsed_time(ev1) / per)
+    med = {eps: float(np.median(t)) for eps, t in times.items()}
+    res = {"dense_us": med[0.0] * 1e3}
+    for eps in thresholds:
         key = f"eps_{eps:g}"
+        ms = med[eps]
         res[key + "_us"] = ms * 1e3
-        res[key + "_skipped_tile_frac"] = skipped / tiles
-        res[key + "_bytes_read_gbs"] = (dec_bytes - skipped * v_tile_bytes) / (ms * 1e-3) / 1e9
-        if eps == 1e-3:
-            best = ms
+        res[key + "_skipped_tile_frac"] = skipped[eps] / tiles
+        res[key + "_bytes_read_gbs"] = (dec_bytes - skipped[eps] * v_tile_bytes) / (ms * 1e-3) / 1e9
+        res[key + "_vs_dense"] = med[0.0] / ms
+    best = med[1e-3]
     _report({"workload": "llama3-8b-shaped 32K decode with the Sparse V gate", "layers": L,
              "q_heads": HQ, "kv_heads": HKV, "head_dim": D, "batch": B, "context": T,
              "bits_k": BK, "bits_v": BV, "eps": 1e-3},
             "decode-attn dense-equivalent GB/s (packed KV bytes a dense decode reads / time), "
             "Sparse V at eps 1e-3", dec_bytes / (best * 1e-3) / 1e9, "GB/s", True,
-            dict(dtype="f32 (f16 matrix-core operands; packed 4-bit K, 2-bit V)", **res),
-            argparse.Namespace(steps=steps, warmup=warmup), best)
+            dict(dtype="f32 (f16 matrix-core operands; packed 4-bit K, 2-bit V)",
+                 timing=f"interleaved: {rounds} rounds x {per} launches per threshold, medians",
+                 **res),
+            argparse.Namespace(steps=rounds, warmup=args.warmup), best)
 
 
 def workload_prefill(args):
