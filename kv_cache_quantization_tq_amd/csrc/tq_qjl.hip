@@ -62,6 +62,21 @@ __device__ inline float rows_sum(float v) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef float float2v __attribute__((ext_vector_type(2)));
+
+/* r0, r1 as fp16 pairs: hi = (fp16(r0), fp16(r1)) and lo = the fp16 of the
+ * exact fp32 remainders r - hi (one pair conversion each, and one
+ * mixed-precision fma per remainder: negone is -1 kept out of the
+ * compiler's sight, so that r + hi * negone stays an fma on the fp16 hi). */
+__device__ inline void split_pair(float r0, float r1, float negone, uint32_t& hw, uint32_t& lw) {
+  const half2v h = __builtin_convertvector((float2v){r0, r1}, half2v);
+  const float l0 = __builtin_fmaf((float)h[0], negone, r0);
+  const float l1 = __builtin_fmaf((float)h[1], negone, r1);
+  hw = __builtin_bit_cast(uint32_t, h);
+  lw = __builtin_bit_cast(uint32_t, __builtin_convertvector((float2v){l0, l1}, half2v));
+}
+
 /* S in LDS (rows padded against bank conflicts) for d <= 128; 256-dim heads
  * read it through the caches */
 template <int D>
@@ -144,9 +159,12 @@ __device__ inline void enc_project(const half8 (&rhi)[D / 32], const half8 (&rlo
       t = __builtin_amdgcn_mfma_f32_16x16x32_f16(sa, rhi[s], t, 0, 0, 0);
       t = __builtin_amdgcn_mfma_f32_16x16x32_f16(sa, rlo[s], t, 0, 0, 0);
     }
-    uint32_t nib = 0;
+    /* bit i = (t[i] >= 0): the complement of the sign bit (no sum here
+     * is -0: each starts from +0) */
+    uint32_t nib = __float_as_uint(t[0]) >> 31;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) nib |= (t[i] >= 0.0f ? 1u : 0u) << i;
+    for (int i = 1; i < 4; ++i) nib |= (__float_as_uint(t[i]) >> 31) << i;
+    nib ^= 0xFu;
     const auto p16 = __builtin_amdgcn_permlane16_swap(nib, nib, false, false);
     const uint32_t byte = p16[0] | (p16[1] << 4);
     const auto p32 = __builtin_amdgcn_permlane32_swap(byte, byte, false, false);
@@ -230,24 +248,23 @@ __device__ inline void enc_keys(const EncSlot<D, B>& r, const QjlEncArgs& a, con
         }
   /* residual in the rotated unit domain: y / (sqrt(d) ||x||) - c[code] */
   const float scale = ss > 0.0f ? 1.0f / (sqrtf((float)D) * sqrtf(ss)) : 0.0f;
-  float g2 = 0.0f;
+  float g2 = 0.0f, negone = -1.0f;
+  asm volatile("" : "+v"(negone));
   half8 rhi[KS], rlo[KS];
   const uint32_t cpy = (uint32_t)lane & 3u;
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
+    uint32_t hw[4], lw[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const float2 c = plev[((r.cw[s] >> (2 * B * u)) & ((1u << (2 * B)) - 1)) * 4 + cpy];
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int j = 2 * u + t;
-        const float rr = y[s][j] * scale - (t ? c.y : c.x);
-        g2 += rr * rr;
-        const _Float16 hi = (_Float16)rr;
-        rhi[s][j] = hi;
-        rlo[s][j] = (_Float16)(rr - (float)hi);
-      }
+      const float r0 = y[s][2 * u] * scale - c.x, r1 = y[s][2 * u + 1] * scale - c.y;
+      g2 += r0 * r0;
+      g2 += r1 * r1;
+      split_pair(r0, r1, negone, hw[u], lw[u]);
     }
+    rhi[s] = __builtin_bit_cast(half8, u32x4{hw[0], hw[1], hw[2], hw[3]});
+    rlo[s] = __builtin_bit_cast(half8, u32x4{lw[0], lw[1], lw[2], lw[3]});
   }
   g2 = rows_sum(g2);
   if (live && kq == 0) a.gamma[v] = f2h(sqrtf(g2));
@@ -318,32 +335,35 @@ __device__ inline void enc_keys_m(const EncSlotM<D, B>& r, const QjlEncArgs& a, 
                                   const uint32_t (&fm)[D / 32][4], int64_t v0, int lane, int n,
                                   int kq) {
   constexpr int KS = D / 32, NL = D / 4;
-  using SL = SLds<D>;
   const int64_t v = v0 + n;
   const bool live = v < a.n;
   /* D x as fp16 operands (an xor of the sign bits), squares for the norm */
   half8 xb[KS];
-  float ss = 0.0f;
+  float sq[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
     u32x4 w;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) w[k] = r.xw[s][k] ^ fm[s][k];
-    xb[s] = __builtin_bit_cast(half8, w);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const float f = (float)xb[s][j];
-      ss += f * f;
+    for (int k = 0; k < 4; ++k) {
+      /* (the word goes through a plain variable: a bit cast of a vector
+       * element compiled to a cast of element 0) */
+      const uint32_t wk = r.xw[s][k] ^ fm[s][k];
+      w[k] = wk;
+      /* the squares of the fp16 pair, one dot product into fp32 */
+      sq[k] = __builtin_amdgcn_fdot2(__builtin_bit_cast(half2v, wk), __builtin_bit_cast(half2v, wk),
+                                     sq[k], false);
     }
+    xb[s] = __builtin_bit_cast(half8, w);
   }
-  ss = rows_sum(ss);
+  const float ss = rows_sum((sq[0] + sq[1]) + (sq[2] + sq[3]));
   /* H D x a 16-row tile at a time: lane (n, kq) gets rotated coordinates
    * l = 4 mt + 0..3 of its slice, turned at once into the residual
    * y / (sqrt(d) ||x||) - c[code] and its two fp16 parts */
   const float scale = ss > 0.0f ? 1.0f / (sqrtf((float)D) * sqrtf(ss)) : 0.0f;
   const uint32_t cpy = (uint32_t)lane & 3u;
-  float g2 = 0.0f;
-  half8 rhi[KS], rlo[KS];
+  float g2 = 0.0f, negone = -1.0f;
+  asm volatile("" : "+v"(negone));
+  uint32_t rhw[KS][4], rlw[KS][4];
 #pragma unroll
   for (int mt = 0; mt < D / 16; ++mt) {
     floatx4 t = {0.f, 0.f, 0.f, 0.f};
@@ -361,17 +381,20 @@ __device__ inline void enc_keys_m(const EncSlotM<D, B>& r, const QjlEncArgs& a, 
     }
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
+      /* coordinates l, l + 1 of the slice, l = 4 mt + 2 h: one fp16 pair */
       const float2 c = plev[pair_field<B>(r.cw, 2 * mt + h) * 4 + cpy];
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int l = 4 * mt + 2 * h + u;
-        const float rr = t[2 * h + u] * scale - (u ? c.y : c.x);
-        g2 += rr * rr;
-        const _Float16 hi = (_Float16)rr;
-        rhi[l / 8][l % 8] = hi;
-        rlo[l / 8][l % 8] = (_Float16)(rr - (float)hi);
-      }
+      const float r0 = t[2 * h] * scale - c.x, r1 = t[2 * h + 1] * scale - c.y;
+      g2 += r0 * r0;
+      g2 += r1 * r1;
+      const int l = 4 * mt + 2 * h;
+      split_pair(r0, r1, negone, rhw[l / 8][(l % 8) / 2], rlw[l / 8][(l % 8) / 2]);
     }
+  }
+  half8 rhi[KS], rlo[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    rhi[s] = __builtin_bit_cast(half8, u32x4{rhw[s][0], rhw[s][1], rhw[s][2], rhw[s][3]});
+    rlo[s] = __builtin_bit_cast(half8, u32x4{rlw[s][0], rlw[s][1], rlw[s][2], rlw[s][3]});
   }
   g2 = rows_sum(g2);
   if (live && kq == 0) a.gamma[v] = f2h(sqrtf(g2));
