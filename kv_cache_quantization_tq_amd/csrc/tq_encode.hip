@@ -739,6 +739,7 @@ __device__ inline TaskIter task_advance(const AppendArgs& a, TaskIter t, int ste
 struct TaskGeo {
   bool live;
   int layer, b, h, tile, jlo, jhi;
+  int full_end;        /* rows below this (and at or above p0) receive appended tokens */
   int64_t rbase;       /* row index (within the layer's rows) of the tile's row 0 */
   int64_t vt;          /* value-tile index within the layer's tiles */
   const uint16_t* src; /* fp16 input row of tile row j0 (the wave's first row) */
@@ -783,7 +784,7 @@ append_kernel(AppendArgs a) {
     g.layer = t.layer;
     g.b = t.b;
     g.h = t.h;
-    g.tile = g.jlo = g.jhi = 0;
+    g.tile = g.jlo = g.jhi = g.full_end = 0;
     g.rbase = g.vt = 0;
     g.src = src_all;
     if (t.task >= tasks) return g;
@@ -794,6 +795,10 @@ append_kernel(AppendArgs a) {
     /* the tile of this slot and its appended rows below capacity (nothing
      * when p0 is negative or at or past capacity) */
     if (!tq_append_tile_rows(p0, a.t_new, a.capacity, slot, &g.tile, &g.jlo, &g.jhi)) return g;
+    {
+      const int64_t fe = (int64_t)p0 + a.t_new;
+      g.full_end = fe < a.capacity ? (int)fe : a.capacity;
+    }
     if (a.block_table) {
       /* paged: the pool page of this tile's page (rows of pages outside the
        * pool are skipped) */
@@ -894,7 +899,19 @@ append_kernel(AppendArgs a) {
    * so the prefetch loads are issued on every path) */
   auto next_geo = [&](int64_t it, const TaskGeo& same) -> TaskGeo {
     if (it + 1 >= last) return same;
+    const int slot0 = tnext.slot;
     tnext = task_advance(a, tnext, kTPB);
+    /* the common case, the same stream's tile kTPB further on, with this
+     * tile and that one wholly appended: the geometry moves by constants */
+    if (!a.block_table && same.live && tnext.slot == slot0 + kTPB && same.jlo == 0 &&
+        same.jhi == 32 && 32 * (same.tile + kTPB) + 32 <= same.full_end) {
+      TaskGeo g = same;
+      g.tile += kTPB;
+      g.rbase += 32 * kTPB;
+      g.vt += kTPB;
+      g.src += (int64_t)32 * kTPB * D;
+      return g;
+    }
     return setup(tnext);
   };
   int64_t it = first;
