@@ -35,4 +35,20 @@ __host__ __device__ inline bool tq_append_tile_rows(int32_t p0, int32_t t_new, i
   return true;
 }
 
+/* The end of the appended rows below capacity: min(p0 + t_new, capacity)
+ * (in 64 bits, then at most capacity). */
+__host__ __device__ inline int32_t tq_append_full_end(int32_t p0, int32_t t_new, int32_t capacity) {
+  const int64_t fe = (int64_t)p0 + t_new;
+  return fe < capacity ? (int32_t)fe : capacity;
+}
+
+/* Whether the tile `step` tiles after `tile` is, like `tile` itself, written
+ * in all 32 rows, given tile's rows [jlo, jhi) and full_end from
+ * tq_append_full_end: then tq_append_tile_rows for the slot `step` further
+ * on gives tile + step, 0, 32. */
+__host__ __device__ inline bool tq_append_next_full(int32_t tile, int32_t jlo, int32_t jhi,
+                                                    int32_t full_end, int32_t step) {
+  return jlo == 0 && jhi == 32 && 32 * ((int64_t)tile + step) + 32 <= full_end;
+}
+
 #endif

@@ -795,10 +795,7 @@ append_kernel(AppendArgs a) {
     /* the tile of this slot and its appended rows below capacity (nothing
      * when p0 is negative or at or past capacity) */
     if (!tq_append_tile_rows(p0, a.t_new, a.capacity, slot, &g.tile, &g.jlo, &g.jhi)) return g;
-    {
-      const int64_t fe = (int64_t)p0 + a.t_new;
-      g.full_end = fe < a.capacity ? (int)fe : a.capacity;
-    }
+    g.full_end = tq_append_full_end(p0, a.t_new, a.capacity);
     if (a.block_table) {
       /* paged: the pool page of this tile's page (rows of pages outside the
        * pool are skipped) */
@@ -903,8 +900,8 @@ append_kernel(AppendArgs a) {
     tnext = task_advance(a, tnext, kTPB);
     /* the common case, the same stream's tile kTPB further on, with this
      * tile and that one wholly appended: the geometry moves by constants */
-    if (!a.block_table && same.live && tnext.slot == slot0 + kTPB && same.jlo == 0 &&
-        same.jhi == 32 && 32 * (same.tile + kTPB) + 32 <= same.full_end) {
+    if (!a.block_table && same.live && tnext.slot == slot0 + kTPB &&
+        tq_append_next_full(same.tile, same.jlo, same.jhi, same.full_end, kTPB)) {
       TaskGeo g = same;
       g.tile += kTPB;
       g.rbase += 32 * kTPB;

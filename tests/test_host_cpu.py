@@ -210,7 +210,9 @@ int main(void) {
     int32_t tile, jlo, jhi;
     bool ok = tq_append_tile_rows((int32_t)p0, (int32_t)t_new, (int32_t)cap, (int32_t)slot,
                                   &tile, &jlo, &jhi);
-    printf("%d %d %d %d\n", ok ? 1 : 0, tile, jlo, jhi);
+    const int32_t fe = tq_append_full_end((int32_t)p0, (int32_t)t_new, (int32_t)cap);
+    const bool nf = ok && tq_append_next_full(tile, jlo, jhi, fe, 2);
+    printf("%d %d %d %d %d\n", ok ? 1 : 0, tile, jlo, jhi, nf ? 1 : 0);
   }
   return 0;
 }
@@ -221,7 +223,8 @@ def test_append_tile_rows_arithmetic(tmp_path):
     """The append kernel's per-slot row arithmetic (tq_append_rows.h, compiled
     here for the host) against a brute-force statement of what an append
     writes: rows p0 .. p0 + t_new - 1 that are below capacity, cut into
-    32-token tiles.  Includes positions within 64 of INT32_MAX, where 32-bit
+    32-token tiles; and its shortcut for a wave's next task (the slot two
+    further on), taken exactly when both tiles are written in all 32 rows.  Includes positions within 64 of INT32_MAX, where 32-bit
     row arithmetic would wrap and write far past the stream."""
     import subprocess
     src = tmp_path / "rows.cpp"
@@ -239,13 +242,16 @@ def test_append_tile_rows_arithmetic(tmp_path):
         for p0 in starts:
             for t_new in (1, 7, 8, 32, 40, 2049, imax - 3):
                 nslots = min((t_new + 31) // 32 + 1, 70)
-                for slot in list(range(min(nslots, 4))) + [nslots - 1]:
+                for slot in sorted(set(list(range(min(nslots, 6))) + [nslots - 3, nslots - 1])):
                     cases.append((p0, t_new, cap, slot))
     inp = "\n".join(" ".join(map(str, c)) for c in cases) + "\n"
     res = subprocess.run([str(exe)], input=inp, capture_output=True, text=True, check=True)
     lines = res.stdout.split("\n")
+    got = {}
     for (p0, t_new, cap, slot), line in zip(cases, lines):
-        ok, tile, jlo, jhi = map(int, line.split())
+        got[(p0, t_new, cap, slot)] = tuple(map(int, line.split()))
+    for (p0, t_new, cap, slot), line in zip(cases, lines):
+        ok, tile, jlo, jhi, nf = map(int, line.split())
         # brute force: appended rows below capacity, within this slot's tile
         want = None
         if 0 <= p0 < cap:
@@ -258,4 +264,16 @@ def test_append_tile_rows_arithmetic(tmp_path):
         else:
             assert ok == 1 and (tile, jlo, jhi) == want, (p0, t_new, cap, slot, line, want)
             assert 32 * tile + jhi <= cap and 0 <= jlo < jhi <= 32
+        # the kernel's shortcut: when tq_append_next_full says so, the slot two
+        # further on is the next-but-one tile, written in all 32 rows
+        full2 = (0 <= p0 < cap and 32 * (p0 // 32 + slot + 2) >= p0
+                 and 32 * (p0 // 32 + slot + 2) + 32 <= min(p0 + t_new, cap))
+        if nf:
+            assert want is not None and (want[1], want[2]) == (0, 32) and full2, \
+                (p0, t_new, cap, slot, line)
+        elif want is not None and (want[1], want[2]) == (0, 32) and full2:
+            raise AssertionError(("shortcut missed", p0, t_new, cap, slot, line))
+        if (p0, t_new, cap, slot + 2) in got and nf:
+            assert got[(p0, t_new, cap, slot + 2)][:4] == (1, tile + 2, 0, 32), \
+                (p0, t_new, cap, slot, got[(p0, t_new, cap, slot + 2)])
     assert len(lines) >= len(cases)
