@@ -38,6 +38,13 @@
 
 #include "tq_internal.h"
 
+/* This source builds two units: by itself, the 128-dim kernels and the
+ * entry point tq_launch_prefill, which hands other head dims to
+ * tq_launch_prefill_other; with TQ_PREFILL_OTHER defined
+ * (tq_prefill_other.hip), the 64- and 256-dim kernels behind that function.
+ * The units are compiled with different scheduling options (the build
+ * script's per-source flags). */
+
 namespace {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
@@ -932,10 +939,17 @@ tq_status launch_prefill_t(const PreArgs& a, int64_t blocks, hipStream_t s) {
 
 }  // namespace
 
+#ifndef TQ_PREFILL_OTHER
 tq_status tq_launch_prefill(const tq_kv_cache* c, const tq_codebook_s* cbk,
                             const tq_codebook_s* cbv, const uint8_t* sign_bits,
                             const uint16_t* q, int q_heads, int t_new, const int32_t* pos,
                             int n_layers, float* out, hipStream_t s) {
+#else
+tq_status tq_launch_prefill_other(const tq_kv_cache* c, const tq_codebook_s* cbk,
+                                  const tq_codebook_s* cbv, const uint8_t* sign_bits,
+                                  const uint16_t* q, int q_heads, int t_new, const int32_t* pos,
+                                  int n_layers, float* out, hipStream_t s) {
+#endif
   PreArgs a;
   a.k_codes = c->k_codes;
   a.v_codes = c->v_codes;
@@ -980,8 +994,15 @@ tq_status tq_launch_prefill(const tq_kv_cache* c, const tq_codebook_s* cbk,
 #define TQ_PRE_D(DD) \
   TQ_PRE(DD, 2, 2) TQ_PRE(DD, 2, 3) TQ_PRE(DD, 2, 4) TQ_PRE(DD, 3, 2) TQ_PRE(DD, 3, 3) \
   TQ_PRE(DD, 3, 4) TQ_PRE(DD, 4, 2) TQ_PRE(DD, 4, 3) TQ_PRE(DD, 4, 4)
-  TQ_PRE_D(64) TQ_PRE_D(128) TQ_PRE_D(256)
+#ifndef TQ_PREFILL_OTHER
+  TQ_PRE_D(128)
+#undef TQ_PRE_D
+#undef TQ_PRE
+  return tq_launch_prefill_other(c, cbk, cbv, sign_bits, q, q_heads, t_new, pos, n_layers, out, s);
+#else
+  TQ_PRE_D(64) TQ_PRE_D(256)
 #undef TQ_PRE_D
 #undef TQ_PRE
   return TQ_ERR_UNSUPPORTED;
+#endif
 }
