@@ -80,11 +80,6 @@ tq_status tq_launch_prefill(const tq_kv_cache* c, const tq_codebook_s* cbk,
                             const tq_codebook_s* cbv, const uint8_t* sign_bits,
                             const uint16_t* q, int q_heads, int t_new, const int32_t* pos,
                             int n_layers, float* out, hipStream_t stream);
-/* tq_launch_prefill for head dims other than 128 (a separate unit) */
-tq_status tq_launch_prefill_other(const tq_kv_cache* c, const tq_codebook_s* cbk,
-                                  const tq_codebook_s* cbv, const uint8_t* sign_bits,
-                                  const uint16_t* q, int q_heads, int t_new, const int32_t* pos,
-                                  int n_layers, float* out, hipStream_t stream);
 
 tq_status tq_launch_qjl_encode(const tq_codebook_s* cb, const uint16_t* x, int64_t n,
                                int64_t stride, const uint8_t* sign_bits, const uint16_t* S,

@@ -44,6 +44,10 @@
  * (tq_prefill_other.hip), the 64- and 256-dim kernels behind that function.
  * The units are compiled with different scheduling options (the build
  * script's per-source flags). */
+tq_status tq_launch_prefill_other(const tq_kv_cache* c, const tq_codebook_s* cbk,
+                                  const tq_codebook_s* cbv, const uint8_t* sign_bits,
+                                  const uint16_t* q, int q_heads, int t_new, const int32_t* pos,
+                                  int n_layers, float* out, hipStream_t stream);
 
 namespace {
 
